@@ -1,0 +1,136 @@
+"""fp64 CPU oracle for SlimKV latent decode attention -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The HIP library never does, and this package
+never imports the library: the two share no code.
+
+``decode`` runs the plain C implementation in ``slimkv_oracle.c`` (double
+precision throughout, OpenMP over (batch, kv head) units).  Its definition
+follows page "Can SlimKV compress KV cache jointly across tokens and
+features", section "Latent-space attention removes the rebuild step": the
+rotated query is projected into each KV head's beacon latent space, scored
+against rotation-free latent beacon keys and rotated raw-token keys under one
+softmax, and the latent value sum is lifted once by U_V.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+HERE = pathlib.Path(__file__).resolve().parent
+SOURCE = HERE / "slimkv_oracle.c"
+LIBRARY = HERE / "libslimkv_oracle.so"
+
+_DTYPE = {np.dtype(np.float64): 0, np.dtype(np.float32): 1, np.dtype(np.uint16): 2}
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_beacons", ctypes.c_int32),
+        ("rank_k", ctypes.c_int32),
+        ("rank_v", ctypes.c_int32),
+        ("raw_window", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+        ("rope_theta", ctypes.c_double),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def build(source: pathlib.Path = SOURCE, target: pathlib.Path = LIBRARY) -> pathlib.Path:
+    """Compile the C oracle with gcc (always rebuilds)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           str(source), "-o", str(target) + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(str(target) + ".tmp", target)
+    return target
+
+
+_lib_cache: dict = {}
+
+
+def load(path=LIBRARY) -> ctypes.CDLL:
+    path = pathlib.Path(path)
+    key = str(path)
+    if key not in _lib_cache:
+        if not path.exists():
+            build(target=path)
+        lib = ctypes.CDLL(key)
+        lib.slimkv_oracle_decode.restype = ctypes.c_int
+        lib.slimkv_oracle_decode.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 8 + [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.slimkv_oracle_max_threads.restype = ctypes.c_int
+        _lib_cache[key] = lib
+    return _lib_cache[key]
+
+
+def max_threads() -> int:
+    return int(load().slimkv_oracle_max_threads())
+
+
+def _arr(x, dtype):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return a
+
+
+def decode(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, scale: float,
+           rope_theta: float, units=None, threads: int = 0, library: pathlib.Path = LIBRARY):
+    """fp64 latent decode attention.
+
+    Arrays are numpy, row-major, all in one storage dtype (float64, float32,
+    or uint16 holding bf16 bits):
+        q [B, H_q, d], q_pos [B] int32, U_K [H_kv, d, r_K], U_V [H_kv, d, r_V],
+        C_K [B, H_kv, N_b, r_K], C_V [B, H_kv, N_b, r_V],
+        K_raw [B, H_kv, W, d] (already rotated), V_raw [B, H_kv, W, d].
+    C_K/C_V (or K_raw/V_raw) may be None when N_b (or W) is 0.
+    ``units`` is an optional list of (b, kv_head) pairs to compute; other
+    rows of the result stay NaN.  Returns (out [B, H_q, d], lse [B, H_q]) in
+    float64; lse is in natural-log units of the scaled scores.
+    """
+    q = np.ascontiguousarray(q)
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported storage dtype {dt}")
+    B, Hq, d = q.shape
+    q_pos = _arr(q_pos, np.dtype(np.int32))
+    nb = 0 if C_K is None else int(np.shape(C_K)[2])
+    w = 0 if K_raw is None else int(np.shape(K_raw)[2])
+    rk = int(np.shape(U_K)[2]) if U_K is not None else 0
+    rv = int(np.shape(U_V)[2]) if U_V is not None else 0
+    U_K, U_V, C_K, C_V, K_raw, V_raw = (_arr(x, dt) for x in (U_K, U_V, C_K, C_V, K_raw, V_raw))
+    prob = _Problem(B, Hq, num_kv_heads, d, nb, rk, rv, w, float(scale), float(rope_theta),
+                    _DTYPE[dt])
+    out = np.full((B, Hq, d), np.nan, dtype=np.float64)
+    lse = np.full((B, Hq), np.nan, dtype=np.float64)
+    if units is None:
+        unit_arr, n_units = None, 0
+    else:
+        unit_arr = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+        n_units = unit_arr.shape[0]
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = load(library).slimkv_oracle_decode(
+        ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+        ptr(K_raw), ptr(V_raw), ptr(unit_arr), n_units, ptr(out), ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out, lse
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,233 @@
+/*
+ * slimkv_oracle.c -- plain fp64 CPU oracle for SlimKV latent decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this file's library.  It shares no code,
+ * header or constant with the HIP library it checks.
+ *
+ * What it computes (page "Can SlimKV compress KV cache jointly across tokens
+ * and features", section "Latent-space attention removes the rebuild step";
+ * the abstract on page "SlimKV: Joint Token-Feature KV Cache Compression with
+ * Reconstruction-Free Beacon Attention"): for one decode query per sequence,
+ * attention over a cache made of
+ *   - N_b beacon rows held as low-rank latents C_K (rank r_K) and C_V
+ *     (rank r_V) whose keys carry no rotary position, and
+ *   - W raw-token rows K_raw, V_raw at full head dimension d whose keys are
+ *     stored already rotated;
+ * the query keeps its rotation.  Beacon scores are taken in latent space as
+ * (q' U_K) . C_K[j], beacon values are summed in latent space as sum_j a_j
+ * C_V[j] and lifted once by U_V; beacon and raw rows share one softmax.
+ *
+ * Every step is done in double precision, in the order the section lists
+ * it, per query head:
+ *   1. q' = RoPE(q, q_pos)           rotate-half pairs (i, i + d/2),
+ *                                      angle q_pos * theta^(-2i/d)
+ *   2. qh = U_K^T q'                   query in the head's latent key space
+ *   3. s_j = scale * qh . C_K[j]       (j < N_b, no rotation on C_K)
+ *      s_{N_b+t} = scale * q' . K_raw[t]
+ *   4. a = softmax(s) over all N_b + W rows jointly
+ *   5. o_lat = sum_j a_j C_V[j],  o_raw = sum_t a_{N_b+t} V_raw[t]
+ *   6. out = U_V o_lat + o_raw,     lse = max(s) + log(sum exp(s - max(s)))
+ * Query head g reads KV head floor(g / G), G = H_q / H_kv.
+ *
+ * Inputs are read in their storage format (fp64, fp32, or bf16 as the top
+ * 16 bits of an IEEE binary32) and widened exactly to double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
+
+enum {
+  ORACLE_OK = 0,
+  ORACLE_BAD_SHAPE = 1,
+  ORACLE_BAD_DTYPE = 2,
+  ORACLE_NO_MEMORY = 3,
+};
+
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_beacons;
+  int32_t rank_k;
+  int32_t rank_v;
+  int32_t raw_window;
+  double scale;
+  double rope_theta;
+  int32_t dtype;
+} oracle_problem;
+
+static double widen(const void* base, int dtype, size_t i) {
+  if (dtype == ORACLE_F64) return ((const double*)base)[i];
+  if (dtype == ORACLE_F32) return (double)((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* One (b, kv head) unit: all G query heads of the group. */
+static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
+                        const int32_t* q_pos, const void* U_K, const void* U_V,
+                        const void* C_K, const void* C_V, const void* K_raw,
+                        const void* V_raw, double* out, double* lse,
+                        double* work) {
+  const int d = p->head_dim, half = p->head_dim / 2;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int nb = p->num_beacons, w = p->raw_window;
+  const int rk = p->rank_k, rv = p->rank_v;
+  const int dt = p->dtype;
+  const size_t n = (size_t)nb + (size_t)w;
+
+  double* qr = work;          /* [d]   rotated query          */
+  double* qh = qr + d;        /* [rk]  latent query           */
+  double* s = qh + rk;        /* [n]   scores, then weights   */
+  double* olat = s + n;       /* [rv]  latent value sum       */
+  double* oraw = olat + rv;   /* [d]   raw value sum          */
+
+  const size_t unit = (size_t)b * p->num_kv_heads + h;
+  const size_t ck0 = unit * (size_t)nb * rk, cv0 = unit * (size_t)nb * rv;
+  const size_t kr0 = unit * (size_t)w * d;
+  const size_t uk0 = (size_t)h * d * rk, uv0 = (size_t)h * d * rv;
+
+  for (int g = 0; g < G; ++g) {
+    const int hq = h * G + g;
+    const size_t q0 = ((size_t)b * p->num_q_heads + hq) * d;
+
+    /* 1. rotary embedding of the query at its own position */
+    for (int i = 0; i < half; ++i) {
+      double inv_freq = pow(p->rope_theta, -2.0 * (double)i / (double)d);
+      double ang = (double)q_pos[b] * inv_freq;
+      double c = cos(ang), sn = sin(ang);
+      double x1 = widen(q, dt, q0 + i), x2 = widen(q, dt, q0 + i + half);
+      qr[i] = x1 * c - x2 * sn;
+      qr[i + half] = x2 * c + x1 * sn;
+    }
+
+    /* 2. projection into the beacon latent key space: qh = U_K^T q' */
+    for (int k = 0; k < rk; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += qr[i] * widen(U_K, dt, uk0 + (size_t)i * rk + k);
+      qh[k] = acc;
+    }
+
+    /* 3. scores: latent beacons, then rotated raw keys */
+    for (int j = 0; j < nb; ++j) {
+      double acc = 0.0;
+      for (int k = 0; k < rk; ++k) acc += qh[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+      s[j] = p->scale * acc;
+    }
+    for (int t = 0; t < w; ++t) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += qr[i] * widen(K_raw, dt, kr0 + (size_t)t * d + i);
+      s[nb + t] = p->scale * acc;
+    }
+
+    /* 4. one softmax over beacon and raw rows together */
+    double m = -INFINITY;
+    for (size_t j = 0; j < n; ++j) m = s[j] > m ? s[j] : m;
+    double l = 0.0;
+    for (size_t j = 0; j < n; ++j) {
+      s[j] = exp(s[j] - m);
+      l += s[j];
+    }
+    for (size_t j = 0; j < n; ++j) s[j] /= l;
+
+    /* 5. value sums: latent for beacons, full width for raw rows */
+    for (int k = 0; k < rv; ++k) olat[k] = 0.0;
+    for (int j = 0; j < nb; ++j)
+      for (int k = 0; k < rv; ++k) olat[k] += s[j] * widen(C_V, dt, cv0 + (size_t)j * rv + k);
+    for (int i = 0; i < d; ++i) oraw[i] = 0.0;
+    for (int t = 0; t < w; ++t)
+      for (int i = 0; i < d; ++i) oraw[i] += s[nb + t] * widen(V_raw, dt, kr0 + (size_t)t * d + i);
+
+    /* 6. lift the latent value sum once: out = U_V o_lat + o_raw */
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * olat[k];
+      out[q0 + i] = acc + oraw[i];
+    }
+    if (lse) lse[(size_t)b * p->num_q_heads + hq] = m + log(l);
+  }
+}
+
+/*
+ * Compute the units listed in `units` (pairs b, h; NULL means every unit).
+ * out: [B, H_q, d] doubles, lse: [B, H_q] doubles or NULL; entries of units
+ * not listed are left untouched.  threads <= 0 uses the OpenMP default.
+ */
+int slimkv_oracle_decode(const oracle_problem* p, const void* q,
+                         const int32_t* q_pos, const void* U_K,
+                         const void* U_V, const void* C_K, const void* C_V,
+                         const void* K_raw, const void* V_raw,
+                         const int32_t* units, int64_t n_units, double* out,
+                         double* lse, int threads) {
+  if (!p || !q || !q_pos || !out) return ORACLE_BAD_SHAPE;
+  if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
+    return ORACLE_BAD_DTYPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 ||
+      p->num_q_heads % p->num_kv_heads != 0 || p->head_dim < 2 || p->head_dim % 2 ||
+      p->num_beacons < 0 || p->raw_window < 0 ||
+      (int64_t)p->num_beacons + p->raw_window < 1)
+    return ORACLE_BAD_SHAPE;
+  if (p->num_beacons > 0 && (p->rank_k < 1 || p->rank_v < 1 || !U_K || !U_V || !C_K || !C_V))
+    return ORACLE_BAD_SHAPE;
+  if (p->raw_window > 0 && (!K_raw || !V_raw)) return ORACLE_BAD_SHAPE;
+
+  const int64_t all = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t count = units ? n_units : all;
+  const int rk = p->num_beacons > 0 ? p->rank_k : 0;
+  const int rv = p->num_beacons > 0 ? p->rank_v : 0;
+  const size_t work_len =
+      2 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window;
+  oracle_problem pp = *p;
+  pp.rank_k = rk;
+  pp.rank_v = rv;
+
+  int failed = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel
+  {
+    double* work = (double*)malloc(work_len * sizeof(double));
+    if (!work) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < count; ++u) {
+      if (!work) continue;
+      int b = units ? units[2 * u] : (int)(u / p->num_kv_heads);
+      int h = units ? units[2 * u + 1] : (int)(u % p->num_kv_heads);
+      if (b < 0 || b >= p->batch || h < 0 || h >= p->num_kv_heads) {
+#pragma omp atomic write
+        failed = 2;
+        continue;
+      }
+      oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse, work);
+    }
+    free(work);
+  }
+  if (failed == 1) return ORACLE_NO_MEMORY;
+  if (failed == 2) return ORACLE_BAD_SHAPE;
+  return ORACLE_OK;
+}
+
+/* Threads an OpenMP parallel region would use (for reporting). */
+int slimkv_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

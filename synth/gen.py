@@ -1,0 +1,186 @@
+"""Seeded tensor generator for one layer of a decode-attention workload.
+
+Layouts (row-major, contiguous), with G = H_q / H_kv and r the layer rank:
+    q       [B, H_q, d]          decode query, before RoPE
+    q_pos   [B]       int32      absolute position of the decode query
+    U_K     [H_kv, d, r]         beacon key basis (orthonormal columns)
+    U_V     [H_kv, d, r]         beacon value basis (orthonormal columns)
+    C_K     [B, H_kv, N_b, r]    latent beacon keys (carry no rotation)
+    C_V     [B, H_kv, N_b, r]    latent beacon values
+    K_raw   [B, H_kv, W, d]      raw-window keys, already rotated at their positions
+    V_raw   [B, H_kv, W, d]      raw-window values
+
+Distributions.  Every tensor except the bases is i.i.d. N(0, sigma^2),
+drawn in fp32 and rounded once to the storage dtype (round-to-nearest-even
+for bf16).  Raw keys are drawn directly in their rotated form: a rotation
+of each (i, i + d/2) pair maps an isotropic Gaussian pair to another one,
+so rotated i.i.d. Gaussian keys are distributed exactly like unrotated
+ones, and the generator needs no positional arithmetic.  The bases are
+the Q factor of a seeded N(0,1) d x r matrix (fp64 QR, columns signed so
+that diag(R) > 0), rounded to the storage dtype.
+
+Token rows (raw keys and values, and a full uncompressed cache) are drawn in
+blocks of ``TOKEN_BLOCK`` positions with one seed per block, so the raw
+window of a compressed cache is bit-identical to the last rows of the full
+cache of the same workload and layer.
+
+Seeds: each tensor's seed is derived from (base seed, workload index,
+layer, tensor id, extra) through numpy's SeedSequence, then fed to a torch
+generator on the target device.  Values generated on the CPU and on a GPU
+therefore differ, but each is reproducible on its own device.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from .configs import Workload
+
+TOKEN_BLOCK = 128
+
+_IDS = {"q": 1, "U_K": 2, "U_V": 3, "C_K": 4, "C_V": 5, "K_tok": 6, "V_tok": 7}
+
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _seed(base: int, wl: Workload, layer: int, name: str, *extra: int) -> int:
+    ss = np.random.SeedSequence([base, wl.index, layer, _IDS[name], *extra])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def _gauss(shape, seed: int, sigma: float, dtype: str, device) -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(_TORCH_DTYPE[dtype])
+
+
+def orthonormal_basis(d: int, r: int, seed: int) -> torch.Tensor:
+    """Q factor (d x r, fp64, CPU) of a seeded Gaussian matrix, diag(R) > 0."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    a = torch.randn((d, r), generator=g, dtype=torch.float64)
+    qm, rm = torch.linalg.qr(a)
+    signs = torch.sign(torch.diagonal(rm))
+    signs[signs == 0] = 1.0
+    return qm * signs
+
+
+def _tokens(wl: Workload, layer: int, name: str, base: int, first: int, count: int, device):
+    """Rows [first, first + count) of the token cache ``name`` ([B,H_kv,count,d])."""
+    assert first % TOKEN_BLOCK == 0 and count % TOKEN_BLOCK == 0
+    blocks = []
+    for start in range(first, first + count, TOKEN_BLOCK):
+        blk = start // TOKEN_BLOCK
+        blocks.append(
+            _gauss((wl.batch, wl.num_kv_heads, TOKEN_BLOCK, wl.head_dim),
+                   _seed(base, wl, layer, name, blk), wl.sigma, wl.dtype, device))
+    if not blocks:
+        return torch.empty((wl.batch, wl.num_kv_heads, 0, wl.head_dim),
+                           dtype=_TORCH_DTYPE[wl.dtype], device=device)
+    return torch.cat(blocks, dim=2).contiguous()
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """All tensors of one layer call, on one device."""
+
+    workload: Workload
+    layer: int
+    rank: int
+    q: torch.Tensor
+    q_pos: torch.Tensor
+    U_K: torch.Tensor
+    U_V: torch.Tensor
+    C_K: torch.Tensor
+    C_V: torch.Tensor
+    K_raw: torch.Tensor
+    V_raw: torch.Tensor
+
+    @property
+    def num_beacons(self) -> int:
+        return int(self.C_K.shape[2])
+
+    @property
+    def raw_window(self) -> int:
+        return int(self.K_raw.shape[2])
+
+    def to(self, device) -> "LayerInputs":
+        moved = {f.name: getattr(self, f.name) for f in dataclasses.fields(self)}
+        for k, v in moved.items():
+            if isinstance(v, torch.Tensor):
+                moved[k] = v.to(device)
+        return LayerInputs(**moved)
+
+
+def make_layer(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu",
+               num_beacons: int | None = None, raw_window: int | None = None) -> LayerInputs:
+    """Generate one layer of ``wl`` on ``device``.
+
+    ``num_beacons`` / ``raw_window`` override the workload's values (tests
+    use this for ragged and degenerate shapes).  Raw rows always end at the
+    decode position: they cover positions [T - W, T).
+    """
+    nb = wl.num_beacons if num_beacons is None else num_beacons
+    w = wl.raw_window if raw_window is None else raw_window
+    r = wl.ranks[layer]
+    d = wl.head_dim
+    dt = _TORCH_DTYPE[wl.dtype]
+
+    q = _gauss((wl.batch, wl.num_q_heads, d), _seed(base_seed, wl, layer, "q"), wl.sigma,
+               wl.dtype, device)
+    q_pos = torch.full((wl.batch,), wl.q_pos, dtype=torch.int32, device=device)
+    uk = torch.stack([orthonormal_basis(d, r, _seed(base_seed, wl, layer, "U_K", h, r))
+                      for h in range(wl.num_kv_heads)]).to(dt).to(device)
+    uv = torch.stack([orthonormal_basis(d, r, _seed(base_seed, wl, layer, "U_V", h, r))
+                      for h in range(wl.num_kv_heads)]).to(dt).to(device)
+    ck = _gauss((wl.batch, wl.num_kv_heads, nb, r), _seed(base_seed, wl, layer, "C_K", nb, r),
+                wl.sigma, wl.dtype, device)
+    cv = _gauss((wl.batch, wl.num_kv_heads, nb, r), _seed(base_seed, wl, layer, "C_V", nb, r),
+                wl.sigma, wl.dtype, device)
+    if w % TOKEN_BLOCK == 0 and wl.context % TOKEN_BLOCK == 0:
+        kr = _tokens(wl, layer, "K_tok", base_seed, wl.context - w, w, device)
+        vr = _tokens(wl, layer, "V_tok", base_seed, wl.context - w, w, device)
+    else:  # ragged windows (tests): one block, seeded by the window length
+        shape = (wl.batch, wl.num_kv_heads, w, d)
+        kr = _gauss(shape, _seed(base_seed, wl, layer, "K_tok", 1 << 30, w), wl.sigma, wl.dtype,
+                    device)
+        vr = _gauss(shape, _seed(base_seed, wl, layer, "V_tok", 1 << 30, w), wl.sigma, wl.dtype,
+                    device)
+    return LayerInputs(wl, layer, r, q, q_pos, uk, uv, ck, cv, kr, vr)
+
+
+def make_full_kv(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu"):
+    """Uncompressed cache of all T tokens, [B, H_kv, T, d] each (keys rotated)."""
+    k = _tokens(wl, layer, "K_tok", base_seed, 0, wl.context, device)
+    v = _tokens(wl, layer, "V_tok", base_seed, 0, wl.context, device)
+    return k, v
+
+
+def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
+    """CPU numpy view of a tensor in its storage format (bf16 as uint16 bits)."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def unit_slices(inp: LayerInputs, b: int, h: int) -> dict:
+    """Storage-format numpy arrays of one (b, kv head) unit, shaped as a
+    problem with batch 1 and a single KV head (G query heads)."""
+    g = inp.workload.group
+    return {
+        "q": to_numpy_storage(inp.q[b:b + 1, h * g:(h + 1) * g]),
+        "q_pos": to_numpy_storage(inp.q_pos[b:b + 1]),
+        "U_K": to_numpy_storage(inp.U_K[h:h + 1]),
+        "U_V": to_numpy_storage(inp.U_V[h:h + 1]),
+        "C_K": to_numpy_storage(inp.C_K[b:b + 1, h:h + 1]),
+        "C_V": to_numpy_storage(inp.C_V[b:b + 1, h:h + 1]),
+        "K_raw": to_numpy_storage(inp.K_raw[b:b + 1, h:h + 1]),
+        "V_raw": to_numpy_storage(inp.V_raw[b:b + 1, h:h + 1]),
+    }

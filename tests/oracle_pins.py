@@ -1,0 +1,255 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle built at
+``library`` disagrees with an independent statement of what the method
+computes (page "Can SlimKV compress KV cache jointly across tokens and
+features", section "Latent-space attention removes the rebuild step"):
+
+* reconstruct-then-attend: building full beacon keys C_K U_K^T and values
+  C_V U_V^T and running ordinary attention (torch's fp64 SDPA) must give the
+  same result as the latent path -- the identity the section rests on;
+* a raw-only window is ordinary rotary GQA attention, with the rotation
+  written independently as complex multiplication;
+* with an identity basis and no raw window, beacon keys enter unrotated;
+* rotary scores depend only on relative position;
+* closed forms of the softmax (zero query, one key, two keys);
+* invariants: weights sum to one, orthogonal re-basing of a latent space,
+  row permutations.
+
+The same functions run against deliberately broken copies of the oracle
+(tests/test_oracle_mutants.py) to show that a plausible mistake fails one.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = 1e-11
+
+
+def _ortho(rng, d, r):
+    a = rng.standard_normal((d, r))
+    qm, rm = np.linalg.qr(a)
+    return qm * np.sign(np.diag(rm))
+
+
+def rope_complex(x: np.ndarray, pos, theta: float) -> np.ndarray:
+    """Rotary embedding as complex multiplication: pair (i, i + d/2) is the
+    complex number x_i + 1j x_{i+d/2}, turned by angle pos * theta**(-2i/d).
+    ``pos`` broadcasts against the leading axes of x."""
+    d = x.shape[-1]
+    half = d // 2
+    freqs = np.exp(-(2.0 * np.arange(half) / d) * math.log(theta))
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * freqs
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def random_problem(seed, *, B=1, Hkv=1, G=4, d=16, nb=5, rk=4, rv=6, w=3, theta=10000.0,
+                   q_pos=None, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    Hq = Hkv * G
+    qp = np.full(B, w + 7 if q_pos is None else q_pos, dtype=np.int32)
+    raw_pos = qp[:, None] - w + 1 + np.arange(w)[None, :]  # [B, W]
+    k_pre = sigma * rng.standard_normal((B, Hkv, w, d))
+    return dict(
+        q=sigma * rng.standard_normal((B, Hq, d)),
+        q_pos=qp,
+        U_K=np.stack([_ortho(rng, d, rk) for _ in range(Hkv)]),
+        U_V=np.stack([_ortho(rng, d, rv) for _ in range(Hkv)]),
+        C_K=sigma * rng.standard_normal((B, Hkv, nb, rk)),
+        C_V=sigma * rng.standard_normal((B, Hkv, nb, rv)),
+        K_pre=k_pre,
+        K_raw=rope_complex(k_pre, raw_pos[:, None, :], theta),
+        V_raw=sigma * rng.standard_normal((B, Hkv, w, d)),
+        theta=theta,
+        scale=1.0 / math.sqrt(d),
+        num_kv_heads=Hkv,
+    )
+
+
+def run_oracle(p, library, **over):
+    args = dict(p)
+    args.update(over)
+    nb = args["C_K"].shape[2]
+    w = args["K_raw"].shape[2]
+    return oracle.decode(
+        args["q"], args["q_pos"], args["U_K"], args["U_V"],
+        args["C_K"] if nb else None, args["C_V"] if nb else None,
+        args["K_raw"] if w else None, args["V_raw"] if w else None,
+        num_kv_heads=args["num_kv_heads"], scale=args["scale"], rope_theta=args["theta"],
+        library=library)
+
+
+def sdpa_reference(q_rot, K, V, scale, G):
+    """Ordinary attention of one query per head; K, V: [B, H_kv, n, d]."""
+    qt = torch.from_numpy(q_rot)[:, :, None, :]  # [B, Hq, 1, d]
+    kt = torch.from_numpy(np.ascontiguousarray(K)).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(np.ascontiguousarray(V)).repeat_interleave(G, dim=1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    scores = scale * torch.matmul(qt, kt.transpose(-1, -2).contiguous())[:, :, 0, :]
+    lse = torch.logsumexp(scores, dim=-1)
+    return out[:, :, 0, :].numpy(), lse.numpy()
+
+
+def reconstruct_reference(p):
+    G = p["q"].shape[1] // p["num_kv_heads"]
+    q_rot = rope_complex(p["q"], p["q_pos"][:, None], p["theta"])
+    kb = np.einsum("bhjr,hdr->bhjd", p["C_K"], p["U_K"])
+    vb = np.einsum("bhjr,hdr->bhjd", p["C_V"], p["U_V"])
+    K = np.concatenate([kb, p["K_raw"]], axis=2)
+    V = np.concatenate([vb, p["V_raw"]], axis=2)
+    return sdpa_reference(q_rot, K, V, p["scale"], G)
+
+
+def _close(a, b, tol=TOL, what=""):
+    err = float(np.max(np.abs(np.asarray(a) - np.asarray(b))))
+    ref = max(1.0, float(np.max(np.abs(b))))
+    assert err <= tol * ref, f"{what}: max abs error {err:.3e} (tolerance {tol * ref:.1e})"
+
+
+SHAPES = [
+    dict(B=1, Hkv=1, G=1, d=8, nb=1, rk=2, rv=3, w=0),
+    dict(B=2, Hkv=2, G=4, d=16, nb=17, rk=4, rv=8, w=3),
+    dict(B=1, Hkv=3, G=5, d=16, nb=0, rk=4, rv=4, w=17),
+    dict(B=2, Hkv=1, G=4, d=128, nb=33, rk=32, rv=48, w=1),
+    dict(B=1, Hkv=2, G=2, d=128, nb=3, rk=64, rv=16, w=17, theta=500000.0, q_pos=131071),
+]
+
+
+def pin_reconstruct_identity(library):
+    for i, shape in enumerate(SHAPES):
+        p = random_problem(100 + i, **shape)
+        out, lse = run_oracle(p, library)
+        ref_out, ref_lse = reconstruct_reference(p)
+        _close(out, ref_out, what=f"out, shape {shape}")
+        _close(lse, ref_lse, what=f"lse, shape {shape}")
+
+
+def pin_raw_only_rope_gqa(library):
+    p = random_problem(7, B=2, Hkv=2, G=4, d=128, nb=0, rk=8, rv=8, w=29, theta=500000.0,
+                       q_pos=32767)
+    out, lse = run_oracle(p, library)
+    q_rot = rope_complex(p["q"], p["q_pos"][:, None], p["theta"])
+    ref_out, ref_lse = sdpa_reference(q_rot, p["K_raw"], p["V_raw"], p["scale"], 4)
+    _close(out, ref_out, what="raw-only out")
+    _close(lse, ref_lse, what="raw-only lse")
+
+
+def pin_beacon_keys_unrotated(library):
+    d = 16
+    p = random_problem(8, B=1, Hkv=2, G=2, d=d, nb=9, rk=d, rv=d, w=0, q_pos=12345)
+    eye = np.stack([np.eye(d), np.eye(d)])
+    p["U_K"], p["U_V"] = eye, eye
+    out, lse = run_oracle(p, library)
+    q_rot = rope_complex(p["q"], p["q_pos"][:, None], p["theta"])
+    ref_out, ref_lse = sdpa_reference(q_rot, p["C_K"], p["C_V"], p["scale"], 2)
+    _close(out, ref_out, what="beacon-only out")
+    _close(lse, ref_lse, what="beacon-only lse")
+
+
+def pin_relative_position(library):
+    """Raw-only window: shifting the query and every raw key by the same
+    offset leaves the result unchanged; shifting only the query changes it.
+    (Beacon keys carry no rotation, so with beacons present the property
+    does not hold and is not tested here.)"""
+    p = random_problem(9, B=1, Hkv=1, G=4, d=32, nb=0, rk=8, rv=8, w=6, q_pos=50)
+    out0, lse0 = run_oracle(p, library)
+    for shift in (1, 1000, 100000):
+        qp = p["q_pos"] + shift
+        raw_pos = qp[:, None] - 6 + 1 + np.arange(6)[None, :]
+        k = rope_complex(p["K_pre"], raw_pos[:, None, :], p["theta"])
+        out1, lse1 = run_oracle(p, library, q_pos=qp.astype(np.int32), K_raw=k)
+        _close(out1, out0, tol=1e-9, what=f"shift {shift}")
+        _close(lse1, lse0, tol=1e-9, what=f"shift {shift}")
+    out2, _ = run_oracle(p, library, q_pos=(p["q_pos"] + 3).astype(np.int32))
+    assert np.max(np.abs(out2 - out0)) > 1e-6, "query position has no effect"
+
+
+def pin_position_zero(library):
+    p = random_problem(10, B=1, Hkv=1, G=2, d=16, nb=0, rk=4, rv=4, w=5, q_pos=0)
+    out, _ = run_oracle(p, library)
+    ref, _ = sdpa_reference(p["q"], p["K_raw"], p["V_raw"], p["scale"], 2)
+    _close(out, ref, what="position 0")
+
+
+def pin_constant_values(library):
+    """Every value row equal to the all-ones vector => out is exactly 1."""
+    d, rv = 16, 4
+    p = random_problem(11, B=2, Hkv=1, G=3, d=d, nb=7, rk=4, rv=rv, w=5)
+    rng = np.random.default_rng(5)
+    basis = np.concatenate([np.ones((d, 1)) / math.sqrt(d), rng.standard_normal((d, rv - 1))], 1)
+    uv, rm = np.linalg.qr(basis)
+    uv = uv * np.sign(np.diag(rm))
+    cv = np.zeros_like(p["C_V"])
+    cv[..., 0] = math.sqrt(d)
+    out, _ = run_oracle(p, library, U_V=uv[None], C_V=cv, V_raw=np.ones_like(p["V_raw"]))
+    _close(out, np.ones_like(out), tol=1e-12, what="constant values")
+
+
+def pin_rebasing(library):
+    """(U_K R, C_K R) and (U_V S, C_V S) with orthogonal R, S leave out unchanged."""
+    p = random_problem(12, B=1, Hkv=2, G=2, d=16, nb=6, rk=5, rv=7, w=2)
+    out0, lse0 = run_oracle(p, library)
+    rng = np.random.default_rng(3)
+    R = _ortho(rng, 5, 5)
+    S = _ortho(rng, 7, 7)
+    out1, lse1 = run_oracle(p, library, U_K=p["U_K"] @ R, C_K=p["C_K"] @ R,
+                            U_V=p["U_V"] @ S, C_V=p["C_V"] @ S)
+    _close(out1, out0, what="re-based out")
+    _close(lse1, lse0, what="re-based lse")
+
+
+def pin_permutations(library):
+    p = random_problem(13, B=1, Hkv=1, G=4, d=16, nb=8, rk=4, rv=4, w=6)
+    out0, _ = run_oracle(p, library)
+    pb = np.random.default_rng(1).permutation(8)
+    pr = np.random.default_rng(2).permutation(6)
+    out1, _ = run_oracle(p, library, C_K=p["C_K"][:, :, pb], C_V=p["C_V"][:, :, pb],
+                         K_raw=p["K_raw"][:, :, pr], V_raw=p["V_raw"][:, :, pr])
+    _close(out1, out0, what="permuted rows")
+
+
+def pin_closed_forms(library):
+    # zero query: uniform weights, out = mean of all value rows, lse = log(n)
+    p = random_problem(14, B=1, Hkv=1, G=2, d=16, nb=5, rk=4, rv=6, w=3)
+    zq = np.zeros_like(p["q"])
+    out, lse = run_oracle(p, library, q=zq)
+    vals = np.concatenate([p["C_V"][0, 0] @ p["U_V"][0].T, p["V_raw"][0, 0]], axis=0)
+    _close(out[0], np.broadcast_to(vals.mean(axis=0), out[0].shape), what="zero query")
+    _close(lse, np.full_like(lse, math.log(8)), what="zero-query lse")
+    # one raw key: out is that value row, lse is its score
+    p1 = random_problem(15, B=1, Hkv=1, G=1, d=16, nb=0, rk=4, rv=4, w=1)
+    out, lse = run_oracle(p1, library)
+    _close(out[0, 0], p1["V_raw"][0, 0, 0], what="single key")
+    q_rot = rope_complex(p1["q"], p1["q_pos"][:, None], p1["theta"])
+    s = p1["scale"] * float(q_rot[0, 0] @ p1["K_raw"][0, 0, 0])
+    _close(lse[0, 0], s, what="single-key lse")
+    # one beacon and one raw key: weight of the beacon is sigmoid(s_b - s_r)
+    p2 = random_problem(16, B=1, Hkv=1, G=1, d=16, nb=1, rk=16, rv=16, w=1)
+    p2["U_K"] = np.eye(16)[None]
+    p2["U_V"] = np.eye(16)[None]
+    out, _ = run_oracle(p2, library)
+    q_rot = rope_complex(p2["q"], p2["q_pos"][:, None], p2["theta"])[0, 0]
+    sb = p2["scale"] * float(q_rot @ p2["C_K"][0, 0, 0])
+    sr = p2["scale"] * float(q_rot @ p2["K_raw"][0, 0, 0])
+    a = 1.0 / (1.0 + math.exp(-(sb - sr)))
+    _close(out[0, 0], a * p2["C_V"][0, 0, 0] + (1 - a) * p2["V_raw"][0, 0, 0], what="two keys")
+
+
+ALL_PINS = [
+    pin_reconstruct_identity,
+    pin_raw_only_rope_gqa,
+    pin_beacon_keys_unrotated,
+    pin_relative_position,
+    pin_position_zero,
+    pin_constant_values,
+    pin_rebasing,
+    pin_permutations,
+    pin_closed_forms,
+]

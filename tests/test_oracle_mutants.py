@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in copies of the oracle source and check that the
+pins catch each one.  Runs on the CPU only; the real oracle is untouched."""
+
+import pathlib
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "no_scale_on_beacon_scores": ("s[j] = p->scale * acc;", "s[j] = acc;"),
+    "rope_sign_flipped": ("qr[i] = x1 * c - x2 * sn;\n      qr[i + half] = x2 * c + x1 * sn;",
+                          "qr[i] = x1 * c + x2 * sn;\n      qr[i + half] = x2 * c - x1 * sn;"),
+    "rope_adjacent_pairs": (
+        "double x1 = widen(q, dt, q0 + i), x2 = widen(q, dt, q0 + i + half);\n"
+        "      qr[i] = x1 * c - x2 * sn;\n      qr[i + half] = x2 * c + x1 * sn;",
+        "double x1 = widen(q, dt, q0 + 2 * i), x2 = widen(q, dt, q0 + 2 * i + 1);\n"
+        "      qr[2 * i] = x1 * c - x2 * sn;\n      qr[2 * i + 1] = x2 * c + x1 * sn;"),
+    "rope_frequency_exponent": ("-2.0 * (double)i / (double)d", "-1.0 * (double)i / (double)d"),
+    "u_k_transposed": ("widen(U_K, dt, uk0 + (size_t)i * rk + k)",
+                       "widen(U_K, dt, uk0 + (size_t)k * d + i)"),
+    "u_v_transposed": ("widen(U_V, dt, uv0 + (size_t)i * rv + k)",
+                       "widen(U_V, dt, uv0 + (size_t)k * d + i)"),
+    "beacon_only_normaliser": ("      l += s[j];", "      if (j < (size_t)nb || nb == 0) l += s[j];"),
+    "gqa_strided_mapping": ("const int hq = h * G + g;", "const int hq = g * p->num_kv_heads + h;"),
+    "lse_without_max": ("lse[(size_t)b * p->num_q_heads + hq] = m + log(l);",
+                        "lse[(size_t)b * p->num_q_heads + hq] = log(l);"),
+    "raw_value_row_shift": ("oraw[i] += s[nb + t] * widen(V_raw",
+                            "oraw[i] += s[nb + (t + 1) % w] * widen(V_raw"),
+    "raw_values_dropped": ("out[q0 + i] = acc + oraw[i];", "out[q0 + i] = acc;"),
+    "no_scale_on_raw_scores": ("s[nb + t] = p->scale * acc;", "s[nb + t] = acc;"),
+}
+
+
+_RUNNER = """
+import sys
+sys.path[:0] = [{root!r}, {tests!r}]
+from oracle_pins import ALL_PINS
+failed = []
+for pin in ALL_PINS:
+    try:
+        pin({lib!r})
+    except (AssertionError, ValueError, FloatingPointError):
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path: pathlib.Path):
+    src = oracle.SOURCE.read_text()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.build(source=mutant_src, target=tmp_path / "libmutant.so")
+    here = pathlib.Path(__file__).resolve().parent
+    code = _RUNNER.format(root=str(here.parent), tests=str(here), lib=str(lib))
+    # A mutant that dies on a signal (a planted index error) counts as caught;
+    # any other non-zero exit is a broken harness and fails the test.
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         timeout=300)
+    if res.returncode < 0:
+        return
+    assert res.returncode == 0, res.stderr[-3000:]
+    line = [x for x in res.stdout.splitlines() if x.startswith("FAILED_PINS")][-1]
+    assert line.split(" ", 1)[1].strip(), f"mutant {name} passed every pin"
