@@ -1,0 +1,182 @@
+/*
+ * slimkv.h -- C ABI of libslimkv.so: SlimKV reconstruction-free latent
+ * decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Can SlimKV compress KV cache jointly across tokens
+ * and features", section "Latent-space attention removes the rebuild step";
+ * also the abstract on page "SlimKV: Joint Token-Feature KV Cache
+ * Compression with Reconstruction-Free Beacon Attention"):
+ *
+ *   A decode step attends over a cache compressed along tokens and
+ *   features.  Older context lives in N_b beacon rows held as low-rank
+ *   latents C_K (rank r_K) and C_V (rank r_V); their keys are trained
+ *   without rotary position, so they are stored and used unrotated.  The W
+ *   most recent tokens stay as raw rows K_raw, V_raw at the full head
+ *   dimension d, their keys rotated at their own positions.  The query is
+ *   always rotated.  After grouped-query grouping, each query head h_q
+ *   (KV head h = h_q / G, G = H_q / H_kv) is projected into its KV head's
+ *   latent key space, (q' U_K), scored against C_K and, at full width,
+ *   against K_raw, with one softmax over all N_b + W scores.  Beacon values
+ *   are summed in latent form, (A C_V), and lifted once by U_V.  Beacon keys
+ *   are never rebuilt at full dimension.
+ *
+ *   Per query head, with q' = RoPE(q, q_pos) (rotate-half pairs (i, i+d/2),
+ *   angle q_pos * theta^(-2i/d)):
+ *     s_j       = scale * (U_K^T q') . C_K[j]        j < N_b
+ *     s_{N_b+t} = scale * q' . K_raw[t]              t < W
+ *     a         = softmax(s)
+ *     out       = U_V (sum_j a_j C_V[j]) + sum_t a_{N_b+t} V_raw[t]
+ *     lse       = log(sum_j exp(s_j))                (natural log)
+ *
+ * Memory and threading rules common to every entry point:
+ *   - Tensor arguments are DEVICE pointers to contiguous row-major arrays
+ *     in the layouts listed below, 16-byte aligned.  The problem struct is
+ *     host memory.
+ *   - The caller owns every buffer; the library never allocates, frees or
+ *     synchronises, and keeps no state between calls.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Buffers must stay valid until the stream has run the call.
+ *   - Inputs are read only.  out, lse and the workspace must not overlap
+ *     any input or each other.
+ *   - Every argument check happens before any HIP call.  On error nothing
+ *     is launched, outputs are untouched, and a status is returned; the
+ *     library never aborts or throws across this ABI.  slimkv_last_error()
+ *     then describes the failed check (per calling thread).
+ *   - The workspace is scratch of slimkv_workspace_bytes() bytes.  It must
+ *     be zero-filled once before its first use; each completed call leaves
+ *     it fit for the next (one workspace per stream: two calls that share a
+ *     workspace must be ordered on one stream).
+ *   - bf16 means the upper 16 bits of an IEEE-754 binary32 (round to
+ *     nearest even is the caller's business).
+ */
+#ifndef SLIMKV_H
+#define SLIMKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SLIMKV_ABI_VERSION 1
+
+typedef enum slimkv_status {
+  SLIMKV_OK = 0,
+  SLIMKV_ERR_NULL = 1,        /* a required pointer is NULL                 */
+  SLIMKV_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes         */
+  SLIMKV_ERR_UNSUPPORTED = 3, /* valid, but outside what the kernels cover  */
+  SLIMKV_ERR_WORKSPACE = 4,   /* workspace smaller than required            */
+  SLIMKV_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned    */
+  SLIMKV_ERR_ALIAS = 6,       /* an output overlaps an input or another one */
+  SLIMKV_ERR_HIP = 7          /* a HIP launch failed                        */
+} slimkv_status;
+
+typedef enum slimkv_dtype {
+  SLIMKV_FP32 = 0, /* IEEE binary32 */
+  SLIMKV_BF16 = 1  /* bfloat16      */
+} slimkv_dtype;
+
+typedef enum slimkv_op {
+  SLIMKV_OP_LATENT = 0,      /* slimkv_decode_attn      */
+  SLIMKV_OP_RECONSTRUCT = 1, /* slimkv_reconstruct_attn */
+  SLIMKV_OP_FULL_KV = 2      /* full_kv_attn            */
+} slimkv_op;
+
+/* Shape of one layer's call (56 bytes, no implicit padding). */
+typedef struct slimkv_problem {
+  int32_t batch;        /* B >= 1                                            */
+  int32_t num_q_heads;  /* H_q, a multiple of H_kv; G = H_q / H_kv <= 8      */
+  int32_t num_kv_heads; /* H_kv >= 1                                         */
+  int32_t head_dim;     /* d; must be 128                                    */
+  int32_t num_beacons;  /* N_b >= 0 beacon rows per (b, kv head)             */
+  int32_t rank_k;       /* r_K: multiple of 16 in [16, 128] when N_b > 0     */
+  int32_t rank_v;       /* r_V: multiple of 16 in [16, 128] when N_b > 0     */
+  int32_t raw_window;   /* W >= 0 raw rows per (b, kv head); N_b + W >= 1    */
+  float scale;          /* softmax scale, finite and > 0 (e.g. 1/sqrt(d))   */
+  int32_t dtype;        /* slimkv_dtype of q, U_K, U_V, C_K, C_V, K, V       */
+  double rope_theta;    /* rotary base, finite and > 1                       */
+  int32_t num_splits;   /* 0: library picks; > 0: row chunks per segment of
+                           each (b, kv head), clipped to what the rows allow */
+  int32_t reserved;     /* must be 0                                         */
+} slimkv_problem;
+
+/*
+ * Workspace bytes the given op needs for this problem, or 0 if the problem
+ * is invalid (the entry point would return an error; slimkv_last_error()
+ * says why).  Pure host arithmetic: makes no HIP call.
+ */
+size_t slimkv_workspace_bytes(const slimkv_problem* problem, slimkv_op op);
+
+/*
+ * slimkv_decode_attn -- latent-space decode attention (the method itself).
+ *
+ *   q      [B, H_q, d]            decode query, before rotation
+ *   q_pos  [B]          int32     absolute position of each decode query
+ *   U_K    [H_kv, d, r_K]         beacon key basis of this layer
+ *   U_V    [H_kv, d, r_V]         beacon value basis of this layer
+ *   C_K    [B, H_kv, N_b, r_K]    latent beacon keys (no rotation)
+ *   C_V    [B, H_kv, N_b, r_V]    latent beacon values
+ *   K_raw  [B, H_kv, W, d]        raw keys, already rotated at their positions
+ *   V_raw  [B, H_kv, W, d]        raw values
+ *   out    [B, H_q, d]    fp32    attention output
+ *   lse    [B, H_q]       fp32    log-sum-exp of the scaled scores, or NULL
+ *
+ * U_K, U_V, C_K, C_V may be NULL when N_b == 0; K_raw, V_raw may be NULL
+ * when W == 0.
+ */
+slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q,
+                                 const int32_t* q_pos, const void* U_K,
+                                 const void* U_V, const void* C_K,
+                                 const void* C_V, const void* K_raw,
+                                 const void* V_raw, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * slimkv_reconstruct_attn -- comparison path: the decode step of the
+ * reconstruction-based variant timed against SlimKV on the same page
+ * (section "Speedups are real, but memory is set by the ratio"): beacon keys
+ * and values are first rebuilt at full dimension, K_b = C_K U_K^T and
+ * V_b = C_V U_V^T, written to the workspace in the problem dtype, and then
+ * attended together with the raw rows by ordinary attention.  The rebuilt
+ * beacon keys get no rotation here, so in exact arithmetic the result
+ * equals slimkv_decode_attn's; it differs only by the rounding of K_b, V_b
+ * to the storage dtype.  Same arguments and layouts as slimkv_decode_attn.
+ */
+slimkv_status slimkv_reconstruct_attn(const slimkv_problem* problem,
+                                      const void* q, const int32_t* q_pos,
+                                      const void* U_K, const void* U_V,
+                                      const void* C_K, const void* C_V,
+                                      const void* K_raw, const void* V_raw,
+                                      float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * full_kv_attn -- comparison path: uncompressed grouped-query decode
+ * attention over all T cached tokens (the "Full KV" baseline of the same
+ * section).  The problem must have num_beacons == 0 and raw_window == T.
+ *
+ *   q [B, H_q, d], q_pos [B] int32 as above;
+ *   K [B, H_kv, T, d] keys already rotated at their positions; V [B, H_kv, T, d];
+ *   out [B, H_q, d] fp32; lse [B, H_q] fp32 or NULL.
+ */
+slimkv_status full_kv_attn(const slimkv_problem* problem, const void* q,
+                           const int32_t* q_pos, const void* K, const void* V,
+                           float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* slimkv_status_string(slimkv_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* slimkv_last_error(void);
+
+/* SLIMKV_ABI_VERSION of the loaded library. */
+int32_t slimkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLIMKV_H */

@@ -1,0 +1,14 @@
+"""SlimKV reconstruction-free latent decode attention for AMD MI355X (gfx950).
+
+The work happens in ``libslimkv.so`` (hand-written HIP kernels behind the C
+ABI in include/slimkv.h).  This package holds its sources (csrc/), the build
+script and a thin ctypes binding with the C names, plus small helpers that
+allocate outputs and workspaces with torch.
+"""
+
+from .binding import (SLIMKV_BF16, SLIMKV_FP32, SLIMKV_OP_FULL_KV,  # noqa: F401
+                      SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn,
+                      load_library, make_problem, slimkv_abi_version, slimkv_decode_attn,
+                      slimkv_last_error, slimkv_problem, slimkv_reconstruct_attn,
+                      slimkv_status_string, slimkv_workspace_bytes)
+from .helpers import alloc_outputs, alloc_workspace, problem_from_tensors  # noqa: F401

@@ -1,0 +1,168 @@
+"""ctypes binding of libslimkv.so, with the C ABI's names.
+
+Argument marshalling only: tensors are torch tensors in device memory, whose
+pointers and the current HIP stream are handed to the library; every step of
+the attention runs in the library's HIP kernels.  There is no fallback: if
+the library is missing, loading fails with an error that says how to build
+it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+LIBRARY = pathlib.Path(__file__).resolve().parent / "libslimkv.so"
+
+SLIMKV_FP32, SLIMKV_BF16 = 0, 1
+SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV = 0, 1, 2
+STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
+                3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
+                6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
+
+EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_reconstruct_attn",
+           "full_kv_attn", "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
+
+
+class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
+    """Mirror of ``slimkv_problem`` in include/slimkv.h (56 bytes)."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_beacons", ctypes.c_int32),
+        ("rank_k", ctypes.c_int32),
+        ("rank_v", ctypes.c_int32),
+        ("raw_window", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+        ("num_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(slimkv_problem) == 56
+
+
+class SlimKVError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
+    """Load libslimkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = pathlib.Path(path) if path else LIBRARY
+    if not p.exists():
+        raise RuntimeError(f"{p} is missing: build it with "
+                           "`python -m latent_decode_attention_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    prob = ctypes.POINTER(slimkv_problem)
+    lib.slimkv_workspace_bytes.argtypes = [prob, ctypes.c_int]
+    lib.slimkv_workspace_bytes.restype = sz
+    lib.slimkv_decode_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
+    lib.slimkv_decode_attn.restype = ctypes.c_int
+    lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
+    lib.slimkv_reconstruct_attn.restype = ctypes.c_int
+    lib.full_kv_attn.argtypes = [prob] + [vp] * 6 + [vp, sz, vp]
+    lib.full_kv_attn.restype = ctypes.c_int
+    lib.slimkv_status_string.argtypes = [ctypes.c_int]
+    lib.slimkv_status_string.restype = ctypes.c_char_p
+    lib.slimkv_last_error.argtypes = []
+    lib.slimkv_last_error.restype = ctypes.c_char_p
+    lib.slimkv_abi_version.argtypes = []
+    lib.slimkv_abi_version.restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_problem(*, batch, num_q_heads, num_kv_heads, num_beacons, rank_k, rank_v, raw_window,
+                 scale, rope_theta, dtype, head_dim=128, num_splits=0) -> slimkv_problem:
+    dt = {"fp32": SLIMKV_FP32, "bf16": SLIMKV_BF16, torch.float32: SLIMKV_FP32,
+          torch.bfloat16: SLIMKV_BF16}.get(dtype, dtype)
+    return slimkv_problem(batch, num_q_heads, num_kv_heads, head_dim, num_beacons, rank_k, rank_v,
+                          raw_window, scale, dt, rope_theta, num_splits, 0)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor or None, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise TypeError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(lib, status: int) -> None:
+    if status != 0:
+        raise SlimKVError(status, lib.slimkv_last_error().decode())
+
+
+def slimkv_workspace_bytes(problem: slimkv_problem, op: int) -> int:
+    lib = load_library()
+    n = lib.slimkv_workspace_bytes(ctypes.byref(problem), op)
+    if n == 0:
+        raise SlimKVError(2, lib.slimkv_last_error().decode())
+    return int(n)
+
+
+def slimkv_decode_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse, workspace,
+                       stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,
+                            workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_reconstruct_attn(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def full_kv_attn(problem, q, q_pos, K, V, out, lse, workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.full_kv_attn(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(K), _ptr(V), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_status_string(status: int) -> str:
+    return load_library().slimkv_status_string(status).decode()
+
+
+def slimkv_last_error() -> str:
+    return load_library().slimkv_last_error().decode()
+
+
+def slimkv_abi_version() -> int:
+    return int(load_library().slimkv_abi_version())

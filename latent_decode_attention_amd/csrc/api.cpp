@@ -1,0 +1,399 @@
+// api.cpp -- the C ABI declared in include/slimkv.h: argument checks, the
+// split plan, workspace layout and the launch sequence of each entry point.
+//
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing, touches no output and works on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "internal.h"
+#include "slimkv.h"
+
+namespace slimkv {
+namespace {
+
+thread_local std::string g_last_error;
+
+slimkv_status fail(slimkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;    // rows per unit and segment
+constexpr int64_t kMaxUnits = int64_t(1) << 20;   // batch * kv heads
+constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
+constexpr int kTargetBlocks = 2048;               // sweep workgroups to aim for
+constexpr int64_t kMinChunkBytes = 32 << 10;
+constexpr int64_t kMaxChunkBytes = 512 << 10;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  SweepArgs sweep;
+  int64_t units;
+  int dtype;
+  int elem;
+  size_t off_q_rot, off_q_lat, off_ml, off_acc, off_kb, off_vb, total;
+};
+
+bool rank_ok(int r) { return r >= 16 && r <= kHeadDim && r % 16 == 0; }
+
+// Shape checks shared by every op.  For full_kv_attn num_beacons must be 0.
+slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
+  if (!p) return fail(SLIMKV_ERR_NULL, "problem is NULL");
+  if (op != SLIMKV_OP_LATENT && op != SLIMKV_OP_RECONSTRUCT && op != SLIMKV_OP_FULL_KV)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "unknown op %d", (int)op);
+  if (p->reserved != 0) return fail(SLIMKV_ERR_SHAPE, "reserved field must be 0");
+  if (p->dtype != SLIMKV_FP32 && p->dtype != SLIMKV_BF16)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p->dtype);
+  if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
+    return fail(SLIMKV_ERR_SHAPE, "batch, num_q_heads and num_kv_heads must be >= 1");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(SLIMKV_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads / p->num_kv_heads > kMaxGroup)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "group size %d exceeds %d",
+                p->num_q_heads / p->num_kv_heads, kMaxGroup);
+  if ((int64_t)p->batch * p->num_kv_heads > kMaxUnits)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "batch * num_kv_heads exceeds %lld", (long long)kMaxUnits);
+  if (p->head_dim != kHeadDim)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "head_dim %d is not %d", p->head_dim, kHeadDim);
+  if (p->num_beacons < 0 || p->raw_window < 0)
+    return fail(SLIMKV_ERR_SHAPE, "num_beacons and raw_window must be >= 0");
+  if ((int64_t)p->num_beacons + p->raw_window < 1)
+    return fail(SLIMKV_ERR_SHAPE, "num_beacons + raw_window must be >= 1");
+  if (p->num_beacons > kMaxRows || p->raw_window > kMaxRows)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "more than %lld rows per unit", (long long)kMaxRows);
+  if (op == SLIMKV_OP_FULL_KV && p->num_beacons != 0)
+    return fail(SLIMKV_ERR_SHAPE, "full_kv_attn needs num_beacons == 0 (raw_window is T)");
+  if (p->num_beacons > 0 && (!rank_ok(p->rank_k) || !rank_ok(p->rank_v)))
+    return fail(SLIMKV_ERR_UNSUPPORTED,
+                "rank_k %d / rank_v %d: each must be a multiple of 16 in [16, %d]", p->rank_k,
+                p->rank_v, kHeadDim);
+  if (!(p->scale > 0.0f) || !isfinite(p->scale))
+    return fail(SLIMKV_ERR_SHAPE, "scale must be finite and > 0");
+  if (!(p->rope_theta > 1.0) || !isfinite(p->rope_theta))
+    return fail(SLIMKV_ERR_SHAPE, "rope_theta must be finite and > 1");
+  if (p->num_splits < 0) return fail(SLIMKV_ERR_SHAPE, "num_splits must be >= 0");
+  return SLIMKV_OK;
+}
+
+// Chunking of one segment: enough row chunks to fill the GPU, each a whole
+// number of tiles, none empty.
+void plan_segment(Segment& sg, int dtype, int64_t units, int64_t chunk_bytes, int forced) {
+  const int tr = tile_rows(dtype, sg.rk, sg.rv);
+  const int64_t max_chunks = std::min<int64_t>(ceil_div(sg.rows, tr), kMaxSplits);
+  int64_t want;
+  if (forced > 0) {
+    want = forced;
+  } else {
+    const int64_t bytes = (int64_t)sg.rows * (sg.rk + sg.rv) * (dtype == 0 ? 4 : 2);
+    want = ceil_div(bytes, chunk_bytes);
+  }
+  want = std::max<int64_t>(1, std::min(want, max_chunks));
+  int64_t chunk = ceil_div(ceil_div(sg.rows, want), tr) * tr;
+  sg.chunk_rows = (int32_t)chunk;
+  sg.splits = (int32_t)ceil_div(sg.rows, chunk);
+  (void)units;
+}
+
+slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
+  slimkv_status st = check_problem(p, op);
+  if (st != SLIMKV_OK) return st;
+  memset(&pl, 0, sizeof pl);
+  pl.dtype = p->dtype;
+  pl.elem = p->dtype == SLIMKV_FP32 ? 4 : 2;
+  pl.units = (int64_t)p->batch * p->num_kv_heads;
+  SweepArgs& a = pl.sweep;
+  a.batch = p->batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+
+  int ns = 0;
+  if (p->num_beacons > 0) {
+    Segment& s = a.seg[ns++];
+    s.rows = p->num_beacons;
+    if (op == SLIMKV_OP_LATENT) {
+      s.kind = kSegLatent;
+      s.rk = p->rank_k;
+      s.rv = p->rank_v;
+    } else {
+      s.kind = kSegFull;
+      s.rk = s.rv = kHeadDim;
+    }
+  }
+  if (p->raw_window > 0) {
+    Segment& s = a.seg[ns++];
+    s.kind = kSegFull;
+    s.rows = p->raw_window;
+    s.rk = s.rv = kHeadDim;
+  }
+  a.nseg = ns;
+
+  int64_t unit_bytes = 0;
+  for (int i = 0; i < ns; ++i) unit_bytes += (int64_t)a.seg[i].rows * (a.seg[i].rk + a.seg[i].rv) * pl.elem;
+  const int64_t total_bytes = unit_bytes * pl.units;
+  const int64_t chunk_bytes =
+      std::min(kMaxChunkBytes, std::max(kMinChunkBytes, ceil_div(total_bytes, kTargetBlocks)));
+  for (int i = 0; i < ns; ++i) plan_segment(a.seg[i], pl.dtype, pl.units, chunk_bytes, p->num_splits);
+  a.splits_total = a.seg[0].splits + (ns > 1 ? a.seg[1].splits : 0);
+  if (pl.units * a.splits_total > (int64_t)INT32_MAX)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
+
+  // workspace layout
+  const int64_t Hq = p->num_q_heads, B = p->batch, G = a.group;
+  size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);  // reserved control words
+  pl.off_q_rot = off;
+  off = round_up(off + (size_t)(B * Hq * kHeadDim) * sizeof(float), kAlign);
+  pl.off_q_lat = off;
+  if (op == SLIMKV_OP_LATENT && p->num_beacons > 0)
+    off = round_up(off + (size_t)(B * Hq * p->rank_k) * sizeof(float), kAlign);
+  pl.off_ml = off;
+  off = round_up(off + (size_t)(pl.units * a.splits_total * G * 2) * sizeof(float), kAlign);
+  pl.off_acc = off;
+  off = round_up(off + (size_t)(pl.units * a.splits_total * G * kHeadDim) * sizeof(float), kAlign);
+  pl.off_kb = pl.off_vb = off;
+  if (op == SLIMKV_OP_RECONSTRUCT && p->num_beacons > 0) {
+    const size_t rebuilt = (size_t)pl.units * p->num_beacons * kHeadDim * pl.elem;
+    off = round_up(off + rebuilt, kAlign);
+    pl.off_vb = off;
+    off = round_up(off + rebuilt, kAlign);
+  }
+  pl.total = off;
+  return SLIMKV_OK;
+}
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& x, const Range& y) {
+  if (!x.p || !y.p || !x.bytes || !y.bytes) return false;
+  const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + x.bytes;
+  const uintptr_t b0 = (uintptr_t)y.p, b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Pointer checks: presence, alignment, and outputs not overlapping inputs
+// or each other.
+slimkv_status check_pointers(const Range* in, int n_in, const Range* req, int n_req,
+                             const Range* outs, int n_out, int align_req) {
+  for (int i = 0; i < n_req; ++i)
+    if (!req[i].p) return fail(SLIMKV_ERR_NULL, "%s is NULL", req[i].name);
+  for (int i = 0; i < n_in; ++i)
+    if (in[i].p && ((uintptr_t)in[i].p % (in[i].bytes == 0 ? 1 : (uintptr_t)align_req)) != 0)
+      return fail(SLIMKV_ERR_ALIGN, "%s is not %d-byte aligned", in[i].name, align_req);
+  for (int i = 0; i < n_out; ++i) {
+    if (outs[i].p && (uintptr_t)outs[i].p % 4 != 0)
+      return fail(SLIMKV_ERR_ALIGN, "%s is not 4-byte aligned", outs[i].name);
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], in[j]))
+        return fail(SLIMKV_ERR_ALIAS, "%s overlaps %s", outs[i].name, in[j].name);
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SLIMKV_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return SLIMKV_OK;
+}
+
+slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const int32_t* q_pos,
+                  const void* U_K, const void* U_V, const void* C_K, const void* C_V,
+                  const void* K_raw, const void* V_raw, float* out, float* lse, void* ws,
+                  size_t ws_bytes, void* stream) {
+  Plan pl;
+  slimkv_status st = make_plan(p, op, pl);
+  if (st != SLIMKV_OK) return st;
+  const size_t e = (size_t)pl.elem;
+  const size_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = kHeadDim;
+  const size_t nb = p->num_beacons, w = p->raw_window;
+  const bool beacons = nb > 0, raw = w > 0;
+  const size_t rk = beacons ? p->rank_k : 0, rv = beacons ? p->rank_v : 0;
+
+  Range in[8] = {
+      {q, B * Hq * d * e, "q"},
+      {q_pos, B * sizeof(int32_t), "q_pos"},
+      {beacons ? U_K : nullptr, Hkv * d * rk * e, "U_K"},
+      {beacons ? U_V : nullptr, Hkv * d * rv * e, "U_V"},
+      {beacons ? C_K : nullptr, B * Hkv * nb * rk * e, "C_K"},
+      {beacons ? C_V : nullptr, B * Hkv * nb * rv * e, "C_V"},
+      {raw ? K_raw : nullptr, B * Hkv * w * d * e, op == SLIMKV_OP_FULL_KV ? "K" : "K_raw"},
+      {raw ? V_raw : nullptr, B * Hkv * w * d * e, op == SLIMKV_OP_FULL_KV ? "V" : "V_raw"},
+  };
+  Range req[9];
+  int n_req = 0;
+  req[n_req++] = in[0];
+  req[n_req++] = in[1];
+  if (beacons)
+    for (int i = 2; i < 6; ++i) req[n_req++] = in[i];
+  if (raw) {
+    req[n_req++] = in[6];
+    req[n_req++] = in[7];
+  }
+  req[n_req++] = Range{out, 1, "out"};
+  Range outs[3] = {{out, B * Hq * d * sizeof(float), "out"},
+                   {lse, lse ? B * Hq * sizeof(float) : 0, "lse"},
+                   {ws, pl.total, "workspace"}};
+  // q_pos only needs int32 alignment; everything read as 16-byte vectors needs 16
+  Range in16[8];
+  int n16 = 0;
+  for (int i = 0; i < 8; ++i)
+    if (i != 1) in16[n16++] = in[i];
+  if ((uintptr_t)q_pos % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "q_pos is not 4-byte aligned");
+  st = check_pointers(in16, n16, req, n_req, outs, 3, 16);
+  if (st != SLIMKV_OK) return st;
+  if (overlap(outs[0], in[1]) || overlap(outs[1], in[1]) || overlap(outs[2], in[1]))
+    return fail(SLIMKV_ERR_ALIAS, "an output overlaps q_pos");
+  if (!ws) return fail(SLIMKV_ERR_NULL, "workspace is NULL");
+  if ((uintptr_t)ws % 16 != 0) return fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < pl.total)
+    return fail(SLIMKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+
+  // ---- all checks passed: launch
+  char* wsb = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SweepArgs& a = pl.sweep;
+  a.q_rot = reinterpret_cast<float*>(wsb + pl.off_q_rot);
+  a.q_lat = reinterpret_cast<float*>(wsb + pl.off_q_lat);
+  a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
+  a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
+
+  PrologueArgs pa{};
+  pa.q = q;
+  pa.q_pos = q_pos;
+  pa.U_K = U_K;
+  pa.batch = p->batch;
+  pa.num_q_heads = p->num_q_heads;
+  pa.num_kv_heads = p->num_kv_heads;
+  pa.group = a.group;
+  pa.rank_k = (int32_t)rk;
+  pa.rope_theta = p->rope_theta;
+  pa.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
+  pa.q_rot = const_cast<float*>(a.q_rot);
+  pa.q_lat = (op == SLIMKV_OP_LATENT && beacons) ? const_cast<float*>(a.q_lat) : nullptr;
+
+  int si = 0;
+  if (beacons) {
+    Segment& sg = a.seg[si++];
+    if (op == SLIMKV_OP_LATENT) {
+      sg.K = C_K;
+      sg.V = C_V;
+    } else {
+      sg.K = wsb + pl.off_kb;
+      sg.V = wsb + pl.off_vb;
+    }
+  }
+  if (raw) {
+    Segment& sg = a.seg[si++];
+    sg.K = K_raw;
+    sg.V = V_raw;
+  }
+
+  CombineArgs ca{};
+  ca.part_ml = a.part_ml;
+  ca.part_acc = a.part_acc;
+  ca.U_V = (op == SLIMKV_OP_LATENT && beacons) ? U_V : nullptr;
+  ca.batch = p->batch;
+  ca.num_q_heads = p->num_q_heads;
+  ca.num_kv_heads = p->num_kv_heads;
+  ca.group = a.group;
+  ca.rank_v = (op == SLIMKV_OP_LATENT && beacons) ? (int32_t)rv : 0;
+  ca.splits_total = a.splits_total;
+  ca.latent_splits = (op == SLIMKV_OP_LATENT && beacons) ? a.seg[0].splits : 0;
+  ca.out = out;
+  ca.lse = lse;
+
+  hipError_t err = launch_prologue(pa, pl.dtype, s);
+  if (err == hipSuccess && op == SLIMKV_OP_RECONSTRUCT && beacons) {
+    RebuildArgs rb{};
+    rb.batch = p->batch;
+    rb.num_kv_heads = p->num_kv_heads;
+    rb.num_beacons = p->num_beacons;
+    rb.C = C_K;
+    rb.U = U_K;
+    rb.dst = wsb + pl.off_kb;
+    rb.rank = (int32_t)rk;
+    err = launch_rebuild(rb, pl.dtype, s);
+    if (err == hipSuccess) {
+      rb.C = C_V;
+      rb.U = U_V;
+      rb.dst = wsb + pl.off_vb;
+      rb.rank = (int32_t)rv;
+      err = launch_rebuild(rb, pl.dtype, s);
+    }
+  }
+  if (err == hipSuccess) err = launch_sweep(a, pl.dtype, s);
+  if (err == hipSuccess) err = launch_combine(ca, pl.dtype, s);
+  if (err != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return SLIMKV_OK;
+}
+
+}  // namespace
+}  // namespace slimkv
+
+extern "C" {
+
+size_t slimkv_workspace_bytes(const slimkv_problem* problem, slimkv_op op) {
+  slimkv::Plan pl;
+  if (slimkv::make_plan(problem, op, pl) != SLIMKV_OK) return 0;
+  return pl.total;
+}
+
+slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q, const int32_t* q_pos,
+                                 const void* U_K, const void* U_V, const void* C_K, const void* C_V,
+                                 const void* K_raw, const void* V_raw, float* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return slimkv::run(problem, SLIMKV_OP_LATENT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
+                     lse, workspace, workspace_bytes, stream);
+}
+
+slimkv_status slimkv_reconstruct_attn(const slimkv_problem* problem, const void* q,
+                                      const int32_t* q_pos, const void* U_K, const void* U_V,
+                                      const void* C_K, const void* C_V, const void* K_raw,
+                                      const void* V_raw, float* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return slimkv::run(problem, SLIMKV_OP_RECONSTRUCT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                     out, lse, workspace, workspace_bytes, stream);
+}
+
+slimkv_status full_kv_attn(const slimkv_problem* problem, const void* q, const int32_t* q_pos,
+                           const void* K, const void* V, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return slimkv::run(problem, SLIMKV_OP_FULL_KV, q, q_pos, nullptr, nullptr, nullptr, nullptr, K,
+                     V, out, lse, workspace, workspace_bytes, stream);
+}
+
+const char* slimkv_status_string(slimkv_status status) {
+  switch (status) {
+    case SLIMKV_OK: return "ok";
+    case SLIMKV_ERR_NULL: return "a required pointer is NULL";
+    case SLIMKV_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case SLIMKV_ERR_UNSUPPORTED: return "valid but unsupported problem";
+    case SLIMKV_ERR_WORKSPACE: return "workspace too small";
+    case SLIMKV_ERR_ALIGN: return "misaligned device pointer";
+    case SLIMKV_ERR_ALIAS: return "an output overlaps an input or another output";
+    case SLIMKV_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* slimkv_last_error(void) { return slimkv::g_last_error.c_str(); }
+
+int32_t slimkv_abi_version(void) { return SLIMKV_ABI_VERSION; }
+
+}  // extern "C"

@@ -92,7 +92,8 @@ class LayerInputs:
 
     workload: Workload
     layer: int
-    rank: int
+    rank_k: int
+    rank_v: int
     q: torch.Tensor
     q_pos: torch.Tensor
     U_K: torch.Tensor
@@ -119,16 +120,19 @@ class LayerInputs:
 
 
 def make_layer(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu",
-               num_beacons: int | None = None, raw_window: int | None = None) -> LayerInputs:
+               num_beacons: int | None = None, raw_window: int | None = None,
+               rank_v: int | None = None) -> LayerInputs:
     """Generate one layer of ``wl`` on ``device``.
 
     ``num_beacons`` / ``raw_window`` override the workload's values (tests
-    use this for ragged and degenerate shapes).  Raw rows always end at the
+    use this for ragged and degenerate shapes); ``rank_v`` gives the value
+    latents a rank other than the key latents'.  Raw rows always end at the
     decode position: they cover positions [T - W, T).
     """
     nb = wl.num_beacons if num_beacons is None else num_beacons
     w = wl.raw_window if raw_window is None else raw_window
     r = wl.ranks[layer]
+    rv = r if rank_v is None else rank_v
     d = wl.head_dim
     dt = _TORCH_DTYPE[wl.dtype]
 
@@ -137,11 +141,11 @@ def make_layer(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu"
     q_pos = torch.full((wl.batch,), wl.q_pos, dtype=torch.int32, device=device)
     uk = torch.stack([orthonormal_basis(d, r, _seed(base_seed, wl, layer, "U_K", h, r))
                       for h in range(wl.num_kv_heads)]).to(dt).to(device)
-    uv = torch.stack([orthonormal_basis(d, r, _seed(base_seed, wl, layer, "U_V", h, r))
+    uv = torch.stack([orthonormal_basis(d, rv, _seed(base_seed, wl, layer, "U_V", h, rv))
                       for h in range(wl.num_kv_heads)]).to(dt).to(device)
     ck = _gauss((wl.batch, wl.num_kv_heads, nb, r), _seed(base_seed, wl, layer, "C_K", nb, r),
                 wl.sigma, wl.dtype, device)
-    cv = _gauss((wl.batch, wl.num_kv_heads, nb, r), _seed(base_seed, wl, layer, "C_V", nb, r),
+    cv = _gauss((wl.batch, wl.num_kv_heads, nb, rv), _seed(base_seed, wl, layer, "C_V", nb, rv),
                 wl.sigma, wl.dtype, device)
     if w % TOKEN_BLOCK == 0 and wl.context % TOKEN_BLOCK == 0:
         kr = _tokens(wl, layer, "K_tok", base_seed, wl.context - w, w, device)
@@ -152,7 +156,7 @@ def make_layer(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu"
                     device)
         vr = _gauss(shape, _seed(base_seed, wl, layer, "V_tok", 1 << 30, w), wl.sigma, wl.dtype,
                     device)
-    return LayerInputs(wl, layer, r, q, q_pos, uk, uv, ck, cv, kr, vr)
+    return LayerInputs(wl, layer, r, rv, q, q_pos, uk, uv, ck, cv, kr, vr)
 
 
 def make_full_kv(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cpu"):

@@ -1,0 +1,149 @@
+"""Helpers for the GPU parity tests: run the HIP library and the fp64 oracle
+on the same seeded inputs and compare.
+
+Tolerances (floating point; nothing here decides an integer):
+  * bf16 caches, fp32 accumulation: max-abs <= 1e-2 and relative L2 <= 5e-3
+    over the call's whole output (or over the sampled units);
+  * fp32: relative L2 <= 1e-5;
+  * lse: |error| <= LSE_TOL[dtype] * max(1, |lse|).  The kernels score with
+    a two-term bf16 split of the fp32 query (about 2^-17 relative) against
+    exact storage keys, accumulate in fp32 and take exp2 in fp32, so score
+    errors stay near 1e-6 * |score| and the log-sum-exp inherits that.
+  * the reconstruction path rounds each rebuilt beacon key element to bf16
+    (relative 2^-9), which moves every beacon score by up to about
+    2^-8 * |score|; its lse tolerance is RECON_LSE_TOL * max(1, |lse|).
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import latent_decode_attention_amd as lda
+import oracle
+import synth
+
+TOL = {"fp32": dict(rel_l2=1e-5, max_abs=None), "bf16": dict(rel_l2=5e-3, max_abs=1e-2)}
+LSE_TOL = {"fp32": 1e-5, "bf16": 1e-4}
+RECON_LSE_TOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+def note(msg: str) -> None:
+    """Name the case before a GPU step, flushed, so a failing run says where."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_splits: int = 0,
+            device="cuda", with_lse: bool = True, full_k=None, full_v=None):
+    """Run one entry point on ``inp`` (moved to the GPU if needed)."""
+    wl = inp.workload
+    g = inp.to(device)
+    if op == lda.SLIMKV_OP_FULL_KV:
+        K, V = full_k.to(device), full_v.to(device)
+        prob = lda.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads,
+                                num_kv_heads=wl.num_kv_heads, num_beacons=0, rank_k=0, rank_v=0,
+                                raw_window=int(K.shape[2]), scale=wl.scale,
+                                rope_theta=wl.rope_theta, dtype=wl.dtype, num_splits=num_splits)
+    else:
+        prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                        rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                        scale=wl.scale, num_splits=num_splits)
+    out, lse = lda.alloc_outputs(prob, device)
+    ws = lda.alloc_workspace(prob, op, device)
+    if not with_lse:
+        lse = None
+    if op == lda.SLIMKV_OP_LATENT:
+        lda.slimkv_decode_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw, g.V_raw,
+                               out, lse, ws)
+    elif op == lda.SLIMKV_OP_RECONSTRUCT:
+        lda.slimkv_reconstruct_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw,
+                                    g.V_raw, out, lse, ws)
+    else:
+        lda.full_kv_attn(prob, g.q, g.q_pos, K, V, out, lse, ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), (None if lse is None else lse.double().cpu().numpy())
+
+
+def oracle_layer(inp: synth.LayerInputs, units=None, threads: int = 0):
+    """Oracle on the whole layer (inputs copied to the host), or on a list of
+    (b, kv head) units."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    nb, w = inp.num_beacons, inp.raw_window
+    return oracle.decode(st(inp.q), st(inp.q_pos), st(inp.U_K), st(inp.U_V),
+                         st(inp.C_K) if nb else None, st(inp.C_V) if nb else None,
+                         st(inp.K_raw) if w else None, st(inp.V_raw) if w else None,
+                         num_kv_heads=wl.num_kv_heads, scale=wl.scale, rope_theta=wl.rope_theta,
+                         units=units, threads=threads)
+
+
+def oracle_units(inp: synth.LayerInputs, units):
+    """Oracle on sampled units, copying only each unit's slices to the host.
+    Returns {(b, h): (out [G, d], lse [G])}."""
+    wl = inp.workload
+    res = {}
+    for b, h in units:
+        s = synth.unit_slices(inp, b, h)
+        nb, w = s["C_K"].shape[2], s["K_raw"].shape[2]
+        o, l = oracle.decode(s["q"], s["q_pos"], s["U_K"], s["U_V"], s["C_K"] if nb else None,
+                             s["C_V"] if nb else None, s["K_raw"] if w else None,
+                             s["V_raw"] if w else None, num_kv_heads=1, scale=wl.scale,
+                             rope_theta=wl.rope_theta)
+        res[(b, h)] = (o[0], l[0])
+    return res
+
+
+def oracle_full_kv_units(wl, q, q_pos, K, V, units):
+    """Oracle for uncompressed attention on sampled units (raw-only problem)."""
+    st = synth.to_numpy_storage
+    G = wl.group
+    res = {}
+    for b, h in units:
+        o, l = oracle.decode(st(q[b:b + 1, h * G:(h + 1) * G]), st(q_pos[b:b + 1]), None, None,
+                             None, None, st(K[b:b + 1, h:h + 1]), st(V[b:b + 1, h:h + 1]),
+                             num_kv_heads=1, scale=wl.scale, rope_theta=wl.rope_theta)
+        res[(b, h)] = (o[0], l[0])
+    return res
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = got - ref
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300))
+    return rel, float(np.max(np.abs(diff)))
+
+
+def assert_parity(got, ref, dtype: str, what: str = "", lse=None, lse_ref=None, lse_tol=None):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    rel, mx = errors(got, ref)
+    tol = TOL[dtype]
+    print(f"[parity] {what}: rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3e} > {tol['rel_l2']}"
+    if tol["max_abs"] is not None:
+        assert mx <= tol["max_abs"], f"{what}: max-abs {mx:.3e} > {tol['max_abs']}"
+    if lse is not None:
+        lerr = np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))
+        print(f"[parity] {what}: lse max scaled err={lerr.max():.3e}", flush=True)
+        tol_l = LSE_TOL[dtype] if lse_tol is None else lse_tol
+        assert lerr.max() <= tol_l, f"{what}: lse error {lerr.max():.3e} > {tol_l}"
+
+
+def sample_units(wl, n: int, seed: int):
+    rng = np.random.default_rng(seed)
+    all_units = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    idx = rng.choice(len(all_units), size=min(n, len(all_units)), replace=False)
+    picked = [all_units[i] for i in sorted(idx)]
+    # always include the first and last unit (address arithmetic at both ends)
+    for u in (all_units[0], all_units[-1]):
+        if u not in picked:
+            picked.append(u)
+    return picked
+
+
+def gather_units(out, lse, wl, units):
+    G = wl.group
+    got = np.stack([out[b, h * G:(h + 1) * G] for b, h in units])
+    got_lse = np.stack([lse[b, h * G:(h + 1) * G] for b, h in units])
+    return got, got_lse

@@ -1,0 +1,172 @@
+"""The C ABI without a GPU: exported symbols, struct layout, and every
+argument check (they all run before any HIP call, so they are safe here)."""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+import latent_decode_attention_amd as lda
+from latent_decode_attention_amd import binding
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "slimkv.h"
+OK, NULL, SHAPE, UNSUP, WS, ALIGN, ALIAS = 0, 1, 2, 3, 4, 5, 6
+
+
+def header_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lda.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert set(names) == set(binding.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_problem_struct_layout():
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct slimkv_problem \{(.*?)\} slimkv_problem;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(int32_t|float|double)\s+(\w+);", body, re.M)
+    assert [f for _, f in fields] == [f for f, _ in binding.slimkv_problem._fields_]
+    assert ctypes.sizeof(binding.slimkv_problem) == 56
+    assert binding.slimkv_problem.rope_theta.offset == 40
+
+
+def test_version_and_status_strings(lib):
+    assert lda.slimkv_abi_version() == 1
+    for code in range(8):
+        assert lda.slimkv_status_string(code)
+    assert lda.slimkv_status_string(99) == "unknown status"
+
+
+def _problem(**over):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, num_beacons=64, rank_k=32, rank_v=32,
+                raw_window=32, scale=0.088, rope_theta=5e5, dtype="bf16")
+    base.update(over)
+    return lda.make_problem(**base)
+
+
+def _call(lib, prob, *, op=0, ptrs=None, ws_bytes=1 << 30):
+    """Call an entry point with fake device addresses (never dereferenced:
+    every case here fails validation before any HIP call)."""
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, out=0x5000000, lse=0x6000000,
+             ws=0x7000000)
+    p.update(ptrs or {})
+    v = {k: (None if x is None else ctypes.c_void_p(x)) for k, x in p.items()}
+    pp = ctypes.byref(prob) if prob is not None else None
+    if op == 2:
+        return lib.full_kv_attn(pp, v["q"], v["q_pos"], v["K_raw"], v["V_raw"], v["out"],
+                                v["lse"], v["ws"], ws_bytes, None)
+    fn = lib.slimkv_decode_attn if op == 0 else lib.slimkv_reconstruct_attn
+    return fn(pp, v["q"], v["q_pos"], v["U_K"], v["U_V"], v["C_K"], v["C_V"], v["K_raw"],
+              v["V_raw"], v["out"], v["lse"], v["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_q_heads=7), SHAPE),
+    (dict(num_q_heads=32, num_kv_heads=2), UNSUP),  # group 16 > 8
+    (dict(head_dim=64), UNSUP),
+    (dict(num_beacons=0, raw_window=0), SHAPE),
+    (dict(num_beacons=-1), SHAPE),
+    (dict(rank_k=40), UNSUP),
+    (dict(rank_v=144), UNSUP),
+    (dict(rank_k=0), UNSUP),
+    (dict(dtype=5), UNSUP),
+    (dict(scale=0.0), SHAPE),
+    (dict(scale=float("inf")), SHAPE),
+    (dict(rope_theta=1.0), SHAPE),
+    (dict(rope_theta=float("nan")), SHAPE),
+    (dict(batch=0), SHAPE),
+    (dict(num_splits=-3), SHAPE),
+    (dict(num_beacons=1 << 25), UNSUP),
+])
+def test_shape_errors(lib, over, status):
+    prob = _problem(**over)
+    assert _call(lib, prob) == status
+    assert lda.slimkv_last_error()
+    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) == 0
+
+
+def test_reserved_must_be_zero(lib):
+    prob = _problem()
+    prob.reserved = 1
+    assert _call(lib, prob) == SHAPE
+
+
+def test_null_problem(lib):
+    assert _call(lib, None) == NULL
+
+
+@pytest.mark.parametrize("name", ["q", "q_pos", "U_K", "U_V", "C_K", "C_V", "K_raw", "V_raw",
+                                  "out", "ws"])
+def test_null_pointers(lib, name):
+    assert _call(lib, _problem(), ptrs={name: None}) == NULL
+    assert name.replace("ws", "workspace") in lda.slimkv_last_error()
+
+
+def test_optional_pointers_follow_sizes(lib):
+    # no beacons: U/C may be NULL; no raw rows: K_raw/V_raw may be NULL.  The
+    # call then fails later, on the workspace size, not on a NULL pointer.
+    prob = _problem(num_beacons=0)
+    st = _call(lib, prob, ptrs=dict(U_K=None, U_V=None, C_K=None, C_V=None), ws_bytes=16)
+    assert st == WS
+    prob = _problem(raw_window=0)
+    assert _call(lib, prob, ptrs=dict(K_raw=None, V_raw=None), ws_bytes=16) == WS
+
+
+def test_workspace_too_small(lib):
+    prob = _problem()
+    need = lib.slimkv_workspace_bytes(ctypes.byref(prob), 0)
+    assert need > 0
+    assert _call(lib, prob, ws_bytes=need - 1) == WS
+    assert str(need) in lda.slimkv_last_error()
+
+
+@pytest.mark.parametrize("name", ["q", "U_K", "C_K", "V_raw", "ws"])
+def test_misaligned(lib, name):
+    base = {"q": 0x100000, "U_K": 0x300000, "C_K": 0x1000000, "V_raw": 0x4000000, "ws": 0x7000000}
+    assert _call(lib, _problem(), ptrs={name: base[name] + 8}) == ALIGN
+
+
+def test_misaligned_q_pos(lib):
+    assert _call(lib, _problem(), ptrs={"q_pos": 0x200002}) == ALIGN
+
+
+@pytest.mark.parametrize("ptrs", [
+    dict(out=0x1000000 + 64),   # out inside C_K
+    dict(lse=0x5000000 + 16),   # lse inside out
+    dict(ws=0x3000000),         # workspace on K_raw
+    dict(out=0x200000),         # out on q_pos
+])
+def test_aliasing(lib, ptrs):
+    assert _call(lib, _problem(), ptrs=ptrs) == ALIAS
+
+
+def test_full_kv_needs_no_beacons(lib):
+    assert _call(lib, _problem(num_beacons=64), op=2) == SHAPE
+    assert _call(lib, _problem(num_beacons=0), op=2, ws_bytes=16) == WS
+
+
+def test_workspace_bytes_by_op(lib):
+    prob = _problem()
+    lat = lib.slimkv_workspace_bytes(ctypes.byref(prob), 0)
+    rec = lib.slimkv_workspace_bytes(ctypes.byref(prob), 1)
+    # the reconstruction path also holds the rebuilt beacon keys and values
+    assert rec - lat >= 2 * 2 * 2 * 64 * 128 * 2 - 32 * 8 * 2 * 4
+    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 7) == 0
+    assert lib.slimkv_workspace_bytes(None, 0) == 0
+
+
+def test_split_override_changes_workspace(lib):
+    a = lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=1)), 0)
+    b = lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=4)), 0)
+    assert b > a
