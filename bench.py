@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark for libslimkv on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+                    [--no-cpu-baseline] [--no-compare]
+
+A step is one decode token's attention over every layer of the workload:
+for the default workload (Llama-3.1-8B shape, 128K context, 16x token
+compression, batch 16) that is 32 calls of slimkv_decode_attn, one per
+layer, each with its own latent rank.  All inputs are generated on the GPU
+before timing and stay resident in HBM.  The timed region is bracketed by
+device synchronisation and measured with events on the stream the library
+launches on.  Prints ONE JSON line.
+
+Reported beside the headline tokens/s:
+  * roofline of the sweep kernel (algorithmic cache bytes per launch over
+    its average launch time, against 8 TB/s);
+  * the comparison at 128K on one layer: latent path at 16x vs the
+    reconstruct-then-attend path on the same beacons and vs uncompressed
+    full-KV attention over all 131072 tokens;
+  * the fp64 CPU oracle timed on a bounded sample on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_call_bytes(wl, layer, elem):
+    """Algorithmic HBM bytes of one latent call: cache rows + bases + q + outputs."""
+    r = wl.ranks[layer]
+    units = wl.batch * wl.num_kv_heads
+    cache = units * (wl.num_beacons * 2 * r + 2 * wl.raw_window * wl.head_dim) * elem
+    bases = wl.num_kv_heads * wl.head_dim * 2 * r * elem
+    q = wl.batch * wl.num_q_heads * wl.head_dim * elem
+    out = wl.batch * wl.num_q_heads * (wl.head_dim + 1) * 4
+    return cache, cache + bases + q + out
+
+
+def attn_kernel_bytes(wl, layer, elem):
+    """Algorithmic bytes the attention kernel of one latent call moves: the
+    cache rows, U_V, and the fp32 out and lse."""
+    r = wl.ranks[layer]
+    units = wl.batch * wl.num_kv_heads
+    cache = units * (wl.num_beacons * 2 * r + 2 * wl.raw_window * wl.head_dim) * elem
+    return cache + wl.num_kv_heads * wl.head_dim * r * elem + \
+        wl.batch * wl.num_q_heads * (wl.head_dim + 1) * 4
+
+
+def time_calls(fn, iters, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the method's "
+              "hot path runs on one GPU's share; see DESIGN.md on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import latent_decode_attention_amd as lda
+    import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.get_workload(args.workload)
+    elem = wl.elem_bytes
+    log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, generating inputs on the GPU")
+    layers = [synth.make_layer(wl, layer, device=dev) for layer in range(wl.layers)]
+    probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                      rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                      scale=wl.scale) for x in layers]
+    ws_bytes = max(lda.slimkv_workspace_bytes(p, lda.SLIMKV_OP_LATENT) for p in probs)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    out, lse = lda.alloc_outputs(probs[0], dev)
+    torch.cuda.synchronize()
+
+    def step():
+        for p, x in zip(probs, layers):
+            lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw,
+                                   out, lse, ws)
+
+    log(f"warmup {args.warmup} steps, timing {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    tokens_per_s = wl.batch / (ms_step * 1e-3)
+    cache_step = sum(layer_call_bytes(wl, layer, elem)[0] for layer in range(wl.layers))
+    total_step = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
+    step_gbps = total_step / (ms_step * 1e-3) / 1e9
+    log(f"{ms_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, {step_gbps:.0f} GB/s "
+        f"(wall {wall:.2f}s)")
+
+    # attention kernel alone: events around each launch (library hook), same steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps * wl.layers)]
+    torch.cuda.synchronize()
+    k = 0
+    for _ in range(args.steps):
+        for p, x in zip(probs, layers):
+            lda.slimkv_set_kernel_events(*evs[k])
+            lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw,
+                                   out, lse, ws)
+            k += 1
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_us = 1e3 * sum(kern_ms) / len(kern_ms)
+    launches = wl.layers
+    kern_bytes = sum(attn_kernel_bytes(wl, layer, elem) for layer in range(wl.layers)) / launches
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
+    log(f"attention kernel: {kern_us:.1f} us average over {len(kern_ms)} launches, "
+        f"{achieved:.0f} GB/s")
+
+    result = {
+        "metric": "decode-attn tokens/s + HBM GB/s (% peak) at 128K, latent vs full-KV, 1 GPU",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded Gaussian caches at the model's shapes, generated on the GPU)",
+        "config": {
+            "workload": (f"{wl.name}: decode attention over {wl.layers} layers, batch "
+                         f"{wl.batch}, {wl.num_q_heads}/{wl.num_kv_heads} heads, d=128, "
+                         f"{wl.context} context as {wl.num_beacons} beacons (ranks "
+                         f"{min(wl.ranks)}-{max(wl.ranks)}, mean {sum(wl.ranks) / wl.layers:g}) "
+                         f"+ {wl.raw_window} raw tokens"),
+            "global_batch": wl.batch,
+            "seq_len": wl.context,
+            "layers": wl.layers,
+            "parallelism": "single GPU",
+        },
+        "hbm_gbps": round(step_gbps, 1),
+        "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "attention_kernel (one launch per layer call, after a small prologue kernel)",
+            "bytes_per_launch": int(kern_bytes),
+            "launch_us": round(kern_us, 2),
+            "launches_timed": len(kern_ms),
+        },
+    }
+
+    if not args.no_compare:
+        result["comparison"] = compare(lda, synth, torch, dev)
+
+    del ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s, synth)
+    print(json.dumps(result), flush=True)
+
+
+def compare(lda, synth, torch, dev):
+    """One 128K layer (B=16): latent at 16x vs reconstruct on the same beacons
+    vs full-KV over 131072 tokens, plus the latent sweep at 4x/8x/32x."""
+    res = {}
+    full_wl = synth.get_workload("c5_full")
+    log("comparison: generating full-KV cache (131072 tokens)")
+    K, V = synth.make_full_kv(full_wl, 0, device=dev)
+    base = synth.make_layer(full_wl, 0, device=dev, num_beacons=0, raw_window=128)
+    pf = lda.make_problem(batch=full_wl.batch, num_q_heads=full_wl.num_q_heads,
+                          num_kv_heads=full_wl.num_kv_heads, num_beacons=0, rank_k=0, rank_v=0,
+                          raw_window=full_wl.context, scale=full_wl.scale,
+                          rope_theta=full_wl.rope_theta, dtype=full_wl.dtype)
+    out, lse = lda.alloc_outputs(pf, dev)
+    ws = lda.alloc_workspace(pf, lda.SLIMKV_OP_FULL_KV, dev)
+    t_full = time_calls(lambda: lda.full_kv_attn(pf, base.q, base.q_pos, K, V, out, lse, ws),
+                        10, 3, torch)
+    bytes_full = 2 * K.numel() * K.element_size()
+    res["full_kv"] = {"us": round(t_full * 1e3, 1), "gbps": round(bytes_full / t_full / 1e6, 1)}
+    del K, V, ws
+    torch.cuda.empty_cache()
+    for key in ("c5_4x", "c5_8x", "c5_16x", "c5_32x"):
+        wl = synth.get_workload(key)
+        x = synth.make_layer(wl, 0, device=dev)
+        p = lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                     rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                     scale=wl.scale)
+        ws = lda.alloc_workspace(p, lda.SLIMKV_OP_LATENT, dev)
+        t = time_calls(lambda: lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K,
+                                                      x.C_V, x.K_raw, x.V_raw, out, lse, ws),
+                       20, 3, torch)
+        cache = wl.layer_bytes(0)
+        entry = {"us": round(t * 1e3, 1), "gbps": round(cache / t / 1e6, 1),
+                 "speedup_vs_full_kv": round(t_full / t, 2)}
+        if key == "c5_16x":
+            wsr = lda.alloc_workspace(p, lda.SLIMKV_OP_RECONSTRUCT, dev)
+            tr = time_calls(lambda: lda.slimkv_reconstruct_attn(
+                p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw, out, lse, wsr),
+                10, 3, torch)
+            entry["reconstruct_us"] = round(tr * 1e3, 1)
+            entry["speedup_vs_reconstruct"] = round(tr / t, 2)
+            del wsr
+        res[key] = entry
+        del x, ws
+        torch.cuda.empty_cache()
+        log(f"comparison {key}: {entry}")
+    return res
+
+
+def cpu_baseline(wl, layers, budget_s, synth):
+    """The fp64 oracle on this host's cores, over whole layers (the same
+    inputs the GPU ran, copied to host memory), until the time budget is
+    spent; the step time is extrapolated by each layer's multiply-add count."""
+    import oracle
+
+    threads = oracle.max_threads()
+
+    def macs(layer):
+        r = wl.ranks[layer]
+        per_head = wl.num_beacons * 2 * r + 2 * wl.raw_window * wl.head_dim + 2 * wl.head_dim * r
+        return wl.batch * wl.num_q_heads * per_head
+
+    st = synth.to_numpy_storage
+    done, spent, layer_list = 0, 0.0, []
+    for layer in range(wl.layers):
+        x = layers[layer]
+        args = [st(t) for t in (x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw)]
+        t0 = time.perf_counter()
+        oracle.decode(*args, num_kv_heads=wl.num_kv_heads, scale=wl.scale,
+                      rope_theta=wl.rope_theta, threads=threads)
+        spent += time.perf_counter() - t0
+        done += macs(layer)
+        layer_list.append(layer)
+        log(f"cpu oracle layer {layer}: {spent:.1f}s cumulative")
+        if spent >= budget_s:
+            break
+    total = sum(macs(layer) for layer in range(wl.layers))
+    step_s = spent * total / done
+    return {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{len(layer_list)} of {wl.layers} layers (all {wl.batch * wl.num_kv_heads} "
+                       f"units each) timed in {spent:.1f}s with fp64 C+OpenMP; step time "
+                       f"extrapolated by multiply-add count to {step_s:.1f}s")}
+
+
+if __name__ == "__main__":
+    main()

@@ -166,6 +166,16 @@ slimkv_status full_kv_attn(const slimkv_problem* problem, const void* q,
                            float* out, float* lse, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * Profiling hook (optional).  The next successful entry-point call made on
+ * this thread records `start` right before it launches its attention kernel
+ * (the kernel that streams the cache) and `stop` right after, both on the
+ * call's stream, then forgets them.  start and stop are hipEvent_t handles
+ * owned by the caller; NULL, NULL clears a pending pair.  Lets a caller time
+ * that one kernel with events; the computation is unchanged.
+ */
+slimkv_status slimkv_set_kernel_events(void* start, void* stop);
+
 /* Static text for a status code. */
 const char* slimkv_status_string(slimkv_status status);
 

@@ -10,5 +10,6 @@ from .binding import (SLIMKV_BF16, SLIMKV_FP32, SLIMKV_OP_FULL_KV,  # noqa: F401
                       SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn,
                       load_library, make_problem, slimkv_abi_version, slimkv_decode_attn,
                       slimkv_last_error, slimkv_problem, slimkv_reconstruct_attn,
-                      slimkv_status_string, slimkv_workspace_bytes)
+                      slimkv_set_kernel_events, slimkv_status_string,
+                      slimkv_workspace_bytes)
 from .helpers import alloc_outputs, alloc_workspace, problem_from_tensors  # noqa: F401

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_reconstruct_attn",
-           "full_kv_attn", "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
+           "full_kv_attn", "slimkv_set_kernel_events", "slimkv_status_string",
+           "slimkv_last_error", "slimkv_abi_version")
 
 
 class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
@@ -82,6 +83,8 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_status_string.restype = ctypes.c_char_p
     lib.slimkv_last_error.argtypes = []
     lib.slimkv_last_error.restype = ctypes.c_char_p
+    lib.slimkv_set_kernel_events.argtypes = [vp, vp]
+    lib.slimkv_set_kernel_events.restype = ctypes.c_int
     lib.slimkv_abi_version.argtypes = []
     lib.slimkv_abi_version.restype = ctypes.c_int32
     if path is None:
@@ -154,6 +157,21 @@ def full_kv_attn(problem, q, q_pos, K, V, out, lse, workspace, stream=None) -> N
     _check(lib, lib.full_kv_attn(
         ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(K), _ptr(V), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_set_kernel_events(start, stop) -> None:
+    """Time the next call's attention kernel with two torch.cuda.Event (or raw
+    hipEvent_t handles); None, None clears a pending pair."""
+    lib = load_library()
+    def handle(e):
+        if e is None:
+            return None
+        if isinstance(e, torch.cuda.Event):
+            if not e.cuda_event:  # torch creates the HIP event on first record
+                e.record()
+            return e.cuda_event
+        return int(e)
+    _check(lib, lib.slimkv_set_kernel_events(handle(start), handle(stop)))
 
 
 def slimkv_status_string(status: int) -> str:

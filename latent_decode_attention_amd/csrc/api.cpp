@@ -19,6 +19,7 @@ namespace slimkv {
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
 
 slimkv_status fail(slimkv_status st, const char* fmt, ...) {
   char buf[512];
@@ -33,19 +34,18 @@ slimkv_status fail(slimkv_status st, const char* fmt, ...) {
 constexpr int64_t kMaxRows = int64_t(1) << 24;    // rows per unit and segment
 constexpr int64_t kMaxUnits = int64_t(1) << 20;   // batch * kv heads
 constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
-constexpr int kTargetBlocks = 2048;               // sweep workgroups to aim for
+constexpr int kTargetBlocks = 2048;               // attention workgroups to aim for
 constexpr int64_t kMinChunkBytes = 32 << 10;
-constexpr int64_t kMaxChunkBytes = 512 << 10;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
-  SweepArgs sweep;
+  AttnArgs attn;
   int64_t units;
   int dtype;
   int elem;
-  size_t off_q_rot, off_q_lat, off_ml, off_acc, off_kb, off_vb, total;
+  size_t off_counters, off_q_rot, off_q_lat, off_ml, off_acc, off_kb, off_vb, total;
 };
 
 bool rank_ok(int r) { return r >= 16 && r <= kHeadDim && r % 16 == 0; }
@@ -116,7 +116,7 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   pl.dtype = p->dtype;
   pl.elem = p->dtype == SLIMKV_FP32 ? 4 : 2;
   pl.units = (int64_t)p->batch * p->num_kv_heads;
-  SweepArgs& a = pl.sweep;
+  AttnArgs& a = pl.attn;
   a.batch = p->batch;
   a.num_q_heads = p->num_q_heads;
   a.num_kv_heads = p->num_kv_heads;
@@ -143,24 +143,37 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   }
   a.nseg = ns;
 
+  // chunk size: about kTargetBlocks workgroups over the whole call, and at
+  // most kMaxMergeSlots / G chunks per unit so one workgroup can merge them
   int64_t unit_bytes = 0;
   for (int i = 0; i < ns; ++i) unit_bytes += (int64_t)a.seg[i].rows * (a.seg[i].rk + a.seg[i].rv) * pl.elem;
   const int64_t total_bytes = unit_bytes * pl.units;
-  const int64_t chunk_bytes =
-      std::min(kMaxChunkBytes, std::max(kMinChunkBytes, ceil_div(total_bytes, kTargetBlocks)));
-  for (int i = 0; i < ns; ++i) plan_segment(a.seg[i], pl.dtype, pl.units, chunk_bytes, p->num_splits);
-  a.splits_total = a.seg[0].splits + (ns > 1 ? a.seg[1].splits : 0);
+  const int64_t max_unit_splits = kMaxMergeSlots / a.group;
+  int64_t chunk_bytes = std::max(kMinChunkBytes, ceil_div(total_bytes, kTargetBlocks));
+  int forced = p->num_splits;
+  if (forced > 0) forced = (int)std::min<int64_t>(forced, max_unit_splits / ns);
+  for (;;) {
+    for (int i = 0; i < ns; ++i) plan_segment(a.seg[i], pl.dtype, pl.units, chunk_bytes, forced);
+    a.splits_total = a.seg[0].splits + (ns > 1 ? a.seg[1].splits : 0);
+    if (a.splits_total <= max_unit_splits) break;
+    chunk_bytes *= 2;
+  }
   if (pl.units * a.splits_total > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
 
-  // workspace layout
-  const int64_t Hq = p->num_q_heads, B = p->batch, G = a.group;
-  size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);  // reserved control words
+  a.latent_splits = a.seg[0].kind == kSegLatent && ns > 0 ? a.seg[0].splits : 0;
+  a.rank_v = a.latent_splits > 0 ? p->rank_v : 0;
+  a.rank_k = a.latent_splits > 0 ? p->rank_k : 0;
+
+  // workspace layout: per-unit counters (must start zeroed), the prologue's
+  // queries, then the chunk partials
+  const int64_t G = a.group;
+  pl.off_counters = 0;
+  size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);
   pl.off_q_rot = off;
-  off = round_up(off + (size_t)(B * Hq * kHeadDim) * sizeof(float), kAlign);
+  off = round_up(off + (size_t)p->batch * p->num_q_heads * kHeadDim * sizeof(float), kAlign);
   pl.off_q_lat = off;
-  if (op == SLIMKV_OP_LATENT && p->num_beacons > 0)
-    off = round_up(off + (size_t)(B * Hq * p->rank_k) * sizeof(float), kAlign);
+  if (a.rank_k > 0) off = round_up(off + (size_t)p->batch * p->num_q_heads * a.rank_k * sizeof(float), kAlign);
   pl.off_ml = off;
   off = round_up(off + (size_t)(pl.units * a.splits_total * G * 2) * sizeof(float), kAlign);
   pl.off_acc = off;
@@ -266,26 +279,20 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   // ---- all checks passed: launch
   char* wsb = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SweepArgs& a = pl.sweep;
+  AttnArgs& a = pl.attn;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.U_K = U_K;
+  a.U_V = U_V;
+  a.log2_theta = log2(p->rope_theta);
+  a.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
+  a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
   a.q_rot = reinterpret_cast<float*>(wsb + pl.off_q_rot);
-  a.q_lat = reinterpret_cast<float*>(wsb + pl.off_q_lat);
+  a.q_lat = a.rank_k > 0 ? reinterpret_cast<float*>(wsb + pl.off_q_lat) : nullptr;
   a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
-
-  PrologueArgs pa{};
-  pa.q = q;
-  pa.q_pos = q_pos;
-  pa.U_K = U_K;
-  pa.batch = p->batch;
-  pa.num_q_heads = p->num_q_heads;
-  pa.num_kv_heads = p->num_kv_heads;
-  pa.group = a.group;
-  pa.rank_k = (int32_t)rk;
-  pa.rope_theta = p->rope_theta;
-  pa.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
-  pa.q_rot = const_cast<float*>(a.q_rot);
-  pa.q_lat = (op == SLIMKV_OP_LATENT && beacons) ? const_cast<float*>(a.q_lat) : nullptr;
-
+  a.out = out;
+  a.lse = lse;
   int si = 0;
   if (beacons) {
     Segment& sg = a.seg[si++];
@@ -303,22 +310,8 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     sg.V = V_raw;
   }
 
-  CombineArgs ca{};
-  ca.part_ml = a.part_ml;
-  ca.part_acc = a.part_acc;
-  ca.U_V = (op == SLIMKV_OP_LATENT && beacons) ? U_V : nullptr;
-  ca.batch = p->batch;
-  ca.num_q_heads = p->num_q_heads;
-  ca.num_kv_heads = p->num_kv_heads;
-  ca.group = a.group;
-  ca.rank_v = (op == SLIMKV_OP_LATENT && beacons) ? (int32_t)rv : 0;
-  ca.splits_total = a.splits_total;
-  ca.latent_splits = (op == SLIMKV_OP_LATENT && beacons) ? a.seg[0].splits : 0;
-  ca.out = out;
-  ca.lse = lse;
-
-  hipError_t err = launch_prologue(pa, pl.dtype, s);
-  if (err == hipSuccess && op == SLIMKV_OP_RECONSTRUCT && beacons) {
+  hipError_t err = hipSuccess;
+  if (op == SLIMKV_OP_RECONSTRUCT && beacons) {
     RebuildArgs rb{};
     rb.batch = p->batch;
     rb.num_kv_heads = p->num_kv_heads;
@@ -336,8 +329,11 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
       err = launch_rebuild(rb, pl.dtype, s);
     }
   }
-  if (err == hipSuccess) err = launch_sweep(a, pl.dtype, s);
-  if (err == hipSuccess) err = launch_combine(ca, pl.dtype, s);
+  if (err == hipSuccess) {
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    err = launch_attention(a, pl.dtype, s, ev0, ev1);
+  }
   if (err != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();
   return SLIMKV_OK;
@@ -393,6 +389,14 @@ const char* slimkv_status_string(slimkv_status status) {
 }
 
 const char* slimkv_last_error(void) { return slimkv::g_last_error.c_str(); }
+
+slimkv_status slimkv_set_kernel_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return slimkv::fail(SLIMKV_ERR_NULL, "start and stop must both be set or both be NULL");
+  slimkv::g_ev_start = static_cast<hipEvent_t>(start);
+  slimkv::g_ev_stop = static_cast<hipEvent_t>(stop);
+  return SLIMKV_OK;
+}
 
 int32_t slimkv_abi_version(void) { return SLIMKV_ABI_VERSION; }
 

@@ -1,6 +1,5 @@
-// aux.hip -- the kernels around the sweep: query prologue, split merge with
-// the single up-projection, and the full-width beacon rebuild used only by
-// the reconstruction comparison path.
+// aux.hip -- the full-width beacon rebuild used only by the reconstruction
+// comparison path, the tile-height rule, and the attention dispatcher.
 #include <math.h>
 
 #include "internal.h"
@@ -10,141 +9,6 @@ namespace slimkv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-template <bool BF16>
-__device__ __forceinline__ float ld(const void* p, size_t i) {
-  if constexpr (BF16)
-    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
-  else
-    return static_cast<const float*>(p)[i];
-}
-
-// ---------------------------------------------------------------------------
-// Prologue, one workgroup per (b, kv head).  Rotates the G query heads of the
-// group at the query position (rotate-half pairs (i, i + d/2), angle
-// pos * theta^(-2i/d), angles and the rotation in double precision) and
-// pre-scales them by scale * log2(e) so later scores are in log2 units.
-// With a latent segment it also projects them into the head's latent key
-// space: q_lat = U_K^T q_rot.  (Page "Can SlimKV compress KV cache jointly
-// across tokens and features", section "Latent-space attention removes the
-// rebuild step": queries keep RoPE and are projected after GQA grouping.)
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void prologue_kernel(PrologueArgs a) {
-  __shared__ float qs[kMaxGroup][kHeadDim];
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
-  const int G = a.group;
-  const double pos = (double)a.q_pos[b];
-  constexpr int half = kHeadDim / 2;
-  for (int p = tid; p < G * half; p += kThreads) {
-    const int g = p / half, i = p - (p / half) * half;
-    const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
-    const double x1 = ld<BF16>(a.q, base + i), x2 = ld<BF16>(a.q, base + i + half);
-    const double inv_freq = pow(a.rope_theta, -(double)(2 * i) / (double)kHeadDim);
-    double sn, cs;
-    sincos(pos * inv_freq, &sn, &cs);
-    const float r1 = (float)((x1 * cs - x2 * sn) * a.score_scale);
-    const float r2 = (float)((x2 * cs + x1 * sn) * a.score_scale);
-    a.q_rot[base + i] = r1;
-    a.q_rot[base + i + half] = r2;
-    qs[g][i] = r1;
-    qs[g][i + half] = r2;
-  }
-  if (!a.q_lat) return;
-  __syncthreads();
-  const int rk = a.rank_k;
-  const size_t u0 = (size_t)h * kHeadDim * rk;
-  for (int p = tid; p < G * rk; p += kThreads) {
-    const int g = p / rk, k = p - (p / rk) * rk;
-    float acc = 0.0f;
-    for (int i = 0; i < kHeadDim; ++i) acc = fmaf(qs[g][i], ld<BF16>(a.U_K, u0 + (size_t)i * rk + k), acc);
-    a.q_lat[((size_t)b * a.num_q_heads + (size_t)h * G + g) * rk + k] = acc;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Combine, one workgroup per (b, kv head).  Merges the per-chunk partials of
-// all G heads by log-sum-exp (one softmax over every beacon and raw row),
-// lifts the merged latent value sum once by U_V and adds the full-width sum:
-//   out = U_V (sum_latent w_s acc_s) / L + (sum_full w_s acc_s) / L,
-//   w_s = 2^(m_s - M), L = sum_s w_s l_s, lse = ln 2 * (M + log2 L).
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  constexpr int kBlock = 256;
-  __shared__ float sM[kMaxGroup], sL[kMaxGroup];
-  __shared__ float wts[kBlock][kMaxGroup];
-  __shared__ float olat[kMaxGroup][kHeadDim];
-  const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
-  const int G = a.group, S = a.splits_total, rv = a.rank_v;
-  const float* ml = a.part_ml + (size_t)unit * S * G * 2;
-  const float* acc = a.part_acc + (size_t)unit * S * G * kHeadDim;
-
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[(s * G + tid) * 2]);
-    float L = 0.0f;
-    for (int s = 0; s < S; ++s) L += exp2f(ml[(s * G + tid) * 2] - M) * ml[(s * G + tid) * 2 + 1];
-    sM[tid] = M;
-    sL[tid] = L;
-  }
-  __syncthreads();
-
-  constexpr int kPer = kMaxGroup * kHeadDim / kThreads;  // outputs per thread
-  float lat[kPer], full[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) lat[j] = full[j] = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += kBlock) {
-    const int ns = min(kBlock, S - s0);
-    for (int q = tid; q < ns * G; q += kThreads) {
-      const int si = q / G, g = q - (q / G) * G;
-      wts[si][g] = exp2f(ml[((s0 + si) * G + g) * 2] - sM[g]) / sL[g];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = tid + kThreads * j;
-      if (p < G * kHeadDim) {
-        const int g = p / kHeadDim, col = p - (p / kHeadDim) * kHeadDim;
-        for (int si = 0; si < ns; ++si) {
-          const int s = s0 + si;
-          const float w = wts[si][g];
-          if (s < a.latent_splits) {
-            if (col < rv) lat[j] = fmaf(w, acc[((size_t)s * G + g) * kHeadDim + col], lat[j]);
-          } else {
-            full[j] = fmaf(w, acc[((size_t)s * G + g) * kHeadDim + col], full[j]);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int p = tid + kThreads * j;
-    if (p < G * kHeadDim) olat[p / kHeadDim][p % kHeadDim] = lat[j];
-  }
-  __syncthreads();
-  const size_t uv0 = (size_t)h * kHeadDim * rv;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int p = tid + kThreads * j;
-    if (p < G * kHeadDim) {
-      const int g = p / kHeadDim, i = p - (p / kHeadDim) * kHeadDim;
-      float o = full[j];
-      if (a.latent_splits > 0)
-        for (int k = 0; k < rv; ++k) o = fmaf(ld<BF16>(a.U_V, uv0 + (size_t)i * rv + k), olat[g][k], o);
-      a.out[((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim + i] = o;
-    }
-  }
-  if (a.lse && tid < G)
-    a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + tid] =
-        (float)(0.69314718055994530942 * ((double)sM[tid] + log2((double)sL[tid])));
-}
 
 // ---------------------------------------------------------------------------
 // Rebuild (reconstruction comparison path only): dst = C U^T per unit, i.e.
@@ -235,24 +99,6 @@ int tile_rows(int dtype, int rk, int rv) {
   return nch == 1 ? 64 : (nch == 2 ? 32 : 16);
 }
 
-hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(kThreads);
-  if (dtype == 0)
-    hipLaunchKernelGGL(prologue_kernel<false>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(prologue_kernel<true>, grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.num_kv_heads)), block(kThreads);
-  if (dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s) {
   const dim3 block(kThreads);
   if (dtype == 0) {
@@ -266,16 +112,17 @@ hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sweep_g1(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g2(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g3(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g4(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g5(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g6(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g7(const SweepArgs&, int, int, hipStream_t);
-hipError_t launch_sweep_g8(const SweepArgs&, int, int, hipStream_t);
+hipError_t launch_attention_g1(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g2(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g3(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g4(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g5(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g6(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g7(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g8(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
 
-hipError_t launch_sweep(const SweepArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev0,
+                            hipEvent_t ev1) {
   int nch = 4;
   if (a.seg[0].kind == kSegLatent) {
     nch = (a.seg[0].rk + 31) / 32;
@@ -283,14 +130,14 @@ hipError_t launch_sweep(const SweepArgs& a, int dtype, hipStream_t s) {
     if (nv > nch) nch = nv;
   }
   switch (a.group) {
-    case 1: return launch_sweep_g1(a, dtype, nch, s);
-    case 2: return launch_sweep_g2(a, dtype, nch, s);
-    case 3: return launch_sweep_g3(a, dtype, nch, s);
-    case 4: return launch_sweep_g4(a, dtype, nch, s);
-    case 5: return launch_sweep_g5(a, dtype, nch, s);
-    case 6: return launch_sweep_g6(a, dtype, nch, s);
-    case 7: return launch_sweep_g7(a, dtype, nch, s);
-    default: return launch_sweep_g8(a, dtype, nch, s);
+    case 1: return launch_attention_g1(a, dtype, nch, s, ev0, ev1);
+    case 2: return launch_attention_g2(a, dtype, nch, s, ev0, ev1);
+    case 3: return launch_attention_g3(a, dtype, nch, s, ev0, ev1);
+    case 4: return launch_attention_g4(a, dtype, nch, s, ev0, ev1);
+    case 5: return launch_attention_g5(a, dtype, nch, s, ev0, ev1);
+    case 6: return launch_attention_g6(a, dtype, nch, s, ev0, ev1);
+    case 7: return launch_attention_g7(a, dtype, nch, s, ev0, ev1);
+    default: return launch_attention_g8(a, dtype, nch, s, ev0, ev1);
   }
 }
 

@@ -9,10 +9,11 @@
 namespace slimkv {
 
 constexpr int kHeadDim = 128;
-constexpr int kWaves = 4;              // waves per sweep workgroup
-constexpr int kThreads = 64 * kWaves;  // sweep / combine workgroup size
+constexpr int kWaves = 4;              // waves per attention workgroup
+constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
 constexpr int kMaxSplits = 4096;       // row chunks per segment per unit
+constexpr int kMaxMergeSlots = 2048;   // splits_total * G a unit's merge holds in LDS
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -22,60 +23,51 @@ enum SegKind : int32_t {
 
 // One run of rows that every (b, kv head) unit owns, e.g. its N_b beacons.
 struct Segment {
-  const void* K;      // [B, H_kv, rows, rk]
-  const void* V;      // [B, H_kv, rows, rv]
-  int32_t kind;       // SegKind
-  int32_t rows;       // rows per unit
-  int32_t rk, rv;     // row widths in elements (d for kSegFull)
-  int32_t splits;     // chunks per unit
-  int32_t chunk_rows; // rows per chunk (multiple of the tile height)
+  const void* K;       // [B, H_kv, rows, rk]
+  const void* V;       // [B, H_kv, rows, rv]
+  int32_t kind;        // SegKind
+  int32_t rows;        // rows per unit
+  int32_t rk, rv;      // row widths in elements (d for kSegFull)
+  int32_t splits;      // chunks per unit
+  int32_t chunk_rows;  // rows per chunk (multiple of the tile height)
 };
 
-// Everything the sweep and combine kernels read.
-struct SweepArgs {
+// Everything the attention kernel reads.  One workgroup per (unit, chunk);
+// the last workgroup of a unit to finish merges the unit's chunks.
+struct AttnArgs {
   Segment seg[2];
   int32_t nseg;
   int32_t batch, num_q_heads, num_kv_heads, group;
-  int32_t splits_total;       // seg[0].splits + seg[1].splits
-  const float* q_lat;         // [B, H_q, r_K] latent query, pre-scaled
-  const float* q_rot;         // [B, H_q, d] rotated query, pre-scaled
-  float* part_ml;             // [units, splits_total, G, 2]  (max, sum)
-  float* part_acc;            // [units, splits_total, G, d]  weighted values
-};
-
-struct PrologueArgs {
-  const void* q;              // [B, H_q, d]
-  const int32_t* q_pos;       // [B]
-  const void* U_K;            // [H_kv, d, r_K] or null
-  int32_t batch, num_q_heads, num_kv_heads, group, rank_k;
-  double rope_theta;
-  double score_scale;         // scale * log2(e): scores come out in log2 units
-  float* q_rot;               // out: [B, H_q, d]
-  float* q_lat;               // out: [B, H_q, r_K] or null
-};
-
-struct CombineArgs {
-  const float* part_ml;
-  const float* part_acc;
-  const void* U_V;            // [H_kv, d, r_V] or null (no latent segment)
-  int32_t batch, num_q_heads, num_kv_heads, group, rank_v;
-  int32_t splits_total;
-  int32_t latent_splits;      // leading splits that hold latent sums (r_V wide)
-  float* out;                 // [B, H_q, d]
-  float* lse;                 // [B, H_q] or null
+  int32_t splits_total;   // seg[0].splits + seg[1].splits
+  int32_t latent_splits;  // leading chunks whose sums are r_V-wide latents
+  int32_t rank_v;         // r_V of the latent segment (0 if none)
+  const void* q;          // [B, H_q, d] before rotation
+  const int32_t* q_pos;   // [B]
+  const void* U_K;        // [H_kv, d, r_K] (latent segment only)
+  const void* U_V;        // [H_kv, d, r_V] (latent segment only)
+  double score_scale;     // scale * log2(e): scores are kept in log2 units
+  double log2_theta;      // log2(rope theta), computed on the host in fp64
+  float* q_rot;           // [B, H_q, d] rotated query, pre-scaled (written by the prologue)
+  float* q_lat;           // [B, H_q, r_K] latent query, pre-scaled (latent segment only)
+  int32_t rank_k;         // r_K of the latent segment (0 if none)
+  uint32_t* counters;     // [units] finished-chunk counters (zero between calls)
+  float* part_ml;         // [units, splits_total, G, 2]  (max, sum of exp)
+  float* part_acc;        // [units, splits_total, G, d]  exp-weighted value sums
+  float* out;             // [B, H_q, d]
+  float* lse;             // [B, H_q] or null
 };
 
 struct RebuildArgs {
-  const void* C;              // [B, H_kv, N_b, r]
-  const void* U;              // [H_kv, d, r]
-  void* dst;                  // [B, H_kv, N_b, d]
+  const void* C;  // [B, H_kv, N_b, r]
+  const void* U;  // [H_kv, d, r]
+  void* dst;      // [B, H_kv, N_b, d]
   int32_t batch, num_kv_heads, num_beacons, rank;
 };
 
 // Host launchers (defined in the .hip files).  dtype: 0 fp32, 1 bf16.
-hipError_t launch_prologue(const PrologueArgs& a, int dtype, hipStream_t s);
-hipError_t launch_sweep(const SweepArgs& a, int dtype, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, int dtype, hipStream_t s);
+// Prologue kernel, then the attention kernel (bracketed by ev0/ev1 if set).
+hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev0,
+                            hipEvent_t ev1);
 hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s);
 
 // Tile height (rows) a segment of the given widths is swept in.

@@ -1,8 +1,9 @@
-// sweep_g2.hip -- sweep kernels for 2 query heads per KV head.
+// sweep_g2.hip -- attention kernels for 2 query heads per KV head.
 #include "sweep_impl.h"
 
 namespace slimkv {
-hipError_t launch_sweep_g2(const SweepArgs& a, int dtype, int nch, hipStream_t s) {
-  return launch_sweep_group<2>(a, dtype, nch, s);
+hipError_t launch_attention_g2(const AttnArgs& a, int dtype, int nch, hipStream_t s,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_attention_group<2>(a, dtype, nch, s, ev0, ev1);
 }
 }  // namespace slimkv

@@ -1,32 +1,42 @@
-// sweep_impl.h -- the split-K sweep over one row chunk of a (b, kv head) unit.
+// sweep_impl.h -- the fused decode-attention kernel: query prologue, split-K
+// sweep over one row chunk of a (b, kv head) unit, and the merge of all of
+// the unit's chunks by whichever workgroup finishes last.
 //
-// What one workgroup computes (page "Can SlimKV compress KV cache jointly
-// across tokens and features", section "Latent-space attention removes the
-// rebuild step"): for the G query heads of one KV head and a contiguous run
-// of cached rows, the scores against the rows' keys (latent keys C_K scored
-// with the latent query U_K^T q', or rotated full-width keys scored with q'),
-// and the online-softmax partial (max, sum of exp, exp-weighted value sum)
-// over those rows.  For beacon rows the value sum stays in latent space
-// (width r_V); it is lifted by U_V only once, after all chunks are merged.
+// What is computed (page "Can SlimKV compress KV cache jointly across tokens
+// and features", section "Latent-space attention removes the rebuild step"):
+// the G query heads of one KV head are rotated at the query position and,
+// for beacon rows, projected into the head's latent key space (q' U_K).
+// Scores against the latent beacon keys C_K (no rotation) and against the
+// rotated raw keys share one softmax.  Beacon values are summed in latent
+// form (A C_V) and lifted once by U_V after every chunk is merged, so beacon
+// keys and values are never rebuilt at full dimension.
 //
-// Mapping onto CDNA4:
-//   * 4 waves per workgroup, each sweeping a contiguous sub-range of the
-//     chunk in tiles of 16/32/64 rows, all with 16-byte global loads.
-//   * Scores are a [G x K] x [K x 16 rows] contraction per 16-row subtile,
-//     done on the matrix cores with v_mfma_f32_16x16x32_bf16 (fp32 data:
-//     v_mfma_f32_16x16x4_f32).  Query heads sit on the M axis (rows >= G
-//     are zero), cache rows on N, features on K.  The bf16 path feeds the
-//     query as two bf16 terms (hi + lo), so scores carry ~16 mantissa bits
-//     of the fp32 query against exact bf16 keys.
+// Mapping onto CDNA4 (gfx950):
+//   * One workgroup of 4 waves per (unit, row chunk); each wave sweeps a
+//     contiguous sub-range of the chunk in tiles of 16/32/64 rows, every
+//     global read a 16-byte load.
+//   * Prologue per workgroup: rotation in double precision (angles reduced
+//     mod 2*pi before sincos), the
+//     latent projection U_K^T q' as an fp32 MFMA (16x16x4) into LDS.  Its
+//     loads and the first tile's loads are all issued up front.
+//   * Scores are a [G x K] x [K x 16 rows] contraction per 16-row subtile on
+//     the matrix cores (v_mfma_f32_16x16x32_bf16; fp32 data uses
+//     v_mfma_f32_16x16x4_f32).  Query heads sit on the M axis, cache rows on
+//     N, features on K.  The bf16 path feeds the fp32 query as two bf16
+//     terms (hi + lo): ~16 mantissa bits of query against exact bf16 keys.
 //   * The MFMA output keeps head 4*(lane/16)+i of row lane%16 in register
-//     i, so the running max is a 16-lane DPP reduction and the softmax
-//     state lives in the same layout.
-//   * exp-weights go through LDS to the value lanes, which hold 16 bytes of
-//     one value row each (rows are read as one contiguous block) and keep
-//     G x 8 fp32 partial sums per lane.
-//   * At the end the four waves' partials are merged through LDS (per head,
-//     rescaled to a common max) and written to the workspace.
+//     i, so the running max is a 16-lane DPP reduction and the softmax state
+//     lives in that layout.  exp-weights reach the value lanes through LDS;
+//     each value lane holds 16 bytes of one value row and G x 8 fp32 sums.
+//   * The waves' partials merge in LDS into one partial per chunk, written
+//     to the workspace with device-coherent stores.  A device-scope counter
+//     per unit elects the last chunk's workgroup, which reads the partials
+//     back with device-coherent loads, merges them by log-sum-exp, lifts the
+//     latent sum with U_V on the matrix cores, writes out and lse, and resets
+//     the counter for the next call.
 #pragma once
+#include <math.h>
+
 #include "internal.h"
 
 namespace slimkv {
@@ -62,20 +72,54 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return u >> 16;
 }
 
+// Eight fp32 values as two bf16 vectors, hi + lo ~= x to ~2^-17 relative.
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
+  u32x4_t hw, lw;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f32_to_bf16_rne(x[2 * e]), h1 = f32_to_bf16_rne(x[2 * e + 1]);
+    const uint32_t l0 = f32_to_bf16_rne(x[2 * e] - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne(x[2 * e + 1] - __uint_as_float(h1 << 16));
+    hw[e] = h0 | (h1 << 16);
+    lw[e] = l0 | (l1 << 16);
+  }
+  hi = __builtin_bit_cast(bf16x8_t, hw);
+  lo = __builtin_bit_cast(bf16x8_t, lw);
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
+// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
+// other).  They are stored and loaded as relaxed agent-scope atomics, i.e.
+// with device-coherent cache policy, so no whole-L2 writeback/invalidate is
+// needed to hand them over -- only completion of the stores (see below).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float ld_elem(const void* p, size_t i) {
+  if constexpr (BF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+  else
+    return static_cast<const float*>(p)[i];
+}
+
 // Storage traits: bytes per element, elements per 16-byte lane load,
-// feature elements one MFMA chunk covers (4 k-groups of lanes).
+// features one MFMA chunk covers (4 k-groups of lanes), loads per tile.
 template <bool BF16>
 struct Traits;
 template <>
 struct Traits<true> {
   static constexpr int kElemBytes = 2;
-  static constexpr int kEpl = 8;       // elements per 16-byte load
-  static constexpr int kChunkK = 32;   // features per MFMA chunk
-  static constexpr int kMaxLoads = 4;  // 16-byte loads per lane per tile (K and V each)
+  static constexpr int kEpl = 8;
+  static constexpr int kChunkK = 32;
+  static constexpr int kMaxLoads = 4;
 };
 template <>
 struct Traits<false> {
@@ -85,94 +129,386 @@ struct Traits<false> {
   static constexpr int kMaxLoads = 8;
 };
 
-// Subtiles of 16 rows per tile for a given chunk count (K or V, the larger).
+// 16-row subtiles per tile for a given chunk count (of K or V, the larger).
 template <bool BF16, int NCH>
 struct TileShape {
   static constexpr int kSub = BF16 ? (NCH == 1 ? 4 : (NCH == 2 ? 2 : 1)) : 1;
   static constexpr int kRows = 16 * kSub;
 };
 
-struct alignas(16) SweepShared {
-  // exp-weights of the current tile, per wave: [rows][GP] (GP = 4 or 8)
-  float p[kWaves][64 * 8];
-  // per-head merge buffer: one fp32 value-chunk per lane per wave
-  float red[kWaves][64][8];
+struct alignas(16) AttnShared {
+  union {
+    float p[kWaves][64 * 8];   // exp-weights of the current tile, per wave
+    float red[kWaves][64][8];  // per-head merge of the waves' value sums
+    struct {
+      float ml[kMaxMergeSlots][2];  // every chunk's (max, sum); then weights
+      float olat[kMaxGroup][kHeadDim];
+      float ofull[kMaxGroup][kHeadDim];
+    } comb;
+  } u;
   float ml[kWaves][kMaxGroup][2];
+  float M[kMaxGroup], L[kMaxGroup];
+  int is_last;
 };
 
-// Sweep rows [r0, r1) of one unit's segment and write one partial.
-// NCH: MFMA feature chunks per row (template so register arrays are static).
+// Angle reduced into [-pi, pi] with a two-term 2*pi (fma keeps each step
+// exact up to one rounding), so sincos never sees a large argument.
+__device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
+  constexpr double kTwoPiHi = 6.283185307179586232;     // 2*pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189534561;
+  const double k = rint(ang * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, ang);
+  r = fma(-k, kTwoPiLo, r);
+  sincos(r, &s, &c);
+}
+
+// ---------------------------------------------------------------------------
+// Prologue kernel, one workgroup per (b, kv head): the G query heads rotated
+// at the query position (rotate-half pairs (i, i + d/2), double precision)
+// and pre-scaled by scale * log2(e), written to q_rot; for a latent segment
+// also q_lat = U_K^T q_rot (fp32 MFMA 16x16x4, exact products).  Every
+// global read is issued up front (one round trip).
+template <int G, bool BF16>
+__global__ __launch_bounds__(kThreads) void prologue_kernel(AttnArgs a) {
+  __shared__ float qrot[kMaxGroup][kHeadDim];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, kg = lane >> 4;
+  const int unit = blockIdx.x;
+  const int b = unit / a.num_kv_heads;
+  const int h = unit - b * a.num_kv_heads;
+  const int rk = a.rank_k;
+  const bool latent = a.q_lat != nullptr;
+  constexpr int half = kHeadDim / 2;
+  constexpr int kPairs = (G * half + kThreads - 1) / kThreads;  // rotation pairs per thread
+  constexpr int kTiles = kHeadDim / 16 / kWaves;                // latent column tiles per wave
+
+  // Loads are unconditional from clamped (in-bounds) addresses: a load under
+  // a divergent branch costs a full wait for the memory round trip.
+  float x1[kPairs], x2[kPairs];
+#pragma unroll
+  for (int j = 0; j < kPairs; ++j) {
+    const int p = min(tid + kThreads * j, G * half - 1);
+    const int g = p / half, i = p % half;
+    const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
+    x1[j] = ld_elem<BF16>(a.q, base + i);
+    x2[j] = ld_elem<BF16>(a.q, base + i + half);
+  }
+  const double pos = (double)a.q_pos[b];
+  float ub[kTiles][kHeadDim / 4];
+  const char* U = static_cast<const char*>(a.U_K) + (size_t)h * kHeadDim * rk * Traits<BF16>::kElemBytes;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const int c0 = 16 * (wave + kWaves * t);
+    if (latent && c0 < rk) {  // wave-uniform
+#pragma unroll
+      for (int s = 0; s < kHeadDim / 4; ++s)
+        ub[t][s] = ld_elem<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < kPairs; ++j) {
+    const int p = tid + kThreads * j;
+    if (p < G * half) {
+      const int g = p / half, i = p % half;
+      double sn, cs;
+      // theta^(-2i/d) = 2^(-(2i/d) log2 theta), in double precision
+      const double inv_freq = exp2(-(double)(2 * i) / (double)kHeadDim * a.log2_theta);
+      rope_sincos(pos * inv_freq, sn, cs);
+      const double v1 = x1[j], v2 = x2[j];
+      const float r1 = (float)((v1 * cs - v2 * sn) * a.score_scale);
+      const float r2 = (float)((v2 * cs + v1 * sn) * a.score_scale);
+      const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
+      a.q_rot[base + i] = r1;
+      a.q_rot[base + i + half] = r2;
+      qrot[g][i] = r1;
+      qrot[g][i + half] = r2;
+    }
+  }
+  if (!latent) return;
+  __syncthreads();
+  // q_lat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
+  float* ql = a.q_lat + ((size_t)b * a.num_q_heads + (size_t)h * G) * rk;
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const int c0 = 16 * (wave + kWaves * t);
+    if (c0 < rk) {
+      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < kHeadDim / 4; ++s) {
+        const float av = n < G ? qrot[n][4 * s + kg] : 0.0f;
+        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, ub[t][s], d, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kg + e < G) ql[(size_t)(4 * kg + e) * rk + c0 + n] = d[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of all chunks of one unit (run by the unit's last workgroup).
+//   M = max_s m_s, L = sum_s 2^(m_s - M) l_s,
+//   o_lat = sum_{latent s} 2^(m_s - M) acc_s / L, o_full likewise,
+//   out = U_V o_lat + o_full, lse = ln 2 * (M + log2 L).
+// U_V rows, every (max, sum) and a first batch of chunk sums are loaded in
+// one round trip; more batches only when a unit has many chunks.
+template <int G, bool BF16>
+__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h,
+                                           AttnShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.splits_total, rv = a.rank_v;
+  const float* ml = a.part_ml + (size_t)unit * S * G * 2;
+  const float* acc = a.part_acc + (size_t)unit * S * G * kHeadDim;
+  float (*sml)[2] = sh.u.comb.ml;
+  constexpr int kPer = (G * kHeadDim + kThreads - 1) / kThreads;  // outputs per thread
+  constexpr int kBatch = 64 / kPer;                               // chunks per load batch
+  constexpr int kMlPer = kMaxMergeSlots * 2 / kThreads;           // (max, sum) loads per thread
+  const int m16 = lane & 15, kg = lane >> 4;
+  const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * Traits<BF16>::kElemBytes;
+
+  // -- one round trip: U_V rows of this wave's output tiles, (max, sum) pairs,
+  //    and the first batch of chunk sums
+  u32x4_t uw[2][4];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 16 * (wave + kWaves * t) + m16, k0 = 32 * c + 8 * kg;
+        // features past r_V are multiplied by zero latent entries below
+        uw[t][c] = a.latent_splits > 0 ? load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2)
+                                       : u32x4_t{0u, 0u, 0u, 0u};
+      }
+  }
+  // (unconditional loads from clamped indexes; out-of-range values unused)
+  float mlv[kMlPer];
+#pragma unroll
+  for (int j = 0; j < kMlPer; ++j)
+    mlv[j] = load_coherent(&ml[min(tid + kThreads * j, S * G * 2 - 1)]);
+  float v[kBatch][kPer];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int su = min(s0 + u, S - 1);
+        const int p = min(tid + kThreads * j, G * kHeadDim - 1);
+        v[u][j] = load_coherent(&acc[(size_t)su * G * kHeadDim + p]);
+      }
+  };
+  load_batch(0);
+#pragma unroll
+  for (int j = 0; j < kMlPer; ++j) {
+    const int q = tid + kThreads * j;
+    if (q < S * G * 2) (&sml[0][0])[q] = mlv[j];
+  }
+  __syncthreads();
+
+  // -- M and L per head: 32 lanes per head; then weights w_s = 2^(m_s - M) / L
+  {
+    const int g = tid >> 5, l32 = tid & 31;
+    float M = -INFINITY;
+    if (g < G)
+      for (int s = l32; s < S; s += 32) M = fmaxf(M, sml[s * G + g][0]);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
+    float L = 0.0f;
+    if (g < G)
+      for (int s = l32; s < S; s += 32) L += __builtin_amdgcn_exp2f(sml[s * G + g][0] - M) * sml[s * G + g][1];
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) L += __shfl_xor(L, off, 32);
+    if (g < G && l32 == 0) {
+      sh.M[g] = M;
+      sh.L[g] = L;
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < S * G; q += kThreads)
+    sml[q][0] = __builtin_amdgcn_exp2f(sml[q][0] - sh.M[q % G]) / sh.L[q % G];
+  __syncthreads();
+
+  // -- weighted sums: thread owns outputs p = tid + 256 j (p = g * d + col)
+  float lat[kPer], full[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) lat[j] = full[j] = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    if (s0 > 0) load_batch(s0);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + u;
+      if (s < S) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int p = tid + kThreads * j;
+          if (p < G * kHeadDim) {
+            const int g = p / kHeadDim, col = p % kHeadDim;
+            const float w = sml[s * G + g][0];
+            if (s < a.latent_splits) {
+              if (col < rv) lat[j] = fmaf(w, v[u][j], lat[j]);
+            } else {
+              full[j] = fmaf(w, v[u][j], full[j]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = tid + kThreads * j;
+    if (p < G * kHeadDim) {
+      sh.u.comb.olat[p / kHeadDim][p % kHeadDim] = lat[j];
+      sh.u.comb.ofull[p / kHeadDim][p % kHeadDim] = full[j];
+    }
+  }
+  __syncthreads();
+
+  // -- lift the latent sum once and add the full-width sum
+  float* out = a.out + ((size_t)b * a.num_q_heads + (size_t)h * G) * kHeadDim;
+  if (a.latent_splits > 0) {
+    // out^T[i][g] = sum_k U_V[i][k] olat[g][k]: D[m=i][n=g] over 16-row tiles of i
+    const int n = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i0 = 16 * (wave + kWaves * t);
+      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (BF16) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (32 * c < rv) {
+            const int k0 = 32 * c + 8 * kg;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (k0 < rv && n < G) ? sh.u.comb.olat[n][k0 + e] : 0.0f;
+            bf16x8_t hi, lo;
+            split_bf16x8(x, hi, lo);
+            const bf16x8_t uv = __builtin_bit_cast(bf16x8_t, uw[t][c]);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, hi, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, lo, d, 0, 0, 0);
+          }
+        }
+      } else {
+        for (int s = 0; s < rv / 4; ++s) {
+          const int k = 4 * s + kg;
+          const float uvv = ld_elem<false>(U, (size_t)(i0 + m16) * rv + k);
+          const float ov = n < G ? sh.u.comb.olat[n][k] : 0.0f;
+          d = __builtin_amdgcn_mfma_f32_16x16x4f32(uvv, ov, d, 0, 0, 0);
+        }
+      }
+      // lane (n = g, kg) holds rows i = i0 + 4kg + e
+      if (n < G) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = i0 + 4 * kg + e;
+          out[(size_t)n * kHeadDim + row] = d[e] + sh.u.comb.ofull[n][row];
+        }
+      }
+    }
+  } else {
+    for (int p = tid; p < G * kHeadDim; p += kThreads)
+      out[(size_t)(p / kHeadDim) * kHeadDim + p % kHeadDim] = sh.u.comb.ofull[p / kHeadDim][p % kHeadDim];
+  }
+  if (a.lse && tid < G)
+    a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + tid] =
+        (float)(0.69314718055994530942 * ((double)sh.M[tid] + log2((double)sh.L[tid])));
+}
+
+// ---------------------------------------------------------------------------
+// Sweep rows [r0, r1) of one unit's segment, write the chunk's partial, and
+// merge the unit if this is its last chunk.
 template <int G, int NCH, bool BF16>
-__device__ __forceinline__ void sweep_segment(const SweepArgs& a, const Segment& sg, int unit,
-                                              int slot, int r0, int r1, SweepShared& sh) {
+__device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& sg, int unit,
+                                             int slot, int r0, int r1, AttnShared& sh) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
   constexpr int SUB = TileShape<BF16, NCH>::kSub;
   constexpr int TR = TileShape<BF16, NCH>::kRows;
   constexpr int VMAX = Tr::kMaxLoads;
-  constexpr int GP = G <= 4 ? 4 : 8;      // padded heads per LDS row
-  constexpr int NGRP = (G + 3) / 4;       // 16-lane groups holding real heads
-  static_assert(SUB * NCH <= Tr::kMaxLoads || !BF16, "tile too large");
+  constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
+  constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
+  static_assert(!BF16 || SUB * NCH <= Tr::kMaxLoads, "tile too large");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = lane & 15;   // MFMA row/column index within a subtile
+  const int n = lane & 15;   // MFMA column (cache row) within a subtile
   const int kg = lane >> 4;  // MFMA k-group / output row group
 
   const int rk = sg.rk, rv = sg.rv;
+  const bool latent = sg.kind == kSegLatent;
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
   const size_t urow = (size_t)unit * (size_t)sg.rows;
   const char* Kb = static_cast<const char*>(sg.K) + urow * rk * Tr::kElemBytes;
   const char* Vb = static_cast<const char*>(sg.V) + urow * rv * Tr::kElemBytes;
 
-  // ---- query operand (A matrix: head m = lane%16, features of k-group kg)
-  const int rq = sg.kind == kSegLatent ? rk : kHeadDim;
-  const float* qsrc = (sg.kind == kSegLatent ? a.q_lat : a.q_rot) +
-                      ((size_t)b * a.num_q_heads + (size_t)h * G) * rq;
-  const int nchk = (rk + KCH - 1) / KCH;  // chunks that carry key features
-  bf16x8_t qhi[BF16 ? NCH : 1], qlo[BF16 ? NCH : 1];
-  float qf[BF16 ? 1 : NCH][4];
-  {
-    const int m = lane & 15;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int k0 = c * KCH + kg * (KCH / 4);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < KCH / 4; ++e)
-        x[e] = (m < G && k0 < rq) ? qsrc[(size_t)m * rq + k0 + e] : 0.0f;
-      if constexpr (BF16) {
-        uint32_t hb[8], lb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hb[e] = f32_to_bf16_rne(x[e]);
-          lb[e] = f32_to_bf16_rne(x[e] - __uint_as_float(hb[e] << 16));
-        }
-        u32x4_t hw, lw;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hw[e] = hb[2 * e] | (hb[2 * e + 1] << 16);
-          lw[e] = lb[2 * e] | (lb[2 * e + 1] << 16);
-        }
-        qhi[c] = __builtin_bit_cast(bf16x8_t, hw);
-        qlo[c] = __builtin_bit_cast(bf16x8_t, lw);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[c][e] = x[e];
-      }
-    }
-  }
-
-  // ---- value-lane mapping: LPR lanes hold one value row, RPI rows per load
+  // value-lane mapping: LPR lanes hold one value row, RPI rows per load
   const int lpr = rv / EPL;
   const int rpi = 64 / lpr;
   const int vrow = lane / lpr;
   const int vcc = lane - vrow * lpr;
   const bool vact = vrow < rpi;
   const int vi_count = (TR + rpi - 1) / rpi;
+  const int nchk = (rk + KCH - 1) / KCH;  // chunks that carry key features
+
+  u32x4_t kbuf[SUB][NCH];
+  u32x4_t vbuf[VMAX];
+  // Every load is unconditional, from an address clamped into [r0, r1) and
+  // the row's width: rows past r1 get score -inf, features past r_K meet
+  // zero query entries, and value rows past r1 get weight 0, so the clamped
+  // data never contributes (a load under a divergent branch would cost a
+  // full memory round trip each).
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int s = 0; s < SUB; ++s)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int row = min(t0 + 16 * s + n, r1 - 1);
+        const int k0 = min(c * KCH + kg * EPL, rk - EPL);
+        kbuf[s][c] = load16(Kb + ((size_t)row * rk + k0) * Tr::kElemBytes);
+      }
+#pragma unroll
+    for (int i = 0; i < VMAX; ++i) {
+      const int row = min(t0 + i * rpi + vrow, r1 - 1);
+      vbuf[i] = load16(Vb + ((size_t)row * rv + vcc * EPL) * Tr::kElemBytes);
+    }
+  };
+
+  // first tile and the query operand in flight together
+  if (r0 < r1) load_tile(r0);
+  const int rq = latent ? rk : kHeadDim;
+  const float* qsrc = (latent ? a.q_lat : a.q_rot) + ((size_t)b * a.num_q_heads + (size_t)h * G) * rq;
+  bf16x8_t qhi[BF16 ? NCH : 1], qlo[BF16 ? NCH : 1];
+  float qf[BF16 ? 1 : NCH][4];
+  {
+    // A matrix: head m = lane%16, features of k-group kg
+    const int m = lane & 15;
+    f32x4_t qv[NCH][KCH / 16];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int k0 = c * KCH + kg * (KCH / 4);
+      const int mc = min(m, G - 1), kc = min(k0, rq - KCH / 4);
+#pragma unroll
+      for (int e = 0; e < KCH / 16; ++e)
+        qv[c][e] = *reinterpret_cast<const f32x4_t*>(qsrc + (size_t)mc * rq + kc + 4 * e);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const bool ok = m < G && c * KCH + kg * (KCH / 4) < rq;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < KCH / 4; ++e) x[e] = ok ? qv[c][e / 4][e % 4] : 0.0f;
+      if constexpr (BF16) {
+        split_bf16x8(x, qhi[c], qlo[c]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf[c][e] = x[e];
+      }
+    }
+  }
 
   float acc[G][EPL];
 #pragma unroll
@@ -185,32 +521,10 @@ __device__ __forceinline__ void sweep_segment(const SweepArgs& a, const Segment&
     m_run[i] = -INFINITY;
     l_run[i] = 0.0f;
   }
-  float* pw = sh.p[wave];
+  float* pw = sh.u.p[wave];
 
   for (int t0 = r0; t0 < r1; t0 += TR) {
-    // -- issue every load of the tile: keys (MFMA B layout) and values
-    u32x4_t kbuf[SUB][NCH];
-#pragma unroll
-    for (int s = 0; s < SUB; ++s)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int row = t0 + 16 * s + n;
-        const int k0 = c * KCH + kg * EPL;
-        if (row < r1 && k0 < rk)
-          kbuf[s][c] = load16(Kb + ((size_t)row * rk + k0) * Tr::kElemBytes);
-        else
-          kbuf[s][c] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    u32x4_t vbuf[VMAX];
-#pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      const int rt = i * rpi + vrow;
-      const bool ok = i < vi_count && vact && rt < TR && t0 + rt < r1;
-      if (ok)
-        vbuf[i] = load16(Vb + ((size_t)(t0 + rt) * rv + vcc * EPL) * Tr::kElemBytes);
-      else
-        vbuf[i] = u32x4_t{0u, 0u, 0u, 0u};
-    }
+    if (t0 != r0) load_tile(t0);
 
     // -- scores on the matrix cores, log2 units (the query is pre-scaled)
     f32x4_t sc[SUB];
@@ -309,13 +623,13 @@ __device__ __forceinline__ void sweep_segment(const SweepArgs& a, const Segment&
           for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[g], v[e], acc[g][e]);
       }
     }
-    // the next tile overwrites pw: make sure every lane has read it
+    // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- merge the four waves' partials and write this chunk's partial
+  // ---- merge the four waves' partials into this chunk's partial
 #pragma unroll
   for (int i = 0; i < 4; ++i) l_run[i] = row16_sum(l_run[i]);
   if (n == 0) {
@@ -338,69 +652,107 @@ __device__ __forceinline__ void sweep_segment(const SweepArgs& a, const Segment&
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][g][0]);
     const float sw = __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sh.red[wave][lane][e] = acc[g][e] * sw;
+    for (int e = 0; e < EPL; ++e) sh.u.red[wave][lane][e] = acc[g][e] * sw;
     __syncthreads();
     for (int col = tid; col < rv; col += kThreads) {
       const int cc = col / EPL, e = col - (col / EPL) * EPL;
       float sum = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w)
-        for (int r = 0; r < rpi; ++r) sum += sh.red[w][r * lpr + cc][e];
-      acc_out[(size_t)g * kHeadDim + col] = sum;
+        for (int r = 0; r < rpi; ++r) sum += sh.u.red[w][r * lpr + cc][e];
+      store_coherent(&acc_out[(size_t)g * kHeadDim + col], sum);
     }
     if (tid == 0) {
       float L = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][g][0] - M) * sh.ml[w][g][1];
-      ml_out[2 * g] = M;
-      ml_out[2 * g + 1] = L;
+      store_coherent(&ml_out[2 * g], M);
+      store_coherent(&ml_out[2 * g + 1], L);
     }
     __syncthreads();
   }
+
+  // ---- last chunk of the unit merges everything.  Every thread waits for
+  // its coherent partial stores to complete before the barrier; only then
+  // does thread 0 count the chunk as done.  The workgroup that brings the
+  // count to splits_total reads all partials with coherent loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(&a.counters[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.is_last = done == (uint32_t)(a.splits_total - 1);
+  }
+  __syncthreads();
+  if (!sh.is_last) return;
+  merge_unit<G, BF16>(a, unit, b, h, sh);
+  if (tid == 0)  // ready for the next call
+    __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Grid: one workgroup per (unit, chunk); chunk index runs over both segments.
 template <int G, int NCH, bool BF16>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(SweepArgs a) {
-  __shared__ SweepShared sh;
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
   const int unit = blockIdx.x / a.splits_total;
   const int s = blockIdx.x - unit * a.splits_total;
-  const int si = s < a.seg[0].splits ? 0 : 1;
-  const Segment sg = si == 0 ? a.seg[0] : a.seg[1];
-  const int chunk = si == 0 ? s : s - a.seg[0].splits;
+  const bool first = s < a.seg[0].splits;
+  // field-wise select: choosing a whole Segment by value would make the
+  // compiler copy the kernel arguments into scratch memory
+  Segment sg;
+  sg.K = first ? a.seg[0].K : a.seg[1].K;
+  sg.V = first ? a.seg[0].V : a.seg[1].V;
+  sg.kind = first ? a.seg[0].kind : a.seg[1].kind;
+  sg.rows = first ? a.seg[0].rows : a.seg[1].rows;
+  sg.rk = first ? a.seg[0].rk : a.seg[1].rk;
+  sg.rv = first ? a.seg[0].rv : a.seg[1].rv;
+  sg.splits = first ? a.seg[0].splits : a.seg[1].splits;
+  sg.chunk_rows = first ? a.seg[0].chunk_rows : a.seg[1].chunk_rows;
+  const int chunk = first ? s : s - a.seg[0].splits;
   const int c0 = chunk * sg.chunk_rows;
   const int c1 = min(sg.rows, c0 + sg.chunk_rows);
-  // split the chunk over the waves in whole tiles
-  const int tr = sg.kind == kSegFull ? TileShape<BF16, BF16 ? 4 : 8>::kRows
-                                     : TileShape<BF16, NCH>::kRows;
+  constexpr int kFullNch = BF16 ? 4 : 8;
+  const int tr = sg.kind == kSegFull ? TileShape<BF16, kFullNch>::kRows : TileShape<BF16, NCH>::kRows;
   const int per_wave = ((c1 - c0 + kWaves - 1) / kWaves + tr - 1) / tr * tr;
   const int wave = threadIdx.x >> 6;
   const int r0 = min(c1, c0 + wave * per_wave);
   const int r1 = min(c1, r0 + per_wave);
   const int slot = unit * a.splits_total + s;
   if (sg.kind == kSegFull)
-    sweep_segment<G, BF16 ? 4 : 8, BF16>(a, sg, unit, slot, r0, r1, sh);
+    attend_chunk<G, kFullNch, BF16>(a, sg, unit, slot, r0, r1, sh);
   else
-    sweep_segment<G, NCH, BF16>(a, sg, unit, slot, r0, r1, sh);
+    attend_chunk<G, NCH, BF16>(a, sg, unit, slot, r0, r1, sh);
 }
 
-// Launch the sweep for group size G; nch is the MFMA chunk count of the
-// latent segment (1..4 for bf16; fp32 always uses 8).
+// Launch for group size G; nch is the MFMA chunk count of the latent
+// segment (1..4 for bf16; fp32 always uses 8).
 template <int G>
-hipError_t launch_sweep_group(const SweepArgs& a, int dtype, int nch, hipStream_t s) {
+hipError_t launch_attention_group(const AttnArgs& a, int dtype, int nch, hipStream_t s,
+                                  hipEvent_t ev0, hipEvent_t ev1) {
+  const dim3 pgrid((unsigned)(a.batch * a.num_kv_heads));
   const dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.splits_total));
   const dim3 block(kThreads);
+  if (dtype == 0)
+    hipLaunchKernelGGL((prologue_kernel<G, false>), pgrid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((prologue_kernel<G, true>), pgrid, block, 0, s, a);
+  if (ev0) {
+    const hipError_t e = hipEventRecord(ev0, s);
+    if (e != hipSuccess) return e;
+  }
   if (dtype == 0) {
-    hipLaunchKernelGGL((sweep_kernel<G, 8, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((attention_kernel<G, 8, false>), grid, block, 0, s, a);
   } else {
     switch (nch) {
-      case 1: hipLaunchKernelGGL((sweep_kernel<G, 1, true>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((sweep_kernel<G, 2, true>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((sweep_kernel<G, 3, true>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((sweep_kernel<G, 4, true>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((attention_kernel<G, 1, true>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((attention_kernel<G, 2, true>), grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL((attention_kernel<G, 3, true>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((attention_kernel<G, 4, true>), grid, block, 0, s, a); break;
     }
   }
-  return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err == hipSuccess && ev1) return hipEventRecord(ev1, s);
+  return err;
 }
 
 }  // namespace slimkv
