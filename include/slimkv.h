@@ -96,8 +96,8 @@ typedef struct slimkv_problem {
   float scale;          /* softmax scale, finite and > 0 (e.g. 1/sqrt(d))   */
   int32_t dtype;        /* slimkv_dtype of q, U_K, U_V, C_K, C_V, K, V       */
   double rope_theta;    /* rotary base, finite and > 1                       */
-  int32_t num_splits;   /* 0: library picks; > 0: row chunks per segment of
-                           each (b, kv head), clipped to what the rows allow */
+  int32_t num_splits;   /* 0: library picks; > 0: equal-byte chunks each
+                           (b, kv head)'s rows are cut into (at most 64)    */
   int32_t reserved;     /* must be 0                                         */
 } slimkv_problem;
 

@@ -34,8 +34,6 @@ slimkv_status fail(slimkv_status st, const char* fmt, ...) {
 constexpr int64_t kMaxRows = int64_t(1) << 24;    // rows per unit and segment
 constexpr int64_t kMaxUnits = int64_t(1) << 20;   // batch * kv heads
 constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
-constexpr int kTargetBlocks = 2048;               // attention workgroups to aim for
-constexpr int64_t kMinChunkBytes = 32 << 10;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -90,25 +88,6 @@ slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
   return SLIMKV_OK;
 }
 
-// Chunking of one segment: enough row chunks to fill the GPU, each a whole
-// number of tiles, none empty.
-void plan_segment(Segment& sg, int dtype, int64_t units, int64_t chunk_bytes, int forced) {
-  const int tr = tile_rows(dtype, sg.rk, sg.rv);
-  const int64_t max_chunks = std::min<int64_t>(ceil_div(sg.rows, tr), kMaxSplits);
-  int64_t want;
-  if (forced > 0) {
-    want = forced;
-  } else {
-    const int64_t bytes = (int64_t)sg.rows * (sg.rk + sg.rv) * (dtype == 0 ? 4 : 2);
-    want = ceil_div(bytes, chunk_bytes);
-  }
-  want = std::max<int64_t>(1, std::min(want, max_chunks));
-  int64_t chunk = ceil_div(ceil_div(sg.rows, want), tr) * tr;
-  sg.chunk_rows = (int32_t)chunk;
-  sg.splits = (int32_t)ceil_div(sg.rows, chunk);
-  (void)units;
-}
-
 slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   slimkv_status st = check_problem(p, op);
   if (st != SLIMKV_OK) return st;
@@ -122,52 +101,36 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   a.num_kv_heads = p->num_kv_heads;
   a.group = p->num_q_heads / p->num_kv_heads;
 
-  int ns = 0;
-  if (p->num_beacons > 0) {
-    Segment& s = a.seg[ns++];
-    s.rows = p->num_beacons;
-    if (op == SLIMKV_OP_LATENT) {
-      s.kind = kSegLatent;
-      s.rk = p->rank_k;
-      s.rv = p->rank_v;
-    } else {
-      s.kind = kSegFull;
-      s.rk = s.rv = kHeadDim;
-    }
+  // seg[0]: beacon rows (latent, or rebuilt at full width); seg[1]: raw rows.
+  // An absent segment has rows = 0.
+  Segment& sb = a.seg[0];
+  sb.rows = p->num_beacons;
+  if (op == SLIMKV_OP_LATENT && p->num_beacons > 0) {
+    sb.kind = kSegLatent;
+    sb.rk = p->rank_k;
+    sb.rv = p->rank_v;
+  } else {
+    sb.kind = kSegFull;
+    sb.rk = sb.rv = kHeadDim;
   }
-  if (p->raw_window > 0) {
-    Segment& s = a.seg[ns++];
-    s.kind = kSegFull;
-    s.rows = p->raw_window;
-    s.rk = s.rv = kHeadDim;
+  Segment& sr = a.seg[1];
+  sr.kind = kSegFull;
+  sr.rows = p->raw_window;
+  sr.rk = sr.rv = kHeadDim;
+  for (Segment* sg : {&sb, &sr}) {
+    sg->row_bytes = (sg->rk + sg->rv) * pl.elem;
+    sg->tile = tile_rows(pl.dtype, sg->rk, sg->rv);
   }
-  a.nseg = ns;
-
-  // chunk size: about kTargetBlocks workgroups over the whole call, and at
-  // most kMaxMergeSlots / G chunks per unit so one workgroup can merge them
-  int64_t unit_bytes = 0;
-  for (int i = 0; i < ns; ++i) unit_bytes += (int64_t)a.seg[i].rows * (a.seg[i].rk + a.seg[i].rv) * pl.elem;
-  const int64_t total_bytes = unit_bytes * pl.units;
-  const int64_t max_unit_splits = kMaxMergeSlots / a.group;
-  int64_t chunk_bytes = std::max(kMinChunkBytes, ceil_div(total_bytes, kTargetBlocks));
-  int forced = p->num_splits;
-  if (forced > 0) forced = (int)std::min<int64_t>(forced, max_unit_splits / ns);
-  for (;;) {
-    for (int i = 0; i < ns; ++i) plan_segment(a.seg[i], pl.dtype, pl.units, chunk_bytes, forced);
-    a.splits_total = a.seg[0].splits + (ns > 1 ? a.seg[1].splits : 0);
-    if (a.splits_total <= max_unit_splits) break;
-    chunk_bytes *= 2;
-  }
-  if (pl.units * a.splits_total > (int64_t)INT32_MAX)
+  a.unit_bytes = (int64_t)sb.rows * sb.row_bytes + (int64_t)sr.rows * sr.row_bytes;
+  a.chunks = p->num_splits > 0 ? std::min(p->num_splits, kMaxChunks) : 0;  // 0: launcher picks
+  if (pl.units * kMaxChunks > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
-
-  a.latent_splits = a.seg[0].kind == kSegLatent && ns > 0 ? a.seg[0].splits : 0;
-  a.rank_v = a.latent_splits > 0 ? p->rank_v : 0;
-  a.rank_k = a.latent_splits > 0 ? p->rank_k : 0;
+  a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
+  a.rank_k = sb.kind == kSegLatent ? p->rank_k : 0;
 
   // workspace layout: per-unit counters (must start zeroed), the prologue's
-  // queries, then the chunk partials
-  const int64_t G = a.group;
+  // queries, then two partial slots per chunk for up to kMaxChunks chunks
+  const int64_t G = a.group, slots = 2 * kMaxChunks;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);
   pl.off_q_rot = off;
@@ -175,9 +138,9 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   pl.off_q_lat = off;
   if (a.rank_k > 0) off = round_up(off + (size_t)p->batch * p->num_q_heads * a.rank_k * sizeof(float), kAlign);
   pl.off_ml = off;
-  off = round_up(off + (size_t)(pl.units * a.splits_total * G * 2) * sizeof(float), kAlign);
+  off = round_up(off + (size_t)(pl.units * slots * G * 2) * sizeof(float), kAlign);
   pl.off_acc = off;
-  off = round_up(off + (size_t)(pl.units * a.splits_total * G * kHeadDim) * sizeof(float), kAlign);
+  off = round_up(off + (size_t)(pl.units * slots * G * kHeadDim) * sizeof(float), kAlign);
   pl.off_kb = pl.off_vb = off;
   if (op == SLIMKV_OP_RECONSTRUCT && p->num_beacons > 0) {
     const size_t rebuilt = (size_t)pl.units * p->num_beacons * kHeadDim * pl.elem;
@@ -293,21 +256,13 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
   a.out = out;
   a.lse = lse;
-  int si = 0;
   if (beacons) {
-    Segment& sg = a.seg[si++];
-    if (op == SLIMKV_OP_LATENT) {
-      sg.K = C_K;
-      sg.V = C_V;
-    } else {
-      sg.K = wsb + pl.off_kb;
-      sg.V = wsb + pl.off_vb;
-    }
+    a.seg[0].K = op == SLIMKV_OP_LATENT ? C_K : wsb + pl.off_kb;
+    a.seg[0].V = op == SLIMKV_OP_LATENT ? C_V : wsb + pl.off_vb;
   }
   if (raw) {
-    Segment& sg = a.seg[si++];
-    sg.K = K_raw;
-    sg.V = V_raw;
+    a.seg[1].K = K_raw;
+    a.seg[1].V = V_raw;
   }
 
   hipError_t err = hipSuccess;

@@ -2,6 +2,10 @@
 // comparison path, the tile-height rule, and the attention dispatcher.
 #include <math.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "internal.h"
 
 namespace slimkv {
@@ -112,19 +116,55 @@ hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attention_g1(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g2(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g3(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g4(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g5(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g6(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g7(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
-hipError_t launch_attention_g8(const AttnArgs&, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+int choose_chunks(int64_t units, int64_t unit_bytes, int64_t slots, int64_t min_chunk_bytes) {
+  int best = 1;
+  double best_fill = -1.0;
+  for (int k = 1; k <= kMaxChunks; ++k) {
+    if (k > 1 && unit_bytes / k < min_chunk_bytes) break;
+    const int64_t wgs = units * k;
+    const int64_t rounds = (wgs + slots - 1) / slots;
+    const double fill = (double)wgs / (double)(rounds * slots);
+    if (fill > best_fill + 1e-9) {  // ties keep the smaller k
+      best = k;
+      best_fill = fill;
+    }
+  }
+  return best;
+}
 
-hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev0,
-                            hipEvent_t ev1) {
+int device_slots(const void* kfn) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const std::pair<int, const void*> key(dev, kfn);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, kThreads, 0) != hipSuccess)
+    return -1;
+  const int slots = cus * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = slots;
+  return slots;
+}
+
+hipError_t launch_attention_g1(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g2(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g3(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g4(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g5(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g6(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g7(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_attention_g8(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
+
+hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   int nch = 4;
-  if (a.seg[0].kind == kSegLatent) {
+  if (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0) {
     nch = (a.seg[0].rk + 31) / 32;
     const int nv = (a.seg[0].rv + 31) / 32;
     if (nv > nch) nch = nv;

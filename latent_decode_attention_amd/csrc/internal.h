@@ -12,8 +12,8 @@ constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
-constexpr int kMaxSplits = 4096;       // row chunks per segment per unit
-constexpr int kMaxMergeSlots = 2048;   // splits_total * G a unit's merge holds in LDS
+constexpr int kMaxChunks = 64;         // row chunks per unit (each writes 2 partial slots)
+constexpr int kMaxMergeSlots = 2048;   // 2 * kMaxChunks * G, held in LDS by a unit's merge
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -26,21 +26,23 @@ struct Segment {
   const void* K;       // [B, H_kv, rows, rk]
   const void* V;       // [B, H_kv, rows, rv]
   int32_t kind;        // SegKind
-  int32_t rows;        // rows per unit
+  int32_t rows;        // rows per unit (0: the segment is absent)
   int32_t rk, rv;      // row widths in elements (d for kSegFull)
-  int32_t splits;      // chunks per unit
-  int32_t chunk_rows;  // rows per chunk (multiple of the tile height)
+  int32_t row_bytes;   // (rk + rv) * element bytes
+  int32_t tile;        // tile height (rows) the segment is swept in
 };
 
-// Everything the attention kernel reads.  One workgroup per (unit, chunk);
-// the last workgroup of a unit to finish merges the unit's chunks.
+// Everything the attention kernel reads.  seg[0] holds each unit's beacon
+// rows, seg[1] its full-width raw rows; a unit's byte stream (beacons, then
+// raw rows) is cut into `chunks` equal pieces, one workgroup each.  A chunk
+// writes two partial slots, 2c (its beacon rows) and 2c+1 (its raw rows),
+// empty ones included; the last workgroup of a unit merges all slots.
 struct AttnArgs {
   Segment seg[2];
-  int32_t nseg;
   int32_t batch, num_q_heads, num_kv_heads, group;
-  int32_t splits_total;   // seg[0].splits + seg[1].splits
-  int32_t latent_splits;  // leading chunks whose sums are r_V-wide latents
-  int32_t rank_v;         // r_V of the latent segment (0 if none)
+  int32_t chunks;         // chunks per unit (grid = units * chunks)
+  int64_t unit_bytes;     // cache bytes per unit over both segments
+  int32_t rank_v;         // r_V of a latent beacon segment (0 if none)
   const void* q;          // [B, H_q, d] before rotation
   const int32_t* q_pos;   // [B]
   const void* U_K;        // [H_kv, d, r_K] (latent segment only)
@@ -51,8 +53,8 @@ struct AttnArgs {
   float* q_lat;           // [B, H_q, r_K] latent query, pre-scaled (latent segment only)
   int32_t rank_k;         // r_K of the latent segment (0 if none)
   uint32_t* counters;     // [units] finished-chunk counters (zero between calls)
-  float* part_ml;         // [units, splits_total, G, 2]  (max, sum of exp)
-  float* part_acc;        // [units, splits_total, G, d]  exp-weighted value sums
+  float* part_ml;         // [units, 2 * chunks, G, 2]  (max, sum of exp)
+  float* part_acc;        // [units, 2 * chunks, G, d]  exp-weighted value sums
   float* out;             // [B, H_q, d]
   float* lse;             // [B, H_q] or null
 };
@@ -66,8 +68,14 @@ struct RebuildArgs {
 
 // Host launchers (defined in the .hip files).  dtype: 0 fp32, 1 bf16.
 // Prologue kernel, then the attention kernel (bracketed by ev0/ev1 if set).
-hipError_t launch_attention(const AttnArgs& a, int dtype, hipStream_t s, hipEvent_t ev0,
+// a.chunks <= 0 lets the launcher pick the chunk count from the device's
+// workgroup slots (CUs x resident workgroups of the chosen kernel).
+hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0,
                             hipEvent_t ev1);
+
+// Chunks per unit: the count in [1, kMaxChunks] whose workgroups fill the
+// device's slots best (no chunk under min_chunk_bytes).
+int choose_chunks(int64_t units, int64_t unit_bytes, int64_t slots, int64_t min_chunk_bytes);
 hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s);
 
 // Tile height (rows) a segment of the given widths is swept in.

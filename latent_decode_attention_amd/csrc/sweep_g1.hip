@@ -2,7 +2,7 @@
 #include "sweep_impl.h"
 
 namespace slimkv {
-hipError_t launch_attention_g1(const AttnArgs& a, int dtype, int nch, hipStream_t s,
+hipError_t launch_attention_g1(AttnArgs a, int dtype, int nch, hipStream_t s,
                                  hipEvent_t ev0, hipEvent_t ev1) {
   return launch_attention_group<1>(a, dtype, nch, s, ev0, ev1);
 }

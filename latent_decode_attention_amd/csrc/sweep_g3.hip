@@ -2,7 +2,7 @@
 #include "sweep_impl.h"
 
 namespace slimkv {
-hipError_t launch_attention_g3(const AttnArgs& a, int dtype, int nch, hipStream_t s,
+hipError_t launch_attention_g3(AttnArgs a, int dtype, int nch, hipStream_t s,
                                  hipEvent_t ev0, hipEvent_t ev1) {
   return launch_attention_group<3>(a, dtype, nch, s, ev0, ev1);
 }

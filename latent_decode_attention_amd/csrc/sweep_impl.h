@@ -138,8 +138,8 @@ struct TileShape {
 
 struct alignas(16) AttnShared {
   union {
-    float p[kWaves][64 * 8];   // exp-weights of the current tile, per wave
-    float red[kWaves][64][8];  // per-head merge of the waves' value sums
+    float p[kWaves][64 * 8];                 // exp-weights of the current tile, per wave
+    float red[kWaves][kMaxGroup][kHeadDim];  // each wave's rescaled value sums
     struct {
       float ml[kMaxMergeSlots][2];  // every chunk's (max, sum); then weights
       float olat[kMaxGroup][kHeadDim];
@@ -258,7 +258,8 @@ template <int G, bool BF16>
 __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h,
                                            AttnShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = a.splits_total, rv = a.rank_v;
+  const int S = 2 * a.chunks, rv = a.rank_v;
+  const bool lat_beacons = a.seg[0].kind == kSegLatent;
   const float* ml = a.part_ml + (size_t)unit * S * G * 2;
   const float* acc = a.part_acc + (size_t)unit * S * G * kHeadDim;
   float (*sml)[2] = sh.u.comb.ml;
@@ -278,8 +279,8 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
       for (int c = 0; c < 4; ++c) {
         const int i = 16 * (wave + kWaves * t) + m16, k0 = 32 * c + 8 * kg;
         // features past r_V are multiplied by zero latent entries below
-        uw[t][c] = a.latent_splits > 0 ? load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2)
-                                       : u32x4_t{0u, 0u, 0u, 0u};
+        uw[t][c] = lat_beacons ? load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2)
+                               : u32x4_t{0u, 0u, 0u, 0u};
       }
   }
   // (unconditional loads from clamped indexes; out-of-range values unused)
@@ -345,10 +346,12 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
           if (p < G * kHeadDim) {
             const int g = p / kHeadDim, col = p % kHeadDim;
             const float w = sml[s * G + g][0];
-            if (s < a.latent_splits) {
-              if (col < rv) lat[j] = fmaf(w, v[u][j], lat[j]);
+            // empty slots carry weight 0 and stale sums: skip, don't multiply
+            const float wv = w != 0.0f ? w * v[u][j] : 0.0f;
+            if ((s & 1) == 0 && lat_beacons) {
+              if (col < rv) lat[j] += wv;
             } else {
-              full[j] = fmaf(w, v[u][j], full[j]);
+              full[j] += wv;
             }
           }
         }
@@ -367,7 +370,7 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 
   // -- lift the latent sum once and add the full-width sum
   float* out = a.out + ((size_t)b * a.num_q_heads + (size_t)h * G) * kHeadDim;
-  if (a.latent_splits > 0) {
+  if (lat_beacons) {
     // out^T[i][g] = sum_k U_V[i][k] olat[g][k]: D[m=i][n=g] over 16-row tiles of i
     const int n = lane & 15;
 #pragma unroll
@@ -416,11 +419,12 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 }
 
 // ---------------------------------------------------------------------------
-// Sweep rows [r0, r1) of one unit's segment, write the chunk's partial, and
-// merge the unit if this is its last chunk.
+// Sweep rows [p0, p1) of one unit's segment with the whole workgroup (each
+// wave a contiguous, tile-aligned sub-range) and write the piece's partial
+// to `slot` (an empty piece writes the neutral partial: max -inf, sum 0).
 template <int G, int NCH, bool BF16>
-__device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& sg, int unit,
-                                             int slot, int r0, int r1, AttnShared& sh) {
+__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& sg, int unit,
+                                             int slot, int p0, int p1, AttnShared& sh) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
@@ -437,6 +441,20 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
   const int n = lane & 15;   // MFMA column (cache row) within a subtile
   const int kg = lane >> 4;  // MFMA k-group / output row group
 
+  float* ml_out = a.part_ml + (size_t)slot * G * 2;
+  float* acc_out = a.part_acc + (size_t)slot * G * kHeadDim;
+  if (p0 >= p1) {
+    if (tid < G) {
+      store_coherent(&ml_out[2 * tid], -INFINITY);
+      store_coherent(&ml_out[2 * tid + 1], 0.0f);
+    }
+    return;
+  }
+  // this wave's rows: the piece split into four tile-aligned runs
+  const int per_wave = ((p1 - p0 + kWaves - 1) / kWaves + TR - 1) / TR * TR;
+  const int r0 = min(p1, p0 + wave * per_wave);
+  const int r1 = min(p1, r0 + per_wave);
+
   const int rk = sg.rk, rv = sg.rv;
   const bool latent = sg.kind == kSegLatent;
   const int b = unit / a.num_kv_heads;
@@ -445,12 +463,15 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
   const char* Kb = static_cast<const char*>(sg.K) + urow * rk * Tr::kElemBytes;
   const char* Vb = static_cast<const char*>(sg.V) + urow * rv * Tr::kElemBytes;
 
-  // value-lane mapping: LPR lanes hold one value row, RPI rows per load
-  const int lpr = rv / EPL;
+  // value-lane mapping: a value row spans rv/EPL lanes, padded to a power of
+  // two (LPR) so the row groups can be summed by a butterfly; RPI rows per load
+  const int lanes_row = rv / EPL;
+  const int lpr = 1 << (32 - __builtin_clz(lanes_row - 1));
   const int rpi = 64 / lpr;
   const int vrow = lane / lpr;
-  const int vcc = lane - vrow * lpr;
-  const bool vact = vrow < rpi;
+  const int vcc = lane & (lpr - 1);
+  const bool vact = vcc < lanes_row;
+  const int vcol = min(vcc, lanes_row - 1) * EPL;  // clamped for idle lanes
   const int vi_count = (TR + rpi - 1) / rpi;
   const int nchk = (rk + KCH - 1) / KCH;  // chunks that carry key features
 
@@ -473,7 +494,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
 #pragma unroll
     for (int i = 0; i < VMAX; ++i) {
       const int row = min(t0 + i * rpi + vrow, r1 - 1);
-      vbuf[i] = load16(Vb + ((size_t)row * rv + vcc * EPL) * Tr::kElemBytes);
+      vbuf[i] = load16(Vb + ((size_t)row * rv + vcol) * Tr::kElemBytes);
     }
   };
 
@@ -630,6 +651,20 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
   }
 
   // ---- merge the four waves' partials into this chunk's partial
+  // (1) per wave: sum the row groups (lanes with equal vcc) by a butterfly:
+  //     DPP rotations inside 16-lane rows, lane swaps across rows
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = acc[g][e];
+      if (lpr <= 8) x += dpp_f<0x128>(x);
+      if (lpr <= 4) x += dpp_f<0x124>(x);
+      if (lpr <= 2) x += dpp_f<0x122>(x);
+      if (lpr <= 16) x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[g][e] = x;
+    }
 #pragma unroll
   for (int i = 0; i < 4; ++i) l_run[i] = row16_sum(l_run[i]);
   if (n == 0) {
@@ -643,45 +678,105 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
     }
   }
   __syncthreads();
-  float* ml_out = a.part_ml + (size_t)slot * G * 2;
-  float* acc_out = a.part_acc + (size_t)slot * G * kHeadDim;
+  // (2) each wave rescales its sums to the workgroup max and parks them in LDS
+  if (vrow == 0 && vact) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float M = sh.ml[0][g][0];
+    for (int g = 0; g < G; ++g) {
+      float M = sh.ml[0][g][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][g][0]);
-    const float sw = __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][g][0]);
+      const float sw = __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) sh.u.red[wave][lane][e] = acc[g][e] * sw;
-    __syncthreads();
-    for (int col = tid; col < rv; col += kThreads) {
-      const int cc = col / EPL, e = col - (col / EPL) * EPL;
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        for (int r = 0; r < rpi; ++r) sum += sh.u.red[w][r * lpr + cc][e];
-      store_coherent(&acc_out[(size_t)g * kHeadDim + col], sum);
+      for (int e = 0; e < EPL; ++e) sh.u.red[wave][g][vcc * EPL + e] = acc[g][e] * sw;
     }
-    if (tid == 0) {
-      float L = 0.0f;
+  }
+  __syncthreads();
+  // (3) sum the four waves, write the piece's partial with coherent stores
+  for (int p = tid; p < G * rv; p += kThreads) {
+    const int g = p / rv, col = p - (p / rv) * rv;
+    float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][g][0] - M) * sh.ml[w][g][1];
-      store_coherent(&ml_out[2 * g], M);
-      store_coherent(&ml_out[2 * g + 1], L);
-    }
-    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) sum += sh.u.red[w][g][col];
+    store_coherent(&acc_out[(size_t)g * kHeadDim + col], sum);
+  }
+  if (tid < G) {
+    float M = sh.ml[0][tid][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][tid][0]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][tid][0] - M) * sh.ml[w][tid][1];
+    store_coherent(&ml_out[2 * tid], M);
+    store_coherent(&ml_out[2 * tid + 1], L);
   }
 
-  // ---- last chunk of the unit merges everything.  Every thread waits for
-  // its coherent partial stores to complete before the barrier; only then
-  // does thread 0 count the chunk as done.  The workgroup that brings the
-  // count to splits_total reads all partials with coherent loads.
+}
+
+// Position of byte `off` of a unit's stream in unified row space (beacon
+// rows first, then raw rows), rounded down to a tile boundary.
+__device__ __forceinline__ int stream_row(const AttnArgs& a, int64_t off) {
+  const int64_t bb = (int64_t)a.seg[0].rows * a.seg[0].row_bytes;
+  if (off < bb) {
+    const int r = (int)(off / a.seg[0].row_bytes);
+    return r - r % a.seg[0].tile;
+  }
+  const int r = (int)((off - bb) / a.seg[1].row_bytes);
+  return a.seg[0].rows + r - r % a.seg[1].tile;
+}
+
+// Grid: one workgroup per (unit, chunk).  Chunk c covers bytes
+// [c T / k, (c+1) T / k) of the unit's stream (T bytes, k chunks): its beacon
+// rows go to slot 2c, its raw rows to slot 2c+1.  The workgroup that
+// finishes a unit's last chunk merges the unit.
+template <int G, int NCH, bool BF16>
+__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
+  const int tid = threadIdx.x;
+  const int k = a.chunks;
+  const int unit = blockIdx.x / k;
+  const int c = blockIdx.x - unit * k;
+  const int b = unit / a.num_kv_heads;
+  const int h = unit - b * a.num_kv_heads;
+  const int nb = a.seg[0].rows;
+  const int R0 = c == 0 ? 0 : stream_row(a, a.unit_bytes * c / k);
+  const int R1 = c == k - 1 ? nb + a.seg[1].rows : stream_row(a, a.unit_bytes * (c + 1) / k);
+  const size_t slot0 = ((size_t)unit * k + c) * 2;
+  constexpr int kFullNch = BF16 ? 4 : 8;
+
+  // beacon rows of this chunk (latent, or rebuilt full-width rows)
+  Segment sg;
+  sg.K = a.seg[0].K;
+  sg.V = a.seg[0].V;
+  sg.kind = a.seg[0].kind;
+  sg.rows = nb;
+  sg.rk = a.seg[0].rk;
+  sg.rv = a.seg[0].rv;
+  if (sg.kind == kSegLatent)
+    attend_piece<G, NCH, BF16>(a, sg, unit, (int)slot0, min(R0, nb), min(R1, nb), sh);
+  else
+    attend_piece<G, kFullNch, BF16>(a, sg, unit, (int)slot0, min(R0, nb), min(R1, nb), sh);
+  __syncthreads();  // LDS is reused by the next piece
+
+  // raw rows of this chunk
+  sg.K = a.seg[1].K;
+  sg.V = a.seg[1].V;
+  sg.kind = kSegFull;
+  sg.rows = a.seg[1].rows;
+  sg.rk = kHeadDim;
+  sg.rv = kHeadDim;
+  attend_piece<G, kFullNch, BF16>(a, sg, unit, (int)slot0 + 1, max(R0, nb) - nb,
+                                  max(R1, nb) - nb, sh);
+
+  // ---- the last chunk of the unit merges everything.  Every thread waits
+  // for its coherent partial stores to complete before the barrier; only
+  // then does thread 0 count the chunk as done.  The workgroup that brings
+  // the count to k reads all partials with coherent loads.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
     const uint32_t done =
         __hip_atomic_fetch_add(&a.counters[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.is_last = done == (uint32_t)(a.splits_total - 1);
+    sh.is_last = done == (uint32_t)(k - 1);
   }
   __syncthreads();
   if (!sh.is_last) return;
@@ -690,48 +785,33 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const Segment& s
     __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Grid: one workgroup per (unit, chunk); chunk index runs over both segments.
-template <int G, int NCH, bool BF16>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
-  __shared__ AttnShared sh;
-  const int unit = blockIdx.x / a.splits_total;
-  const int s = blockIdx.x - unit * a.splits_total;
-  const bool first = s < a.seg[0].splits;
-  // field-wise select: choosing a whole Segment by value would make the
-  // compiler copy the kernel arguments into scratch memory
-  Segment sg;
-  sg.K = first ? a.seg[0].K : a.seg[1].K;
-  sg.V = first ? a.seg[0].V : a.seg[1].V;
-  sg.kind = first ? a.seg[0].kind : a.seg[1].kind;
-  sg.rows = first ? a.seg[0].rows : a.seg[1].rows;
-  sg.rk = first ? a.seg[0].rk : a.seg[1].rk;
-  sg.rv = first ? a.seg[0].rv : a.seg[1].rv;
-  sg.splits = first ? a.seg[0].splits : a.seg[1].splits;
-  sg.chunk_rows = first ? a.seg[0].chunk_rows : a.seg[1].chunk_rows;
-  const int chunk = first ? s : s - a.seg[0].splits;
-  const int c0 = chunk * sg.chunk_rows;
-  const int c1 = min(sg.rows, c0 + sg.chunk_rows);
-  constexpr int kFullNch = BF16 ? 4 : 8;
-  const int tr = sg.kind == kSegFull ? TileShape<BF16, kFullNch>::kRows : TileShape<BF16, NCH>::kRows;
-  const int per_wave = ((c1 - c0 + kWaves - 1) / kWaves + tr - 1) / tr * tr;
-  const int wave = threadIdx.x >> 6;
-  const int r0 = min(c1, c0 + wave * per_wave);
-  const int r1 = min(c1, r0 + per_wave);
-  const int slot = unit * a.splits_total + s;
-  if (sg.kind == kSegFull)
-    attend_chunk<G, kFullNch, BF16>(a, sg, unit, slot, r0, r1, sh);
-  else
-    attend_chunk<G, NCH, BF16>(a, sg, unit, slot, r0, r1, sh);
-}
+// Workgroups of `kfn` resident per CU and the CU count of the current
+// device, cached per (device, kernel).
+int device_slots(const void* kfn);
 
 // Launch for group size G; nch is the MFMA chunk count of the latent
 // segment (1..4 for bf16; fp32 always uses 8).
 template <int G>
-hipError_t launch_attention_group(const AttnArgs& a, int dtype, int nch, hipStream_t s,
-                                  hipEvent_t ev0, hipEvent_t ev1) {
-  const dim3 pgrid((unsigned)(a.batch * a.num_kv_heads));
-  const dim3 grid((unsigned)(a.batch * a.num_kv_heads * a.splits_total));
-  const dim3 block(kThreads);
+hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s, hipEvent_t ev0,
+                                  hipEvent_t ev1) {
+  const void* kfn;
+  if (dtype == 0) {
+    kfn = reinterpret_cast<const void*>(&attention_kernel<G, 8, false>);
+  } else {
+    switch (nch) {
+      case 1: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 1, true>); break;
+      case 2: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 2, true>); break;
+      case 3: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 3, true>); break;
+      default: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 4, true>); break;
+    }
+  }
+  const int64_t units = (int64_t)a.batch * a.num_kv_heads;
+  if (a.chunks <= 0) {
+    const int slots = device_slots(kfn);
+    if (slots <= 0) return hipErrorInvalidDeviceFunction;
+    a.chunks = choose_chunks(units, a.unit_bytes, slots, 64 << 10);
+  }
+  const dim3 pgrid((unsigned)units), grid((unsigned)(units * a.chunks)), block(kThreads);
   if (dtype == 0)
     hipLaunchKernelGGL((prologue_kernel<G, false>), pgrid, block, 0, s, a);
   else
@@ -740,17 +820,9 @@ hipError_t launch_attention_group(const AttnArgs& a, int dtype, int nch, hipStre
     const hipError_t e = hipEventRecord(ev0, s);
     if (e != hipSuccess) return e;
   }
-  if (dtype == 0) {
-    hipLaunchKernelGGL((attention_kernel<G, 8, false>), grid, block, 0, s, a);
-  } else {
-    switch (nch) {
-      case 1: hipLaunchKernelGGL((attention_kernel<G, 1, true>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((attention_kernel<G, 2, true>), grid, block, 0, s, a); break;
-      case 3: hipLaunchKernelGGL((attention_kernel<G, 3, true>), grid, block, 0, s, a); break;
-      default: hipLaunchKernelGGL((attention_kernel<G, 4, true>), grid, block, 0, s, a); break;
-    }
-  }
-  const hipError_t err = hipGetLastError();
+  void* args[] = {&a};
+  hipError_t err = hipLaunchKernel(kfn, grid, block, args, 0, s);
+  if (err == hipSuccess) err = hipGetLastError();
   if (err == hipSuccess && ev1) return hipEventRecord(ev1, s);
   return err;
 }

@@ -166,7 +166,8 @@ def test_workspace_bytes_by_op(lib):
     assert lib.slimkv_workspace_bytes(None, 0) == 0
 
 
-def test_split_override_changes_workspace(lib):
-    a = lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=1)), 0)
-    b = lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=4)), 0)
-    assert b > a
+def test_workspace_does_not_depend_on_split_choice(lib):
+    # sized for the largest chunk count, so one workspace serves any split
+    sizes = {lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=s)), 0)
+             for s in (0, 1, 4, 64, 1000)}
+    assert len(sizes) == 1
