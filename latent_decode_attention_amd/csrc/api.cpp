@@ -43,7 +43,7 @@ struct Plan {
   int64_t units;
   int dtype;
   int elem;
-  size_t off_counters, off_q_rot, off_q_lat, off_ml, off_acc, off_kb, off_vb, total;
+  size_t off_counters, off_ml, off_acc, off_kb, off_vb, total;
 };
 
 bool rank_ok(int r) { return r >= 16 && r <= kHeadDim && r % 16 == 0; }
@@ -128,15 +128,11 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
   a.rank_k = sb.kind == kSegLatent ? p->rank_k : 0;
 
-  // workspace layout: per-unit counters (must start zeroed), the prologue's
-  // queries, then two partial slots per chunk for up to kMaxChunks chunks
+  // workspace layout: per-unit counters (must start zeroed), then two
+  // partial slots per chunk for up to kMaxChunks chunks
   const int64_t G = a.group, slots = 2 * kMaxChunks;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);
-  pl.off_q_rot = off;
-  off = round_up(off + (size_t)p->batch * p->num_q_heads * kHeadDim * sizeof(float), kAlign);
-  pl.off_q_lat = off;
-  if (a.rank_k > 0) off = round_up(off + (size_t)p->batch * p->num_q_heads * a.rank_k * sizeof(float), kAlign);
   pl.off_ml = off;
   off = round_up(off + (size_t)(pl.units * slots * G * 2) * sizeof(float), kAlign);
   pl.off_acc = off;
@@ -250,8 +246,6 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   a.log2_theta = log2(p->rope_theta);
   a.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
   a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
-  a.q_rot = reinterpret_cast<float*>(wsb + pl.off_q_rot);
-  a.q_lat = a.rank_k > 0 ? reinterpret_cast<float*>(wsb + pl.off_q_lat) : nullptr;
   a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
   a.out = out;

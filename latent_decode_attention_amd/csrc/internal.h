@@ -49,9 +49,7 @@ struct AttnArgs {
   const void* U_V;        // [H_kv, d, r_V] (latent segment only)
   double score_scale;     // scale * log2(e): scores are kept in log2 units
   double log2_theta;      // log2(rope theta), computed on the host in fp64
-  float* q_rot;           // [B, H_q, d] rotated query, pre-scaled (written by the prologue)
-  float* q_lat;           // [B, H_q, r_K] latent query, pre-scaled (latent segment only)
-  int32_t rank_k;         // r_K of the latent segment (0 if none)
+  int32_t rank_k;         // r_K of a latent beacon segment (0 if none)
   uint32_t* counters;     // [units] finished-chunk counters (zero between calls)
   float* part_ml;         // [units, 2 * chunks, G, 2]  (max, sum of exp)
   float* part_acc;        // [units, 2 * chunks, G, d]  exp-weighted value sums
@@ -67,7 +65,7 @@ struct RebuildArgs {
 };
 
 // Host launchers (defined in the .hip files).  dtype: 0 fp32, 1 bf16.
-// Prologue kernel, then the attention kernel (bracketed by ev0/ev1 if set).
+// The attention kernel (bracketed by ev0/ev1 if set).
 // a.chunks <= 0 lets the launcher pick the chunk count from the device's
 // workgroup slots (CUs x resident workgroups of the chosen kernel).
 hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0,

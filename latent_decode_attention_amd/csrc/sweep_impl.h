@@ -146,6 +146,8 @@ struct alignas(16) AttnShared {
       float ofull[kMaxGroup][kHeadDim];
     } comb;
   } u;
+  float qrot[kMaxGroup][kHeadDim];  // rotated query, pre-scaled (prologue)
+  float qlat[kMaxGroup][kHeadDim];  // latent query, pre-scaled (prologue)
   float ml[kWaves][kMaxGroup][2];
   float M[kMaxGroup], L[kMaxGroup];
   int is_last;
@@ -164,27 +166,23 @@ __device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
 }
 
 // ---------------------------------------------------------------------------
-// Prologue kernel, one workgroup per (b, kv head): the G query heads rotated
-// at the query position (rotate-half pairs (i, i + d/2), double precision)
-// and pre-scaled by scale * log2(e), written to q_rot; for a latent segment
-// also q_lat = U_K^T q_rot (fp32 MFMA 16x16x4, exact products).  Every
-// global read is issued up front (one round trip).
+// Prologue, run by every workgroup for its (b, kv head): the G query heads
+// rotated at the query position (rotate-half pairs (i, i + d/2), double
+// precision, angles reduced mod 2*pi) and pre-scaled by scale * log2(e) into
+// sh.qrot; with a latent beacon segment also sh.qlat = U_K^T qrot (fp32 MFMA
+// 16x16x4, exact products).  Every global read is issued up front.
 template <int G, bool BF16>
-__global__ __launch_bounds__(kThreads) void prologue_kernel(AttnArgs a) {
-  __shared__ float qrot[kMaxGroup][kHeadDim];
+__device__ __forceinline__ void prologue(const AttnArgs& a, int b, int h, AttnShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int unit = blockIdx.x;
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
   const int rk = a.rank_k;
-  const bool latent = a.q_lat != nullptr;
+  const bool latent = rk > 0;
   constexpr int half = kHeadDim / 2;
   constexpr int kPairs = (G * half + kThreads - 1) / kThreads;  // rotation pairs per thread
   constexpr int kTiles = kHeadDim / 16 / kWaves;                // latent column tiles per wave
 
-  // Loads are unconditional from clamped (in-bounds) addresses: a load under
-  // a divergent branch costs a full wait for the memory round trip.
+  // loads are unconditional from clamped (in-bounds) addresses: a load under
+  // a divergent branch costs a full wait for the memory round trip
   float x1[kPairs], x2[kPairs];
 #pragma unroll
   for (int j = 0; j < kPairs; ++j) {
@@ -195,17 +193,15 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(AttnArgs a) {
     x2[j] = ld_elem<BF16>(a.q, base + i + half);
   }
   const double pos = (double)a.q_pos[b];
-  float ub[kTiles][kHeadDim / 4];
+  // U_K columns of this wave's first latent tile (a second tile, r_K > 64,
+  // is loaded after the first one's products)
+  float ub[kHeadDim / 4];
   const char* U = static_cast<const char*>(a.U_K) + (size_t)h * kHeadDim * rk * Traits<BF16>::kElemBytes;
+  auto load_ub = [&](int c0) {
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    const int c0 = 16 * (wave + kWaves * t);
-    if (latent && c0 < rk) {  // wave-uniform
-#pragma unroll
-      for (int s = 0; s < kHeadDim / 4; ++s)
-        ub[t][s] = ld_elem<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
-    }
-  }
+    for (int s = 0; s < kHeadDim / 4; ++s) ub[s] = ld_elem<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
+  };
+  if (latent && 16 * wave < rk) load_ub(16 * wave);  // wave-uniform
 
 #pragma unroll
   for (int j = 0; j < kPairs; ++j) {
@@ -217,34 +213,30 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(AttnArgs a) {
       const double inv_freq = exp2(-(double)(2 * i) / (double)kHeadDim * a.log2_theta);
       rope_sincos(pos * inv_freq, sn, cs);
       const double v1 = x1[j], v2 = x2[j];
-      const float r1 = (float)((v1 * cs - v2 * sn) * a.score_scale);
-      const float r2 = (float)((v2 * cs + v1 * sn) * a.score_scale);
-      const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
-      a.q_rot[base + i] = r1;
-      a.q_rot[base + i + half] = r2;
-      qrot[g][i] = r1;
-      qrot[g][i + half] = r2;
+      sh.qrot[g][i] = (float)((v1 * cs - v2 * sn) * a.score_scale);
+      sh.qrot[g][i + half] = (float)((v2 * cs + v1 * sn) * a.score_scale);
     }
   }
-  if (!latent) return;
   __syncthreads();
-  // q_lat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
-  float* ql = a.q_lat + ((size_t)b * a.num_q_heads + (size_t)h * G) * rk;
+  if (!latent) return;
+  // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
     const int c0 = 16 * (wave + kWaves * t);
     if (c0 < rk) {
+      if (t > 0) load_ub(c0);
       f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < kHeadDim / 4; ++s) {
-        const float av = n < G ? qrot[n][4 * s + kg] : 0.0f;
-        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, ub[t][s], d, 0, 0, 0);
+        const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
+        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, ub[s], d, 0, 0, 0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * kg + e < G) ql[(size_t)(4 * kg + e) * rk + c0 + n] = d[e];
+        if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
     }
   }
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -419,12 +411,17 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 }
 
 // ---------------------------------------------------------------------------
-// Sweep rows [p0, p1) of one unit's segment with the whole workgroup (each
-// wave a contiguous, tile-aligned sub-range) and write the piece's partial
-// to `slot` (an empty piece writes the neutral partial: max -inf, sum 0).
+// This workgroup's share of one unit's segment.  The unit's tiles (beacon
+// tiles, then raw tiles; all about the same size in bytes) are dealt
+// round-robin to the unit's `nwaves` waves, so every wave gets the same
+// number of tiles to within one and all waves of a unit advance through one
+// sliding window of rows.  `base` is the dealt index of this segment's first
+// tile, `wu` this wave's number.  Writes the workgroup's partial to `slot`
+// (max -inf, sum 0 if none of its waves got a tile).
 template <int G, int NCH, bool BF16>
-__device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& sg, int unit,
-                                             int slot, int p0, int p1, AttnShared& sh) {
+__device__ __forceinline__ void attend_segment(const AttnArgs& a, const Segment& sg, int unit,
+                                               int slot, int wu, int nwaves, int base,
+                                               bool run_prologue, AttnShared& sh) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
@@ -443,22 +440,25 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
 
   float* ml_out = a.part_ml + (size_t)slot * G * 2;
   float* acc_out = a.part_acc + (size_t)slot * G * kHeadDim;
-  if (p0 >= p1) {
+  const int ntiles = (sg.rows + TR - 1) / TR;
+  // this wave's first tile in the segment: the first index >= base dealt to wu
+  const int first = ((wu - base) % nwaves + nwaves) % nwaves;
+  const int b = unit / a.num_kv_heads;
+  const int h = unit - b * a.num_kv_heads;
+  if (__syncthreads_or(first < ntiles) == 0) {  // no wave of this workgroup has a tile
     if (tid < G) {
       store_coherent(&ml_out[2 * tid], -INFINITY);
       store_coherent(&ml_out[2 * tid + 1], 0.0f);
     }
+    if (run_prologue) prologue<G, BF16>(a, b, h, sh);
     return;
   }
-  // this wave's rows: the piece split into four tile-aligned runs
-  const int per_wave = ((p1 - p0 + kWaves - 1) / kWaves + TR - 1) / TR * TR;
-  const int r0 = min(p1, p0 + wave * per_wave);
-  const int r1 = min(p1, r0 + per_wave);
+  // this wave's tiles: first, first + nwaves, ...; rows past the segment end masked
+  const int r1 = sg.rows;
+  const int t_first = first * TR, t_step = nwaves * TR;
 
   const int rk = sg.rk, rv = sg.rv;
   const bool latent = sg.kind == kSegLatent;
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
   const size_t urow = (size_t)unit * (size_t)sg.rows;
   const char* Kb = static_cast<const char*>(sg.K) + urow * rk * Tr::kElemBytes;
   const char* Vb = static_cast<const char*>(sg.V) + urow * rv * Tr::kElemBytes;
@@ -477,12 +477,12 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
 
   u32x4_t kbuf[SUB][NCH];
   u32x4_t vbuf[VMAX];
-  // Every load is unconditional, from an address clamped into [r0, r1) and
+  // Every load is unconditional, from an address clamped into the segment and
   // the row's width: rows past r1 get score -inf, features past r_K meet
   // zero query entries, and value rows past r1 get weight 0, so the clamped
   // data never contributes (a load under a divergent branch would cost a
   // full memory round trip each).
-  auto load_tile = [&](int t0) {
+  auto load_keys = [&](int t0) {
 #pragma unroll
     for (int s = 0; s < SUB; ++s)
 #pragma unroll
@@ -491,6 +491,8 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
         const int k0 = min(c * KCH + kg * EPL, rk - EPL);
         kbuf[s][c] = load16(Kb + ((size_t)row * rk + k0) * Tr::kElemBytes);
       }
+  };
+  auto load_values = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < VMAX; ++i) {
       const int row = min(t0 + i * rpi + vrow, r1 - 1);
@@ -498,30 +500,27 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
     }
   };
 
-  // first tile and the query operand in flight together
-  if (r0 < r1) load_tile(r0);
+  // the first tile is in flight while the prologue runs
+  if (t_first < r1) {
+    load_keys(t_first);
+    load_values(t_first);
+  }
+  if (run_prologue) prologue<G, BF16>(a, b, h, sh);
   const int rq = latent ? rk : kHeadDim;
-  const float* qsrc = (latent ? a.q_lat : a.q_rot) + ((size_t)b * a.num_q_heads + (size_t)h * G) * rq;
+  const float* qsrc = latent ? &sh.qlat[0][0] : &sh.qrot[0][0];  // row stride kHeadDim
   bf16x8_t qhi[BF16 ? NCH : 1], qlo[BF16 ? NCH : 1];
   float qf[BF16 ? 1 : NCH][4];
   {
     // A matrix: head m = lane%16, features of k-group kg
     const int m = lane & 15;
-    f32x4_t qv[NCH][KCH / 16];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int k0 = c * KCH + kg * (KCH / 4);
+      const bool ok = m < G && k0 < rq;
       const int mc = min(m, G - 1), kc = min(k0, rq - KCH / 4);
-#pragma unroll
-      for (int e = 0; e < KCH / 16; ++e)
-        qv[c][e] = *reinterpret_cast<const f32x4_t*>(qsrc + (size_t)mc * rq + kc + 4 * e);
-    }
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const bool ok = m < G && c * KCH + kg * (KCH / 4) < rq;
       float x[8];
 #pragma unroll
-      for (int e = 0; e < KCH / 4; ++e) x[e] = ok ? qv[c][e / 4][e % 4] : 0.0f;
+      for (int e = 0; e < KCH / 4; ++e) x[e] = ok ? qsrc[mc * kHeadDim + kc + e] : 0.0f;
       if constexpr (BF16) {
         split_bf16x8(x, qhi[c], qlo[c]);
       } else {
@@ -544,8 +543,11 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
   }
   float* pw = sh.u.p[wave];
 
-  for (int t0 = r0; t0 < r1; t0 += TR) {
-    if (t0 != r0) load_tile(t0);
+  // Software pipeline: the next tile's keys are requested as soon as the
+  // scores have consumed this tile's keys, its values as soon as the value
+  // sums have consumed this tile's values.
+  for (int t0 = t_first; t0 < r1; t0 += t_step) {
+    const int tn = t0 + t_step;
 
     // -- scores on the matrix cores, log2 units (the query is pre-scaled)
     f32x4_t sc[SUB];
@@ -570,6 +572,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
       if (t0 + 16 * s + n >= r1) d = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       sc[s] = d;
     }
+    if (tn < r1) load_keys(tn);
 
     // -- online softmax: tile max per head, rescale only when it grows
     float mnew[4];
@@ -644,6 +647,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
           for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[g], v[e], acc[g][e]);
       }
     }
+    if (tn < r1) load_values(tn);
     // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -685,7 +689,7 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
       float M = sh.ml[0][g][0];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][g][0]);
-      const float sw = __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
+      const float sw = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) sh.u.red[wave][g][vcc * EPL + e] = acc[g][e] * sw;
     }
@@ -704,32 +708,21 @@ __device__ __forceinline__ void attend_piece(const AttnArgs& a, const Segment& s
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][tid][0]);
     float L = 0.0f;
+    if (M != -INFINITY)
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][tid][0] - M) * sh.ml[w][tid][1];
+      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][tid][0] - M) * sh.ml[w][tid][1];
     store_coherent(&ml_out[2 * tid], M);
     store_coherent(&ml_out[2 * tid + 1], L);
   }
 
 }
 
-// Position of byte `off` of a unit's stream in unified row space (beacon
-// rows first, then raw rows), rounded down to a tile boundary.
-__device__ __forceinline__ int stream_row(const AttnArgs& a, int64_t off) {
-  const int64_t bb = (int64_t)a.seg[0].rows * a.seg[0].row_bytes;
-  if (off < bb) {
-    const int r = (int)(off / a.seg[0].row_bytes);
-    return r - r % a.seg[0].tile;
-  }
-  const int r = (int)((off - bb) / a.seg[1].row_bytes);
-  return a.seg[0].rows + r - r % a.seg[1].tile;
-}
-
-// Grid: one workgroup per (unit, chunk).  Chunk c covers bytes
-// [c T / k, (c+1) T / k) of the unit's stream (T bytes, k chunks): its beacon
-// rows go to slot 2c, its raw rows to slot 2c+1.  The workgroup that
-// finishes a unit's last chunk merges the unit.
+// Grid: `chunks` workgroups per (b, kv head) unit.  Workgroup c hosts the
+// unit's waves 4c .. 4c+3; the unit's tiles (beacon, then raw) are dealt
+// round-robin over its 4*chunks waves.  The beacon rows' partial goes to slot 2c, the
+// raw rows' to slot 2c+1; the workgroup that finishes last merges the unit.
 template <int G, int NCH, bool BF16>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int tid = threadIdx.x;
   const int k = a.chunks;
@@ -737,35 +730,37 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
   const int c = blockIdx.x - unit * k;
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
-  const int nb = a.seg[0].rows;
-  const int R0 = c == 0 ? 0 : stream_row(a, a.unit_bytes * c / k);
-  const int R1 = c == k - 1 ? nb + a.seg[1].rows : stream_row(a, a.unit_bytes * (c + 1) / k);
+  const int nwaves = kWaves * k;
+  const int wu = kWaves * c + (tid >> 6);
   const size_t slot0 = ((size_t)unit * k + c) * 2;
   constexpr int kFullNch = BF16 ? 4 : 8;
 
-  // beacon rows of this chunk (latent, or rebuilt full-width rows)
+  // beacon rows (latent, or rebuilt at full width)
   Segment sg;
   sg.K = a.seg[0].K;
   sg.V = a.seg[0].V;
   sg.kind = a.seg[0].kind;
-  sg.rows = nb;
+  sg.rows = a.seg[0].rows;
   sg.rk = a.seg[0].rk;
   sg.rv = a.seg[0].rv;
+  const int btile = sg.kind == kSegLatent ? TileShape<BF16, NCH>::kRows
+                                           : TileShape<BF16, kFullNch>::kRows;
+  const int beacon_tiles = (sg.rows + btile - 1) / btile;
   if (sg.kind == kSegLatent)
-    attend_piece<G, NCH, BF16>(a, sg, unit, (int)slot0, min(R0, nb), min(R1, nb), sh);
+    attend_segment<G, NCH, BF16>(a, sg, unit, (int)slot0, wu, nwaves, 0, true, sh);
   else
-    attend_piece<G, kFullNch, BF16>(a, sg, unit, (int)slot0, min(R0, nb), min(R1, nb), sh);
-  __syncthreads();  // LDS is reused by the next piece
+    attend_segment<G, kFullNch, BF16>(a, sg, unit, (int)slot0, wu, nwaves, 0, true, sh);
+  __syncthreads();  // LDS is reused by the next segment
 
-  // raw rows of this chunk
+  // raw rows
   sg.K = a.seg[1].K;
   sg.V = a.seg[1].V;
   sg.kind = kSegFull;
   sg.rows = a.seg[1].rows;
   sg.rk = kHeadDim;
   sg.rv = kHeadDim;
-  attend_piece<G, kFullNch, BF16>(a, sg, unit, (int)slot0 + 1, max(R0, nb) - nb,
-                                  max(R1, nb) - nb, sh);
+  attend_segment<G, kFullNch, BF16>(a, sg, unit, (int)slot0 + 1, wu, nwaves, beacon_tiles,
+                                    false, sh);
 
   // ---- the last chunk of the unit merges everything.  Every thread waits
   // for its coherent partial stores to complete before the barrier; only
@@ -811,11 +806,7 @@ hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s,
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
     a.chunks = choose_chunks(units, a.unit_bytes, slots, 64 << 10);
   }
-  const dim3 pgrid((unsigned)units), grid((unsigned)(units * a.chunks)), block(kThreads);
-  if (dtype == 0)
-    hipLaunchKernelGGL((prologue_kernel<G, false>), pgrid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((prologue_kernel<G, true>), pgrid, block, 0, s, a);
+  const dim3 grid((unsigned)(units * a.chunks)), block(kThreads);
   if (ev0) {
     const hipError_t e = hipEventRecord(ev0, s);
     if (e != hipSuccess) return e;
