@@ -163,7 +163,7 @@ hipError_t launch_attention_g7(AttnArgs, int, int, hipStream_t, hipEvent_t, hipE
 hipError_t launch_attention_g8(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
 
 hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  int nch = 4;
+  int nch = 0;  // beacon rows at full width, or none
   if (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0) {
     nch = (a.seg[0].rk + 31) / 32;
     const int nv = (a.seg[0].rv + 31) / 32;

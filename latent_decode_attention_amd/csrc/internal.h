@@ -13,7 +13,6 @@ constexpr int kWaves = 4;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
 constexpr int kMaxChunks = 64;         // row chunks per unit (each writes 2 partial slots)
-constexpr int kMaxMergeSlots = 2048;   // 2 * kMaxChunks * G, held in LDS by a unit's merge
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent

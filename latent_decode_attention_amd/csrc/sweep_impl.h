@@ -1,6 +1,6 @@
 // sweep_impl.h -- the fused decode-attention kernel: query prologue, split-K
-// sweep over one row chunk of a (b, kv head) unit, and the merge of all of
-// the unit's chunks by whichever workgroup finishes last.
+// sweep over one unit's rows, and the merge of all of the unit's workgroups
+// by whichever finishes last.
 //
 // What is computed (page "Can SlimKV compress KV cache jointly across tokens
 // and features", section "Latent-space attention removes the rebuild step"):
@@ -8,17 +8,17 @@
 // for beacon rows, projected into the head's latent key space (q' U_K).
 // Scores against the latent beacon keys C_K (no rotation) and against the
 // rotated raw keys share one softmax.  Beacon values are summed in latent
-// form (A C_V) and lifted once by U_V after every chunk is merged, so beacon
-// keys and values are never rebuilt at full dimension.
+// form (A C_V) and lifted once by U_V after every partial is merged, so
+// beacon keys and values are never rebuilt at full dimension.
 //
 // Mapping onto CDNA4 (gfx950):
-//   * One workgroup of 4 waves per (unit, row chunk); each wave sweeps a
-//     contiguous sub-range of the chunk in tiles of 16/32/64 rows, every
-//     global read a 16-byte load.
+//   * Workgroups of 4 waves; a unit's tiles (16/32/64 rows, every global read
+//     a 16-byte load) are dealt round-robin over all waves of its workgroups,
+//     beacon tiles first, then raw tiles.  One tile per wave is in flight at
+//     all times, across the boundary between the two segments too.
 //   * Prologue per workgroup: rotation in double precision (angles reduced
-//     mod 2*pi before sincos), the
-//     latent projection U_K^T q' as an fp32 MFMA (16x16x4) into LDS.  Its
-//     loads and the first tile's loads are all issued up front.
+//     mod 2*pi before sincos), the latent projection U_K^T q' as an fp32 MFMA
+//     (16x16x4) into LDS, both while the first tile is in flight.
 //   * Scores are a [G x K] x [K x 16 rows] contraction per 16-row subtile on
 //     the matrix cores (v_mfma_f32_16x16x32_bf16; fp32 data uses
 //     v_mfma_f32_16x16x4_f32).  Query heads sit on the M axis, cache rows on
@@ -28,12 +28,14 @@
 //     i, so the running max is a 16-lane DPP reduction and the softmax state
 //     lives in that layout.  exp-weights reach the value lanes through LDS;
 //     each value lane holds 16 bytes of one value row and G x 8 fp32 sums.
-//   * The waves' partials merge in LDS into one partial per chunk, written
-//     to the workspace with device-coherent stores.  A device-scope counter
-//     per unit elects the last chunk's workgroup, which reads the partials
-//     back with device-coherent loads, merges them by log-sum-exp, lifts the
-//     latent sum with U_V on the matrix cores, writes out and lse, and resets
-//     the counter for the next call.
+//   * Each wave parks its beacon state in LDS and goes straight on to its raw
+//     tiles; at the end the four waves merge both segments in LDS and the
+//     workgroup writes one partial per segment with device-coherent stores.
+//     A device-scope counter per unit elects the unit's last workgroup, which
+//     reads the partials back with device-coherent loads, merges them by
+//     log-sum-exp, lifts the latent sum with U_V on the matrix cores (its
+//     U_V rows were requested before the count), writes out and lse, and
+//     resets the counter for the next call.
 #pragma once
 #include <math.h>
 
@@ -91,15 +93,11 @@ __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Partials cross workgroups (and XCDs, whose L2s are not coherent with each
-// other).  They are stored and loaded as relaxed agent-scope atomics, i.e.
-// with device-coherent cache policy, so no whole-L2 writeback/invalidate is
-// needed to hand them over -- only completion of the stores (see below).
+// The (max, sum) pairs of partials are stored as relaxed agent-scope atomics,
+// i.e. with the device-coherent cache policy, so no whole-L2 writeback or
+// invalidate is needed to hand them over -- only completion of the stores.
 __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool BF16>
@@ -136,19 +134,27 @@ struct TileShape {
   static constexpr int kRows = 16 * kSub;
 };
 
+// LDS of one attention workgroup.  The sweep arrays are dead once the
+// workgroup's partials are written; the unit merge then reuses them.
 struct alignas(16) AttnShared {
   union {
-    float p[kWaves][64 * 8];                 // exp-weights of the current tile, per wave
-    float red[kWaves][kMaxGroup][kHeadDim];  // each wave's rescaled value sums
     struct {
-      float ml[kMaxMergeSlots][2];  // every chunk's (max, sum); then weights
+      union {
+        float p[kWaves][64 * 8];                 // exp-weights of the current tile, per wave
+        float raw[kWaves][kMaxGroup][kHeadDim];  // each wave's raw-row sums (after the sweeps)
+      } t;
+      float beacon[kWaves][kMaxGroup][kHeadDim];  // each wave's beacon-row sums
+    } s;
+    struct {
+      float ml[2 * kMaxChunks * kMaxGroup][2];  // every slot's (max, sum); then its weight
+      f32x4_t part[kThreads][2];                // per-thread sums over one group of slots
       float olat[kMaxGroup][kHeadDim];
       float ofull[kMaxGroup][kHeadDim];
-    } comb;
+    } m;
   } u;
-  float qrot[kMaxGroup][kHeadDim];  // rotated query, pre-scaled (prologue)
-  float qlat[kMaxGroup][kHeadDim];  // latent query, pre-scaled (prologue)
-  float ml[kWaves][kMaxGroup][2];
+  float qrot[kMaxGroup][kHeadDim];     // rotated query, pre-scaled (prologue)
+  float qlat[kMaxGroup][kHeadDim];     // latent query, pre-scaled (prologue)
+  float wml[2][kWaves][kMaxGroup][2];  // each wave's (max, sum) per head, per segment
   float M[kMaxGroup], L[kMaxGroup];
   int is_last;
 };
@@ -171,12 +177,13 @@ __device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
 // precision, angles reduced mod 2*pi) and pre-scaled by scale * log2(e) into
 // sh.qrot; with a latent beacon segment also sh.qlat = U_K^T qrot (fp32 MFMA
 // 16x16x4, exact products).  Every global read is issued up front.
-template <int G, bool BF16>
+template <int G, bool BF16, bool BLAT>
 __device__ __forceinline__ void prologue(const AttnArgs& a, int b, int h, AttnShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int n = lane & 15, kg = lane >> 4;
   const int rk = a.rank_k;
-  const bool latent = rk > 0;
+  constexpr bool latent = BLAT;
   constexpr int half = kHeadDim / 2;
   constexpr int kPairs = (G * half + kThreads - 1) / kThreads;  // rotation pairs per thread
   constexpr int kTiles = kHeadDim / 16 / kWaves;                // latent column tiles per wave
@@ -218,7 +225,7 @@ __device__ __forceinline__ void prologue(const AttnArgs& a, int b, int h, AttnSh
     }
   }
   __syncthreads();
-  if (!latent) return;
+  if constexpr (!latent) return;
   // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
 #pragma unroll
   for (int t = 0; t < kTiles; ++t) {
@@ -240,62 +247,400 @@ __device__ __forceinline__ void prologue(const AttnArgs& a, int b, int h, AttnSh
 }
 
 // ---------------------------------------------------------------------------
-// Merge of all chunks of one unit (run by the unit's last workgroup).
-//   M = max_s m_s, L = sum_s 2^(m_s - M) l_s,
-//   o_lat = sum_{latent s} 2^(m_s - M) acc_s / L, o_full likewise,
-//   out = U_V o_lat + o_full, lse = ln 2 * (M + log2 L).
-// U_V rows, every (max, sum) and a first batch of chunk sums are loaded in
-// one round trip; more batches only when a unit has many chunks.
-template <int G, bool BF16>
-__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h,
-                                           AttnShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = 2 * a.chunks, rv = a.rank_v;
-  const bool lat_beacons = a.seg[0].kind == kSegLatent;
-  const float* ml = a.part_ml + (size_t)unit * S * G * 2;
-  const float* acc = a.part_acc + (size_t)unit * S * G * kHeadDim;
-  float (*sml)[2] = sh.u.comb.ml;
-  constexpr int kPer = (G * kHeadDim + kThreads - 1) / kThreads;  // outputs per thread
-  constexpr int kBatch = 64 / kPer;                               // chunks per load batch
-  constexpr int kMlPer = kMaxMergeSlots * 2 / kThreads;           // (max, sum) loads per thread
-  const int m16 = lane & 15, kg = lane >> 4;
-  const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * Traits<BF16>::kElemBytes;
+// Partials cross workgroups and XCDs (whose L2s are not coherent with each
+// other).  The 16-byte ones go through buffer instructions with the
+// device-coherent cache policy (sc1); the descriptor's size also bounds them.
+constexpr int kCoherent = 16;  // cache-policy bits: sc1
 
-  // -- one round trip: U_V rows of this wave's output tiles, (max, sum) pairs,
-  //    and the first batch of chunk sums
-  u32x4_t uw[2][4];
-  if constexpr (BF16) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// One segment of one unit (a run of rows: its beacons, or its raw window) as
+// this lane sees it: where its tile loads go and which value columns it sums.
+// Tiles are kRows rows; a value row spans rv / EPL lanes, padded to a power
+// of two (lpr) so that row groups can be summed by a butterfly.
+template <int NCH, bool BF16>
+struct SegView {
+  using Tr = Traits<BF16>;
+  static constexpr int kSub = TileShape<BF16, NCH>::kSub;
+  static constexpr int kRows = TileShape<BF16, NCH>::kRows;
+  const char* K;
+  const char* V;
+  int rows, rk, rv, ntiles;
+  int lpr, rpi, vrow, vcc, vcol, lanes_row;
+  bool vact;
+
+  __device__ __forceinline__ void init(const void* Kp, const void* Vp, int rows_, int rk_, int rv_,
+                                       int unit, int lane) {
+    rows = rows_;
+    rk = rk_;
+    rv = rv_;
+    const size_t urow = (size_t)unit * (size_t)rows;
+    K = static_cast<const char*>(Kp) + urow * rk * Tr::kElemBytes;
+    V = static_cast<const char*>(Vp) + urow * rv * Tr::kElemBytes;
+    ntiles = (rows + kRows - 1) / kRows;
+    lanes_row = rv / Tr::kEpl;
+    lpr = 1 << (32 - __builtin_clz(lanes_row - 1));
+    rpi = 64 / lpr;
+    vrow = lane / lpr;
+    vcc = lane & (lpr - 1);
+    vact = vcc < lanes_row;
+    vcol = min(vcc, lanes_row - 1) * Tr::kEpl;  // clamped for idle lanes
+  }
+
+  // Every load is unconditional, from an address clamped into the segment
+  // and the row's width: rows past `rows` get score -inf, features past r_K
+  // meet zero query entries, and value rows past `rows` get weight 0, so the
+  // clamped data never contributes (a load under a divergent branch would
+  // cost a full memory round trip each).  Callers only ask for tiles that
+  // exist, so `rows` >= 1 here.
+  // Keys as MFMA B operands: lane (n, kg) holds features c*KCH + kg*EPL ...
+  // of row t0 + 16 s + n in kb[s * NCH + c].
+  __device__ __forceinline__ void load_keys(int t0, u32x4_t* kb, int n, int kg) const {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int sb = 0; sb < kSub; ++sb)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 16 * (wave + kWaves * t) + m16, k0 = 32 * c + 8 * kg;
-        // features past r_V are multiplied by zero latent entries below
-        uw[t][c] = lat_beacons ? load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2)
-                               : u32x4_t{0u, 0u, 0u, 0u};
+      for (int c = 0; c < NCH; ++c) {
+        const int row = min(t0 + 16 * sb + n, rows - 1);
+        const int k0 = min(c * Tr::kChunkK + kg * Tr::kEpl, rk - Tr::kEpl);
+        kb[sb * NCH + c] = load16(K + ((size_t)row * rk + k0) * Tr::kElemBytes);
       }
   }
-  // (unconditional loads from clamped indexes; out-of-range values unused)
-  float mlv[kMlPer];
+  // Values: load i covers rows t0 + i * rpi + vrow, this lane's 16 bytes.
+  __device__ __forceinline__ void load_values(int t0, u32x4_t* vb) const {
 #pragma unroll
-  for (int j = 0; j < kMlPer; ++j)
-    mlv[j] = load_coherent(&ml[min(tid + kThreads * j, S * G * 2 - 1)]);
-  float v[kBatch][kPer];
-  auto load_batch = [&](int s0) {
+    for (int i = 0; i < Tr::kMaxLoads; ++i) {
+      const int row = min(t0 + i * rpi + vrow, rows - 1);
+      vb[i] = load16(V + ((size_t)row * rv + vcol) * Tr::kElemBytes);
+    }
+  }
+};
+
+// One wave's running softmax state over the rows it has swept: max and sum
+// per head in the MFMA output layout (head 4*kg + i in element i), value sums
+// for this lane's columns.
+template <int G, bool BF16>
+struct WaveState {
+  float m[4], l[4];
+  float acc[G][Traits<BF16>::kEpl];
+  __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
+    for (int i = 0; i < 4; ++i) {
+      m[i] = -INFINITY;
+      l[i] = 0.0f;
+    }
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int su = min(s0 + u, S - 1);
-        const int p = min(tid + kThreads * j, G * kHeadDim - 1);
-        v[u][j] = load_coherent(&acc[(size_t)su * G * kHeadDim + p]);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < Traits<BF16>::kEpl; ++e) acc[g][e] = 0.0f;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// One wave's tiles of one segment: j0, j0 + jstep, ... < sv.ntiles.  The
+// loads of tile j0 are already in kbuf/vbuf.  Software pipeline: the next
+// tile's keys are requested as soon as the scores have consumed this tile's
+// keys, its values as soon as the value sums have consumed this tile's
+// values.  After the last tile the next segment's first tile for this wave
+// (`nx` at row nx_t0; nx_t0 < 0: none) is requested the same way, so the
+// stream of loads does not stop between segments.
+template <int G, int NCH, bool BF16, int NCH2>
+__device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegView<NCH2, BF16>& nx,
+                                      int j0, int jstep, int nx_t0, const float* qsrc, int rq,
+                                      u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
+                                      WaveState<G, BF16>& st) {
+  using Tr = Traits<BF16>;
+  constexpr int EPL = Tr::kEpl;
+  constexpr int KCH = Tr::kChunkK;
+  constexpr int SUB = SegView<NCH, BF16>::kSub;
+  constexpr int TR = SegView<NCH, BF16>::kRows;
+  constexpr int VMAX = Tr::kMaxLoads;
+  constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
+  constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
+  static_assert(SUB * NCH <= Tr::kMaxLoads, "tile too large");
+  if (j0 >= sv.ntiles) return;  // wave-uniform
+
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;   // MFMA column (cache row) within a subtile
+  const int kg = lane >> 4;  // MFMA k-group / output row group
+
+  // A operand: head m = lane % 16, features of k-group kg (qsrc row stride d)
+  bf16x8_t qhi[BF16 ? NCH : 1], qlo[BF16 ? NCH : 1];
+  float qf[BF16 ? 1 : NCH][4];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int k0 = c * KCH + kg * (KCH / 4);
+    const bool ok = n < G && k0 < rq;
+    const int mc = min(n, G - 1), kc = min(k0, rq - KCH / 4);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < KCH / 4; ++e) x[e] = ok ? qsrc[mc * kHeadDim + kc + e] : 0.0f;
+    if constexpr (BF16) {
+      split_bf16x8(x, qhi[c], qlo[c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[c][e] = x[e];
+    }
+  }
+  const int nchk = (sv.rk + KCH - 1) / KCH;  // chunks that carry key features
+  const int r1 = sv.rows;
+
+  for (int j = j0; j < sv.ntiles; j += jstep) {
+    const int t0 = j * TR;
+    const bool more = j + jstep < sv.ntiles;  // wave-uniform
+    const int tn = t0 + jstep * TR;
+
+    // -- scores on the matrix cores, log2 units (the query is pre-scaled)
+    f32x4_t sc[SUB];
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (c < nchk) {
+          if constexpr (BF16) {
+            const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, kbuf[s * NCH + c]);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[c], kv, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[c], kv, d, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              d = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c][e], __uint_as_float(kbuf[s * NCH + c][e]),
+                                                       d, 0, 0, 0);
+          }
+        }
       }
+      if (t0 + 16 * s + n >= r1) d = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      sc[s] = d;
+    }
+    if (more) {
+      sv.load_keys(tn, kbuf, n, kg);
+    } else if (nx_t0 >= 0) {
+      // opaque copy: keeps the address arithmetic of this once-per-segment
+      // load from being hoisted out of the loop (it would hold registers)
+      int t = nx_t0;
+      asm volatile("" : "+s"(t));
+      nx.load_keys(t, kbuf, n, kg);
+    }
+
+    // -- online softmax: tile max per head, rescale only when it grows
+    float mnew[4];
+    bool grew = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = sc[0][i];
+#pragma unroll
+      for (int s = 1; s < SUB; ++s) mx = fmaxf(mx, sc[s][i]);
+      mx = row16_max(mx);
+      mnew[i] = fmaxf(st.m[i], mx);
+      grew |= mnew[i] > st.m[i];
+    }
+    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        alpha[i] = __builtin_amdgcn_exp2f(st.m[i] - mnew[i]);
+        st.l[i] *= alpha[i];
+        st.m[i] = mnew[i];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float ag =
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[g & 3]), 16 * (g >> 2)));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.acc[g][e] *= ag;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[s][i] - st.m[i]);
+        st.l[i] += p;
+        sc[s][i] = p;
+      }
+      if (kg < NGRP) *reinterpret_cast<f32x4_t*>(&pw[(16 * s + n) * GP + 4 * kg]) = sc[s];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // -- value sums: acc[g][:] += p[row][g] * V[row][cols of this lane]
+    const int vi_count = (TR + sv.rpi - 1) / sv.rpi;
+#pragma unroll
+    for (int i = 0; i < VMAX; ++i) {
+      if (i < vi_count) {
+        const int rt = i * sv.rpi + sv.vrow;
+        const bool ok = sv.vact && rt < TR && t0 + rt < r1;
+        const int rr = ok ? rt : 0;
+        float pv[GP];
+#pragma unroll
+        for (int jj = 0; jj < GP; jj += 4) {
+          const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&pw[rr * GP + jj]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[jj + e] = ok ? p4[e] : 0.0f;
+        }
+        float v[EPL];
+        if constexpr (BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(vbuf[i][e] << 16);
+            v[2 * e + 1] = __uint_as_float(vbuf[i][e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(vbuf[i][e]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) st.acc[g][e] = fmaf(pv[g], v[e], st.acc[g][e]);
+      }
+    }
+    if (more) {
+      sv.load_values(tn, vbuf);
+    } else if (nx_t0 >= 0) {
+      int t = nx_t0;
+      asm volatile("" : "+s"(t));
+      nx.load_values(t, vbuf);
+    }
+    // the next tile overwrites pw: every lane has read it by now
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Sum a wave's state over its row groups: the value sums of lanes with equal
+// column (vcc) by a butterfly -- DPP rotations inside 16-lane rows, lane swaps
+// across rows -- and the softmax sums over the 16 lanes of each head row.
+template <int G, bool BF16>
+__device__ __forceinline__ void wave_reduce(WaveState<G, BF16>& st, int lpr) {
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < Traits<BF16>::kEpl; ++e) {
+      float x = st.acc[g][e];
+      if (lpr <= 8) x += dpp_f<0x128>(x);
+      if (lpr <= 4) x += dpp_f<0x124>(x);
+      if (lpr <= 2) x += dpp_f<0x122>(x);
+      if (lpr <= 16) x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      st.acc[g][e] = x;
+    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.l[i] = row16_sum(st.l[i]);
+}
+
+// Park a reduced wave state in LDS: (max, sum) per head and the G x rv sums.
+template <int G, int NCH, bool BF16>
+__device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const SegView<NCH, BF16>& sv,
+                                          float (*wacc)[kHeadDim], float (*wml)[2]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, kg = lane >> 4;
+  if (n == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G) {
+        wml[g][0] = st.m[i];
+        wml[g][1] = st.l[i];
+      }
+    }
+  }
+  if (sv.vrow == 0 && sv.vact) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < Traits<BF16>::kEpl; ++e)
+        wacc[g][sv.vcc * Traits<BF16>::kEpl + e] = st.acc[g][e];
+  }
+}
+
+// The workgroup's partial of one segment: the four waves' sums rescaled to
+// their common max, written with device-coherent stores.
+template <int G>
+__device__ __forceinline__ void combine_store(const float (*wacc)[kMaxGroup][kHeadDim],
+                                              const float (*wml)[kMaxGroup][2], int rv,
+                                              float* ml_out, float* acc_out) {
+  const int tid = threadIdx.x;
+  const int c4n = rv / 4;  // 16-byte words per head (G * c4n <= kThreads)
+  if (tid < G * c4n) {
+    const int g = tid / c4n, col = 4 * (tid - g * c4n);
+    float M = wml[0][g][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wml[w][g][0]);
+    f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sw = __builtin_amdgcn_exp2f(wml[w][g][0] - M);
+        sum += sw * *reinterpret_cast<const f32x4_t*>(&wacc[w][g][col]);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(acc_out, G * kHeadDim * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), rs,
+                                           (g * kHeadDim + col) * 4, 0, kCoherent);
+  }
+  if (tid < G) {
+    float M = wml[0][tid][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wml[w][tid][0]);
+    float L = 0.0f;
+    if (M != -INFINITY)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(wml[w][tid][0] - M) * wml[w][tid][1];
+    store_coherent(&ml_out[2 * tid], M);
+    store_coherent(&ml_out[2 * tid + 1], L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of all slots of one unit (run by the unit's last workgroup).
+//   M = max_s m_s, L = sum_s 2^(m_s - M) l_s,
+//   o_lat = sum_{beacon s} 2^(m_s - M) acc_s / L, o_full likewise over raw s,
+//   out = U_V o_lat + o_full, lse = ln 2 * (M + log2 L).
+// Thread t owns 16-byte column t % C4 of every slot in its group t / C4; the
+// (max, sum) pairs and a first batch of slot sums are loaded in one round
+// trip.  `uw` holds this wave's U_V rows for the lift (bf16, latent beacons).
+template <int G, bool BF16, bool BLAT>
+__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h,
+                                           AttnShared& sh, const u32x4_t (&uw)[2][4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  const int S = 2 * a.chunks, rv = a.rank_v;
+  constexpr int C4 = G * kHeadDim / 4;                    // 16-byte columns of a slot
+  constexpr int NG = C4 >= kThreads ? 1 : kThreads / C4;  // slot groups
+  constexpr int kB = 8;                                   // slots per load batch
+  float (*sml)[2] = sh.u.m.ml;
+  const __amdgpu_buffer_rsrc_t rml =
+      coherent_rsrc(a.part_ml + (size_t)unit * S * G * 2, (uint32_t)(S * G * 2 * 4));
+  const __amdgpu_buffer_rsrc_t racc =
+      coherent_rsrc(a.part_acc + (size_t)unit * S * G * kHeadDim, (uint32_t)(S * G * kHeadDim * 4));
+  const int c4 = tid % C4, grp = tid / C4;
+  const bool active = grp < NG;
+
+  // -- one round trip: every (max, sum) and the first batch of slot sums
+  // (unconditional loads from clamped offsets; surplus values are unused)
+  const int n4 = S * G / 2;  // (max, sum) pairs as 16-byte words; S is even
+  u32x4_t mlv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    mlv[j] = __builtin_amdgcn_raw_buffer_load_b128(rml, min(tid + kThreads * j, n4 - 1) * 16, 0,
+                                                   kCoherent);
+  u32x4_t v[kB];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int s = min(grp + NG * (i0 + u), S - 1);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(racc, (s * C4 + c4) * 16, 0, kCoherent);
+    }
   };
   load_batch(0);
 #pragma unroll
-  for (int j = 0; j < kMlPer; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int q = tid + kThreads * j;
-    if (q < S * G * 2) (&sml[0][0])[q] = mlv[j];
+    if (q < n4) *reinterpret_cast<u32x4_t*>(&sml[2 * q][0]) = mlv[j];
   }
   __syncthreads();
 
@@ -322,49 +667,50 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
     sml[q][0] = __builtin_amdgcn_exp2f(sml[q][0] - sh.M[q % G]) / sh.L[q % G];
   __syncthreads();
 
-  // -- weighted sums: thread owns outputs p = tid + 256 j (p = g * d + col)
-  float lat[kPer], full[kPer];
+  // -- weighted sums of this thread's column over its slots
+  const int g = c4 / (kHeadDim / 4), col = 4 * (c4 % (kHeadDim / 4));
+  f32x4_t lat = {0.0f, 0.0f, 0.0f, 0.0f}, full = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int per = (S + NG - 1) / NG;  // batches cover the largest group (uniform)
+  for (int i0 = 0; i0 < per; i0 += kB) {
+    if (i0 > 0) load_batch(i0);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) lat[j] = full[j] = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += kBatch) {
-    if (s0 > 0) load_batch(s0);
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int s = s0 + u;
-      if (s < S) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int p = tid + kThreads * j;
-          if (p < G * kHeadDim) {
-            const int g = p / kHeadDim, col = p % kHeadDim;
-            const float w = sml[s * G + g][0];
-            // empty slots carry weight 0 and stale sums: skip, don't multiply
-            const float wv = w != 0.0f ? w * v[u][j] : 0.0f;
-            if ((s & 1) == 0 && lat_beacons) {
-              if (col < rv) lat[j] += wv;
-            } else {
-              full[j] += wv;
-            }
+    for (int u = 0; u < kB; ++u) {
+      const int s = grp + NG * (i0 + u);
+      if (active && s < S) {
+        const float w = sml[s * G + g][0];
+        // empty slots carry weight 0 and stale sums: skip, don't multiply
+        if (w != 0.0f) {
+          const f32x4_t wv = w * __builtin_bit_cast(f32x4_t, v[u]);
+          if (BLAT && (s & 1) == 0) {
+            if (col < rv) lat += wv;
+          } else {
+            full += wv;
           }
         }
       }
     }
   }
+  sh.u.m.part[tid][0] = lat;
+  sh.u.m.part[tid][1] = full;
+  __syncthreads();
+  if (tid < C4) {
+    f32x4_t sl = sh.u.m.part[tid][0], sf = sh.u.m.part[tid][1];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int p = tid + kThreads * j;
-    if (p < G * kHeadDim) {
-      sh.u.comb.olat[p / kHeadDim][p % kHeadDim] = lat[j];
-      sh.u.comb.ofull[p / kHeadDim][p % kHeadDim] = full[j];
+    for (int gi = 1; gi < NG; ++gi) {
+      sl += sh.u.m.part[tid + C4 * gi][0];
+      sf += sh.u.m.part[tid + C4 * gi][1];
     }
+    *reinterpret_cast<f32x4_t*>(&sh.u.m.olat[g][col]) = sl;
+    *reinterpret_cast<f32x4_t*>(&sh.u.m.ofull[g][col]) = sf;
   }
   __syncthreads();
 
   // -- lift the latent sum once and add the full-width sum
   float* out = a.out + ((size_t)b * a.num_q_heads + (size_t)h * G) * kHeadDim;
-  if (lat_beacons) {
+  if constexpr (BLAT) {
     // out^T[i][g] = sum_k U_V[i][k] olat[g][k]: D[m=i][n=g] over 16-row tiles of i
-    const int n = lane & 15;
+    const int n = lane & 15, m16 = lane & 15, kg = lane >> 4;
+    const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * Traits<BF16>::kElemBytes;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int i0 = 16 * (wave + kWaves * t);
@@ -376,7 +722,7 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
             const int k0 = 32 * c + 8 * kg;
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (k0 < rv && n < G) ? sh.u.comb.olat[n][k0 + e] : 0.0f;
+            for (int e = 0; e < 8; ++e) x[e] = (k0 < rv && n < G) ? sh.u.m.olat[n][k0 + e] : 0.0f;
             bf16x8_t hi, lo;
             split_bf16x8(x, hi, lo);
             const bf16x8_t uv = __builtin_bit_cast(bf16x8_t, uw[t][c]);
@@ -388,7 +734,7 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
         for (int s = 0; s < rv / 4; ++s) {
           const int k = 4 * s + kg;
           const float uvv = ld_elem<false>(U, (size_t)(i0 + m16) * rv + k);
-          const float ov = n < G ? sh.u.comb.olat[n][k] : 0.0f;
+          const float ov = n < G ? sh.u.m.olat[n][k] : 0.0f;
           d = __builtin_amdgcn_mfma_f32_16x16x4f32(uvv, ov, d, 0, 0, 0);
         }
       }
@@ -397,13 +743,13 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = i0 + 4 * kg + e;
-          out[(size_t)n * kHeadDim + row] = d[e] + sh.u.comb.ofull[n][row];
+          out[(size_t)n * kHeadDim + row] = d[e] + sh.u.m.ofull[n][row];
         }
       }
     }
   } else {
     for (int p = tid; p < G * kHeadDim; p += kThreads)
-      out[(size_t)(p / kHeadDim) * kHeadDim + p % kHeadDim] = sh.u.comb.ofull[p / kHeadDim][p % kHeadDim];
+      out[(size_t)(p / kHeadDim) * kHeadDim + p % kHeadDim] = sh.u.m.ofull[p / kHeadDim][p % kHeadDim];
   }
   if (a.lse && tid < G)
     a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + tid] =
@@ -411,361 +757,100 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 }
 
 // ---------------------------------------------------------------------------
-// This workgroup's share of one unit's segment.  The unit's tiles (beacon
-// tiles, then raw tiles; all about the same size in bytes) are dealt
-// round-robin to the unit's `nwaves` waves, so every wave gets the same
-// number of tiles to within one and all waves of a unit advance through one
-// sliding window of rows.  `base` is the dealt index of this segment's first
-// tile, `wu` this wave's number.  Writes the workgroup's partial to `slot`
-// (max -inf, sum 0 if none of its waves got a tile).
-template <int G, int NCH, bool BF16>
-__device__ __forceinline__ void attend_segment(const AttnArgs& a, const Segment& sg, int unit,
-                                               int slot, int wu, int nwaves, int base,
-                                               bool run_prologue, AttnShared& sh) {
-  using Tr = Traits<BF16>;
-  constexpr int EPL = Tr::kEpl;
-  constexpr int KCH = Tr::kChunkK;
-  constexpr int SUB = TileShape<BF16, NCH>::kSub;
-  constexpr int TR = TileShape<BF16, NCH>::kRows;
-  constexpr int VMAX = Tr::kMaxLoads;
-  constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
-  constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
-  static_assert(!BF16 || SUB * NCH <= Tr::kMaxLoads, "tile too large");
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int n = lane & 15;   // MFMA column (cache row) within a subtile
-  const int kg = lane >> 4;  // MFMA k-group / output row group
-
-  float* ml_out = a.part_ml + (size_t)slot * G * 2;
-  float* acc_out = a.part_acc + (size_t)slot * G * kHeadDim;
-  const int ntiles = (sg.rows + TR - 1) / TR;
-  // this wave's first tile in the segment: the first index >= base dealt to wu
-  const int first = ((wu - base) % nwaves + nwaves) % nwaves;
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
-  if (__syncthreads_or(first < ntiles) == 0) {  // no wave of this workgroup has a tile
-    if (tid < G) {
-      store_coherent(&ml_out[2 * tid], -INFINITY);
-      store_coherent(&ml_out[2 * tid + 1], 0.0f);
-    }
-    if (run_prologue) prologue<G, BF16>(a, b, h, sh);
-    return;
-  }
-  // this wave's tiles: first, first + nwaves, ...; rows past the segment end masked
-  const int r1 = sg.rows;
-  const int t_first = first * TR, t_step = nwaves * TR;
-
-  const int rk = sg.rk, rv = sg.rv;
-  const bool latent = sg.kind == kSegLatent;
-  const size_t urow = (size_t)unit * (size_t)sg.rows;
-  const char* Kb = static_cast<const char*>(sg.K) + urow * rk * Tr::kElemBytes;
-  const char* Vb = static_cast<const char*>(sg.V) + urow * rv * Tr::kElemBytes;
-
-  // value-lane mapping: a value row spans rv/EPL lanes, padded to a power of
-  // two (LPR) so the row groups can be summed by a butterfly; RPI rows per load
-  const int lanes_row = rv / EPL;
-  const int lpr = 1 << (32 - __builtin_clz(lanes_row - 1));
-  const int rpi = 64 / lpr;
-  const int vrow = lane / lpr;
-  const int vcc = lane & (lpr - 1);
-  const bool vact = vcc < lanes_row;
-  const int vcol = min(vcc, lanes_row - 1) * EPL;  // clamped for idle lanes
-  const int vi_count = (TR + rpi - 1) / rpi;
-  const int nchk = (rk + KCH - 1) / KCH;  // chunks that carry key features
-
-  u32x4_t kbuf[SUB][NCH];
-  u32x4_t vbuf[VMAX];
-  // Every load is unconditional, from an address clamped into the segment and
-  // the row's width: rows past r1 get score -inf, features past r_K meet
-  // zero query entries, and value rows past r1 get weight 0, so the clamped
-  // data never contributes (a load under a divergent branch would cost a
-  // full memory round trip each).
-  auto load_keys = [&](int t0) {
-#pragma unroll
-    for (int s = 0; s < SUB; ++s)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int row = min(t0 + 16 * s + n, r1 - 1);
-        const int k0 = min(c * KCH + kg * EPL, rk - EPL);
-        kbuf[s][c] = load16(Kb + ((size_t)row * rk + k0) * Tr::kElemBytes);
-      }
-  };
-  auto load_values = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      const int row = min(t0 + i * rpi + vrow, r1 - 1);
-      vbuf[i] = load16(Vb + ((size_t)row * rv + vcol) * Tr::kElemBytes);
-    }
-  };
-
-  // the first tile is in flight while the prologue runs
-  if (t_first < r1) {
-    load_keys(t_first);
-    load_values(t_first);
-  }
-  if (run_prologue) prologue<G, BF16>(a, b, h, sh);
-  const int rq = latent ? rk : kHeadDim;
-  const float* qsrc = latent ? &sh.qlat[0][0] : &sh.qrot[0][0];  // row stride kHeadDim
-  bf16x8_t qhi[BF16 ? NCH : 1], qlo[BF16 ? NCH : 1];
-  float qf[BF16 ? 1 : NCH][4];
-  {
-    // A matrix: head m = lane%16, features of k-group kg
-    const int m = lane & 15;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const int k0 = c * KCH + kg * (KCH / 4);
-      const bool ok = m < G && k0 < rq;
-      const int mc = min(m, G - 1), kc = min(k0, rq - KCH / 4);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < KCH / 4; ++e) x[e] = ok ? qsrc[mc * kHeadDim + kc + e] : 0.0f;
-      if constexpr (BF16) {
-        split_bf16x8(x, qhi[c], qlo[c]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qf[c][e] = x[e];
-      }
-    }
-  }
-
-  float acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-  }
-  float* pw = sh.u.p[wave];
-
-  // Software pipeline: the next tile's keys are requested as soon as the
-  // scores have consumed this tile's keys, its values as soon as the value
-  // sums have consumed this tile's values.
-  for (int t0 = t_first; t0 < r1; t0 += t_step) {
-    const int tn = t0 + t_step;
-
-    // -- scores on the matrix cores, log2 units (the query is pre-scaled)
-    f32x4_t sc[SUB];
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        if (c < nchk) {
-          if constexpr (BF16) {
-            const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, kbuf[s][c]);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qhi[c], kv, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qlo[c], kv, d, 0, 0, 0);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              d = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[c][e], __uint_as_float(kbuf[s][c][e]),
-                                                       d, 0, 0, 0);
-          }
-        }
-      }
-      if (t0 + 16 * s + n >= r1) d = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      sc[s] = d;
-    }
-    if (tn < r1) load_keys(tn);
-
-    // -- online softmax: tile max per head, rescale only when it grows
-    float mnew[4];
-    bool grew = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = sc[0][i];
-#pragma unroll
-      for (int s = 1; s < SUB; ++s) mx = fmaxf(mx, sc[s][i]);
-      mx = row16_max(mx);
-      mnew[i] = fmaxf(m_run[i], mx);
-      grew |= mnew[i] > m_run[i];
-    }
-    if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-      float alpha[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        alpha[i] = __builtin_amdgcn_exp2f(m_run[i] - mnew[i]);
-        l_run[i] *= alpha[i];
-        m_run[i] = mnew[i];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float ag =
-            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[g & 3]), 16 * (g >> 2)));
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[g][e] *= ag;
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[s][i] - m_run[i]);
-        l_run[i] += p;
-        sc[s][i] = p;
-      }
-      if (kg < NGRP) *reinterpret_cast<f32x4_t*>(&pw[(16 * s + n) * GP + 4 * kg]) = sc[s];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // -- value sums: acc[g][:] += p[row][g] * V[row][cols of this lane]
-#pragma unroll
-    for (int i = 0; i < VMAX; ++i) {
-      if (i < vi_count) {
-        const int rt = i * rpi + vrow;
-        const bool ok = vact && rt < TR && t0 + rt < r1;
-        const int rr = ok ? rt : 0;
-        float pv[GP];
-#pragma unroll
-        for (int j = 0; j < GP; j += 4) {
-          const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&pw[rr * GP + j]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pv[j + e] = ok ? p4[e] : 0.0f;
-        }
-        float v[EPL];
-        if constexpr (BF16) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(vbuf[i][e] << 16);
-            v[2 * e + 1] = __uint_as_float(vbuf[i][e] & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(vbuf[i][e]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pv[g], v[e], acc[g][e]);
-      }
-    }
-    if (tn < r1) load_values(tn);
-    // the next tile overwrites pw: every lane has read it by now
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- merge the four waves' partials into this chunk's partial
-  // (1) per wave: sum the row groups (lanes with equal vcc) by a butterfly:
-  //     DPP rotations inside 16-lane rows, lane swaps across rows
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float x = acc[g][e];
-      if (lpr <= 8) x += dpp_f<0x128>(x);
-      if (lpr <= 4) x += dpp_f<0x124>(x);
-      if (lpr <= 2) x += dpp_f<0x122>(x);
-      if (lpr <= 16) x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[g][e] = x;
-    }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) l_run[i] = row16_sum(l_run[i]);
-  if (n == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = 4 * kg + i;
-      if (g < G) {
-        sh.ml[wave][g][0] = m_run[i];
-        sh.ml[wave][g][1] = l_run[i];
-      }
-    }
-  }
-  __syncthreads();
-  // (2) each wave rescales its sums to the workgroup max and parks them in LDS
-  if (vrow == 0 && vact) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float M = sh.ml[0][g][0];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][g][0]);
-      const float sw = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sh.ml[wave][g][0] - M);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sh.u.red[wave][g][vcc * EPL + e] = acc[g][e] * sw;
-    }
-  }
-  __syncthreads();
-  // (3) sum the four waves, write the piece's partial with coherent stores
-  for (int p = tid; p < G * rv; p += kThreads) {
-    const int g = p / rv, col = p - (p / rv) * rv;
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += sh.u.red[w][g][col];
-    store_coherent(&acc_out[(size_t)g * kHeadDim + col], sum);
-  }
-  if (tid < G) {
-    float M = sh.ml[0][tid][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.ml[w][tid][0]);
-    float L = 0.0f;
-    if (M != -INFINITY)
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.ml[w][tid][0] - M) * sh.ml[w][tid][1];
-    store_coherent(&ml_out[2 * tid], M);
-    store_coherent(&ml_out[2 * tid + 1], L);
-  }
-
-}
-
-// Grid: `chunks` workgroups per (b, kv head) unit.  Workgroup c hosts the
-// unit's waves 4c .. 4c+3; the unit's tiles (beacon, then raw) are dealt
-// round-robin over its 4*chunks waves.  The beacon rows' partial goes to slot 2c, the
-// raw rows' to slot 2c+1; the workgroup that finishes last merges the unit.
+// Grid: `chunks` workgroups per (b, kv head) unit; workgroup c hosts the
+// unit's waves 4c .. 4c+3.  The unit's tiles -- beacon tiles, then raw tiles,
+// all about the same size in bytes -- are dealt round-robin over its
+// 4*chunks waves as one list, so every wave gets the same number of tiles to
+// within one and the waves of a unit advance through one sliding window of
+// rows.  Each wave keeps one tile in flight across the segment boundary.
+// The workgroup writes its beacon partial to slot 2c and its raw partial to
+// slot 2c+1; the workgroup that finishes last merges the unit.
+// NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
+// are full width (rebuilt beacons) or absent.
 template <int G, int NCH, bool BF16>
 __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
+  constexpr bool BLAT = NCH > 0;
+  constexpr int kFullNch = BF16 ? 4 : 8;
+  constexpr int BN = BLAT ? NCH : kFullNch;
   __shared__ AttnShared sh;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
+  const int n = lane & 15, kg = lane >> 4;
   const int k = a.chunks;
   const int unit = blockIdx.x / k;
   const int c = blockIdx.x - unit * k;
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
   const int nwaves = kWaves * k;
-  const int wu = kWaves * c + (tid >> 6);
+  const int wu = kWaves * c + wave;  // this wave's number within the unit
   const size_t slot0 = ((size_t)unit * k + c) * 2;
-  constexpr int kFullNch = BF16 ? 4 : 8;
 
-  // beacon rows (latent, or rebuilt at full width)
-  Segment sg;
-  sg.K = a.seg[0].K;
-  sg.V = a.seg[0].V;
-  sg.kind = a.seg[0].kind;
-  sg.rows = a.seg[0].rows;
-  sg.rk = a.seg[0].rk;
-  sg.rv = a.seg[0].rv;
-  const int btile = sg.kind == kSegLatent ? TileShape<BF16, NCH>::kRows
-                                           : TileShape<BF16, kFullNch>::kRows;
-  const int beacon_tiles = (sg.rows + btile - 1) / btile;
-  if (sg.kind == kSegLatent)
-    attend_segment<G, NCH, BF16>(a, sg, unit, (int)slot0, wu, nwaves, 0, true, sh);
-  else
-    attend_segment<G, kFullNch, BF16>(a, sg, unit, (int)slot0, wu, nwaves, 0, true, sh);
-  __syncthreads();  // LDS is reused by the next segment
+  SegView<BN, BF16> bv;  // beacon rows
+  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, BLAT ? a.seg[0].rk : kHeadDim,
+          BLAT ? a.seg[0].rv : kHeadDim, unit, lane);
+  SegView<kFullNch, BF16> rw;  // raw rows
+  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
+  // dealt positions wu, wu + nwaves, ...: beacon tiles first, then raw tiles;
+  // jr is this wave's first raw tile
+  const int nbt = bv.ntiles;
+  const int jr = ((wu - nbt) % nwaves + nwaves) % nwaves;
+  const int raw_t0 = jr < rw.ntiles ? jr * SegView<kFullNch, BF16>::kRows : -1;
 
-  // raw rows
-  sg.K = a.seg[1].K;
-  sg.V = a.seg[1].V;
-  sg.kind = kSegFull;
-  sg.rows = a.seg[1].rows;
-  sg.rk = kHeadDim;
-  sg.rv = kHeadDim;
-  attend_segment<G, kFullNch, BF16>(a, sg, unit, (int)slot0 + 1, wu, nwaves, beacon_tiles,
-                                    false, sh);
+  // the wave's first tile is in flight while the prologue runs
+  u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
+  if (wu < nbt) {
+    bv.load_keys(wu * SegView<BN, BF16>::kRows, kbuf, n, kg);
+    bv.load_values(wu * SegView<BN, BF16>::kRows, vbuf);
+  } else if (raw_t0 >= 0) {
+    rw.load_keys(raw_t0, kbuf, n, kg);
+    rw.load_values(raw_t0, vbuf);
+  }
+  prologue<G, BF16, BLAT>(a, b, h, sh);
 
-  // ---- the last chunk of the unit merges everything.  Every thread waits
-  // for its coherent partial stores to complete before the barrier; only
-  // then does thread 0 count the chunk as done.  The workgroup that brings
-  // the count to k reads all partials with coherent loads.
+  float* pw = sh.u.s.t.p[wave];
+  WaveState<G, BF16> st;
+  st.reset();
+  sweep<G, BN, BF16, kFullNch>(bv, rw, wu, nwaves, raw_t0, BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0],
+                               bv.rk, kbuf, vbuf, pw, st);
+  wave_reduce<G, BF16>(st, bv.lpr);
+  wave_park<G, BN, BF16>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
+  st.reset();
+  sweep<G, kFullNch, BF16, kFullNch>(rw, rw, jr, nwaves, -1, &sh.qrot[0][0], kHeadDim, kbuf, vbuf,
+                                     pw, st);
+  wave_reduce<G, BF16>(st, rw.lpr);
+  __syncthreads();  // every wave is done with its exp-weights, which alias the raw sums
+  wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
+  __syncthreads();
+
+  // U_V rows of this wave's lift tiles: in flight while the partials are
+  // written, in case this workgroup turns out to be the unit's last
+  u32x4_t uw[2][4];
+  if constexpr (BF16 && BLAT) {
+    const int rv = a.rank_v;
+    const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int i = 16 * (wave + kWaves * t) + n, k0 = 32 * cc + 8 * kg;
+        // features past r_V meet zero latent entries in the lift
+        uw[t][cc] = load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) uw[t][cc] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  combine_store<G>(sh.u.s.beacon, sh.wml[0], bv.rv, a.part_ml + slot0 * G * 2,
+                   a.part_acc + slot0 * G * kHeadDim);
+  combine_store<G>(sh.u.s.t.raw, sh.wml[1], kHeadDim, a.part_ml + (slot0 + 1) * G * 2,
+                   a.part_acc + (slot0 + 1) * G * kHeadDim);
+
+  // ---- the last workgroup of the unit merges everything.  Every thread
+  // waits for its coherent partial stores to complete before the barrier;
+  // only then does thread 0 count the workgroup as done.  The workgroup that
+  // brings the count to k reads all partials with coherent loads.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -775,7 +860,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   }
   __syncthreads();
   if (!sh.is_last) return;
-  merge_unit<G, BF16>(a, unit, b, h, sh);
+  merge_unit<G, BF16, BLAT>(a, unit, b, h, sh, uw);
   if (tid == 0)  // ready for the next call
     __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -784,16 +869,18 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
 // device, cached per (device, kernel).
 int device_slots(const void* kfn);
 
-// Launch for group size G; nch is the MFMA chunk count of the latent
-// segment (1..4 for bf16; fp32 always uses 8).
+// Launch for group size G; nch is the MFMA chunk count of a latent beacon
+// segment (1..4 for bf16; fp32 uses 8), 0 for full-width or absent beacons.
 template <int G>
 hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   const void* kfn;
   if (dtype == 0) {
-    kfn = reinterpret_cast<const void*>(&attention_kernel<G, 8, false>);
+    kfn = nch == 0 ? reinterpret_cast<const void*>(&attention_kernel<G, 0, false>)
+                   : reinterpret_cast<const void*>(&attention_kernel<G, 8, false>);
   } else {
     switch (nch) {
+      case 0: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 0, true>); break;
       case 1: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 1, true>); break;
       case 2: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 2, true>); break;
       case 3: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 3, true>); break;
