@@ -100,6 +100,20 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Raw storage bits of element i (bf16 zero-extended), converted later by
+// bits_to_float: the conversion is what a load's wait attaches to.
+template <bool BF16>
+__device__ __forceinline__ uint32_t ld_bits(const void* p, size_t i) {
+  if constexpr (BF16)
+    return static_cast<const uint16_t*>(p)[i];
+  else
+    return static_cast<const uint32_t*>(p)[i];
+}
+template <bool BF16>
+__device__ __forceinline__ float bits_to_float(uint32_t u) {
+  return __uint_as_float(BF16 ? u << 16 : u);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void* p, size_t i) {
   if constexpr (BF16)
@@ -175,76 +189,91 @@ __device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
 // Prologue, run by every workgroup for its (b, kv head): the G query heads
 // rotated at the query position (rotate-half pairs (i, i + d/2), double
 // precision, angles reduced mod 2*pi) and pre-scaled by scale * log2(e) into
-// sh.qrot; with a latent beacon segment also sh.qlat = U_K^T qrot (fp32 MFMA
-// 16x16x4, exact products).  Every global read is issued up front.
+// sh.qrot; with latent beacons also sh.qlat = U_K^T qrot (fp32 MFMA 16x16x4,
+// exact products).  issue() requests every input; the caller then requests
+// its first cache tile and calls finish().  Memory returns in request order,
+// so the prologue's inputs arrive ahead of the tile and its arithmetic
+// overlaps the tile's flight.
 template <int G, bool BF16, bool BLAT>
-__device__ __forceinline__ void prologue(const AttnArgs& a, int b, int h, AttnShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int n = lane & 15, kg = lane >> 4;
-  const int rk = a.rank_k;
-  constexpr bool latent = BLAT;
-  constexpr int half = kHeadDim / 2;
-  constexpr int kPairs = (G * half + kThreads - 1) / kThreads;  // rotation pairs per thread
-  constexpr int kTiles = kHeadDim / 16 / kWaves;                // latent column tiles per wave
+struct QueryPrologue {
+  static constexpr int kHalf = kHeadDim / 2;
+  static constexpr int kPairs = (G * kHalf + kThreads - 1) / kThreads;  // rotation pairs per thread
+  static constexpr int kTiles = BLAT ? kHeadDim / 16 / kWaves : 0;       // latent column tiles per wave
+  uint32_t x1[kPairs], x2[kPairs];                   // storage bits of the query pairs
+  int pos;
+  uint32_t ub[kTiles > 0 ? kTiles : 1][kHeadDim / 4];  // U_K column (c0 + n) of each tile, rows 4s + kg
 
-  // loads are unconditional from clamped (in-bounds) addresses: a load under
-  // a divergent branch costs a full wait for the memory round trip
-  float x1[kPairs], x2[kPairs];
+  // Every load here is unconditional, from a clamped (in-bounds) address, and
+  // nothing converts its result before finish(): a load whose value is used
+  // under a branch, or converted early, would be waited for before the tile's
+  // loads are even issued.
+  __device__ __forceinline__ void issue(const AttnArgs& a, int b, int h, int wave) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n = lane & 15, kg = lane >> 4;
 #pragma unroll
-  for (int j = 0; j < kPairs; ++j) {
-    const int p = min(tid + kThreads * j, G * half - 1);
-    const int g = p / half, i = p % half;
-    const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
-    x1[j] = ld_elem<BF16>(a.q, base + i);
-    x2[j] = ld_elem<BF16>(a.q, base + i + half);
-  }
-  const double pos = (double)a.q_pos[b];
-  // U_K columns of this wave's first latent tile (a second tile, r_K > 64,
-  // is loaded after the first one's products)
-  float ub[kHeadDim / 4];
-  const char* U = static_cast<const char*>(a.U_K) + (size_t)h * kHeadDim * rk * Traits<BF16>::kElemBytes;
-  auto load_ub = [&](int c0) {
-#pragma unroll
-    for (int s = 0; s < kHeadDim / 4; ++s) ub[s] = ld_elem<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
-  };
-  if (latent && 16 * wave < rk) load_ub(16 * wave);  // wave-uniform
-
-#pragma unroll
-  for (int j = 0; j < kPairs; ++j) {
-    const int p = tid + kThreads * j;
-    if (p < G * half) {
-      const int g = p / half, i = p % half;
-      double sn, cs;
-      // theta^(-2i/d) = 2^(-(2i/d) log2 theta), in double precision
-      const double inv_freq = exp2(-(double)(2 * i) / (double)kHeadDim * a.log2_theta);
-      rope_sincos(pos * inv_freq, sn, cs);
-      const double v1 = x1[j], v2 = x2[j];
-      sh.qrot[g][i] = (float)((v1 * cs - v2 * sn) * a.score_scale);
-      sh.qrot[g][i + half] = (float)((v2 * cs + v1 * sn) * a.score_scale);
+    for (int j = 0; j < kPairs; ++j) {
+      const int p = min(tid + kThreads * j, G * kHalf - 1);
+      const int g = p / kHalf, i = p % kHalf;
+      const size_t base = ((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
+      x1[j] = ld_bits<BF16>(a.q, base + i);
+      x2[j] = ld_bits<BF16>(a.q, base + i + kHalf);
     }
-  }
-  __syncthreads();
-  if constexpr (!latent) return;
-  // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
+    pos = a.q_pos[b];
+    if constexpr (BLAT) {
+      const int rk = a.rank_k;
+      const char* U = static_cast<const char*>(a.U_K) + (size_t)h * kHeadDim * rk * Traits<BF16>::kElemBytes;
 #pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    const int c0 = 16 * (wave + kWaves * t);
-    if (c0 < rk) {
-      if (t > 0) load_ub(c0);
-      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < kTiles; ++t) {
+        // tiles past r_K load a valid tile again (a branch here would make
+        // the compiler wait for these loads); finish() skips them
+        const int c0 = min(16 * (wave + kWaves * t), rk - 16);
 #pragma unroll
-      for (int s = 0; s < kHeadDim / 4; ++s) {
-        const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
-        d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, ub[s], d, 0, 0, 0);
+        for (int s = 0; s < kHeadDim / 4; ++s)
+          ub[t][s] = ld_bits<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
     }
   }
-  __syncthreads();
-}
+
+  __device__ __forceinline__ void finish(const AttnArgs& a, AttnShared& sh, int wave) const {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int n = lane & 15, kg = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+      const int p = tid + kThreads * j;
+      if (p < G * kHalf) {
+        const int g = p / kHalf, i = p % kHalf;
+        double sn, cs;
+        // theta^(-2i/d) = 2^(-(2i/d) log2 theta), in double precision
+        const double inv_freq = exp2(-(double)(2 * i) / (double)kHeadDim * a.log2_theta);
+        rope_sincos((double)pos * inv_freq, sn, cs);
+        const double v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
+        sh.qrot[g][i] = (float)((v1 * cs - v2 * sn) * a.score_scale);
+        sh.qrot[g][i + kHalf] = (float)((v2 * cs + v1 * sn) * a.score_scale);
+      }
+    }
+    __syncthreads();
+    if constexpr (BLAT) {
+      const int rk = a.rank_k;
+      // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int c0 = 16 * (wave + kWaves * t);
+        if (c0 < rk) {
+          f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int s = 0; s < kHeadDim / 4; ++s) {
+            const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
+            d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bits_to_float<BF16>(ub[t][s]), d, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
+        }
+      }
+      __syncthreads();
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Partials cross workgroups and XCDs (whose L2s are not coherent with each
@@ -796,7 +825,10 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int jr = ((wu - nbt) % nwaves + nwaves) % nwaves;
   const int raw_t0 = jr < rw.ntiles ? jr * SegView<kFullNch, BF16>::kRows : -1;
 
-  // the wave's first tile is in flight while the prologue runs
+  // the prologue's inputs, then the wave's first tile: the prologue's
+  // arithmetic runs while the tile is in flight
+  QueryPrologue<G, BF16, BLAT> pro;
+  pro.issue(a, b, h, wave);
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
   if (wu < nbt) {
     bv.load_keys(wu * SegView<BN, BF16>::kRows, kbuf, n, kg);
@@ -805,7 +837,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
     rw.load_keys(raw_t0, kbuf, n, kg);
     rw.load_values(raw_t0, vbuf);
   }
-  prologue<G, BF16, BLAT>(a, b, h, sh);
+  pro.finish(a, sh, wave);
 
   float* pw = sh.u.s.t.p[wave];
   WaveState<G, BF16> st;
