@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 1
+#define SLIMKV_ABI_VERSION 2
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -96,10 +96,21 @@ typedef struct slimkv_problem {
   float scale;          /* softmax scale, finite and > 0 (e.g. 1/sqrt(d))   */
   int32_t dtype;        /* slimkv_dtype of q, U_K, U_V, C_K, C_V, K, V       */
   double rope_theta;    /* rotary base, finite and > 1                       */
-  int32_t num_splits;   /* 0: library picks; > 0: equal-byte chunks each
-                           (b, kv head)'s rows are cut into (at most 64)    */
-  int32_t reserved;     /* must be 0                                         */
+  int32_t num_splits;   /* 0: library picks; > 0: workgroups that share each
+                           (b, kv head)'s rows (at most 64)                 */
+  int32_t flags;        /* 0 or SLIMKV_FLAG_DETERMINISTIC; other bits 0      */
 } slimkv_problem;
+
+/*
+ * Row scheduling.  By default the workgroups of a (b, kv head) take its
+ * rows tile by tile from a shared counter, so faster ones take more; the
+ * order in which rows are summed then depends on timing, and repeated calls
+ * agree only to rounding (well inside the documented tolerances).  With
+ * SLIMKV_FLAG_DETERMINISTIC the tiles are dealt round-robin in a fixed
+ * order: repeated calls on the same device and problem give bitwise equal
+ * out and lse, somewhat slower.
+ */
+#define SLIMKV_FLAG_DETERMINISTIC 1
 
 /*
  * Workspace bytes the given op needs for this problem, or 0 if the problem

@@ -18,6 +18,7 @@ LIBRARY = pathlib.Path(__file__).resolve().parent / "libslimkv.so"
 
 SLIMKV_FP32, SLIMKV_BF16 = 0, 1
 SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV = 0, 1, 2
+SLIMKV_FLAG_DETERMINISTIC = 1
 STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
@@ -43,7 +44,7 @@ class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
         ("dtype", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
         ("num_splits", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -93,11 +94,11 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
 
 
 def make_problem(*, batch, num_q_heads, num_kv_heads, num_beacons, rank_k, rank_v, raw_window,
-                 scale, rope_theta, dtype, head_dim=128, num_splits=0) -> slimkv_problem:
+                 scale, rope_theta, dtype, head_dim=128, num_splits=0, flags=0) -> slimkv_problem:
     dt = {"fp32": SLIMKV_FP32, "bf16": SLIMKV_BF16, torch.float32: SLIMKV_FP32,
           torch.bfloat16: SLIMKV_BF16}.get(dtype, dtype)
     return slimkv_problem(batch, num_q_heads, num_kv_heads, head_dim, num_beacons, rank_k, rank_v,
-                          raw_window, scale, dt, rope_theta, num_splits, 0)
+                          raw_window, scale, dt, rope_theta, num_splits, flags)
 
 
 def _ptr(t) -> int | None:

@@ -53,7 +53,8 @@ slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
   if (!p) return fail(SLIMKV_ERR_NULL, "problem is NULL");
   if (op != SLIMKV_OP_LATENT && op != SLIMKV_OP_RECONSTRUCT && op != SLIMKV_OP_FULL_KV)
     return fail(SLIMKV_ERR_UNSUPPORTED, "unknown op %d", (int)op);
-  if (p->reserved != 0) return fail(SLIMKV_ERR_SHAPE, "reserved field must be 0");
+  if ((p->flags & ~SLIMKV_FLAG_DETERMINISTIC) != 0)
+    return fail(SLIMKV_ERR_SHAPE, "unknown flag bits 0x%x", (unsigned)p->flags);
   if (p->dtype != SLIMKV_FP32 && p->dtype != SLIMKV_BF16)
     return fail(SLIMKV_ERR_UNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p->dtype);
   if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
@@ -123,6 +124,7 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   }
   a.unit_bytes = (int64_t)sb.rows * sb.row_bytes + (int64_t)sr.rows * sr.row_bytes;
   a.chunks = p->num_splits > 0 ? std::min(p->num_splits, kMaxChunks) : 0;  // 0: launcher picks
+  a.deterministic = (p->flags & SLIMKV_FLAG_DETERMINISTIC) != 0;
   if (pl.units * kMaxChunks > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
@@ -132,7 +134,7 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   // partial slots per chunk for up to kMaxChunks chunks
   const int64_t G = a.group, slots = 2 * kMaxChunks;
   pl.off_counters = 0;
-  size_t off = round_up(pl.units * sizeof(uint32_t), kAlign);
+  size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
   off = round_up(off + (size_t)(pl.units * slots * G * 2) * sizeof(float), kAlign);
   pl.off_acc = off;

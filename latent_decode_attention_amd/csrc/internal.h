@@ -12,7 +12,8 @@ constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
-constexpr int kMaxChunks = 64;         // row chunks per unit (each writes 2 partial slots)
+constexpr int kMaxChunks = 64;         // workgroups per unit (each writes 2 partial slots)
+constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -39,7 +40,8 @@ struct Segment {
 struct AttnArgs {
   Segment seg[2];
   int32_t batch, num_q_heads, num_kv_heads, group;
-  int32_t chunks;         // chunks per unit (grid = units * chunks)
+  int32_t chunks;         // workgroups per unit (grid = units * chunks)
+  int32_t deterministic;  // 1: tiles dealt round-robin, not from the counter
   int64_t unit_bytes;     // cache bytes per unit over both segments
   int32_t rank_v;         // r_V of a latent beacon segment (0 if none)
   const void* q;          // [B, H_q, d] before rotation
@@ -49,7 +51,8 @@ struct AttnArgs {
   double score_scale;     // scale * log2(e): scores are kept in log2 units
   double log2_theta;      // log2(rope theta), computed on the host in fp64
   int32_t rank_k;         // r_K of a latent beacon segment (0 if none)
-  uint32_t* counters;     // [units] finished-chunk counters (zero between calls)
+  uint32_t* counters;     // [units][kCounterStride]: workgroups done, tiles handed out
+                          // (zero between calls)
   float* part_ml;         // [units, 2 * chunks, G, 2]  (max, sum of exp)
   float* part_acc;        // [units, 2 * chunks, G, d]  exp-weighted value sums
   float* out;             // [B, H_q, d]

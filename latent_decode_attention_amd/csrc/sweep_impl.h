@@ -148,8 +148,9 @@ struct TileShape {
   static constexpr int kRows = 16 * kSub;
 };
 
-// LDS of one attention workgroup.  The sweep arrays are dead once the
-// workgroup's partials are written; the unit merge then reuses them.
+// LDS of one attention workgroup.  The prologue's staged U_K is dead once
+// the latent query is formed, the sweep arrays once the workgroup's partials
+// are written; the sweep and the unit merge reuse that space.
 struct alignas(16) AttnShared {
   union {
     struct {
@@ -159,6 +160,9 @@ struct alignas(16) AttnShared {
       } t;
       float beacon[kWaves][kMaxGroup][kHeadDim];  // each wave's beacon-row sums
     } s;
+    struct {
+      uint16_t uk[kHeadDim * (kHeadDim + 2)];  // bf16 U_K, rows padded by 2 elements
+    } pro;
     struct {
       float ml[2 * kMaxChunks * kMaxGroup][2];  // every slot's (max, sum); then its weight
       f32x4_t part[kThreads][2];                // per-thread sums over one group of slots
@@ -194,19 +198,26 @@ __device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
 // its first cache tile and calls finish().  Memory returns in request order,
 // so the prologue's inputs arrive ahead of the tile and its arithmetic
 // overlaps the tile's flight.
-template <int G, bool BF16, bool BLAT>
+template <int G, bool BF16, int NCH>
 struct QueryPrologue {
+  static constexpr bool kLat = NCH > 0;           // latent beacons: project the query
+  static constexpr bool kStage = BF16 && kLat;    // U_K staged through LDS
   static constexpr int kHalf = kHeadDim / 2;
   static constexpr int kPairs = (G * kHalf + kThreads - 1) / kThreads;  // rotation pairs per thread
-  static constexpr int kTiles = BLAT ? kHeadDim / 16 / kWaves : 0;       // latent column tiles per wave
-  uint32_t x1[kPairs], x2[kPairs];                   // storage bits of the query pairs
+  static constexpr int kTiles = kLat ? kHeadDim / 16 / kWaves : 0;       // latent column tiles per wave
+  // 16-byte words of U_K per thread when staged: r_K <= 32 * NCH
+  static constexpr int kWords = kStage ? kHeadDim * 32 * NCH / 8 / kThreads : 1;
+  static constexpr int kGather = (kLat && !kStage) ? kTiles : 1;
+
+  uint32_t x1[kPairs], x2[kPairs];    // storage bits of the query pairs
   int pos;
-  uint32_t ub[kTiles > 0 ? kTiles : 1][kHeadDim / 4];  // U_K column (c0 + n) of each tile, rows 4s + kg
+  u32x4_t uk[kWords];                 // staged: U_K words, row-major
+  uint32_t ub[kGather][kHeadDim / 4]; // fp32: U_K column (c0 + n) of each tile, rows 4s + kg
 
   // Every load here is unconditional, from a clamped (in-bounds) address, and
-  // nothing converts its result before finish(): a load whose value is used
-  // under a branch, or converted early, would be waited for before the tile's
-  // loads are even issued.
+  // nothing converts or stores its result before finish(): a load whose
+  // value is used under a branch, or early, would be waited for before the
+  // tile's loads are even issued.
   __device__ __forceinline__ void issue(const AttnArgs& a, int b, int h, int wave) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;
@@ -219,17 +230,22 @@ struct QueryPrologue {
       x2[j] = ld_bits<BF16>(a.q, base + i + kHalf);
     }
     pos = a.q_pos[b];
-    if constexpr (BLAT) {
+    if constexpr (kLat) {
       const int rk = a.rank_k;
       const char* U = static_cast<const char*>(a.U_K) + (size_t)h * kHeadDim * rk * Traits<BF16>::kElemBytes;
+      if constexpr (kStage) {
+        const int words = kHeadDim * rk / 8;  // surplus words load the last one again
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        // tiles past r_K load a valid tile again (a branch here would make
-        // the compiler wait for these loads); finish() skips them
-        const int c0 = min(16 * (wave + kWaves * t), rk - 16);
+        for (int w = 0; w < kWords; ++w) uk[w] = load16(U + (size_t)min(tid + kThreads * w, words - 1) * 16);
+      } else {
 #pragma unroll
-        for (int s = 0; s < kHeadDim / 4; ++s)
-          ub[t][s] = ld_bits<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
+        for (int t = 0; t < kTiles; ++t) {
+          // tiles past r_K load a valid tile again; finish() skips them
+          const int c0 = min(16 * (wave + kWaves * t), rk - 16);
+#pragma unroll
+          for (int s = 0; s < kHeadDim / 4; ++s)
+            ub[t][s] = ld_bits<BF16>(U, (size_t)(4 * s + kg) * rk + c0 + n);
+        }
       }
     }
   }
@@ -237,6 +253,22 @@ struct QueryPrologue {
   __device__ __forceinline__ void finish(const AttnArgs& a, AttnShared& sh, int wave) const {
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;
+    const int rk = kLat ? a.rank_k : 0;
+    const int ustride = rk + 2;  // staged row stride in elements: conflict-free column reads
+    uint16_t* ul = sh.u.pro.uk;
+    if constexpr (kStage) {
+      const int words = kHeadDim * rk / 8, wpr = rk / 8;
+#pragma unroll
+      for (int w = 0; w < kWords; ++w) {
+        const int idx = tid + kThreads * w;
+        if (idx < words) {
+          const int row = idx / wpr, c8 = idx - row * wpr;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(ul + row * ustride + c8 * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[e] = uk[w][e];
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kPairs; ++j) {
       const int p = tid + kThreads * j;
@@ -252,18 +284,41 @@ struct QueryPrologue {
       }
     }
     __syncthreads();
-    if constexpr (BLAT) {
-      const int rk = a.rank_k;
-      // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k], K = i in steps of 4
+    if constexpr (kLat) {
+      // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k] per 16-column tile
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
         const int c0 = 16 * (wave + kWaves * t);
         if (c0 < rk) {
           f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (kStage) {
+            // bf16 MFMA over K = i in chunks of 32: the query as hi + lo bf16
+            // terms, U_K exact; lane (n, kg) takes rows 32c + 8kg .. +7 of
+            // column c0 + n
 #pragma unroll
-          for (int s = 0; s < kHeadDim / 4; ++s) {
-            const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
-            d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bits_to_float<BF16>(ub[t][s]), d, 0, 0, 0);
+            for (int c = 0; c < kHeadDim / 32; ++c) {
+              const int i0 = 32 * c + 8 * kg;
+              float x[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) x[e] = n < G ? sh.qrot[n][i0 + e] : 0.0f;
+              bf16x8_t hi, lo;
+              split_bf16x8(x, hi, lo);
+              u32x4_t bw;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                bw[e] = (uint32_t)ul[(i0 + 2 * e) * ustride + c0 + n] |
+                        ((uint32_t)ul[(i0 + 2 * e + 1) * ustride + c0 + n] << 16);
+              const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, d, 0, 0, 0);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, d, 0, 0, 0);
+            }
+          } else {
+            // fp32: exact products, K = i in steps of 4
+#pragma unroll
+            for (int s = 0; s < kHeadDim / 4; ++s) {
+              const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
+              d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bits_to_float<BF16>(ub[t][s]), d, 0, 0, 0);
+            }
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -318,33 +373,55 @@ struct SegView {
     vcol = min(vcc, lanes_row - 1) * Tr::kEpl;  // clamped for idle lanes
   }
 
-  // Every load is unconditional, from an address clamped into the segment
-  // and the row's width: rows past `rows` get score -inf, features past r_K
-  // meet zero query entries, and value rows past `rows` get weight 0, so the
-  // clamped data never contributes (a load under a divergent branch would
-  // cost a full memory round trip each).  Callers only ask for tiles that
-  // exist, so `rows` >= 1 here.
-  // Keys as MFMA B operands: lane (n, kg) holds features c*KCH + kg*EPL ...
-  // of row t0 + 16 s + n in kb[s * NCH + c].
-  __device__ __forceinline__ void load_keys(int t0, u32x4_t* kb, int n, int kg) const {
-#pragma unroll
-    for (int sb = 0; sb < kSub; ++sb)
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int row = min(t0 + 16 * sb + n, rows - 1);
-        const int k0 = min(c * Tr::kChunkK + kg * Tr::kEpl, rk - Tr::kEpl);
-        kb[sb * NCH + c] = load16(K + ((size_t)row * rk + k0) * Tr::kElemBytes);
-      }
+  // Addresses are clamped into the segment and the row's width: rows past
+  // `rows` get score -inf, features past r_K meet zero query entries, and
+  // value rows past `rows` get weight 0, so the clamped data never
+  // contributes.  Only called for segments with rows >= 1 when the address
+  // is used.
+  // Key slot i = s * NCH + c as an MFMA B operand: lane (n, kg) holds
+  // features c*KCH + kg*EPL ... of row t0 + 16 s + n.
+  __device__ __forceinline__ const char* key_ptr(int t0, int i, int n, int kg) const {
+    const int sb = i / NCH, c = i - (i / NCH) * NCH;
+    const int row = min(t0 + 16 * sb + n, rows - 1);
+    const int k0 = min(c * Tr::kChunkK + kg * Tr::kEpl, rk - Tr::kEpl);
+    return K + ((size_t)row * rk + k0) * Tr::kElemBytes;
   }
-  // Values: load i covers rows t0 + i * rpi + vrow, this lane's 16 bytes.
-  __device__ __forceinline__ void load_values(int t0, u32x4_t* vb) const {
-#pragma unroll
-    for (int i = 0; i < Tr::kMaxLoads; ++i) {
-      const int row = min(t0 + i * rpi + vrow, rows - 1);
-      vb[i] = load16(V + ((size_t)row * rv + vcol) * Tr::kElemBytes);
-    }
+  // Value slot i: row t0 + i * rpi + vrow, this lane's 16 bytes.
+  __device__ __forceinline__ const char* val_ptr(int t0, int i) const {
+    const int row = min(t0 + i * rpi + vrow, rows - 1);
+    return V + ((size_t)row * rv + vcol) * Tr::kElemBytes;
   }
 };
+
+// Request one tile's keys (or values) into the wave's tile registers: tile
+// ta of `a` if use_a, else tile tb of `b` if use_b, else nothing useful (a
+// re-read of `dummy`, any valid 16-byte-aligned address).  Every slot is one
+// unconditional load whose address is selected, so the registers need no
+// copies afterwards (separate loads per source under a branch would be
+// merged by copies that wait for the loads).
+template <int NA, int NB, bool BF16>
+__device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16>& a, int ta, bool use_a,
+                                               const SegView<NB, BF16>& b, int tb, bool use_b,
+                                               const void* dummy, u32x4_t* kbuf, int n, int kg) {
+  constexpr int KA = SegView<NA, BF16>::kSub * NA, KB = SegView<NB, BF16>::kSub * NB;
+  constexpr int K = KA > KB ? KA : KB;
+  const char* d = static_cast<const char*>(dummy);
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const char* pa = i < KA ? a.key_ptr(ta, i, n, kg) : d;
+    const char* pb = i < KB ? b.key_ptr(tb, i, n, kg) : d;
+    kbuf[i] = load16(use_a ? pa : (use_b ? pb : d));
+  }
+}
+template <int NA, int NB, bool BF16>
+__device__ __forceinline__ void load_tile_values(const SegView<NA, BF16>& a, int ta, bool use_a,
+                                                 const SegView<NB, BF16>& b, int tb, bool use_b,
+                                                 const void* dummy, u32x4_t* vbuf) {
+  const char* d = static_cast<const char*>(dummy);
+#pragma unroll
+  for (int i = 0; i < Traits<BF16>::kMaxLoads; ++i)
+    vbuf[i] = load16(use_a ? a.val_ptr(ta, i) : (use_b ? b.val_ptr(tb, i) : d));
+}
 
 // One wave's running softmax state over the rows it has swept: max and sum
 // per head in the MFMA output layout (head 4*kg + i in element i), value sums
@@ -367,18 +444,50 @@ struct WaveState {
 };
 
 // ---------------------------------------------------------------------------
-// One wave's tiles of one segment: j0, j0 + jstep, ... < sv.ntiles.  The
-// loads of tile j0 are already in kbuf/vbuf.  Software pipeline: the next
-// tile's keys are requested as soon as the scores have consumed this tile's
-// keys, its values as soon as the value sums have consumed this tile's
-// values.  After the last tile the next segment's first tile for this wave
-// (`nx` at row nx_t0; nx_t0 < 0: none) is requested the same way, so the
-// stream of loads does not stop between segments.
+// Where a wave's next tile comes from.  A unit's tiles have positions
+// 0 .. total-1 (beacon tiles, then raw tiles); wave w of the unit starts at
+// position w, and every later position is handed out by the unit's counter
+// (offset by the unit's wave count), so waves that run faster take more
+// tiles and the unit's waves finish together.  Positions only grow, so a
+// wave meets its beacon tiles before its raw tiles.  A position is requested
+// one tile ahead: the counter's reply comes back while a tile is in flight.
+// With `fixed` set the positions are dealt round-robin instead (wave w gets
+// w, w + base, w + 2 base, ...): the same tiles in the same order on every
+// call, so results repeat bit for bit.
+struct TileFeed {
+  uint32_t* grab;    // the unit's counter (zero between calls)
+  int base;          // positions below base are the waves' first tiles
+  bool fixed;        // wave-uniform
+  uint32_t pending;  // lane 0: the counter's reply to the last request
+
+  // An increment with wrap-around at 2^32 - 1, i.e. a plain +1.  (A fetch-add
+  // here would be rewritten into a wave-wide atomic whose per-lane results
+  // are formed right away, waiting for every load in flight.)
+  __device__ __forceinline__ void request(int lane) {
+    if (!fixed && lane == 0)
+      pending = __builtin_amdgcn_atomic_inc32(grab, 0xffffffffu, __ATOMIC_RELAXED, "agent");
+  }
+  // the position after j
+  __device__ __forceinline__ int take(int j) const {
+    return fixed ? j + base : base + (int)__builtin_amdgcn_readfirstlane(pending);
+  }
+};
+
+// One wave's tiles of one segment, whose tile 0 has position pbase.  On
+// entry the loads of the tile at position j are in kbuf/vbuf and a request
+// to `feed` is outstanding.  Software pipeline: the next tile's keys are
+// requested as soon as the scores have consumed this tile's keys, its
+// values as soon as the value sums have consumed this tile's values.  When
+// the next position lies past this segment but before pend, it is a tile of
+// the next segment (`nx`, tile 0 at position nxbase) and is requested the
+// same way, so the stream of loads does not stop between segments (past
+// pend the slots re-read this segment's first row instead).  On exit j is
+// the first position past this segment the wave drew.
 template <int G, int NCH, bool BF16, int NCH2>
-__device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegView<NCH2, BF16>& nx,
-                                      int j0, int jstep, int nx_t0, const float* qsrc, int rq,
-                                      u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
-                                      WaveState<G, BF16>& st) {
+__device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
+                                      const SegView<NCH2, BF16>& nx, int nxbase, int pend, int& j,
+                                      TileFeed& feed, const float* qsrc, int rq, u32x4_t* kbuf,
+                                      u32x4_t* vbuf, float* pw, WaveState<G, BF16>& st) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
@@ -388,7 +497,9 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegVie
   constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
   constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
   static_assert(SUB * NCH <= Tr::kMaxLoads, "tile too large");
-  if (j0 >= sv.ntiles) return;  // wave-uniform
+  constexpr int TR2 = SegView<NCH2, BF16>::kRows;
+  const int pstop = pbase + sv.ntiles;
+  if (j >= pstop) return;  // wave-uniform
 
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;   // MFMA column (cache row) within a subtile
@@ -415,10 +526,8 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegVie
   const int nchk = (sv.rk + KCH - 1) / KCH;  // chunks that carry key features
   const int r1 = sv.rows;
 
-  for (int j = j0; j < sv.ntiles; j += jstep) {
-    const int t0 = j * TR;
-    const bool more = j + jstep < sv.ntiles;  // wave-uniform
-    const int tn = t0 + jstep * TR;
+  while (j < pstop) {
+    const int t0 = (j - pbase) * TR;
 
     // -- scores on the matrix cores, log2 units (the query is pre-scaled)
     f32x4_t sc[SUB];
@@ -443,15 +552,11 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegVie
       if (t0 + 16 * s + n >= r1) d = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       sc[s] = d;
     }
-    if (more) {
-      sv.load_keys(tn, kbuf, n, kg);
-    } else if (nx_t0 >= 0) {
-      // opaque copy: keeps the address arithmetic of this once-per-segment
-      // load from being hoisted out of the loop (it would hold registers)
-      int t = nx_t0;
-      asm volatile("" : "+s"(t));
-      nx.load_keys(t, kbuf, n, kg);
-    }
+    const int jn = feed.take(j);  // wave-uniform
+    const bool more = jn < pstop;
+    const bool cross = !more && jn < pend;
+    load_tile_keys(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, sv.K, kbuf, n, kg);
+    feed.request(lane);
 
     // -- online softmax: tile max per head, rescale only when it grows
     float mnew[4];
@@ -527,17 +632,12 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, const SegVie
           for (int e = 0; e < EPL; ++e) st.acc[g][e] = fmaf(pv[g], v[e], st.acc[g][e]);
       }
     }
-    if (more) {
-      sv.load_values(tn, vbuf);
-    } else if (nx_t0 >= 0) {
-      int t = nx_t0;
-      asm volatile("" : "+s"(t));
-      nx.load_values(t, vbuf);
-    }
+    load_tile_values(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, sv.K, vbuf);
     // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    j = jn;
   }
 }
 
@@ -786,14 +886,20 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 }
 
 // ---------------------------------------------------------------------------
-// Grid: `chunks` workgroups per (b, kv head) unit; workgroup c hosts the
-// unit's waves 4c .. 4c+3.  The unit's tiles -- beacon tiles, then raw tiles,
-// all about the same size in bytes -- are dealt round-robin over its
-// 4*chunks waves as one list, so every wave gets the same number of tiles to
-// within one and the waves of a unit advance through one sliding window of
-// rows.  Each wave keeps one tile in flight across the segment boundary.
-// The workgroup writes its beacon partial to slot 2c and its raw partial to
-// slot 2c+1; the workgroup that finishes last merges the unit.
+// Grid: `chunks` workgroups per (b, kv head) unit, numbered chunk-major
+// (block = c * units + (unit - c) mod units).  Workgroups are placed on the
+// CUs in block order, the older workgroups on a CU are served first, and
+// blocks are dealt to the XCDs in turn, whose speeds differ a little; so a
+// unit made of consecutive blocks, or of blocks on one XCD, would run at the
+// speed of its slot or its XCD.  This numbering gives every unit workgroups
+// of every age on different XCDs, and the unit's tile counter lets the
+// faster ones take more tiles, so the units finish together.  Workgroup c hosts the unit's waves 4c .. 4c+3.  The unit's
+// tiles -- beacon tiles, then raw tiles, all about the same size in bytes --
+// are handed out in order (see TileFeed), so the waves of a unit advance
+// through one sliding window of rows; each wave keeps one tile in flight,
+// across the segment boundary too.  The workgroup writes its beacon
+// partial to slot 2c and its raw partial to slot 2c+1; the workgroup that
+// finishes last merges the unit.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
 template <int G, int NCH, bool BF16>
@@ -806,8 +912,10 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int n = lane & 15, kg = lane >> 4;
   const int k = a.chunks;
-  const int unit = blockIdx.x / k;
-  const int c = blockIdx.x - unit * k;
+  const int units = a.batch * a.num_kv_heads;
+  const int c = blockIdx.x / units;
+  // rotated by c, so that a unit's blocks sit on different XCDs
+  const int unit = (int)(((int64_t)blockIdx.x - (int64_t)c * units + c) % units);
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
   const int nwaves = kWaves * k;
@@ -819,36 +927,39 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
           BLAT ? a.seg[0].rv : kHeadDim, unit, lane);
   SegView<kFullNch, BF16> rw;  // raw rows
   rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
-  // dealt positions wu, wu + nwaves, ...: beacon tiles first, then raw tiles;
-  // jr is this wave's first raw tile
-  const int nbt = bv.ntiles;
-  const int jr = ((wu - nbt) % nwaves + nwaves) % nwaves;
-  const int raw_t0 = jr < rw.ntiles ? jr * SegView<kFullNch, BF16>::kRows : -1;
+  // tile positions: beacon tiles 0 .. nbt-1, then raw tiles; this wave's
+  // first is wu, later ones come from the unit's counter
+  const int nbt = bv.ntiles, total = nbt + rw.ntiles;
+  TileFeed feed;
+  feed.grab = a.counters + (size_t)unit * kCounterStride + 1;
+  feed.base = nwaves;
+  feed.fixed = a.deterministic != 0;
+  feed.pending = 0;
+  feed.request(lane);
 
   // the prologue's inputs, then the wave's first tile: the prologue's
   // arithmetic runs while the tile is in flight
-  QueryPrologue<G, BF16, BLAT> pro;
+  QueryPrologue<G, BF16, NCH> pro;
   pro.issue(a, b, h, wave);
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
-  if (wu < nbt) {
-    bv.load_keys(wu * SegView<BN, BF16>::kRows, kbuf, n, kg);
-    bv.load_values(wu * SegView<BN, BF16>::kRows, vbuf);
-  } else if (raw_t0 >= 0) {
-    rw.load_keys(raw_t0, kbuf, n, kg);
-    rw.load_values(raw_t0, vbuf);
+  int j = wu;
+  {
+    const int tb = j * SegView<BN, BF16>::kRows, tr = (j - nbt) * SegView<kFullNch, BF16>::kRows;
+    load_tile_keys(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, a.q, kbuf, n, kg);
+    load_tile_values(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, a.q, vbuf);
   }
   pro.finish(a, sh, wave);
 
   float* pw = sh.u.s.t.p[wave];
   WaveState<G, BF16> st;
   st.reset();
-  sweep<G, BN, BF16, kFullNch>(bv, rw, wu, nwaves, raw_t0, BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0],
-                               bv.rk, kbuf, vbuf, pw, st);
+  sweep<G, BN, BF16, kFullNch>(bv, 0, rw, nbt, total, j, feed,
+                               BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf, pw, st);
   wave_reduce<G, BF16>(st, bv.lpr);
   wave_park<G, BN, BF16>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
   st.reset();
-  sweep<G, kFullNch, BF16, kFullNch>(rw, rw, jr, nwaves, -1, &sh.qrot[0][0], kHeadDim, kbuf, vbuf,
-                                     pw, st);
+  sweep<G, kFullNch, BF16, kFullNch>(rw, nbt, rw, total, total, j, feed, &sh.qrot[0][0], kHeadDim,
+                                     kbuf, vbuf, pw, st);
   wave_reduce<G, BF16>(st, rw.lpr);
   __syncthreads();  // every wave is done with its exp-weights, which alias the raw sums
   wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
@@ -886,15 +997,18 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t done =
-        __hip_atomic_fetch_add(&a.counters[unit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t done = __hip_atomic_fetch_add(&a.counters[(size_t)unit * kCounterStride], 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.is_last = done == (uint32_t)(k - 1);
   }
   __syncthreads();
   if (!sh.is_last) return;
   merge_unit<G, BF16, BLAT>(a, unit, b, h, sh, uw);
-  if (tid == 0)  // ready for the next call
-    __hip_atomic_store(&a.counters[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // ready for the next call: every workgroup of the unit has counted itself
+  // done, after its last request to the tile counter had completed
+  if (tid < 2)
+    __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroups of `kfn` resident per CU and the CU count of the current

@@ -10,8 +10,8 @@ from .binding import make_problem, slimkv_problem, slimkv_workspace_bytes
 
 
 def problem_from_tensors(q, U_K, C_K, K_raw, *, rope_theta: float, num_kv_heads: int,
-                         scale: float | None = None, U_V=None, num_splits: int = 0
-                         ) -> slimkv_problem:
+                         scale: float | None = None, U_V=None, num_splits: int = 0,
+                         flags: int = 0) -> slimkv_problem:
     """Problem struct read off the tensor shapes (C_K/U_K or K_raw may be None)."""
     B, Hq, d = q.shape
     nb = 0 if C_K is None else int(C_K.shape[2])
@@ -21,7 +21,8 @@ def problem_from_tensors(q, U_K, C_K, K_raw, *, rope_theta: float, num_kv_heads:
     return make_problem(batch=B, num_q_heads=Hq, num_kv_heads=num_kv_heads, num_beacons=nb,
                         rank_k=rk, rank_v=rv, raw_window=w,
                         scale=(1.0 / math.sqrt(d)) if scale is None else scale,
-                        rope_theta=rope_theta, dtype=q.dtype, head_dim=d, num_splits=num_splits)
+                        rope_theta=rope_theta, dtype=q.dtype, head_dim=d, num_splits=num_splits,
+                        flags=flags)
 
 
 def alloc_workspace(problem: slimkv_problem, op: int, device) -> torch.Tensor:

@@ -37,7 +37,7 @@ def note(msg: str) -> None:
 
 
 def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_splits: int = 0,
-            device="cuda", with_lse: bool = True, full_k=None, full_v=None):
+            device="cuda", with_lse: bool = True, full_k=None, full_v=None, flags: int = 0):
     """Run one entry point on ``inp`` (moved to the GPU if needed)."""
     wl = inp.workload
     g = inp.to(device)
@@ -46,11 +46,12 @@ def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_split
         prob = lda.make_problem(batch=wl.batch, num_q_heads=wl.num_q_heads,
                                 num_kv_heads=wl.num_kv_heads, num_beacons=0, rank_k=0, rank_v=0,
                                 raw_window=int(K.shape[2]), scale=wl.scale,
-                                rope_theta=wl.rope_theta, dtype=wl.dtype, num_splits=num_splits)
+                                rope_theta=wl.rope_theta, dtype=wl.dtype, num_splits=num_splits,
+                                flags=flags)
     else:
         prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
                                         rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
-                                        scale=wl.scale, num_splits=num_splits)
+                                        scale=wl.scale, num_splits=num_splits, flags=flags)
     out, lse = lda.alloc_outputs(prob, device)
     ws = lda.alloc_workspace(prob, op, device)
     if not with_lse:

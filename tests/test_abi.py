@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 1
+    assert lda.slimkv_abi_version() == 2
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -96,10 +96,14 @@ def test_shape_errors(lib, over, status):
     assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) == 0
 
 
-def test_reserved_must_be_zero(lib):
+def test_unknown_flag_bits_rejected(lib):
     prob = _problem()
-    prob.reserved = 1
+    prob.flags = 2
     assert _call(lib, prob) == SHAPE
+    assert "flag" in lda.slimkv_last_error()
+    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) == 0
+    prob.flags = lda.SLIMKV_FLAG_DETERMINISTIC
+    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) > 0
 
 
 def test_null_problem(lib):
