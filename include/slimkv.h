@@ -89,10 +89,11 @@ typedef struct slimkv_problem {
   int32_t num_q_heads;  /* H_q, a multiple of H_kv; G = H_q / H_kv <= 8      */
   int32_t num_kv_heads; /* H_kv >= 1                                         */
   int32_t head_dim;     /* d; must be 128                                    */
-  int32_t num_beacons;  /* N_b >= 0 beacon rows per (b, kv head)             */
+  int32_t num_beacons;  /* N_b >= 0 beacon rows per (b, kv head), <= 2^22    */
   int32_t rank_k;       /* r_K: multiple of 16 in [16, 128] when N_b > 0     */
   int32_t rank_v;       /* r_V: multiple of 16 in [16, 128] when N_b > 0     */
-  int32_t raw_window;   /* W >= 0 raw rows per (b, kv head); N_b + W >= 1    */
+  int32_t raw_window;   /* W >= 0 raw rows per (b, kv head), <= 2^22;
+                           N_b + W >= 1                                      */
   float scale;          /* softmax scale, finite and > 0 (e.g. 1/sqrt(d))   */
   int32_t dtype;        /* slimkv_dtype of q, U_K, U_V, C_K, C_V, K, V       */
   double rope_theta;    /* rotary base, finite and > 1                       */

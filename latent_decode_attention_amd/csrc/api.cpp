@@ -31,7 +31,9 @@ slimkv_status fail(slimkv_status st, const char* fmt, ...) {
   return st;
 }
 
-constexpr int64_t kMaxRows = int64_t(1) << 24;    // rows per unit and segment
+// rows per unit and segment: a unit's rows are addressed with 32-bit byte
+// offsets (at most 2^22 rows x 512 bytes)
+constexpr int64_t kMaxRows = int64_t(1) << 22;
 constexpr int64_t kMaxUnits = int64_t(1) << 20;   // batch * kv heads
 constexpr size_t kAlign = 256;                    // workspace sub-buffer alignment
 
@@ -130,9 +132,9 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
   a.rank_k = sb.kind == kSegLatent ? p->rank_k : 0;
 
-  // workspace layout: per-unit counters (must start zeroed), then two
-  // partial slots per chunk for up to kMaxChunks chunks
-  const int64_t G = a.group, slots = 2 * kMaxChunks;
+  // workspace layout: per-unit counters (must start zeroed), then one
+  // partial slot per workgroup for up to kMaxChunks workgroups per unit
+  const int64_t G = a.group, slots = kMaxChunks;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
   pl.off_ml = off;

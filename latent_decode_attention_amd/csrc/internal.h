@@ -12,7 +12,7 @@ constexpr int kHeadDim = 128;
 constexpr int kWaves = 4;              // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
-constexpr int kMaxChunks = 64;         // workgroups per unit (each writes 2 partial slots)
+constexpr int kMaxChunks = 64;         // workgroups per unit (each writes one partial slot)
 constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
 
 enum SegKind : int32_t {
@@ -33,10 +33,9 @@ struct Segment {
 };
 
 // Everything the attention kernel reads.  seg[0] holds each unit's beacon
-// rows, seg[1] its full-width raw rows; a unit's byte stream (beacons, then
-// raw rows) is cut into `chunks` equal pieces, one workgroup each.  A chunk
-// writes two partial slots, 2c (its beacon rows) and 2c+1 (its raw rows),
-// empty ones included; the last workgroup of a unit merges all slots.
+// rows, seg[1] its full-width raw rows.  `chunks` workgroups share a unit's
+// rows tile by tile; each writes one partial slot (empty ones included) and
+// the last workgroup of a unit merges all of them.
 struct AttnArgs {
   Segment seg[2];
   int32_t batch, num_q_heads, num_kv_heads, group;
@@ -53,8 +52,8 @@ struct AttnArgs {
   int32_t rank_k;         // r_K of a latent beacon segment (0 if none)
   uint32_t* counters;     // [units][kCounterStride]: workgroups done, tiles handed out
                           // (zero between calls)
-  float* part_ml;         // [units, 2 * chunks, G, 2]  (max, sum of exp)
-  float* part_acc;        // [units, 2 * chunks, G, d]  exp-weighted value sums
+  float* part_ml;         // [units, chunks, G, 2]  (max, sum of exp), log2 units
+  float* part_acc;        // [units, chunks, G, d]  exp-weighted value sums
   float* out;             // [B, H_q, d]
   float* lse;             // [B, H_q] or null
 };

@@ -68,25 +68,16 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// Eight fp32 values as two bf16 vectors, hi + lo ~= x to ~2^-17 relative.
+// Eight fp32 values as two bf16 vectors, hi + lo ~= x to ~2^-17 relative:
+// hi = x rounded to bf16 by the hardware conversion (nearest even), lo = the
+// exact fp32 remainder x - hi, rounded the same way.
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8_t& hi, bf16x8_t& lo) {
-  u32x4_t hw, lw;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t h0 = f32_to_bf16_rne(x[2 * e]), h1 = f32_to_bf16_rne(x[2 * e + 1]);
-    const uint32_t l0 = f32_to_bf16_rne(x[2 * e] - __uint_as_float(h0 << 16));
-    const uint32_t l1 = f32_to_bf16_rne(x[2 * e + 1] - __uint_as_float(h1 << 16));
-    hw[e] = h0 | (h1 << 16);
-    lw[e] = l0 | (l1 << 16);
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - (float)h);
   }
-  hi = __builtin_bit_cast(bf16x8_t, hw);
-  lo = __builtin_bit_cast(bf16x8_t, lw);
 }
 
 __device__ __forceinline__ u32x4_t load16(const void* p) {
@@ -149,10 +140,12 @@ struct TileShape {
 };
 
 // LDS of one attention workgroup.  The prologue's staged U_K is dead once
-// the latent query is formed, the sweep arrays once the workgroup's partials
-// are written; the sweep and the unit merge reuse that space.
+// the latent query is formed; the sweep reuses its space.
 struct alignas(16) AttnShared {
   union {
+    struct {
+      uint16_t uk[kHeadDim * (kHeadDim + 2)];  // bf16 U_K, rows padded by 2 elements
+    } pro;
     struct {
       union {
         float p[kWaves][64 * 8];                 // exp-weights of the current tile, per wave
@@ -160,20 +153,13 @@ struct alignas(16) AttnShared {
       } t;
       float beacon[kWaves][kMaxGroup][kHeadDim];  // each wave's beacon-row sums
     } s;
-    struct {
-      uint16_t uk[kHeadDim * (kHeadDim + 2)];  // bf16 U_K, rows padded by 2 elements
-    } pro;
-    struct {
-      float ml[2 * kMaxChunks * kMaxGroup][2];  // every slot's (max, sum); then its weight
-      f32x4_t part[kThreads][2];                // per-thread sums over one group of slots
-      float olat[kMaxGroup][kHeadDim];
-      float ofull[kMaxGroup][kHeadDim];
-    } m;
   } u;
-  float qrot[kMaxGroup][kHeadDim];     // rotated query, pre-scaled (prologue)
-  float qlat[kMaxGroup][kHeadDim];     // latent query, pre-scaled (prologue)
+  // rotated and latent query, pre-scaled (prologue); after the sweeps the
+  // workgroup's merged raw and beacon sums
+  float qrot[kMaxGroup][kHeadDim];
+  float qlat[kMaxGroup][kHeadDim];
   float wml[2][kWaves][kMaxGroup][2];  // each wave's (max, sum) per head, per segment
-  float M[kMaxGroup], L[kMaxGroup];
+  float sml[2][kMaxGroup][2];          // the workgroup's (max, sum) per head, per segment
   int is_last;
 };
 
@@ -340,19 +326,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* bas
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// Cache-policy bits of the cache-row loads: non-temporal.  Every row is read
+// once per call, so the rows should not push the small, reused data (the
+// bases, the query, partials, counters) out of the caches.
+constexpr int kStream = 2;
+
+// Buffer descriptor over `bytes` bytes at `base` (raw, no swizzle): loads at
+// offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
 // One segment of one unit (a run of rows: its beacons, or its raw window) as
-// this lane sees it: where its tile loads go and which value columns it sums.
-// Tiles are kRows rows; a value row spans rv / EPL lanes, padded to a power
-// of two (lpr) so that row groups can be summed by a butterfly.
+// this lane sees it.  Keys and values are read through buffer descriptors
+// bounded by the unit's rows, so loads past its last row return zeros: rows
+// past `rows` get score -inf and weight 0 anyway, and features past r_K (a
+// chunk wider than the keys) meet zero query entries.  A value row spans
+// rv / EPL lanes, padded to a power of two (lpr) so that row groups can be
+// summed by a butterfly.  Tiles are kRows rows.
 template <int NCH, bool BF16>
 struct SegView {
   using Tr = Traits<BF16>;
   static constexpr int kSub = TileShape<BF16, NCH>::kSub;
   static constexpr int kRows = TileShape<BF16, NCH>::kRows;
-  const char* K;
-  const char* V;
+  static constexpr int kKeySlots = kSub * NCH;
+  __amdgpu_buffer_rsrc_t kr, vr;  // this unit's key and value rows
   int rows, rk, rv, ntiles;
-  int lpr, rpi, vrow, vcc, vcol, lanes_row;
+  int kstride, vstride;  // bytes per key / value row
+  int klane, vlane;      // this lane's byte offset within a tile (row 0 of the tile)
+  int lpr, rpi, vrow, vcc, lanes_row;
   bool vact;
 
   __device__ __forceinline__ void init(const void* Kp, const void* Vp, int rows_, int rk_, int rv_,
@@ -360,9 +362,11 @@ struct SegView {
     rows = rows_;
     rk = rk_;
     rv = rv_;
+    kstride = rk * Tr::kElemBytes;
+    vstride = rv * Tr::kElemBytes;
     const size_t urow = (size_t)unit * (size_t)rows;
-    K = static_cast<const char*>(Kp) + urow * rk * Tr::kElemBytes;
-    V = static_cast<const char*>(Vp) + urow * rv * Tr::kElemBytes;
+    kr = make_rsrc(static_cast<const char*>(Kp) + urow * kstride, (uint32_t)rows * kstride);
+    vr = make_rsrc(static_cast<const char*>(Vp) + urow * vstride, (uint32_t)rows * vstride);
     ntiles = (rows + kRows - 1) / kRows;
     lanes_row = rv / Tr::kEpl;
     lpr = 1 << (32 - __builtin_clz(lanes_row - 1));
@@ -370,57 +374,69 @@ struct SegView {
     vrow = lane / lpr;
     vcc = lane & (lpr - 1);
     vact = vcc < lanes_row;
-    vcol = min(vcc, lanes_row - 1) * Tr::kEpl;  // clamped for idle lanes
+    const int n = lane & 15, kg = lane >> 4;
+    // key slot s * NCH + c as an MFMA B operand: lane (n, kg) holds features
+    // c*KCH + kg*EPL ... of row 16 s + n
+    klane = n * kstride + kg * Tr::kEpl * Tr::kElemBytes;
+    // value slot i: row i * rpi + vrow, this lane's 16 bytes (idle lanes clamped)
+    vlane = vrow * vstride + min(vcc, lanes_row - 1) * 16;
   }
+  // uniform byte offsets of key / value slot i within a tile
+  __device__ __forceinline__ int key_off(int i) const {
+    return (i / NCH) * 16 * kstride + (i % NCH) * Tr::kChunkK * Tr::kElemBytes;
+  }
+  __device__ __forceinline__ int val_off(int i) const { return i * rpi * vstride; }
+};
 
-  // Addresses are clamped into the segment and the row's width: rows past
-  // `rows` get score -inf, features past r_K meet zero query entries, and
-  // value rows past `rows` get weight 0, so the clamped data never
-  // contributes.  Only called for segments with rows >= 1 when the address
-  // is used.
-  // Key slot i = s * NCH + c as an MFMA B operand: lane (n, kg) holds
-  // features c*KCH + kg*EPL ... of row t0 + 16 s + n.
-  __device__ __forceinline__ const char* key_ptr(int t0, int i, int n, int kg) const {
-    const int sb = i / NCH, c = i - (i / NCH) * NCH;
-    const int row = min(t0 + 16 * sb + n, rows - 1);
-    const int k0 = min(c * Tr::kChunkK + kg * Tr::kEpl, rk - Tr::kEpl);
-    return K + ((size_t)row * rk + k0) * Tr::kElemBytes;
-  }
-  // Value slot i: row t0 + i * rpi + vrow, this lane's 16 bytes.
-  __device__ __forceinline__ const char* val_ptr(int t0, int i) const {
-    const int row = min(t0 + i * rpi + vrow, rows - 1);
-    return V + ((size_t)row * rv + vcol) * Tr::kElemBytes;
-  }
+// Where a wave's tile slots read when it has no further tile.
+// DummyTail: q again (any valid bytes; the values go unused).  LiftTail
+// (bf16, latent beacons): this wave's U_V rows for the lift -- key slot c
+// holds row 16 wave + n, value slot c row 16 wave + 64 + n, features
+// 32c + 8kg .. +7 (past r_V they read on into the next row, or zeros past
+// the end, and meet zero latent entries) -- so the lift's inputs arrive
+// while the wave's last tile is processed.
+struct TailRows {
+  __amdgpu_buffer_rsrc_t r;
+  int klane, vlane;
+  __device__ __forceinline__ int key_off(int c) const { return c * 64; }
+  __device__ __forceinline__ int val_off(int c) const { return c * 64; }
 };
 
 // Request one tile's keys (or values) into the wave's tile registers: tile
-// ta of `a` if use_a, else tile tb of `b` if use_b, else nothing useful (a
-// re-read of `dummy`, any valid 16-byte-aligned address).  Every slot is one
-// unconditional load whose address is selected, so the registers need no
-// copies afterwards (separate loads per source under a branch would be
-// merged by copies that wait for the loads).
-template <int NA, int NB, bool BF16>
+// starting at row ta of `a` if use_a, else row tb of `b` if use_b (only with
+// CROSS), else the tail's rows.  The choice is wave-uniform, so it selects a
+// descriptor and a base offset; every slot is one unconditional load, and the
+// registers need no copies afterwards (separate loads per source under a
+// branch would be merged by copies that wait for the loads).
+template <bool CROSS, int NA, int NB, bool BF16>
 __device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16>& a, int ta, bool use_a,
                                                const SegView<NB, BF16>& b, int tb, bool use_b,
-                                               const void* dummy, u32x4_t* kbuf, int n, int kg) {
-  constexpr int KA = SegView<NA, BF16>::kSub * NA, KB = SegView<NB, BF16>::kSub * NB;
-  constexpr int K = KA > KB ? KA : KB;
-  const char* d = static_cast<const char*>(dummy);
+                                               const TailRows& tail, u32x4_t* kbuf) {
+  constexpr int KA = SegView<NA, BF16>::kKeySlots, KB = SegView<NB, BF16>::kKeySlots;
+  constexpr int K = Traits<BF16>::kMaxLoads;
+  static_assert(KA <= K && KB <= K, "tile too large");
+  const bool ub = CROSS && use_b;
+  const __amdgpu_buffer_rsrc_t r = use_a ? a.kr : (ub ? b.kr : tail.r);
+  const int base = use_a ? a.klane + ta * a.kstride : (ub ? b.klane + tb * b.kstride : tail.klane);
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    const char* pa = i < KA ? a.key_ptr(ta, i, n, kg) : d;
-    const char* pb = i < KB ? b.key_ptr(tb, i, n, kg) : d;
-    kbuf[i] = load16(use_a ? pa : (use_b ? pb : d));
+    const int off = use_a ? (i < KA ? a.key_off(i) : 0)
+                          : (ub ? (i < KB ? b.key_off(i) : 0) : tail.key_off(i));
+    kbuf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + off, 0, kStream);
   }
 }
-template <int NA, int NB, bool BF16>
+template <bool CROSS, int NA, int NB, bool BF16>
 __device__ __forceinline__ void load_tile_values(const SegView<NA, BF16>& a, int ta, bool use_a,
                                                  const SegView<NB, BF16>& b, int tb, bool use_b,
-                                                 const void* dummy, u32x4_t* vbuf) {
-  const char* d = static_cast<const char*>(dummy);
+                                                 const TailRows& tail, u32x4_t* vbuf) {
+  const bool ub = CROSS && use_b;
+  const __amdgpu_buffer_rsrc_t r = use_a ? a.vr : (ub ? b.vr : tail.r);
+  const int base = use_a ? a.vlane + ta * a.vstride : (ub ? b.vlane + tb * b.vstride : tail.vlane);
 #pragma unroll
-  for (int i = 0; i < Traits<BF16>::kMaxLoads; ++i)
-    vbuf[i] = load16(use_a ? a.val_ptr(ta, i) : (use_b ? b.val_ptr(tb, i) : d));
+  for (int i = 0; i < Traits<BF16>::kMaxLoads; ++i) {
+    const int off = use_a ? a.val_off(i) : (ub ? b.val_off(i) : tail.val_off(i));
+    vbuf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + off, 0, kStream);
+  }
 }
 
 // One wave's running softmax state over the rows it has swept: max and sum
@@ -480,14 +496,15 @@ struct TileFeed {
 // values as soon as the value sums have consumed this tile's values.  When
 // the next position lies past this segment but before pend, it is a tile of
 // the next segment (`nx`, tile 0 at position nxbase) and is requested the
-// same way, so the stream of loads does not stop between segments (past
-// pend the slots re-read this segment's first row instead).  On exit j is
-// the first position past this segment the wave drew.
-template <int G, int NCH, bool BF16, int NCH2>
+// same way, so the stream of loads does not stop between segments (CROSS;
+// past pend the slots take the tail's addresses instead).  On exit j is the
+// first position past this segment the wave drew.
+template <int G, int NCH, bool BF16, bool CROSS, int NCH2>
 __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
                                       const SegView<NCH2, BF16>& nx, int nxbase, int pend, int& j,
-                                      TileFeed& feed, const float* qsrc, int rq, u32x4_t* kbuf,
-                                      u32x4_t* vbuf, float* pw, WaveState<G, BF16>& st) {
+                                      TileFeed& feed, const TailRows& tail, const float* qsrc, int rq,
+                                      u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
+                                      WaveState<G, BF16>& st) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
@@ -554,8 +571,8 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
     }
     const int jn = feed.take(j);  // wave-uniform
     const bool more = jn < pstop;
-    const bool cross = !more && jn < pend;
-    load_tile_keys(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, sv.K, kbuf, n, kg);
+    const bool cross = CROSS && !more && jn < pend;
+    load_tile_keys<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, kbuf);
     feed.request(lane);
 
     // -- online softmax: tile max per head, rescale only when it grows
@@ -632,7 +649,7 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
           for (int e = 0; e < EPL; ++e) st.acc[g][e] = fmaf(pv[g], v[e], st.acc[g][e]);
       }
     }
-    load_tile_values(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, sv.K, vbuf);
+    load_tile_values<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, vbuf);
     // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -686,203 +703,189 @@ __device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const Se
   }
 }
 
-// The workgroup's partial of one segment: the four waves' sums rescaled to
-// their common max, written with device-coherent stores.
-template <int G>
-__device__ __forceinline__ void combine_store(const float (*wacc)[kMaxGroup][kHeadDim],
-                                              const float (*wml)[kMaxGroup][2], int rv,
-                                              float* ml_out, float* acc_out) {
-  const int tid = threadIdx.x;
-  const int c4n = rv / 4;  // 16-byte words per head (G * c4n <= kThreads)
-  if (tid < G * c4n) {
-    const int g = tid / c4n, col = 4 * (tid - g * c4n);
-    float M = wml[0][g][0];
+// ---------------------------------------------------------------------------
+// The workgroup's partial.  The four waves' parked states are merged per
+// segment in LDS (beacon sums into qlat, raw sums into qrot, each scaled to
+// its segment's max); the latent beacon sum is lifted once with U_V on the
+// matrix cores (bf16: the latent sum as hi + lo bf16 terms; fp32: exact
+// products); beacon and raw are combined by their maxima; the result --
+// (max, sum) and G x d sums per head -- is written with device-coherent
+// stores.
+template <int G, bool BF16, bool BLAT>
+__device__ __forceinline__ void wg_partial(const AttnArgs& a, AttnShared& sh, int h, int wave, int rvb,
+                                           const u32x4_t (&uw)[2][4], float* ml_out, float* acc_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  // (1) each segment's sums over the waves, rescaled to the segment's max
+  // (columns past `width` are written as zeros, so the lift can read whole
+  // 32-column chunks)
+  auto merge_waves = [&](const float (*wacc)[kMaxGroup][kHeadDim], const float (*wml)[kMaxGroup][2],
+                         int width, float (*dst)[kHeadDim]) {
+    if (tid < G * kHeadDim / 4) {  // one 16-byte word of one head each
+      const int g = tid / (kHeadDim / 4), col = 4 * (tid % (kHeadDim / 4));
+      float M = wml[0][g][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wml[w][g][0]);
-    f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (M != -INFINITY) {
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wml[w][g][0]);
+      f32x4_t sum = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (M != -INFINITY && col < width) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float sw = __builtin_amdgcn_exp2f(wml[w][g][0] - M);
-        sum += sw * *reinterpret_cast<const f32x4_t*>(&wacc[w][g][col]);
+        for (int w = 0; w < kWaves; ++w)
+          sum += __builtin_amdgcn_exp2f(wml[w][g][0] - M) * *reinterpret_cast<const f32x4_t*>(&wacc[w][g][col]);
       }
+      *reinterpret_cast<f32x4_t*>(&dst[g][col]) = sum;
     }
-    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(acc_out, G * kHeadDim * 4);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, sum), rs,
-                                           (g * kHeadDim + col) * 4, 0, kCoherent);
-  }
-  if (tid < G) {
-    float M = wml[0][tid][0];
+  };
+  merge_waves(sh.u.s.beacon, sh.wml[0], rvb, sh.qlat);
+  merge_waves(sh.u.s.t.raw, sh.wml[1], kHeadDim, sh.qrot);
+  if (tid < 2 * G) {
+    const int sg = tid / G, g = tid - sg * G;
+    float M = sh.wml[sg][0][g][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wml[w][tid][0]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.wml[sg][w][g][0]);
     float L = 0.0f;
     if (M != -INFINITY)
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(wml[w][tid][0] - M) * wml[w][tid][1];
+      for (int w = 0; w < kWaves; ++w) L += __builtin_amdgcn_exp2f(sh.wml[sg][w][g][0] - M) * sh.wml[sg][w][g][1];
+    sh.sml[sg][g][0] = M;
+    sh.sml[sg][g][1] = L;
+  }
+  __syncthreads();
+
+  // weights of the two segments for head g within the combined partial
+  auto weights = [&](int g, float& wb, float& wr) {
+    const float mb = sh.sml[0][g][0], mr = sh.sml[1][g][0];
+    const float M = fmaxf(mb, mr);
+    wb = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mb - M);
+    wr = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mr - M);
+  };
+  if constexpr (BLAT) {
+    // out^T[i][g] = sum_k U_V[i][k] olat[g][k]: D[m=i][n=g] over this wave's
+    // two 16-row tiles of i.  B operand: latent sums of head n, features
+    // 32c + 8kg .. +7 (columns n >= G compute heads that are never stored;
+    // latent columns past r_V hold zeros).
+    const int rv = a.rank_v;
+    const int gl = n & (kMaxGroup - 1);
+    f32x4_t d[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    if constexpr (BF16) {
+      // the latent sums as hi + lo bf16 terms, read and split once for both tiles
+      bf16x8_t hi[4], lo[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sh.qlat[gl][32 * c + 8 * kg]);
+        const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(&sh.qlat[gl][32 * c + 8 * kg + 4]);
+        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        split_bf16x8(x, hi[c], lo[c]);
+      }
+      const int nc = (rv + 31) / 32;  // wave-uniform
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (c < nc) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16x8_t uv = __builtin_bit_cast(bf16x8_t, uw[t][c]);
+            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, hi[c], d[t], 0, 0, 0);
+            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, lo[c], d[t], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+      const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * 4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i0 = 16 * (wave + kWaves * t);
+        for (int s4 = 0; s4 < rv / 4; ++s4) {
+          const int kk = 4 * s4 + kg;
+          const float uvv = ld_elem<false>(U, (size_t)(i0 + n) * rv + kk);
+          d[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(uvv, sh.qlat[gl][kk], d[t], 0, 0, 0);
+        }
+      }
+    }
+    // lane (n = g, kg) holds rows 16 (wave + 4t) + 4kg + e
+    float wb, wr;
+    weights(gl, wb, wr);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 16 * (wave + kWaves * t) + 4 * kg;
+      const f32x4_t raw = *reinterpret_cast<const f32x4_t*>(&sh.qrot[gl][r0]);
+      if (n < G) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_coherent(&acc_out[n * kHeadDim + r0 + e], wb * d[t][e] + wr * raw[e]);
+      }
+    }
+  } else {
+    // full-width (or absent) beacon rows: no lift
+    if (tid < G * kHeadDim / 4) {
+      const int g = tid / (kHeadDim / 4), col = 4 * (tid % (kHeadDim / 4));
+      float wb, wr;
+      weights(g, wb, wr);
+      const f32x4_t v = wb * *reinterpret_cast<const f32x4_t*>(&sh.qlat[g][col]) +
+                        wr * *reinterpret_cast<const f32x4_t*>(&sh.qrot[g][col]);
+      const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(acc_out, G * kHeadDim * 4);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (g * kHeadDim + col) * 4, 0,
+                                             kCoherent);
+    }
+  }
+  if (tid < G) {
+    float wb, wr;
+    weights(tid, wb, wr);
+    const float M = fmaxf(sh.sml[0][tid][0], sh.sml[1][tid][0]);
     store_coherent(&ml_out[2 * tid], M);
-    store_coherent(&ml_out[2 * tid + 1], L);
+    store_coherent(&ml_out[2 * tid + 1], wb * sh.sml[0][tid][1] + wr * sh.sml[1][tid][1]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Merge of all slots of one unit (run by the unit's last workgroup).
-//   M = max_s m_s, L = sum_s 2^(m_s - M) l_s,
-//   o_lat = sum_{beacon s} 2^(m_s - M) acc_s / L, o_full likewise over raw s,
-//   out = U_V o_lat + o_full, lse = ln 2 * (M + log2 L).
-// Thread t owns 16-byte column t % C4 of every slot in its group t / C4; the
-// (max, sum) pairs and a first batch of slot sums are loaded in one round
-// trip.  `uw` holds this wave's U_V rows for the lift (bf16, latent beacons).
-template <int G, bool BF16, bool BLAT>
-__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h,
-                                           AttnShared& sh, const u32x4_t (&uw)[2][4]) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
-  const int S = 2 * a.chunks, rv = a.rank_v;
-  constexpr int C4 = G * kHeadDim / 4;                    // 16-byte columns of a slot
-  constexpr int NG = C4 >= kThreads ? 1 : kThreads / C4;  // slot groups
-  constexpr int kB = 8;                                   // slots per load batch
-  float (*sml)[2] = sh.u.m.ml;
+// Merge of the unit's k partials (run by the unit's last workgroup):
+//   M = max_s m_s, L = sum_s 2^(m_s - M) l_s, out = sum_s 2^(m_s - M) acc_s / L,
+//   lse = ln 2 * (M + log2 L).
+// Thread (g, c4) owns 16-byte column c4 of head g and folds the partials in
+// one at a time; a batch of 8 partials' loads is in flight at once.  No LDS,
+// no barriers.
+template <int G>
+__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h) {
+  const int tid = threadIdx.x;
+  if (tid >= G * kHeadDim / 4) return;
+  const int k = a.chunks;
+  const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+  constexpr int kB = 8;
   const __amdgpu_buffer_rsrc_t rml =
-      coherent_rsrc(a.part_ml + (size_t)unit * S * G * 2, (uint32_t)(S * G * 2 * 4));
+      coherent_rsrc(a.part_ml + (size_t)unit * k * G * 2, (uint32_t)(k * G * 2 * 4));
   const __amdgpu_buffer_rsrc_t racc =
-      coherent_rsrc(a.part_acc + (size_t)unit * S * G * kHeadDim, (uint32_t)(S * G * kHeadDim * 4));
-  const int c4 = tid % C4, grp = tid / C4;
-  const bool active = grp < NG;
-
-  // -- one round trip: every (max, sum) and the first batch of slot sums
-  // (unconditional loads from clamped offsets; surplus values are unused)
-  const int n4 = S * G / 2;  // (max, sum) pairs as 16-byte words; S is even
-  u32x4_t mlv[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    mlv[j] = __builtin_amdgcn_raw_buffer_load_b128(rml, min(tid + kThreads * j, n4 - 1) * 16, 0,
-                                                   kCoherent);
-  u32x4_t v[kB];
-  auto load_batch = [&](int i0) {
+      coherent_rsrc(a.part_acc + (size_t)unit * k * G * kHeadDim, (uint32_t)(k * G * kHeadDim * 4));
+  float M = -INFINITY, L = 0.0f;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < k; s0 += kB) {
+    // unconditional loads from clamped slots; surplus ones are not folded in
+    uint32_t mlw[kB][2];
+    u32x4_t v[kB];
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int s = min(grp + NG * (i0 + u), S - 1);
-      v[u] = __builtin_amdgcn_raw_buffer_load_b128(racc, (s * C4 + c4) * 16, 0, kCoherent);
+      const int s = min(s0 + u, k - 1);
+      const int base = (s * G + g) * 8;
+      mlw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rml, base, 0, kCoherent);
+      mlw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rml, base + 4, 0, kCoherent);
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(racc, ((s * G + g) * kHeadDim + 4 * c4) * 4, 0, kCoherent);
     }
-  };
-  load_batch(0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int q = tid + kThreads * j;
-    if (q < n4) *reinterpret_cast<u32x4_t*>(&sml[2 * q][0]) = mlv[j];
-  }
-  __syncthreads();
-
-  // -- M and L per head: 32 lanes per head; then weights w_s = 2^(m_s - M) / L
-  {
-    const int g = tid >> 5, l32 = tid & 31;
-    float M = -INFINITY;
-    if (g < G)
-      for (int s = l32; s < S; s += 32) M = fmaxf(M, sml[s * G + g][0]);
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
-    float L = 0.0f;
-    if (g < G)
-      for (int s = l32; s < S; s += 32) L += __builtin_amdgcn_exp2f(sml[s * G + g][0] - M) * sml[s * G + g][1];
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) L += __shfl_xor(L, off, 32);
-    if (g < G && l32 == 0) {
-      sh.M[g] = M;
-      sh.L[g] = L;
-    }
-  }
-  __syncthreads();
-  for (int q = tid; q < S * G; q += kThreads)
-    sml[q][0] = __builtin_amdgcn_exp2f(sml[q][0] - sh.M[q % G]) / sh.L[q % G];
-  __syncthreads();
-
-  // -- weighted sums of this thread's column over its slots
-  const int g = c4 / (kHeadDim / 4), col = 4 * (c4 % (kHeadDim / 4));
-  f32x4_t lat = {0.0f, 0.0f, 0.0f, 0.0f}, full = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int per = (S + NG - 1) / NG;  // batches cover the largest group (uniform)
-  for (int i0 = 0; i0 < per; i0 += kB) {
-    if (i0 > 0) load_batch(i0);
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
-      const int s = grp + NG * (i0 + u);
-      if (active && s < S) {
-        const float w = sml[s * G + g][0];
-        // empty slots carry weight 0 and stale sums: skip, don't multiply
-        if (w != 0.0f) {
-          const f32x4_t wv = w * __builtin_bit_cast(f32x4_t, v[u]);
-          if (BLAT && (s & 1) == 0) {
-            if (col < rv) lat += wv;
-          } else {
-            full += wv;
-          }
+      if (s0 + u < k) {
+        const float m = __uint_as_float(mlw[u][0]), l = __uint_as_float(mlw[u][1]);
+        const float mn = fmaxf(M, m);
+        if (mn != -INFINITY) {  // a partial with no rows (m = -inf, l = 0, sums 0) adds nothing
+          const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(m - mn);
+          L = L * a1 + l * a2;
+          acc = acc * a1 + __builtin_bit_cast(f32x4_t, v[u]) * a2;
+          M = mn;
         }
       }
     }
   }
-  sh.u.m.part[tid][0] = lat;
-  sh.u.m.part[tid][1] = full;
-  __syncthreads();
-  if (tid < C4) {
-    f32x4_t sl = sh.u.m.part[tid][0], sf = sh.u.m.part[tid][1];
-#pragma unroll
-    for (int gi = 1; gi < NG; ++gi) {
-      sl += sh.u.m.part[tid + C4 * gi][0];
-      sf += sh.u.m.part[tid + C4 * gi][1];
-    }
-    *reinterpret_cast<f32x4_t*>(&sh.u.m.olat[g][col]) = sl;
-    *reinterpret_cast<f32x4_t*>(&sh.u.m.ofull[g][col]) = sf;
-  }
-  __syncthreads();
-
-  // -- lift the latent sum once and add the full-width sum
-  float* out = a.out + ((size_t)b * a.num_q_heads + (size_t)h * G) * kHeadDim;
-  if constexpr (BLAT) {
-    // out^T[i][g] = sum_k U_V[i][k] olat[g][k]: D[m=i][n=g] over 16-row tiles of i
-    const int n = lane & 15, m16 = lane & 15, kg = lane >> 4;
-    const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * Traits<BF16>::kElemBytes;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int i0 = 16 * (wave + kWaves * t);
-      f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (32 * c < rv) {
-            const int k0 = 32 * c + 8 * kg;
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (k0 < rv && n < G) ? sh.u.m.olat[n][k0 + e] : 0.0f;
-            bf16x8_t hi, lo;
-            split_bf16x8(x, hi, lo);
-            const bf16x8_t uv = __builtin_bit_cast(bf16x8_t, uw[t][c]);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, hi, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(uv, lo, d, 0, 0, 0);
-          }
-        }
-      } else {
-        for (int s = 0; s < rv / 4; ++s) {
-          const int k = 4 * s + kg;
-          const float uvv = ld_elem<false>(U, (size_t)(i0 + m16) * rv + k);
-          const float ov = n < G ? sh.u.m.olat[n][k] : 0.0f;
-          d = __builtin_amdgcn_mfma_f32_16x16x4f32(uvv, ov, d, 0, 0, 0);
-        }
-      }
-      // lane (n = g, kg) holds rows i = i0 + 4kg + e
-      if (n < G) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = i0 + 4 * kg + e;
-          out[(size_t)n * kHeadDim + row] = d[e] + sh.u.m.ofull[n][row];
-        }
-      }
-    }
-  } else {
-    for (int p = tid; p < G * kHeadDim; p += kThreads)
-      out[(size_t)(p / kHeadDim) * kHeadDim + p % kHeadDim] = sh.u.m.ofull[p / kHeadDim][p % kHeadDim];
-  }
-  if (a.lse && tid < G)
-    a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + tid] =
-        (float)(0.69314718055994530942 * ((double)sh.M[tid] + log2((double)sh.L[tid])));
+  const float inv = 1.0f / L;
+  float* out = a.out + (((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim + 4 * c4);
+  *reinterpret_cast<f32x4_t*>(out) = acc * inv;
+  if (a.lse && c4 == 0)
+    a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + g] =
+        (float)(0.69314718055994530942 * ((double)M + log2((double)L)));
 }
 
 // ---------------------------------------------------------------------------
@@ -897,9 +900,8 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 // tiles -- beacon tiles, then raw tiles, all about the same size in bytes --
 // are handed out in order (see TileFeed), so the waves of a unit advance
 // through one sliding window of rows; each wave keeps one tile in flight,
-// across the segment boundary too.  The workgroup writes its beacon
-// partial to slot 2c and its raw partial to slot 2c+1; the workgroup that
-// finishes last merges the unit.
+// across the segment boundary too.  The workgroup writes one partial (slot
+// c of the unit); the workgroup that finishes last merges the unit.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
 template <int G, int NCH, bool BF16>
@@ -920,7 +922,6 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int h = unit - b * a.num_kv_heads;
   const int nwaves = kWaves * k;
   const int wu = kWaves * c + wave;  // this wave's number within the unit
-  const size_t slot0 = ((size_t)unit * k + c) * 2;
 
   SegView<BN, BF16> bv;  // beacon rows
   bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, BLAT ? a.seg[0].rk : kHeadDim,
@@ -936,6 +937,19 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   feed.fixed = a.deterministic != 0;
   feed.pending = 0;
   feed.request(lane);
+  // after its last tile a wave loads its U_V rows for the lift (bf16 latent
+  // beacons); otherwise the tail loads fall outside a 16-byte window on q
+  // and return zeros
+  TailRows tail;
+  if constexpr (BF16 && BLAT) {
+    tail.r = make_rsrc(static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * a.rank_v * 2,
+                       (uint32_t)(kHeadDim * a.rank_v * 2));
+    tail.klane = ((16 * wave + n) * a.rank_v + 8 * kg) * 2;
+    tail.vlane = tail.klane + 64 * a.rank_v * 2;
+  } else {
+    tail.r = make_rsrc(a.q, 16);
+    tail.klane = tail.vlane = 64;
+  }
 
   // the prologue's inputs, then the wave's first tile: the prologue's
   // arithmetic runs while the tile is in flight
@@ -945,50 +959,40 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   int j = wu;
   {
     const int tb = j * SegView<BN, BF16>::kRows, tr = (j - nbt) * SegView<kFullNch, BF16>::kRows;
-    load_tile_keys(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, a.q, kbuf, n, kg);
-    load_tile_values(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, a.q, vbuf);
+    load_tile_keys<true>(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, tail, kbuf);
+    load_tile_values<true>(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, tail, vbuf);
   }
   pro.finish(a, sh, wave);
 
   float* pw = sh.u.s.t.p[wave];
   WaveState<G, BF16> st;
   st.reset();
-  sweep<G, BN, BF16, kFullNch>(bv, 0, rw, nbt, total, j, feed,
-                               BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf, pw, st);
+  sweep<G, BN, BF16, true>(bv, 0, rw, nbt, total, j, feed, tail,
+                           BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf, pw, st);
   wave_reduce<G, BF16>(st, bv.lpr);
   wave_park<G, BN, BF16>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
   st.reset();
-  sweep<G, kFullNch, BF16, kFullNch>(rw, nbt, rw, total, total, j, feed, &sh.qrot[0][0], kHeadDim,
-                                     kbuf, vbuf, pw, st);
+  sweep<G, kFullNch, BF16, false>(rw, nbt, rw, total, total, j, feed, tail, &sh.qrot[0][0], kHeadDim,
+                                  kbuf, vbuf, pw, st);
+  // From here on the wave only finishes the unit: raise its issue priority
+  // over the waves on its SIMD that are still streaming tiles, so the tail
+  // (on the critical path of the whole call) is not starved by them.
+  __builtin_amdgcn_s_setprio(2);
+  // bf16 latent beacons: the tile registers now hold the lift's U_V rows
+  u32x4_t uw[2][4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    uw[0][cc] = kbuf[cc];
+    uw[1][cc] = vbuf[cc];
+  }
   wave_reduce<G, BF16>(st, rw.lpr);
-  __syncthreads();  // every wave is done with its exp-weights, which alias the raw sums
+  __syncthreads();  // every wave is done with its exp-weights (which alias the raw sums)
+                    // and with the query (whose space takes the merged sums)
   wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
   __syncthreads();
-
-  // U_V rows of this wave's lift tiles: in flight while the partials are
-  // written, in case this workgroup turns out to be the unit's last
-  u32x4_t uw[2][4];
-  if constexpr (BF16 && BLAT) {
-    const int rv = a.rank_v;
-    const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * 2;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int i = 16 * (wave + kWaves * t) + n, k0 = 32 * cc + 8 * kg;
-        // features past r_V meet zero latent entries in the lift
-        uw[t][cc] = load16(U + ((size_t)i * rv + min(k0, rv - 8)) * 2);
-      }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) uw[t][cc] = u32x4_t{0u, 0u, 0u, 0u};
-  }
-  combine_store<G>(sh.u.s.beacon, sh.wml[0], bv.rv, a.part_ml + slot0 * G * 2,
-                   a.part_acc + slot0 * G * kHeadDim);
-  combine_store<G>(sh.u.s.t.raw, sh.wml[1], kHeadDim, a.part_ml + (slot0 + 1) * G * 2,
-                   a.part_acc + (slot0 + 1) * G * kHeadDim);
+  const size_t slot = (size_t)unit * k + c;
+  wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw, a.part_ml + slot * G * 2,
+                            a.part_acc + slot * G * kHeadDim);
 
   // ---- the last workgroup of the unit merges everything.  Every thread
   // waits for its coherent partial stores to complete before the barrier;
@@ -1003,12 +1007,12 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   }
   __syncthreads();
   if (!sh.is_last) return;
-  merge_unit<G, BF16, BLAT>(a, unit, b, h, sh, uw);
   // ready for the next call: every workgroup of the unit has counted itself
   // done, after its last request to the tile counter had completed
   if (tid < 2)
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  merge_unit<G>(a, unit, b, h);
 }
 
 // Workgroups of `kfn` resident per CU and the CU count of the current
