@@ -99,19 +99,20 @@ typedef struct slimkv_problem {
   double rope_theta;    /* rotary base, finite and > 1                       */
   int32_t num_splits;   /* 0: library picks; > 0: workgroups that share each
                            (b, kv head)'s rows (at most 64)                 */
-  int32_t flags;        /* 0 or SLIMKV_FLAG_DETERMINISTIC; other bits 0      */
+  int32_t flags;        /* 0 or SLIMKV_FLAG_DYNAMIC_TILES; other bits 0      */
 } slimkv_problem;
 
 /*
- * Row scheduling.  By default the workgroups of a (b, kv head) take its
- * rows tile by tile from a shared counter, so faster ones take more; the
- * order in which rows are summed then depends on timing, and repeated calls
- * agree only to rounding (well inside the documented tolerances).  With
- * SLIMKV_FLAG_DETERMINISTIC the tiles are dealt round-robin in a fixed
- * order: repeated calls on the same device and problem give bitwise equal
- * out and lse, somewhat slower.
+ * Row scheduling.  By default the tiles of a (b, kv head)'s rows are dealt
+ * round-robin over its workgroups' waves in a fixed order: repeated calls
+ * on the same device and problem give bitwise equal out and lse.  With
+ * SLIMKV_FLAG_DYNAMIC_TILES the waves take tiles from a shared counter
+ * instead, so faster ones take more (useful when other work shares the
+ * GPU); the order in which rows are summed then depends on timing, and
+ * repeated calls agree only to rounding (well inside the documented
+ * tolerances).
  */
-#define SLIMKV_FLAG_DETERMINISTIC 1
+#define SLIMKV_FLAG_DYNAMIC_TILES 1
 
 /*
  * Workspace bytes the given op needs for this problem, or 0 if the problem

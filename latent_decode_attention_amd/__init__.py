@@ -6,7 +6,7 @@ script and a thin ctypes binding with the C names, plus small helpers that
 allocate outputs and workspaces with torch.
 """
 
-from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DETERMINISTIC, SLIMKV_FP32,  # noqa: F401
+from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # noqa: F401
                       SLIMKV_OP_FULL_KV,
                       SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn,
                       load_library, make_problem, slimkv_abi_version, slimkv_decode_attn,

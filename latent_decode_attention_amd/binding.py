@@ -18,7 +18,7 @@ LIBRARY = pathlib.Path(__file__).resolve().parent / "libslimkv.so"
 
 SLIMKV_FP32, SLIMKV_BF16 = 0, 1
 SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV = 0, 1, 2
-SLIMKV_FLAG_DETERMINISTIC = 1
+SLIMKV_FLAG_DYNAMIC_TILES = 1
 STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}

@@ -55,7 +55,7 @@ slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
   if (!p) return fail(SLIMKV_ERR_NULL, "problem is NULL");
   if (op != SLIMKV_OP_LATENT && op != SLIMKV_OP_RECONSTRUCT && op != SLIMKV_OP_FULL_KV)
     return fail(SLIMKV_ERR_UNSUPPORTED, "unknown op %d", (int)op);
-  if ((p->flags & ~SLIMKV_FLAG_DETERMINISTIC) != 0)
+  if ((p->flags & ~SLIMKV_FLAG_DYNAMIC_TILES) != 0)
     return fail(SLIMKV_ERR_SHAPE, "unknown flag bits 0x%x", (unsigned)p->flags);
   if (p->dtype != SLIMKV_FP32 && p->dtype != SLIMKV_BF16)
     return fail(SLIMKV_ERR_UNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p->dtype);
@@ -126,7 +126,7 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   }
   a.unit_bytes = (int64_t)sb.rows * sb.row_bytes + (int64_t)sr.rows * sr.row_bytes;
   a.chunks = p->num_splits > 0 ? std::min(p->num_splits, kMaxChunks) : 0;  // 0: launcher picks
-  a.deterministic = (p->flags & SLIMKV_FLAG_DETERMINISTIC) != 0;
+  a.deterministic = (p->flags & SLIMKV_FLAG_DYNAMIC_TILES) == 0;
   if (pl.units * kMaxChunks > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;

@@ -40,7 +40,7 @@ struct AttnArgs {
   Segment seg[2];
   int32_t batch, num_q_heads, num_kv_heads, group;
   int32_t chunks;         // workgroups per unit (grid = units * chunks)
-  int32_t deterministic;  // 1: tiles dealt round-robin, not from the counter
+  int32_t deterministic;  // 1: tiles dealt round-robin (default), 0: from the counter
   int64_t unit_bytes;     // cache bytes per unit over both segments
   int32_t rank_v;         // r_V of a latent beacon segment (0 if none)
   const void* q;          // [B, H_q, d] before rotation

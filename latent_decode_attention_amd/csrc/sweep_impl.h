@@ -80,6 +80,16 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8_t& hi, bf16x
   }
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() is a workgroup
+// fence over all memory, so each wave would first wait for every global load,
+// store and atomic it has in flight (the next tile, the tile counter's reply);
+// data exchanged through LDS needs only its own LDS operations complete.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
@@ -269,7 +279,7 @@ struct QueryPrologue {
         sh.qrot[g][i + kHalf] = (float)((v2 * cs + v1 * sn) * a.score_scale);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if constexpr (kLat) {
       // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k] per 16-column tile
 #pragma unroll
@@ -311,7 +321,7 @@ struct QueryPrologue {
             if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
 };
@@ -462,14 +472,14 @@ struct WaveState {
 // ---------------------------------------------------------------------------
 // Where a wave's next tile comes from.  A unit's tiles have positions
 // 0 .. total-1 (beacon tiles, then raw tiles); wave w of the unit starts at
-// position w, and every later position is handed out by the unit's counter
-// (offset by the unit's wave count), so waves that run faster take more
-// tiles and the unit's waves finish together.  Positions only grow, so a
-// wave meets its beacon tiles before its raw tiles.  A position is requested
-// one tile ahead: the counter's reply comes back while a tile is in flight.
-// With `fixed` set the positions are dealt round-robin instead (wave w gets
-// w, w + base, w + 2 base, ...): the same tiles in the same order on every
-// call, so results repeat bit for bit.
+// position w.  By default (`fixed`) the positions are dealt round-robin:
+// wave w gets w, w + base, w + 2 base, ... -- the same tiles in the same
+// order on every call, so results repeat bit for bit.  Otherwise every later
+// position is handed out by the unit's counter (offset by the unit's wave
+// count), so waves that run faster take more tiles; a position is then
+// requested one tile ahead, and the counter's reply comes back while a tile
+// is in flight.  Either way positions only grow, so a wave meets its beacon
+// tiles before its raw tiles.
 struct TileFeed {
   uint32_t* grab;    // the unit's counter (zero between calls)
   int base;          // positions below base are the waves' first tiles
@@ -749,7 +759,7 @@ __device__ __forceinline__ void wg_partial(const AttnArgs& a, AttnShared& sh, in
     sh.sml[sg][g][0] = M;
     sh.sml[sg][g][1] = L;
   }
-  __syncthreads();
+  lds_barrier();
 
   // weights of the two segments for head g within the combined partial
   auto weights = [&](int g, float& wb, float& wr) {
@@ -895,13 +905,13 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 // blocks are dealt to the XCDs in turn, whose speeds differ a little; so a
 // unit made of consecutive blocks, or of blocks on one XCD, would run at the
 // speed of its slot or its XCD.  This numbering gives every unit workgroups
-// of every age on different XCDs, and the unit's tile counter lets the
-// faster ones take more tiles, so the units finish together.  Workgroup c hosts the unit's waves 4c .. 4c+3.  The unit's
-// tiles -- beacon tiles, then raw tiles, all about the same size in bytes --
-// are handed out in order (see TileFeed), so the waves of a unit advance
-// through one sliding window of rows; each wave keeps one tile in flight,
-// across the segment boundary too.  The workgroup writes one partial (slot
-// c of the unit); the workgroup that finishes last merges the unit.
+// of every age on different XCDs, so the units finish together.  Workgroup c
+// hosts the unit's waves 4c .. 4c+3.  The unit's tiles -- beacon tiles, then
+// raw tiles, all about the same size in bytes -- are handed out in order
+// (see TileFeed), so the waves of a unit advance through one sliding window
+// of rows; each wave keeps one tile in flight, across the segment boundary
+// too.  The workgroup writes one partial (slot c of the unit); the
+// workgroup that finishes last merges the unit.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
 template <int G, int NCH, bool BF16>
@@ -986,10 +996,10 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
     uw[1][cc] = vbuf[cc];
   }
   wave_reduce<G, BF16>(st, rw.lpr);
-  __syncthreads();  // every wave is done with its exp-weights (which alias the raw sums)
+  lds_barrier();  // every wave is done with its exp-weights (which alias the raw sums)
                     // and with the query (whose space takes the merged sums)
   wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
-  __syncthreads();
+  lds_barrier();
   const size_t slot = (size_t)unit * k + c;
   wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw, a.part_ml + slot * G * 2,
                             a.part_acc + slot * G * kHeadDim);
@@ -999,13 +1009,13 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   // only then does thread 0 count the workgroup as done.  The workgroup that
   // brings the count to k reads all partials with coherent loads.
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  __syncthreads();  // (nothing is in flight any more: costs no extra wait)
   if (tid == 0) {
     const uint32_t done = __hip_atomic_fetch_add(&a.counters[(size_t)unit * kCounterStride], 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.is_last = done == (uint32_t)(k - 1);
   }
-  __syncthreads();
+  lds_barrier();
   if (!sh.is_last) return;
   // ready for the next call: every workgroup of the unit has counted itself
   // done, after its last request to the tile counter had completed

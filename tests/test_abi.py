@@ -102,7 +102,7 @@ def test_unknown_flag_bits_rejected(lib):
     assert _call(lib, prob) == SHAPE
     assert "flag" in lda.slimkv_last_error()
     assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) == 0
-    prob.flags = lda.SLIMKV_FLAG_DETERMINISTIC
+    prob.flags = lda.SLIMKV_FLAG_DYNAMIC_TILES
     assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) > 0
 
 

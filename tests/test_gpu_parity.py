@@ -156,18 +156,17 @@ def test_constant_values_give_exact_ones(gpu_device):
 
 
 def test_repeat_calls_identical_and_lse_optional(gpu_device):
-    """With the deterministic flag repeated calls are bitwise equal; by
-    default (tiles taken from a shared counter) they agree to rounding."""
+    """By default repeated calls are bitwise equal; with tiles taken from a
+    shared counter they agree to rounding."""
     inp = synth.make_layer(custom(B=2, Hkv=2, G=5, nb=700, w=90, r=48, index=97))
     note("determinism")
-    det = lda.SLIMKV_FLAG_DETERMINISTIC
-    a, la = run_gpu(inp, LAT, flags=det)
-    b, lb = run_gpu(inp, LAT, flags=det)
-    c, lc = run_gpu(inp, LAT, with_lse=False, flags=det)
+    a, la = run_gpu(inp, LAT)
+    b, lb = run_gpu(inp, LAT)
+    c, lc = run_gpu(inp, LAT, with_lse=False)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
     assert np.array_equal(a, c) and lc is None
     for _ in range(3):
-        d, ld = run_gpu(inp, LAT)
+        d, ld = run_gpu(inp, LAT, flags=lda.SLIMKV_FLAG_DYNAMIC_TILES)
         assert np.abs(d - a).max() <= 1e-5 * np.abs(a).max()
         assert np.abs(ld - la).max() <= 1e-5
 
@@ -256,7 +255,7 @@ def test_many_chunks_repeatable(gpu_device):
     probs = [lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
                                       rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
                                       scale=wl.scale, num_splits=48, flags=f)
-             for f in (lda.SLIMKV_FLAG_DETERMINISTIC, 0)]
+             for f in (0, lda.SLIMKV_FLAG_DYNAMIC_TILES)]
     ws = lda.alloc_workspace(probs[0], LAT, "cuda")
     outs = []
     note("many chunks x40, both schedules, one workspace")
@@ -271,7 +270,7 @@ def test_many_chunks_repeatable(gpu_device):
                   outs[0][1].double().cpu().numpy(), ref_lse)
     scale = outs[0][0].abs().max().item()
     for i, (o, l) in enumerate(outs[1:], start=1):
-        if i % 2 == 0:  # deterministic schedule: bitwise equal
+        if i % 2 == 0:  # fixed schedule: bitwise equal
             assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
         else:           # counter schedule: equal up to summation order
             assert (o - outs[0][0]).abs().max().item() <= 1e-5 * scale
