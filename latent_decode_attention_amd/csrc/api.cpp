@@ -247,7 +247,8 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   a.q_pos = q_pos;
   a.U_K = U_K;
   a.U_V = U_V;
-  a.log2_theta = log2(p->rope_theta);
+  for (int k = 0; k < 6; ++k)  // rotary frequencies theta^(-2i/d), i < d/2 = 64
+    a.inv_freq_pow2[k] = pow(p->rope_theta, -2.0 * (double)(1 << k) / (double)kHeadDim);
   a.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
   a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
   a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);

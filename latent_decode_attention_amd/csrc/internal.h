@@ -48,7 +48,8 @@ struct AttnArgs {
   const void* U_K;        // [H_kv, d, r_K] (latent segment only)
   const void* U_V;        // [H_kv, d, r_V] (latent segment only)
   double score_scale;     // scale * log2(e): scores are kept in log2 units
-  double log2_theta;      // log2(rope theta), computed on the host in fp64
+  double inv_freq_pow2[6];  // theta^(-2 * 2^k / d), k = 0..5, on the host in fp64:
+                            // theta^(-2i/d) is the product over i's set bits
   int32_t rank_k;         // r_K of a latent beacon segment (0 if none)
   uint32_t* counters;     // [units][kCounterStride]: workgroups done, tiles handed out
                           // (zero between calls)

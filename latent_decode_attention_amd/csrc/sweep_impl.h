@@ -16,9 +16,10 @@
 //     a 16-byte load) are dealt round-robin over all waves of its workgroups,
 //     beacon tiles first, then raw tiles.  One tile per wave is in flight at
 //     all times, across the boundary between the two segments too.
-//   * Prologue per workgroup: rotation in double precision (angles reduced
-//     mod 2*pi before sincos), the latent projection U_K^T q' as an fp32 MFMA
-//     (16x16x4) into LDS, both while the first tile is in flight.
+//   * Prologue per workgroup: the rotation angle formed and reduced mod 2*pi
+//     in double precision, sine and cosine of the reduced angle in fp32; the
+//     latent projection U_K^T q' on the matrix cores (U_K staged in LDS), both
+//     while the first tile is in flight.
 //   * Scores are a [G x K] x [K x 16 rows] contraction per 16-row subtile on
 //     the matrix cores (v_mfma_f32_16x16x32_bf16; fp32 data uses
 //     v_mfma_f32_16x16x4_f32).  Query heads sit on the M axis, cache rows on
@@ -173,22 +174,29 @@ struct alignas(16) AttnShared {
   int is_last;
 };
 
-// Angle reduced into [-pi, pi] with a two-term 2*pi (fma keeps each step
-// exact up to one rounding), so sincos never sees a large argument.
-__device__ __forceinline__ void rope_sincos(double ang, double& s, double& c) {
+// Rotation angle q_pos * theta^(-2i/d) for pair i < 64: the frequency is the
+// product of the host's theta^(-2 * 2^k / d) over i's set bits (a few fp64
+// roundings), the angle is formed and reduced into [-pi, pi] in fp64 with a
+// two-term 2*pi (each fma step exact up to one rounding), and only the sine
+// and cosine of the reduced angle are taken in fp32 (~2e-7 absolute).
+__device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, float& s, float& c) {
+  double f = 1.0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) f *= ((i >> k) & 1) ? a.inv_freq_pow2[k] : 1.0;
+  const double ang = (double)pos * f;
   constexpr double kTwoPiHi = 6.283185307179586232;     // 2*pi rounded to double
   constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
   constexpr double kInvTwoPi = 0.15915494309189534561;
-  const double k = rint(ang * kInvTwoPi);
-  double r = fma(-k, kTwoPiHi, ang);
-  r = fma(-k, kTwoPiLo, r);
-  sincos(r, &s, &c);
+  const double kk = rint(ang * kInvTwoPi);
+  double r = fma(-kk, kTwoPiHi, ang);
+  r = fma(-kk, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
 }
 
 // ---------------------------------------------------------------------------
 // Prologue, run by every workgroup for its (b, kv head): the G query heads
-// rotated at the query position (rotate-half pairs (i, i + d/2), double
-// precision, angles reduced mod 2*pi) and pre-scaled by scale * log2(e) into
+// rotated at the query position (rotate-half pairs (i, i + d/2), angles in
+// fp64 reduced mod 2*pi, see rope_sincos) and pre-scaled by scale * log2(e) into
 // sh.qrot; with latent beacons also sh.qlat = U_K^T qrot (fp32 MFMA 16x16x4,
 // exact products).  issue() requests every input; the caller then requests
 // its first cache tile and calls finish().  Memory returns in request order,
@@ -270,13 +278,12 @@ struct QueryPrologue {
       const int p = tid + kThreads * j;
       if (p < G * kHalf) {
         const int g = p / kHalf, i = p % kHalf;
-        double sn, cs;
-        // theta^(-2i/d) = 2^(-(2i/d) log2 theta), in double precision
-        const double inv_freq = exp2(-(double)(2 * i) / (double)kHeadDim * a.log2_theta);
-        rope_sincos((double)pos * inv_freq, sn, cs);
-        const double v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
-        sh.qrot[g][i] = (float)((v1 * cs - v2 * sn) * a.score_scale);
-        sh.qrot[g][i + kHalf] = (float)((v2 * cs + v1 * sn) * a.score_scale);
+        float sn, cs;
+        rope_sincos(a, pos, i, sn, cs);
+        const float v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
+        const float sc = (float)a.score_scale;
+        sh.qrot[g][i] = (v1 * cs - v2 * sn) * sc;
+        sh.qrot[g][i + kHalf] = (v2 * cs + v1 * sn) * sc;
       }
     }
     lds_barrier();
@@ -294,9 +301,11 @@ struct QueryPrologue {
 #pragma unroll
             for (int c = 0; c < kHeadDim / 32; ++c) {
               const int i0 = 32 * c + 8 * kg;
-              float x[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) x[e] = n < G ? sh.qrot[n][i0 + e] : 0.0f;
+              // A operand: query head n (rows n >= G compute heads that are
+              // never stored)
+              const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0]);
+              const f32x4_t x1v = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0 + 4]);
+              const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1v[0], x1v[1], x1v[2], x1v[3]};
               bf16x8_t hi, lo;
               split_bf16x8(x, hi, lo);
               u32x4_t bw;
