@@ -289,45 +289,60 @@ struct QueryPrologue {
     lds_barrier();
     if constexpr (kLat) {
       // qlat[g][k] = sum_i qrot[g][i] U_K[i][k]: D[m=g][n=k] per 16-column tile
+      if constexpr (kStage) {
+        // bf16 MFMA over K = i in chunks of 32.  A operand: query head n as
+        // hi + lo bf16 terms (rows n >= G compute heads that are never
+        // stored), split once for all of this wave's tiles; B operand: U_K
+        // exact, lane (n, kg) takes rows 32c + 8kg .. +7 of column c0 + n.
+        bf16x8_t qh[kHeadDim / 32], ql[kHeadDim / 32];
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const int c0 = 16 * (wave + kWaves * t);
-        if (c0 < rk) {
-          f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-          if constexpr (kStage) {
-            // bf16 MFMA over K = i in chunks of 32: the query as hi + lo bf16
-            // terms, U_K exact; lane (n, kg) takes rows 32c + 8kg .. +7 of
-            // column c0 + n
+        for (int c = 0; c < kHeadDim / 32; ++c) {
+          const int i0 = 32 * c + 8 * kg;
+          const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0]);
+          const f32x4_t x1v = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0 + 4]);
+          const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1v[0], x1v[1], x1v[2], x1v[3]};
+          split_bf16x8(x, qh[c], ql[c]);
+        }
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const int c0 = 16 * (wave + kWaves * t);
+          if (c0 < rk) {
+            u32x4_t bw[kHeadDim / 32];  // every LDS read first, then the products
+#pragma unroll
+            for (int c = 0; c < kHeadDim / 32; ++c)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int i = 32 * c + 8 * kg + 2 * e;
+                bw[c][e] = (uint32_t)ul[i * ustride + c0 + n] | ((uint32_t)ul[(i + 1) * ustride + c0 + n] << 16);
+              }
+            f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int c = 0; c < kHeadDim / 32; ++c) {
-              const int i0 = 32 * c + 8 * kg;
-              // A operand: query head n (rows n >= G compute heads that are
-              // never stored)
-              const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0]);
-              const f32x4_t x1v = *reinterpret_cast<const f32x4_t*>(&sh.qrot[n & (kMaxGroup - 1)][i0 + 4]);
-              const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1v[0], x1v[1], x1v[2], x1v[3]};
-              bf16x8_t hi, lo;
-              split_bf16x8(x, hi, lo);
-              u32x4_t bw;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                bw[e] = (uint32_t)ul[(i0 + 2 * e) * ustride + c0 + n] |
-                        ((uint32_t)ul[(i0 + 2 * e + 1) * ustride + c0 + n] << 16);
-              const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw);
-              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, d, 0, 0, 0);
-              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, d, 0, 0, 0);
+              const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bw[c]);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[c], bv, d, 0, 0, 0);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[c], bv, d, 0, 0, 0);
             }
-          } else {
-            // fp32: exact products, K = i in steps of 4
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
+          }
+        }
+      } else {
+        // fp32: exact products, K = i in steps of 4
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const int c0 = 16 * (wave + kWaves * t);
+          if (c0 < rk) {
+            f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < kHeadDim / 4; ++s) {
               const float av = n < G ? sh.qrot[n][4 * s + kg] : 0.0f;
               d = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bits_to_float<BF16>(ub[t][s]), d, 0, 0, 0);
             }
-          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
+            for (int e = 0; e < 4; ++e)
+              if (4 * kg + e < G) sh.qlat[4 * kg + e][c0 + n] = d[e];
+          }
         }
       }
       lds_barrier();
