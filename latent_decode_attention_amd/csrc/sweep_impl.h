@@ -53,6 +53,18 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// x + x of lane ^ 16 (resp. ^ 32), on the VALU: gfx950's permlane swap of x
+// with itself returns, in every lane, its own 16-lane row's value and the
+// partner row's, whose sum is the butterfly step.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // All-reduce within each 16-lane DPP row (row_ror 8, 4, 2, 1).
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp_f<0x128>(x));
@@ -693,8 +705,8 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
 }
 
 // Sum a wave's state over its row groups: the value sums of lanes with equal
-// column (vcc) by a butterfly -- DPP rotations inside 16-lane rows, lane swaps
-// across rows -- and the softmax sums over the 16 lanes of each head row.
+// column (vcc) by a butterfly -- DPP rotations inside 16-lane rows, permlane
+// swaps across rows -- and the softmax sums over the 16 lanes of each head row.
 template <int G, bool BF16>
 __device__ __forceinline__ void wave_reduce(WaveState<G, BF16>& st, int lpr) {
 #pragma unroll
@@ -705,8 +717,8 @@ __device__ __forceinline__ void wave_reduce(WaveState<G, BF16>& st, int lpr) {
       if (lpr <= 8) x += dpp_f<0x128>(x);
       if (lpr <= 4) x += dpp_f<0x124>(x);
       if (lpr <= 2) x += dpp_f<0x122>(x);
-      if (lpr <= 16) x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
+      if (lpr <= 16) x = xor16_sum(x);
+      x = xor32_sum(x);
       st.acc[g][e] = x;
     }
 #pragma unroll
