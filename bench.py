@@ -2,14 +2,16 @@
 """Decode-attention benchmark for libslimkv on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
-                    [--no-cpu-baseline] [--no-compare]
+                    [--no-cpu-baseline] [--no-compare] [--eager]
 
 A step is one decode token's attention over every layer of the workload:
 for the default workload (Llama-3.1-8B shape, 128K context, 16x token
 compression, batch 16) that is 32 calls of slimkv_decode_attn, one per
 layer, each with its own latent rank.  All inputs are generated on the GPU
-before timing and stay resident in HBM.  The timed region is bracketed by
-device synchronisation and measured with events on the stream the library
+before timing and stay resident in HBM.  The step's calls are captured once
+as a HIP graph and replayed (checked bit for bit against the eager step;
+--eager launches them directly).  The timed region is bracketed by device
+synchronisation and measured with events on the stream the library
 launches on.  Prints ONE JSON line.
 
 Reported beside the headline tokens/s:
@@ -46,6 +48,9 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch each step's calls directly instead of replaying the step as one "
+                         "captured HIP graph")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
                          "reduction, for scaling hardware byte counters and as a read ceiling")
@@ -140,11 +145,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run, launch = step, "eager launches"
+    if not args.eager:
+        # A decode step's calls have no host work between them; a serving loop
+        # replays them as one captured graph.  The replay must reproduce the
+        # eager step bit for bit (the library allocates and resets nothing
+        # outside its kernels, so the captured launches are the whole step).
+        ref_out, ref_lse = out.clone(), lse.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        out.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+            raise RuntimeError("graph replay differs from the eager step")
+        run, launch = graph.replay, f"one captured HIP graph per step ({wl.layers} calls)"
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step()
+        run()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -157,8 +179,8 @@ def main():
         f"(wall {wall:.2f}s)")
 
     # Each latent call is one kernel launch, so the events around the timed
-    # region divided by the launches give that kernel's average launch time
-    # (back-to-back launches leave no measurable gap between them).
+    # region divided by the launches give that kernel's average launch time,
+    # the short gap between back-to-back launches included.
     launches = wl.layers * args.steps
     kern_us = ms_step * 1e3 / wl.layers
     kern_bytes = sum(attn_kernel_bytes(wl, layer, elem) for layer in range(wl.layers)) / wl.layers
@@ -189,6 +211,7 @@ def main():
             "seq_len": wl.context,
             "layers": wl.layers,
             "parallelism": "single GPU",
+            "launch": launch,
         },
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
