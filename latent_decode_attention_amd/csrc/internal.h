@@ -14,6 +14,7 @@ constexpr int kThreads = 64 * kWaves;  // attention workgroup size
 constexpr int kMaxGroup = 8;           // query heads per KV head (G)
 constexpr int kMaxChunks = 64;         // workgroups per unit (each writes one partial slot)
 constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
+constexpr int kWgPerCu = 2;            // resident attention workgroups per CU the grid targets
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent

@@ -1061,8 +1061,8 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   merge_unit<G>(a, unit, b, h);
 }
 
-// Workgroups of `kfn` resident per CU and the CU count of the current
-// device, cached per (device, kernel).
+// Workgroup slots the grid fills on the current device: CUs x resident
+// workgroups of `kfn` per CU (at most kWgPerCu), cached per (device, kernel).
 int device_slots(const void* kfn);
 
 // Launch for group size G; nch is the MFMA chunk count of a latent beacon
