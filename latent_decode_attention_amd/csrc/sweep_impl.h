@@ -8,14 +8,16 @@
 // for beacon rows, projected into the head's latent key space (q' U_K).
 // Scores against the latent beacon keys C_K (no rotation) and against the
 // rotated raw keys share one softmax.  Beacon values are summed in latent
-// form (A C_V) and lifted once by U_V after every partial is merged, so
-// beacon keys and values are never rebuilt at full dimension.
+// form (A C_V) and lifted by U_V once per workgroup, on the workgroup's
+// merged latent sum, so beacon keys and values are never rebuilt at full
+// dimension.
 //
 // Mapping onto CDNA4 (gfx950):
 //   * Workgroups of 4 waves; a unit's tiles (16/32/64 rows, every global read
-//     a 16-byte load) are dealt round-robin over all waves of its workgroups,
-//     beacon tiles first, then raw tiles.  One tile per wave is in flight at
-//     all times, across the boundary between the two segments too.
+//     a 16-byte non-temporal buffer load) are dealt round-robin over all waves
+//     of its workgroups, beacon tiles first, then raw tiles.  One tile per
+//     wave is in flight at all times, across the boundary between the two
+//     segments too.
 //   * Prologue per workgroup: the rotation angle formed and reduced mod 2*pi
 //     in double precision, sine and cosine of the reduced angle in fp32; the
 //     latent projection U_K^T q' on the matrix cores (U_K staged in LDS), both
@@ -30,13 +32,14 @@
 //     lives in that layout.  exp-weights reach the value lanes through LDS;
 //     each value lane holds 16 bytes of one value row and G x 8 fp32 sums.
 //   * Each wave parks its beacon state in LDS and goes straight on to its raw
-//     tiles; at the end the four waves merge both segments in LDS and the
-//     workgroup writes one partial per segment with device-coherent stores.
-//     A device-scope counter per unit elects the unit's last workgroup, which
-//     reads the partials back with device-coherent loads, merges them by
-//     log-sum-exp, lifts the latent sum with U_V on the matrix cores (its
-//     U_V rows were requested before the count), writes out and lse, and
-//     resets the counter for the next call.
+//     tiles.  At the end the four waves merge both segments in LDS, the
+//     workgroup lifts its latent sum with U_V on the matrix cores (each wave
+//     requested its U_V rows in place of a further tile, so they arrive with
+//     its last tile), combines it with the raw sum and writes one partial
+//     with device-coherent stores.  A device-scope counter per unit elects
+//     the unit's last workgroup, which reads the partials back with
+//     device-coherent loads, merges them by log-sum-exp, writes out and lse,
+//     and resets the counters for the next call.
 #pragma once
 #include <math.h>
 
@@ -209,8 +212,9 @@ __device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, f
 // Prologue, run by every workgroup for its (b, kv head): the G query heads
 // rotated at the query position (rotate-half pairs (i, i + d/2), angles in
 // fp64 reduced mod 2*pi, see rope_sincos) and pre-scaled by scale * log2(e) into
-// sh.qrot; with latent beacons also sh.qlat = U_K^T qrot (fp32 MFMA 16x16x4,
-// exact products).  issue() requests every input; the caller then requests
+// sh.qrot; with latent beacons also sh.qlat = U_K^T qrot on the matrix cores
+// (bf16: the query as hi + lo bf16 terms against exact U_K staged in LDS;
+// fp32: exact products).  issue() requests every input; the caller then requests
 // its first cache tile and calls finish().  Memory returns in request order,
 // so the prologue's inputs arrive ahead of the tile and its arithmetic
 // overlaps the tile's flight.
@@ -434,13 +438,13 @@ struct SegView {
   __device__ __forceinline__ int val_off(int i) const { return i * rpi * vstride; }
 };
 
-// Where a wave's tile slots read when it has no further tile.
-// DummyTail: q again (any valid bytes; the values go unused).  LiftTail
-// (bf16, latent beacons): this wave's U_V rows for the lift -- key slot c
+// Where a wave's tile slots read when it has no further tile: with bf16
+// latent beacons, this wave's U_V rows for the lift -- key slot c
 // holds row 16 wave + n, value slot c row 16 wave + 64 + n, features
 // 32c + 8kg .. +7 (past r_V they read on into the next row, or zeros past
 // the end, and meet zero latent entries) -- so the lift's inputs arrive
-// while the wave's last tile is processed.
+// while the wave's last tile is processed; otherwise a 16-byte window on q
+// at offsets past its end, so the loads return zeros and go unused.
 struct TailRows {
   __amdgpu_buffer_rsrc_t r;
   int klane, vlane;
@@ -975,7 +979,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   SegView<kFullNch, BF16> rw;  // raw rows
   rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
   // tile positions: beacon tiles 0 .. nbt-1, then raw tiles; this wave's
-  // first is wu, later ones come from the unit's counter
+  // first is wu, later ones round-robin or from the unit's counter
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
   TileFeed feed;
   feed.grab = a.counters + (size_t)unit * kCounterStride + 1;
