@@ -5,7 +5,8 @@ leg may import this package.  The HIP library never does, and this package
 never imports the library: the two share no code.
 
 ``decode`` runs the plain C implementation in ``slimkv_oracle.c`` (double
-precision throughout, OpenMP over (batch, kv head) units).  Its definition
+precision throughout, OpenMP over (batch, kv head) units); ``decode_ragged``
+the same with per-sequence lengths and the decode step's new token.  Its definition
 follows page "Can SlimKV compress KV cache jointly across tokens and
 features", section "Latent-space attention removes the rebuild step": the
 rotated query is projected into each KV head's beacon latent space, scored
@@ -47,10 +48,11 @@ class _Problem(ctypes.Structure):
 
 def build(source: pathlib.Path = SOURCE, target: pathlib.Path = LIBRARY) -> pathlib.Path:
     """Compile the C oracle with gcc (always rebuilds)."""
+    tmp = f"{target}.{os.getpid()}.tmp"  # concurrent builds each write their own file
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
-           str(source), "-o", str(target) + ".tmp", "-lm"]
+           str(source), "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(str(target) + ".tmp", target)
+    os.replace(tmp, target)
     return target
 
 
@@ -67,6 +69,10 @@ def load(path=LIBRARY) -> ctypes.CDLL:
         lib.slimkv_oracle_decode.restype = ctypes.c_int
         lib.slimkv_oracle_decode.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 8 + [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.slimkv_oracle_decode_ragged.restype = ctypes.c_int
+        lib.slimkv_oracle_decode_ragged.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 12 + [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int]
         lib.slimkv_oracle_max_threads.restype = ctypes.c_int
         _lib_cache[key] = lib
     return _lib_cache[key]
@@ -129,6 +135,58 @@ def decode(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, sca
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return out, lse
+
+
+def decode_ragged(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, scale: float,
+                  rope_theta: float, num_beacons=None, raw_len=None, k_new=None, v_new=None,
+                  units=None, threads: int = 0, library: pathlib.Path = LIBRARY):
+    """fp64 decode attention over a ragged batch, with the step's new token.
+
+    The cache arrays are as for ``decode`` but sized to capacities: C_K
+    [B, H_kv, N_cap, r_K] etc., K_raw [B, H_kv, W_cap, d].  ``num_beacons``
+    and ``raw_len`` ([B] int32, None = the capacity) give each sequence's
+    live rows (clamped to [0, capacity]).  ``k_new``, ``v_new`` ([B, H_kv, d],
+    storage dtype, both or neither) are the new token's key before rotation
+    and its value: the key is rotated at q_pos[b], rounded to the storage
+    precision and attended as one more raw row.  Returns (out, lse, k_app):
+    k_app [B, H_kv, d] float64 holds the rounded rotated new keys (NaN
+    without a new token).  A sequence without rows gets out 0, lse -inf.
+    """
+    q = np.ascontiguousarray(q)
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported storage dtype {dt}")
+    B, Hq, d = q.shape
+    q_pos = _arr(q_pos, np.dtype(np.int32))
+    ncap = 0 if C_K is None else int(np.shape(C_K)[2])
+    wcap = 0 if K_raw is None else int(np.shape(K_raw)[2])
+    rk = int(np.shape(U_K)[2]) if U_K is not None else 0
+    rv = int(np.shape(U_V)[2]) if U_V is not None else 0
+    U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new = (
+        _arr(x, dt) for x in (U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new))
+    nbl = _arr(num_beacons, np.dtype(np.int32))
+    rwl = _arr(raw_len, np.dtype(np.int32))
+    prob = _Problem(B, Hq, num_kv_heads, d, ncap, rk, rv, wcap, float(scale), float(rope_theta),
+                    _DTYPE[dt])
+    out = np.full((B, Hq, d), np.nan, dtype=np.float64)
+    lse = np.full((B, Hq), np.nan, dtype=np.float64)
+    k_app = np.full((B, num_kv_heads, d), np.nan, dtype=np.float64)
+    if units is None:
+        unit_arr, n_units = None, 0
+    else:
+        unit_arr = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+        n_units = unit_arr.shape[0]
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = load(library).slimkv_oracle_decode_ragged(
+        ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+        ptr(K_raw), ptr(V_raw), ptr(nbl), ptr(rwl), ptr(k_new), ptr(v_new), ptr(unit_arr),
+        n_units, ptr(out), ptr(lse), ptr(k_app), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out, lse, k_app
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

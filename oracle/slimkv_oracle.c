@@ -32,6 +32,11 @@
  *
  * Inputs are read in their storage format (fp64, fp32, or bf16 as the top
  * 16 bits of an IEEE binary32) and widened exactly to double.
+ *
+ * slimkv_oracle_decode_ragged adds what a serving decode step needs around
+ * that computation: per-sequence numbers of live beacon and raw rows in
+ * capacity-sized arrays, and the step's new token, whose key is rotated at
+ * the query position and attended as one more raw row (see oracle_unit).
  */
 #include <math.h>
 #include <stdint.h>
@@ -73,33 +78,86 @@ static double widen(const void* base, int dtype, size_t i) {
   return (double)f;
 }
 
-/* One (b, kv head) unit: all G query heads of the group. */
+/*
+ * One (b, kv head) unit: all G query heads of the group, in the steps above.
+ *
+ * Ragged batches with an optional new token (one decode step with append):
+ * the cache arrays keep the capacities of the problem as their row strides
+ * (N_cap = num_beacons, W_cap = raw_window); sequence b uses the first
+ * nb_b = clamp(num_beacons_b[b], 0, N_cap) beacon rows and the first
+ * w_b = clamp(raw_len[b], 0, W_cap) raw rows.  With k_new / v_new
+ * ([B, H_kv, d], the new token's key before rotation and its value), the
+ * token's key is rotated at its own position q_pos[b] (the decode token
+ * attends to itself), rounded to the storage precision as a cache row is,
+ * and takes part in the softmax as one more raw row after the w_b others;
+ * when w_b < W_cap it is also the row the cache would store at index w_b,
+ * and k_app (if given) receives that rounded key.  A sequence with no rows
+ * at all gets out = 0 and lse = -inf.  With nb_len = raw_len = NULL and no
+ * new token this is the plain call: every capacity row is live.
+ */
+
+/* Round to the storage precision, to nearest with ties to even. */
+static double narrow(double x, int dtype) {
+  if (dtype == ORACLE_F64) return x;
+  if (dtype == ORACLE_F32) return (double)(float)x;
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  const double m = frexp(x, &e); /* x = m 2^e, 1/2 <= |m| < 1 */
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8); /* 8 significant bits */
+}
+
 static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
                         const int32_t* q_pos, const void* U_K, const void* U_V,
                         const void* C_K, const void* C_V, const void* K_raw,
-                        const void* V_raw, double* out, double* lse,
-                        double* work) {
+                        const void* V_raw, const int32_t* nb_len,
+                        const int32_t* raw_len, const void* k_new,
+                        const void* v_new, double* out, double* lse,
+                        double* k_app, double* work) {
   const int d = p->head_dim, half = p->head_dim / 2;
   const int G = p->num_q_heads / p->num_kv_heads;
-  const int nb = p->num_beacons, w = p->raw_window;
+  const int ncap = p->num_beacons, wcap = p->raw_window;
   const int rk = p->rank_k, rv = p->rank_v;
   const int dt = p->dtype;
-  const size_t n = (size_t)nb + (size_t)w;
+  int nb = nb_len ? nb_len[b] : ncap, w = raw_len ? raw_len[b] : wcap;
+  nb = nb < 0 ? 0 : (nb > ncap ? ncap : nb);
+  w = w < 0 ? 0 : (w > wcap ? wcap : w);
+  const int app = k_new != NULL;
+  const size_t n = (size_t)nb + (size_t)w + (size_t)app;
 
   double* qr = work;          /* [d]   rotated query          */
-  double* qh = qr + d;        /* [rk]  latent query           */
+  double* ka = qr + d;        /* [d]   rotated new key        */
+  double* qh = ka + d;        /* [rk]  latent query           */
   double* s = qh + rk;        /* [n]   scores, then weights   */
   double* olat = s + n;       /* [rv]  latent value sum       */
   double* oraw = olat + rv;   /* [d]   raw value sum          */
 
   const size_t unit = (size_t)b * p->num_kv_heads + h;
-  const size_t ck0 = unit * (size_t)nb * rk, cv0 = unit * (size_t)nb * rv;
-  const size_t kr0 = unit * (size_t)w * d;
+  const size_t ck0 = unit * (size_t)ncap * rk, cv0 = unit * (size_t)ncap * rv;
+  const size_t kr0 = unit * (size_t)wcap * d;
   const size_t uk0 = (size_t)h * d * rk, uv0 = (size_t)h * d * rv;
+
+  /* the new token's key: rotated at q_pos[b], rounded like a cache row */
+  if (app) {
+    for (int i = 0; i < half; ++i) {
+      double inv_freq = pow(p->rope_theta, -2.0 * (double)i / (double)d);
+      double ang = (double)q_pos[b] * inv_freq;
+      double c = cos(ang), sn = sin(ang);
+      double x1 = widen(k_new, dt, unit * d + i), x2 = widen(k_new, dt, unit * d + i + half);
+      ka[i] = narrow(x1 * c - x2 * sn, dt);
+      ka[i + half] = narrow(x2 * c + x1 * sn, dt);
+    }
+    if (k_app)
+      for (int i = 0; i < d; ++i) k_app[unit * d + i] = ka[i];
+  }
 
   for (int g = 0; g < G; ++g) {
     const int hq = h * G + g;
     const size_t q0 = ((size_t)b * p->num_q_heads + hq) * d;
+    if (n == 0) {
+      for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;
+      if (lse) lse[(size_t)b * p->num_q_heads + hq] = -INFINITY;
+      continue;
+    }
 
     /* 1. rotary embedding of the query at its own position */
     for (int i = 0; i < half; ++i) {
@@ -110,7 +168,6 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
       qr[i] = x1 * c - x2 * sn;
       qr[i + half] = x2 * c + x1 * sn;
     }
-
     /* 2. projection into the beacon latent key space: qh = U_K^T q' */
     for (int k = 0; k < rk; ++k) {
       double acc = 0.0;
@@ -118,7 +175,7 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
       qh[k] = acc;
     }
 
-    /* 3. scores: latent beacons, then rotated raw keys */
+    /* 3. scores: live latent beacons, live rotated raw keys, the new token */
     for (int j = 0; j < nb; ++j) {
       double acc = 0.0;
       for (int k = 0; k < rk; ++k) acc += qh[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
@@ -128,6 +185,11 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
       double acc = 0.0;
       for (int i = 0; i < d; ++i) acc += qr[i] * widen(K_raw, dt, kr0 + (size_t)t * d + i);
       s[nb + t] = p->scale * acc;
+    }
+    if (app) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += qr[i] * ka[i];
+      s[nb + w] = p->scale * acc;
     }
 
     /* 4. one softmax over beacon and raw rows together */
@@ -147,6 +209,8 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
     for (int i = 0; i < d; ++i) oraw[i] = 0.0;
     for (int t = 0; t < w; ++t)
       for (int i = 0; i < d; ++i) oraw[i] += s[nb + t] * widen(V_raw, dt, kr0 + (size_t)t * d + i);
+    if (app)
+      for (int i = 0; i < d; ++i) oraw[i] += s[nb + w] * widen(v_new, dt, unit * d + i);
 
     /* 6. lift the latent value sum once: out = U_V o_lat + o_raw */
     for (int i = 0; i < d; ++i) {
@@ -186,7 +250,7 @@ int slimkv_oracle_decode(const oracle_problem* p, const void* q,
   const int rk = p->num_beacons > 0 ? p->rank_k : 0;
   const int rv = p->num_beacons > 0 ? p->rank_v : 0;
   const size_t work_len =
-      2 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window;
+      3 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
   oracle_problem pp = *p;
   pp.rank_k = rk;
   pp.rank_v = rv;
@@ -214,7 +278,77 @@ int slimkv_oracle_decode(const oracle_problem* p, const void* q,
         failed = 2;
         continue;
       }
-      oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse, work);
+      oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, NULL, NULL, NULL, NULL,
+                  out, lse, NULL, work);
+    }
+    free(work);
+  }
+  if (failed == 1) return ORACLE_NO_MEMORY;
+  if (failed == 2) return ORACLE_BAD_SHAPE;
+  return ORACLE_OK;
+}
+
+/*
+ * Ragged counterpart of slimkv_oracle_decode (see oracle_unit).
+ * num_beacons_b, raw_len: [B] live rows per sequence (NULL: the capacity);
+ * k_new, v_new: [B, H_kv, d] in the storage dtype, both or neither;
+ * k_app: [B, H_kv, d] doubles receiving the rounded new keys, or NULL.
+ */
+int slimkv_oracle_decode_ragged(const oracle_problem* p, const void* q,
+                                const int32_t* q_pos, const void* U_K,
+                                const void* U_V, const void* C_K, const void* C_V,
+                                const void* K_raw, const void* V_raw,
+                                const int32_t* num_beacons_b, const int32_t* raw_len,
+                                const void* k_new, const void* v_new,
+                                const int32_t* units, int64_t n_units, double* out,
+                                double* lse, double* k_app, int threads) {
+  if (!p || !q || !q_pos || !out) return ORACLE_BAD_SHAPE;
+  if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
+    return ORACLE_BAD_DTYPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 ||
+      p->num_q_heads % p->num_kv_heads != 0 || p->head_dim < 2 || p->head_dim % 2 ||
+      p->num_beacons < 0 || p->raw_window < 0)
+    return ORACLE_BAD_SHAPE;
+  if (p->num_beacons > 0 && (p->rank_k < 1 || p->rank_v < 1 || !U_K || !U_V || !C_K || !C_V))
+    return ORACLE_BAD_SHAPE;
+  if (p->raw_window > 0 && (!K_raw || !V_raw)) return ORACLE_BAD_SHAPE;
+  if ((k_new == NULL) != (v_new == NULL)) return ORACLE_BAD_SHAPE;
+
+  const int64_t all = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t count = units ? n_units : all;
+  const int rk = p->num_beacons > 0 ? p->rank_k : 0;
+  const int rv = p->num_beacons > 0 ? p->rank_v : 0;
+  const size_t work_len =
+      3 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
+  oracle_problem pp = *p;
+  pp.rank_k = rk;
+  pp.rank_v = rv;
+
+  int failed = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel
+  {
+    double* work = (double*)malloc(work_len * sizeof(double));
+    if (!work) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < count; ++u) {
+      if (!work) continue;
+      int b = units ? units[2 * u] : (int)(u / p->num_kv_heads);
+      int h = units ? units[2 * u + 1] : (int)(u % p->num_kv_heads);
+      if (b < 0 || b >= p->batch || h < 0 || h >= p->num_kv_heads) {
+#pragma omp atomic write
+        failed = 2;
+        continue;
+      }
+      oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b, raw_len,
+                  k_new, v_new, out, lse, k_app, work);
     }
     free(work);
   }

@@ -242,6 +242,156 @@ def pin_closed_forms(library):
     _close(out[0, 0], a * p2["C_V"][0, 0, 0] + (1 - a) * p2["V_raw"][0, 0, 0], what="two keys")
 
 
+# ---------------------------------------------------------------------------
+# Ragged batches and the decode step's new token (oracle.decode_ragged).  A
+# serving step attends each sequence over its own live rows of capacity-sized
+# arrays, after rotating the new token's key at the query position and adding
+# it as one more raw row; the references below rebuild each sequence's rows
+# and run ordinary attention on them.
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 to the nearest bfloat16 value (ties to even), on the
+    IEEE bit pattern: keep 1 + 8 + 7 bits of 1 + 11 + 52."""
+    bits = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    drop = np.uint64(52 - 7)
+    half = np.uint64(1) << (drop - np.uint64(1))
+    keep_lsb = (bits >> drop) & np.uint64(1)
+    rounded = (bits + half - np.uint64(1) + keep_lsb) >> drop << drop
+    return rounded.view(np.float64)
+
+
+def ragged_problem(seed, *, B=4, Hkv=2, G=2, d=16, ncap=9, rk=4, rv=6, wcap=7, theta=10000.0,
+                   q_pos=None, append=True):
+    p = random_problem(seed, B=B, Hkv=Hkv, G=G, d=d, nb=ncap, rk=rk, rv=rv, w=wcap, theta=theta,
+                       q_pos=q_pos)
+    rng = np.random.default_rng(seed + 1000)
+    p["num_beacons"] = rng.integers(0, ncap + 1, size=B).astype(np.int32)
+    p["raw_len"] = rng.integers(0, wcap + 1, size=B).astype(np.int32)
+    if append:
+        p["k_new"] = rng.standard_normal((B, Hkv, d))
+        p["v_new"] = rng.standard_normal((B, Hkv, d))
+    return p
+
+
+def run_ragged(p, library, **over):
+    args = dict(p)
+    args.update(over)
+    ncap = args["C_K"].shape[2]
+    wcap = args["K_raw"].shape[2]
+    return oracle.decode_ragged(
+        args["q"], args["q_pos"], args["U_K"], args["U_V"],
+        args["C_K"] if ncap else None, args["C_V"] if ncap else None,
+        args["K_raw"] if wcap else None, args["V_raw"] if wcap else None,
+        num_kv_heads=args["num_kv_heads"], scale=args["scale"], rope_theta=args["theta"],
+        num_beacons=args.get("num_beacons"), raw_len=args.get("raw_len"),
+        k_new=args.get("k_new"), v_new=args.get("v_new"), library=library)
+
+
+def ragged_reference(p, b):
+    """Sequence b alone: its live beacon rows rebuilt to full keys and
+    values, its live raw rows, and the new token (key rotated at q_pos[b])
+    as the last row; ordinary attention over them.  Returns (out [H_q, d],
+    lse [H_q]); a sequence without rows gives zeros and -inf."""
+    Hkv = p["num_kv_heads"]
+    G = p["q"].shape[1] // Hkv
+    nbc = int(np.clip(p["num_beacons"][b], 0, p["C_K"].shape[2]))
+    wc = int(np.clip(p["raw_len"][b], 0, p["K_raw"].shape[2]))
+    kb = np.einsum("hjr,hdr->hjd", p["C_K"][b, :, :nbc], p["U_K"])
+    vb = np.einsum("hjr,hdr->hjd", p["C_V"][b, :, :nbc], p["U_V"])
+    K = [kb, p["K_raw"][b, :, :wc]]
+    V = [vb, p["V_raw"][b, :, :wc]]
+    if p.get("k_new") is not None:
+        K.append(rope_complex(p["k_new"][b], np.full(Hkv, p["q_pos"][b]), p["theta"])[:, None, :])
+        V.append(p["v_new"][b][:, None, :])
+    K = np.concatenate(K, axis=1)[None]
+    V = np.concatenate(V, axis=1)[None]
+    if K.shape[2] == 0:
+        d = p["q"].shape[2]
+        return np.zeros((Hkv * G, d)), np.full(Hkv * G, -np.inf)
+    q_rot = rope_complex(p["q"][b:b + 1], p["q_pos"][b:b + 1, None], p["theta"])
+    out, lse = sdpa_reference(q_rot, K, V, p["scale"], G)
+    return out[0], lse[0]
+
+
+def pin_ragged_lengths(library):
+    """Per-sequence live rows of capacity-sized arrays, without a new token;
+    dead rows hold large values that must not leak in."""
+    for seed, shape in ((40, dict(B=5, Hkv=2, G=2, d=16, ncap=9, rk=4, rv=6, wcap=7)),
+                        (41, dict(B=3, Hkv=1, G=4, d=32, ncap=0, rk=4, rv=4, wcap=11)),
+                        (42, dict(B=3, Hkv=2, G=1, d=16, ncap=13, rk=8, rv=4, wcap=0))):
+        p = ragged_problem(seed, append=False, **shape)
+        p["num_beacons"][0] = shape["ncap"]
+        p["raw_len"][0] = shape["wcap"]
+        if shape["B"] > 2:
+            p["num_beacons"][1] = 0
+            p["raw_len"][1] = 0
+            # lengths outside [0, capacity] are clamped
+            p["num_beacons"][2] = shape["ncap"] + 5
+            p["raw_len"][2] = -3
+        for name, n in (("C_K", "num_beacons"), ("C_V", "num_beacons"), ("K_raw", "raw_len"),
+                        ("V_raw", "raw_len")):
+            for b in range(shape["B"]):
+                p[name][b, :, max(p[n][b], 0):] = 1e6
+        out, lse, _ = run_ragged(p, library)
+        for b in range(shape["B"]):
+            ref_out, ref_lse = ragged_reference(p, b)
+            _close(out[b], ref_out, what=f"ragged out, seq {b}, {shape}")
+            if np.isinf(ref_lse).all():
+                assert np.all(np.isneginf(lse[b])), "empty sequence lse"
+            else:
+                _close(lse[b], ref_lse, what=f"ragged lse, seq {b}, {shape}")
+
+
+def pin_append_token(library):
+    """The new token joins its sequence as a rotated raw row; its stored key
+    is the rotation of k_new at the query position."""
+    for seed, shape in ((43, dict(B=4, Hkv=2, G=2, d=16, ncap=6, rk=4, rv=4, wcap=5)),
+                        (44, dict(B=2, Hkv=1, G=4, d=128, ncap=33, rk=32, rv=16, wcap=3,
+                                  theta=500000.0, q_pos=131071))):
+        p = ragged_problem(seed, **shape)
+        p["raw_len"][0] = shape["wcap"]  # full window: attended, not storable
+        out, lse, k_app = run_ragged(p, library)
+        for b in range(shape["B"]):
+            ref_out, ref_lse = ragged_reference(p, b)
+            _close(out[b], ref_out, what=f"append out, seq {b}")
+            _close(lse[b], ref_lse, what=f"append lse, seq {b}")
+        ref_k = rope_complex(p["k_new"], p["q_pos"][:, None], p["theta"])
+        _close(k_app, ref_k, tol=1e-10, what="rotated new key")
+
+
+def pin_append_self_score(library):
+    """A sequence holding only the new token: the output is its value and the
+    log-sum-exp is its score, which is scale * q.k whatever the position
+    (query and key turn by the same angle)."""
+    for q_pos in (0, 77, 131071):
+        p = ragged_problem(45, B=2, Hkv=2, G=3, d=32, ncap=4, rk=4, rv=4, wcap=3, q_pos=q_pos,
+                           theta=500000.0)
+        p["num_beacons"][:] = 0
+        p["raw_len"][:] = 0
+        out, lse, _ = run_ragged(p, library)
+        for b in range(2):
+            for hq in range(6):
+                h = hq // 3
+                _close(out[b, hq], p["v_new"][b, h], tol=1e-14, what="single-token out")
+                s = p["scale"] * float(p["q"][b, hq] @ p["k_new"][b, h])
+                _close(lse[b, hq], s, tol=1e-11, what=f"single-token score at {q_pos}")
+
+
+def pin_append_rounding(library):
+    """bf16 storage: the new key is the rotation rounded once to bf16."""
+    p = ragged_problem(46, B=3, Hkv=2, G=2, d=64, ncap=5, rk=16, rv=16, wcap=4, theta=500000.0,
+                       q_pos=40000)
+    bits = {}
+    for name in ("q", "U_K", "U_V", "C_K", "C_V", "K_raw", "V_raw", "k_new", "v_new"):
+        bits[name] = (p[name].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    pb = dict(p)
+    pb.update(bits)
+    _, _, k_app = run_ragged(pb, library)
+    rot = rope_complex(oracle.bf16_to_f64(bits["k_new"]), p["q_pos"][:, None], p["theta"])
+    assert np.array_equal(k_app, bf16_round(rot)), "new key not rounded once to bf16"
+
+
 ALL_PINS = [
     pin_reconstruct_identity,
     pin_raw_only_rope_gqa,
@@ -252,4 +402,8 @@ ALL_PINS = [
     pin_rebasing,
     pin_permutations,
     pin_closed_forms,
+    pin_ragged_lengths,
+    pin_append_token,
+    pin_append_self_score,
+    pin_append_rounding,
 ]

@@ -32,6 +32,17 @@ MUTANTS = {
                             "oraw[i] += s[nb + (t + 1) % w] * widen(V_raw"),
     "raw_values_dropped": ("out[q0 + i] = acc + oraw[i];", "out[q0 + i] = acc;"),
     "no_scale_on_raw_scores": ("s[nb + t] = p->scale * acc;", "s[nb + t] = acc;"),
+    "new_key_unrotated": ("ka[i] = narrow(x1 * c - x2 * sn, dt);\n      ka[i + half] = narrow(x2 * c + x1 * sn, dt);",
+                          "ka[i] = narrow(x1, dt);\n      ka[i + half] = narrow(x2, dt);"),
+    "new_key_one_position_back": ("double ang = (double)q_pos[b] * inv_freq;\n      double c = cos(ang), sn = sin(ang);\n      double x1 = widen(k_new",
+                                  "double ang = (double)(q_pos[b] - 1) * inv_freq;\n      double c = cos(ang), sn = sin(ang);\n      double x1 = widen(k_new"),
+    "new_value_dropped": ("oraw[i] += s[nb + w] * widen(v_new", "oraw[i] += 0.0 * widen(v_new"),
+    "raw_rows_strided_by_live_length": ("const size_t kr0 = unit * (size_t)wcap * d;",
+                                        "const size_t kr0 = unit * (size_t)w * d;"),
+    "beacon_rows_not_clamped": ("nb = nb < 0 ? 0 : (nb > ncap ? ncap : nb);", "nb = nb < 0 ? 0 : nb;"),
+    "bf16_rounding_truncates": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
+    "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
+                               "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
 
 
@@ -53,7 +64,9 @@ print("FAILED_PINS", ",".join(failed))
 def test_mutant_is_caught(name, tmp_path: pathlib.Path):
     src = oracle.SOURCE.read_text()
     old, new = MUTANTS[name]
-    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    # an anchor that occurs more than once (the rotation of the query and of
+    # a new token's key) is mutated everywhere
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
     mutant_src = tmp_path / "mutant.c"
     mutant_src.write_text(src.replace(old, new))
     lib = oracle.build(source=mutant_src, target=tmp_path / "libmutant.so")
