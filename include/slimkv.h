@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 2
+#define SLIMKV_ABI_VERSION 3
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -80,7 +80,8 @@ typedef enum slimkv_dtype {
 typedef enum slimkv_op {
   SLIMKV_OP_LATENT = 0,      /* slimkv_decode_attn      */
   SLIMKV_OP_RECONSTRUCT = 1, /* slimkv_reconstruct_attn */
-  SLIMKV_OP_FULL_KV = 2      /* full_kv_attn            */
+  SLIMKV_OP_FULL_KV = 2,     /* full_kv_attn            */
+  SLIMKV_OP_LATENT_RAGGED = 3 /* slimkv_decode_attn_ragged */
 } slimkv_op;
 
 /* Shape of one layer's call (56 bytes, no implicit padding). */
@@ -145,6 +146,53 @@ slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q,
                                  const void* V_raw, float* out, float* lse,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * slimkv_decode_attn_ragged -- the same attention for one serving decode
+ * step over a ragged batch, with the step's new token.
+ *
+ * The cache arrays are sized to capacities: problem->num_beacons is N_cap,
+ * the beacon rows each (b, kv head) holds in C_K [B, H_kv, N_cap, r_K] and
+ * C_V, and problem->raw_window is W_cap, the raw rows of K_raw, V_raw
+ * [B, H_kv, W_cap, d].  Sequence b uses only its first
+ *   n_b = clamp(num_beacons_b[b], 0, N_cap) beacon rows and
+ *   w_b = clamp(raw_len[b], 0, W_cap) raw rows.
+ * With k_new and v_new ([B, H_kv, d], the new token's key before rotation
+ * and its value, in the problem dtype) the token joins sequence b as one
+ * more raw row: its key is rotated at q_pos[b] (the decode token attends to
+ * itself), computed in double precision and rounded once to the storage
+ * dtype, and scored and summed like the other raw rows.  When w_b < W_cap
+ * the call also stores that rotated key and the value as row w_b of
+ * K_raw and V_raw (the only cache rows it writes; the caller then counts
+ * the row in raw_len).  With a full window the token is attended but not
+ * stored.  A sequence with no rows at all (no new token, n_b = w_b = 0)
+ * gets out = 0 and lse = -inf.
+ *
+ *   num_beacons_b [B] int32  live beacon rows per sequence (device), or
+ *                            NULL for N_cap each
+ *   raw_len       [B] int32  live raw rows before this step (device), or
+ *                            NULL for W_cap each
+ *   k_new, v_new  [B, H_kv, d] the new token (device), both or neither
+ *   K_raw, V_raw  written at the rows above when k_new is given
+ * Other arguments as for slimkv_decode_attn.  N_cap + W_cap may be 0 (then
+ * only the new token is attended).  The batch is at most 1024 sequences and
+ * flags must be 0 (the tiles of the whole batch are shared out over the
+ * grid in a fixed order, so repeated calls are bitwise equal).  num_splits
+ * > 0 sets the number of workgroups of the launch (at most 64 per
+ * (b, kv head)); 0 lets the library pick.  Workspace: slimkv_workspace_bytes
+ * with SLIMKV_OP_LATENT_RAGGED, zero-filled before first use, as for the
+ * other entry points.
+ */
+slimkv_status slimkv_decode_attn_ragged(const slimkv_problem* problem,
+                                        const void* q, const int32_t* q_pos,
+                                        const void* U_K, const void* U_V,
+                                        const void* C_K, const void* C_V,
+                                        void* K_raw, void* V_raw,
+                                        const int32_t* num_beacons_b,
+                                        const int32_t* raw_len,
+                                        const void* k_new, const void* v_new,
+                                        float* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * slimkv_reconstruct_attn -- comparison path: the decode step of the

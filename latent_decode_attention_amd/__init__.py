@@ -7,10 +7,11 @@ allocate outputs and workspaces with torch.
 """
 
 from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # noqa: F401
-                      SLIMKV_OP_FULL_KV,
-                      SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn,
-                      load_library, make_problem, slimkv_abi_version, slimkv_decode_attn,
-                      slimkv_last_error, slimkv_problem, slimkv_reconstruct_attn,
+                      SLIMKV_OP_FULL_KV, SLIMKV_OP_LATENT, SLIMKV_OP_LATENT_RAGGED,
+                      SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn, load_library,
+                      make_problem, slimkv_abi_version, slimkv_decode_attn,
+                      slimkv_decode_attn_ragged, slimkv_last_error, slimkv_problem,
+                      slimkv_reconstruct_attn,
                       slimkv_set_kernel_events, slimkv_status_string,
                       slimkv_workspace_bytes)
 from .helpers import alloc_outputs, alloc_workspace, problem_from_tensors  # noqa: F401

@@ -17,15 +17,15 @@ import torch
 LIBRARY = pathlib.Path(__file__).resolve().parent / "libslimkv.so"
 
 SLIMKV_FP32, SLIMKV_BF16 = 0, 1
-SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV = 0, 1, 2
+SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV, SLIMKV_OP_LATENT_RAGGED = 0, 1, 2, 3
 SLIMKV_FLAG_DYNAMIC_TILES = 1
 STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
-EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_reconstruct_attn",
-           "full_kv_attn", "slimkv_set_kernel_events", "slimkv_status_string",
-           "slimkv_last_error", "slimkv_abi_version")
+EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
+           "slimkv_reconstruct_attn", "full_kv_attn", "slimkv_set_kernel_events",
+           "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
 
 
 class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
@@ -76,6 +76,8 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_workspace_bytes.restype = sz
     lib.slimkv_decode_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_decode_attn.restype = ctypes.c_int
+    lib.slimkv_decode_attn_ragged.argtypes = [prob] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_ragged.restype = ctypes.c_int
     lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_reconstruct_attn.restype = ctypes.c_int
     lib.full_kv_attn.argtypes = [prob] + [vp] * 6 + [vp, sz, vp]
@@ -140,6 +142,16 @@ def slimkv_decode_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
         ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
         _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def slimkv_decode_attn_ragged(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons,
+                              raw_len, k_new, v_new, out, lse, workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_ragged(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,

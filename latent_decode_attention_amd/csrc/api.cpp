@@ -53,10 +53,16 @@ bool rank_ok(int r) { return r >= 16 && r <= kHeadDim && r % 16 == 0; }
 // Shape checks shared by every op.  For full_kv_attn num_beacons must be 0.
 slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
   if (!p) return fail(SLIMKV_ERR_NULL, "problem is NULL");
-  if (op != SLIMKV_OP_LATENT && op != SLIMKV_OP_RECONSTRUCT && op != SLIMKV_OP_FULL_KV)
+  if (op != SLIMKV_OP_LATENT && op != SLIMKV_OP_RECONSTRUCT && op != SLIMKV_OP_FULL_KV &&
+      op != SLIMKV_OP_LATENT_RAGGED)
     return fail(SLIMKV_ERR_UNSUPPORTED, "unknown op %d", (int)op);
+  const bool ragged = op == SLIMKV_OP_LATENT_RAGGED;
   if ((p->flags & ~SLIMKV_FLAG_DYNAMIC_TILES) != 0)
     return fail(SLIMKV_ERR_SHAPE, "unknown flag bits 0x%x", (unsigned)p->flags);
+  if (ragged && p->flags != 0)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "ragged calls take no flags (fixed schedule only)");
+  if (ragged && p->batch > kMaxRaggedBatch)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "ragged batch %d exceeds %d", p->batch, kMaxRaggedBatch);
   if (p->dtype != SLIMKV_FP32 && p->dtype != SLIMKV_BF16)
     return fail(SLIMKV_ERR_UNSUPPORTED, "dtype %d is not fp32 (0) or bf16 (1)", p->dtype);
   if (p->batch < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1)
@@ -73,7 +79,7 @@ slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
     return fail(SLIMKV_ERR_UNSUPPORTED, "head_dim %d is not %d", p->head_dim, kHeadDim);
   if (p->num_beacons < 0 || p->raw_window < 0)
     return fail(SLIMKV_ERR_SHAPE, "num_beacons and raw_window must be >= 0");
-  if ((int64_t)p->num_beacons + p->raw_window < 1)
+  if (!ragged && (int64_t)p->num_beacons + p->raw_window < 1)
     return fail(SLIMKV_ERR_SHAPE, "num_beacons + raw_window must be >= 1");
   if (p->num_beacons > kMaxRows || p->raw_window > kMaxRows)
     return fail(SLIMKV_ERR_UNSUPPORTED, "more than %lld rows per unit", (long long)kMaxRows);
@@ -108,7 +114,7 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   // An absent segment has rows = 0.
   Segment& sb = a.seg[0];
   sb.rows = p->num_beacons;
-  if (op == SLIMKV_OP_LATENT && p->num_beacons > 0) {
+  if ((op == SLIMKV_OP_LATENT || op == SLIMKV_OP_LATENT_RAGGED) && p->num_beacons > 0) {
     sb.kind = kSegLatent;
     sb.rk = p->rank_k;
     sb.rv = p->rank_v;
@@ -129,12 +135,20 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   a.deterministic = (p->flags & SLIMKV_FLAG_DYNAMIC_TILES) == 0;
   if (pl.units * kMaxChunks > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");
+  const bool ragged = op == SLIMKV_OP_LATENT_RAGGED;
+  if (ragged) {
+    // tile positions of the whole batch are 32-bit
+    const int64_t tiles = ceil_div(sb.rows, sb.tile) + ceil_div(sr.rows, sr.tile);
+    if (pl.units * tiles > (int64_t)INT32_MAX)
+      return fail(SLIMKV_ERR_UNSUPPORTED, "too many tiles in the batch");
+  }
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
   a.rank_k = sb.kind == kSegLatent ? p->rank_k : 0;
 
   // workspace layout: per-unit counters (must start zeroed), then one
   // partial slot per workgroup for up to kMaxChunks workgroups per unit
-  const int64_t G = a.group, slots = kMaxChunks;
+  // (ragged: one per piece, fewer than grid + units)
+  const int64_t G = a.group, slots = ragged ? kMaxChunks + 1 : kMaxChunks;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
@@ -293,6 +307,112 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   return SLIMKV_OK;
 }
 
+slimkv_status run_ragged(const slimkv_problem* p, const void* q, const int32_t* q_pos,
+                         const void* U_K, const void* U_V, const void* C_K, const void* C_V,
+                         void* K_raw, void* V_raw, const int32_t* seq_beacons,
+                         const int32_t* seq_raw, const void* k_new, const void* v_new, float* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  slimkv_status st = make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
+  if (st != SLIMKV_OK) return st;
+  const size_t e = (size_t)pl.elem;
+  const size_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = kHeadDim;
+  const size_t nb = p->num_beacons, w = p->raw_window;
+  const bool beacons = nb > 0, raw = w > 0, append = k_new != nullptr || v_new != nullptr;
+  const size_t rk = beacons ? p->rank_k : 0, rv = beacons ? p->rank_v : 0;
+  if (append && (!k_new || !v_new)) return fail(SLIMKV_ERR_NULL, "k_new and v_new go together");
+
+  // Inputs read as 16-byte vectors, then the int32 ones; with a new token
+  // the raw arrays are also written, so they count as outputs too.
+  Range in[10] = {
+      {q, B * Hq * d * e, "q"},
+      {beacons ? U_K : nullptr, Hkv * d * rk * e, "U_K"},
+      {beacons ? U_V : nullptr, Hkv * d * rv * e, "U_V"},
+      {beacons ? C_K : nullptr, B * Hkv * nb * rk * e, "C_K"},
+      {beacons ? C_V : nullptr, B * Hkv * nb * rv * e, "C_V"},
+      {append ? k_new : nullptr, B * Hkv * d * e, "k_new"},
+      {append ? v_new : nullptr, B * Hkv * d * e, "v_new"},
+      {q_pos, B * sizeof(int32_t), "q_pos"},
+      {seq_beacons, seq_beacons ? B * sizeof(int32_t) : 0, "num_beacons_b"},
+      {seq_raw, seq_raw ? B * sizeof(int32_t) : 0, "raw_len"},
+  };
+  const Range kr{raw ? K_raw : nullptr, B * Hkv * w * d * e, "K_raw"};
+  const Range vr{raw ? V_raw : nullptr, B * Hkv * w * d * e, "V_raw"};
+  Range req[11];
+  int n_req = 0;
+  req[n_req++] = in[0];
+  req[n_req++] = in[7];
+  if (beacons)
+    for (int i = 1; i < 5; ++i) req[n_req++] = in[i];
+  if (raw) {
+    req[n_req++] = kr;
+    req[n_req++] = vr;
+  }
+  req[n_req++] = Range{out, 1, "out"};
+  Range outs[5] = {{out, B * Hq * d * sizeof(float), "out"},
+                   {lse, lse ? B * Hq * sizeof(float) : 0, "lse"},
+                   {ws, pl.total, "workspace"},
+                   {append ? kr.p : nullptr, append ? kr.bytes : 0, "K_raw"},
+                   {append ? vr.p : nullptr, append ? vr.bytes : 0, "V_raw"}};
+  Range all_in[12];
+  int n_in = 0;
+  for (int i = 0; i < 10; ++i) all_in[n_in++] = in[i];
+  if (!append) {
+    all_in[n_in++] = kr;
+    all_in[n_in++] = vr;
+  }
+  for (int i = 7; i < 10; ++i)
+    if (in[i].p && (uintptr_t)in[i].p % 4 != 0)
+      return fail(SLIMKV_ERR_ALIGN, "%s is not 4-byte aligned", in[i].name);
+  for (const Range* x : {&kr, &vr})
+    if (x->p && (uintptr_t)x->p % 16 != 0)
+      return fail(SLIMKV_ERR_ALIGN, "%s is not 16-byte aligned", x->name);
+  st = check_pointers(in, 7, req, n_req, outs, 0, 16);  // presence and 16-byte alignment
+  if (st != SLIMKV_OK) return st;
+  st = check_pointers(all_in, n_in, req, 0, outs, 5, 1);  // overlaps
+  if (st != SLIMKV_OK) return st;
+  if (!ws) return fail(SLIMKV_ERR_NULL, "workspace is NULL");
+  if ((uintptr_t)ws % 16 != 0) return fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < pl.total)
+    return fail(SLIMKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+
+  char* wsb = static_cast<char*>(ws);
+  AttnArgs& a = pl.attn;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.U_K = U_K;
+  a.U_V = U_V;
+  for (int k = 0; k < 6; ++k)
+    a.inv_freq_pow2[k] = pow(p->rope_theta, -2.0 * (double)(1 << k) / (double)kHeadDim);
+  a.score_scale = (double)p->scale * 1.4426950408889634074;
+  a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
+  a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
+  a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
+  a.out = out;
+  a.lse = lse;
+  if (beacons) {
+    a.seg[0].K = C_K;
+    a.seg[0].V = C_V;
+  }
+  if (raw) {
+    a.seg[1].K = K_raw;
+    a.seg[1].V = V_raw;
+  }
+  a.seq_beacons = seq_beacons;
+  a.seq_raw = seq_raw;
+  a.k_new = append ? k_new : nullptr;
+  a.v_new = append ? v_new : nullptr;
+  a.k_store = K_raw;
+  a.v_store = V_raw;
+  a.deterministic = 1;
+  const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+  g_ev_start = g_ev_stop = nullptr;
+  const hipError_t err = launch_ragged(a, pl.dtype, static_cast<hipStream_t>(stream), ev0, ev1);
+  if (err != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+  g_last_error.clear();
+  return SLIMKV_OK;
+}
+
 }  // namespace
 }  // namespace slimkv
 
@@ -326,6 +446,16 @@ slimkv_status full_kv_attn(const slimkv_problem* problem, const void* q, const i
                            size_t workspace_bytes, void* stream) {
   return slimkv::run(problem, SLIMKV_OP_FULL_KV, q, q_pos, nullptr, nullptr, nullptr, nullptr, K,
                      V, out, lse, workspace, workspace_bytes, stream);
+}
+
+slimkv_status slimkv_decode_attn_ragged(const slimkv_problem* problem, const void* q,
+                                        const int32_t* q_pos, const void* U_K, const void* U_V,
+                                        const void* C_K, const void* C_V, void* K_raw, void* V_raw,
+                                        const int32_t* num_beacons_b, const int32_t* raw_len,
+                                        const void* k_new, const void* v_new, float* out, float* lse,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return slimkv::run_ragged(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b,
+                            raw_len, k_new, v_new, out, lse, workspace, workspace_bytes, stream);
 }
 
 const char* slimkv_status_string(slimkv_status status) {

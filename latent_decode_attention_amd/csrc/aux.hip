@@ -168,6 +168,37 @@ hipError_t launch_attention_g6(AttnArgs, int, int, hipStream_t, hipEvent_t, hipE
 hipError_t launch_attention_g7(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
 hipError_t launch_attention_g8(AttnArgs, int, int, hipStream_t, hipEvent_t, hipEvent_t);
 
+hipError_t launch_ragged_g1(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g2(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g3(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g4(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g5(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g6(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g7(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+hipError_t launch_ragged_g8(AttnArgs, int, int, int64_t, hipStream_t, hipEvent_t, hipEvent_t);
+
+// MFMA chunks of a latent beacon segment's rows (0: full width, or none)
+static int beacon_chunks(const AttnArgs& a) {
+  if (a.seg[0].kind != kSegLatent || a.seg[0].rows <= 0) return 0;
+  return std::max((a.seg[0].rk + 31) / 32, (a.seg[0].rv + 31) / 32);
+}
+
+hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const int nch = beacon_chunks(a);
+  // partial slots: one per (workgroup, unit) piece, rank + unit < grid + units
+  const int64_t max_wgs = (int64_t)a.batch * a.num_kv_heads * kMaxChunks;
+  switch (a.group) {
+    case 1: return launch_ragged_g1(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 2: return launch_ragged_g2(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 3: return launch_ragged_g3(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 4: return launch_ragged_g4(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 5: return launch_ragged_g5(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 6: return launch_ragged_g6(a, dtype, nch, max_wgs, s, ev0, ev1);
+    case 7: return launch_ragged_g7(a, dtype, nch, max_wgs, s, ev0, ev1);
+    default: return launch_ragged_g8(a, dtype, nch, max_wgs, s, ev0, ev1);
+  }
+}
+
 hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   int nch = 0;  // beacon rows at full width, or none
   if (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0) {

@@ -15,6 +15,7 @@ constexpr int kMaxGroup = 8;           // query heads per KV head (G)
 constexpr int kMaxChunks = 64;         // workgroups per unit (each writes one partial slot)
 constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
 constexpr int kWgPerCu = 2;            // resident attention workgroups per CU the grid targets
+constexpr int kMaxRaggedBatch = 1024;  // sequences per ragged call (their lengths sit in LDS)
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -58,6 +59,14 @@ struct AttnArgs {
   float* part_acc;        // [units, chunks, G, d]  exp-weighted value sums
   float* out;             // [B, H_q, d]
   float* lse;             // [B, H_q] or null
+  // Ragged calls only (seg[0].rows, seg[1].rows are then the capacities,
+  // i.e. the row strides of each unit's arrays):
+  const int32_t* seq_beacons;  // [B] live beacon rows per sequence, or null (all)
+  const int32_t* seq_raw;      // [B] live raw rows before the new token, or null (all)
+  const void* k_new;           // [B, H_kv, d] the new token's key before rotation, or null
+  const void* v_new;           // [B, H_kv, d] its value (with k_new)
+  void* k_store;               // K_raw / V_raw: the new token's row is written at
+  void* v_store;               //   index seq_raw[b] when that is below the capacity
 };
 
 struct RebuildArgs {
@@ -73,6 +82,8 @@ struct RebuildArgs {
 // workgroup slots (CUs x resident workgroups of the chosen kernel).
 hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0,
                             hipEvent_t ev1);
+// The ragged-batch attention kernel (one launch; see ragged_impl.h).
+hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 // Chunks per unit: the count in [1, kMaxChunks] whose workgroups fill the
 // device's slots best (no chunk under min_chunk_bytes).

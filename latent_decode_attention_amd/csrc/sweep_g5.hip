@@ -1,9 +1,13 @@
-// sweep_g5.hip -- attention kernels for 5 query heads per KV head.
+// sweep_g5.hip -- attention kernels (uniform and ragged) for 5 query heads per KV head.
 #include "sweep_impl.h"
 
 namespace slimkv {
 hipError_t launch_attention_g5(AttnArgs a, int dtype, int nch, hipStream_t s,
                                  hipEvent_t ev0, hipEvent_t ev1) {
   return launch_attention_group<5>(a, dtype, nch, s, ev0, ev1);
+}
+hipError_t launch_ragged_g5(AttnArgs a, int dtype, int nch, int64_t max_wgs, hipStream_t s,
+                              hipEvent_t ev0, hipEvent_t ev1) {
+  return launch_ragged_group<5>(a, dtype, nch, max_wgs, s, ev0, ev1);
 }
 }  // namespace slimkv

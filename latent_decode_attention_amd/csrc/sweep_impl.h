@@ -43,6 +43,8 @@
 #pragma once
 #include <math.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace slimkv {
@@ -407,14 +409,15 @@ struct SegView {
   int lpr, rpi, vrow, vcc, lanes_row;
   bool vact;
 
-  __device__ __forceinline__ void init(const void* Kp, const void* Vp, int rows_, int rk_, int rv_,
-                                       int unit, int lane) {
+  // cap: rows each unit's arrays hold (the unit stride); rows_: live rows
+  __device__ __forceinline__ void init(const void* Kp, const void* Vp, int cap, int rows_, int rk_,
+                                       int rv_, int unit, int lane) {
     rows = rows_;
     rk = rk_;
     rv = rv_;
     kstride = rk * Tr::kElemBytes;
     vstride = rv * Tr::kElemBytes;
-    const size_t urow = (size_t)unit * (size_t)rows;
+    const size_t urow = (size_t)unit * (size_t)cap;
     kr = make_rsrc(static_cast<const char*>(Kp) + urow * kstride, (uint32_t)rows * kstride);
     vr = make_rsrc(static_cast<const char*>(Vp) + urow * vstride, (uint32_t)rows * vstride);
     ntiles = (rows + kRows - 1) / kRows;
@@ -547,8 +550,9 @@ struct TileFeed {
 // the next position lies past this segment but before pend, it is a tile of
 // the next segment (`nx`, tile 0 at position nxbase) and is requested the
 // same way, so the stream of loads does not stop between segments (CROSS;
-// past pend the slots take the tail's addresses instead).  On exit j is the
-// first position past this segment the wave drew.
+// past pend the slots take the tail's addresses instead).  Positions from
+// pend on are not this sweep's to process.  On exit j is the first position
+// past this segment (or pend) the wave drew.
 template <int G, int NCH, bool BF16, bool CROSS, int NCH2>
 __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
                                       const SegView<NCH2, BF16>& nx, int nxbase, int pend, int& j,
@@ -565,7 +569,7 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
   constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
   static_assert(SUB * NCH <= Tr::kMaxLoads, "tile too large");
   constexpr int TR2 = SegView<NCH2, BF16>::kRows;
-  const int pstop = pbase + sv.ntiles;
+  const int pstop = min(pbase + sv.ntiles, pend);
   if (j >= pstop) return;  // wave-uniform
 
   const int lane = threadIdx.x & 63;
@@ -974,10 +978,10 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int wu = kWaves * c + wave;  // this wave's number within the unit
 
   SegView<BN, BF16> bv;  // beacon rows
-  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, BLAT ? a.seg[0].rk : kHeadDim,
+  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, a.seg[0].rows, BLAT ? a.seg[0].rk : kHeadDim,
           BLAT ? a.seg[0].rv : kHeadDim, unit, lane);
   SegView<kFullNch, BF16> rw;  // raw rows
-  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
+  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
   // tile positions: beacon tiles 0 .. nbt-1, then raw tiles; this wave's
   // first is wu, later ones round-robin or from the unit's counter
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
@@ -1106,3 +1110,5 @@ hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s,
 }
 
 }  // namespace slimkv
+
+#include "ragged_impl.h"

@@ -41,7 +41,8 @@ from .configs import Workload
 
 TOKEN_BLOCK = 128
 
-_IDS = {"q": 1, "U_K": 2, "U_V": 3, "C_K": 4, "C_V": 5, "K_tok": 6, "V_tok": 7}
+_IDS = {"q": 1, "U_K": 2, "U_V": 3, "C_K": 4, "C_V": 5, "K_tok": 6, "V_tok": 7, "lengths": 8,
+        "k_new": 9, "v_new": 10}
 
 _TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -164,6 +165,42 @@ def make_full_kv(wl: Workload, layer: int = 0, *, base_seed: int = 0, device="cp
     k = _tokens(wl, layer, "K_tok", base_seed, 0, wl.context, device)
     v = _tokens(wl, layer, "V_tok", base_seed, 0, wl.context, device)
     return k, v
+
+
+@dataclasses.dataclass
+class StepInputs:
+    """What a serving decode step adds to a layer's cache arrays: each
+    sequence's live beacon and raw rows, and the step's new token (its key
+    before rotation, and its value) per KV head."""
+
+    num_beacons: torch.Tensor  # [B] int32
+    raw_len: torch.Tensor      # [B] int32
+    k_new: torch.Tensor        # [B, H_kv, d]
+    v_new: torch.Tensor        # [B, H_kv, d]
+
+    def to(self, device) -> "StepInputs":
+        return StepInputs(*(getattr(self, f.name).to(device) for f in dataclasses.fields(self)))
+
+
+def make_step(wl: Workload, inp: LayerInputs, *, base_seed: int = 0, device="cpu",
+              beacons=(0.0, 1.0), raw=(0.0, 1.0), fixed: dict | None = None) -> StepInputs:
+    """Seeded per-sequence lengths for ``inp``'s capacity-sized arrays and
+    the step's new token.  Live rows are drawn uniformly from
+    [lo * capacity, hi * capacity] for the given fractions (beacons, raw);
+    ``fixed`` maps a sequence index to a (beacons, raw) pair that overrides
+    its draw (edge cases: empty, full, beyond the capacity)."""
+    ncap, wcap = inp.num_beacons, inp.raw_window
+    ss = np.random.SeedSequence([base_seed, wl.index, inp.layer, _IDS["lengths"], ncap, wcap])
+    rng = np.random.default_rng(ss)
+    nb = rng.integers(int(beacons[0] * ncap), int(beacons[1] * ncap) + 1, size=wl.batch)
+    rw = rng.integers(int(raw[0] * wcap), int(raw[1] * wcap) + 1, size=wl.batch)
+    for b, (x, y) in (fixed or {}).items():
+        nb[b], rw[b] = x, y
+    shape = (wl.batch, wl.num_kv_heads, wl.head_dim)
+    k = _gauss(shape, _seed(base_seed, wl, inp.layer, "k_new"), wl.sigma, wl.dtype, device)
+    v = _gauss(shape, _seed(base_seed, wl, inp.layer, "v_new"), wl.sigma, wl.dtype, device)
+    return StepInputs(torch.from_numpy(nb.astype(np.int32)).to(device),
+                      torch.from_numpy(rw.astype(np.int32)).to(device), k, v)
 
 
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:

@@ -148,3 +148,110 @@ def gather_units(out, lse, wl, units):
     got = np.stack([out[b, h * G:(h + 1) * G] for b, h in units])
     got_lse = np.stack([lse[b, h * G:(h + 1) * G] for b, h in units])
     return got, got_lse
+
+
+def run_gpu_ragged(inp: synth.LayerInputs, step: synth.StepInputs, *, append: bool = True,
+                   lengths: bool = True, num_splits: int = 0, device="cuda"):
+    """slimkv_decode_attn_ragged on ``inp`` (capacity-sized arrays) and
+    ``step``.  The raw cache is cloned first (the call writes the new rows);
+    returns (out, lse, K_raw, V_raw) on the host."""
+    wl = inp.workload
+    g = inp.to(device)
+    st = step.to(device)
+    K, V = g.K_raw.clone(), g.V_raw.clone()
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=num_splits)
+    out, lse = lda.alloc_outputs(prob, device)
+    ws = lda.alloc_workspace(prob, lda.SLIMKV_OP_LATENT_RAGGED, device)
+    lda.slimkv_decode_attn_ragged(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, K, V,
+                                  st.num_beacons if lengths else None,
+                                  st.raw_len if lengths else None,
+                                  st.k_new if append else None, st.v_new if append else None,
+                                  out, lse, ws)
+    torch.cuda.synchronize()
+    return (out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu())
+
+
+def oracle_ragged(inp: synth.LayerInputs, step: synth.StepInputs, *, append: bool = True,
+                  lengths: bool = True, units=None):
+    """oracle.decode_ragged on the whole layer (or the listed units)."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    nb, w = inp.num_beacons, inp.raw_window
+    return oracle.decode_ragged(
+        st(inp.q), st(inp.q_pos), st(inp.U_K), st(inp.U_V), st(inp.C_K) if nb else None,
+        st(inp.C_V) if nb else None, st(inp.K_raw) if w else None, st(inp.V_raw) if w else None,
+        num_kv_heads=wl.num_kv_heads, scale=wl.scale, rope_theta=wl.rope_theta,
+        num_beacons=st(step.num_beacons) if lengths else None,
+        raw_len=st(step.raw_len) if lengths else None,
+        k_new=st(step.k_new) if append else None, v_new=st(step.v_new) if append else None,
+        units=units)
+
+
+def oracle_ragged_units(inp: synth.LayerInputs, step: synth.StepInputs, units):
+    """oracle.decode_ragged on sampled units, copying only each unit's slices.
+    Returns {(b, h): (out [G, d], lse [G], k_app [d])}."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    res = {}
+    for b, h in units:
+        s = synth.unit_slices(inp, b, h)
+        nb, w = s["C_K"].shape[2], s["K_raw"].shape[2]
+        o, l, k = oracle.decode_ragged(
+            s["q"], s["q_pos"], s["U_K"], s["U_V"], s["C_K"] if nb else None,
+            s["C_V"] if nb else None, s["K_raw"] if w else None, s["V_raw"] if w else None,
+            num_kv_heads=1, scale=wl.scale, rope_theta=wl.rope_theta,
+            num_beacons=st(step.num_beacons[b:b + 1]), raw_len=st(step.raw_len[b:b + 1]),
+            k_new=st(step.k_new[b:b + 1, h:h + 1]), v_new=st(step.v_new[b:b + 1, h:h + 1]))
+        res[(b, h)] = (o[0], l[0], k[0, 0])
+    return res
+
+
+def storage_to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 values of a bf16 or fp32 tensor."""
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def assert_new_rows(K_after, V_after, K_before, V_before, step, k_app, units=None):
+    """The call wrote exactly the new token's rows (row raw_len[b] of each
+    unit whose window has room): keys equal the oracle's rotated, rounded
+    key -- bit for bit, up to a rare one-ulp difference where the fp64
+    rotation lands on a rounding tie (counted, at most 1 in 10^4) -- and
+    values equal v_new; every other row is untouched."""
+    Ka, Va = storage_to_f64(K_after), storage_to_f64(V_after)
+    Kb, Vb = storage_to_f64(K_before), storage_to_f64(V_before)
+    vnew = storage_to_f64(step.v_new)
+    B, Hkv, wcap, d = Ka.shape
+    mask = np.zeros((B, Hkv, wcap), dtype=bool)
+    raw_len = step.raw_len.cpu().numpy()
+    units = units or [(b, h) for b in range(B) for h in range(Hkv)]
+    off_by_ulp = compared = 0
+    for b, h in units:
+        w = int(np.clip(raw_len[b], 0, wcap))
+        if w >= wcap:
+            continue
+        mask[b, h, w] = True
+        got, exp = Ka[b, h, w], k_app[(b, h)] if isinstance(k_app, dict) else k_app[b, h]
+        diff = got != exp
+        if diff.any():
+            ulp = np.abs(np.spacing(exp.astype(np.float32)).astype(np.float64))
+            if K_after.dtype == torch.bfloat16:
+                ulp = ulp * 65536.0
+            assert np.all(np.abs(got - exp)[diff] <= ulp[diff] * 1.0001), \
+                f"stored key of ({b}, {h}) off by more than one ulp"
+            off_by_ulp += int(diff.sum())
+        compared += d
+        assert np.array_equal(Va[b, h, w], vnew[b, h]), f"stored value of ({b}, {h})"
+    assert off_by_ulp <= max(1, compared // 10000), f"{off_by_ulp} of {compared} key elements"
+    keep = ~mask
+    if units is not None:
+        sel = np.zeros((B, Hkv), dtype=bool)
+        for b, h in units:
+            sel[b, h] = True
+        keep &= sel[:, :, None]
+    assert np.array_equal(Ka[keep], Kb[keep]) and np.array_equal(Va[keep], Vb[keep]), \
+        "rows other than the new token's were written"
+    print(f"[parity] new rows: {int(mask.sum())} written, {off_by_ulp} key elements one ulp off",
+          flush=True)
+

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 2
+    assert lda.slimkv_abi_version() == 3
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -175,3 +175,51 @@ def test_workspace_does_not_depend_on_split_choice(lib):
     sizes = {lib.slimkv_workspace_bytes(ctypes.byref(_problem(num_splits=s)), 0)
              for s in (0, 1, 4, 64, 1000)}
     assert len(sizes) == 1
+
+
+def _call_ragged(lib, prob, *, ptrs=None, ws_bytes=1 << 30):
+    """slimkv_decode_attn_ragged with fake device addresses (every case
+    fails validation before any HIP call)."""
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, nb=0x210000, raw=0x220000,
+             k_new=0x230000, v_new=0x240000, out=0x5000000, lse=0x6000000, ws=0x7000000)
+    p.update(ptrs or {})
+    v = {k: (None if x is None else ctypes.c_void_p(x)) for k, x in p.items()}
+    pp = ctypes.byref(prob) if prob is not None else None
+    return lib.slimkv_decode_attn_ragged(pp, v["q"], v["q_pos"], v["U_K"], v["U_V"], v["C_K"],
+                                         v["C_V"], v["K_raw"], v["V_raw"], v["nb"], v["raw"],
+                                         v["k_new"], v["v_new"], v["out"], v["lse"], v["ws"],
+                                         ws_bytes, None)
+
+
+def test_ragged_checks(lib):
+    ragged = lda.SLIMKV_OP_LATENT_RAGGED
+    prob = _problem()
+    need = lib.slimkv_workspace_bytes(ctypes.byref(prob), ragged)
+    assert need > lib.slimkv_workspace_bytes(ctypes.byref(prob), 0)
+    assert _call_ragged(lib, prob, ws_bytes=need - 1) == WS
+    # only the new token: no cache rows at all is a valid ragged problem
+    empty = _problem(num_beacons=0, raw_window=0)
+    assert lib.slimkv_workspace_bytes(ctypes.byref(empty), ragged) > 0
+    assert lib.slimkv_workspace_bytes(ctypes.byref(empty), 0) == 0
+    assert _call_ragged(lib, empty, ptrs=dict(U_K=None, U_V=None, C_K=None, C_V=None,
+                                               K_raw=None, V_raw=None), ws_bytes=16) == WS
+    # the schedule is fixed; the lengths live in LDS
+    prob.flags = lda.SLIMKV_FLAG_DYNAMIC_TILES
+    assert _call_ragged(lib, prob) == UNSUP
+    assert _call_ragged(lib, _problem(batch=1025)) == UNSUP
+    assert _call_ragged(lib, _problem(batch=1024), ws_bytes=16) == WS
+    # the new token's key and value come together
+    assert _call_ragged(lib, _problem(), ptrs=dict(v_new=None)) == NULL
+    assert _call_ragged(lib, _problem(), ptrs=dict(k_new=None)) == NULL
+    # lengths are optional; no new token is fine
+    assert _call_ragged(lib, _problem(), ptrs=dict(nb=None, raw=None, k_new=None, v_new=None),
+                        ws_bytes=16) == WS
+    assert _call_ragged(lib, _problem(), ptrs=dict(raw=0x220002)) == ALIGN
+    assert _call_ragged(lib, _problem(), ptrs=dict(k_new=0x230008)) == ALIGN
+    # with a new token the raw window is written: it must not overlap inputs
+    assert _call_ragged(lib, _problem(), ptrs=dict(k_new=0x3000000 + 256)) == ALIAS
+    assert _call_ragged(lib, _problem(), ptrs=dict(ws=0x4000000)) == ALIAS
+    # without one it is only read, and may not overlap the outputs either
+    assert _call_ragged(lib, _problem(), ptrs=dict(k_new=None, v_new=None, out=0x3000000)) == ALIAS
+

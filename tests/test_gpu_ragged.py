@@ -1,0 +1,136 @@
+"""slimkv_decode_attn_ragged against the fp64 oracle: ragged batches in
+capacity-sized arrays, and the decode step's new token (attended as a rotated
+raw row, and stored when the window has room)."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import latent_decode_attention_amd as lda
+import synth
+from parity_util import (assert_new_rows, assert_parity, gather_units, note, oracle_layer,
+                         oracle_ragged, oracle_ragged_units, run_gpu, run_gpu_ragged,
+                         sample_units)
+
+pytestmark = pytest.mark.gpu
+
+
+def custom(dtype="bf16", B=8, Hkv=2, G=4, nb=1000, w=300, r=64, sigma=1.0, theta=5e5,
+           context=32768, index=95):
+    return dataclasses.replace(
+        synth.get_workload("c2"), name="ragged", index=index, batch=B, num_q_heads=Hkv * G,
+        num_kv_heads=Hkv, num_beacons=nb, raw_window=w, ranks=(r,), dtype=dtype, sigma=sigma,
+        rope_theta=theta, context=context)
+
+
+# sequence index -> (live beacons, live raw rows): no rows, full (the new
+# token is attended but not stored), beyond the capacity (clamped), one row
+def edge_cases(nb, w):
+    return {0: (0, 0), 1: (nb, w), 2: (nb + 7, -5), 3: (1, 1)}
+
+
+def check_ragged(wl, *, rank_v=None, append=True, lengths=True, num_splits=0, fixed=None,
+                 what=""):
+    inp = synth.make_layer(wl, rank_v=rank_v)
+    step = synth.make_step(wl, inp, fixed=edge_cases(inp.num_beacons, inp.raw_window)
+                           if fixed is None else fixed)
+    note(f"ragged {what}: B={wl.batch} Hkv={wl.num_kv_heads} G={wl.group} "
+         f"cap=({inp.num_beacons}, {inp.raw_window}) r=({inp.rank_k}, {inp.rank_v}) {wl.dtype} "
+         f"append={append} lengths={lengths} splits={num_splits}")
+    out, lse, K, V = run_gpu_ragged(inp, step, append=append, lengths=lengths,
+                                    num_splits=num_splits)
+    ref, ref_lse, k_app = oracle_ragged(inp, step, append=append, lengths=lengths)
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty), "sequences without rows"
+    assert np.all(out[empty] == 0.0)
+    assert_parity(out, ref, wl.dtype, what, np.where(empty, 0.0, lse), np.where(empty, 0.0, ref_lse))
+    if append:
+        assert_new_rows(K, V, inp.K_raw, inp.V_raw, step, k_app)
+    else:
+        assert torch.equal(K, inp.K_raw) and torch.equal(V, inp.V_raw)
+    return out, lse
+
+
+def test_bf16_append(gpu_device):
+    check_ragged(custom(), what="bf16 G4 append")
+
+
+def test_bf16_lengths_only(gpu_device):
+    check_ragged(custom(), append=False, what="bf16 G4 no new token")
+
+
+def test_bf16_g5_uneven_ranks(gpu_device):
+    wl = custom(B=5, Hkv=3, G=5, nb=777, w=129, r=48, theta=1e6, index=96)
+    check_ragged(wl, rank_v=96, what="bf16 G5 r48/96")
+
+
+@pytest.mark.parametrize("G,r", [(1, 32), (8, 128)])
+def test_bf16_group_extremes(G, r, gpu_device):
+    check_ragged(custom(B=6, Hkv=1, G=G, nb=500, w=70, r=r, index=97 + G), what=f"bf16 G{G}")
+
+
+def test_fp32(gpu_device):
+    wl = custom(dtype="fp32", B=6, Hkv=2, G=5, nb=300, w=45, r=32, index=99)
+    check_ragged(wl, what="fp32 G5")
+
+
+def test_fp32_no_beacons(gpu_device):
+    wl = custom(dtype="fp32", B=4, Hkv=2, G=4, nb=0, w=64, r=32, index=100)
+    check_ragged(wl, fixed={0: (0, 0), 1: (0, 64), 2: (0, 63)}, what="fp32 raw only")
+
+
+def test_only_new_token(gpu_device):
+    """No cache capacity at all: each sequence attends only to its new token
+    (nothing can be stored)."""
+    wl = custom(B=4, Hkv=2, G=4, nb=0, w=0, index=101)
+    check_ragged(wl, fixed={}, what="new token only")
+    check_ragged(wl, fixed={}, append=False, what="nothing at all")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64, 333])
+def test_grid_sizes(splits, gpu_device):
+    """Shares that cut units anywhere (down to one workgroup for the batch)."""
+    check_ragged(custom(B=8, Hkv=2, G=4, nb=600, w=200, index=102), num_splits=splits,
+                 what=f"grid {splits}")
+
+
+def test_repeatable(gpu_device):
+    wl = custom(index=103)
+    a = check_ragged(wl, what="first")
+    b = check_ragged(wl, what="second")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_full_lengths_match_plain_call(gpu_device):
+    """No lengths and no new token: the plain entry point's problem."""
+    inp = synth.make_layer(custom(B=4, index=104))
+    step = synth.make_step(inp.workload, inp)
+    out, lse, _, _ = run_gpu_ragged(inp, step, append=False, lengths=False)
+    ref, ref_lse = oracle_layer(inp)
+    assert_parity(out, ref, "bf16", "ragged, full lengths", lse, ref_lse)
+    plain, plain_lse = run_gpu(inp)
+    assert np.max(np.abs(plain - out)) < 1e-3
+
+
+@pytest.mark.parametrize("layer", [0, 6])  # ranks 48, 128
+def test_c3_ragged_sampled(layer, gpu_device):
+    """The 128K Llama step's shapes: beacons live from half to all of 8192,
+    raw rows from half to all of 2048 minus one, and the new token."""
+    wl = synth.get_workload("c3")
+    note(f"c3 ragged layer {layer}")
+    inp = synth.make_layer(wl, layer, device=gpu_device)
+    step = synth.make_step(wl, inp, device=gpu_device, beacons=(0.5, 1.0), raw=(0.5, 1.0),
+                           fixed={0: (8192, 2047), 1: (0, 0)})
+    out, lse, K, V = run_gpu_ragged(inp, step)
+    units = sample_units(wl, 12, seed=layer)
+    ref = oracle_ragged_units(inp, step, units)
+    got, got_lse = gather_units(out, lse, wl, units)
+    exp = np.stack([ref[u][0] for u in units])
+    exp_lse = np.stack([ref[u][1] for u in units])
+    assert_parity(got, exp, wl.dtype, f"c3 ragged L{layer}", got_lse, exp_lse)
+    k_app = {u: ref[u][2] for u in units}
+    assert_new_rows(K, V, inp.K_raw, inp.V_raw, step, k_app, units=units)
+    del inp, K, V
+    torch.cuda.empty_cache()
