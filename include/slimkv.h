@@ -177,11 +177,12 @@ slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q,
  * Other arguments as for slimkv_decode_attn.  N_cap + W_cap may be 0 (then
  * only the new token is attended).  The batch is at most 1024 sequences and
  * flags must be 0 (the tiles of the whole batch are shared out over the
- * grid in a fixed order, so repeated calls are bitwise equal).  num_splits
- * > 0 sets the number of workgroups of the launch (at most 64 per
- * (b, kv head)); 0 lets the library pick.  Workspace: slimkv_workspace_bytes
- * with SLIMKV_OP_LATENT_RAGGED, zero-filled before first use, as for the
- * other entry points.
+ * grid in a fixed order, so repeated calls are bitwise equal).  Work is
+ * shared out by tiles: each (b, kv head) gets workgroups in proportion to
+ * its live rows, shaped for P workgroup slots -- the device's (num_splits
+ * = 0) or num_splits -- with at most 64 per (b, kv head).  Workspace:
+ * slimkv_workspace_bytes with SLIMKV_OP_LATENT_RAGGED, zero-filled before
+ * first use, as for the other entry points.
  */
 slimkv_status slimkv_decode_attn_ragged(const slimkv_problem* problem,
                                         const void* q, const int32_t* q_pos,

@@ -131,7 +131,11 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
     sg->tile = tile_rows(pl.dtype, sg->rk, sg->rv);
   }
   a.unit_bytes = (int64_t)sb.rows * sb.row_bytes + (int64_t)sr.rows * sr.row_bytes;
-  a.chunks = p->num_splits > 0 ? std::min(p->num_splits, kMaxChunks) : 0;  // 0: launcher picks
+  // 0: the launcher picks; ragged calls read num_splits as the workgroup
+  // slots the pieces are shaped for (the launcher caps it), the others as
+  // workgroups per unit
+  a.chunks = p->num_splits <= 0 ? 0
+             : (op == SLIMKV_OP_LATENT_RAGGED ? p->num_splits : std::min(p->num_splits, kMaxChunks));
   a.deterministic = (p->flags & SLIMKV_FLAG_DYNAMIC_TILES) == 0;
   if (pl.units * kMaxChunks > (int64_t)INT32_MAX)
     return fail(SLIMKV_ERR_UNSUPPORTED, "too many workgroups");

@@ -194,9 +194,10 @@ struct alignas(16) AttnShared {
 // Rotation angle q_pos * theta^(-2i/d) for pair i < 64: the frequency is the
 // product of the host's theta^(-2 * 2^k / d) over i's set bits (a few fp64
 // roundings), the angle is formed and reduced into [-pi, pi] in fp64 with a
-// two-term 2*pi (each fma step exact up to one rounding), and only the sine
-// and cosine of the reduced angle are taken in fp32 (~2e-7 absolute).
-__device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, float& s, float& c) {
+// two-term 2*pi (each fma step exact up to one rounding).  For the query
+// only the sine and cosine of the reduced angle are taken in fp32 (~2e-7
+// absolute).
+__device__ __forceinline__ double rope_angle(const AttnArgs& a, int pos, int i) {
   double f = 1.0;
 #pragma unroll
   for (int k = 0; k < 6; ++k) f *= ((i >> k) & 1) ? a.inv_freq_pow2[k] : 1.0;
@@ -206,8 +207,10 @@ __device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, f
   constexpr double kInvTwoPi = 0.15915494309189534561;
   const double kk = rint(ang * kInvTwoPi);
   double r = fma(-kk, kTwoPiHi, ang);
-  r = fma(-kk, kTwoPiLo, r);
-  sincosf((float)r, &s, &c);
+  return fma(-kk, kTwoPiLo, r);
+}
+__device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, float& s, float& c) {
+  sincosf((float)rope_angle(a, pos, i), &s, &c);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,46 +945,162 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
         (float)(0.69314718055994530942 * ((double)M + log2((double)L)));
 }
 
+// A value of the storage dtype, rounded once from double to nearest (ties
+// to even), as storage bits: bf16 keeps 8 significant bits.
+template <bool BF16>
+__device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
+  if constexpr (BF16) {
+    if (x == 0.0 || !isfinite(x)) return __float_as_uint((float)x) >> 16;
+    int e;
+    const double m = frexp(x, &e);
+    const double r = ldexp(rint(ldexp(m, 8)), e - 8);  // exact in fp32
+    return __float_as_uint((float)r) >> 16;
+  } else {
+    return __float_as_uint((float)x);
+  }
+}
+
+// Merge for ragged calls (run by the unit's last workgroup): fold the unit's
+// nslots partials (slots slot0 ..) as merge_unit does, then the decode
+// step's new token as a one-row partial -- its key rotated at q_pos in fp64
+// and rounded once to the storage dtype, i.e. the row the cache keeps,
+// scored against the query rotated as in the prologue; write out and lse,
+// and store the token's row when the raw window has room (wlive < its
+// capacity).  Thread (g, c4) owns 16-byte column c4 of head g.  With no
+// rows at all the unit gets out 0 and lse -inf.
+template <int G, bool BF16>
+__device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, int h, int slot0,
+                                              int nslots, int wlive) {
+  const int tid = threadIdx.x;
+  if (tid >= G * kHeadDim / 4) return;
+  const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+  constexpr int kB = 8;
+  float M = -INFINITY, L = 0.0f;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (nslots > 0) {
+    const __amdgpu_buffer_rsrc_t rml =
+        coherent_rsrc(a.part_ml + (size_t)slot0 * G * 2, (uint32_t)(nslots * G * 2 * 4));
+    const __amdgpu_buffer_rsrc_t racc =
+        coherent_rsrc(a.part_acc + (size_t)slot0 * G * kHeadDim, (uint32_t)(nslots * G * kHeadDim * 4));
+    for (int s0 = 0; s0 < nslots; s0 += kB) {
+      uint32_t mlw[kB][2];
+      u32x4_t v[kB];
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        const int s = min(s0 + k, nslots - 1);
+        const int base = (s * G + g) * 8;
+        mlw[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rml, base, 0, kCoherent);
+        mlw[k][1] = __builtin_amdgcn_raw_buffer_load_b32(rml, base + 4, 0, kCoherent);
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(racc, ((s * G + g) * kHeadDim + 4 * c4) * 4, 0,
+                                                    kCoherent);
+      }
+#pragma unroll
+      for (int k = 0; k < kB; ++k) {
+        if (s0 + k < nslots) {
+          const float m = __uint_as_float(mlw[k][0]), l = __uint_as_float(mlw[k][1]);
+          const float mn = fmaxf(M, m);
+          if (mn != -INFINITY) {
+            const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(m - mn);
+            L = L * a1 + l * a2;
+            acc = acc * a1 + __builtin_bit_cast(f32x4_t, v[k]) * a2;
+            M = mn;
+          }
+        }
+      }
+    }
+  }
+  const size_t hq = (size_t)b * a.num_q_heads + (size_t)h * G + g;
+  if (a.k_new) {
+    // the new token: key rotated at q_pos in fp64 and rounded once to the
+    // storage dtype (the row the cache keeps), query rotated as in the
+    // prologue; the score is summed over the 32 threads of head g
+    const int pos = a.q_pos[b];
+    const size_t qb = hq * kHeadDim, kb = (size_t)u * kHeadDim;
+    float dot = 0.0f;
+    uint32_t kbits[4];
+    float vnew[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * c4 + e, pi = i & (kHeadDim / 2 - 1), ip = i ^ (kHeadDim / 2);
+      const bool lo = i < kHeadDim / 2;
+      float sn, cs;
+      rope_sincos(a, pos, pi, sn, cs);
+      const float qi = ld_elem<BF16>(a.q, qb + i), qp = ld_elem<BF16>(a.q, qb + ip);
+      const float qr = lo ? qi * cs - qp * sn : qi * cs + qp * sn;
+      double s64, c64;
+      sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
+      const double ki = (double)ld_elem<BF16>(a.k_new, kb + i), kp = (double)ld_elem<BF16>(a.k_new, kb + ip);
+      kbits[e] = storage_bits_from_f64<BF16>(lo ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
+      dot += qr * bits_to_float<BF16>(kbits[e]);
+      vnew[e] = ld_elem<BF16>(a.v_new, kb + i);
+    }
+    dot = xor16_sum(row16_sum(dot));  // the 32 lanes of head g
+    const float s2 = dot * (float)a.score_scale;
+    const float mn = fmaxf(M, s2);
+    const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(s2 - mn);
+    L = L * a1 + a2;
+    acc = acc * a1 + f32x4_t{vnew[0], vnew[1], vnew[2], vnew[3]} * a2;
+    M = mn;
+    if (g == 0 && wlive < a.seg[1].rows) {
+      const size_t row = ((size_t)u * a.seg[1].rows + wlive) * kHeadDim + 4 * c4;
+      if constexpr (BF16) {
+        uint32_t* kd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.k_store) + row);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.v_store) + row);
+        const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb + 4 * c4;
+        kd[0] = kbits[0] | (kbits[1] << 16);
+        kd[1] = kbits[2] | (kbits[3] << 16);
+        vd[0] = (uint32_t)vs[0] | ((uint32_t)vs[1] << 16);
+        vd[1] = (uint32_t)vs[2] | ((uint32_t)vs[3] << 16);
+      } else {
+        float* kd = static_cast<float*>(a.k_store) + row;
+        float* vd = static_cast<float*>(a.v_store) + row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kd[e] = __uint_as_float(kbits[e]);
+          vd[e] = vnew[e];
+        }
+      }
+    }
+  }
+  float* out = a.out + hq * kHeadDim + 4 * c4;
+  if (L > 0.0f) {
+    *reinterpret_cast<f32x4_t*>(out) = acc * (1.0f / L);
+    if (a.lse && c4 == 0) a.lse[hq] = (float)(0.69314718055994530942 * ((double)M + log2((double)L)));
+  } else {
+    *reinterpret_cast<f32x4_t*>(out) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.lse && c4 == 0) a.lse[hq] = -INFINITY;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Grid: `chunks` workgroups per (b, kv head) unit, numbered chunk-major
-// (block = c * units + (unit - c) mod units).  Workgroups are placed on the
-// CUs in block order, the older workgroups on a CU are served first, and
-// blocks are dealt to the XCDs in turn, whose speeds differ a little; so a
-// unit made of consecutive blocks, or of blocks on one XCD, would run at the
-// speed of its slot or its XCD.  This numbering gives every unit workgroups
-// of every age on different XCDs, so the units finish together.  Workgroup c
-// hosts the unit's waves 4c .. 4c+3.  The unit's tiles -- beacon tiles, then
-// raw tiles, all about the same size in bytes -- are handed out in order
-// (see TileFeed), so the waves of a unit advance through one sliding window
-// of rows; each wave keeps one tile in flight, across the segment boundary
-// too.  The workgroup writes one partial (slot c of the unit); the
-// workgroup that finishes last merges the unit.
+// The work of one workgroup: workgroup c of the k that share unit (b, h)'s
+// rows.  Workgroup c hosts the unit's waves 4c .. 4c+3.  The unit's tiles --
+// beacon tiles, then raw tiles, all about the same size in bytes -- are
+// handed out in order (see TileFeed), so the waves of a unit advance through
+// one sliding window of rows; each wave keeps one tile in flight, across the
+// segment boundary too.  The workgroup writes one partial (slot slot0 + c);
+// the workgroup that finishes last merges the unit.  nbr, wr: the unit's
+// live beacon and raw rows (the arrays hold a.seg[*].rows per unit).
+// RAGGED: the merge also takes in the decode step's new token (ragged_finish).
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
-template <int G, int NCH, bool BF16>
-__global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
+template <int G, int NCH, bool BF16, bool RAGGED>
+__device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, int unit, int b, int h,
+                                            int c, int k, int nbr, int wr, int slot0) {
   constexpr bool BLAT = NCH > 0;
   constexpr int kFullNch = BF16 ? 4 : 8;
   constexpr int BN = BLAT ? NCH : kFullNch;
-  __shared__ AttnShared sh;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int n = lane & 15, kg = lane >> 4;
-  const int k = a.chunks;
-  const int units = a.batch * a.num_kv_heads;
-  const int c = blockIdx.x / units;
-  // rotated by c, so that a unit's blocks sit on different XCDs
-  const int unit = (int)(((int64_t)blockIdx.x - (int64_t)c * units + c) % units);
-  const int b = unit / a.num_kv_heads;
-  const int h = unit - b * a.num_kv_heads;
   const int nwaves = kWaves * k;
   const int wu = kWaves * c + wave;  // this wave's number within the unit
 
   SegView<BN, BF16> bv;  // beacon rows
-  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, a.seg[0].rows, BLAT ? a.seg[0].rk : kHeadDim,
+  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, nbr, BLAT ? a.seg[0].rk : kHeadDim,
           BLAT ? a.seg[0].rv : kHeadDim, unit, lane);
   SegView<kFullNch, BF16> rw;  // raw rows
-  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, a.seg[1].rows, kHeadDim, kHeadDim, unit, lane);
+  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
   // tile positions: beacon tiles 0 .. nbt-1, then raw tiles; this wave's
   // first is wu, later ones round-robin or from the unit's counter
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
@@ -1044,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
                     // and with the query (whose space takes the merged sums)
   wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
   lds_barrier();
-  const size_t slot = (size_t)unit * k + c;
+  const size_t slot = (size_t)slot0 + c;
   wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw, a.part_ml + slot * G * 2,
                             a.part_acc + slot * G * kHeadDim);
 
@@ -1066,7 +1185,30 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   if (tid < 2)
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  merge_unit<G>(a, unit, b, h);
+  if constexpr (RAGGED)
+    ragged_finish<G, BF16>(a, unit, b, h, slot0, k, wr);
+  else
+    merge_unit<G>(a, unit, b, h);
+}
+
+// Grid: `chunks` workgroups per (b, kv head) unit, numbered chunk-major
+// (block = c * units + (unit - c) mod units).  Workgroups are placed on the
+// CUs in block order, the older workgroups on a CU are served first, and
+// blocks are dealt to the XCDs in turn, whose speeds differ a little; so a
+// unit made of consecutive blocks, or of blocks on one XCD, would run at the
+// speed of its slot or its XCD.  This numbering gives every unit workgroups
+// of every age on different XCDs, so the units finish together.
+template <int G, int NCH, bool BF16>
+__global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
+  const int k = a.chunks;
+  const int units = a.batch * a.num_kv_heads;
+  const int c = blockIdx.x / units;
+  // rotated by c, so that a unit's blocks sit on different XCDs
+  const int unit = (int)(((int64_t)blockIdx.x - (int64_t)c * units + c) % units);
+  const int b = unit / a.num_kv_heads;
+  const int h = unit - b * a.num_kv_heads;
+  attend_unit<G, NCH, BF16, false>(a, sh, unit, b, h, c, k, a.seg[0].rows, a.seg[1].rows, unit * k);
 }
 
 // Workgroup slots the grid fills on the current device: CUs x resident
