@@ -231,6 +231,10 @@ def main():
 
     if not args.no_compare:
         result["comparison"] = compare(lda, synth, torch, dev)
+        if args.workload == "c3":
+            result["comparison"]["c3_ragged_step"] = ragged_step(lda, synth, torch, dev, wl, layers,
+                                                                 args.steps)
+            result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
 
     del ws
     torch.cuda.empty_cache()
@@ -301,6 +305,93 @@ def compare(lda, synth, torch, dev):
         del x, ws
         torch.cuda.empty_cache()
         log(f"comparison {key}: {entry}")
+    return res
+
+
+def replay_ms(torch, step, steps):
+    """Capture ``step`` as one graph and time its replays (ms per step)."""
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    return time_calls(graph.replay, steps, 3, torch)
+
+
+def ragged_step(lda, synth, torch, dev, wl, layers, steps):
+    """The same 32-layer step as a serving step over a ragged batch: each
+    sequence keeps a seeded number of live beacons (4096..8192) and raw rows
+    (1024..2047) in the arrays, and every layer attends and stores the step's
+    new token (slimkv_decode_attn_ragged).  Bytes: the live rows, the new
+    token's key and value read and written, q, the bases, out and lse."""
+    elem = wl.elem_bytes
+    first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
+    steps_in, probs, bytes_step = [], [], 0
+    nb = first.num_beacons.cpu().numpy().clip(0, wl.num_beacons)
+    rw = first.raw_len.cpu().numpy().clip(0, wl.raw_window)
+    for layer, x in enumerate(layers):
+        st = synth.make_step(wl, x, device=dev)
+        st.num_beacons, st.raw_len = first.num_beacons, first.raw_len  # lengths are per sequence
+        steps_in.append(st)
+        probs.append(lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                              rope_theta=wl.rope_theta,
+                                              num_kv_heads=wl.num_kv_heads, scale=wl.scale))
+        r = wl.ranks[layer]
+        rows = wl.num_kv_heads * (int(nb.sum()) * 2 * r + int(rw.sum()) * 2 * wl.head_dim)
+        new_tok = wl.batch * wl.num_kv_heads * wl.head_dim * 2 * 2  # k, v read and stored
+        bytes_step += ((rows + new_tok) * elem + wl.num_kv_heads * wl.head_dim * 2 * r * elem
+                       + wl.batch * wl.num_q_heads * wl.head_dim * elem
+                       + wl.batch * wl.num_q_heads * (wl.head_dim + 1) * 4)
+    ws = torch.zeros(max(lda.slimkv_workspace_bytes(p, lda.SLIMKV_OP_LATENT_RAGGED) for p in probs),
+                     dtype=torch.uint8, device=dev)
+    out, lse = lda.alloc_outputs(probs[0], dev)
+
+    def step():
+        for p, x, st in zip(probs, layers, steps_in):
+            lda.slimkv_decode_attn_ragged(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
+                                          x.V_raw, st.num_beacons, st.raw_len, st.k_new,
+                                          st.v_new, out, lse, ws)
+
+    ms = replay_ms(torch, step, steps)
+    gbps = bytes_step / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
+           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
+                        f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + new token"}
+    log(f"ragged step: {res}")
+    del ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def other_step(lda, synth, torch, dev, name, steps):
+    """Another workload's full decode step (every layer), replayed as a graph."""
+    wl = synth.get_workload(name)
+    elem = wl.elem_bytes
+    log(f"{name}: generating {wl.layers} layers")
+    layers = [synth.make_layer(wl, layer, device=dev) for layer in range(wl.layers)]
+    probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                      rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                      scale=wl.scale) for x in layers]
+    ws = torch.zeros(max(lda.slimkv_workspace_bytes(p, lda.SLIMKV_OP_LATENT) for p in probs),
+                     dtype=torch.uint8, device=dev)
+    out, lse = lda.alloc_outputs(probs[0], dev)
+
+    def step():
+        for p, x in zip(probs, layers):
+            lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw,
+                                   out, lse, ws)
+
+    ms = replay_ms(torch, step, steps)
+    total = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
+    gbps = total / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
+           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    log(f"{name} step: {res}")
+    del layers, ws
+    torch.cuda.empty_cache()
     return res
 
 
