@@ -51,6 +51,9 @@ def parse_args():
     ap.add_argument("--eager", action="store_true",
                     help="launch each step's calls directly instead of replaying the step as one "
                          "captured HIP graph")
+    ap.add_argument("--ragged", action="store_true",
+                    help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
+                         "of the capacities, new token stored) and print its figures as one JSON line")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
                          "reduction, for scaling hardware byte counters and as a read ceiling")
@@ -128,6 +131,9 @@ def main():
     elem = wl.elem_bytes
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, generating inputs on the GPU")
     layers = [synth.make_layer(wl, layer, device=dev) for layer in range(wl.layers)]
+    if args.ragged:
+        print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps)), flush=True)
+        return
     probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
                                       rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
                                       scale=wl.scale) for x in layers]
