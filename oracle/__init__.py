@@ -69,10 +69,16 @@ def load(path=LIBRARY) -> ctypes.CDLL:
         lib.slimkv_oracle_decode.restype = ctypes.c_int
         lib.slimkv_oracle_decode.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 8 + [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
-        lib.slimkv_oracle_decode_ragged.restype = ctypes.c_int
-        lib.slimkv_oracle_decode_ragged.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 12 + [
-            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_int]
+        if hasattr(lib, "slimkv_oracle_decode_beacon_rope"):
+            lib.slimkv_oracle_decode_beacon_rope.restype = ctypes.c_int
+            lib.slimkv_oracle_decode_beacon_rope.argtypes = [ctypes.POINTER(_Problem)] + [
+                ctypes.c_void_p] * 9 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "slimkv_oracle_decode_ragged"):
+            lib.slimkv_oracle_decode_ragged.restype = ctypes.c_int
+            lib.slimkv_oracle_decode_ragged.argtypes = [ctypes.POINTER(_Problem)] + [
+                ctypes.c_void_p] * 12 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.slimkv_oracle_max_threads.restype = ctypes.c_int
         _lib_cache[key] = lib
     return _lib_cache[key]
@@ -92,7 +98,8 @@ def _arr(x, dtype):
 
 
 def decode(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, scale: float,
-           rope_theta: float, units=None, threads: int = 0, library: pathlib.Path = LIBRARY):
+           rope_theta: float, units=None, threads: int = 0, library: pathlib.Path = LIBRARY,
+           beacon_pos=None):
     """fp64 latent decode attention.
 
     Arrays are numpy, row-major, all in one storage dtype (float64, float32,
@@ -104,6 +111,9 @@ def decode(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, sca
     ``units`` is an optional list of (b, kv_head) pairs to compute; other
     rows of the result stay NaN.  Returns (out [B, H_q, d], lse [B, H_q]) in
     float64; lse is in natural-log units of the scaled scores.
+    ``beacon_pos`` ([N_b] int32) selects the reconstruction variant that keeps
+    beacon-key rotation: beacon j's key is rebuilt as U_K C_K[j] and rotated
+    at beacon_pos[j] before it is scored.
     """
     q = np.ascontiguousarray(q)
     dt = q.dtype
@@ -129,9 +139,16 @@ def decode(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, sca
     def ptr(a):
         return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
-    rc = load(library).slimkv_oracle_decode(
-        ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
-        ptr(K_raw), ptr(V_raw), ptr(unit_arr), n_units, ptr(out), ptr(lse), int(threads))
+    if beacon_pos is None:
+        rc = load(library).slimkv_oracle_decode(
+            ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+            ptr(K_raw), ptr(V_raw), ptr(unit_arr), n_units, ptr(out), ptr(lse), int(threads))
+    else:
+        bp = _arr(beacon_pos, np.dtype(np.int32))
+        rc = load(library).slimkv_oracle_decode_beacon_rope(
+            ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+            ptr(K_raw), ptr(V_raw), ptr(bp), ptr(unit_arr), n_units, ptr(out), ptr(lse),
+            int(threads))
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return out, lse

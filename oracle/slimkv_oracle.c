@@ -94,6 +94,12 @@ static double widen(const void* base, int dtype, size_t i) {
  * and k_app (if given) receives that rounded key.  A sequence with no rows
  * at all gets out = 0 and lse = -inf.  With nb_len = raw_len = NULL and no
  * new token this is the plain call: every capacity row is live.
+ *
+ * bpos (the reconstruction variant that keeps beacon-key rotation): beacon
+ * j's key is rebuilt at full dimension, U_K C_K[j], and rotated at position
+ * bpos[j] before it is scored against the rotated query; values are as in
+ * the latent path (sum_j a_j U_V C_V[j] = U_V sum_j a_j C_V[j]).  NULL: the
+ * latent scores of step 3.
  */
 
 /* Round to the storage precision, to nearest with ties to even. */
@@ -111,8 +117,8 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
                         const void* C_K, const void* C_V, const void* K_raw,
                         const void* V_raw, const int32_t* nb_len,
                         const int32_t* raw_len, const void* k_new,
-                        const void* v_new, double* out, double* lse,
-                        double* k_app, double* work) {
+                        const void* v_new, const int32_t* bpos, double* out,
+                        double* lse, double* k_app, double* work) {
   const int d = p->head_dim, half = p->head_dim / 2;
   const int G = p->num_q_heads / p->num_kv_heads;
   const int ncap = p->num_beacons, wcap = p->raw_window;
@@ -130,6 +136,7 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
   double* s = qh + rk;        /* [n]   scores, then weights   */
   double* olat = s + n;       /* [rv]  latent value sum       */
   double* oraw = olat + rv;   /* [d]   raw value sum          */
+  double* kb = oraw + d;      /* [d]   rebuilt beacon key (bpos) */
 
   const size_t unit = (size_t)b * p->num_kv_heads + h;
   const size_t ck0 = unit * (size_t)ncap * rk, cv0 = unit * (size_t)ncap * rv;
@@ -176,9 +183,26 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
     }
 
     /* 3. scores: live latent beacons, live rotated raw keys, the new token */
-    for (int j = 0; j < nb; ++j) {
+    for (int j = 0; j < nb && !bpos; ++j) {
       double acc = 0.0;
       for (int k = 0; k < rk; ++k) acc += qh[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+      s[j] = p->scale * acc;
+    }
+    for (int j = 0; j < nb && bpos; ++j) {
+      /* the reconstruction variant: rebuild the key, rotate it at bpos[j] */
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < rk; ++k)
+          acc += widen(U_K, dt, uk0 + (size_t)i * rk + k) * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+        kb[i] = acc;
+      }
+      double acc = 0.0;
+      for (int i = 0; i < half; ++i) {
+        double inv_freq = pow(p->rope_theta, -2.0 * (double)i / (double)d);
+        double ang = (double)bpos[j] * inv_freq;
+        double c = cos(ang), sn = sin(ang);
+        acc += qr[i] * (kb[i] * c - kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c + kb[i] * sn);
+      }
       s[j] = p->scale * acc;
     }
     for (int t = 0; t < w; ++t) {
@@ -227,12 +251,11 @@ static void oracle_unit(const oracle_problem* p, int b, int h, const void* q,
  * out: [B, H_q, d] doubles, lse: [B, H_q] doubles or NULL; entries of units
  * not listed are left untouched.  threads <= 0 uses the OpenMP default.
  */
-int slimkv_oracle_decode(const oracle_problem* p, const void* q,
-                         const int32_t* q_pos, const void* U_K,
-                         const void* U_V, const void* C_K, const void* C_V,
-                         const void* K_raw, const void* V_raw,
-                         const int32_t* units, int64_t n_units, double* out,
-                         double* lse, int threads) {
+static int decode_units(const oracle_problem* p, const void* q, const int32_t* q_pos,
+                        const void* U_K, const void* U_V, const void* C_K, const void* C_V,
+                        const void* K_raw, const void* V_raw, const int32_t* bpos,
+                        const int32_t* units, int64_t n_units, double* out, double* lse,
+                        int threads) {
   if (!p || !q || !q_pos || !out) return ORACLE_BAD_SHAPE;
   if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
     return ORACLE_BAD_DTYPE;
@@ -250,7 +273,7 @@ int slimkv_oracle_decode(const oracle_problem* p, const void* q,
   const int rk = p->num_beacons > 0 ? p->rank_k : 0;
   const int rv = p->num_beacons > 0 ? p->rank_v : 0;
   const size_t work_len =
-      3 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
+      4 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
   oracle_problem pp = *p;
   pp.rank_k = rk;
   pp.rank_v = rv;
@@ -279,13 +302,43 @@ int slimkv_oracle_decode(const oracle_problem* p, const void* q,
         continue;
       }
       oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, NULL, NULL, NULL, NULL,
-                  out, lse, NULL, work);
+                  bpos, out, lse, NULL, work);
     }
     free(work);
   }
   if (failed == 1) return ORACLE_NO_MEMORY;
   if (failed == 2) return ORACLE_BAD_SHAPE;
   return ORACLE_OK;
+}
+
+int slimkv_oracle_decode(const oracle_problem* p, const void* q,
+                         const int32_t* q_pos, const void* U_K,
+                         const void* U_V, const void* C_K, const void* C_V,
+                         const void* K_raw, const void* V_raw,
+                         const int32_t* units, int64_t n_units, double* out,
+                         double* lse, int threads) {
+  return decode_units(p, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, NULL, units, n_units, out,
+                      lse, threads);
+}
+
+/*
+ * The reconstruction variant that keeps beacon-key rotation (page "Can
+ * SlimKV compress KV cache jointly across tokens and features", section
+ * "Speedups are real, but memory is set by the ratio"): as
+ * slimkv_oracle_decode, but beacon j's key is rebuilt as U_K C_K[j] and
+ * rotated at bpos[j] ([N_b] int32, the same for every sequence) before it
+ * is scored.
+ */
+int slimkv_oracle_decode_beacon_rope(const oracle_problem* p, const void* q,
+                                     const int32_t* q_pos, const void* U_K,
+                                     const void* U_V, const void* C_K,
+                                     const void* C_V, const void* K_raw,
+                                     const void* V_raw, const int32_t* bpos,
+                                     const int32_t* units, int64_t n_units,
+                                     double* out, double* lse, int threads) {
+  if (p && p->num_beacons > 0 && !bpos) return ORACLE_BAD_SHAPE;
+  return decode_units(p, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, bpos, units, n_units, out,
+                      lse, threads);
 }
 
 /*
@@ -319,7 +372,7 @@ int slimkv_oracle_decode_ragged(const oracle_problem* p, const void* q,
   const int rk = p->num_beacons > 0 ? p->rank_k : 0;
   const int rv = p->num_beacons > 0 ? p->rank_v : 0;
   const size_t work_len =
-      3 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
+      4 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window + 1;
   oracle_problem pp = *p;
   pp.rank_k = rk;
   pp.rank_v = rv;
@@ -348,7 +401,7 @@ int slimkv_oracle_decode_ragged(const oracle_problem* p, const void* q,
         continue;
       }
       oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b, raw_len,
-                  k_new, v_new, out, lse, k_app, work);
+                  k_new, v_new, NULL, out, lse, k_app, work);
     }
     free(work);
   }

@@ -73,7 +73,7 @@ def random_problem(seed, *, B=1, Hkv=1, G=4, d=16, nb=5, rk=4, rv=6, w=3, theta=
     )
 
 
-def run_oracle(p, library, **over):
+def run_oracle(p, library, beacon_pos=None, **over):
     args = dict(p)
     args.update(over)
     nb = args["C_K"].shape[2]
@@ -83,7 +83,7 @@ def run_oracle(p, library, **over):
         args["C_K"] if nb else None, args["C_V"] if nb else None,
         args["K_raw"] if w else None, args["V_raw"] if w else None,
         num_kv_heads=args["num_kv_heads"], scale=args["scale"], rope_theta=args["theta"],
-        library=library)
+        library=library, beacon_pos=beacon_pos)
 
 
 def sdpa_reference(q_rot, K, V, scale, G):
@@ -392,6 +392,63 @@ def pin_append_rounding(library):
     assert np.array_equal(k_app, bf16_round(rot)), "new key not rounded once to bf16"
 
 
+# ---------------------------------------------------------------------------
+# The reconstruction variant that keeps beacon-key rotation (oracle.decode
+# with beacon_pos): rebuilt beacon keys are rotated at their positions.
+
+
+def beacon_rope_reference(p, beacon_pos):
+    """Independent statement: rebuild C_K U_K^T and C_V U_V^T, rotate the
+    rebuilt keys at their positions (complex multiplication), append the raw
+    rows, and run torch's SDPA with the rotated query."""
+    G = p["q"].shape[1] // p["num_kv_heads"]
+    q_rot = rope_complex(p["q"], p["q_pos"][:, None], p["theta"])
+    kb = np.einsum("bhjr,hdr->bhjd", p["C_K"], p["U_K"])
+    kb = rope_complex(kb, np.asarray(beacon_pos)[None, None, :], p["theta"])
+    vb = np.einsum("bhjr,hdr->bhjd", p["C_V"], p["U_V"])
+    K = np.concatenate([kb, p["K_raw"]], axis=2)
+    V = np.concatenate([vb, p["V_raw"]], axis=2)
+    return sdpa_reference(q_rot, K, V, p["scale"], G)
+
+
+def pin_beacon_rope_reference(library):
+    for seed, shape in ((60, dict(B=2, Hkv=2, G=4, d=16, nb=17, rk=4, rv=8, w=3)),
+                        (61, dict(B=1, Hkv=2, G=5, d=128, nb=33, rk=32, rv=48, w=9, theta=500000.0,
+                                  q_pos=131071))):
+        p = random_problem(seed, **shape)
+        ratio = 16
+        bpos = ((np.arange(shape["nb"]) + 1) * ratio - 1).astype(np.int32)
+        out, lse = run_oracle(p, library, beacon_pos=bpos)
+        ref_out, ref_lse = beacon_rope_reference(p, bpos)
+        _close(out, ref_out, tol=1e-10, what=f"beacon-rope out {shape}")
+        _close(lse, ref_lse, tol=1e-10, what=f"beacon-rope lse {shape}")
+
+
+def pin_beacon_rope_relative(library):
+    """Beacons at the query position turn with the query, so (no raw rows)
+    the scores are those of the unrotated query against the unrotated keys:
+    the latent path with the query at position 0.  Shifting the query, the
+    beacons and the raw keys together leaves the output unchanged; moving
+    only the beacons changes it."""
+    pb = random_problem(63, B=2, Hkv=1, G=4, d=32, nb=9, rk=8, rv=8, w=0, q_pos=777)
+    out, lse = run_oracle(pb, library, beacon_pos=np.full(9, 777, dtype=np.int32))
+    lat, lat_lse = run_oracle(pb, library, q_pos=np.zeros(2, dtype=np.int32))
+    _close(out, lat, tol=1e-11, what="beacons at the query position")
+    _close(lse, lat_lse, tol=1e-11, what="beacons at the query position, lse")
+    p = random_problem(62, B=2, Hkv=1, G=4, d=32, nb=9, rk=8, rv=8, w=5, q_pos=777)
+    bpos = (np.arange(9) * 50 + 3).astype(np.int32)
+    out0, _ = run_oracle(p, library, beacon_pos=bpos)
+    shift = 100000
+    qp = p["q_pos"] + shift
+    raw_pos = qp[:, None] - 5 + 1 + np.arange(5)[None, :]
+    k = rope_complex(p["K_pre"], raw_pos[:, None, :], p["theta"])
+    out1, _ = run_oracle(p, library, q_pos=qp.astype(np.int32), K_raw=k,
+                         beacon_pos=(bpos + shift).astype(np.int32))
+    _close(out1, out0, tol=1e-9, what="beacon-rope shift")
+    out2, _ = run_oracle(p, library, beacon_pos=(bpos + 7).astype(np.int32))
+    assert np.max(np.abs(out2 - out0)) > 1e-6, "beacon positions have no effect"
+
+
 ALL_PINS = [
     pin_reconstruct_identity,
     pin_raw_only_rope_gqa,
@@ -406,4 +463,6 @@ ALL_PINS = [
     pin_append_token,
     pin_append_self_score,
     pin_append_rounding,
+    pin_beacon_rope_reference,
+    pin_beacon_rope_relative,
 ]

@@ -41,6 +41,11 @@ MUTANTS = {
                                         "const size_t kr0 = unit * (size_t)w * d;"),
     "beacon_rows_not_clamped": ("nb = nb < 0 ? 0 : (nb > ncap ? ncap : nb);", "nb = nb < 0 ? 0 : nb;"),
     "bf16_rounding_truncates": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
+    "beacon_key_unrotated": ("acc += qr[i] * (kb[i] * c - kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c + kb[i] * sn);",
+                             "acc += qr[i] * kb[i] + qr[i + half] * kb[i + half];"),
+    "beacon_key_rotated_backwards": ("acc += qr[i] * (kb[i] * c - kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c + kb[i] * sn);",
+                                     "acc += qr[i] * (kb[i] * c + kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c - kb[i] * sn);"),
+    "beacon_key_at_query_position": ("double ang = (double)bpos[j] * inv_freq;", "double ang = (double)q_pos[b] * inv_freq;"),
     "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
                                "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
