@@ -18,8 +18,9 @@ Reported beside the headline tokens/s:
   * roofline of the sweep kernel (algorithmic cache bytes per launch over
     its average launch time, against 8 TB/s);
   * the comparison at 128K on one layer: latent path at 16x vs the
-    reconstruct-then-attend path on the same beacons and vs uncompressed
-    full-KV attention over all 131072 tokens;
+    reconstruct-then-attend paths on the same beacons (without and with the
+    rotation of rebuilt beacon keys) and vs uncompressed full-KV attention
+    over all 131072 tokens; the ragged serving step; the 48-layer Qwen step;
   * the fp64 CPU oracle timed on a bounded sample on this host's cores.
 """
 
@@ -306,6 +307,16 @@ def compare(lda, synth, torch, dev):
                 10, 3, torch)
             entry["reconstruct_us"] = round(tr * 1e3, 1)
             entry["speedup_vs_reconstruct"] = round(tr / t, 2)
+            # the variant the page times: rebuilt beacon keys rotated at their
+            # positions (one beacon per s tokens, at the end of its span)
+            s_tok = wl.context // wl.num_beacons
+            bpos = ((torch.arange(wl.num_beacons, device=dev, dtype=torch.int64) + 1) * s_tok
+                    - 1).to(torch.int32)
+            trr = time_calls(lambda: lda.slimkv_reconstruct_rope_attn(
+                p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw, bpos, out, lse,
+                wsr), 10, 3, torch)
+            entry["reconstruct_rope_us"] = round(trr * 1e3, 1)
+            entry["speedup_vs_reconstruct_rope"] = round(trr / t, 2)
             del wsr
         res[key] = entry
         del x, ws

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 3
+#define SLIMKV_ABI_VERSION 4
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -213,6 +213,33 @@ slimkv_status slimkv_reconstruct_attn(const slimkv_problem* problem,
                                       const void* K_raw, const void* V_raw,
                                       float* out, float* lse, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * slimkv_reconstruct_rope_attn -- the reconstruction variant exactly as the
+ * same section times it: it keeps the rotation of beacon keys.  Beacon keys
+ * and values are rebuilt at full dimension into the workspace as in
+ * slimkv_reconstruct_attn, but each rebuilt key K_b[j] = U_K C_K[j] is
+ * rotated at position beacon_pos[j] (rotate-half pairs, angle
+ * beacon_pos[j] * theta^(-2i/d)) before it is rounded to the dtype; the
+ * rotated query then attends over the rebuilt and raw rows.  This is not
+ * the latent result (SlimKV's beacon keys carry no rotation); it is the
+ * baseline the SlimKV timings are compared with.
+ *
+ *   beacon_pos [N_b] int32 (device)  position of beacon j, the same for
+ *                                     every sequence (e.g. (j + 1) * s - 1
+ *                                     for one beacon per s tokens); may be
+ *                                     NULL when N_b == 0
+ * Other arguments, layouts and the workspace (slimkv_workspace_bytes with
+ * SLIMKV_OP_RECONSTRUCT) as for slimkv_reconstruct_attn.
+ */
+slimkv_status slimkv_reconstruct_rope_attn(const slimkv_problem* problem,
+                                           const void* q, const int32_t* q_pos,
+                                           const void* U_K, const void* U_V,
+                                           const void* C_K, const void* C_V,
+                                           const void* K_raw, const void* V_raw,
+                                           const int32_t* beacon_pos, float* out,
+                                           float* lse, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /*
  * full_kv_attn -- comparison path: uncompressed grouped-query decode

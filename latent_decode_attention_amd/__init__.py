@@ -11,7 +11,7 @@ from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # no
                       SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn, load_library,
                       make_problem, slimkv_abi_version, slimkv_decode_attn,
                       slimkv_decode_attn_ragged, slimkv_last_error, slimkv_problem,
-                      slimkv_reconstruct_attn,
+                      slimkv_reconstruct_attn, slimkv_reconstruct_rope_attn,
                       slimkv_set_kernel_events, slimkv_status_string,
                       slimkv_workspace_bytes)
 from .helpers import alloc_outputs, alloc_workspace, problem_from_tensors  # noqa: F401

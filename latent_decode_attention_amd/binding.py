@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
-           "slimkv_reconstruct_attn", "full_kv_attn", "slimkv_set_kernel_events",
+           "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
+           "slimkv_set_kernel_events",
            "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
 
 
@@ -80,6 +81,8 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_decode_attn_ragged.restype = ctypes.c_int
     lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_reconstruct_attn.restype = ctypes.c_int
+    lib.slimkv_reconstruct_rope_attn.argtypes = [prob] + [vp] * 11 + [vp, sz, vp]
+    lib.slimkv_reconstruct_rope_attn.restype = ctypes.c_int
     lib.full_kv_attn.argtypes = [prob] + [vp] * 6 + [vp, sz, vp]
     lib.full_kv_attn.restype = ctypes.c_int
     lib.slimkv_status_string.argtypes = [ctypes.c_int]
@@ -162,6 +165,16 @@ def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
         ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
         _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def slimkv_reconstruct_rope_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                                 beacon_pos, out, lse, workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_reconstruct_rope_attn(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(beacon_pos), _ptr(out), _ptr(lse), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def full_kv_attn(problem, q, q_pos, K, V, out, lse, workspace, stream=None) -> None:

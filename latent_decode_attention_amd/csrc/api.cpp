@@ -208,7 +208,7 @@ slimkv_status check_pointers(const Range* in, int n_in, const Range* req, int n_
 slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const int32_t* q_pos,
                   const void* U_K, const void* U_V, const void* C_K, const void* C_V,
                   const void* K_raw, const void* V_raw, float* out, float* lse, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  size_t ws_bytes, void* stream, const int32_t* beacon_pos = nullptr) {
   Plan pl;
   slimkv_status st = make_plan(p, op, pl);
   if (st != SLIMKV_OK) return st;
@@ -252,6 +252,12 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   if (st != SLIMKV_OK) return st;
   if (overlap(outs[0], in[1]) || overlap(outs[1], in[1]) || overlap(outs[2], in[1]))
     return fail(SLIMKV_ERR_ALIAS, "an output overlaps q_pos");
+  if (beacon_pos) {
+    const Range bp{beacon_pos, nb * sizeof(int32_t), "beacon_pos"};
+    if ((uintptr_t)beacon_pos % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "beacon_pos is not 4-byte aligned");
+    for (const Range& o : outs)
+      if (overlap(o, bp)) return fail(SLIMKV_ERR_ALIAS, "%s overlaps beacon_pos", o.name);
+  }
   if (!ws) return fail(SLIMKV_ERR_NULL, "workspace is NULL");
   if ((uintptr_t)ws % 16 != 0) return fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (ws_bytes < pl.total)
@@ -292,12 +298,15 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     rb.U = U_K;
     rb.dst = wsb + pl.off_kb;
     rb.rank = (int32_t)rk;
+    rb.pos = beacon_pos;  // keys only
+    for (int k = 0; k < 6; ++k) rb.inv_freq_pow2[k] = a.inv_freq_pow2[k];
     err = launch_rebuild(rb, pl.dtype, s);
     if (err == hipSuccess) {
       rb.C = C_V;
       rb.U = U_V;
       rb.dst = wsb + pl.off_vb;
       rb.rank = (int32_t)rv;
+      rb.pos = nullptr;
       err = launch_rebuild(rb, pl.dtype, s);
     }
   }
@@ -443,6 +452,18 @@ slimkv_status slimkv_reconstruct_attn(const slimkv_problem* problem, const void*
                                       size_t workspace_bytes, void* stream) {
   return slimkv::run(problem, SLIMKV_OP_RECONSTRUCT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
                      out, lse, workspace, workspace_bytes, stream);
+}
+
+slimkv_status slimkv_reconstruct_rope_attn(const slimkv_problem* problem, const void* q,
+                                           const int32_t* q_pos, const void* U_K, const void* U_V,
+                                           const void* C_K, const void* C_V, const void* K_raw,
+                                           const void* V_raw, const int32_t* beacon_pos, float* out,
+                                           float* lse, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (problem && problem->num_beacons > 0 && !beacon_pos)
+    return slimkv::fail(SLIMKV_ERR_NULL, "beacon_pos is NULL");
+  return slimkv::run(problem, SLIMKV_OP_RECONSTRUCT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                     out, lse, workspace, workspace_bytes, stream, beacon_pos);
 }
 
 slimkv_status full_kv_attn(const slimkv_problem* problem, const void* q, const int32_t* q_pos,

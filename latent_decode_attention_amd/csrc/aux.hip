@@ -16,10 +16,30 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Rebuild (reconstruction comparison path only): dst = C U^T per unit, i.e.
+// Rebuild (reconstruction comparison paths only): dst = C U^T per unit, i.e.
 // the full-dimension beacon keys or values the latent path never forms,
-// rounded to the storage dtype.  bf16: one wave per 16 rows, MFMA
-// 16x16x32 over 8 column tiles, staged through LDS for 16-byte stores.
+// rounded to the storage dtype.  With a.pos (the variant that keeps
+// beacon-key rotation, page "Can SlimKV compress KV cache jointly across
+// tokens and features", section "Speedups are real, but memory is set by
+// the ratio") row j is rotated at position pos[j] -- rotate-half pairs
+// (i, i + d/2), angle pos * theta^(-2i/d) formed and reduced mod 2*pi in
+// fp64, sine and cosine in fp32 -- before it is rounded.  bf16: one wave
+// per 16 rows, MFMA 16x16x32 over 8 column tiles, staged through LDS in
+// fp32 for 16-byte stores.
+
+// Sine and cosine of pos * theta^(-2i/d) for pair i < 64 (see above).
+__device__ __forceinline__ void rebuild_sincos(const RebuildArgs& a, int pos, int i, float& s,
+                                               float& c) {
+  double f = 1.0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) f *= ((i >> k) & 1) ? a.inv_freq_pow2[k] : 1.0;
+  const double ang = (double)pos * f;
+  constexpr double kTwoPiHi = 6.283185307179586232;
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;
+  const double kk = rint(ang * 0.15915494309189534561);
+  const double r = fma(-kk, kTwoPiLo, fma(-kk, kTwoPiHi, ang));
+  sincosf((float)r, &s, &c);
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   uint32_t u = __float_as_uint(x);
   u += 0x7fffu + ((u >> 16) & 1u);
@@ -27,8 +47,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 }
 
 __global__ __launch_bounds__(kThreads) void rebuild_bf16_kernel(RebuildArgs a) {
-  constexpr int kPitch = kHeadDim + 8;  // bf16 elements per LDS row
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kWaves][16][kPitch];
+  constexpr int kPitch = kHeadDim + 4;  // fp32 elements per LDS row
+  __shared__ __attribute__((aligned(16))) float tile[kWaves][16][kPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
   const int nblk = (a.num_beacons + 63) / 64;
@@ -64,18 +84,46 @@ __global__ __launch_bounds__(kThreads) void rebuild_bf16_kernel(RebuildArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[wave][4 * kg + e][nt * 16 + n] = f32_to_bf16(d[e]);
+    for (int e = 0; e < 4; ++e) tile[wave][4 * kg + e][nt * 16 + n] = d[e];
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // each lane writes 8 columns of both halves of a row, i.e. the 8 rotation
+  // pairs (i, i + d/2) of one row, whose angles it computes once
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int idx = lane + 64 * j;
-    const int row = idx >> 4, seg = idx & 15;
-    if (row0 + row < a.num_beacons)
-      *reinterpret_cast<u32x4_t*>(D + (size_t)(row0 + row) * kHeadDim + seg * 8) =
-          *reinterpret_cast<const u32x4_t*>(&tile[wave][row][seg * 8]);
+    const int row = idx >> 3, seg = idx & 7;
+    if (row0 + row < a.num_beacons) {
+      const float* t = &tile[wave][row][0];
+      float lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lo[e] = t[seg * 8 + e];
+        hi[e] = t[seg * 8 + e + kHeadDim / 2];
+      }
+      if (a.pos) {
+        const int p = a.pos[row0 + row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float sn, cs;
+          rebuild_sincos(a, p, seg * 8 + e, sn, cs);
+          const float x = lo[e], y = hi[e];
+          lo[e] = x * cs - y * sn;
+          hi[e] = y * cs + x * sn;
+        }
+      }
+      u32x4_t wl, wh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wl[e] = (uint32_t)f32_to_bf16(lo[2 * e]) | ((uint32_t)f32_to_bf16(lo[2 * e + 1]) << 16);
+        wh[e] = (uint32_t)f32_to_bf16(hi[2 * e]) | ((uint32_t)f32_to_bf16(hi[2 * e + 1]) << 16);
+      }
+      uint16_t* dst = D + (size_t)(row0 + row) * kHeadDim + seg * 8;
+      *reinterpret_cast<u32x4_t*>(dst) = wl;
+      *reinterpret_cast<u32x4_t*>(dst + kHeadDim / 2) = wh;
+    }
   }
 }
 
@@ -92,6 +140,16 @@ __global__ __launch_bounds__(kThreads) void rebuild_f32_kernel(RebuildArgs a) {
   const float* U = static_cast<const float*>(a.U) + ((size_t)h * kHeadDim + col) * r;
   float acc = 0.0f;
   for (int k = 0; k < r; ++k) acc = fmaf(C[k], U[k], acc);
+  if (a.pos) {
+    // the partner column i +- d/2 of the same row, rebuilt the same way
+    const int pc = col ^ (kHeadDim / 2);
+    const float* Up = static_cast<const float*>(a.U) + ((size_t)h * kHeadDim + pc) * r;
+    float pacc = 0.0f;
+    for (int k = 0; k < r; ++k) pacc = fmaf(C[k], Up[k], pacc);
+    float sn, cs;
+    rebuild_sincos(a, a.pos[row % a.num_beacons], col & (kHeadDim / 2 - 1), sn, cs);
+    acc = col < kHeadDim / 2 ? acc * cs - pacc * sn : acc * cs + pacc * sn;
+  }
   static_cast<float*>(a.dst)[idx] = acc;
 }
 

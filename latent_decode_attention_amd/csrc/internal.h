@@ -74,6 +74,8 @@ struct RebuildArgs {
   const void* U;  // [H_kv, d, r]
   void* dst;      // [B, H_kv, N_b, d]
   int32_t batch, num_kv_heads, num_beacons, rank;
+  const int32_t* pos;       // [N_b]: rotate row j at pos[j] before rounding (keys), or null
+  double inv_freq_pow2[6];  // theta^(-2 * 2^k / d), as in AttnArgs (with pos)
 };
 
 // Host launchers (defined in the .hip files).  dtype: 0 fp32, 1 bf16.

@@ -37,8 +37,11 @@ def note(msg: str) -> None:
 
 
 def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_splits: int = 0,
-            device="cuda", with_lse: bool = True, full_k=None, full_v=None, flags: int = 0):
-    """Run one entry point on ``inp`` (moved to the GPU if needed)."""
+            device="cuda", with_lse: bool = True, full_k=None, full_v=None, flags: int = 0,
+            beacon_pos=None):
+    """Run one entry point on ``inp`` (moved to the GPU if needed).  With
+    op = RECONSTRUCT and beacon_pos ([N_b] int32), the variant that rotates
+    the rebuilt beacon keys (slimkv_reconstruct_rope_attn)."""
     wl = inp.workload
     g = inp.to(device)
     if op == lda.SLIMKV_OP_FULL_KV:
@@ -59,6 +62,9 @@ def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_split
     if op == lda.SLIMKV_OP_LATENT:
         lda.slimkv_decode_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw, g.V_raw,
                                out, lse, ws)
+    elif op == lda.SLIMKV_OP_RECONSTRUCT and beacon_pos is not None:
+        lda.slimkv_reconstruct_rope_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw,
+                                         g.V_raw, beacon_pos.to(device), out, lse, ws)
     elif op == lda.SLIMKV_OP_RECONSTRUCT:
         lda.slimkv_reconstruct_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw,
                                     g.V_raw, out, lse, ws)
@@ -68,9 +74,9 @@ def run_gpu(inp: synth.LayerInputs, op: int = lda.SLIMKV_OP_LATENT, *, num_split
     return out.double().cpu().numpy(), (None if lse is None else lse.double().cpu().numpy())
 
 
-def oracle_layer(inp: synth.LayerInputs, units=None, threads: int = 0):
+def oracle_layer(inp: synth.LayerInputs, units=None, threads: int = 0, beacon_pos=None):
     """Oracle on the whole layer (inputs copied to the host), or on a list of
-    (b, kv head) units."""
+    (b, kv head) units; beacon_pos selects the rotated-beacon reconstruction."""
     wl = inp.workload
     st = synth.to_numpy_storage
     nb, w = inp.num_beacons, inp.raw_window
@@ -78,10 +84,11 @@ def oracle_layer(inp: synth.LayerInputs, units=None, threads: int = 0):
                          st(inp.C_K) if nb else None, st(inp.C_V) if nb else None,
                          st(inp.K_raw) if w else None, st(inp.V_raw) if w else None,
                          num_kv_heads=wl.num_kv_heads, scale=wl.scale, rope_theta=wl.rope_theta,
-                         units=units, threads=threads)
+                         units=units, threads=threads,
+                         beacon_pos=None if beacon_pos is None else st(beacon_pos))
 
 
-def oracle_units(inp: synth.LayerInputs, units):
+def oracle_units(inp: synth.LayerInputs, units, beacon_pos=None):
     """Oracle on sampled units, copying only each unit's slices to the host.
     Returns {(b, h): (out [G, d], lse [G])}."""
     wl = inp.workload
@@ -92,9 +99,18 @@ def oracle_units(inp: synth.LayerInputs, units):
         o, l = oracle.decode(s["q"], s["q_pos"], s["U_K"], s["U_V"], s["C_K"] if nb else None,
                              s["C_V"] if nb else None, s["K_raw"] if w else None,
                              s["V_raw"] if w else None, num_kv_heads=1, scale=wl.scale,
-                             rope_theta=wl.rope_theta)
+                             rope_theta=wl.rope_theta,
+                             beacon_pos=None if beacon_pos is None
+                             else synth.to_numpy_storage(beacon_pos))
         res[(b, h)] = (o[0], l[0])
     return res
+
+
+def beacon_positions(num_beacons: int, context: int) -> torch.Tensor:
+    """One beacon per s = context / num_beacons tokens, at the last position
+    of its span: (j + 1) s - 1."""
+    s = max(context // max(num_beacons, 1), 1)
+    return ((torch.arange(num_beacons, dtype=torch.int64) + 1) * s - 1).to(torch.int32)
 
 
 def oracle_full_kv_units(wl, q, q_pos, K, V, units):

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 3
+    assert lda.slimkv_abi_version() == 4
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -222,4 +222,24 @@ def test_ragged_checks(lib):
     assert _call_ragged(lib, _problem(), ptrs=dict(ws=0x4000000)) == ALIAS
     # without one it is only read, and may not overlap the outputs either
     assert _call_ragged(lib, _problem(), ptrs=dict(k_new=None, v_new=None, out=0x3000000)) == ALIAS
+
+
+def test_reconstruct_rope_checks(lib):
+    prob = _problem()
+    v = {k: ctypes.c_void_p(x) for k, x in dict(q=0x100000, q_pos=0x200000, U_K=0x300000,
+                                                 U_V=0x400000, C_K=0x1000000, C_V=0x2000000,
+                                                 K_raw=0x3000000, V_raw=0x4000000, bp=0x210000,
+                                                 out=0x5000000, lse=0x6000000,
+                                                 ws=0x7000000).items()}
+
+    def call(bp=v["bp"], ws_bytes=16, out=v["out"], p=prob):
+        return lib.slimkv_reconstruct_rope_attn(ctypes.byref(p), v["q"], v["q_pos"], v["U_K"],
+                                                v["U_V"], v["C_K"], v["C_V"], v["K_raw"],
+                                                v["V_raw"], bp, out, v["lse"], v["ws"], ws_bytes,
+                                                None)
+    assert call() == WS  # every pointer check passes; the workspace is too small
+    assert call(bp=None) == NULL and "beacon_pos" in lda.slimkv_last_error()
+    assert call(bp=ctypes.c_void_p(0x210002)) == ALIGN
+    assert call(out=ctypes.c_void_p(0x210000 - 16)) == ALIAS  # out runs into beacon_pos
+    assert call(bp=None, p=_problem(num_beacons=0)) == WS      # no beacons: no positions needed
 

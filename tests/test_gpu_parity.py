@@ -13,8 +13,8 @@ import torch
 
 import latent_decode_attention_amd as lda
 import synth
-from parity_util import (RECON_LSE_TOL, assert_parity, gather_units, note, oracle_full_kv_units,
-                         oracle_layer, oracle_units, run_gpu, sample_units)
+from parity_util import (RECON_LSE_TOL, assert_parity, beacon_positions, gather_units, note,
+                         oracle_full_kv_units, oracle_layer, oracle_units, run_gpu, sample_units)
 
 pytestmark = pytest.mark.gpu
 
@@ -311,3 +311,37 @@ def test_graph_replays_match_eager(gpu_device):
             assert torch.equal(o, ro) and torch.equal(l, rl)
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype,G,nb,w,rk,rv", [("bf16", 4, 300, 50, 64, 64),
+                                               ("bf16", 5, 777, 17, 48, 96),
+                                               ("fp32", 4, 200, 33, 32, 32)])
+def test_reconstruct_rope_small(dtype, G, nb, w, rk, rv, gpu_device):
+    """The reconstruction variant that rotates rebuilt beacon keys at their
+    positions (16x spacing), whole output against the oracle."""
+    inp = synth.make_layer(custom(dtype=dtype, B=2, Hkv=2, G=G, nb=nb, w=w, r=rk, index=91,
+                                  context=nb * 16), rank_v=rv)
+    pos = beacon_positions(nb, nb * 16)
+    note(f"reconstruct-rope {dtype} G={G} nb={nb} w={w} r=({rk},{rv})")
+    out, lse = run_gpu(inp, REC, beacon_pos=pos)
+    ref, ref_lse = oracle_layer(inp, beacon_pos=pos)
+    assert_parity(out, ref, dtype, "reconstruct-rope", lse, ref_lse,
+                  lse_tol=RECON_LSE_TOL[dtype])
+    lat, _ = oracle_layer(inp)
+    assert np.max(np.abs(ref - lat)) > 1e-3  # the rotation matters: not the latent result
+
+
+def test_c5_reconstruct_rope_sampled(gpu_device):
+    wl = synth.get_workload("c5_16x")
+    note("c5_16x reconstruct-rope sampled")
+    inp = synth.make_layer(wl, 0, device=gpu_device)
+    pos = beacon_positions(wl.num_beacons, wl.context)
+    out, lse = run_gpu(inp, REC, beacon_pos=pos)
+    units = sample_units(wl, 10, seed=5)
+    ref = oracle_units(inp, units, beacon_pos=pos)
+    got, got_lse = gather_units(out, lse, wl, units)
+    assert_parity(got, np.stack([ref[u][0] for u in units]), wl.dtype, "c5 reconstruct-rope",
+                  got_lse, np.stack([ref[u][1] for u in units]), lse_tol=RECON_LSE_TOL[wl.dtype])
+    del inp
+    torch.cuda.empty_cache()
+
