@@ -20,7 +20,8 @@ Reported beside the headline tokens/s:
   * the comparison at 128K on one layer: latent path at 16x vs the
     reconstruct-then-attend paths on the same beacons (without and with the
     rotation of rebuilt beacon keys) and vs uncompressed full-KV attention
-    over all 131072 tokens; the ragged serving step; the 48-layer Qwen step;
+    over all 131072 tokens; the ragged serving step, over capacity-sized
+    arrays and over a paged cache; the 48-layer Qwen step;
   * the fp64 CPU oracle timed on a bounded sample on this host's cores.
 """
 
@@ -55,6 +56,9 @@ def parse_args():
     ap.add_argument("--ragged", action="store_true",
                     help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
                          "of the capacities, new token stored) and print its figures as one JSON line")
+    ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
+                    help="with --ragged: the cache in pages of ROWS rows (a power of two >= 64) "
+                         "at shuffled page ids, through slimkv_decode_attn_paged")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
                          "reduction, for scaling hardware byte counters and as a read ceiling")
@@ -133,7 +137,8 @@ def main():
     log(f"workload {wl.name}: {wl.layers} layers, B={wl.batch}, generating inputs on the GPU")
     layers = [synth.make_layer(wl, layer, device=dev) for layer in range(wl.layers)]
     if args.ragged:
-        print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps)), flush=True)
+        print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps,
+                                     page_rows=args.paged)), flush=True)
         return
     probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
                                       rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
@@ -241,6 +246,8 @@ def main():
         if args.workload == "c3":
             result["comparison"]["c3_ragged_step"] = ragged_step(lda, synth, torch, dev, wl, layers,
                                                                  args.steps)
+            result["comparison"]["c3_paged_step"] = ragged_step(lda, synth, torch, dev, wl, layers,
+                                                                args.steps, page_rows=64)
             result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
 
     del ws
@@ -335,12 +342,15 @@ def replay_ms(torch, step, steps):
     return time_calls(graph.replay, steps, 3, torch)
 
 
-def ragged_step(lda, synth, torch, dev, wl, layers, steps):
+def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
     """The same 32-layer step as a serving step over a ragged batch: each
     sequence keeps a seeded number of live beacons (4096..8192) and raw rows
     (1024..2047) in the arrays, and every layer attends and stores the step's
-    new token (slimkv_decode_attn_ragged).  Bytes: the live rows, the new
-    token's key and value read and written, q, the bases, out and lse."""
+    new token (slimkv_decode_attn_ragged).  page_rows > 0: the cache lies in
+    pages of that many rows at seeded, shuffled page ids, and the step runs
+    slimkv_decode_attn_paged on them.  Bytes: the live rows, the new token's
+    key and value read and written, q, the bases, out and lse (the page
+    tables add 4 bytes per page, left out)."""
     elem = wl.elem_bytes
     first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
     steps_in, probs, bytes_step = [], [], 0
@@ -363,11 +373,23 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps):
                      dtype=torch.uint8, device=dev)
     out, lse = lda.alloc_outputs(probs[0], dev)
 
-    def step():
-        for p, x, st in zip(probs, layers, steps_in):
-            lda.slimkv_decode_attn_ragged(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
-                                          x.V_raw, st.num_beacons, st.raw_len, st.k_new,
-                                          st.v_new, out, lse, ws)
+    if page_rows:
+        paged = [synth.make_paged(x, st, page_rows=page_rows) for x, st in zip(layers, steps_in)]
+        tables = [lda.make_pages(page_rows=page_rows, beacon_table=pc.beacon_table,
+                                 raw_table=pc.raw_table, beacon_pages=pc.beacon_pages,
+                                 raw_pages=pc.raw_pages) for pc in paged]
+
+        def step():
+            for p, x, st, pc, tb in zip(probs, layers, steps_in, paged, tables):
+                lda.slimkv_decode_attn_paged(p, tb, x.q, x.q_pos, x.U_K, x.U_V, pc.C_K, pc.C_V,
+                                             pc.K_raw, pc.V_raw, st.num_beacons, st.raw_len,
+                                             st.k_new, st.v_new, out, lse, ws)
+    else:
+        def step():
+            for p, x, st in zip(probs, layers, steps_in):
+                lda.slimkv_decode_attn_ragged(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V,
+                                              x.K_raw, x.V_raw, st.num_beacons, st.raw_len,
+                                              st.k_new, st.v_new, out, lse, ws)
 
     ms = replay_ms(torch, step, steps)
     gbps = bytes_step / (ms * 1e-3) / 1e9
@@ -376,7 +398,10 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps):
            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
            "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
                         f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + new token"}
-    log(f"ragged step: {res}")
+    if page_rows:
+        res["page_rows"] = page_rows
+        del paged, tables
+    log(f"{'paged' if page_rows else 'ragged'} step: {res}")
     del ws
     torch.cuda.empty_cache()
     return res

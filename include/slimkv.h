@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 4
+#define SLIMKV_ABI_VERSION 5
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -81,7 +81,7 @@ typedef enum slimkv_op {
   SLIMKV_OP_LATENT = 0,      /* slimkv_decode_attn      */
   SLIMKV_OP_RECONSTRUCT = 1, /* slimkv_reconstruct_attn */
   SLIMKV_OP_FULL_KV = 2,     /* full_kv_attn            */
-  SLIMKV_OP_LATENT_RAGGED = 3 /* slimkv_decode_attn_ragged */
+  SLIMKV_OP_LATENT_RAGGED = 3 /* slimkv_decode_attn_ragged, _paged */
 } slimkv_op;
 
 /* Shape of one layer's call (56 bytes, no implicit padding). */
@@ -194,6 +194,70 @@ slimkv_status slimkv_decode_attn_ragged(const slimkv_problem* problem,
                                         const void* k_new, const void* v_new,
                                         float* out, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream);
+
+/*
+ * Page tables of a paged cache (slimkv_decode_attn_paged).  Rows live in
+ * fixed-size pages drawn from pools shared by the whole batch:
+ *   C_K pool   [beacon_pages, H_kv, page_rows, r_K]
+ *   C_V pool   [beacon_pages, H_kv, page_rows, r_V]
+ *   K_raw pool [raw_pages,    H_kv, page_rows, d]
+ *   V_raw pool [raw_pages,    H_kv, page_rows, d]
+ * so one page holds page_rows consecutive rows of a sequence for all of its
+ * KV heads.  Beacon row j of sequence b lies in page
+ * beacon_table[b * beacon_table_width + j / page_rows] at row
+ * j % page_rows; raw rows likewise through raw_table.  (40 bytes.)
+ */
+typedef struct slimkv_pages {
+  int32_t page_rows;          /* rows per page: a power of two, 64 .. 65536     */
+  int32_t beacon_pages;       /* pages in the C_K / C_V pools (>= 0)            */
+  int32_t raw_pages;          /* pages in the K_raw / V_raw pools (>= 0)        */
+  int32_t beacon_table_width; /* entries per sequence in beacon_table: at least
+                                 ceil(N_cap / page_rows)                        */
+  int32_t raw_table_width;    /* entries per sequence in raw_table: at least
+                                 ceil(W_cap / page_rows)                        */
+  int32_t reserved;           /* must be 0                                      */
+  const int32_t* beacon_table; /* [B, beacon_table_width] int32 (device), or
+                                  NULL when N_cap == 0                           */
+  const int32_t* raw_table;    /* [B, raw_table_width] int32 (device), or NULL
+                                  when W_cap == 0                                */
+} slimkv_pages;
+
+/*
+ * slimkv_decode_attn_paged -- slimkv_decode_attn_ragged over a paged cache.
+ *
+ * Computes exactly what slimkv_decode_attn_ragged computes for the logical
+ * arrays the pages describe (out and lse are bitwise equal to that call's
+ * on the same rows): the same clamped lengths n_b <= N_cap and w_b <= W_cap
+ * (problem->num_beacons, problem->raw_window), the same new token, and the
+ * same store of its rotated key and value as raw row w_b when w_b < W_cap,
+ * here into the page that raw_table gives for that row.  The call reads
+ * only the table entries of pages that hold live rows (and of the page
+ * that receives the new token), and only the live rows of those pages.
+ * A table entry outside [0, pages) reads as a page of zeros and is never
+ * written; the library never touches memory outside the pools.  Pages may
+ * be shared between sequences (a common prefix) except for a page that
+ * receives a new token in this call.  ceil(N_cap / page_rows) +
+ * ceil(W_cap / page_rows) must not exceed 4096 (the tables of a sequence are
+ * staged on chip).
+ *
+ *   pages              host struct above; its tables are device memory
+ *   C_K, C_V           beacon pools (NULL when N_cap == 0)
+ *   K_raw, V_raw       raw pools (NULL when W_cap == 0); written only at the
+ *                      new token's rows
+ * Other arguments, limits and the workspace (slimkv_workspace_bytes with
+ * SLIMKV_OP_LATENT_RAGGED) as for slimkv_decode_attn_ragged.
+ */
+slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
+                                       const slimkv_pages* pages,
+                                       const void* q, const int32_t* q_pos,
+                                       const void* U_K, const void* U_V,
+                                       const void* C_K, const void* C_V,
+                                       void* K_raw, void* V_raw,
+                                       const int32_t* num_beacons_b,
+                                       const int32_t* raw_len,
+                                       const void* k_new, const void* v_new,
+                                       float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /*
  * slimkv_reconstruct_attn -- comparison path: the decode step of the

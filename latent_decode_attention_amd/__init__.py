@@ -9,8 +9,9 @@ allocate outputs and workspaces with torch.
 from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # noqa: F401
                       SLIMKV_OP_FULL_KV, SLIMKV_OP_LATENT, SLIMKV_OP_LATENT_RAGGED,
                       SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn, load_library,
-                      make_problem, slimkv_abi_version, slimkv_decode_attn,
-                      slimkv_decode_attn_ragged, slimkv_last_error, slimkv_problem,
+                      make_pages, make_problem, slimkv_abi_version, slimkv_decode_attn,
+                      slimkv_decode_attn_paged, slimkv_decode_attn_ragged, slimkv_last_error,
+                      slimkv_pages, slimkv_problem,
                       slimkv_reconstruct_attn, slimkv_reconstruct_rope_attn,
                       slimkv_set_kernel_events, slimkv_status_string,
                       slimkv_workspace_bytes)

@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
+           "slimkv_decode_attn_paged",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
            "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
@@ -50,6 +51,25 @@ class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
 
 
 assert ctypes.sizeof(slimkv_problem) == 56
+
+
+class slimkv_pages(ctypes.Structure):  # noqa: N801  (C name)
+    """Mirror of ``slimkv_pages`` in include/slimkv.h (40 bytes); the tables
+    are device pointers."""
+
+    _fields_ = [
+        ("page_rows", ctypes.c_int32),
+        ("beacon_pages", ctypes.c_int32),
+        ("raw_pages", ctypes.c_int32),
+        ("beacon_table_width", ctypes.c_int32),
+        ("raw_table_width", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("beacon_table", ctypes.c_void_p),
+        ("raw_table", ctypes.c_void_p),
+    ]
+
+
+assert ctypes.sizeof(slimkv_pages) == 40
 
 
 class SlimKVError(RuntimeError):
@@ -79,6 +99,9 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_decode_attn.restype = ctypes.c_int
     lib.slimkv_decode_attn_ragged.argtypes = [prob] + [vp] * 14 + [vp, sz, vp]
     lib.slimkv_decode_attn_ragged.restype = ctypes.c_int
+    lib.slimkv_decode_attn_paged.argtypes = [prob, ctypes.POINTER(slimkv_pages)] + [vp] * 14 + [
+        vp, sz, vp]
+    lib.slimkv_decode_attn_paged.restype = ctypes.c_int
     lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_reconstruct_attn.restype = ctypes.c_int
     lib.slimkv_reconstruct_rope_attn.argtypes = [prob] + [vp] * 11 + [vp, sz, vp]
@@ -155,6 +178,31 @@ def slimkv_decode_attn_ragged(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_ra
         ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
         _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new),
         _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def make_pages(*, page_rows, beacon_table=None, raw_table=None, beacon_pages=0,
+               raw_pages=0) -> slimkv_pages:
+    """slimkv_pages from int32 tables [B, width] (device tensors or None)."""
+    def width(t):
+        if t is None:
+            return 0
+        if t.dtype != torch.int32 or t.dim() != 2:
+            raise TypeError("page tables are int32 [B, width] tensors")
+        return t.shape[1]
+    return slimkv_pages(page_rows, beacon_pages, raw_pages, width(beacon_table), width(raw_table),
+                        0, _ptr(beacon_table), _ptr(raw_table))
+
+
+def slimkv_decode_attn_paged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                             num_beacons, raw_len, k_new, v_new, out, lse, workspace,
+                             stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_paged(
+        ctypes.byref(problem), ctypes.byref(pages) if pages is not None else None, _ptr(q),
+        _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw),
+        _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,

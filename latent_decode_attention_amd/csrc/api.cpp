@@ -320,11 +320,58 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   return SLIMKV_OK;
 }
 
-slimkv_status run_ragged(const slimkv_problem* p, const void* q, const int32_t* q_pos,
-                         const void* U_K, const void* U_V, const void* C_K, const void* C_V,
-                         void* K_raw, void* V_raw, const int32_t* seq_beacons,
+// Page-table checks of a paged call: the page size, the table widths
+// against the capacities and the on-chip table limit.  Sets *shift to
+// log2(page_rows) and pool_bytes to the sizes of the C_K, C_V, K_raw and
+// V_raw pools.
+slimkv_status check_pages(const slimkv_problem* p, const slimkv_pages* pg, int elem, int* shift,
+                          size_t pool_bytes[4]) {
+  if (!pg) return fail(SLIMKV_ERR_NULL, "pages is NULL");
+  const int pr = pg->page_rows;
+  if (pr < (1 << kMinPageShift) || pr > (1 << kMaxPageShift) || (pr & (pr - 1)) != 0)
+    return fail(SLIMKV_ERR_SHAPE, "page_rows %d is not a power of two in [%d, %d]", pr,
+                1 << kMinPageShift, 1 << kMaxPageShift);
+  if (pg->reserved != 0) return fail(SLIMKV_ERR_SHAPE, "pages->reserved must be 0");
+  *shift = __builtin_ctz((unsigned)pr);
+  const int64_t nbp = ceil_div(p->num_beacons, pr), nrp = ceil_div(p->raw_window, pr);
+  if (nbp + nrp > kMaxPageEntries)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "%lld + %lld pages per sequence exceed %d",
+                (long long)nbp, (long long)nrp, kMaxPageEntries);
+  const struct {
+    int64_t need;
+    int32_t width, pages;
+    const int32_t* table;
+    const char* name;
+  } seg[2] = {{nbp, pg->beacon_table_width, pg->beacon_pages, pg->beacon_table, "beacon"},
+              {nrp, pg->raw_table_width, pg->raw_pages, pg->raw_table, "raw"}};
+  for (const auto& sg : seg) {
+    if (sg.need == 0) continue;
+    if (!sg.table) return fail(SLIMKV_ERR_NULL, "%s_table is NULL", sg.name);
+    if ((uintptr_t)sg.table % 4 != 0)
+      return fail(SLIMKV_ERR_ALIGN, "%s_table is not 4-byte aligned", sg.name);
+    if (sg.width < sg.need)
+      return fail(SLIMKV_ERR_SHAPE, "%s_table_width %d is below the %lld pages of the capacity",
+                  sg.name, sg.width, (long long)sg.need);
+    if (sg.pages < 1) return fail(SLIMKV_ERR_SHAPE, "%s_pages must be >= 1", sg.name);
+  }
+  // pool bytes: pages x H_kv x page_rows x width x elem, for C_K, C_V, K_raw, V_raw
+  const int64_t widths[4] = {p->num_beacons > 0 ? p->rank_k : 0, p->num_beacons > 0 ? p->rank_v : 0,
+                             kHeadDim, kHeadDim};
+  for (int i = 0; i < 4; ++i) {
+    const auto& sg = seg[i / 2];
+    const double bytes = (double)sg.pages * p->num_kv_heads * pr * widths[i] * elem;
+    if (sg.need > 0 && bytes > 4.0e18)
+      return fail(SLIMKV_ERR_SHAPE, "the %s pools are too large", sg.name);
+    pool_bytes[i] = sg.need > 0 ? (size_t)sg.pages * p->num_kv_heads * pr * widths[i] * elem : 0;
+  }
+  return SLIMKV_OK;
+}
+
+slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const void* q,
+                         const int32_t* q_pos, const void* U_K, const void* U_V, const void* C_K,
+                         const void* C_V, void* K_raw, void* V_raw, const int32_t* seq_beacons,
                          const int32_t* seq_raw, const void* k_new, const void* v_new, float* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         float* lse, void* ws, size_t ws_bytes, void* stream, bool paged) {
   Plan pl;
   slimkv_status st = make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
   if (st != SLIMKV_OK) return st;
@@ -333,24 +380,37 @@ slimkv_status run_ragged(const slimkv_problem* p, const void* q, const int32_t* 
   const size_t nb = p->num_beacons, w = p->raw_window;
   const bool beacons = nb > 0, raw = w > 0, append = k_new != nullptr || v_new != nullptr;
   const size_t rk = beacons ? p->rank_k : 0, rv = beacons ? p->rank_v : 0;
+  // bytes of C_K, C_V, K_raw, V_raw: capacity arrays, or page pools
+  size_t cache_bytes[4] = {B * Hkv * nb * rk * e, B * Hkv * nb * rv * e, B * Hkv * w * d * e,
+                           B * Hkv * w * d * e};
+  int shift = 0;
+  if (paged) {
+    st = check_pages(p, pg, pl.elem, &shift, cache_bytes);
+    if (st != SLIMKV_OK) return st;
+  }
   if (append && (!k_new || !v_new)) return fail(SLIMKV_ERR_NULL, "k_new and v_new go together");
 
   // Inputs read as 16-byte vectors, then the int32 ones; with a new token
   // the raw arrays are also written, so they count as outputs too.
-  Range in[10] = {
+  const bool btab = paged && beacons, rtab = paged && raw;
+  Range in[12] = {
       {q, B * Hq * d * e, "q"},
       {beacons ? U_K : nullptr, Hkv * d * rk * e, "U_K"},
       {beacons ? U_V : nullptr, Hkv * d * rv * e, "U_V"},
-      {beacons ? C_K : nullptr, B * Hkv * nb * rk * e, "C_K"},
-      {beacons ? C_V : nullptr, B * Hkv * nb * rv * e, "C_V"},
+      {beacons ? C_K : nullptr, cache_bytes[0], "C_K"},
+      {beacons ? C_V : nullptr, cache_bytes[1], "C_V"},
       {append ? k_new : nullptr, B * Hkv * d * e, "k_new"},
       {append ? v_new : nullptr, B * Hkv * d * e, "v_new"},
       {q_pos, B * sizeof(int32_t), "q_pos"},
       {seq_beacons, seq_beacons ? B * sizeof(int32_t) : 0, "num_beacons_b"},
       {seq_raw, seq_raw ? B * sizeof(int32_t) : 0, "raw_len"},
+      {btab ? pg->beacon_table : nullptr, btab ? B * pg->beacon_table_width * sizeof(int32_t) : 0,
+       "beacon_table"},
+      {rtab ? pg->raw_table : nullptr, rtab ? B * pg->raw_table_width * sizeof(int32_t) : 0,
+       "raw_table"},
   };
-  const Range kr{raw ? K_raw : nullptr, B * Hkv * w * d * e, "K_raw"};
-  const Range vr{raw ? V_raw : nullptr, B * Hkv * w * d * e, "V_raw"};
+  const Range kr{raw ? K_raw : nullptr, cache_bytes[2], "K_raw"};
+  const Range vr{raw ? V_raw : nullptr, cache_bytes[3], "V_raw"};
   Range req[11];
   int n_req = 0;
   req[n_req++] = in[0];
@@ -367,9 +427,9 @@ slimkv_status run_ragged(const slimkv_problem* p, const void* q, const int32_t* 
                    {ws, pl.total, "workspace"},
                    {append ? kr.p : nullptr, append ? kr.bytes : 0, "K_raw"},
                    {append ? vr.p : nullptr, append ? vr.bytes : 0, "V_raw"}};
-  Range all_in[12];
+  Range all_in[14];
   int n_in = 0;
-  for (int i = 0; i < 10; ++i) all_in[n_in++] = in[i];
+  for (int i = 0; i < 12; ++i) all_in[n_in++] = in[i];
   if (!append) {
     all_in[n_in++] = kr;
     all_in[n_in++] = vr;
@@ -417,6 +477,15 @@ slimkv_status run_ragged(const slimkv_problem* p, const void* q, const int32_t* 
   a.v_new = append ? v_new : nullptr;
   a.k_store = K_raw;
   a.v_store = V_raw;
+  if (paged) {
+    a.page_table[0] = btab ? pg->beacon_table : nullptr;
+    a.page_table[1] = rtab ? pg->raw_table : nullptr;
+    a.table_width[0] = pg->beacon_table_width;
+    a.table_width[1] = pg->raw_table_width;
+    a.num_pages[0] = pg->beacon_pages;
+    a.num_pages[1] = pg->raw_pages;
+    a.page_shift = shift;
+  }
   a.deterministic = 1;
   const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
@@ -479,8 +548,21 @@ slimkv_status slimkv_decode_attn_ragged(const slimkv_problem* problem, const voi
                                         const int32_t* num_beacons_b, const int32_t* raw_len,
                                         const void* k_new, const void* v_new, float* out, float* lse,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  return slimkv::run_ragged(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b,
-                            raw_len, k_new, v_new, out, lse, workspace, workspace_bytes, stream);
+  return slimkv::run_ragged(problem, nullptr, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, false);
+}
+
+slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem, const slimkv_pages* pages,
+                                       const void* q, const int32_t* q_pos, const void* U_K,
+                                       const void* U_V, const void* C_K, const void* C_V,
+                                       void* K_raw, void* V_raw, const int32_t* num_beacons_b,
+                                       const int32_t* raw_len, const void* k_new,
+                                       const void* v_new, float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, true);
 }
 
 const char* slimkv_status_string(slimkv_status status) {

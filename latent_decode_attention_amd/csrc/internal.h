@@ -16,6 +16,9 @@ constexpr int kMaxChunks = 64;         // workgroups per unit (each writes one p
 constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
 constexpr int kWgPerCu = 2;            // resident attention workgroups per CU the grid targets
 constexpr int kMaxRaggedBatch = 1024;  // sequences per ragged call (their lengths sit in LDS)
+constexpr int kMaxPageEntries = 4096;  // page-table entries of one sequence (staged in LDS)
+constexpr int kMinPageShift = 6;       // pages hold at least 64 rows: no tile spans two pages
+constexpr int kMaxPageShift = 16;
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -67,6 +70,13 @@ struct AttnArgs {
   const void* v_new;           // [B, H_kv, d] its value (with k_new)
   void* k_store;               // K_raw / V_raw: the new token's row is written at
   void* v_store;               //   index seq_raw[b] when that is below the capacity
+  // Paged ragged calls (page_table[0] or [1] set): seg[s].K / V are then
+  // pools [num_pages[s], H_kv, 1 << page_shift, width] and sequence b's row
+  // i of segment s lies in page page_table[s][b * table_width[s] + (i >> page_shift)]
+  const int32_t* page_table[2];
+  int32_t table_width[2];
+  int32_t num_pages[2];
+  int32_t page_shift;
 };
 
 struct RebuildArgs {
@@ -84,7 +94,8 @@ struct RebuildArgs {
 // workgroup slots (CUs x resident workgroups of the chosen kernel).
 hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0,
                             hipEvent_t ev1);
-// The ragged-batch attention kernel (one launch; see ragged_impl.h).
+// The ragged-batch attention kernel (one launch; see ragged_impl.h), over
+// capacity-sized arrays or, with page tables in `a`, over page pools.
 hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 // Chunks per unit: the count in [1, kMaxChunks] whose workgroups fill the

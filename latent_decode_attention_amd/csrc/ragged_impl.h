@@ -27,6 +27,12 @@
 //   * The merge also folds in the new token as a one-row partial (its score
 //     computed there), writes out and lse, and stores the token's row; a
 //     unit without rows still gets its one piece, which finds no tiles.
+//   * Paged caches: rows sit in pages of at least 64 rows (a whole number
+//     of tiles) from shared pools.  Each workgroup stages its sequence's
+//     page ids in LDS once; a tile then costs one LDS read for its page id
+//     and a descriptor over that page's live rows, so the tile loop and
+//     the order of the arithmetic are those of the contiguous layout and
+//     the results are bitwise the same.
 #pragma once
 
 namespace slimkv {
@@ -153,8 +159,11 @@ __device__ __forceinline__ int ragged_piece_of(int blk, int P) {
 // slots, P), or one block per unit if the units are more; that is enough
 // for every piece, and blocks past the last piece return at once.  Piece i of the
 // batch is workgroup c of unit (b, h) as in the uniform kernel, with the
-// unit's live rows and its k[b] workgroups.
-template <int G, int NCH, bool BF16>
+// unit's live rows and its k[b] workgroups.  PG: the cache is paged; the
+// workgroup first stages sequence b's page ids that it uses -- the pages
+// of its live beacon rows, then of its live raw rows and of the row that
+// receives the new token -- in LDS.
+template <int G, int NCH, bool BF16, bool PG>
 __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel(AttnArgs a) {
   constexpr bool BLAT = NCH > 0;
   constexpr int kFullNch = BF16 ? 4 : 8;
@@ -162,6 +171,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel
   constexpr int TRB = SegView<BN, BF16>::kRows, TRR = SegView<kFullNch, BF16>::kRows;
   __shared__ AttnShared sh;
   __shared__ RaggedShared rs;
+  __shared__ int32_t ptab[PG ? kMaxPageEntries : 1];
   const int tid = threadIdx.x;
   const int B = a.batch, Hkv = a.num_kv_heads, P = a.chunks;
   if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, rs, tid & 63, P);
@@ -179,22 +189,33 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel
   const int b = lo;
   const int kb = uni(rs.k[b]), first = uni(rs.kpre[b]);
   const int h = (pi - first) / kb, c = pi - first - h * kb;
-  attend_unit<G, NCH, BF16, true>(a, sh, b * Hkv + h, b, h, c, kb, uni(rs.nb[b]), uni(rs.w[b]),
-                                  first + h * kb);
+  const int nbr = uni(rs.nb[b]), wr = uni(rs.w[b]);
+  if constexpr (PG) {
+    // at most ceil(N_cap / rows) + ceil(W_cap / rows) <= kMaxPageEntries ids
+    const int sh_ = a.page_shift, pm = (1 << sh_) - 1;
+    const int nbp = (nbr + pm) >> sh_;
+    const int wst = (a.k_new && wr < a.seg[1].rows) ? wr + 1 : wr;
+    const int n = nbp + ((wst + pm) >> sh_);
+    const int32_t* bt = a.page_table[0] + (size_t)b * a.table_width[0];
+    const int32_t* rt = a.page_table[1] + (size_t)b * a.table_width[1];
+    for (int i = tid; i < n; i += kThreads) ptab[i] = i < nbp ? bt[i] : rt[i - nbp];
+    lds_barrier();
+  }
+  attend_unit<G, NCH, BF16, true, PG>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb, ptab);
 }
 
 // Launch for group size G; nch as for launch_attention_group.
-template <int G>
+template <int G, bool PG>
 const void* ragged_kernel_for(int dtype, int nch) {
   if (dtype == 0)
-    return nch == 0 ? reinterpret_cast<const void*>(&ragged_kernel<G, 0, false>)
-                    : reinterpret_cast<const void*>(&ragged_kernel<G, 8, false>);
+    return nch == 0 ? reinterpret_cast<const void*>(&ragged_kernel<G, 0, false, PG>)
+                    : reinterpret_cast<const void*>(&ragged_kernel<G, 8, false, PG>);
   switch (nch) {
-    case 0: return reinterpret_cast<const void*>(&ragged_kernel<G, 0, true>);
-    case 1: return reinterpret_cast<const void*>(&ragged_kernel<G, 1, true>);
-    case 2: return reinterpret_cast<const void*>(&ragged_kernel<G, 2, true>);
-    case 3: return reinterpret_cast<const void*>(&ragged_kernel<G, 3, true>);
-    default: return reinterpret_cast<const void*>(&ragged_kernel<G, 4, true>);
+    case 0: return reinterpret_cast<const void*>(&ragged_kernel<G, 0, true, PG>);
+    case 1: return reinterpret_cast<const void*>(&ragged_kernel<G, 1, true, PG>);
+    case 2: return reinterpret_cast<const void*>(&ragged_kernel<G, 2, true, PG>);
+    case 3: return reinterpret_cast<const void*>(&ragged_kernel<G, 3, true, PG>);
+    default: return reinterpret_cast<const void*>(&ragged_kernel<G, 4, true, PG>);
   }
 }
 
@@ -203,7 +224,8 @@ const void* ragged_kernel_for(int dtype, int nch) {
 template <int G>
 hipError_t launch_ragged_group(AttnArgs a, int dtype, int nch, int64_t max_wgs, hipStream_t s,
                                hipEvent_t ev0, hipEvent_t ev1) {
-  const void* kfn = ragged_kernel_for<G>(dtype, nch);
+  const bool paged = a.page_table[0] != nullptr || a.page_table[1] != nullptr;
+  const void* kfn = paged ? ragged_kernel_for<G, true>(dtype, nch) : ragged_kernel_for<G, false>(dtype, nch);
   int64_t P = a.chunks;
   if (P <= 0) {
     P = device_slots(kfn);

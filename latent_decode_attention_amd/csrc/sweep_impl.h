@@ -399,18 +399,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // chunk wider than the keys) meet zero query entries.  A value row spans
 // rv / EPL lanes, padded to a power of two (lpr) so that row groups can be
 // summed by a butterfly.  Tiles are kRows rows.
-template <int NCH, bool BF16>
+//
+// PAGED: the rows lie in pages of 2^pshift rows (at least 64, so no tile
+// spans two pages) drawn from pools [pages, H_kv, 2^pshift, width]; the
+// unit's page ids sit in LDS (tab, from index tab0).  Each tile then gets
+// its own descriptors, over the live rows of its page only; a page id
+// outside [0, npages) gets empty descriptors, so its rows read as zeros.
+template <int NCH, bool BF16, bool PAGED = false>
 struct SegView {
   using Tr = Traits<BF16>;
   static constexpr int kSub = TileShape<BF16, NCH>::kSub;
   static constexpr int kRows = TileShape<BF16, NCH>::kRows;
   static constexpr int kKeySlots = kSub * NCH;
-  __amdgpu_buffer_rsrc_t kr, vr;  // this unit's key and value rows
+  static_assert(kRows <= (1 << kMinPageShift), "a tile must fit in a page");
+  __amdgpu_buffer_rsrc_t kr, vr;  // this unit's key and value rows (contiguous)
   int rows, rk, rv, ntiles;
   int kstride, vstride;  // bytes per key / value row
   int klane, vlane;      // this lane's byte offset within a tile (row 0 of the tile)
   int lpr, rpi, vrow, vcc, lanes_row;
   bool vact;
+  // paged only
+  const char* kp;               // this head's row 0 of page 0 in the key pool
+  const char* vp;               // and in the value pool
+  size_t kpage, vpage;          // bytes per page (all heads)
+  const int32_t* tab;           // the unit's page ids (LDS)
+  int tab0, pshift, npages;
 
   // cap: rows each unit's arrays hold (the unit stride); rows_: live rows
   __device__ __forceinline__ void init(const void* Kp, const void* Vp, int cap, int rows_, int rk_,
@@ -423,6 +436,30 @@ struct SegView {
     const size_t urow = (size_t)unit * (size_t)cap;
     kr = make_rsrc(static_cast<const char*>(Kp) + urow * kstride, (uint32_t)rows * kstride);
     vr = make_rsrc(static_cast<const char*>(Vp) + urow * vstride, (uint32_t)rows * vstride);
+    lane_init(lane);
+  }
+  // pools of `pages` pages of 2^shift rows; h of hkv heads; the unit's page
+  // ids at tab_[t0 ..]
+  __device__ __forceinline__ void init_paged(const void* Kp, const void* Vp, int shift, int pages,
+                                             int rows_, int rk_, int rv_, int h, int hkv,
+                                             const int32_t* tab_, int t0, int lane) {
+    rows = rows_;
+    rk = rk_;
+    rv = rv_;
+    kstride = rk * Tr::kElemBytes;
+    vstride = rv * Tr::kElemBytes;
+    pshift = shift;
+    npages = pages;
+    tab = tab_;
+    tab0 = t0;
+    const size_t hrow = (size_t)h << shift;
+    kp = static_cast<const char*>(Kp) + hrow * kstride;
+    vp = static_cast<const char*>(Vp) + hrow * vstride;
+    kpage = ((size_t)hkv << shift) * kstride;
+    vpage = ((size_t)hkv << shift) * vstride;
+    lane_init(lane);
+  }
+  __device__ __forceinline__ void lane_init(int lane) {
     ntiles = (rows + kRows - 1) / kRows;
     lanes_row = rv / Tr::kEpl;
     lpr = 1 << (32 - __builtin_clz(lanes_row - 1));
@@ -436,6 +473,28 @@ struct SegView {
     klane = n * kstride + kg * Tr::kEpl * Tr::kElemBytes;
     // value slot i: row i * rpi + vrow, this lane's 16 bytes (idle lanes clamped)
     vlane = vrow * vstride + min(vcc, lanes_row - 1) * 16;
+  }
+  // descriptor and this lane's byte offset for the keys / values of the
+  // tile at row ta (pid: its page id when paged)
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* pool, size_t page,
+                                                              int stride, int ta, int pid) const {
+    const bool ok = (uint32_t)pid < (uint32_t)npages;
+    const int live = min(rows - ((ta >> pshift) << pshift), 1 << pshift);
+    return make_rsrc(pool + (size_t)(ok ? pid : 0) * page, ok ? (uint32_t)(live * stride) : 0u);
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_rsrc(int ta, int pid) const {
+    if constexpr (PAGED) return page_rsrc(kp, kpage, kstride, ta, pid);
+    else return kr;
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t val_rsrc(int ta, int pid) const {
+    if constexpr (PAGED) return page_rsrc(vp, vpage, vstride, ta, pid);
+    else return vr;
+  }
+  __device__ __forceinline__ int key_base(int ta) const {
+    return klane + (PAGED ? (ta & ((1 << pshift) - 1)) : ta) * kstride;
+  }
+  __device__ __forceinline__ int val_base(int ta) const {
+    return vlane + (PAGED ? (ta & ((1 << pshift) - 1)) : ta) * vstride;
   }
   // uniform byte offsets of key / value slot i within a tile
   __device__ __forceinline__ int key_off(int i) const {
@@ -458,22 +517,37 @@ struct TailRows {
   __device__ __forceinline__ int val_off(int c) const { return c * 64; }
 };
 
+// Page id of the tile a wave requests next (row ta of `a` if use_a, else
+// row tb of `b` if use_b), one LDS read; 0 for contiguous views and for the
+// tail.
+template <int NA, int NB, bool BF16, bool PG>
+__device__ __forceinline__ int tile_page(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
+                                         const SegView<NB, BF16, PG>& b, int tb, bool use_b) {
+  if constexpr (!PG) {
+    return 0;
+  } else {
+    const int i = use_a ? a.tab0 + (ta >> a.pshift) : (use_b ? b.tab0 + (tb >> b.pshift) : 0);
+    return __builtin_amdgcn_readfirstlane(a.tab[i]);
+  }
+}
+
 // Request one tile's keys (or values) into the wave's tile registers: tile
 // starting at row ta of `a` if use_a, else row tb of `b` if use_b (only with
 // CROSS), else the tail's rows.  The choice is wave-uniform, so it selects a
 // descriptor and a base offset; every slot is one unconditional load, and the
 // registers need no copies afterwards (separate loads per source under a
-// branch would be merged by copies that wait for the loads).
-template <bool CROSS, int NA, int NB, bool BF16>
-__device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16>& a, int ta, bool use_a,
-                                               const SegView<NB, BF16>& b, int tb, bool use_b,
-                                               const TailRows& tail, u32x4_t* kbuf) {
-  constexpr int KA = SegView<NA, BF16>::kKeySlots, KB = SegView<NB, BF16>::kKeySlots;
+// branch would be merged by copies that wait for the loads).  pid: the
+// chosen tile's page id (see tile_page) when the views are paged.
+template <bool CROSS, int NA, int NB, bool BF16, bool PG>
+__device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
+                                               const SegView<NB, BF16, PG>& b, int tb, bool use_b,
+                                               const TailRows& tail, int pid, u32x4_t* kbuf) {
+  constexpr int KA = SegView<NA, BF16, PG>::kKeySlots, KB = SegView<NB, BF16, PG>::kKeySlots;
   constexpr int K = Traits<BF16>::kMaxLoads;
   static_assert(KA <= K && KB <= K, "tile too large");
   const bool ub = CROSS && use_b;
-  const __amdgpu_buffer_rsrc_t r = use_a ? a.kr : (ub ? b.kr : tail.r);
-  const int base = use_a ? a.klane + ta * a.kstride : (ub ? b.klane + tb * b.kstride : tail.klane);
+  const __amdgpu_buffer_rsrc_t r = use_a ? a.key_rsrc(ta, pid) : (ub ? b.key_rsrc(tb, pid) : tail.r);
+  const int base = use_a ? a.key_base(ta) : (ub ? b.key_base(tb) : tail.klane);
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     const int off = use_a ? (i < KA ? a.key_off(i) : 0)
@@ -481,13 +555,13 @@ __device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16>& a, int t
     kbuf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + off, 0, kStream);
   }
 }
-template <bool CROSS, int NA, int NB, bool BF16>
-__device__ __forceinline__ void load_tile_values(const SegView<NA, BF16>& a, int ta, bool use_a,
-                                                 const SegView<NB, BF16>& b, int tb, bool use_b,
-                                                 const TailRows& tail, u32x4_t* vbuf) {
+template <bool CROSS, int NA, int NB, bool BF16, bool PG>
+__device__ __forceinline__ void load_tile_values(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
+                                                 const SegView<NB, BF16, PG>& b, int tb, bool use_b,
+                                                 const TailRows& tail, int pid, u32x4_t* vbuf) {
   const bool ub = CROSS && use_b;
-  const __amdgpu_buffer_rsrc_t r = use_a ? a.vr : (ub ? b.vr : tail.r);
-  const int base = use_a ? a.vlane + ta * a.vstride : (ub ? b.vlane + tb * b.vstride : tail.vlane);
+  const __amdgpu_buffer_rsrc_t r = use_a ? a.val_rsrc(ta, pid) : (ub ? b.val_rsrc(tb, pid) : tail.r);
+  const int base = use_a ? a.val_base(ta) : (ub ? b.val_base(tb) : tail.vlane);
 #pragma unroll
   for (int i = 0; i < Traits<BF16>::kMaxLoads; ++i) {
     const int off = use_a ? a.val_off(i) : (ub ? b.val_off(i) : tail.val_off(i));
@@ -556,22 +630,22 @@ struct TileFeed {
 // past pend the slots take the tail's addresses instead).  Positions from
 // pend on are not this sweep's to process.  On exit j is the first position
 // past this segment (or pend) the wave drew.
-template <int G, int NCH, bool BF16, bool CROSS, int NCH2>
-__device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
-                                      const SegView<NCH2, BF16>& nx, int nxbase, int pend, int& j,
+template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG>
+__device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbase,
+                                      const SegView<NCH2, BF16, PG>& nx, int nxbase, int pend, int& j,
                                       TileFeed& feed, const TailRows& tail, const float* qsrc, int rq,
                                       u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
                                       WaveState<G, BF16>& st) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
-  constexpr int SUB = SegView<NCH, BF16>::kSub;
-  constexpr int TR = SegView<NCH, BF16>::kRows;
+  constexpr int SUB = SegView<NCH, BF16, PG>::kSub;
+  constexpr int TR = SegView<NCH, BF16, PG>::kRows;
   constexpr int VMAX = Tr::kMaxLoads;
   constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
   constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
   static_assert(SUB * NCH <= Tr::kMaxLoads, "tile too large");
-  constexpr int TR2 = SegView<NCH2, BF16>::kRows;
+  constexpr int TR2 = SegView<NCH2, BF16, PG>::kRows;
   const int pstop = min(pbase + sv.ntiles, pend);
   if (j >= pstop) return;  // wave-uniform
 
@@ -629,7 +703,9 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
     const int jn = feed.take(j);  // wave-uniform
     const bool more = jn < pstop;
     const bool cross = CROSS && !more && jn < pend;
-    load_tile_keys<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, kbuf);
+    const int pid = tile_page(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross);
+    load_tile_keys<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, pid,
+                          kbuf);
     feed.request(lane);
 
     // -- online softmax: tile max per head, rescale only when it grows
@@ -706,7 +782,8 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16>& sv, int pbase,
           for (int e = 0; e < EPL; ++e) st.acc[g][e] = fmaf(pv[g], v[e], st.acc[g][e]);
       }
     }
-    load_tile_values<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, vbuf);
+    load_tile_values<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, pid,
+                            vbuf);
     // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -737,8 +814,8 @@ __device__ __forceinline__ void wave_reduce(WaveState<G, BF16>& st, int lpr) {
 }
 
 // Park a reduced wave state in LDS: (max, sum) per head and the G x rv sums.
-template <int G, int NCH, bool BF16>
-__device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const SegView<NCH, BF16>& sv,
+template <int G, int NCH, bool BF16, bool PG>
+__device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const SegView<NCH, BF16, PG>& sv,
                                           float (*wacc)[kHeadDim], float (*wml)[2]) {
   const int lane = threadIdx.x & 63, n = lane & 15, kg = lane >> 4;
   if (n == 0) {
@@ -967,10 +1044,13 @@ __device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
 // scored against the query rotated as in the prologue; write out and lse,
 // and store the token's row when the raw window has room (wlive < its
 // capacity).  Thread (g, c4) owns 16-byte column c4 of head g.  With no
-// rows at all the unit gets out 0 and lse -inf.
-template <int G, bool BF16>
+// rows at all the unit gets out 0 and lse -inf.  PG: the raw rows are
+// paged, the page ids of the unit's raw pages at ptab[rtab0 ..] (LDS); the
+// row goes to its page, or nowhere if the page id is out of range.
+template <int G, bool BF16, bool PG>
 __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, int h, int slot0,
-                                              int nslots, int wlive) {
+                                              int nslots, int wlive, const int32_t* ptab,
+                                              int rtab0) {
   const int tid = threadIdx.x;
   if (tid >= G * kHeadDim / 4) return;
   const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
@@ -1041,8 +1121,16 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
     L = L * a1 + a2;
     acc = acc * a1 + f32x4_t{vnew[0], vnew[1], vnew[2], vnew[3]} * a2;
     M = mn;
-    if (g == 0 && wlive < a.seg[1].rows) {
-      const size_t row = ((size_t)u * a.seg[1].rows + wlive) * kHeadDim + 4 * c4;
+    size_t row = ((size_t)u * a.seg[1].rows + wlive) * kHeadDim + 4 * c4;
+    bool store = g == 0 && wlive < a.seg[1].rows;
+    if constexpr (PG) {
+      const int sh = a.page_shift;
+      const int pid = store ? ptab[rtab0 + (wlive >> sh)] : -1;
+      store = store && (uint32_t)pid < (uint32_t)a.num_pages[1];
+      row = (((((size_t)pid * a.num_kv_heads + h) << sh) + (wlive & ((1 << sh) - 1))) * kHeadDim) +
+            4 * c4;
+    }
+    if (store) {
       if constexpr (BF16) {
         uint32_t* kd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.k_store) + row);
         uint32_t* vd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.v_store) + row);
@@ -1082,11 +1170,14 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
 // the workgroup that finishes last merges the unit.  nbr, wr: the unit's
 // live beacon and raw rows (the arrays hold a.seg[*].rows per unit).
 // RAGGED: the merge also takes in the decode step's new token (ragged_finish).
+// PG (ragged only): the rows are paged; ptab (LDS) holds the unit's beacon
+// page ids, then its raw page ids.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
-template <int G, int NCH, bool BF16, bool RAGGED>
+template <int G, int NCH, bool BF16, bool RAGGED, bool PG = false>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, int unit, int b, int h,
-                                            int c, int k, int nbr, int wr, int slot0) {
+                                            int c, int k, int nbr, int wr, int slot0,
+                                            const int32_t* ptab = nullptr) {
   constexpr bool BLAT = NCH > 0;
   constexpr int kFullNch = BF16 ? 4 : 8;
   constexpr int BN = BLAT ? NCH : kFullNch;
@@ -1096,11 +1187,20 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   const int nwaves = kWaves * k;
   const int wu = kWaves * c + wave;  // this wave's number within the unit
 
-  SegView<BN, BF16> bv;  // beacon rows
-  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, nbr, BLAT ? a.seg[0].rk : kHeadDim,
-          BLAT ? a.seg[0].rv : kHeadDim, unit, lane);
-  SegView<kFullNch, BF16> rw;  // raw rows
-  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
+  SegView<BN, BF16, PG> bv;        // beacon rows
+  SegView<kFullNch, BF16, PG> rw;  // raw rows
+  const int brk = BLAT ? a.seg[0].rk : kHeadDim, brv = BLAT ? a.seg[0].rv : kHeadDim;
+  int nbp = 0;  // the unit's beacon pages (paged)
+  if constexpr (PG) {
+    nbp = (nbr + (1 << a.page_shift) - 1) >> a.page_shift;
+    bv.init_paged(a.seg[0].K, a.seg[0].V, a.page_shift, a.num_pages[0], nbr, brk, brv, h,
+                  a.num_kv_heads, ptab, 0, lane);
+    rw.init_paged(a.seg[1].K, a.seg[1].V, a.page_shift, a.num_pages[1], wr, kHeadDim, kHeadDim, h,
+                  a.num_kv_heads, ptab, nbp, lane);
+  } else {
+    bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, nbr, brk, brv, unit, lane);
+    rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
+  }
   // tile positions: beacon tiles 0 .. nbt-1, then raw tiles; this wave's
   // first is wu, later ones round-robin or from the unit's counter
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
@@ -1131,9 +1231,11 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
   int j = wu;
   {
-    const int tb = j * SegView<BN, BF16>::kRows, tr = (j - nbt) * SegView<kFullNch, BF16>::kRows;
-    load_tile_keys<true>(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, tail, kbuf);
-    load_tile_values<true>(bv, tb, j < nbt, rw, tr, j >= nbt && j < total, tail, vbuf);
+    const int tb = j * SegView<BN, BF16, PG>::kRows, tr = (j - nbt) * SegView<kFullNch, BF16, PG>::kRows;
+    const bool ub = j < nbt, ur = j >= nbt && j < total;
+    const int pid = tile_page(bv, tb, ub, rw, tr, ur);
+    load_tile_keys<true>(bv, tb, ub, rw, tr, ur, tail, pid, kbuf);
+    load_tile_values<true>(bv, tb, ub, rw, tr, ur, tail, pid, vbuf);
   }
   pro.finish(a, sh, wave);
 
@@ -1143,7 +1245,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   sweep<G, BN, BF16, true>(bv, 0, rw, nbt, total, j, feed, tail,
                            BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf, pw, st);
   wave_reduce<G, BF16>(st, bv.lpr);
-  wave_park<G, BN, BF16>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
+  wave_park<G, BN, BF16, PG>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
   st.reset();
   sweep<G, kFullNch, BF16, false>(rw, nbt, rw, total, total, j, feed, tail, &sh.qrot[0][0], kHeadDim,
                                   kbuf, vbuf, pw, st);
@@ -1161,7 +1263,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   wave_reduce<G, BF16>(st, rw.lpr);
   lds_barrier();  // every wave is done with its exp-weights (which alias the raw sums)
                     // and with the query (whose space takes the merged sums)
-  wave_park<G, kFullNch, BF16>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
+  wave_park<G, kFullNch, BF16, PG>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
   lds_barrier();
   const size_t slot = (size_t)slot0 + c;
   wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw, a.part_ml + slot * G * 2,
@@ -1186,7 +1288,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (RAGGED)
-    ragged_finish<G, BF16>(a, unit, b, h, slot0, k, wr);
+    ragged_finish<G, BF16, PG>(a, unit, b, h, slot0, k, wr, ptab, nbp);
   else
     merge_unit<G>(a, unit, b, h);
 }

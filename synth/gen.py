@@ -42,7 +42,7 @@ from .configs import Workload
 TOKEN_BLOCK = 128
 
 _IDS = {"q": 1, "U_K": 2, "U_V": 3, "C_K": 4, "C_V": 5, "K_tok": 6, "V_tok": 7, "lengths": 8,
-        "k_new": 9, "v_new": 10}
+        "k_new": 9, "v_new": 10, "pages": 11}
 
 _TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
@@ -201,6 +201,89 @@ def make_step(wl: Workload, inp: LayerInputs, *, base_seed: int = 0, device="cpu
     v = _gauss(shape, _seed(base_seed, wl, inp.layer, "v_new"), wl.sigma, wl.dtype, device)
     return StepInputs(torch.from_numpy(nb.astype(np.int32)).to(device),
                       torch.from_numpy(rw.astype(np.int32)).to(device), k, v)
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """A layer's cache laid out in pages drawn from shared pools:
+    C_K, C_V [beacon_pages, H_kv, page_rows, r] and K_raw, V_raw
+    [raw_pages, H_kv, page_rows, d]; sequence b's row i of a segment lies in
+    page table[b, i // page_rows] at row i % page_rows."""
+
+    page_rows: int
+    C_K: torch.Tensor
+    C_V: torch.Tensor
+    K_raw: torch.Tensor
+    V_raw: torch.Tensor
+    beacon_table: torch.Tensor  # [B, width] int32
+    raw_table: torch.Tensor     # [B, width] int32
+
+    @property
+    def beacon_pages(self) -> int:
+        return int(self.C_K.shape[0])
+
+    @property
+    def raw_pages(self) -> int:
+        return int(self.K_raw.shape[0])
+
+
+def _nan_fill(t: torch.Tensor) -> torch.Tensor:
+    return t.fill_(float("nan"))
+
+
+def _page_out(x: torch.Tensor, live: torch.Tensor, table: torch.Tensor, pages: int,
+              page_rows: int) -> torch.Tensor:
+    """Scatter capacity rows x [B, H, cap, w] into a pool of ``pages`` pages
+    through ``table``; rows at or past each sequence's ``live`` count, and
+    pages no sequence maps, hold NaN."""
+    B, H, cap, w = x.shape
+    n = table.shape[1]
+    pool = _nan_fill(torch.empty((pages, H, page_rows, w), dtype=x.dtype, device=x.device))
+    if cap == 0 or n == 0:
+        return pool
+    padded = _nan_fill(torch.empty((B, H, n * page_rows, w), dtype=x.dtype, device=x.device))
+    rows = torch.arange(cap, device=x.device)
+    keep = (rows[None, :] < live[:, None].to(x.device)).view(B, 1, cap, 1)
+    padded[:, :, :cap] = torch.where(keep, x, torch.full_like(x, float("nan")))
+    blocks = padded.view(B, H, n, page_rows, w).permute(0, 2, 1, 3, 4).reshape(B * n, H,
+                                                                                 page_rows, w)
+    pool[table.reshape(-1).to(torch.int64).to(x.device)] = blocks
+    return pool
+
+
+def make_paged(inp: LayerInputs, step: StepInputs, *, page_rows: int, base_seed: int = 0,
+               spare: int = 3, extra_width: int = 1) -> PagedCache:
+    """Page out ``inp``'s capacity arrays: each sequence gets
+    ceil(capacity / page_rows) pages per segment, at page ids drawn as a
+    seeded permutation of a pool with ``spare`` more pages than needed.
+    Rows past a sequence's live length (lengths clamped to the capacity,
+    as the kernels clamp them) and unmapped pages hold NaN, so reading any
+    of them would show.  Tables get ``extra_width`` more columns, set to -1."""
+    wl = inp.workload
+    B = wl.batch
+    ncap, wcap = inp.num_beacons, inp.raw_window
+    nbp, nrp = -(-ncap // page_rows), -(-wcap // page_rows)
+    ss = np.random.SeedSequence([base_seed, wl.index, inp.layer, _IDS["pages"], page_rows])
+    rng = np.random.default_rng(ss)
+
+    def table(need):
+        pages = B * need + (spare if need else 0)
+        ids = rng.permutation(pages)[:B * need].reshape(B, need).astype(np.int32)
+        full = np.full((B, need + extra_width if need else 0), -1, dtype=np.int32)
+        full[:, :need] = ids
+        return pages, torch.from_numpy(full).to(inp.q.device)
+
+    bpages, bt = table(nbp)
+    rpages, rt = table(nrp)
+    nb_live = step.num_beacons.clamp(0, ncap)
+    w_live = step.raw_len.clamp(0, wcap)
+    return PagedCache(
+        page_rows,
+        _page_out(inp.C_K, nb_live, bt[:, :nbp], bpages, page_rows),
+        _page_out(inp.C_V, nb_live, bt[:, :nbp], bpages, page_rows),
+        _page_out(inp.K_raw, w_live, rt[:, :nrp], rpages, page_rows),
+        _page_out(inp.V_raw, w_live, rt[:, :nrp], rpages, page_rows),
+        bt, rt)
 
 
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:

@@ -16,6 +16,7 @@ Tolerances (floating point; nothing here decides an integer):
 
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -166,6 +167,22 @@ def gather_units(out, lse, wl, units):
     return got, got_lse
 
 
+def ragged_workload(dtype="bf16", B=8, Hkv=2, G=4, nb=1000, w=300, r=64, sigma=1.0, theta=5e5,
+                    context=32768, index=95):
+    """A small workload for ragged and paged tests: capacities nb, w."""
+    return dataclasses.replace(
+        synth.get_workload("c2"), name="ragged", index=index, batch=B, num_q_heads=Hkv * G,
+        num_kv_heads=Hkv, num_beacons=nb, raw_window=w, ranks=(r,), dtype=dtype, sigma=sigma,
+        rope_theta=theta, context=context)
+
+
+def ragged_edge_cases(nb, w):
+    """Sequence index -> (live beacons, live raw rows): no rows, full (the
+    new token is attended but not stored), beyond the capacity (clamped),
+    one row."""
+    return {0: (0, 0), 1: (nb, w), 2: (nb + 7, -5), 3: (1, 1)}
+
+
 def run_gpu_ragged(inp: synth.LayerInputs, step: synth.StepInputs, *, append: bool = True,
                    lengths: bool = True, num_splits: int = 0, device="cuda"):
     """slimkv_decode_attn_ragged on ``inp`` (capacity-sized arrays) and
@@ -229,6 +246,19 @@ def storage_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().to(torch.float64).numpy()
 
 
+def _key_ulps(got, exp, dtype, where) -> int:
+    """Elements of a stored key that differ from the oracle's (each by at
+    most one ulp of the storage dtype, asserted)."""
+    diff = got != exp
+    if diff.any():
+        ulp = np.abs(np.spacing(exp.astype(np.float32)).astype(np.float64))
+        if dtype == torch.bfloat16:
+            ulp = ulp * 65536.0
+        assert np.all(np.abs(got - exp)[diff] <= ulp[diff] * 1.0001), \
+            f"stored key of {where} off by more than one ulp"
+    return int(diff.sum())
+
+
 def assert_new_rows(K_after, V_after, K_before, V_before, step, k_app, units=None):
     """The call wrote exactly the new token's rows (row raw_len[b] of each
     unit whose window has room): keys equal the oracle's rotated, rounded
@@ -248,15 +278,8 @@ def assert_new_rows(K_after, V_after, K_before, V_before, step, k_app, units=Non
         if w >= wcap:
             continue
         mask[b, h, w] = True
-        got, exp = Ka[b, h, w], k_app[(b, h)] if isinstance(k_app, dict) else k_app[b, h]
-        diff = got != exp
-        if diff.any():
-            ulp = np.abs(np.spacing(exp.astype(np.float32)).astype(np.float64))
-            if K_after.dtype == torch.bfloat16:
-                ulp = ulp * 65536.0
-            assert np.all(np.abs(got - exp)[diff] <= ulp[diff] * 1.0001), \
-                f"stored key of ({b}, {h}) off by more than one ulp"
-            off_by_ulp += int(diff.sum())
+        exp = k_app[(b, h)] if isinstance(k_app, dict) else k_app[b, h]
+        off_by_ulp += _key_ulps(Ka[b, h, w], exp, K_after.dtype, (b, h))
         compared += d
         assert np.array_equal(Va[b, h, w], vnew[b, h]), f"stored value of ({b}, {h})"
     assert off_by_ulp <= max(1, compared // 10000), f"{off_by_ulp} of {compared} key elements"
@@ -271,3 +294,85 @@ def assert_new_rows(K_after, V_after, K_before, V_before, step, k_app, units=Non
     print(f"[parity] new rows: {int(mask.sum())} written, {off_by_ulp} key elements one ulp off",
           flush=True)
 
+
+
+def run_gpu_paged(inp: synth.LayerInputs, step: synth.StepInputs, pc: synth.PagedCache, *,
+                  append: bool = True, lengths: bool = True, num_splits: int = 0,
+                  beacon_table=None, raw_table=None, device="cuda"):
+    """slimkv_decode_attn_paged on ``pc`` (the pages of ``inp``'s capacity
+    arrays) and ``step``; tables default to pc's.  The raw pools are cloned
+    first (the call writes the new rows); returns (out, lse, K pool, V pool)
+    on the host."""
+    wl = inp.workload
+    g = inp.to(device)
+    st = step.to(device)
+    ncap, wcap = inp.num_beacons, inp.raw_window
+    bt = (pc.beacon_table if beacon_table is None else beacon_table).to(device)
+    rt = (pc.raw_table if raw_table is None else raw_table).to(device)
+    CK, CV = pc.C_K.to(device), pc.C_V.to(device)
+    K, V = pc.K_raw.to(device).clone(), pc.V_raw.to(device).clone()
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=num_splits)
+    pages = lda.make_pages(page_rows=pc.page_rows, beacon_table=bt if ncap else None,
+                           raw_table=rt if wcap else None, beacon_pages=pc.beacon_pages,
+                           raw_pages=pc.raw_pages)
+    out, lse = lda.alloc_outputs(prob, device)
+    ws = lda.alloc_workspace(prob, lda.SLIMKV_OP_LATENT_RAGGED, device)
+    lda.slimkv_decode_attn_paged(prob, pages, g.q, g.q_pos, g.U_K, g.U_V,
+                                 CK if ncap else None, CV if ncap else None,
+                                 K if wcap else None, V if wcap else None,
+                                 st.num_beacons if lengths else None,
+                                 st.raw_len if lengths else None,
+                                 st.k_new if append else None, st.v_new if append else None,
+                                 out, lse, ws)
+    torch.cuda.synchronize()
+    return (out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu())
+
+
+def storage_bits(t: torch.Tensor) -> np.ndarray:
+    """The bit patterns of a bf16 or fp32 tensor (NaNs compare equal)."""
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy()
+
+
+def assert_paged_writes(K_after, V_after, pc: synth.PagedCache, step, k_app, wcap: int,
+                        raw_table=None, units=None):
+    """The paged call wrote exactly the new token's rows -- row raw_len[b] of
+    each unit whose window has room, in the page the raw table gives for it
+    (none if that id is out of range) -- with the oracle's key (as in
+    assert_new_rows) and v_new, checked for ``units`` (default all); every
+    other element of both pools, NaN fillers of unused rows and pages
+    included, keeps its bits.  k_app None: no new token, nothing written."""
+    table = (pc.raw_table if raw_table is None else raw_table).cpu().numpy()
+    PR = pc.page_rows
+    Ka, Va = storage_to_f64(K_after), storage_to_f64(V_after)
+    vnew = storage_to_f64(step.v_new)
+    raw_len = step.raw_len.cpu().numpy()
+    B, Hkv = vnew.shape[0], vnew.shape[1]
+    check = set(units or [(b, h) for b in range(B) for h in range(Hkv)])
+    mask = np.zeros(K_after.shape[:3], dtype=bool)
+    off_by_ulp = compared = 0
+    for b in range(B if k_app is not None else 0):
+        w = int(np.clip(raw_len[b], 0, wcap))
+        if w >= wcap:
+            continue
+        pid = int(table[b, w // PR])
+        if not 0 <= pid < K_after.shape[0]:
+            continue
+        r = w % PR
+        mask[pid, :, r] = True
+        for h in range(Hkv):
+            if (b, h) in check:
+                exp = k_app[(b, h)] if isinstance(k_app, dict) else k_app[b, h]
+                off_by_ulp += _key_ulps(Ka[pid, h, r], exp, K_after.dtype, (b, h))
+                compared += Ka.shape[-1]
+                assert np.array_equal(Va[pid, h, r], vnew[b, h]), f"stored value of ({b}, {h})"
+    assert off_by_ulp <= max(1, compared // 10000), f"{off_by_ulp} of {compared} key elements"
+    keep = ~mask
+    assert np.array_equal(storage_bits(K_after)[keep], storage_bits(pc.K_raw)[keep]), \
+        "K pool: other rows written"
+    assert np.array_equal(storage_bits(V_after)[keep], storage_bits(pc.V_raw)[keep]), \
+        "V pool: other rows written"
+    print(f"[parity] paged new rows: {int(mask.sum())} written, {off_by_ulp} key elements one "
+          f"ulp off", flush=True)

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 4
+    assert lda.slimkv_abi_version() == 5
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -222,6 +222,87 @@ def test_ragged_checks(lib):
     assert _call_ragged(lib, _problem(), ptrs=dict(ws=0x4000000)) == ALIAS
     # without one it is only read, and may not overlap the outputs either
     assert _call_ragged(lib, _problem(), ptrs=dict(k_new=None, v_new=None, out=0x3000000)) == ALIAS
+
+
+def test_pages_struct_layout():
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct slimkv_pages \{(.*?)\} slimkv_pages;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(?:const )?(int32_t\*?|int32_t)\s+(\w+);", body, re.M)
+    assert [f for _, f in fields] == [f for f, _ in binding.slimkv_pages._fields_]
+    assert ctypes.sizeof(binding.slimkv_pages) == 40
+    assert binding.slimkv_pages.beacon_table.offset == 24
+
+
+def _call_paged(lib, prob, pages, *, ptrs=None, ws_bytes=16):
+    """slimkv_decode_attn_paged with fake device addresses (every case fails
+    validation before any HIP call: at the latest, the 16-byte workspace is
+    too small)."""
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, nb=0x210000, raw=0x220000,
+             k_new=0x230000, v_new=0x240000, out=0x5000000, lse=0x6000000, ws=0x7000000)
+    p.update(ptrs or {})
+    v = {k: (None if x is None else ctypes.c_void_p(x)) for k, x in p.items()}
+    pg = ctypes.byref(pages) if pages is not None else None
+    return lib.slimkv_decode_attn_paged(ctypes.byref(prob), pg, v["q"], v["q_pos"], v["U_K"],
+                                        v["U_V"], v["C_K"], v["C_V"], v["K_raw"], v["V_raw"],
+                                        v["nb"], v["raw"], v["k_new"], v["v_new"], v["out"],
+                                        v["lse"], v["ws"], ws_bytes, None)
+
+
+def _pages(**over):
+    base = dict(page_rows=64, beacon_pages=4, raw_pages=4, beacon_table_width=1,
+                raw_table_width=1, reserved=0, beacon_table=0x250000, raw_table=0x260000)
+    base.update(over)
+    return binding.slimkv_pages(**base)
+
+
+def test_paged_checks(lib):
+    prob = _problem()  # 64 beacons, 32 raw rows: one page each at 64 rows a page
+    assert _call_paged(lib, prob, _pages()) == WS  # every check passes; workspace too small
+    assert _call_paged(lib, prob, None) == NULL
+    for rows in (32, 96, 1 << 17, 0, -64):
+        assert _call_paged(lib, prob, _pages(page_rows=rows)) == SHAPE, rows
+    # the largest page (beacon pools of one page, 8 MiB each here)
+    assert _call_paged(lib, _problem(raw_window=0),
+                       _pages(page_rows=1 << 16, beacon_pages=1, raw_table=None, raw_pages=0),
+                       ptrs=dict(K_raw=None, V_raw=None)) == WS
+    # pools are pages x H_kv x page_rows x width: 32 pages of 2 x 4096 x 32 x 2 B end
+    # where out starts, 33 run into it
+    at = dict(K_raw=None, V_raw=None, C_V=0x8000000, out=0x1000000 + 32 * 2 * 4096 * 32 * 2)
+    for pages, status in ((32, WS), (33, ALIAS)):
+        assert _call_paged(lib, _problem(raw_window=0),
+                           _pages(page_rows=4096, beacon_pages=pages, raw_table=None,
+                                  raw_pages=0), ptrs=at) == status
+    assert _call_paged(lib, prob, _pages(reserved=1)) == SHAPE
+    assert _call_paged(lib, prob, _pages(beacon_table=None)) == NULL
+    assert _call_paged(lib, prob, _pages(raw_table=None)) == NULL
+    assert _call_paged(lib, prob, _pages(beacon_table=0x250002)) == ALIGN
+    assert _call_paged(lib, prob, _pages(beacon_table_width=0)) == SHAPE
+    assert _call_paged(lib, prob, _pages(raw_pages=0)) == SHAPE
+    # a segment without capacity needs no table, pools or pages
+    assert _call_paged(lib, _problem(num_beacons=0), _pages(beacon_table=None, beacon_pages=0,
+                                                            beacon_table_width=0),
+                       ptrs=dict(U_K=None, U_V=None, C_K=None, C_V=None)) == WS
+    assert _call_paged(lib, _problem(raw_window=0), _pages(raw_table=None, raw_pages=0),
+                       ptrs=dict(K_raw=None, V_raw=None)) == WS
+    # two pages of 64 rows for 65..128 rows
+    assert _call_paged(lib, _problem(num_beacons=65), _pages()) == SHAPE
+    assert _call_paged(lib, _problem(num_beacons=65), _pages(beacon_table_width=2)) == WS
+    # the tables of a sequence are staged on chip: at most 4096 entries
+    big = _problem(num_beacons=4096 * 64, raw_window=32)
+    assert _call_paged(lib, big, _pages(beacon_table_width=4096)) == UNSUP
+    assert _call_paged(lib, _problem(num_beacons=4095 * 64),
+                       _pages(beacon_table_width=4095)) == WS
+    # the raw pools are written with a new token (4 pages x 2 heads x 64 rows x 256 B)
+    assert _call_paged(lib, prob, _pages(), ptrs=dict(k_new=0x3000000 + 4 * 32768 - 16)) == ALIAS
+    assert _call_paged(lib, prob, _pages(), ptrs=dict(k_new=0x3000000 + 4 * 32768)) == WS
+    assert _call_paged(lib, prob, _pages(raw_pages=5),
+                       ptrs=dict(k_new=0x3000000 + 4 * 32768)) == ALIAS
+    # outputs must not overlap the tables
+    assert _call_paged(lib, prob, _pages(), ptrs=dict(lse=0x260000 - 4)) == ALIAS
+    assert _call_paged(lib, prob, _pages(raw_table=0x6000000 + 8)) == ALIAS
+    # the same flags and batch limits as the ragged call
+    assert _call_paged(lib, _problem(batch=1025), _pages()) == UNSUP
 
 
 def test_reconstruct_rope_checks(lib):

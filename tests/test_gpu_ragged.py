@@ -2,33 +2,17 @@
 capacity-sized arrays, and the decode step's new token (attended as a rotated
 raw row, and stored when the window has room)."""
 
-import dataclasses
-
 import numpy as np
 import pytest
 import torch
 
-import latent_decode_attention_amd as lda
 import synth
-from parity_util import (assert_new_rows, assert_parity, gather_units, note, oracle_layer,
-                         oracle_ragged, oracle_ragged_units, run_gpu, run_gpu_ragged,
-                         sample_units)
+from parity_util import assert_new_rows, assert_parity, gather_units, note, oracle_layer
+from parity_util import oracle_ragged, oracle_ragged_units, run_gpu, run_gpu_ragged, sample_units
+from parity_util import ragged_edge_cases as edge_cases
+from parity_util import ragged_workload as custom
 
 pytestmark = pytest.mark.gpu
-
-
-def custom(dtype="bf16", B=8, Hkv=2, G=4, nb=1000, w=300, r=64, sigma=1.0, theta=5e5,
-           context=32768, index=95):
-    return dataclasses.replace(
-        synth.get_workload("c2"), name="ragged", index=index, batch=B, num_q_heads=Hkv * G,
-        num_kv_heads=Hkv, num_beacons=nb, raw_window=w, ranks=(r,), dtype=dtype, sigma=sigma,
-        rope_theta=theta, context=context)
-
-
-# sequence index -> (live beacons, live raw rows): no rows, full (the new
-# token is attended but not stored), beyond the capacity (clamped), one row
-def edge_cases(nb, w):
-    return {0: (0, 0), 1: (nb, w), 2: (nb + 7, -5), 3: (1, 1)}
 
 
 def check_ragged(wl, *, rank_v=None, append=True, lengths=True, num_splits=0, fixed=None,
