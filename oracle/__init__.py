@@ -6,7 +6,8 @@ never imports the library: the two share no code.
 
 ``decode`` runs the plain C implementation in ``slimkv_oracle.c`` (double
 precision throughout, OpenMP over (batch, kv head) units); ``decode_ragged``
-the same with per-sequence lengths and the decode step's new token.  Its definition
+the same with per-sequence lengths and the decode step's new token;
+``decode_chunk`` a chunk of several query tokens per sequence.  Its definition
 follows page "Can SlimKV compress KV cache jointly across tokens and
 features", section "Latent-space attention removes the rebuild step": the
 rotated query is projected into each KV head's beacon latent space, scored
@@ -77,6 +78,11 @@ def load(path=LIBRARY) -> ctypes.CDLL:
         if hasattr(lib, "slimkv_oracle_decode_ragged"):
             lib.slimkv_oracle_decode_ragged.restype = ctypes.c_int
             lib.slimkv_oracle_decode_ragged.argtypes = [ctypes.POINTER(_Problem)] + [
+                ctypes.c_void_p] * 12 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "slimkv_oracle_decode_chunk"):
+            lib.slimkv_oracle_decode_chunk.restype = ctypes.c_int
+            lib.slimkv_oracle_decode_chunk.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int] + [
                 ctypes.c_void_p] * 12 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.slimkv_oracle_max_threads.restype = ctypes.c_int
@@ -199,6 +205,57 @@ def decode_ragged(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: i
 
     rc = load(library).slimkv_oracle_decode_ragged(
         ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+        ptr(K_raw), ptr(V_raw), ptr(nbl), ptr(rwl), ptr(k_new), ptr(v_new), ptr(unit_arr),
+        n_units, ptr(out), ptr(lse), ptr(k_app), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out, lse, k_app
+
+
+def decode_chunk(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: int, scale: float,
+                 rope_theta: float, num_beacons=None, raw_len=None, k_new=None, v_new=None,
+                 units=None, threads: int = 0, library: pathlib.Path = LIBRARY):
+    """fp64 attention of a chunk of Q query tokens per sequence (speculative
+    decoding, chunked prefill) over a ragged cache.
+
+    q [B, Q, H_q, d]: token t of sequence b at position q_pos[b] + t.  The
+    cache arrays, lengths and their clamping are those of ``decode_ragged``.
+    ``k_new``, ``v_new`` ([B, Q, H_kv, d], both or neither): the chunk's
+    tokens; token t's query attends over the live cache rows and new tokens
+    0..t, each key rotated at its own position and rounded to the storage
+    precision.  Returns (out [B, Q, H_q, d], lse [B, Q, H_q], k_app
+    [B, Q, H_kv, d]) in float64 (k_app NaN without new tokens).
+    """
+    q = np.ascontiguousarray(q)
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported storage dtype {dt}")
+    B, Q, Hq, d = q.shape
+    q_pos = _arr(q_pos, np.dtype(np.int32))
+    ncap = 0 if C_K is None else int(np.shape(C_K)[2])
+    wcap = 0 if K_raw is None else int(np.shape(K_raw)[2])
+    rk = int(np.shape(U_K)[2]) if U_K is not None else 0
+    rv = int(np.shape(U_V)[2]) if U_V is not None else 0
+    U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new = (
+        _arr(x, dt) for x in (U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new))
+    nbl = _arr(num_beacons, np.dtype(np.int32))
+    rwl = _arr(raw_len, np.dtype(np.int32))
+    prob = _Problem(B, Hq, num_kv_heads, d, ncap, rk, rv, wcap, float(scale), float(rope_theta),
+                    _DTYPE[dt])
+    out = np.full((B, Q, Hq, d), np.nan, dtype=np.float64)
+    lse = np.full((B, Q, Hq), np.nan, dtype=np.float64)
+    k_app = np.full((B, Q, num_kv_heads, d), np.nan, dtype=np.float64)
+    if units is None:
+        unit_arr, n_units = None, 0
+    else:
+        unit_arr = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+        n_units = unit_arr.shape[0]
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = load(library).slimkv_oracle_decode_chunk(
+        ctypes.byref(prob), int(Q), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
         ptr(K_raw), ptr(V_raw), ptr(nbl), ptr(rwl), ptr(k_new), ptr(v_new), ptr(unit_arr),
         n_units, ptr(out), ptr(lse), ptr(k_app), int(threads))
     if rc != 0:

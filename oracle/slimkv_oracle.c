@@ -37,6 +37,9 @@
  * that computation: per-sequence numbers of live beacon and raw rows in
  * capacity-sized arrays, and the step's new token, whose key is rotated at
  * the query position and attended as one more raw row (see oracle_unit).
+ * slimkv_oracle_decode_chunk takes a chunk of several query tokens per
+ * sequence, each attending causally to the chunk's new tokens (see
+ * oracle_chunk_unit).
  */
 #include <math.h>
 #include <stdint.h>
@@ -402,6 +405,204 @@ int slimkv_oracle_decode_ragged(const oracle_problem* p, const void* q,
       }
       oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b, raw_len,
                   k_new, v_new, NULL, out, lse, k_app, work);
+    }
+    free(work);
+  }
+  if (failed == 1) return ORACLE_NO_MEMORY;
+  if (failed == 2) return ORACLE_BAD_SHAPE;
+  return ORACLE_OK;
+}
+
+/*
+ * Multi-token queries against the compressed cache: a chunk of Q tokens per
+ * sequence, as when speculative decoding checks several drafted tokens in
+ * one pass or a prompt is fed Q tokens at a time (the query side of the
+ * same attention; page "Can SlimKV compress KV cache jointly across tokens
+ * and features", section "Latent-space attention removes the rebuild
+ * step").  Token t of sequence b sits at position q_pos[b] + t.  Each of
+ * its G query heads is rotated at that position and attends, under one
+ * softmax, over the live beacon rows, the live raw rows and the chunk's new
+ * tokens 0 .. t -- token u's key rotated at its own position q_pos[b] + u
+ * and rounded like a cache row -- but not over the chunk's later tokens.
+ * Without new tokens every query of the chunk attends over the cache rows
+ * only.  Lengths are clamped as in oracle_unit.  k_app (if given) receives
+ * token u's rounded key, the row the cache would store at w_b + u.
+ * Layouts: q, out [B, Q, H_q, d]; lse [B, Q, H_q]; k_new, v_new, k_app
+ * [B, Q, H_kv, d].  With Q = 1 this is oracle_unit's computation.
+ */
+static void oracle_chunk_unit(const oracle_problem* p, int ntok, int b, int h, const void* q,
+                              const int32_t* q_pos, const void* U_K, const void* U_V,
+                              const void* C_K, const void* C_V, const void* K_raw,
+                              const void* V_raw, const int32_t* nb_len, const int32_t* raw_len,
+                              const void* k_new, const void* v_new, double* out, double* lse,
+                              double* k_app, double* work) {
+  const int d = p->head_dim, half = p->head_dim / 2;
+  const int H = p->num_kv_heads, Hq = p->num_q_heads, G = Hq / H;
+  const int ncap = p->num_beacons, wcap = p->raw_window;
+  const int rk = p->rank_k, rv = p->rank_v;
+  const int dt = p->dtype;
+  int nb = nb_len ? nb_len[b] : ncap, w = raw_len ? raw_len[b] : wcap;
+  nb = nb < 0 ? 0 : (nb > ncap ? ncap : nb);
+  w = w < 0 ? 0 : (w > wcap ? wcap : w);
+  const int app = k_new != NULL;
+
+  double* qrot = work;                       /* [d]             rotated query     */
+  double* qlat = qrot + d;                   /* [rk]            latent query      */
+  double* sc = qlat + rk;                    /* [nb + w + Q]    scores, weights   */
+  double* vl = sc + (size_t)nb + w + ntok;   /* [rv]            latent value sum  */
+  double* vr = vl + rv;                      /* [d]             raw value sum     */
+  double* kt = vr + d;                       /* [Q * d]         rotated new keys  */
+
+  const size_t unit = (size_t)b * H + h;
+  const size_t ck0 = unit * (size_t)ncap * rk, cv0 = unit * (size_t)ncap * rv;
+  const size_t kr0 = unit * (size_t)wcap * d;
+  const size_t uk0 = (size_t)h * d * rk, uv0 = (size_t)h * d * rv;
+
+  /* the chunk's new keys, token u rotated at q_pos[b] + u and rounded */
+  for (int u = 0; u < ntok && app; ++u) {
+    const size_t k0 = (((size_t)b * ntok + u) * H + h) * d;
+    const double tpos = (double)q_pos[b] + (double)u;
+    for (int i = 0; i < half; ++i) {
+      const double ang = tpos * pow(p->rope_theta, -2.0 * (double)i / (double)d);
+      const double c = cos(ang), sn = sin(ang);
+      const double x1 = widen(k_new, dt, k0 + i), x2 = widen(k_new, dt, k0 + i + half);
+      kt[(size_t)u * d + i] = narrow(x1 * c - x2 * sn, dt);
+      kt[(size_t)u * d + i + half] = narrow(x2 * c + x1 * sn, dt);
+    }
+    if (k_app)
+      for (int i = 0; i < d; ++i) k_app[k0 + i] = kt[(size_t)u * d + i];
+  }
+
+  for (int t = 0; t < ntok; ++t) {
+    const double qpos = (double)q_pos[b] + (double)t;
+    const int seen = app ? t + 1 : 0; /* new tokens this query attends to */
+    const size_t n = (size_t)nb + (size_t)w + (size_t)seen;
+    for (int g = 0; g < G; ++g) {
+      const int hq = h * G + g;
+      const size_t row = ((size_t)b * ntok + t) * Hq + hq;
+      const size_t q0 = row * d;
+      if (n == 0) {
+        for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;
+        if (lse) lse[row] = -INFINITY;
+        continue;
+      }
+      /* rotate the query at its token's position, then project it */
+      for (int i = 0; i < half; ++i) {
+        const double ang = qpos * pow(p->rope_theta, -2.0 * (double)i / (double)d);
+        const double c = cos(ang), sn = sin(ang);
+        const double x1 = widen(q, dt, q0 + i), x2 = widen(q, dt, q0 + i + half);
+        qrot[i] = x1 * c - x2 * sn;
+        qrot[i + half] = x2 * c + x1 * sn;
+      }
+      for (int k = 0; k < rk; ++k) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qrot[i] * widen(U_K, dt, uk0 + (size_t)i * rk + k);
+        qlat[k] = acc;
+      }
+      /* scores: latent beacons, rotated raw keys, new tokens 0 .. t */
+      for (int j = 0; j < nb; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < rk; ++k) acc += qlat[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+        sc[j] = p->scale * acc;
+      }
+      for (int j = 0; j < w; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qrot[i] * widen(K_raw, dt, kr0 + (size_t)j * d + i);
+        sc[nb + j] = p->scale * acc;
+      }
+      for (int u = 0; u < seen; ++u) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qrot[i] * kt[(size_t)u * d + i];
+        sc[nb + w + u] = p->scale * acc;
+      }
+      /* one softmax over all of them */
+      double mx = -INFINITY;
+      for (size_t j = 0; j < n; ++j) mx = sc[j] > mx ? sc[j] : mx;
+      double den = 0.0;
+      for (size_t j = 0; j < n; ++j) {
+        sc[j] = exp(sc[j] - mx);
+        den += sc[j];
+      }
+      for (size_t j = 0; j < n; ++j) sc[j] /= den;
+      /* value sums (latent for beacons), then the lift */
+      for (int k = 0; k < rv; ++k) vl[k] = 0.0;
+      for (int j = 0; j < nb; ++j)
+        for (int k = 0; k < rv; ++k) vl[k] += sc[j] * widen(C_V, dt, cv0 + (size_t)j * rv + k);
+      for (int i = 0; i < d; ++i) vr[i] = 0.0;
+      for (int j = 0; j < w; ++j)
+        for (int i = 0; i < d; ++i) vr[i] += sc[nb + j] * widen(V_raw, dt, kr0 + (size_t)j * d + i);
+      for (int u = 0; u < seen; ++u) {
+        const size_t v0 = (((size_t)b * ntok + u) * H + h) * d;
+        for (int i = 0; i < d; ++i) vr[i] += sc[nb + w + u] * widen(v_new, dt, v0 + i);
+      }
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * vl[k];
+        out[q0 + i] = acc + vr[i];
+      }
+      if (lse) lse[row] = mx + log(den);
+    }
+  }
+}
+
+/*
+ * Multi-token counterpart of slimkv_oracle_decode_ragged (see
+ * oracle_chunk_unit): num_tokens = Q >= 1 query tokens per sequence.
+ */
+int slimkv_oracle_decode_chunk(const oracle_problem* p, int num_tokens, const void* q,
+                               const int32_t* q_pos, const void* U_K, const void* U_V,
+                               const void* C_K, const void* C_V, const void* K_raw,
+                               const void* V_raw, const int32_t* num_beacons_b,
+                               const int32_t* raw_len, const void* k_new, const void* v_new,
+                               const int32_t* units, int64_t n_units, double* out, double* lse,
+                               double* k_app, int threads) {
+  if (!p || !q || !q_pos || !out || num_tokens < 1) return ORACLE_BAD_SHAPE;
+  if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
+    return ORACLE_BAD_DTYPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 ||
+      p->num_q_heads % p->num_kv_heads != 0 || p->head_dim < 2 || p->head_dim % 2 ||
+      p->num_beacons < 0 || p->raw_window < 0)
+    return ORACLE_BAD_SHAPE;
+  if (p->num_beacons > 0 && (p->rank_k < 1 || p->rank_v < 1 || !U_K || !U_V || !C_K || !C_V))
+    return ORACLE_BAD_SHAPE;
+  if (p->raw_window > 0 && (!K_raw || !V_raw)) return ORACLE_BAD_SHAPE;
+  if ((k_new == NULL) != (v_new == NULL)) return ORACLE_BAD_SHAPE;
+
+  const int64_t all = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t count = units ? n_units : all;
+  const int rk = p->num_beacons > 0 ? p->rank_k : 0;
+  const int rv = p->num_beacons > 0 ? p->rank_v : 0;
+  const size_t work_len = (3 + (size_t)num_tokens) * (size_t)p->head_dim + rk + rv +
+                          (size_t)p->num_beacons + p->raw_window + num_tokens;
+  oracle_problem pp = *p;
+  pp.rank_k = rk;
+  pp.rank_v = rv;
+
+  int failed = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel
+  {
+    double* work = (double*)malloc(work_len * sizeof(double));
+    if (!work) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < count; ++u) {
+      if (!work) continue;
+      int b = units ? units[2 * u] : (int)(u / p->num_kv_heads);
+      int h = units ? units[2 * u + 1] : (int)(u % p->num_kv_heads);
+      if (b < 0 || b >= p->batch || h < 0 || h >= p->num_kv_heads) {
+#pragma omp atomic write
+        failed = 2;
+        continue;
+      }
+      oracle_chunk_unit(&pp, num_tokens, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                        num_beacons_b, raw_len, k_new, v_new, out, lse, k_app, work);
     }
     free(work);
   }

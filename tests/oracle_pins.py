@@ -449,6 +449,156 @@ def pin_beacon_rope_relative(library):
     assert np.max(np.abs(out2 - out0)) > 1e-6, "beacon positions have no effect"
 
 
+# ---------------------------------------------------------------------------
+# Chunks of several query tokens per sequence (oracle.decode_chunk).
+
+
+def chunk_problem(seed, *, Q=3, room=True, **shape):
+    """A ragged problem with Q query tokens per sequence and Q new tokens;
+    room: every sequence's window has space for the whole chunk."""
+    p = ragged_problem(seed, append=False, **shape)
+    rng = np.random.default_rng(seed + 2000)
+    B, Hq, d = p["q"].shape
+    Hkv, wcap = p["num_kv_heads"], p["K_raw"].shape[2]
+    p["q"] = rng.standard_normal((B, Q, Hq, d))
+    p["k_new"] = rng.standard_normal((B, Q, Hkv, d))
+    p["v_new"] = rng.standard_normal((B, Q, Hkv, d))
+    if room:
+        p["raw_len"] = rng.integers(0, wcap - Q + 1, size=B).astype(np.int32)
+    return p
+
+
+def run_chunk(p, library, **over):
+    args = dict(p)
+    args.update(over)
+    ncap = args["C_K"].shape[2]
+    wcap = args["K_raw"].shape[2]
+    return oracle.decode_chunk(
+        args["q"], args["q_pos"], args["U_K"], args["U_V"],
+        args["C_K"] if ncap else None, args["C_V"] if ncap else None,
+        args["K_raw"] if wcap else None, args["V_raw"] if wcap else None,
+        num_kv_heads=args["num_kv_heads"], scale=args["scale"], rope_theta=args["theta"],
+        num_beacons=args.get("num_beacons"), raw_len=args.get("raw_len"),
+        k_new=args.get("k_new"), v_new=args.get("v_new"), library=library)
+
+
+def chunk_reference(p, b, t):
+    """Token t of sequence b: its live beacon rows rebuilt to full keys and
+    values, its live raw rows, and the chunk's tokens 0..t (token u's key
+    rotated at q_pos[b] + u); ordinary attention of the query rotated at
+    q_pos[b] + t.  Returns (out [H_q, d], lse [H_q])."""
+    Hkv = p["num_kv_heads"]
+    G = p["q"].shape[2] // Hkv
+    nbc = int(np.clip(p["num_beacons"][b], 0, p["C_K"].shape[2]))
+    wc = int(np.clip(p["raw_len"][b], 0, p["K_raw"].shape[2]))
+    pos = int(p["q_pos"][b])
+    K = [np.einsum("hjr,hdr->hjd", p["C_K"][b, :, :nbc], p["U_K"]), p["K_raw"][b, :, :wc]]
+    V = [np.einsum("hjr,hdr->hjd", p["C_V"][b, :, :nbc], p["U_V"]), p["V_raw"][b, :, :wc]]
+    for u in range(t + 1):
+        K.append(rope_complex(p["k_new"][b, u], np.full(Hkv, pos + u), p["theta"])[:, None, :])
+        V.append(p["v_new"][b, u][:, None, :])
+    K = np.concatenate(K, axis=1)[None]
+    V = np.concatenate(V, axis=1)[None]
+    q_rot = rope_complex(p["q"][b:b + 1, t], np.array([[pos + t]]), p["theta"])
+    out, lse = sdpa_reference(q_rot, K, V, p["scale"], G)
+    return out[0], lse[0]
+
+
+def pin_chunk_reference(library):
+    """Each token of a chunk against plain attention over the cache rows and
+    the chunk's tokens up to it; full windows included (the chunk is
+    attended whether or not it can be stored)."""
+    for seed, shape in ((60, dict(B=4, Hkv=2, G=2, d=16, ncap=6, rk=4, rv=6, wcap=7)),
+                        (61, dict(B=2, Hkv=1, G=3, d=128, ncap=20, rk=32, rv=16, wcap=4,
+                                  theta=500000.0, q_pos=131060))):
+        p = chunk_problem(seed, Q=3, room=False, **shape)
+        p["raw_len"][0] = shape["wcap"]
+        p["num_beacons"][1] = 0
+        out, lse, _ = run_chunk(p, library)
+        for b in range(shape["B"]):
+            for t in range(3):
+                ref_out, ref_lse = chunk_reference(p, b, t)
+                _close(out[b, t], ref_out, what=f"chunk out, seq {b} token {t}")
+                _close(lse[b, t], ref_lse, what=f"chunk lse, seq {b} token {t}")
+
+
+def pin_chunk_single_token(library):
+    """A chunk of one token is the ragged decode step."""
+    p = chunk_problem(62, Q=1, room=False, B=5, Hkv=2, G=2, d=16, ncap=9, rk=4, rv=6, wcap=7)
+    out, lse, k_app = run_chunk(p, library)
+    r_out, r_lse, r_k = run_ragged(p, library, q=p["q"][:, 0], k_new=p["k_new"][:, 0],
+                                   v_new=p["v_new"][:, 0])
+    _close(out[:, 0], r_out, tol=1e-13, what="chunk of one: out")
+    _close(lse[:, 0], r_lse, tol=1e-13, what="chunk of one: lse")
+    _close(k_app[:, 0], r_k, tol=1e-14, what="chunk of one: stored key")
+
+
+def pin_chunk_sequential(library):
+    """A chunk equals its tokens decoded one after another, each step
+    appending its token to the raw window before the next (the window has
+    room for all of them)."""
+    for seed, shape in ((63, dict(B=4, Hkv=2, G=2, d=16, ncap=6, rk=4, rv=6, wcap=9)),
+                        (64, dict(B=3, Hkv=2, G=1, d=32, ncap=0, rk=4, rv=4, wcap=8))):
+        Q = 4
+        p = chunk_problem(seed, Q=Q, **shape)
+        out, lse, k_app = run_chunk(p, library)
+        K, V = p["K_raw"].copy(), p["V_raw"].copy()
+        for t in range(Q):
+            o, l_, k = run_ragged(p, library, q=p["q"][:, t], q_pos=(p["q_pos"] + t).astype(np.int32),
+                                  K_raw=K, V_raw=V, raw_len=(p["raw_len"] + t).astype(np.int32),
+                                  k_new=p["k_new"][:, t], v_new=p["v_new"][:, t])
+            _close(out[:, t], o, tol=1e-12, what=f"sequential out, token {t}")
+            _close(lse[:, t], l_, tol=1e-12, what=f"sequential lse, token {t}")
+            _close(k_app[:, t], k, tol=1e-14, what=f"sequential stored key, token {t}")
+            for b in range(shape["B"]):
+                K[b, :, p["raw_len"][b] + t] = k[b]
+                V[b, :, p["raw_len"][b] + t] = p["v_new"][b, t]
+
+
+def pin_chunk_causal(library):
+    """Token t sees the chunk's tokens up to t only: changing later tokens
+    leaves its output untouched, changing token t does not."""
+    p = chunk_problem(65, Q=4, B=3, Hkv=2, G=2, d=16, ncap=5, rk=4, rv=4, wcap=9)
+    out, lse, _ = run_chunk(p, library)
+    for t in range(3):
+        k2, v2 = p["k_new"].copy(), p["v_new"].copy()
+        k2[:, t + 1:] += 3.0
+        v2[:, t + 1:] -= 2.0
+        o2, l2, _ = run_chunk(p, library, k_new=k2, v_new=v2)
+        assert np.array_equal(o2[:, :t + 1], out[:, :t + 1]), f"token {t} sees later tokens"
+        assert np.array_equal(l2[:, :t + 1], lse[:, :t + 1])
+        assert np.max(np.abs(o2[:, t + 1:] - out[:, t + 1:])) > 1e-6, "later tokens ignored"
+
+
+def pin_chunk_without_new_tokens(library):
+    """Without new tokens each query of the chunk attends over the cache only,
+    at its own position."""
+    p = chunk_problem(66, Q=3, room=False, B=3, Hkv=2, G=2, d=16, ncap=6, rk=4, rv=4, wcap=5)
+    out, lse, k_app = run_chunk(p, library, k_new=None, v_new=None)
+    assert np.all(np.isnan(k_app))
+    for t in range(3):
+        o, l_, _ = run_ragged(p, library, q=p["q"][:, t], q_pos=(p["q_pos"] + t).astype(np.int32),
+                              k_new=None, v_new=None)
+        _close(out[:, t], o, tol=1e-13, what=f"no new tokens, token {t}")
+        _close(lse[:, t], l_, tol=1e-13, what=f"no new tokens lse, token {t}")
+
+
+def pin_chunk_rounding(library):
+    """bf16 storage: each new key is its rotation at its own position, rounded
+    once to bf16."""
+    p = chunk_problem(67, Q=3, room=False, B=2, Hkv=2, G=2, d=64, ncap=5, rk=16, rv=16, wcap=4,
+                      theta=500000.0, q_pos=70000)
+    bits = {}
+    for name in ("q", "U_K", "U_V", "C_K", "C_V", "K_raw", "V_raw", "k_new", "v_new"):
+        bits[name] = (p[name].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    pb = dict(p)
+    pb.update(bits)
+    _, _, k_app = run_chunk(pb, library)
+    pos = p["q_pos"][:, None, None] + np.arange(3)[None, :, None]
+    rot = rope_complex(oracle.bf16_to_f64(bits["k_new"]), pos, p["theta"])
+    assert np.array_equal(k_app, bf16_round(rot)), "chunk keys not rounded once to bf16"
+
+
 ALL_PINS = [
     pin_reconstruct_identity,
     pin_raw_only_rope_gqa,
@@ -465,4 +615,10 @@ ALL_PINS = [
     pin_append_rounding,
     pin_beacon_rope_reference,
     pin_beacon_rope_relative,
+    pin_chunk_reference,
+    pin_chunk_single_token,
+    pin_chunk_sequential,
+    pin_chunk_causal,
+    pin_chunk_without_new_tokens,
+    pin_chunk_rounding,
 ]

@@ -46,6 +46,18 @@ MUTANTS = {
     "beacon_key_rotated_backwards": ("acc += qr[i] * (kb[i] * c - kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c + kb[i] * sn);",
                                      "acc += qr[i] * (kb[i] * c + kb[i + half] * sn) + qr[i + half] * (kb[i + half] * c - kb[i] * sn);"),
     "beacon_key_at_query_position": ("double ang = (double)bpos[j] * inv_freq;", "double ang = (double)q_pos[b] * inv_freq;"),
+    "chunk_query_position_ignored": ("const double qpos = (double)q_pos[b] + (double)t;",
+                                     "const double qpos = (double)q_pos[b];"),
+    "chunk_keys_at_first_position": ("const double tpos = (double)q_pos[b] + (double)u;",
+                                     "const double tpos = (double)q_pos[b];"),
+    "chunk_future_tokens_visible": ("const int seen = app ? t + 1 : 0;",
+                                    "const int seen = app ? ntok : 0;"),
+    "chunk_token_excludes_itself": ("const int seen = app ? t + 1 : 0;",
+                                    "const int seen = app ? t : 0;"),
+    "chunk_values_of_first_token": ("const size_t v0 = (((size_t)b * ntok + u) * H + h) * d;",
+                                    "const size_t v0 = (((size_t)b * ntok + 0) * H + h) * d;"),
+    "chunk_rows_head_major": ("const size_t row = ((size_t)b * ntok + t) * Hq + hq;",
+                              "const size_t row = ((size_t)b * Hq + hq) * ntok + t;"),
     "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
                                "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
