@@ -59,6 +59,9 @@ def parse_args():
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
                     help="with --ragged: the cache in pages of ROWS rows (a power of two >= 64) "
                          "at shuffled page ids, through slimkv_decode_attn_paged")
+    ap.add_argument("--chunk", type=int, default=0, metavar="Q",
+                    help="only time the ragged serving step with Q query tokens per sequence "
+                         "(slimkv_decode_attn_chunk) and print its figures as one JSON line")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
                          "reduction, for scaling hardware byte counters and as a read ceiling")
@@ -139,6 +142,10 @@ def main():
     if args.ragged:
         print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps,
                                      page_rows=args.paged)), flush=True)
+        return
+    if args.chunk:
+        print(json.dumps(chunk_step(lda, synth, torch, dev, wl, layers, args.steps, args.chunk)),
+              flush=True)
         return
     probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
                                       rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
@@ -403,6 +410,58 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
         del paged, tables
     log(f"{'paged' if page_rows else 'ragged'} step: {res}")
     del ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens):
+    """The ragged serving step of ragged_step with a chunk of num_tokens
+    query tokens per sequence (e.g. drafted tokens checked in one pass):
+    every layer attends each token over the live rows and the chunk's tokens
+    up to it, and stores the tokens (slimkv_decode_attn_chunk).  Bytes: the
+    live rows, the tokens' keys and values read and written, the queries,
+    the bases, out and lse."""
+    elem = wl.elem_bytes
+    Q = num_tokens
+    first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
+    nb = first.num_beacons.cpu().numpy().clip(0, wl.num_beacons)
+    rw = first.raw_len.cpu().numpy().clip(0, wl.raw_window - Q)
+    raw_len = torch.from_numpy(rw.astype("int32")).to(dev)
+    chunks, probs, bytes_step = [], [], 0
+    for layer, x in enumerate(layers):
+        c = synth.make_chunk(wl, x, Q, device=dev)
+        c.num_beacons, c.raw_len = first.num_beacons, raw_len  # lengths are per sequence
+        chunks.append(c)
+        probs.append(lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                              rope_theta=wl.rope_theta,
+                                              num_kv_heads=wl.num_kv_heads, scale=wl.scale))
+        r = wl.ranks[layer]
+        rows = wl.num_kv_heads * (int(nb.sum()) * 2 * r + int(rw.sum()) * 2 * wl.head_dim)
+        new_tok = Q * wl.batch * wl.num_kv_heads * wl.head_dim * 2 * 2  # k, v read and stored
+        bytes_step += ((rows + new_tok) * elem + wl.num_kv_heads * wl.head_dim * 2 * r * elem
+                       + Q * wl.batch * wl.num_q_heads * wl.head_dim * elem
+                       + Q * wl.batch * wl.num_q_heads * (wl.head_dim + 1) * 4)
+    ws = torch.zeros(max(lda.slimkv_chunk_workspace_bytes(p, Q) for p in probs),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.batch, Q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.batch, Q, wl.num_q_heads), dtype=torch.float32, device=dev)
+
+    def step():
+        for p, x, c in zip(probs, layers, chunks):
+            lda.slimkv_decode_attn_chunk(p, Q, c.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
+                                         x.V_raw, c.num_beacons, c.raw_len, c.k_new, c.v_new, out,
+                                         lse, ws)
+
+    ms = replay_ms(torch, step, steps)
+    gbps = bytes_step / (ms * 1e-3) / 1e9
+    res = {"tokens_per_chunk": Q, "ms_per_step": round(ms, 4),
+           "us_per_layer": round(ms * 1e3 / wl.layers, 2),
+           "query_tokens_per_s": round(wl.batch * Q / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+           "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
+                        f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + {Q} tokens"}
+    log(f"chunk step: {res}")
+    del ws, chunks
     torch.cuda.empty_cache()
     return res
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 5
+#define SLIMKV_ABI_VERSION 6
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -253,6 +253,45 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
                                        const void* U_K, const void* U_V,
                                        const void* C_K, const void* C_V,
                                        void* K_raw, void* V_raw,
+                                       const int32_t* num_beacons_b,
+                                       const int32_t* raw_len,
+                                       const void* k_new, const void* v_new,
+                                       float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * slimkv_decode_attn_chunk -- the same attention for a chunk of Q query
+ * tokens per sequence: speculative decoding checks several drafted tokens
+ * in one pass, chunked prefill feeds a prompt Q tokens at a time.  Token t
+ * of sequence b sits at position q_pos[b] + t.  Each of its query heads is
+ * rotated there and attends, under one softmax, over the sequence's live
+ * beacon rows (latent, as in slimkv_decode_attn), its live raw rows, and the
+ * chunk's new tokens 0 .. t -- token u's key rotated at q_pos[b] + u in
+ * double precision and rounded once to bf16 -- but not over the chunk's
+ * later tokens.  The tokens u with w_b + u < W_cap are then stored as raw
+ * rows w_b + u of K_raw and V_raw (rotated key, value); the others are
+ * attended but not stored.  Without k_new and v_new every query of the
+ * chunk attends over the cache rows only.  With Q = 1 this is
+ * slimkv_decode_attn_ragged.
+ *
+ *   num_tokens    Q >= 1, with (H_q / H_kv) * Q <= 16 (the query rows of one
+ *                 KV head fill one matrix-core tile)
+ *   q             [B, Q, H_q, d]   the chunk's queries, before rotation
+ *   k_new, v_new  [B, Q, H_kv, d]  the chunk's tokens (key before rotation),
+ *                                  both or neither
+ *   out           [B, Q, H_q, d] fp32;  lse [B, Q, H_q] fp32 or NULL
+ * Capacity-sized caches, lengths, clamping, limits (batch <= 1024, flags 0)
+ * and num_splits as for slimkv_decode_attn_ragged.  bf16 only.  Workspace:
+ * slimkv_chunk_workspace_bytes(problem, num_tokens) bytes, zero-filled
+ * before first use.
+ */
+size_t slimkv_chunk_workspace_bytes(const slimkv_problem* problem, int32_t num_tokens);
+
+slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem,
+                                       int32_t num_tokens, const void* q,
+                                       const int32_t* q_pos, const void* U_K,
+                                       const void* U_V, const void* C_K,
+                                       const void* C_V, void* K_raw, void* V_raw,
                                        const int32_t* num_beacons_b,
                                        const int32_t* raw_len,
                                        const void* k_new, const void* v_new,

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
-           "slimkv_decode_attn_paged",
+           "slimkv_decode_attn_paged", "slimkv_chunk_workspace_bytes", "slimkv_decode_attn_chunk",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
            "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
@@ -102,6 +102,10 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_decode_attn_paged.argtypes = [prob, ctypes.POINTER(slimkv_pages)] + [vp] * 14 + [
         vp, sz, vp]
     lib.slimkv_decode_attn_paged.restype = ctypes.c_int
+    lib.slimkv_chunk_workspace_bytes.argtypes = [prob, ctypes.c_int32]
+    lib.slimkv_chunk_workspace_bytes.restype = sz
+    lib.slimkv_decode_attn_chunk.argtypes = [prob, ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_chunk.restype = ctypes.c_int
     lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_reconstruct_attn.restype = ctypes.c_int
     lib.slimkv_reconstruct_rope_attn.argtypes = [prob] + [vp] * 11 + [vp, sz, vp]
@@ -203,6 +207,26 @@ def slimkv_decode_attn_paged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw
         _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw),
         _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_chunk_workspace_bytes(problem: slimkv_problem, num_tokens: int) -> int:
+    lib = load_library()
+    n = lib.slimkv_chunk_workspace_bytes(ctypes.byref(problem), int(num_tokens))
+    if n == 0:
+        raise SlimKVError(2, lib.slimkv_last_error().decode())
+    return int(n)
+
+
+def slimkv_decode_attn_chunk(problem, num_tokens, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                             num_beacons, raw_len, k_new, v_new, out, lse, workspace,
+                             stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_chunk(
+        ctypes.byref(problem), int(num_tokens), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V),
+        _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len),
+        _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,

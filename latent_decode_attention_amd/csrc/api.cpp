@@ -170,6 +170,32 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   return SLIMKV_OK;
 }
 
+// Plan of a chunk call: the ragged call's segments and schedule limits,
+// bf16 only, G * Q <= kChunkRows query rows per unit; partial slots for
+// every piece the launcher can make (at most units + kChunkMaxSlots), each
+// holding G * Q rows.
+slimkv_status make_chunk_plan(const slimkv_problem* p, int32_t num_tokens, Plan& pl) {
+  slimkv_status st = make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
+  if (st != SLIMKV_OK) return st;
+  if (p->dtype != SLIMKV_BF16) return fail(SLIMKV_ERR_UNSUPPORTED, "chunk calls take bf16 caches");
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (num_tokens < 1) return fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
+  if ((int64_t)G * num_tokens > kChunkRows)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "group %d x %d tokens exceeds %d query rows per KV head", G,
+                num_tokens, kChunkRows);
+  const int64_t M = (int64_t)G * num_tokens, slots = pl.units + kChunkMaxSlots;
+  pl.attn.num_tokens = num_tokens;
+  pl.off_counters = 0;
+  size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+  pl.off_ml = off;
+  off = round_up(off + (size_t)(slots * M * 2) * sizeof(float), kAlign);
+  pl.off_acc = off;
+  off = round_up(off + (size_t)(slots * M * kHeadDim) * sizeof(float), kAlign);
+  pl.off_kb = pl.off_vb = off;
+  pl.total = off;
+  return SLIMKV_OK;
+}
+
 struct Range {
   const void* p;
   size_t bytes;
@@ -367,15 +393,20 @@ slimkv_status check_pages(const slimkv_problem* p, const slimkv_pages* pg, int e
   return SLIMKV_OK;
 }
 
+// The ragged and paged calls (chunk = 0) and the chunk call (chunk = Q
+// query tokens per sequence: q, out, lse, k_new and v_new carry a token axis).
 slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const void* q,
                          const int32_t* q_pos, const void* U_K, const void* U_V, const void* C_K,
                          const void* C_V, void* K_raw, void* V_raw, const int32_t* seq_beacons,
                          const int32_t* seq_raw, const void* k_new, const void* v_new, float* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream, bool paged) {
+                         float* lse, void* ws, size_t ws_bytes, void* stream, bool paged,
+                         int32_t chunk = 0) {
   Plan pl;
-  slimkv_status st = make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
+  slimkv_status st = chunk > 0 ? make_chunk_plan(p, chunk, pl)
+                               : make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
   if (st != SLIMKV_OK) return st;
   const size_t e = (size_t)pl.elem;
+  const size_t T = chunk > 0 ? (size_t)chunk : 1;  // query tokens per sequence
   const size_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = kHeadDim;
   const size_t nb = p->num_beacons, w = p->raw_window;
   const bool beacons = nb > 0, raw = w > 0, append = k_new != nullptr || v_new != nullptr;
@@ -394,13 +425,13 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   // the raw arrays are also written, so they count as outputs too.
   const bool btab = paged && beacons, rtab = paged && raw;
   Range in[12] = {
-      {q, B * Hq * d * e, "q"},
+      {q, T * B * Hq * d * e, "q"},
       {beacons ? U_K : nullptr, Hkv * d * rk * e, "U_K"},
       {beacons ? U_V : nullptr, Hkv * d * rv * e, "U_V"},
       {beacons ? C_K : nullptr, cache_bytes[0], "C_K"},
       {beacons ? C_V : nullptr, cache_bytes[1], "C_V"},
-      {append ? k_new : nullptr, B * Hkv * d * e, "k_new"},
-      {append ? v_new : nullptr, B * Hkv * d * e, "v_new"},
+      {append ? k_new : nullptr, T * B * Hkv * d * e, "k_new"},
+      {append ? v_new : nullptr, T * B * Hkv * d * e, "v_new"},
       {q_pos, B * sizeof(int32_t), "q_pos"},
       {seq_beacons, seq_beacons ? B * sizeof(int32_t) : 0, "num_beacons_b"},
       {seq_raw, seq_raw ? B * sizeof(int32_t) : 0, "raw_len"},
@@ -422,8 +453,8 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
     req[n_req++] = vr;
   }
   req[n_req++] = Range{out, 1, "out"};
-  Range outs[5] = {{out, B * Hq * d * sizeof(float), "out"},
-                   {lse, lse ? B * Hq * sizeof(float) : 0, "lse"},
+  Range outs[5] = {{out, T * B * Hq * d * sizeof(float), "out"},
+                   {lse, lse ? T * B * Hq * sizeof(float) : 0, "lse"},
                    {ws, pl.total, "workspace"},
                    {append ? kr.p : nullptr, append ? kr.bytes : 0, "K_raw"},
                    {append ? vr.p : nullptr, append ? vr.bytes : 0, "V_raw"}};
@@ -489,7 +520,9 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   a.deterministic = 1;
   const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
-  const hipError_t err = launch_ragged(a, pl.dtype, static_cast<hipStream_t>(stream), ev0, ev1);
+  const hipError_t err = chunk > 0
+                            ? launch_chunk(a, static_cast<hipStream_t>(stream), ev0, ev1)
+                            : launch_ragged(a, pl.dtype, static_cast<hipStream_t>(stream), ev0, ev1);
   if (err != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();
   return SLIMKV_OK;
@@ -563,6 +596,25 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem, const slim
   return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
                             num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
                             workspace_bytes, stream, true);
+}
+
+size_t slimkv_chunk_workspace_bytes(const slimkv_problem* problem, int32_t num_tokens) {
+  slimkv::Plan pl;
+  if (slimkv::make_chunk_plan(problem, num_tokens, pl) != SLIMKV_OK) return 0;
+  return pl.total;
+}
+
+slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem, int32_t num_tokens,
+                                       const void* q, const int32_t* q_pos, const void* U_K,
+                                       const void* U_V, const void* C_K, const void* C_V,
+                                       void* K_raw, void* V_raw, const int32_t* num_beacons_b,
+                                       const int32_t* raw_len, const void* k_new,
+                                       const void* v_new, float* out, float* lse, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (num_tokens < 1) return slimkv::fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
+  return slimkv::run_ragged(problem, nullptr, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, false, num_tokens);
 }
 
 const char* slimkv_status_string(slimkv_status status) {

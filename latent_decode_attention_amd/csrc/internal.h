@@ -19,6 +19,8 @@ constexpr int kMaxRaggedBatch = 1024;  // sequences per ragged call (their lengt
 constexpr int kMaxPageEntries = 4096;  // page-table entries of one sequence (staged in LDS)
 constexpr int kMinPageShift = 6;       // pages hold at least 64 rows: no tile spans two pages
 constexpr int kMaxPageShift = 16;
+constexpr int kChunkRows = 16;         // query rows (tokens x heads) per unit in chunk calls
+constexpr int kChunkMaxSlots = 2048;   // workgroup slots a chunk call is shaped for, at most
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -77,6 +79,9 @@ struct AttnArgs {
   int32_t table_width[2];
   int32_t num_pages[2];
   int32_t page_shift;
+  // Chunk calls: query tokens per sequence (q, out [B, Q, H_q, d], lse
+  // [B, Q, H_q], k_new, v_new [B, Q, H_kv, d]); partials hold G * Q rows
+  int32_t num_tokens;
 };
 
 struct RebuildArgs {
@@ -97,6 +102,10 @@ hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0
 // The ragged-batch attention kernel (one launch; see ragged_impl.h), over
 // capacity-sized arrays or, with page tables in `a`, over page pools.
 hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+// A chunk of query tokens per sequence over a ragged cache (bf16; one
+// launch; see chunk_impl.h).
+hipError_t launch_chunk(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 // Chunks per unit: the count in [1, kMaxChunks] whose workgroups fill the
 // device's slots best (no chunk under min_chunk_bytes).

@@ -204,6 +204,43 @@ def make_step(wl: Workload, inp: LayerInputs, *, base_seed: int = 0, device="cpu
 
 
 @dataclasses.dataclass
+class ChunkInputs:
+    """A chunk of Q query tokens per sequence: the queries (token t of
+    sequence b at position q_pos[b] + t), each sequence's live rows, and the
+    chunk's tokens (keys before rotation, values) per KV head."""
+
+    q: torch.Tensor            # [B, Q, H_q, d]
+    num_beacons: torch.Tensor  # [B] int32
+    raw_len: torch.Tensor      # [B] int32
+    k_new: torch.Tensor        # [B, Q, H_kv, d]
+    v_new: torch.Tensor        # [B, Q, H_kv, d]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[1])
+
+    def to(self, device) -> "ChunkInputs":
+        return ChunkInputs(*(getattr(self, f.name).to(device) for f in dataclasses.fields(self)))
+
+
+def make_chunk(wl: Workload, inp: LayerInputs, num_tokens: int, *, base_seed: int = 0,
+               device="cpu", beacons=(0.0, 1.0), raw=(0.0, 1.0),
+               fixed: dict | None = None) -> ChunkInputs:
+    """Seeded chunk of ``num_tokens`` query tokens per sequence for ``inp``'s
+    capacity-sized arrays: queries and tokens N(0, sigma^2) in the storage
+    dtype, lengths drawn as in ``make_step``."""
+    step = make_step(wl, inp, base_seed=base_seed, device=device, beacons=beacons, raw=raw,
+                     fixed=fixed)
+    B, Q, d = wl.batch, num_tokens, wl.head_dim
+    q = _gauss((B, Q, wl.num_q_heads, d), _seed(base_seed, wl, inp.layer, "q", Q), wl.sigma,
+               wl.dtype, device)
+    shape = (B, Q, wl.num_kv_heads, d)
+    k = _gauss(shape, _seed(base_seed, wl, inp.layer, "k_new", Q), wl.sigma, wl.dtype, device)
+    v = _gauss(shape, _seed(base_seed, wl, inp.layer, "v_new", Q), wl.sigma, wl.dtype, device)
+    return ChunkInputs(q, step.num_beacons, step.raw_len, k, v)
+
+
+@dataclasses.dataclass
 class PagedCache:
     """A layer's cache laid out in pages drawn from shared pools:
     C_K, C_V [beacon_pages, H_kv, page_rows, r] and K_raw, V_raw

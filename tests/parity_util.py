@@ -376,3 +376,105 @@ def assert_paged_writes(K_after, V_after, pc: synth.PagedCache, step, k_app, wca
         "V pool: other rows written"
     print(f"[parity] paged new rows: {int(mask.sum())} written, {off_by_ulp} key elements one "
           f"ulp off", flush=True)
+
+
+def run_gpu_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool = True,
+                  lengths: bool = True, num_splits: int = 0, device="cuda"):
+    """slimkv_decode_attn_chunk on ``inp`` (capacity-sized arrays) and the
+    chunk ``ch``; the raw cache is cloned first.  Returns (out [B, Q, H_q, d],
+    lse [B, Q, H_q], K_raw, V_raw) on the host."""
+    wl = inp.workload
+    g = inp.to(device)
+    c = ch.to(device)
+    Q = ch.num_tokens
+    K, V = g.K_raw.clone(), g.V_raw.clone()
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=num_splits)
+    B, Hq, d = g.q.shape
+    out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device=device)
+    lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=device)
+    ws = torch.zeros(lda.slimkv_chunk_workspace_bytes(prob, Q), dtype=torch.uint8, device=device)
+    lda.slimkv_decode_attn_chunk(prob, Q, c.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, K, V,
+                                 c.num_beacons if lengths else None,
+                                 c.raw_len if lengths else None,
+                                 c.k_new if append else None, c.v_new if append else None,
+                                 out, lse, ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu()
+
+
+def oracle_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool = True,
+                 lengths: bool = True, units=None):
+    """oracle.decode_chunk on the whole layer (or the listed units)."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    nb, w = inp.num_beacons, inp.raw_window
+    return oracle.decode_chunk(
+        st(ch.q), st(inp.q_pos), st(inp.U_K), st(inp.U_V), st(inp.C_K) if nb else None,
+        st(inp.C_V) if nb else None, st(inp.K_raw) if w else None, st(inp.V_raw) if w else None,
+        num_kv_heads=wl.num_kv_heads, scale=wl.scale, rope_theta=wl.rope_theta,
+        num_beacons=st(ch.num_beacons) if lengths else None,
+        raw_len=st(ch.raw_len) if lengths else None,
+        k_new=st(ch.k_new) if append else None, v_new=st(ch.v_new) if append else None,
+        units=units)
+
+
+def oracle_chunk_units(inp: synth.LayerInputs, ch: synth.ChunkInputs, units):
+    """oracle.decode_chunk on sampled units, copying only each unit's slices.
+    Returns {(b, h): (out [Q, G, d], lse [Q, G], k_app [Q, d])}."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    G = wl.group
+    res = {}
+    for b, h in units:
+        hs = slice(h * G, (h + 1) * G)
+        nb, w = inp.num_beacons, inp.raw_window
+        out, lse, k_app = oracle.decode_chunk(
+            st(ch.q[b:b + 1, :, hs]), st(inp.q_pos[b:b + 1]), st(inp.U_K[h:h + 1]),
+            st(inp.U_V[h:h + 1]), st(inp.C_K[b:b + 1, h:h + 1]) if nb else None,
+            st(inp.C_V[b:b + 1, h:h + 1]) if nb else None,
+            st(inp.K_raw[b:b + 1, h:h + 1]) if w else None,
+            st(inp.V_raw[b:b + 1, h:h + 1]) if w else None,
+            num_kv_heads=1, scale=wl.scale, rope_theta=wl.rope_theta,
+            num_beacons=st(ch.num_beacons[b:b + 1]), raw_len=st(ch.raw_len[b:b + 1]),
+            k_new=st(ch.k_new[b:b + 1, :, h:h + 1]), v_new=st(ch.v_new[b:b + 1, :, h:h + 1]))
+        res[(b, h)] = (out[0], lse[0], k_app[0, :, 0])
+    return res
+
+
+def assert_chunk_rows(K_after, V_after, K_before, V_before, ch: synth.ChunkInputs, k_app,
+                      units=None):
+    """The chunk call wrote exactly its tokens' rows -- raw row w_b + u for
+    every token u with w_b + u below the capacity -- with the oracle's keys
+    (as in assert_new_rows; k_app [B, Q, H_kv, d] or {(b, h): [Q, d]}) and
+    v_new, checked for ``units`` (default all); every other row keeps its
+    bits.  k_app None: no tokens, nothing written."""
+    Ka, Va = storage_to_f64(K_after), storage_to_f64(V_after)
+    vnew = storage_to_f64(ch.v_new)
+    B, Hkv, wcap, d = Ka.shape
+    Q = ch.num_tokens
+    raw_len = ch.raw_len.cpu().numpy()
+    check = set(units or [(b, h) for b in range(B) for h in range(Hkv)])
+    mask = np.zeros((B, Hkv, wcap), dtype=bool)
+    off_by_ulp = compared = 0
+    for b in range(B if k_app is not None else 0):
+        w = int(np.clip(raw_len[b], 0, wcap))
+        for u in range(Q):
+            if w + u >= wcap:
+                break
+            mask[b, :, w + u] = True
+            for h in range(Hkv):
+                if (b, h) in check:
+                    exp = k_app[(b, h)][u] if isinstance(k_app, dict) else k_app[b, u, h]
+                    off_by_ulp += _key_ulps(Ka[b, h, w + u], exp, K_after.dtype, (b, h, u))
+                    compared += d
+                    assert np.array_equal(Va[b, h, w + u], vnew[b, u, h]), f"value ({b}, {h}, {u})"
+    assert off_by_ulp <= max(1, compared // 10000), f"{off_by_ulp} of {compared} key elements"
+    keep = ~mask
+    assert np.array_equal(storage_bits(K_after)[keep], storage_bits(K_before)[keep]), \
+        "K_raw: other rows written"
+    assert np.array_equal(storage_bits(V_after)[keep], storage_bits(V_before)[keep]), \
+        "V_raw: other rows written"
+    print(f"[parity] chunk rows: {int(mask.sum())} written, {off_by_ulp} key elements one ulp off",
+          flush=True)

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 5
+    assert lda.slimkv_abi_version() == 6
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -303,6 +303,52 @@ def test_paged_checks(lib):
     assert _call_paged(lib, prob, _pages(raw_table=0x6000000 + 8)) == ALIAS
     # the same flags and batch limits as the ragged call
     assert _call_paged(lib, _problem(batch=1025), _pages()) == UNSUP
+
+
+def _call_chunk(lib, prob, Q, *, ptrs=None, ws_bytes=16):
+    """slimkv_decode_attn_chunk with fake device addresses (every case fails
+    validation before any HIP call: at the latest, the 16-byte workspace is
+    too small)."""
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, nb=0x210000, raw=0x220000,
+             k_new=0x230000, v_new=0x240000, out=0x5000000, lse=0x6000000, ws=0x7000000)
+    p.update(ptrs or {})
+    v = {k: (None if x is None else ctypes.c_void_p(x)) for k, x in p.items()}
+    return lib.slimkv_decode_attn_chunk(ctypes.byref(prob), Q, v["q"], v["q_pos"], v["U_K"],
+                                        v["U_V"], v["C_K"], v["C_V"], v["K_raw"], v["V_raw"],
+                                        v["nb"], v["raw"], v["k_new"], v["v_new"], v["out"],
+                                        v["lse"], v["ws"], ws_bytes, None)
+
+
+def test_chunk_checks(lib):
+    prob = _problem()  # G = 4, batch 2, 8 query heads
+    ws = lib.slimkv_chunk_workspace_bytes
+    assert ws(ctypes.byref(prob), 4) > ws(ctypes.byref(prob), 1) > 0
+    # the query rows of a KV head fill one 16-row tile; bf16 only
+    assert ws(ctypes.byref(prob), 5) == 0 and "16" in lda.slimkv_last_error()
+    assert ws(ctypes.byref(prob), 0) == 0
+    assert ws(ctypes.byref(_problem(dtype="fp32")), 1) == 0
+    assert ws(ctypes.byref(_problem(num_q_heads=2)), 16) > 0
+    assert _call_chunk(lib, prob, 4) == WS
+    assert _call_chunk(lib, prob, 4, ws_bytes=ws(ctypes.byref(prob), 4) - 1) == WS
+    assert _call_chunk(lib, prob, 5) == UNSUP
+    assert _call_chunk(lib, prob, 0) == SHAPE
+    assert _call_chunk(lib, _problem(dtype="fp32"), 2) == UNSUP
+    flagged = _problem()
+    flagged.flags = lda.SLIMKV_FLAG_DYNAMIC_TILES
+    assert _call_chunk(lib, flagged, 2) == UNSUP
+    assert _call_chunk(lib, prob, 2, ptrs=dict(v_new=None)) == NULL
+    assert _call_chunk(lib, prob, 2, ptrs=dict(k_new=None, v_new=None)) == WS
+    # q, k_new, v_new, out and lse carry the token axis: 3 tokens of q are
+    # 3 x 2 x 8 x 128 x 2 bytes, so out may start right after, not before
+    q_bytes = 3 * 2 * 8 * 128 * 2
+    assert _call_chunk(lib, prob, 3, ptrs=dict(out=0x100000 + q_bytes)) == WS
+    assert _call_chunk(lib, prob, 3, ptrs=dict(out=0x100000 + q_bytes - 16)) == ALIAS
+    lse_bytes = 3 * 2 * 8 * 4
+    assert _call_chunk(lib, prob, 3, ptrs=dict(lse=0x240000 - lse_bytes)) == WS
+    assert _call_chunk(lib, prob, 3, ptrs=dict(lse=0x240000 - lse_bytes + 4)) == ALIAS
+    # the raw window is written with new tokens
+    assert _call_chunk(lib, prob, 2, ptrs=dict(k_new=0x3000000 + 64)) == ALIAS
 
 
 def test_reconstruct_rope_checks(lib):
