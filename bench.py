@@ -21,7 +21,8 @@ Reported beside the headline tokens/s:
     reconstruct-then-attend paths on the same beacons (without and with the
     rotation of rebuilt beacon keys) and vs uncompressed full-KV attention
     over all 131072 tokens; the ragged serving step, over capacity-sized
-    arrays and over a paged cache; the 48-layer Qwen step;
+    arrays and over a paged cache, and with 4 query tokens per sequence;
+    the 48-layer Qwen step;
   * the fp64 CPU oracle timed on a bounded sample on this host's cores.
 """
 
@@ -255,6 +256,8 @@ def main():
                                                                  args.steps)
             result["comparison"]["c3_paged_step"] = ragged_step(lda, synth, torch, dev, wl, layers,
                                                                 args.steps, page_rows=64)
+            result["comparison"]["c3_chunk4_step"] = chunk_step(lda, synth, torch, dev, wl, layers,
+                                                                 args.steps, 4)
             result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
 
     del ws
