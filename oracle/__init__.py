@@ -85,6 +85,11 @@ def load(path=LIBRARY) -> ctypes.CDLL:
             lib.slimkv_oracle_decode_chunk.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int] + [
                 ctypes.c_void_p] * 12 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "slimkv_oracle_decode_alibi"):
+            lib.slimkv_oracle_decode_alibi.restype = ctypes.c_int
+            lib.slimkv_oracle_decode_alibi.argtypes = [ctypes.POINTER(_Problem)] + [
+                ctypes.c_void_p] * 10 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int]
         lib.slimkv_oracle_max_threads.restype = ctypes.c_int
         _lib_cache[key] = lib
     return _lib_cache[key]
@@ -261,6 +266,50 @@ def decode_chunk(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, num_kv_heads: in
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return out, lse, k_app
+
+
+def decode_alibi(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, beacon_pos, slopes,
+                 num_kv_heads: int, scale: float, units=None, threads: int = 0,
+                 library: pathlib.Path = LIBRARY):
+    """fp64 latent decode attention of an ALiBi backbone: no rotation; score
+    j gets -slopes[h_q] * (q_pos - k_pos) after the scaled product, with
+    beacon j at beacon_pos[j] ([N_b] int32) and raw row t at
+    q_pos - W + 1 + t.  Arrays and the result as for ``decode``; slopes
+    [H_q] float64."""
+    q = np.ascontiguousarray(q)
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported storage dtype {dt}")
+    B, Hq, d = q.shape
+    q_pos = _arr(q_pos, np.dtype(np.int32))
+    nb = 0 if C_K is None else int(np.shape(C_K)[2])
+    w = 0 if K_raw is None else int(np.shape(K_raw)[2])
+    rk = int(np.shape(U_K)[2]) if U_K is not None else 0
+    rv = int(np.shape(U_V)[2]) if U_V is not None else 0
+    U_K, U_V, C_K, C_V, K_raw, V_raw = (_arr(x, dt) for x in (U_K, U_V, C_K, C_V, K_raw, V_raw))
+    bp = _arr(beacon_pos, np.dtype(np.int32)) if nb else None
+    sl = np.ascontiguousarray(slopes, dtype=np.float64)
+    if sl.shape != (Hq,):
+        raise ValueError("slopes must have one entry per query head")
+    prob = _Problem(B, Hq, num_kv_heads, d, nb, rk, rv, w, float(scale), 10000.0, _DTYPE[dt])
+    out = np.full((B, Hq, d), np.nan, dtype=np.float64)
+    lse = np.full((B, Hq), np.nan, dtype=np.float64)
+    if units is None:
+        unit_arr, n_units = None, 0
+    else:
+        unit_arr = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+        n_units = unit_arr.shape[0]
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = load(library).slimkv_oracle_decode_alibi(
+        ctypes.byref(prob), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+        ptr(K_raw), ptr(V_raw), ptr(bp), ptr(sl), ptr(unit_arr), n_units, ptr(out), ptr(lse),
+        int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    return out, lse
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

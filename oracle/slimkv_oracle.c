@@ -39,7 +39,8 @@
  * the query position and attended as one more raw row (see oracle_unit).
  * slimkv_oracle_decode_chunk takes a chunk of several query tokens per
  * sequence, each attending causally to the chunk's new tokens (see
- * oracle_chunk_unit).
+ * oracle_chunk_unit).  slimkv_oracle_decode_alibi is the ALiBi variant (no
+ * rotation, a linear distance bias on every score; see oracle_alibi_unit).
  */
 #include <math.h>
 #include <stdint.h>
@@ -405,6 +406,145 @@ int slimkv_oracle_decode_ragged(const oracle_problem* p, const void* q,
       }
       oracle_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons_b, raw_len,
                   k_new, v_new, NULL, out, lse, k_app, work);
+    }
+    free(work);
+  }
+  if (failed == 1) return ORACLE_NO_MEMORY;
+  if (failed == 2) return ORACLE_BAD_SHAPE;
+  return ORACLE_OK;
+}
+
+/*
+ * The ALiBi variant (page "Can SlimKV compress KV cache jointly across
+ * tokens and features": ALiBi adds its positional bias after the query-key
+ * product, so it composes with the latent scores).  An ALiBi backbone has
+ * no rotary embedding: neither the query nor any key is rotated, and every
+ * score gets the bias -slope[hq] * (q_pos - k_pos) added after the scaled
+ * product, with the query head's slope.  Key positions: beacon j at
+ * bpos[j]; raw row t at q_pos[b] - W + 1 + t (the window ends at the
+ * query's position).  Otherwise the steps of oracle_unit: project the
+ * query, score latent beacons and raw keys, one softmax, latent value sum
+ * lifted once.
+ */
+static void oracle_alibi_unit(const oracle_problem* p, int b, int h, const void* q,
+                              const int32_t* q_pos, const void* U_K, const void* U_V,
+                              const void* C_K, const void* C_V, const void* K_raw,
+                              const void* V_raw, const int32_t* bpos, const double* slope,
+                              double* out, double* lse, double* work) {
+  const int d = p->head_dim;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int nb = p->num_beacons, w = p->raw_window;
+  const int rk = p->rank_k, rv = p->rank_v;
+  const int dt = p->dtype;
+  const size_t n = (size_t)nb + (size_t)w;
+  double* qv = work;        /* [d]  the query (no rotation)  */
+  double* qh = qv + d;      /* [rk] latent query             */
+  double* s = qh + rk;      /* [n]  scores, then weights     */
+  double* olat = s + n;     /* [rv] latent value sum         */
+  double* oraw = olat + rv; /* [d]  raw value sum            */
+  const size_t unit = (size_t)b * p->num_kv_heads + h;
+  const size_t ck0 = unit * (size_t)nb * rk, cv0 = unit * (size_t)nb * rv;
+  const size_t kr0 = unit * (size_t)w * d;
+  const size_t uk0 = (size_t)h * d * rk, uv0 = (size_t)h * d * rv;
+  const double qp = (double)q_pos[b];
+  for (int g = 0; g < G; ++g) {
+    const int hq = h * G + g;
+    const size_t q0 = ((size_t)b * p->num_q_heads + hq) * d;
+    const double m_h = slope[hq];
+    for (int i = 0; i < d; ++i) qv[i] = widen(q, dt, q0 + i);
+    for (int k = 0; k < rk; ++k) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += qv[i] * widen(U_K, dt, uk0 + (size_t)i * rk + k);
+      qh[k] = acc;
+    }
+    for (int j = 0; j < nb; ++j) {
+      double acc = 0.0;
+      for (int k = 0; k < rk; ++k) acc += qh[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+      s[j] = p->scale * acc - m_h * (qp - (double)bpos[j]);
+    }
+    for (int t = 0; t < w; ++t) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i) acc += qv[i] * widen(K_raw, dt, kr0 + (size_t)t * d + i);
+      const double kpos = qp - (double)w + 1.0 + (double)t;
+      s[nb + t] = p->scale * acc - m_h * (qp - kpos);
+    }
+    double mx = -INFINITY;
+    for (size_t j = 0; j < n; ++j) mx = s[j] > mx ? s[j] : mx;
+    double den = 0.0;
+    for (size_t j = 0; j < n; ++j) {
+      s[j] = exp(s[j] - mx);
+      den += s[j];
+    }
+    for (size_t j = 0; j < n; ++j) s[j] /= den;
+    for (int k = 0; k < rv; ++k) olat[k] = 0.0;
+    for (int j = 0; j < nb; ++j)
+      for (int k = 0; k < rv; ++k) olat[k] += s[j] * widen(C_V, dt, cv0 + (size_t)j * rv + k);
+    for (int i = 0; i < d; ++i) oraw[i] = 0.0;
+    for (int t = 0; t < w; ++t)
+      for (int i = 0; i < d; ++i) oraw[i] += s[nb + t] * widen(V_raw, dt, kr0 + (size_t)t * d + i);
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * olat[k];
+      out[q0 + i] = acc + oraw[i];
+    }
+    if (lse) lse[(size_t)b * p->num_q_heads + hq] = mx + log(den);
+  }
+}
+
+/*
+ * ALiBi counterpart of slimkv_oracle_decode (see oracle_alibi_unit):
+ * bpos [N_b] int32 beacon positions (the same for every sequence), slope
+ * [H_q] doubles.
+ */
+int slimkv_oracle_decode_alibi(const oracle_problem* p, const void* q, const int32_t* q_pos,
+                               const void* U_K, const void* U_V, const void* C_K,
+                               const void* C_V, const void* K_raw, const void* V_raw,
+                               const int32_t* bpos, const double* slope, const int32_t* units,
+                               int64_t n_units, double* out, double* lse, int threads) {
+  if (!p || !q || !q_pos || !out || !slope) return ORACLE_BAD_SHAPE;
+  if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
+    return ORACLE_BAD_DTYPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 ||
+      p->num_q_heads % p->num_kv_heads != 0 || p->head_dim < 1 || p->num_beacons < 0 ||
+      p->raw_window < 0 || (int64_t)p->num_beacons + p->raw_window < 1)
+    return ORACLE_BAD_SHAPE;
+  if (p->num_beacons > 0 &&
+      (p->rank_k < 1 || p->rank_v < 1 || !U_K || !U_V || !C_K || !C_V || !bpos))
+    return ORACLE_BAD_SHAPE;
+  if (p->raw_window > 0 && (!K_raw || !V_raw)) return ORACLE_BAD_SHAPE;
+  const int64_t all = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t count = units ? n_units : all;
+  const int rk = p->num_beacons > 0 ? p->rank_k : 0;
+  const int rv = p->num_beacons > 0 ? p->rank_v : 0;
+  const size_t work_len = 2 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons + p->raw_window;
+  oracle_problem pp = *p;
+  pp.rank_k = rk;
+  pp.rank_v = rv;
+  int failed = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel
+  {
+    double* work = (double*)malloc(work_len * sizeof(double));
+    if (!work) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < count; ++u) {
+      if (!work) continue;
+      int b = units ? units[2 * u] : (int)(u / p->num_kv_heads);
+      int h = units ? units[2 * u + 1] : (int)(u % p->num_kv_heads);
+      if (b < 0 || b >= p->batch || h < 0 || h >= p->num_kv_heads) {
+#pragma omp atomic write
+        failed = 2;
+        continue;
+      }
+      oracle_alibi_unit(&pp, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, bpos, slope, out,
+                        lse, work);
     }
     free(work);
   }

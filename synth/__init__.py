@@ -7,6 +7,6 @@ the HIP library can be fed from it without sharing any of the method.
 """
 
 from .configs import RANK_SET, WORKLOADS, Workload, draw_ranks, get_workload  # noqa: F401
-from .gen import (ChunkInputs, LayerInputs, PagedCache, StepInputs, make_chunk,  # noqa: F401
-                  make_full_kv, make_layer, make_paged, make_step, orthonormal_basis,
+from .gen import (ChunkInputs, LayerInputs, PagedCache, StepInputs, alibi_slopes,  # noqa: F401
+                  beacon_grid, make_chunk, make_full_kv, make_layer, make_paged, make_step, orthonormal_basis,
                   to_numpy_storage, unit_slices)

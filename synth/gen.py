@@ -323,6 +323,28 @@ def make_paged(inp: LayerInputs, step: StepInputs, *, page_rows: int, base_seed:
         bt, rt)
 
 
+def alibi_slopes(num_heads: int) -> np.ndarray:
+    """Per-head ALiBi slopes (inputs of the ALiBi variant): for n heads, n a
+    power of two, the geometric sequence 2^(-8/n), 2^(-16/n), ...; otherwise
+    the slopes of the largest power of two below n, then every other slope
+    of twice as many heads."""
+    def pow2(n):
+        start = 2.0 ** (-8.0 / n)
+        return [start ** (i + 1) for i in range(n)]
+    n = 1 << (num_heads.bit_length() - 1)
+    s = pow2(n)
+    if n < num_heads:
+        s += pow2(2 * n)[0::2][:num_heads - n]
+    return np.asarray(s, dtype=np.float64)
+
+
+def beacon_grid(ratio: int) -> tuple:
+    """Positions of beacons that each summarise `ratio` tokens, beacon j
+    covering tokens [j * ratio, (j + 1) * ratio) and placed at its last
+    token: (first, stride) = (ratio - 1, ratio)."""
+    return ratio - 1, ratio
+
+
 def to_numpy_storage(t: torch.Tensor) -> np.ndarray:
     """CPU numpy view of a tensor in its storage format (bf16 as uint16 bits)."""
     t = t.detach().to("cpu").contiguous()

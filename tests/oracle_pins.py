@@ -599,6 +599,118 @@ def pin_chunk_rounding(library):
     assert np.array_equal(k_app, bf16_round(rot)), "chunk keys not rounded once to bf16"
 
 
+# ---------------------------------------------------------------------------
+# The ALiBi variant (oracle.decode_alibi): no rotation, a linear distance
+# bias on every score.
+
+
+def run_alibi(p, library, **over):
+    args = dict(p)
+    args.update(over)
+    nb = args["C_K"].shape[2]
+    return oracle.decode_alibi(
+        args["q"], args["q_pos"], args["U_K"], args["U_V"], args["C_K"] if nb else None,
+        args["C_V"] if nb else None, args["K_raw"], args["V_raw"],
+        beacon_pos=args["beacon_pos"], slopes=args["slopes"],
+        num_kv_heads=args["num_kv_heads"], scale=args["scale"], library=library)
+
+
+def alibi_problem(seed, *, ratio=4, q_pos=None, **shape):
+    p = random_problem(seed, q_pos=q_pos, **shape)
+    nb = p["C_K"].shape[2]
+    p["beacon_pos"] = ((np.arange(nb) + 1) * ratio - 1).astype(np.int32)
+    rng = np.random.default_rng(seed + 3000)
+    p["slopes"] = rng.uniform(0.01, 0.5, size=p["q"].shape[1])
+    return p
+
+
+def alibi_reference(p):
+    """Plain attention over the rebuilt beacon rows and the raw rows, no
+    rotation, scores scale * q.k - slope * (q_pos - k_pos)."""
+    q = p["q"]
+    B, Hq, d = q.shape
+    Hkv = p["num_kv_heads"]
+    G = Hq // Hkv
+    w = p["K_raw"].shape[2]
+    kb = np.einsum("bhjr,hdr->bhjd", p["C_K"], p["U_K"])
+    vb = np.einsum("bhjr,hdr->bhjd", p["C_V"], p["U_V"])
+    K = np.concatenate([kb, p["K_raw"]], axis=2)
+    V = np.concatenate([vb, p["V_raw"]], axis=2)
+    out = np.zeros((B, Hq, d))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        qp = int(p["q_pos"][b])
+        kpos = np.concatenate([p["beacon_pos"], qp - w + 1 + np.arange(w)]).astype(np.float64)
+        for hq in range(Hq):
+            h = hq // G
+            s = p["scale"] * (K[b, h] @ q[b, hq]) - p["slopes"][hq] * (qp - kpos)
+            m = s.max()
+            e = np.exp(s - m)
+            out[b, hq] = e @ V[b, h] / e.sum()
+            lse[b, hq] = m + np.log(e.sum())
+    return out, lse
+
+
+def pin_alibi_reference(library):
+    for seed, shape in ((70, dict(B=2, Hkv=2, G=2, d=16, nb=6, rk=4, rv=6, w=5)),
+                        (71, dict(B=1, Hkv=1, G=4, d=128, nb=40, rk=32, rv=16, w=9,
+                                  q_pos=131071))):
+        p = alibi_problem(seed, **shape)
+        out, lse = run_alibi(p, library)
+        ref, ref_lse = alibi_reference(p)
+        _close(out, ref, what=f"alibi out {shape}")
+        _close(lse, ref_lse, what=f"alibi lse {shape}")
+
+
+def pin_alibi_zero_slopes(library):
+    """Without bias, an ALiBi backbone's attention is RoPE attention at
+    position 0 (every rotation the identity)."""
+    p = alibi_problem(72, B=2, Hkv=2, G=3, d=32, nb=7, rk=8, rv=8, w=4, q_pos=5000)
+    out, lse = run_alibi(p, library, slopes=np.zeros(6))
+    ref, ref_lse = run_oracle(p, library, q_pos=np.zeros(2, dtype=np.int32))
+    _close(out, ref, tol=1e-13, what="alibi without bias")
+    _close(lse, ref_lse, tol=1e-13, what="alibi without bias lse")
+
+
+def pin_alibi_translation(library):
+    """Only distances count: moving the query and the beacons by the same
+    offset (raw rows move with the query) changes nothing."""
+    p = alibi_problem(73, B=2, Hkv=1, G=2, d=16, nb=6, rk=4, rv=4, w=5, q_pos=30)
+    out, lse = run_alibi(p, library)
+    out2, lse2 = run_alibi(p, library, q_pos=(p["q_pos"] + 99991).astype(np.int32),
+                           beacon_pos=(p["beacon_pos"] + 99991).astype(np.int32))
+    _close(out2, out, tol=1e-12, what="alibi translation")
+    _close(lse2, lse - 0.0, tol=1e-9, what="alibi translation lse")
+    out3, _ = run_alibi(p, library, beacon_pos=(p["beacon_pos"] + 3).astype(np.int32))
+    assert np.max(np.abs(out3 - out)) > 1e-6, "beacon positions have no effect"
+
+
+def pin_alibi_two_rows(library):
+    """One beacon and one raw row: a two-way softmax in closed form."""
+    p = alibi_problem(74, B=1, Hkv=1, G=1, d=8, nb=1, rk=4, rv=4, w=1, q_pos=50)
+    p["beacon_pos"] = np.array([20], dtype=np.int32)
+    out, lse = run_alibi(p, library)
+    q = p["q"][0, 0]
+    kb = p["U_K"][0] @ p["C_K"][0, 0, 0]
+    vb = p["U_V"][0] @ p["C_V"][0, 0, 0]
+    m = p["slopes"][0]
+    s0 = p["scale"] * q @ kb - m * 30.0          # beacon at distance 30
+    s1 = p["scale"] * q @ p["K_raw"][0, 0, 0]    # the raw row sits at the query's position
+    a0 = 1.0 / (1.0 + np.exp(s1 - s0))
+    _close(out[0, 0], a0 * vb + (1.0 - a0) * p["V_raw"][0, 0, 0], what="two-row alibi")
+    _close(lse[0, 0], np.logaddexp(s0, s1), what="two-row alibi lse")
+
+
+def pin_alibi_steep(library):
+    """A steep slope leaves only the nearest row: the raw row at the query's
+    position."""
+    p = alibi_problem(75, B=2, Hkv=1, G=2, d=16, nb=5, rk=4, rv=4, w=4, q_pos=100)
+    out, _ = run_alibi(p, library, slopes=np.full(2, 200.0))
+    for b in range(2):
+        for hq in range(2):
+            _close(out[b, hq], p["V_raw"][b, 0, -1], tol=1e-12, what="steep alibi")
+
+
 ALL_PINS = [
     pin_reconstruct_identity,
     pin_raw_only_rope_gqa,
@@ -621,4 +733,9 @@ ALL_PINS = [
     pin_chunk_causal,
     pin_chunk_without_new_tokens,
     pin_chunk_rounding,
+    pin_alibi_reference,
+    pin_alibi_zero_slopes,
+    pin_alibi_translation,
+    pin_alibi_two_rows,
+    pin_alibi_steep,
 ]

@@ -58,6 +58,15 @@ MUTANTS = {
                                     "const size_t v0 = (((size_t)b * ntok + 0) * H + h) * d;"),
     "chunk_rows_head_major": ("const size_t row = ((size_t)b * ntok + t) * Hq + hq;",
                               "const size_t row = ((size_t)b * Hq + hq) * ntok + t;"),
+    "alibi_bias_sign_flipped": ("s[j] = p->scale * acc - m_h * (qp - (double)bpos[j]);",
+                                "s[j] = p->scale * acc + m_h * (qp - (double)bpos[j]);"),
+    "alibi_bias_scaled": ("s[nb + t] = p->scale * acc - m_h * (qp - kpos);",
+                          "s[nb + t] = p->scale * (acc - m_h * (qp - kpos));"),
+    "alibi_raw_position_off_by_one": ("const double kpos = qp - (double)w + 1.0 + (double)t;",
+                                      "const double kpos = qp - (double)w + (double)t;"),
+    "alibi_slope_of_kv_head": ("const double m_h = slope[hq];", "const double m_h = slope[h];"),
+    "alibi_beacons_unbiased": ("s[j] = p->scale * acc - m_h * (qp - (double)bpos[j]);",
+                               "s[j] = p->scale * acc;"),
     "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
                                "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
