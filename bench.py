@@ -22,7 +22,7 @@ Reported beside the headline tokens/s:
     rotation of rebuilt beacon keys) and vs uncompressed full-KV attention
     over all 131072 tokens; the ragged serving step, over capacity-sized
     arrays and over a paged cache, and with 4 query tokens per sequence;
-    the 48-layer Qwen step;
+    the same step as an ALiBi backbone runs it; the 48-layer Qwen step;
   * the fp64 CPU oracle timed on a bounded sample on this host's cores.
 """
 
@@ -258,6 +258,8 @@ def main():
                                                                 args.steps, page_rows=64)
             result["comparison"]["c3_chunk4_step"] = chunk_step(lda, synth, torch, dev, wl, layers,
                                                                  args.steps, 4)
+            result["comparison"]["c3_alibi_step"] = alibi_step(lda, synth, torch, dev, wl, layers,
+                                                               args.steps)
             result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
 
     del ws
@@ -465,6 +467,38 @@ def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens):
                         f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + {Q} tokens"}
     log(f"chunk step: {res}")
     del ws, chunks
+    torch.cuda.empty_cache()
+    return res
+
+
+def alibi_step(lda, synth, torch, dev, wl, layers, steps):
+    """The same 32-layer step as an ALiBi backbone would run it
+    (slimkv_decode_attn_alibi: no rotation, the ALiBi paper's slopes, one
+    beacon per 16 tokens).  Bytes as for the headline step."""
+    import numpy as np
+    elem = wl.elem_bytes
+    probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+                                      rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                      scale=wl.scale) for x in layers]
+    ws = torch.zeros(max(lda.slimkv_workspace_bytes(p, lda.SLIMKV_OP_LATENT) for p in probs),
+                     dtype=torch.uint8, device=dev)
+    out, lse = lda.alloc_outputs(probs[0], dev)
+    slopes = torch.as_tensor(synth.alibi_slopes(wl.num_q_heads).astype(np.float32), device=dev)
+    first, stride = synth.beacon_grid(16)
+
+    def step():
+        for p, x in zip(probs, layers):
+            lda.slimkv_decode_attn_alibi(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
+                                         x.V_raw, slopes, first, stride, out, lse, ws)
+
+    ms = replay_ms(torch, step, steps)
+    total = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
+    gbps = total / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
+           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    log(f"alibi step: {res}")
+    del ws
     torch.cuda.empty_cache()
     return res
 

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 6
+#define SLIMKV_ABI_VERSION 7
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -297,6 +297,38 @@ slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem,
                                        const void* k_new, const void* v_new,
                                        float* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * slimkv_decode_attn_alibi -- the latent decode attention of an ALiBi
+ * backbone.  Page "Can SlimKV compress KV cache jointly across tokens and
+ * features" notes that ALiBi adds its positional bias after the query-key
+ * product, so it composes with the latent beacon scores.  Such a backbone
+ * has no rotary embedding: neither the query nor any key is rotated (raw
+ * keys are stored as they are), and each score gets
+ *   s_j = scale * (q . k_j) - slopes[h_q] * (q_pos[b] - pos_j)
+ * (beacon scores in latent form, (q U_K) . C_K[j], as in
+ * slimkv_decode_attn), with the query head's slope, before the softmax.
+ * Key positions:
+ *   beacon j   pos_j = beacon_first + j * beacon_stride (e.g. one beacon
+ *              per s tokens at its last token: first s - 1, stride s);
+ *   raw row t  pos = q_pos[b] - W + 1 + t (the window ends at the query).
+ *
+ *   slopes  [H_q] fp32 (device), e.g. the ALiBi paper's geometric slopes
+ * beacon_first >= 0, beacon_stride >= 0 and the last beacon's position
+ * must fit in int32; distances are formed in int32 and converted to fp32
+ * (exact below 2^24).  Other arguments, layouts and the workspace
+ * (slimkv_workspace_bytes with SLIMKV_OP_LATENT) as for slimkv_decode_attn;
+ * rope_theta is unused but still checked.
+ */
+slimkv_status slimkv_decode_attn_alibi(const slimkv_problem* problem,
+                                       const void* q, const int32_t* q_pos,
+                                       const void* U_K, const void* U_V,
+                                       const void* C_K, const void* C_V,
+                                       const void* K_raw, const void* V_raw,
+                                       const float* slopes, int32_t beacon_first,
+                                       int32_t beacon_stride, float* out, float* lse,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * slimkv_reconstruct_attn -- comparison path: the decode step of the

@@ -25,6 +25,7 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
            "slimkv_decode_attn_paged", "slimkv_chunk_workspace_bytes", "slimkv_decode_attn_chunk",
+           "slimkv_decode_attn_alibi",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
            "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
@@ -102,6 +103,9 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_decode_attn_paged.argtypes = [prob, ctypes.POINTER(slimkv_pages)] + [vp] * 14 + [
         vp, sz, vp]
     lib.slimkv_decode_attn_paged.restype = ctypes.c_int
+    lib.slimkv_decode_attn_alibi.argtypes = [prob] + [vp] * 9 + [ctypes.c_int32, ctypes.c_int32] + [
+        vp, vp, vp, sz, vp]
+    lib.slimkv_decode_attn_alibi.restype = ctypes.c_int
     lib.slimkv_chunk_workspace_bytes.argtypes = [prob, ctypes.c_int32]
     lib.slimkv_chunk_workspace_bytes.restype = sz
     lib.slimkv_decode_attn_chunk.argtypes = [prob, ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
@@ -207,6 +211,16 @@ def slimkv_decode_attn_paged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw
         _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw),
         _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_decode_attn_alibi(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, slopes,
+                             beacon_first, beacon_stride, out, lse, workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_alibi(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(slopes), int(beacon_first), int(beacon_stride), _ptr(out),
+        _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def slimkv_chunk_workspace_bytes(problem: slimkv_problem, num_tokens: int) -> int:

@@ -231,13 +231,27 @@ slimkv_status check_pointers(const Range* in, int n_in, const Range* req, int n_
   return SLIMKV_OK;
 }
 
+// ALiBi parameters of a latent call (slopes null: a rotary call)
+struct Alibi {
+  const float* slopes = nullptr;  // [H_q] (device)
+  int32_t first = 0, stride = 0;  // beacon j at first + j * stride
+};
+
 slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const int32_t* q_pos,
                   const void* U_K, const void* U_V, const void* C_K, const void* C_V,
                   const void* K_raw, const void* V_raw, float* out, float* lse, void* ws,
-                  size_t ws_bytes, void* stream, const int32_t* beacon_pos = nullptr) {
+                  size_t ws_bytes, void* stream, const int32_t* beacon_pos = nullptr,
+                  const Alibi& alibi = Alibi()) {
   Plan pl;
   slimkv_status st = make_plan(p, op, pl);
   if (st != SLIMKV_OK) return st;
+  if (alibi.slopes) {
+    const int64_t last = (int64_t)alibi.first + (int64_t)std::max(p->num_beacons - 1, 0) * alibi.stride;
+    if (alibi.stride < 0 || alibi.first < 0 || last > INT32_MAX)
+      return fail(SLIMKV_ERR_SHAPE, "beacon positions first %d + j * stride %d must be >= 0 and "
+                  "fit in int32", alibi.first, alibi.stride);
+    if ((uintptr_t)alibi.slopes % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "slopes is not 4-byte aligned");
+  }
   const size_t e = (size_t)pl.elem;
   const size_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = kHeadDim;
   const size_t nb = p->num_beacons, w = p->raw_window;
@@ -278,6 +292,11 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   if (st != SLIMKV_OK) return st;
   if (overlap(outs[0], in[1]) || overlap(outs[1], in[1]) || overlap(outs[2], in[1]))
     return fail(SLIMKV_ERR_ALIAS, "an output overlaps q_pos");
+  if (alibi.slopes) {
+    const Range sl{alibi.slopes, Hq * sizeof(float), "slopes"};
+    for (const Range& o : outs)
+      if (overlap(o, sl)) return fail(SLIMKV_ERR_ALIAS, "%s overlaps slopes", o.name);
+  }
   if (beacon_pos) {
     const Range bp{beacon_pos, nb * sizeof(int32_t), "beacon_pos"};
     if ((uintptr_t)beacon_pos % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "beacon_pos is not 4-byte aligned");
@@ -305,6 +324,9 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
   a.out = out;
   a.lse = lse;
+  a.alibi_slopes = alibi.slopes;
+  a.beacon_first = alibi.first;
+  a.beacon_stride = alibi.stride;
   if (beacons) {
     a.seg[0].K = op == SLIMKV_OP_LATENT ? C_K : wsb + pl.off_kb;
     a.seg[0].V = op == SLIMKV_OP_LATENT ? C_V : wsb + pl.off_vb;
@@ -596,6 +618,22 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem, const slim
   return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
                             num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
                             workspace_bytes, stream, true);
+}
+
+slimkv_status slimkv_decode_attn_alibi(const slimkv_problem* problem, const void* q,
+                                       const int32_t* q_pos, const void* U_K, const void* U_V,
+                                       const void* C_K, const void* C_V, const void* K_raw,
+                                       const void* V_raw, const float* slopes,
+                                       int32_t beacon_first, int32_t beacon_stride, float* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!slopes) return slimkv::fail(SLIMKV_ERR_NULL, "slopes is NULL");
+  slimkv::Alibi al;
+  al.slopes = slopes;
+  al.first = beacon_first;
+  al.stride = beacon_stride;
+  return slimkv::run(problem, SLIMKV_OP_LATENT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
+                     lse, workspace, workspace_bytes, stream, nullptr, al);
 }
 
 size_t slimkv_chunk_workspace_bytes(const slimkv_problem* problem, int32_t num_tokens) {

@@ -82,6 +82,11 @@ struct AttnArgs {
   // Chunk calls: query tokens per sequence (q, out [B, Q, H_q, d], lse
   // [B, Q, H_q], k_new, v_new [B, Q, H_kv, d]); partials hold G * Q rows
   int32_t num_tokens;
+  // ALiBi calls (alibi_slopes set): nothing is rotated and score j gets
+  // -slope[h_q] * (q_pos - k_pos); beacon j at beacon_first + j *
+  // beacon_stride, raw row t at q_pos - W + 1 + t
+  const float* alibi_slopes;  // [H_q]
+  int32_t beacon_first, beacon_stride;
 };
 
 struct RebuildArgs {

@@ -294,13 +294,14 @@ struct QueryPrologue {
         }
       }
     }
+    const bool rotate = a.alibi_slopes == nullptr;  // an ALiBi backbone rotates nothing
 #pragma unroll
     for (int j = 0; j < kPairs; ++j) {
       const int p = tid + kThreads * j;
       if (p < G * kHalf) {
         const int g = p / kHalf, i = p % kHalf;
-        float sn, cs;
-        rope_sincos(a, pos, i, sn, cs);
+        float sn = 0.0f, cs = 1.0f;
+        if (rotate) rope_sincos(a, pos, i, sn, cs);
         const float v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
         const float sc = (float)a.score_scale;
         sh.qrot[g][i] = (v1 * cs - v2 * sn) * sc;
@@ -630,12 +631,17 @@ struct TileFeed {
 // past pend the slots take the tail's addresses instead).  Positions from
 // pend on are not this sweep's to process.  On exit j is the first position
 // past this segment (or pend) the wave drew.
-template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG>
+//
+// ALIBI: each score also gets slope2[i] * (row * astep - adist0) for head
+// 4kg + i (slope2 = the head's slope times log2 e; row * astep - adist0 =
+// k_pos - q_pos for this segment's row, an affine function of the row).
+template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG, bool ALIBI = false>
 __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbase,
                                       const SegView<NCH2, BF16, PG>& nx, int nxbase, int pend, int& j,
                                       TileFeed& feed, const TailRows& tail, const float* qsrc, int rq,
                                       u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
-                                      WaveState<G, BF16>& st) {
+                                      WaveState<G, BF16>& st, const float* slope2 = nullptr,
+                                      int adist0 = 0, int astep = 0) {
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
@@ -696,6 +702,11 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbas
                                                        d, 0, 0, 0);
           }
         }
+      }
+      if constexpr (ALIBI) {
+        const float x = (float)((t0 + 16 * s + n) * astep - adist0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = fmaf(slope2[i], x, d[i]);
       }
       if (t0 + 16 * s + n >= r1) d = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       sc[s] = d;
@@ -1174,7 +1185,7 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
 // page ids, then its raw page ids.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
-template <int G, int NCH, bool BF16, bool RAGGED, bool PG = false>
+template <int G, int NCH, bool BF16, bool RAGGED, bool PG = false, bool ALIBI = false>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, int unit, int b, int h,
                                             int c, int k, int nbr, int wr, int slot0,
                                             const int32_t* ptab = nullptr) {
@@ -1240,15 +1251,28 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   pro.finish(a, sh, wave);
 
   float* pw = sh.u.s.t.p[wave];
+  // ALiBi: this lane's heads' slopes in log2 units, and each segment's
+  // k_pos - q_pos as row * step - dist0
+  float slope2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int bdist0 = 0, rdist0 = 0;
+  if constexpr (ALIBI) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      slope2[i] = a.alibi_slopes[h * G + min(4 * kg + i, G - 1)] * 1.4426950408889634f;
+    bdist0 = a.q_pos[b] - a.beacon_first;
+    rdist0 = wr - 1;
+  }
   WaveState<G, BF16> st;
   st.reset();
-  sweep<G, BN, BF16, true>(bv, 0, rw, nbt, total, j, feed, tail,
-                           BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf, pw, st);
+  sweep<G, BN, BF16, true, kFullNch, PG, ALIBI>(bv, 0, rw, nbt, total, j, feed, tail,
+                                          BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf,
+                                          pw, st, slope2, bdist0, a.beacon_stride);
   wave_reduce<G, BF16>(st, bv.lpr);
   wave_park<G, BN, BF16, PG>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
   st.reset();
-  sweep<G, kFullNch, BF16, false>(rw, nbt, rw, total, total, j, feed, tail, &sh.qrot[0][0], kHeadDim,
-                                  kbuf, vbuf, pw, st);
+  sweep<G, kFullNch, BF16, false, kFullNch, PG, ALIBI>(rw, nbt, rw, total, total, j, feed, tail,
+                                                       &sh.qrot[0][0], kHeadDim, kbuf, vbuf, pw, st,
+                                                       slope2, rdist0, 1);
   // From here on the wave only finishes the unit: raise its issue priority
   // over the waves on its SIMD that are still streaming tiles, so the tail
   // (on the critical path of the whole call) is not starved by them.
@@ -1300,7 +1324,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
 // unit made of consecutive blocks, or of blocks on one XCD, would run at the
 // speed of its slot or its XCD.  This numbering gives every unit workgroups
 // of every age on different XCDs, so the units finish together.
-template <int G, int NCH, bool BF16>
+template <int G, int NCH, bool BF16, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int k = a.chunks;
@@ -1310,30 +1334,40 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int unit = (int)(((int64_t)blockIdx.x - (int64_t)c * units + c) % units);
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
-  attend_unit<G, NCH, BF16, false>(a, sh, unit, b, h, c, k, a.seg[0].rows, a.seg[1].rows, unit * k);
+  attend_unit<G, NCH, BF16, false, false, ALIBI>(a, sh, unit, b, h, c, k, a.seg[0].rows,
+                                                 a.seg[1].rows, unit * k);
 }
 
 // Workgroup slots the grid fills on the current device: CUs x resident
 // workgroups of `kfn` per CU (at most kWgPerCu), cached per (device, kernel).
 int device_slots(const void* kfn);
 
-// Launch for group size G; nch is the MFMA chunk count of a latent beacon
-// segment (1..4 for bf16; fp32 uses 8), 0 for full-width or absent beacons.
+// The kernel for group size G; nch is the MFMA chunk count of a latent
+// beacon segment (1..4 for bf16; fp32 uses 8), 0 for full-width or absent
+// beacons.
+template <int G, bool ALIBI>
+const void* attention_kernel_for(int dtype, int nch) {
+  if (dtype == 0)
+    return nch == 0 ? reinterpret_cast<const void*>(&attention_kernel<G, 0, false, ALIBI>)
+                    : reinterpret_cast<const void*>(&attention_kernel<G, 8, false, ALIBI>);
+  switch (nch) {
+    case 0: return reinterpret_cast<const void*>(&attention_kernel<G, 0, true, ALIBI>);
+    case 1: return reinterpret_cast<const void*>(&attention_kernel<G, 1, true, ALIBI>);
+    case 2: return reinterpret_cast<const void*>(&attention_kernel<G, 2, true, ALIBI>);
+    case 3: return reinterpret_cast<const void*>(&attention_kernel<G, 3, true, ALIBI>);
+    default: return reinterpret_cast<const void*>(&attention_kernel<G, 4, true, ALIBI>);
+  }
+}
+
+// Launch for group size G (nch as for attention_kernel_for).
 template <int G>
 hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s, hipEvent_t ev0,
                                   hipEvent_t ev1) {
   const void* kfn;
-  if (dtype == 0) {
-    kfn = nch == 0 ? reinterpret_cast<const void*>(&attention_kernel<G, 0, false>)
-                   : reinterpret_cast<const void*>(&attention_kernel<G, 8, false>);
+  if (a.alibi_slopes) {
+    kfn = attention_kernel_for<G, true>(dtype, nch);
   } else {
-    switch (nch) {
-      case 0: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 0, true>); break;
-      case 1: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 1, true>); break;
-      case 2: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 2, true>); break;
-      case 3: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 3, true>); break;
-      default: kfn = reinterpret_cast<const void*>(&attention_kernel<G, 4, true>); break;
-    }
+    kfn = attention_kernel_for<G, false>(dtype, nch);
   }
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   if (a.chunks <= 0) {

@@ -478,3 +478,38 @@ def assert_chunk_rows(K_after, V_after, K_before, V_before, ch: synth.ChunkInput
         "V_raw: other rows written"
     print(f"[parity] chunk rows: {int(mask.sum())} written, {off_by_ulp} key elements one ulp off",
           flush=True)
+
+
+def run_gpu_alibi(inp: synth.LayerInputs, slopes: np.ndarray, first: int, stride: int, *,
+                  num_splits: int = 0, device="cuda"):
+    """slimkv_decode_attn_alibi on ``inp`` with per-query-head slopes and
+    beacon j at first + j * stride; returns (out, lse) on the host."""
+    wl = inp.workload
+    g = inp.to(device)
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=num_splits)
+    out, lse = lda.alloc_outputs(prob, device)
+    ws = lda.alloc_workspace(prob, lda.SLIMKV_OP_LATENT, device)
+    sl = torch.as_tensor(np.asarray(slopes, dtype=np.float32), device=device)
+    nb, w = inp.num_beacons, inp.raw_window
+    lda.slimkv_decode_attn_alibi(prob, g.q, g.q_pos, g.U_K if nb else None, g.U_V if nb else None,
+                                 g.C_K if nb else None, g.C_V if nb else None,
+                                 g.K_raw if w else None, g.V_raw if w else None, sl, first, stride,
+                                 out, lse, ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def oracle_alibi(inp: synth.LayerInputs, slopes: np.ndarray, first: int, stride: int, units=None):
+    """oracle.decode_alibi on the whole layer (or the listed units); the
+    slopes are taken as the fp32 values the GPU receives."""
+    wl = inp.workload
+    st = synth.to_numpy_storage
+    nb, w = inp.num_beacons, inp.raw_window
+    bpos = (first + stride * np.arange(nb)).astype(np.int32)
+    return oracle.decode_alibi(
+        st(inp.q), st(inp.q_pos), st(inp.U_K), st(inp.U_V), st(inp.C_K) if nb else None,
+        st(inp.C_V) if nb else None, st(inp.K_raw) if w else None, st(inp.V_raw) if w else None,
+        beacon_pos=bpos, slopes=np.asarray(slopes, dtype=np.float32).astype(np.float64),
+        num_kv_heads=wl.num_kv_heads, scale=wl.scale, units=units)

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 6
+    assert lda.slimkv_abi_version() == 7
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -349,6 +349,29 @@ def test_chunk_checks(lib):
     assert _call_chunk(lib, prob, 3, ptrs=dict(lse=0x240000 - lse_bytes + 4)) == ALIAS
     # the raw window is written with new tokens
     assert _call_chunk(lib, prob, 2, ptrs=dict(k_new=0x3000000 + 64)) == ALIAS
+
+
+def test_alibi_checks(lib):
+    prob = _problem()
+    v = {k: ctypes.c_void_p(x) for k, x in dict(q=0x100000, q_pos=0x200000, U_K=0x300000,
+                                                 U_V=0x400000, C_K=0x1000000, C_V=0x2000000,
+                                                 K_raw=0x3000000, V_raw=0x4000000, sl=0x210000,
+                                                 out=0x5000000, lse=0x6000000,
+                                                 ws=0x7000000).items()}
+
+    def call(sl=v["sl"], first=15, stride=16, lse=v["lse"], p=prob):
+        return lib.slimkv_decode_attn_alibi(ctypes.byref(p), v["q"], v["q_pos"], v["U_K"],
+                                            v["U_V"], v["C_K"], v["C_V"], v["K_raw"], v["V_raw"],
+                                            sl, first, stride, v["out"], lse, v["ws"], 16, None)
+    assert call() == WS  # every pointer check passes; the workspace is too small
+    assert call(sl=None) == NULL and "slopes" in lda.slimkv_last_error()
+    assert call(sl=ctypes.c_void_p(0x210002)) == ALIGN
+    assert call(stride=-1) == SHAPE
+    assert call(first=-5) == SHAPE
+    assert call(first=2**31 - 100, stride=16) == SHAPE  # the last of 64 beacons overflows int32
+    assert call(first=2**31 - 100, stride=0) == WS
+    assert call(lse=ctypes.c_void_p(0x210000 - 16)) == ALIAS  # lse runs into the slopes (8 heads)
+    assert call(lse=ctypes.c_void_p(0x210000 - 64)) == WS
 
 
 def test_reconstruct_rope_checks(lib):
