@@ -223,7 +223,7 @@ __device__ __forceinline__ void rope_sincos(const AttnArgs& a, int pos, int i, f
 // its first cache tile and calls finish().  Memory returns in request order,
 // so the prologue's inputs arrive ahead of the tile and its arithmetic
 // overlaps the tile's flight.
-template <int G, bool BF16, int NCH>
+template <int G, bool BF16, int NCH, bool ROTATE = true>
 struct QueryPrologue {
   static constexpr bool kLat = NCH > 0;           // latent beacons: project the query
   static constexpr bool kStage = BF16 && kLat;    // U_K staged through LDS
@@ -294,18 +294,22 @@ struct QueryPrologue {
         }
       }
     }
-    const bool rotate = a.alibi_slopes == nullptr;  // an ALiBi backbone rotates nothing
 #pragma unroll
     for (int j = 0; j < kPairs; ++j) {
       const int p = tid + kThreads * j;
       if (p < G * kHalf) {
         const int g = p / kHalf, i = p % kHalf;
-        float sn = 0.0f, cs = 1.0f;
-        if (rotate) rope_sincos(a, pos, i, sn, cs);
         const float v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
         const float sc = (float)a.score_scale;
-        sh.qrot[g][i] = (v1 * cs - v2 * sn) * sc;
-        sh.qrot[g][i + kHalf] = (v2 * cs + v1 * sn) * sc;
+        if constexpr (ROTATE) {
+          float sn, cs;
+          rope_sincos(a, pos, i, sn, cs);
+          sh.qrot[g][i] = (v1 * cs - v2 * sn) * sc;
+          sh.qrot[g][i + kHalf] = (v2 * cs + v1 * sn) * sc;
+        } else {  // an ALiBi backbone rotates nothing
+          sh.qrot[g][i] = v1 * sc;
+          sh.qrot[g][i + kHalf] = v2 * sc;
+        }
       }
     }
     lds_barrier();
@@ -1237,7 +1241,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
 
   // the prologue's inputs, then the wave's first tile: the prologue's
   // arithmetic runs while the tile is in flight
-  QueryPrologue<G, BF16, NCH> pro;
+  QueryPrologue<G, BF16, NCH, !ALIBI> pro;
   pro.issue(a, b, h, wave);
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
   int j = wu;
