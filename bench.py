@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="only time the ragged serving step with Q query tokens per sequence "
                          "(slimkv_decode_attn_chunk) and print its figures as one JSON line")
+    ap.add_argument("--alibi", action="store_true",
+                    help="only time the step as an ALiBi backbone runs it (slimkv_decode_attn_alibi) "
+                         "and print its figures as one JSON line")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
                          "reduction, for scaling hardware byte counters and as a read ceiling")
@@ -143,6 +146,9 @@ def main():
     if args.ragged:
         print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps,
                                      page_rows=args.paged)), flush=True)
+        return
+    if args.alibi:
+        print(json.dumps(alibi_step(lda, synth, torch, dev, wl, layers, args.steps)), flush=True)
         return
     if args.chunk:
         print(json.dumps(chunk_step(lda, synth, torch, dev, wl, layers, args.steps, args.chunk)),

@@ -639,6 +639,11 @@ struct TileFeed {
 // ALIBI: each score also gets slope2[i] * (row * astep - adist0) for head
 // 4kg + i (slope2 = the head's slope times log2 e; row * astep - adist0 =
 // k_pos - q_pos for this segment's row, an affine function of the row).
+// The bias grows towards the query, so the positions of a segment map to
+// its tiles in reverse (position p -> tile ntiles - 1 - p): each wave takes
+// its nearest tiles first, and its running max stops growing after its
+// first tile of the segment instead of growing (and rescaling every sum)
+// on every tile.
 template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG, bool ALIBI = false>
 __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbase,
                                       const SegView<NCH2, BF16, PG>& nx, int nxbase, int pend, int& j,
@@ -685,7 +690,7 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbas
   const int r1 = sv.rows;
 
   while (j < pstop) {
-    const int t0 = (j - pbase) * TR;
+    const int t0 = (ALIBI ? sv.ntiles - 1 - (j - pbase) : j - pbase) * TR;
 
     // -- scores on the matrix cores, log2 units (the query is pre-scaled)
     f32x4_t sc[SUB];
@@ -718,8 +723,10 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbas
     const int jn = feed.take(j);  // wave-uniform
     const bool more = jn < pstop;
     const bool cross = CROSS && !more && jn < pend;
-    const int pid = tile_page(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross);
-    load_tile_keys<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, pid,
+    const int ta = (ALIBI ? sv.ntiles - 1 - (jn - pbase) : jn - pbase) * TR;
+    const int tb = (ALIBI ? nx.ntiles - 1 - (jn - nxbase) : jn - nxbase) * TR2;
+    const int pid = tile_page(sv, ta, more, nx, tb, cross);
+    load_tile_keys<CROSS>(sv, ta, more, nx, tb, cross, tail, pid,
                           kbuf);
     feed.request(lane);
 
@@ -797,7 +804,7 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbas
           for (int e = 0; e < EPL; ++e) st.acc[g][e] = fmaf(pv[g], v[e], st.acc[g][e]);
       }
     }
-    load_tile_values<CROSS>(sv, (jn - pbase) * TR, more, nx, (jn - nxbase) * TR2, cross, tail, pid,
+    load_tile_values<CROSS>(sv, ta, more, nx, tb, cross, tail, pid,
                             vbuf);
     // the next tile overwrites pw: every lane has read it by now
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1246,7 +1253,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
   int j = wu;
   {
-    const int tb = j * SegView<BN, BF16, PG>::kRows, tr = (j - nbt) * SegView<kFullNch, BF16, PG>::kRows;
+    // (ALiBi: each segment's tiles in reverse, as in sweep)
+    const int tb = (ALIBI ? nbt - 1 - j : j) * SegView<BN, BF16, PG>::kRows;
+    const int tr = (ALIBI ? rw.ntiles - 1 - (j - nbt) : j - nbt) * SegView<kFullNch, BF16, PG>::kRows;
     const bool ub = j < nbt, ur = j >= nbt && j < total;
     const int pid = tile_page(bv, tb, ub, rw, tr, ur);
     load_tile_keys<true>(bv, tb, ub, rw, tr, ur, tail, pid, kbuf);
