@@ -58,6 +58,7 @@ struct alignas(16) ChunkShared {
     float park[kWaves][kChunkRows][kHeadDim];  // each wave's full-width sums
     struct {
       float kn[kChunkRows][kHeadDim];  // the chunk's new keys, rotated and rounded
+      float vn[kChunkRows][kHeadDim];  // their values
       float qf[kChunkRows][kHeadDim];  // the query rows rotated again, pre-scaled
     } fin;
   } u;
@@ -349,7 +350,10 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, i
 // ..), then, query row by query row, the chunk's tokens 0 .. t as one-row
 // partials (keys rotated at q_pos + u in fp64 and rounded once, i.e. the
 // rows the cache keeps); write out and lse; store the tokens' rows while
-// the window has room (w + u < its capacity).  A row with nothing to
+// the window has room (w + u < its capacity).  The tokens' keys and values
+// and the rotated query rows are staged in LDS first, so the per-token
+// steps wait for no memory; thread (m, c8) then owns 8 columns of query
+// row m (16 threads, one DPP row, per query row).  A row with nothing to
 // attend gets out 0 and lse -inf.
 __device__ __forceinline__ void chunk_finish(const AttnArgs& a, ChunkShared& sh, int u, int b, int h,
                                              int slot0, int nslots, int wlive, int M, int G) {
@@ -359,28 +363,8 @@ __device__ __forceinline__ void chunk_finish(const AttnArgs& a, ChunkShared& sh,
   const int pos0 = a.q_pos[b];
   constexpr int kHalf = kHeadDim / 2;
   if (a.k_new) {
-    for (int p = tid; p < Q * kHalf; p += kThreads) {
-      const int t = p / kHalf, i = p % kHalf;
-      const size_t kb = (((size_t)b * Q + t) * Hkv + h) * kHeadDim;
-      double s64, c64;
-      sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
-      const double k1 = (double)ld_elem<true>(a.k_new, kb + i);
-      const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
-      const uint32_t b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
-      const uint32_t b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
-      sh.u.fin.kn[t][i] = bits_to_float<true>(b1);
-      sh.u.fin.kn[t][i + kHalf] = bits_to_float<true>(b2);
-      if (wlive + t < wcap) {
-        const size_t row = ((size_t)u * wcap + wlive + t) * kHeadDim;
-        uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
-        uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
-        const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
-        kd[i] = (uint16_t)b1;
-        kd[i + kHalf] = (uint16_t)b2;
-        vd[i] = vs[i];
-        vd[i + kHalf] = vs[i + kHalf];
-      }
-    }
+    // the query rows first: their loads are then in flight with the tokens'
+    // (which come after stores to the cache that the compiler may not pass)
     for (int p = tid; p < M * kHalf; p += kThreads) {
       const int m = p / kHalf, i = p % kHalf;
       const int t = m / G, g = m - t * G;
@@ -392,76 +376,96 @@ __device__ __forceinline__ void chunk_finish(const AttnArgs& a, ChunkShared& sh,
       sh.u.fin.qf[m][i] = (v1 * cs - v2 * sn) * sc;
       sh.u.fin.qf[m][i + kHalf] = (v2 * cs + v1 * sn) * sc;
     }
-    lds_barrier();
+    for (int p = tid; p < Q * kHalf; p += kThreads) {
+      const int t = p / kHalf, i = p % kHalf;
+      const size_t kb = (((size_t)b * Q + t) * Hkv + h) * kHeadDim;
+      double s64, c64;
+      sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
+      const double k1 = (double)ld_elem<true>(a.k_new, kb + i);
+      const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
+      const uint32_t b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
+      const uint32_t b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
+      const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
+      const uint16_t v1 = vs[i], v2 = vs[i + kHalf];
+      sh.u.fin.kn[t][i] = bits_to_float<true>(b1);
+      sh.u.fin.kn[t][i + kHalf] = bits_to_float<true>(b2);
+      sh.u.fin.vn[t][i] = bits_to_float<true>(v1);
+      sh.u.fin.vn[t][i + kHalf] = bits_to_float<true>(v2);
+      if (wlive + t < wcap) {
+        const size_t row = ((size_t)u * wcap + wlive + t) * kHeadDim;
+        uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
+        uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
+        kd[i] = (uint16_t)b1;
+        kd[i + kHalf] = (uint16_t)b2;
+        vd[i] = v1;
+        vd[i + kHalf] = v2;
+      }
+    }
   }
-  const int c4 = tid & 31;
+  const int mm = tid / 16, c8 = tid & 15;  // query row, 8-column group
+  const int m = min(mm, M - 1);
   constexpr int kB = 8;
   const __amdgpu_buffer_rsrc_t rml =
       coherent_rsrc(a.part_ml + (size_t)slot0 * M * 2, (uint32_t)(nslots * M * 2 * 4));
   const __amdgpu_buffer_rsrc_t racc =
       coherent_rsrc(a.part_acc + (size_t)slot0 * M * kHeadDim, (uint32_t)(nslots * M * kHeadDim * 4));
-#pragma unroll 1
-  for (int pass = 0; pass < kChunkRows / 8; ++pass) {
-    const int m = min(tid / 32 + 8 * pass, M - 1);  // 32 threads per row
-    const bool mine = tid / 32 + 8 * pass < M;
-    float Mx = -INFINITY, L = 0.0f;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int s0 = 0; s0 < nslots; s0 += kB) {
-      uint32_t mlw[kB][2];
-      u32x4_t v[kB];
+  float Mx = -INFINITY, L = 0.0f;
+  f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int s0 = 0; s0 < nslots; s0 += kB) {
+    uint32_t mlw[kB][2];
+    u32x4_t v[kB][2];
 #pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        const int s = min(s0 + k, nslots - 1);
-        const int base = (s * M + m) * 8;
-        mlw[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rml, base, 0, kCoherent);
-        mlw[k][1] = __builtin_amdgcn_raw_buffer_load_b32(rml, base + 4, 0, kCoherent);
-        v[k] = __builtin_amdgcn_raw_buffer_load_b128(racc, ((s * M + m) * kHeadDim + 4 * c4) * 4, 0,
-                                                    kCoherent);
-      }
+    for (int k = 0; k < kB; ++k) {
+      const int s = min(s0 + k, nslots - 1);
+      const int base = (s * M + m) * 8;
+      mlw[k][0] = __builtin_amdgcn_raw_buffer_load_b32(rml, base, 0, kCoherent);
+      mlw[k][1] = __builtin_amdgcn_raw_buffer_load_b32(rml, base + 4, 0, kCoherent);
 #pragma unroll
-      for (int k = 0; k < kB; ++k) {
-        if (s0 + k < nslots) {
-          const float mm = __uint_as_float(mlw[k][0]), ll = __uint_as_float(mlw[k][1]);
-          const float mn = fmaxf(Mx, mm);
-          if (mn != -INFINITY) {
-            const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(mm - mn);
-            L = L * a1 + ll * a2;
-            acc = acc * a1 + __builtin_bit_cast(f32x4_t, v[k]) * a2;
-            Mx = mn;
-          }
+      for (int hf = 0; hf < 2; ++hf)
+        v[k][hf] = __builtin_amdgcn_raw_buffer_load_b128(
+            racc, ((s * M + m) * kHeadDim + 8 * c8 + 4 * hf) * 4, 0, kCoherent);
+    }
+#pragma unroll
+    for (int k = 0; k < kB; ++k) {
+      if (s0 + k < nslots) {
+        const float ms = __uint_as_float(mlw[k][0]), ls = __uint_as_float(mlw[k][1]);
+        const float mn = fmaxf(Mx, ms);
+        if (mn != -INFINITY) {
+          const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(ms - mn);
+          L = L * a1 + ls * a2;
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            acc[hf] = acc[hf] * a1 + __builtin_bit_cast(f32x4_t, v[k][hf]) * a2;
+          Mx = mn;
         }
       }
     }
-    const int t = m / G, g = m - t * G;
-    if (a.k_new) {
-      // the chunk's tokens 0 .. t; the score is summed over the row's 32 threads
-      for (int tk = 0; tk <= t; ++tk) {
-        float dot = 0.0f;
+  }
+  const int t = m / G, g = m - t * G;
+  if (a.k_new) {
+    lds_barrier();  // the staged tokens and query rows
+    for (int tk = 0; tk <= t; ++tk) {  // the 16 threads of a row share t
+      float dot = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot += sh.u.fin.qf[m][4 * c4 + e] * sh.u.fin.kn[tk][4 * c4 + e];
-        dot = xor16_sum(row16_sum(dot));
-        const size_t vb = (((size_t)b * Q + tk) * Hkv + h) * kHeadDim + 4 * c4;
-        f32x4_t vn;
+      for (int e = 0; e < 8; ++e) dot += sh.u.fin.qf[m][8 * c8 + e] * sh.u.fin.kn[tk][8 * c8 + e];
+      dot = row16_sum(dot);
+      const float mn = fmaxf(Mx, dot);
+      const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(dot - mn);
+      L = L * a1 + a2;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vn[e] = ld_elem<true>(a.v_new, vb + e);
-        const float mn = fmaxf(Mx, dot);
-        const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(dot - mn);
-        L = L * a1 + a2;
-        acc = acc * a1 + vn * a2;
-        Mx = mn;
-      }
+      for (int hf = 0; hf < 2; ++hf)
+        acc[hf] = acc[hf] * a1 + *reinterpret_cast<const f32x4_t*>(&sh.u.fin.vn[tk][8 * c8 + 4 * hf]) * a2;
+      Mx = mn;
     }
-    if (mine) {
-      const size_t row = ((size_t)b * Q + t) * Hq + (size_t)h * G + g;
-      float* out = a.out + row * kHeadDim + 4 * c4;
-      if (L > 0.0f) {
-        *reinterpret_cast<f32x4_t*>(out) = acc * (1.0f / L);
-        if (a.lse && c4 == 0) a.lse[row] = (float)(0.69314718055994530942 * ((double)Mx + log2((double)L)));
-      } else {
-        *reinterpret_cast<f32x4_t*>(out) = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (a.lse && c4 == 0) a.lse[row] = -INFINITY;
-      }
-    }
+  }
+  if (mm < M) {
+    const size_t row = ((size_t)b * Q + t) * Hq + (size_t)h * G + g;
+    float* out = a.out + row * kHeadDim + 8 * c8;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) *reinterpret_cast<f32x4_t*>(out + 4 * hf) = acc[hf] * inv;
+    if (a.lse && c8 == 0)
+      a.lse[row] = L > 0.0f ? (float)(0.69314718055994530942 * ((double)Mx + log2((double)L))) : -INFINITY;
   }
 }
 
@@ -487,9 +491,22 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   SegView<4, true> rw;
   rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
-  TailRows tail;  // past the last tile: a 16-byte window on q, read past its end (zeros)
-  tail.r = make_rsrc(a.q, 16);
-  tail.klane = tail.vlane = 64;
+  // Past its last tile a wave's load slots fetch its quarter of the head's
+  // U_V for the lift (bytes 8192 wave .. +8191 of the 128 x r_V block: lanes
+  // 4j .. 4j+3 take 256-byte block j through their four key slots, 64 bytes
+  // apart, and block 16 + j through their value slots; bytes past the block
+  // read as zeros), so it arrives with the wave's last tile.  Without
+  // latent beacons the slots read a 16-byte window on q past its end.
+  TailRows tail;
+  if constexpr (BLAT) {
+    tail.r = make_rsrc(static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * 2,
+                       (uint32_t)(kHeadDim * rv * 2));
+    tail.klane = wave * 8192 + (lane & 3) * 16 + (lane >> 2) * 256;
+    tail.vlane = tail.klane + 4096;
+  } else {
+    tail.r = make_rsrc(a.q, 16);
+    tail.klane = tail.vlane = 64;
+  }
 
   ChunkPrologue<NCH> pro;
   pro.issue(a, b, h, M, G);
@@ -529,24 +546,21 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   __builtin_amdgcn_s_setprio(2);  // from here on only the unit's finish: ahead of streaming waves
   lds_barrier();  // every wave is done with the query and value tiles (U_V and the park alias them)
   if constexpr (BLAT) {
-    // U_V of head h staged in LDS (rows padded), then each wave lifts its
-    // latent sum: accr^T[d][m] += sum_k U_V[d][k] accb^T[k][m] per 16-row
-    // block of d; A operand lane (n, kg): U_V row 16 db + n, columns
-    // 16 cb + 4kg .. +3; B operand: the latent sum as hi + lo bf16 terms
-    const int ncb = rv / 16, upitch = rv + kVPad, words = kHeadDim * rv / 8;
-    const char* U = static_cast<const char*>(a.U_V) + (size_t)h * kHeadDim * rv * 2;
-    constexpr int kUw = kHeadDim * kHeadDim / 8 / kThreads;
-    u32x4_t uw[kUw];
+    // U_V of head h staged in LDS (rows padded) from the waves' tail loads,
+    // then each wave lifts its latent sum: accr^T[d][m] += sum_k U_V[d][k]
+    // accb^T[k][m] per 16-row block of d; A operand lane (n, kg): U_V row
+    // 16 db + n, columns 16 cb + 4kg .. +3; B operand: the latent sum as
+    // hi + lo bf16 terms
+    const int ncb = rv / 16, upitch = rv + kVPad, ubytes = kHeadDim * rv * 2;
 #pragma unroll
-    for (int w = 0; w < kUw; ++w) uw[w] = load16(U + (size_t)min(tid + kThreads * w, words - 1) * 16);
+    for (int i = 0; i < 2 * Traits<true>::kMaxLoads; ++i) {
+      const int off = (i < 4 ? tail.klane : tail.vlane) + 64 * (i & 3);
+      if (off < ubytes) {
+        const int row = off / (2 * rv), col = (off - row * 2 * rv) / 2;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(sh.u.uv + row * upitch + col);
+        const u32x4_t w = i < 4 ? kbuf[i] : vbuf[i - 4];
 #pragma unroll
-    for (int w = 0; w < kUw; ++w) {
-      const int idx = tid + kThreads * w;
-      if (idx < words) {
-        const int row = idx / (rv / 8), c8 = idx - row * (rv / 8);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(sh.u.uv + row * upitch + c8 * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = uw[w][e];
+        for (int e = 0; e < 4; ++e) dst[e] = w[e];
       }
     }
     lds_barrier();
