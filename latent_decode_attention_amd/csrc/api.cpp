@@ -530,6 +530,11 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   a.v_new = append ? v_new : nullptr;
   a.k_store = K_raw;
   a.v_store = V_raw;
+  // the pieces' partials use slots below units * kMaxChunks; the ragged
+  // workspace holds units * (kMaxChunks + 1) slots, so unit u's new-token
+  // partial takes slot units * kMaxChunks + u (chunk calls fold their
+  // tokens in the merge and use no token slot)
+  a.tok_slot0 = chunk > 0 ? 0 : (int32_t)(pl.units * kMaxChunks);
   if (paged) {
     a.page_table[0] = btab ? pg->beacon_table : nullptr;
     a.page_table[1] = rtab ? pg->raw_table : nullptr;

@@ -72,6 +72,7 @@ struct AttnArgs {
   const void* v_new;           // [B, H_kv, d] its value (with k_new)
   void* k_store;               // K_raw / V_raw: the new token's row is written at
   void* v_store;               //   index seq_raw[b] when that is below the capacity
+  int32_t tok_slot0;           // partial slot of unit 0's new-token partial (then one per unit)
   // Paged ragged calls (page_table[0] or [1] set): seg[s].K / V are then
   // pools [num_pages[s], H_kv, 1 << page_shift, width] and sequence b's row
   // i of segment s lies in page page_table[s][b * table_width[s] + (i >> page_shift)]

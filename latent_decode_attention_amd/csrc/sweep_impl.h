@@ -1059,26 +1059,115 @@ __device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
   }
 }
 
+// The decode step's new token as a one-row partial, made by the unit's first
+// workgroup in its prologue, while its first tile is in flight: thread
+// (g, c4) owns 16-byte column c4 of head g.  The token's key is rotated at
+// q_pos in fp64 and rounded once to the storage dtype -- the row the cache
+// keeps -- and scored against the rotated, pre-scaled query in LDS (summed
+// over the head's 32 threads); the partial (score, 1, value) goes to the
+// unit's token slot (a.tok_slot0 + u) with device-coherent stores, for the
+// merge.  The token's row is stored when the raw window has room (wlive <
+// its capacity): no workgroup reads that row in this call.  PG: through the
+// raw pages' ids at ptab[rtab0 ..] (no store if the id is out of range).
+template <int G, bool BF16>
+struct TokenPartial {
+  uint32_t k1[4], k2[4], v[4];  // storage bits: key elements i and their rotation partners, values
+  __device__ __forceinline__ void issue(const AttnArgs& a, int u) {
+    const int tid = threadIdx.x;
+    const int c4 = tid % (kHeadDim / 4);
+    const size_t kb = (size_t)u * kHeadDim;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * c4 + e;
+      k1[e] = ld_bits<BF16>(a.k_new, kb + i);
+      k2[e] = ld_bits<BF16>(a.k_new, kb + (i ^ (kHeadDim / 2)));
+      v[e] = ld_bits<BF16>(a.v_new, kb + i);
+    }
+  }
+  template <bool PG>
+  __device__ __forceinline__ void finish(const AttnArgs& a, const AttnShared& sh, int u, int b, int h,
+                                         int wlive, const int32_t* ptab, int rtab0) const {
+    const int tid = threadIdx.x;
+    const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+    const int pos = a.q_pos[b];
+    uint32_t kbits[4];
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * c4 + e, pi = i & (kHeadDim / 2 - 1);
+      double s64, c64;
+      sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
+      const double ki = (double)bits_to_float<BF16>(k1[e]), kp = (double)bits_to_float<BF16>(k2[e]);
+      kbits[e] = storage_bits_from_f64<BF16>(i < kHeadDim / 2 ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
+      dot += sh.qrot[g][i] * bits_to_float<BF16>(kbits[e]);
+    }
+    dot = xor16_sum(row16_sum(dot));  // the 32 threads of head g; log2 units (pre-scaled query)
+    const size_t slot = (size_t)a.tok_slot0 + u;
+    if (c4 == 0) {
+      store_coherent(&a.part_ml[(slot * G + g) * 2], dot);
+      store_coherent(&a.part_ml[(slot * G + g) * 2 + 1], 1.0f);
+    }
+    f32x4_t vf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vf[e] = bits_to_float<BF16>(v[e]);
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(a.part_acc + slot * G * kHeadDim, G * kHeadDim * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, vf), rs, (g * kHeadDim + 4 * c4) * 4,
+                                           0, kCoherent);
+    size_t row = ((size_t)u * a.seg[1].rows + wlive) * kHeadDim + 4 * c4;
+    bool store = g == 0 && wlive < a.seg[1].rows;
+    if constexpr (PG) {
+      const int sh_ = a.page_shift;
+      const int pid = store ? ptab[rtab0 + (wlive >> sh_)] : -1;
+      store = store && (uint32_t)pid < (uint32_t)a.num_pages[1];
+      row = (((((size_t)pid * a.num_kv_heads + h) << sh_) + (wlive & ((1 << sh_) - 1))) * kHeadDim) +
+            4 * c4;
+    }
+    if (store) {
+      if constexpr (BF16) {
+        uint32_t* kd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.k_store) + row);
+        uint32_t* vd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.v_store) + row);
+        kd[0] = kbits[0] | (kbits[1] << 16);
+        kd[1] = kbits[2] | (kbits[3] << 16);
+        vd[0] = v[0] | (v[1] << 16);
+        vd[1] = v[2] | (v[3] << 16);
+      } else {
+        float* kd = static_cast<float*>(a.k_store) + row;
+        float* vd = static_cast<float*>(a.v_store) + row;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kd[e] = __uint_as_float(kbits[e]);
+          vd[e] = __uint_as_float(v[e]);
+        }
+      }
+    }
+  }
+};
+
 // Merge for ragged calls (run by the unit's last workgroup): fold the unit's
 // nslots partials (slots slot0 ..) as merge_unit does, then the decode
-// step's new token as a one-row partial -- its key rotated at q_pos in fp64
-// and rounded once to the storage dtype, i.e. the row the cache keeps,
-// scored against the query rotated as in the prologue; write out and lse,
-// and store the token's row when the raw window has room (wlive < its
-// capacity).  Thread (g, c4) owns 16-byte column c4 of head g.  With no
-// rows at all the unit gets out 0 and lse -inf.  PG: the raw rows are
-// paged, the page ids of the unit's raw pages at ptab[rtab0 ..] (LDS); the
-// row goes to its page, or nowhere if the page id is out of range.
-template <int G, bool BF16, bool PG>
+// step's new token's one-row partial (see TokenPartial; its loads are
+// requested with the first partials', so the merge waits for memory
+// once); write out and lse.  Thread (g, c4) owns 16-byte column c4 of head
+// g.  With no rows at all the unit gets out 0 and lse -inf.
+template <int G, bool BF16>
 __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, int h, int slot0,
-                                              int nslots, int wlive, const int32_t* ptab,
-                                              int rtab0) {
+                                              int nslots) {
   const int tid = threadIdx.x;
   if (tid >= G * kHeadDim / 4) return;
   const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
   constexpr int kB = 8;
   float M = -INFINITY, L = 0.0f;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool tok = a.k_new != nullptr;
+  uint32_t tml = 0;
+  u32x4_t tacc = {0u, 0u, 0u, 0u};
+  if (tok) {
+    const size_t ts = (size_t)a.tok_slot0 + u;
+    const __amdgpu_buffer_rsrc_t tm = coherent_rsrc(a.part_ml + ts * G * 2, G * 2 * 4);
+    const __amdgpu_buffer_rsrc_t ta = coherent_rsrc(a.part_acc + ts * G * kHeadDim, G * kHeadDim * 4);
+    tml = __builtin_amdgcn_raw_buffer_load_b32(tm, g * 8, 0, kCoherent);
+    tacc = __builtin_amdgcn_raw_buffer_load_b128(ta, (g * kHeadDim + 4 * c4) * 4, 0, kCoherent);
+  }
   if (nslots > 0) {
     const __amdgpu_buffer_rsrc_t rml =
         coherent_rsrc(a.part_ml + (size_t)slot0 * G * 2, (uint32_t)(nslots * G * 2 * 4));
@@ -1111,67 +1200,15 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
       }
     }
   }
-  const size_t hq = (size_t)b * a.num_q_heads + (size_t)h * G + g;
-  if (a.k_new) {
-    // the new token: key rotated at q_pos in fp64 and rounded once to the
-    // storage dtype (the row the cache keeps), query rotated as in the
-    // prologue; the score is summed over the 32 threads of head g
-    const int pos = a.q_pos[b];
-    const size_t qb = hq * kHeadDim, kb = (size_t)u * kHeadDim;
-    float dot = 0.0f;
-    uint32_t kbits[4];
-    float vnew[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * c4 + e, pi = i & (kHeadDim / 2 - 1), ip = i ^ (kHeadDim / 2);
-      const bool lo = i < kHeadDim / 2;
-      float sn, cs;
-      rope_sincos(a, pos, pi, sn, cs);
-      const float qi = ld_elem<BF16>(a.q, qb + i), qp = ld_elem<BF16>(a.q, qb + ip);
-      const float qr = lo ? qi * cs - qp * sn : qi * cs + qp * sn;
-      double s64, c64;
-      sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
-      const double ki = (double)ld_elem<BF16>(a.k_new, kb + i), kp = (double)ld_elem<BF16>(a.k_new, kb + ip);
-      kbits[e] = storage_bits_from_f64<BF16>(lo ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
-      dot += qr * bits_to_float<BF16>(kbits[e]);
-      vnew[e] = ld_elem<BF16>(a.v_new, kb + i);
-    }
-    dot = xor16_sum(row16_sum(dot));  // the 32 lanes of head g
-    const float s2 = dot * (float)a.score_scale;
+  if (tok) {  // the token's partial: (score, 1, value)
+    const float s2 = __uint_as_float(tml);
     const float mn = fmaxf(M, s2);
     const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(s2 - mn);
     L = L * a1 + a2;
-    acc = acc * a1 + f32x4_t{vnew[0], vnew[1], vnew[2], vnew[3]} * a2;
+    acc = acc * a1 + __builtin_bit_cast(f32x4_t, tacc) * a2;
     M = mn;
-    size_t row = ((size_t)u * a.seg[1].rows + wlive) * kHeadDim + 4 * c4;
-    bool store = g == 0 && wlive < a.seg[1].rows;
-    if constexpr (PG) {
-      const int sh = a.page_shift;
-      const int pid = store ? ptab[rtab0 + (wlive >> sh)] : -1;
-      store = store && (uint32_t)pid < (uint32_t)a.num_pages[1];
-      row = (((((size_t)pid * a.num_kv_heads + h) << sh) + (wlive & ((1 << sh) - 1))) * kHeadDim) +
-            4 * c4;
-    }
-    if (store) {
-      if constexpr (BF16) {
-        uint32_t* kd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.k_store) + row);
-        uint32_t* vd = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.v_store) + row);
-        const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb + 4 * c4;
-        kd[0] = kbits[0] | (kbits[1] << 16);
-        kd[1] = kbits[2] | (kbits[3] << 16);
-        vd[0] = (uint32_t)vs[0] | ((uint32_t)vs[1] << 16);
-        vd[1] = (uint32_t)vs[2] | ((uint32_t)vs[3] << 16);
-      } else {
-        float* kd = static_cast<float*>(a.k_store) + row;
-        float* vd = static_cast<float*>(a.v_store) + row;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kd[e] = __uint_as_float(kbits[e]);
-          vd[e] = vnew[e];
-        }
-      }
-    }
   }
+  const size_t hq = (size_t)b * a.num_q_heads + (size_t)h * G + g;
   float* out = a.out + hq * kHeadDim + 4 * c4;
   if (L > 0.0f) {
     *reinterpret_cast<f32x4_t*>(out) = acc * (1.0f / L);
@@ -1250,6 +1287,10 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   // arithmetic runs while the tile is in flight
   QueryPrologue<G, BF16, NCH, !ALIBI> pro;
   pro.issue(a, b, h, wave);
+  // ragged calls: the unit's first workgroup makes the new token's partial
+  TokenPartial<G, BF16> tokp;
+  const bool tok = RAGGED && c == 0 && a.k_new != nullptr && tid < G * kHeadDim / 4;
+  if (tok) tokp.issue(a, unit);
   u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
   int j = wu;
   {
@@ -1262,6 +1303,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
     load_tile_values<true>(bv, tb, ub, rw, tr, ur, tail, pid, vbuf);
   }
   pro.finish(a, sh, wave);
+  if constexpr (RAGGED)
+    if (tok) tokp.template finish<PG>(a, sh, unit, b, h, wr, ptab, nbp);
 
   float* pw = sh.u.s.t.p[wave];
   // ALiBi: this lane's heads' slopes in log2 units, and each segment's
@@ -1325,7 +1368,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (RAGGED)
-    ragged_finish<G, BF16, PG>(a, unit, b, h, slot0, k, wr, ptab, nbp);
+    ragged_finish<G, BF16>(a, unit, b, h, slot0, k);
   else
     merge_unit<G>(a, unit, b, h);
 }
