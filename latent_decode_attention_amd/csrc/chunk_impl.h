@@ -645,23 +645,17 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(
   constexpr int BN = NCH > 0 ? NCH : 4;
   constexpr int TRB = SegView<BN, true>::kRows, TRR = SegView<4, true>::kRows;
   __shared__ ChunkShared sh;
-  __shared__ RaggedShared rs;
+  __shared__ RaggedPick pick;
   const int tid = threadIdx.x;
-  const int B = a.batch, Hkv = a.num_kv_heads, P = a.chunks;
-  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, rs, tid & 63, P);
+  const int Hkv = a.num_kv_heads, P = a.chunks;
+  const int pi = ragged_piece_of((int)blockIdx.x, P);
+  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, pick, tid & 63, P, pi);
   lds_barrier();
   const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-  const int pi = ragged_piece_of((int)blockIdx.x, P);
-  if (pi >= uni(rs.kpre[B])) return;
-  int lo = 0, hi = B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (uni(rs.kpre[mid]) <= pi) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int kb = uni(rs.k[b]), first = uni(rs.kpre[b]);
+  if (pi >= uni(pick.total)) return;
+  const int b = uni(pick.b), kb = uni(pick.k), first = uni(pick.first);
   const int h = (pi - first) / kb, c = pi - first - h * kb;
-  chunk_unit<NCH>(a, sh, b * Hkv + h, b, h, c, kb, uni(rs.nb[b]), uni(rs.w[b]), first + h * kb);
+  chunk_unit<NCH>(a, sh, b * Hkv + h, b, h, c, kb, uni(pick.nb), uni(pick.w), first + h * kb);
 }
 
 }  // namespace slimkv

@@ -21,7 +21,8 @@
 //     dealt round-robin over all its pieces' waves, one partial per piece,
 //     the last piece merging.
 //   * Each workgroup recomputes the schedule from the lengths at its start:
-//     one wave loads them and scans into LDS.
+//     one wave loads them, finds the share and finds its own piece, with
+//     wave-wide sums on the VALU (no LDS tables, no shuffles through LDS).
 //   * Pieces alternate between the CUs' first and second workgroup slots
 //     and spread over the XCDs (see ragged_piece_of).
 //   * The merge also folds in the new token as a one-row partial (its score
@@ -37,33 +38,77 @@
 
 namespace slimkv {
 
-// Per-workgroup schedule: sequence b's H_kv units each have k[b] pieces
-// (workgroups), the first of them numbered kpre[b]; nb, w are its live row
-// counts.
-struct RaggedShared {
-  int32_t kpre[kMaxRaggedBatch + 1];
-  int32_t k[kMaxRaggedBatch];
-  int32_t nb[kMaxRaggedBatch];
-  int32_t w[kMaxRaggedBatch];
+// The piece a workgroup runs: workgroup c of the k that share unit
+// (b, h), c = (pi - first) % k, h = (pi - first) / k; sequence b has nb, w
+// live rows; total pieces in the batch (a workgroup with pi >= total has
+// nothing to do).
+struct RaggedPick {
+  int32_t b, first, k, nb, w, total;
 };
+
+// Wave-wide sums and maxima of integers on the VALU (DPP rotations within
+// 16-lane rows, then permlane swaps across rows): no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp_i<0x128>(x);
+  x += dpp_i<0x124>(x);
+  x += dpp_i<0x122>(x);
+  x += dpp_i<0x121>(x);
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(r[0] + r[1]);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, dpp_i<0x128>(x));
+  x = max(x, dpp_i<0x124>(x));
+  x = max(x, dpp_i<0x122>(x));
+  x = max(x, dpp_i<0x121>(x));
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = max((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+// Inclusive prefix sum over the wave's lanes: shifts within 16-lane rows
+// (lanes past a row's start read zero), then each row adds the totals of
+// the rows before it.
+__device__ __forceinline__ int wave_scan_i(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
 
 // Run by one wave: live rows clamped to [0, capacity], the tiles t of each
 // of a sequence's units, and the pieces (workgroups) per unit
 // k = clamp(ceil(t / L), 1, kMaxChunks) for the smallest share L (tiles per
 // piece) at which all pieces fit in the P workgroup slots -- so the busiest
 // workgroup has as few tiles as the slots allow -- or one piece per unit if
-// even that does not fit.  A unit without rows still gets its piece.  k is
-// scanned over the sequences into kpre (lane L takes a run of consecutive
-// sequences; every load is requested before any is used).
+// even that does not fit.  A unit without rows still gets its piece.  The
+// pieces are numbered sequence by sequence (lane L takes a run of
+// consecutive sequences; every load is requested before any is used), and
+// the lane whose sequence holds piece pi writes it to `pick`.
 template <int TRB, int TRR>
-__device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedShared& rs, int lane, int P) {
+__device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedPick& pick, int lane, int P,
+                                                int pi) {
   constexpr int kPer = kMaxRaggedBatch / 64;
   const int B = a.batch, ncap = a.seg[0].rows, wcap = a.seg[1].rows, Hkv = a.num_kv_heads;
+  // Every per-lane loop below stops after `per` (wave-uniform) iterations:
+  // unrolled to kPer with only a guard, the divisions of all kPer
+  // iterations would run under an execution mask at every step of the search.
   const int per = (B + 63) / 64;
   const int b0 = lane * per;
   int nbv[kPer], wv[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
+    if (k == per) break;
     const int b = min(b0 + k, B - 1);
     nbv[k] = a.seq_beacons ? a.seq_beacons[b] : ncap;
     wv[k] = a.seq_raw ? a.seq_raw[b] : wcap;
@@ -72,43 +117,35 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedShared&
   int sum = 0, tmax = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    const int nbc = min(max(nbv[k], 0), ncap), wc = min(max(wv[k], 0), wcap);
-    const bool mine = k < per && b0 + k < B;
-    tiles[k] = mine ? (nbc + TRB - 1) / TRB + (wc + TRR - 1) / TRR : -1;  // -1: not a sequence
+    if (k == per) break;
+    nbv[k] = min(max(nbv[k], 0), ncap);
+    wv[k] = min(max(wv[k], 0), wcap);
+    const bool mine = b0 + k < B;
+    tiles[k] = mine ? (nbv[k] + TRB - 1) / TRB + (wv[k] + TRR - 1) / TRR : -1;  // -1: not a sequence
     if (mine) {
-      rs.nb[b0 + k] = nbc;
-      rs.w[b0 + k] = wc;
       sum += tiles[k];
       tmax = max(tmax, tiles[k]);
     }
   }
-  const auto wave_sum = [](int v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
-  };
-  const auto wave_max = [](int v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off, 64));
-    return v;
-  };
   const auto pieces = [](int t, int L) { return t < 0 ? 0 : min(max((t + L - 1) / L, 1), kMaxChunks); };
   // pieces of the whole batch at share L
   const auto count = [&](int L) {
     int c = 0;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (k < per) c += pieces(tiles[k], L);  // per is wave-uniform: no division past it
-    return wave_sum(c) * Hkv;
+    for (int k = 0; k < kPer; ++k) {
+      if (k == per) break;
+      c += pieces(tiles[k], L);
+    }
+    return wave_sum_i(c) * Hkv;
   };
-  const int64_t T = (int64_t)wave_sum(sum) * Hkv;
-  tmax = wave_max(tmax);
+  const int T = wave_sum_i(sum) * Hkv;  // the host checks that the batch's tiles fit in int32
+  tmax = wave_max_i(tmax);
   // L >= T / P, as P pieces must hold T tiles; and L = T / (P - units)
   // always fits (sum of ceil(t / L) <= T / L + units), which bounds the
   // search when the slots outnumber the units
   const int units = B * Hkv;
-  int lo = (int)max<int64_t>(1, (T + P - 1) / P), hi = max(lo, tmax);
-  if (P > units) hi = (int)min<int64_t>(hi, max<int64_t>(lo, (T + (P - units) - 1) / (P - units)));
+  int lo = max(1, (T + P - 1) / P), hi = max(lo, tmax);
+  if (P > units) hi = min(hi, max(lo, (T + (P - units) - 1) / (P - units)));
   if (count(lo) <= P) {
     hi = lo;
   } else if (count(hi) <= P) {  // the smallest L in (lo, hi] with count(L) <= P (count falls with L)
@@ -122,23 +159,25 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedShared&
   int psum = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    pk[k] = k < per ? pieces(tiles[k], L) : 0;
-    if (pk[k] > 0) rs.k[b0 + k] = pk[k];
+    if (k == per) break;
+    pk[k] = pieces(tiles[k], L);
     psum += pk[k] * Hkv;
   }
-  int incl = psum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += v;
-  }
+  const int incl = wave_scan_i(psum, lane);
   int run = incl - psum;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    if (pk[k] > 0) rs.kpre[b0 + k] = run;
+    if (k == per) break;
+    if (pk[k] > 0 && pi >= run && pi < run + pk[k] * Hkv) {
+      pick.b = b0 + k;
+      pick.first = run;
+      pick.k = pk[k];
+      pick.nb = nbv[k];
+      pick.w = wv[k];
+    }
     run += pk[k] * Hkv;
   }
-  if (lane == 63) rs.kpre[B] = incl;
+  if (lane == 63) pick.total = incl;
 }
 
 // Piece (workgroup slot) of block blk among the first P blocks, which take
@@ -170,26 +209,20 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel
   constexpr int BN = BLAT ? NCH : kFullNch;
   constexpr int TRB = SegView<BN, BF16>::kRows, TRR = SegView<kFullNch, BF16>::kRows;
   __shared__ AttnShared sh;
-  __shared__ RaggedShared rs;
+  __shared__ RaggedPick pick;
   __shared__ int32_t ptab[PG ? kMaxPageEntries : 1];
   const int tid = threadIdx.x;
-  const int B = a.batch, Hkv = a.num_kv_heads, P = a.chunks;
-  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, rs, tid & 63, P);
+  const int Hkv = a.num_kv_heads, P = a.chunks;
+  const int pi = ragged_piece_of((int)blockIdx.x, P);
+  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, pick, tid & 63, P, pi);
   lds_barrier();
   // values read back from LDS are the same in every lane: readfirstlane
   // keeps what derives from them (addresses, descriptors) in scalar registers
   const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-  const int pi = ragged_piece_of((int)blockIdx.x, P);
-  if (pi >= uni(rs.kpre[B])) return;  // workgroup-uniform
-  int lo = 0, hi = B;  // the sequence holding piece pi: the last b with kpre[b] <= pi
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (uni(rs.kpre[mid]) <= pi) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  const int kb = uni(rs.k[b]), first = uni(rs.kpre[b]);
+  if (pi >= uni(pick.total)) return;  // workgroup-uniform
+  const int b = uni(pick.b), kb = uni(pick.k), first = uni(pick.first);
   const int h = (pi - first) / kb, c = pi - first - h * kb;
-  const int nbr = uni(rs.nb[b]), wr = uni(rs.w[b]);
+  const int nbr = uni(pick.nb), wr = uni(pick.w);
   if constexpr (PG) {
     // at most ceil(N_cap / rows) + ceil(W_cap / rows) <= kMaxPageEntries ids
     const int sh_ = a.page_shift, pm = (1 << sh_) - 1;
