@@ -118,3 +118,12 @@ def test_c3_ragged_sampled(layer, gpu_device):
     assert_new_rows(K, V, inp.K_raw, inp.V_raw, step, k_app, units=units)
     del inp, K, V
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,splits", [(200, 0), (200, 150), (1024, 0)])
+def test_large_batches(B, splits, gpu_device):
+    """Batches past 64 sequences (each schedule lane takes several), with
+    more slots than units and with fewer (one piece per unit)."""
+    wl = custom(B=B, Hkv=1, G=4, nb=64, w=40, r=32, index=105 + B % 7)
+    fixed = {0: (0, 0), 1: (64, 40), B - 1: (70, -3), B // 2: (1, 0)}
+    check_ragged(wl, num_splits=splits, fixed=fixed, what=f"B={B} splits={splits}")
