@@ -183,7 +183,9 @@ slimkv_status make_chunk_plan(const slimkv_problem* p, int32_t num_tokens, Plan&
   if ((int64_t)G * num_tokens > kChunkRows)
     return fail(SLIMKV_ERR_UNSUPPORTED, "group %d x %d tokens exceeds %d query rows per KV head", G,
                 num_tokens, kChunkRows);
-  const int64_t M = (int64_t)G * num_tokens, slots = pl.units + kChunkMaxSlots;
+  // slots: the pieces' (at most max(units, kChunkMaxSlots)), then one for
+  // each unit's tokens
+  const int64_t M = (int64_t)G * num_tokens, slots = 2 * pl.units + kChunkMaxSlots;
   pl.attn.num_tokens = num_tokens;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
@@ -530,11 +532,10 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   a.v_new = append ? v_new : nullptr;
   a.k_store = K_raw;
   a.v_store = V_raw;
-  // the pieces' partials use slots below units * kMaxChunks; the ragged
-  // workspace holds units * (kMaxChunks + 1) slots, so unit u's new-token
-  // partial takes slot units * kMaxChunks + u (chunk calls fold their
-  // tokens in the merge and use no token slot)
-  a.tok_slot0 = chunk > 0 ? 0 : (int32_t)(pl.units * kMaxChunks);
+  // unit u's new-token partial takes the slot after all pieces' (ragged:
+  // pieces below units * kMaxChunks of units * (kMaxChunks + 1) slots;
+  // chunk: below units + kChunkMaxSlots of 2 units + kChunkMaxSlots)
+  a.tok_slot0 = (int32_t)(chunk > 0 ? pl.units + kChunkMaxSlots : pl.units * kMaxChunks);
   if (paged) {
     a.page_table[0] = btab ? pg->beacon_table : nullptr;
     a.page_table[1] = rtab ? pg->raw_table : nullptr;

@@ -31,8 +31,10 @@
 //     the layout of the full-width sum.  Each wave lifts its own latent sum
 //     after its last tile and parks one full-width sum.
 //   * Work is shared out by tiles as in the ragged kernel (ragged_schedule,
-//     ragged_piece_of); each workgroup writes one partial of M rows and the
-//     unit's last workgroup merges them and folds in the chunk's tokens.
+//     ragged_piece_of); each workgroup writes one partial of M rows; the
+//     unit's first workgroup also makes the chunk's tokens' partial before
+//     its sweep, while its first tiles are in flight; the unit's last
+//     workgroup merges them all.
 #pragma once
 
 namespace slimkv {
@@ -50,17 +52,14 @@ struct alignas(16) ChunkShared {
       union {
         uint16_t uk[64 * (kHeadDim + 2)];   // half of U_K's rows, padded (prologue)
         uint16_t vt[kWaves][kVTileElems];   // each wave's value tile (sweep)
+        float tok[2][kChunkRows][kHeadDim];  // the chunk's keys (rotated, rounded) and values
+                                             // (the unit's first workgroup, before its sweep)
       } x;
       float qrot[kChunkRows][kHeadDim];     // rotated query rows, pre-scaled
       float qlat[kChunkRows][kHeadDim];     // the same projected by U_K
     } s;
     uint16_t uv[kHeadDim * (kHeadDim + kVPad)];  // U_V, rows padded (the lift)
     float park[kWaves][kChunkRows][kHeadDim];  // each wave's full-width sums
-    struct {
-      float kn[kChunkRows][kHeadDim];  // the chunk's new keys, rotated and rounded
-      float vn[kChunkRows][kHeadDim];  // their values
-      float qf[kChunkRows][kHeadDim];  // the query rows rotated again, pre-scaled
-    } fin;
   } u;
   float wml[kWaves][kChunkRows][2];  // each wave's (max, sum) per query row
   int is_last;
@@ -346,71 +345,126 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, i
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The unit's last workgroup: fold the unit's nslots partials (slots slot0
-// ..), then, query row by query row, the chunk's tokens 0 .. t as one-row
-// partials (keys rotated at q_pos + u in fp64 and rounded once, i.e. the
-// rows the cache keeps); write out and lse; store the tokens' rows while
-// the window has room (w + u < its capacity).  The tokens' keys and values
-// and the rotated query rows are staged in LDS first, so the per-token
-// steps wait for no memory; thread (m, c8) then owns 8 columns of query
-// row m (16 threads, one DPP row, per query row).  A row with nothing to
-// attend gets out 0 and lse -inf.
-__device__ __forceinline__ void chunk_finish(const AttnArgs& a, ChunkShared& sh, int u, int b, int h,
-                                             int slot0, int nslots, int wlive, int M, int G) {
+// The chunk's tokens as an M-row partial, made by the unit's first
+// workgroup between its prologue and its sweep, while its first tiles are in
+// flight: query row m (token t, head g) over tokens 0 .. t, keys rotated at
+// q_pos + u in fp64 and rounded once (the rows the cache keeps), scored
+// against the rotated, pre-scaled query rows in LDS.  The partial --
+// (max, sum) and the d sums per row -- goes to the unit's token slot
+// (a.tok_slot0 + u) with device-coherent stores, for the merge; the
+// tokens' rows are stored where the window has room (w + u < its
+// capacity: no workgroup reads those rows in this call).  Thread (m, c8)
+// owns 8 columns of row m (16 threads, one DPP row, per query row).
+__device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShared& sh, int u, int b,
+                                                    int h, int wlive, int M, int G) {
   const int tid = threadIdx.x;
-  const int Q = a.num_tokens, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int Q = a.num_tokens, Hkv = a.num_kv_heads;
   const int wcap = a.seg[1].rows;
   const int pos0 = a.q_pos[b];
   constexpr int kHalf = kHeadDim / 2;
-  if (a.k_new) {
-    // the query rows first: their loads are then in flight with the tokens'
-    // (which come after stores to the cache that the compiler may not pass)
-    for (int p = tid; p < M * kHalf; p += kThreads) {
-      const int m = p / kHalf, i = p % kHalf;
-      const int t = m / G, g = m - t * G;
-      const size_t qb = (((size_t)b * Q + t) * Hq + (size_t)h * G + g) * kHeadDim;
-      float sn, cs;
-      rope_sincos(a, pos0 + t, i, sn, cs);
-      const float v1 = ld_elem<true>(a.q, qb + i), v2 = ld_elem<true>(a.q, qb + i + kHalf);
-      const float sc = (float)a.score_scale;
-      sh.u.fin.qf[m][i] = (v1 * cs - v2 * sn) * sc;
-      sh.u.fin.qf[m][i + kHalf] = (v2 * cs + v1 * sn) * sc;
-    }
-    for (int p = tid; p < Q * kHalf; p += kThreads) {
-      const int t = p / kHalf, i = p % kHalf;
-      const size_t kb = (((size_t)b * Q + t) * Hkv + h) * kHeadDim;
-      double s64, c64;
-      sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
-      const double k1 = (double)ld_elem<true>(a.k_new, kb + i);
-      const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
-      const uint32_t b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
-      const uint32_t b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
-      const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
-      const uint16_t v1 = vs[i], v2 = vs[i + kHalf];
-      sh.u.fin.kn[t][i] = bits_to_float<true>(b1);
-      sh.u.fin.kn[t][i + kHalf] = bits_to_float<true>(b2);
-      sh.u.fin.vn[t][i] = bits_to_float<true>(v1);
-      sh.u.fin.vn[t][i + kHalf] = bits_to_float<true>(v2);
-      if (wlive + t < wcap) {
-        const size_t row = ((size_t)u * wcap + wlive + t) * kHeadDim;
-        uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
-        uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
-        kd[i] = (uint16_t)b1;
-        kd[i + kHalf] = (uint16_t)b2;
-        vd[i] = v1;
-        vd[i + kHalf] = v2;
-      }
+  float (*kn)[kHeadDim] = sh.u.s.x.tok[0];
+  float (*vn)[kHeadDim] = sh.u.s.x.tok[1];
+  for (int p = tid; p < Q * kHalf; p += kThreads) {
+    const int t = p / kHalf, i = p % kHalf;
+    const size_t kb = (((size_t)b * Q + t) * Hkv + h) * kHeadDim;
+    const double k1 = (double)ld_elem<true>(a.k_new, kb + i);
+    const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
+    const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
+    const uint16_t v1 = vs[i], v2 = vs[i + kHalf];
+    double s64, c64;
+    sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
+    const uint32_t b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
+    const uint32_t b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
+    kn[t][i] = bits_to_float<true>(b1);
+    kn[t][i + kHalf] = bits_to_float<true>(b2);
+    vn[t][i] = bits_to_float<true>(v1);
+    vn[t][i + kHalf] = bits_to_float<true>(v2);
+    if (wlive + t < wcap) {
+      const size_t row = ((size_t)u * wcap + wlive + t) * kHeadDim;
+      uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
+      uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
+      kd[i] = (uint16_t)b1;
+      kd[i + kHalf] = (uint16_t)b2;
+      vd[i] = v1;
+      vd[i + kHalf] = v2;
     }
   }
+  lds_barrier();
+  const int mm = tid / 16, c8 = tid & 15;
+  const int m = min(mm, M - 1), t = m / G;
+  float Mx = -INFINITY, L = 0.0f;
+  f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  for (int tk = 0; tk <= t; ++tk) {  // the 16 threads of a row share t
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot += sh.u.s.qrot[m][8 * c8 + e] * kn[tk][8 * c8 + e];
+    dot = row16_sum(dot);
+    const float mn = fmaxf(Mx, dot);
+    const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(dot - mn);
+    L = L * a1 + a2;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      acc[hf] = acc[hf] * a1 + *reinterpret_cast<const f32x4_t*>(&vn[tk][8 * c8 + 4 * hf]) * a2;
+    Mx = mn;
+  }
+  if (mm < M) {
+    const size_t slot = (size_t)a.tok_slot0 + u;
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(a.part_acc + slot * M * kHeadDim, M * kHeadDim * 4);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[hf]), rs,
+                                             (m * kHeadDim + 8 * c8 + 4 * hf) * 4, 0, kCoherent);
+    if (c8 == 0) {
+      store_coherent(&a.part_ml[(slot * M + m) * 2], Mx);
+      store_coherent(&a.part_ml[(slot * M + m) * 2 + 1], L);
+    }
+  }
+  lds_barrier();  // every thread is done with the staged tokens (the sweep's value tiles alias them)
+}
+
+// The unit's last workgroup: fold the unit's nslots partials (slots slot0
+// ..) and the chunk's tokens' partial (see chunk_token_partial; its loads
+// are requested with the first partials', so the merge waits for memory
+// once), then write out and lse.  Thread (m, c8) owns 8 columns of query
+// row m.  A row with nothing to attend gets out 0 and lse -inf.
+__device__ __forceinline__ void chunk_finish(const AttnArgs& a, int u, int b, int h, int slot0,
+                                             int nslots, int M, int G) {
+  const int tid = threadIdx.x;
+  const int Q = a.num_tokens, Hq = a.num_q_heads;
   const int mm = tid / 16, c8 = tid & 15;  // query row, 8-column group
   const int m = min(mm, M - 1);
+  const bool tok = a.k_new != nullptr;
   constexpr int kB = 8;
+  uint32_t tml[2] = {0u, 0u};
+  u32x4_t tacc[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  if (tok) {
+    const size_t ts = (size_t)a.tok_slot0 + u;
+    const __amdgpu_buffer_rsrc_t tm = coherent_rsrc(a.part_ml + ts * M * 2, M * 2 * 4);
+    const __amdgpu_buffer_rsrc_t ta = coherent_rsrc(a.part_acc + ts * M * kHeadDim, M * kHeadDim * 4);
+    tml[0] = __builtin_amdgcn_raw_buffer_load_b32(tm, m * 8, 0, kCoherent);
+    tml[1] = __builtin_amdgcn_raw_buffer_load_b32(tm, m * 8 + 4, 0, kCoherent);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      tacc[hf] = __builtin_amdgcn_raw_buffer_load_b128(ta, (m * kHeadDim + 8 * c8 + 4 * hf) * 4, 0,
+                                                      kCoherent);
+  }
   const __amdgpu_buffer_rsrc_t rml =
       coherent_rsrc(a.part_ml + (size_t)slot0 * M * 2, (uint32_t)(nslots * M * 2 * 4));
   const __amdgpu_buffer_rsrc_t racc =
       coherent_rsrc(a.part_acc + (size_t)slot0 * M * kHeadDim, (uint32_t)(nslots * M * kHeadDim * 4));
   float Mx = -INFINITY, L = 0.0f;
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  const auto fold = [&](uint32_t mbits, uint32_t lbits, const u32x4_t (&v)[2]) {
+    const float ms = __uint_as_float(mbits), ls = __uint_as_float(lbits);
+    const float mn = fmaxf(Mx, ms);
+    if (mn != -INFINITY) {
+      const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(ms - mn);
+      L = L * a1 + ls * a2;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) acc[hf] = acc[hf] * a1 + __builtin_bit_cast(f32x4_t, v[hf]) * a2;
+      Mx = mn;
+    }
+  };
   for (int s0 = 0; s0 < nslots; s0 += kB) {
     uint32_t mlw[kB][2];
     u32x4_t v[kB][2];
@@ -426,39 +480,12 @@ __device__ __forceinline__ void chunk_finish(const AttnArgs& a, ChunkShared& sh,
             racc, ((s * M + m) * kHeadDim + 8 * c8 + 4 * hf) * 4, 0, kCoherent);
     }
 #pragma unroll
-    for (int k = 0; k < kB; ++k) {
-      if (s0 + k < nslots) {
-        const float ms = __uint_as_float(mlw[k][0]), ls = __uint_as_float(mlw[k][1]);
-        const float mn = fmaxf(Mx, ms);
-        if (mn != -INFINITY) {
-          const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(ms - mn);
-          L = L * a1 + ls * a2;
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            acc[hf] = acc[hf] * a1 + __builtin_bit_cast(f32x4_t, v[k][hf]) * a2;
-          Mx = mn;
-        }
-      }
-    }
+    for (int k = 0; k < kB; ++k)
+      if (s0 + k < nslots) fold(mlw[k][0], mlw[k][1], v[k]);
   }
-  const int t = m / G, g = m - t * G;
-  if (a.k_new) {
-    lds_barrier();  // the staged tokens and query rows
-    for (int tk = 0; tk <= t; ++tk) {  // the 16 threads of a row share t
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += sh.u.fin.qf[m][8 * c8 + e] * sh.u.fin.kn[tk][8 * c8 + e];
-      dot = row16_sum(dot);
-      const float mn = fmaxf(Mx, dot);
-      const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(dot - mn);
-      L = L * a1 + a2;
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        acc[hf] = acc[hf] * a1 + *reinterpret_cast<const f32x4_t*>(&sh.u.fin.vn[tk][8 * c8 + 4 * hf]) * a2;
-      Mx = mn;
-    }
-  }
+  if (tok) fold(tml[0], tml[1], tacc);
   if (mm < M) {
+    const int t = m / G, g = m - t * G;
     const size_t row = ((size_t)b * Q + t) * Hq + (size_t)h * G + g;
     float* out = a.out + row * kHeadDim + 8 * c8;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -515,6 +542,7 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   load_tile_keys<true>(bv, j * TRB, j < nbt, rw, (j - nbt) * TRR, j >= nbt && j < total, tail, 0, kbuf);
   load_tile_values<true>(bv, j * TRB, j < nbt, rw, (j - nbt) * TRR, j >= nbt && j < total, tail, 0, vbuf);
   pro.finish(a, sh, wave, M, G);
+  if (c == 0 && a.k_new) chunk_token_partial(a, sh, unit, b, h, wr, M, G);  // workgroup-uniform
 
   constexpr int NB = BLAT ? 2 * BN : 1;  // latent sum blocks: r_V <= 32 NCH
   ChunkState<NB> st;
@@ -635,7 +663,7 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   if (tid < 2)
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  chunk_finish(a, sh, unit, b, h, slot0, k, wr, M, G);
+  chunk_finish(a, unit, b, h, slot0, k, M, G);
 }
 
 // One workgroup per piece, scheduled as the ragged kernel (ragged_schedule,
