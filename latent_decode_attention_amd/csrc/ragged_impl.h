@@ -25,9 +25,11 @@
 //     wave-wide sums on the VALU (no LDS tables, no shuffles through LDS).
 //   * Pieces alternate between the CUs' first and second workgroup slots
 //     and spread over the XCDs (see ragged_piece_of).
-//   * The merge also folds in the new token as a one-row partial (its score
-//     computed there), writes out and lse, and stores the token's row; a
-//     unit without rows still gets its one piece, which finds no tiles.
+//   * The unit's first workgroup scores the new token and stores its row
+//     in its prologue, while its first tile is in flight, and leaves a
+//     one-row partial; the merge folds it in with the pieces' partials and
+//     writes out and lse.  A unit without rows still gets its one piece,
+//     which finds no tiles.
 //   * Paged caches: rows sit in pages of at least 64 rows (a whole number
 //     of tiles) from shared pools.  Each workgroup stages its sequence's
 //     page ids in LDS once; a tile then costs one LDS read for its page id

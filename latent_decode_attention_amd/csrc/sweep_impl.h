@@ -1228,7 +1228,8 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
 // segment boundary too.  The workgroup writes one partial (slot slot0 + c);
 // the workgroup that finishes last merges the unit.  nbr, wr: the unit's
 // live beacon and raw rows (the arrays hold a.seg[*].rows per unit).
-// RAGGED: the merge also takes in the decode step's new token (ragged_finish).
+// RAGGED: the unit's first workgroup also makes the decode step's new
+// token's partial (TokenPartial), which the merge (ragged_finish) folds in.
 // PG (ragged only): the rows are paged; ptab (LDS) holds the unit's beacon
 // page ids, then its raw page ids.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
