@@ -148,7 +148,33 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedPick& p
   const int units = B * Hkv;
   int lo = max(1, (T + P - 1) / P), hi = max(lo, tmax);
   if (P > units) hi = min(hi, max(lo, (T + (P - units) - 1) / (P - units)));
-  if (count(lo) <= P) {
+  if (per == 1 && hi - lo < 64 && tmax < (1 << 23)) {
+    // Every sequence in a lane of its own and fewer than 64 candidates: lane
+    // j counts the pieces at share lo + j over the whole batch, all lanes
+    // at once, and the smallest share that fits wins (as the search below
+    // would find).  The quotient is formed from the reciprocal, clamped to
+    // 65 and corrected by one either way (24-bit products): exact wherever
+    // the clamp to kMaxChunks does not hide it, for t and L below 2^23.
+    // Four sequences per pass keep four independent chains in flight.
+    const int Lc = lo + lane;
+    const float rc = __builtin_amdgcn_rcpf((float)Lc);
+    const auto pieces_at = [&](int t) {
+      int q = min((int)__builtin_ceilf((float)t * rc), kMaxChunks + 1);
+      if (__mul24(q - 1, Lc) >= t) --q;
+      if (__mul24(q, Lc) < t) ++q;
+      return min(max(q, 1), kMaxChunks);
+    };
+    int c = 0;
+    for (int s = 0; s < B; s += 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = pieces_at(__builtin_amdgcn_readlane(tiles[0], min(s + i, 63)));
+        c += s + i < B ? p : 0;
+      }
+    }
+    const uint64_t fits = __builtin_amdgcn_ballot_w64(c * Hkv <= P && Lc <= hi);
+    if (fits) hi = lo + __builtin_ctzll(fits);
+  } else if (count(lo) <= P) {
     hi = lo;
   } else if (count(hi) <= P) {  // the smallest L in (lo, hi] with count(L) <= P (count falls with L)
     while (hi - lo > 1) {
