@@ -58,8 +58,9 @@ def parse_args():
                     help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
                          "of the capacities, new token stored) and print its figures as one JSON line")
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
-                    help="with --ragged: the cache in pages of ROWS rows (a power of two >= 64) "
-                         "at shuffled page ids, through slimkv_decode_attn_paged")
+                    help="with --ragged or --chunk: the cache in pages of ROWS rows (a power "
+                         "of two >= 64) at shuffled page ids, through slimkv_decode_attn_paged "
+                         "or slimkv_decode_attn_chunk_paged")
     ap.add_argument("--chunk", type=int, default=0, metavar="Q",
                     help="only time the ragged serving step with Q query tokens per sequence "
                          "(slimkv_decode_attn_chunk) and print its figures as one JSON line")
@@ -151,7 +152,8 @@ def main():
         print(json.dumps(alibi_step(lda, synth, torch, dev, wl, layers, args.steps)), flush=True)
         return
     if args.chunk:
-        print(json.dumps(chunk_step(lda, synth, torch, dev, wl, layers, args.steps, args.chunk)),
+        print(json.dumps(chunk_step(lda, synth, torch, dev, wl, layers, args.steps, args.chunk,
+                                    page_rows=args.paged)),
               flush=True)
         return
     probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
@@ -264,6 +266,8 @@ def main():
                                                                 args.steps, page_rows=64)
             result["comparison"]["c3_chunk4_step"] = chunk_step(lda, synth, torch, dev, wl, layers,
                                                                  args.steps, 4)
+            result["comparison"]["c3_chunk4_paged_step"] = chunk_step(
+                lda, synth, torch, dev, wl, layers, args.steps, 4, page_rows=64)
             result["comparison"]["c3_alibi_step"] = alibi_step(lda, synth, torch, dev, wl, layers,
                                                                args.steps)
             result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
@@ -425,13 +429,14 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
     return res
 
 
-def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens):
+def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens, page_rows=0):
     """The ragged serving step of ragged_step with a chunk of num_tokens
     query tokens per sequence (e.g. drafted tokens checked in one pass):
     every layer attends each token over the live rows and the chunk's tokens
-    up to it, and stores the tokens (slimkv_decode_attn_chunk).  Bytes: the
-    live rows, the tokens' keys and values read and written, the queries,
-    the bases, out and lse."""
+    up to it, and stores the tokens (slimkv_decode_attn_chunk).  page_rows >
+    0: the cache lies in pages of that many rows at seeded, shuffled page
+    ids (slimkv_decode_attn_chunk_paged).  Bytes: the live rows, the tokens'
+    keys and values read and written, the queries, the bases, out and lse."""
     elem = wl.elem_bytes
     Q = num_tokens
     first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
@@ -457,11 +462,23 @@ def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens):
     out = torch.empty((wl.batch, Q, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((wl.batch, Q, wl.num_q_heads), dtype=torch.float32, device=dev)
 
-    def step():
-        for p, x, c in zip(probs, layers, chunks):
-            lda.slimkv_decode_attn_chunk(p, Q, c.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
-                                         x.V_raw, c.num_beacons, c.raw_len, c.k_new, c.v_new, out,
-                                         lse, ws)
+    if page_rows:
+        paged = [synth.make_paged(x, c, page_rows=page_rows) for x, c in zip(layers, chunks)]
+        tables = [lda.make_pages(page_rows=page_rows, beacon_table=pc.beacon_table,
+                                 raw_table=pc.raw_table, beacon_pages=pc.beacon_pages,
+                                 raw_pages=pc.raw_pages) for pc in paged]
+
+        def step():
+            for p, x, c, pc, tb in zip(probs, layers, chunks, paged, tables):
+                lda.slimkv_decode_attn_chunk_paged(p, tb, Q, c.q, x.q_pos, x.U_K, x.U_V, pc.C_K,
+                                                   pc.C_V, pc.K_raw, pc.V_raw, c.num_beacons,
+                                                   c.raw_len, c.k_new, c.v_new, out, lse, ws)
+    else:
+        def step():
+            for p, x, c in zip(probs, layers, chunks):
+                lda.slimkv_decode_attn_chunk(p, Q, c.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V,
+                                             x.K_raw, x.V_raw, c.num_beacons, c.raw_len, c.k_new,
+                                             c.v_new, out, lse, ws)
 
     ms = replay_ms(torch, step, steps)
     gbps = bytes_step / (ms * 1e-3) / 1e9
@@ -471,7 +488,10 @@ def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens):
            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
            "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
                         f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + {Q} tokens"}
-    log(f"chunk step: {res}")
+    if page_rows:
+        res["page_rows"] = page_rows
+        del paged, tables
+    log(f"{'paged ' if page_rows else ''}chunk step: {res}")
     del ws, chunks
     torch.cuda.empty_cache()
     return res

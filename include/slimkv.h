@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 7
+#define SLIMKV_ABI_VERSION 8
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -297,6 +297,39 @@ slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem,
                                        const void* k_new, const void* v_new,
                                        float* out, float* lse, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * slimkv_decode_attn_chunk_paged -- slimkv_decode_attn_chunk over a paged
+ * cache (speculative decoding in a serving engine whose cache lives in
+ * pages).
+ *
+ * Computes exactly what slimkv_decode_attn_chunk computes for the logical
+ * arrays the pages describe (out and lse are bitwise equal to that call's
+ * on the same rows), with the pools, tables and their rules as for
+ * slimkv_decode_attn_paged: the chunk's tokens u with w_b + u < W_cap are
+ * stored as raw rows w_b + u in the pages raw_table gives for those rows
+ * (not where an entry is outside [0, raw_pages)), and a page that receives
+ * a token in this call must not be shared.  The call reads the table
+ * entries of pages that hold live rows or receive tokens.
+ *
+ *   pages         host struct as for slimkv_decode_attn_paged
+ *   C_K, C_V      beacon pools (NULL when N_cap == 0)
+ *   K_raw, V_raw  raw pools (NULL when W_cap == 0); written only at the
+ *                 chunk's tokens' rows
+ * Other arguments, limits and the workspace (slimkv_chunk_workspace_bytes)
+ * as for slimkv_decode_attn_chunk.
+ */
+slimkv_status slimkv_decode_attn_chunk_paged(const slimkv_problem* problem,
+                                             const slimkv_pages* pages,
+                                             int32_t num_tokens, const void* q,
+                                             const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K,
+                                             const void* C_V, void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b,
+                                             const int32_t* raw_len,
+                                             const void* k_new, const void* v_new,
+                                             float* out, float* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream);
 
 /*
  * slimkv_decode_attn_alibi -- the latent decode attention of an ALiBi

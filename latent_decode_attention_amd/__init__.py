@@ -11,7 +11,7 @@ from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # no
                       SLIMKV_OP_RECONSTRUCT, SlimKVError, full_kv_attn, load_library,
                       make_pages, make_problem, slimkv_abi_version,
                       slimkv_chunk_workspace_bytes, slimkv_decode_attn, slimkv_decode_attn_alibi,
-                      slimkv_decode_attn_chunk,
+                      slimkv_decode_attn_chunk, slimkv_decode_attn_chunk_paged,
                       slimkv_decode_attn_paged, slimkv_decode_attn_ragged, slimkv_last_error,
                       slimkv_pages, slimkv_problem,
                       slimkv_reconstruct_attn, slimkv_reconstruct_rope_attn,

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
 
 EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
            "slimkv_decode_attn_paged", "slimkv_chunk_workspace_bytes", "slimkv_decode_attn_chunk",
-           "slimkv_decode_attn_alibi",
+           "slimkv_decode_attn_chunk_paged", "slimkv_decode_attn_alibi",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
            "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
@@ -110,6 +110,9 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_chunk_workspace_bytes.restype = sz
     lib.slimkv_decode_attn_chunk.argtypes = [prob, ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
     lib.slimkv_decode_attn_chunk.restype = ctypes.c_int
+    lib.slimkv_decode_attn_chunk_paged.argtypes = [prob, ctypes.POINTER(slimkv_pages),
+                                                   ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_chunk_paged.restype = ctypes.c_int
     lib.slimkv_reconstruct_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_reconstruct_attn.restype = ctypes.c_int
     lib.slimkv_reconstruct_rope_attn.argtypes = [prob] + [vp] * 11 + [vp, sz, vp]
@@ -241,6 +244,18 @@ def slimkv_decode_attn_chunk(problem, num_tokens, q, q_pos, U_K, U_V, C_K, C_V, 
         _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len),
         _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def slimkv_decode_attn_chunk_paged(problem, pages, num_tokens, q, q_pos, U_K, U_V, C_K, C_V,
+                                   K_raw, V_raw, num_beacons, raw_len, k_new, v_new, out, lse,
+                                   workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_chunk_paged(
+        ctypes.byref(problem), ctypes.byref(pages) if pages is not None else None,
+        int(num_tokens), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def slimkv_reconstruct_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,

@@ -661,6 +661,21 @@ slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem, int32_t nu
                             workspace_bytes, stream, false, num_tokens);
 }
 
+slimkv_status slimkv_decode_attn_chunk_paged(const slimkv_problem* problem,
+                                             const slimkv_pages* pages, int32_t num_tokens,
+                                             const void* q, const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K, const void* C_V,
+                                             void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b, const int32_t* raw_len,
+                                             const void* k_new, const void* v_new, float* out,
+                                             float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (num_tokens < 1) return slimkv::fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
+  return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, true, num_tokens);
+}
+
 const char* slimkv_status_string(slimkv_status status) {
   switch (status) {
     case SLIMKV_OK: return "ok";

@@ -1,17 +1,18 @@
-// chunk.hip -- the chunk kernel (several query tokens per sequence, bf16)
-// and its launcher.
+// chunk.hip -- the chunk kernel (several query tokens per sequence, bf16;
+// capacity-sized or paged caches) and its launcher.
 #include "sweep_impl.h"
 #include "chunk_impl.h"
 
 namespace slimkv {
 
+template <bool PG>
 static const void* chunk_kernel_for(int nch) {
   switch (nch) {
-    case 0: return reinterpret_cast<const void*>(&chunk_kernel<0>);
-    case 1: return reinterpret_cast<const void*>(&chunk_kernel<1>);
-    case 2: return reinterpret_cast<const void*>(&chunk_kernel<2>);
-    case 3: return reinterpret_cast<const void*>(&chunk_kernel<3>);
-    default: return reinterpret_cast<const void*>(&chunk_kernel<4>);
+    case 0: return reinterpret_cast<const void*>(&chunk_kernel<0, PG>);
+    case 1: return reinterpret_cast<const void*>(&chunk_kernel<1, PG>);
+    case 2: return reinterpret_cast<const void*>(&chunk_kernel<2, PG>);
+    case 3: return reinterpret_cast<const void*>(&chunk_kernel<3, PG>);
+    default: return reinterpret_cast<const void*>(&chunk_kernel<4, PG>);
   }
 }
 
@@ -23,7 +24,8 @@ hipError_t launch_chunk(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev
   const int nch = (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0)
                       ? std::max((a.seg[0].rk + 31) / 32, (a.seg[0].rv + 31) / 32)
                       : 0;
-  const void* kfn = chunk_kernel_for(nch);
+  const bool paged = a.page_table[0] != nullptr || a.page_table[1] != nullptr;
+  const void* kfn = paged ? chunk_kernel_for<true>(nch) : chunk_kernel_for<false>(nch);
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   int64_t P = a.chunks;
   if (P <= 0) {

@@ -241,16 +241,17 @@ struct ChunkState {
 // key features; width: value columns.  RAW: a raw tile, summed into accr
 // (a rescale then applies to accb too); else a beacon tile, summed into
 // accb (accr is not started: a wave's beacon tiles come first).
-template <int S, bool RAW, int NB, int SA, int SB>
-__device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, int nchk, int width,
+template <int S, bool RAW, int NB, int SA, int SB, bool PG>
+__device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t0, int nchk, int width,
                                            const bf16x8_t (&qh)[S], const bf16x8_t (&ql)[S],
                                            ChunkState<NB>& st, uint16_t* vt,
-                                           const SegView<SA, true>& bv, const SegView<SB, true>& rw,
-                                           int jn, int nbt, int total, const TailRows& tail,
-                                           u32x4_t* kbuf, u32x4_t* vbuf) {
-  constexpr int SUB = SegView<S, true>::kSub;
-  constexpr int TR = SegView<S, true>::kRows;
-  constexpr int TRA = SegView<SA, true>::kRows, TRB = SegView<SB, true>::kRows;
+                                           const SegView<SA, true, PG>& bv,
+                                           const SegView<SB, true, PG>& rw, int jn, int nbt,
+                                           int total, const TailRows& tail, u32x4_t* kbuf,
+                                           u32x4_t* vbuf) {
+  constexpr int SUB = SegView<S, true, PG>::kSub;
+  constexpr int TR = SegView<S, true, PG>::kRows;
+  constexpr int TRA = SegView<SA, true, PG>::kRows, TRB = SegView<SB, true, PG>::kRows;
   constexpr int VMAX = Traits<true>::kMaxLoads;
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kg = lane >> 4;
@@ -274,7 +275,8 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, i
     sc[s] = d;
   }
   const bool ua = jn < nbt, ub = jn >= nbt && jn < total;
-  load_tile_keys<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, 0, kbuf);
+  const int pid = tile_page(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub);
+  load_tile_keys<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, kbuf);
 
   // this tile's values into the wave's LDS tile, row-major with padded rows
   const int pitch = width + kVPad;
@@ -290,7 +292,7 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, i
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  load_tile_values<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, 0, vbuf);
+  load_tile_values<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, vbuf);
 
   // online softmax per query row (max over the row's 4 k-group lanes)
   float mx = sc[0][0];
@@ -353,10 +355,14 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true>& sv, int t0, i
 // (max, sum) and the d sums per row -- goes to the unit's token slot
 // (a.tok_slot0 + u) with device-coherent stores, for the merge; the
 // tokens' rows are stored where the window has room (w + u < its
-// capacity: no workgroup reads those rows in this call).  Thread (m, c8)
-// owns 8 columns of row m (16 threads, one DPP row, per query row).
+// capacity: no workgroup reads those rows in this call); PG: in the page
+// the raw table gives for the row (ptab from rtab0; none if that id is out
+// of range).  Thread (m, c8) owns 8 columns of row m (16 threads, one DPP
+// row, per query row).
+template <bool PG>
 __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShared& sh, int u, int b,
-                                                    int h, int wlive, int M, int G) {
+                                                    int h, int wlive, int M, int G,
+                                                    const int32_t* ptab, int rtab0) {
   const int tid = threadIdx.x;
   const int Q = a.num_tokens, Hkv = a.num_kv_heads;
   const int wcap = a.seg[1].rows;
@@ -380,13 +386,23 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
     vn[t][i] = bits_to_float<true>(v1);
     vn[t][i + kHalf] = bits_to_float<true>(v2);
     if (wlive + t < wcap) {
-      const size_t row = ((size_t)u * wcap + wlive + t) * kHeadDim;
-      uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
-      uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
-      kd[i] = (uint16_t)b1;
-      kd[i + kHalf] = (uint16_t)b2;
-      vd[i] = v1;
-      vd[i + kHalf] = v2;
+      const int r = wlive + t;
+      size_t row = ((size_t)u * wcap + r) * kHeadDim;
+      bool store = true;
+      if constexpr (PG) {
+        const int sh_ = a.page_shift;
+        const int pid = ptab[rtab0 + (r >> sh_)];
+        store = (uint32_t)pid < (uint32_t)a.num_pages[1];
+        row = ((((size_t)pid * a.num_kv_heads + h) << sh_) + (r & ((1 << sh_) - 1))) * kHeadDim;
+      }
+      if (store) {
+        uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
+        uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
+        kd[i] = (uint16_t)b1;
+        kd[i + kHalf] = (uint16_t)b2;
+        vd[i] = v1;
+        vd[i + kHalf] = v2;
+      }
     }
   }
   lds_barrier();
@@ -497,13 +513,16 @@ __device__ __forceinline__ void chunk_finish(const AttnArgs& a, int u, int b, in
 }
 
 // The work of one workgroup of a chunk call: workgroup c of the k that share
-// unit (b, h), as attend_unit, with the unit's live rows nbr, wr.
-template <int NCH>
+// unit (b, h), as attend_unit, with the unit's live rows nbr, wr.  PG: the
+// rows are paged; ptab (LDS) holds the unit's beacon page ids, then its raw
+// page ids (those of its live rows and of the rows its tokens are stored in).
+template <int NCH, bool PG>
 __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, int unit, int b, int h,
-                                           int c, int k, int nbr, int wr, int slot0) {
+                                           int c, int k, int nbr, int wr, int slot0,
+                                           const int32_t* ptab) {
   constexpr bool BLAT = NCH > 0;
   constexpr int BN = BLAT ? NCH : 4;
-  constexpr int TRB = SegView<BN, true>::kRows, TRR = SegView<4, true>::kRows;
+  constexpr int TRB = SegView<BN, true, PG>::kRows, TRR = SegView<4, true, PG>::kRows;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, kg = lane >> 4;
@@ -512,11 +531,20 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   const int wu = kWaves * c + wave;
   const int rk = BLAT ? a.seg[0].rk : 0, rv = BLAT ? a.seg[0].rv : 0;
 
-  SegView<BN, true> bv;
-  bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, nbr, BLAT ? rk : kHeadDim, BLAT ? rv : kHeadDim,
-          unit, lane);
-  SegView<4, true> rw;
-  rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
+  SegView<BN, true, PG> bv;
+  SegView<4, true, PG> rw;
+  int nbp = 0;  // the unit's beacon pages (paged)
+  if constexpr (PG) {
+    nbp = (nbr + (1 << a.page_shift) - 1) >> a.page_shift;
+    bv.init_paged(a.seg[0].K, a.seg[0].V, a.page_shift, a.num_pages[0], nbr,
+                  BLAT ? rk : kHeadDim, BLAT ? rv : kHeadDim, h, a.num_kv_heads, ptab, 0, lane);
+    rw.init_paged(a.seg[1].K, a.seg[1].V, a.page_shift, a.num_pages[1], wr, kHeadDim, kHeadDim, h,
+                  a.num_kv_heads, ptab, nbp, lane);
+  } else {
+    bv.init(a.seg[0].K, a.seg[0].V, a.seg[0].rows, nbr, BLAT ? rk : kHeadDim, BLAT ? rv : kHeadDim,
+            unit, lane);
+    rw.init(a.seg[1].K, a.seg[1].V, a.seg[1].rows, wr, kHeadDim, kHeadDim, unit, lane);
+  }
   const int nbt = bv.ntiles, total = nbt + rw.ntiles;
   // Past its last tile a wave's load slots fetch its quarter of the head's
   // U_V for the lift (bytes 8192 wave .. +8191 of the 128 x r_V block: lanes
@@ -539,10 +567,15 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   pro.issue(a, b, h, M, G);
   u32x4_t kbuf[Traits<true>::kMaxLoads], vbuf[Traits<true>::kMaxLoads];
   int j = wu;
-  load_tile_keys<true>(bv, j * TRB, j < nbt, rw, (j - nbt) * TRR, j >= nbt && j < total, tail, 0, kbuf);
-  load_tile_values<true>(bv, j * TRB, j < nbt, rw, (j - nbt) * TRR, j >= nbt && j < total, tail, 0, vbuf);
+  {
+    const bool ub = j < nbt, ur = j >= nbt && j < total;
+    const int pid = tile_page(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur);
+    load_tile_keys<true>(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur, tail, pid, kbuf);
+    load_tile_values<true>(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur, tail, pid, vbuf);
+  }
   pro.finish(a, sh, wave, M, G);
-  if (c == 0 && a.k_new) chunk_token_partial(a, sh, unit, b, h, wr, M, G);  // workgroup-uniform
+  if (c == 0 && a.k_new)  // workgroup-uniform
+    chunk_token_partial<PG>(a, sh, unit, b, h, wr, M, G, ptab, nbp);
 
   constexpr int NB = BLAT ? 2 * BN : 1;  // latent sum blocks: r_V <= 32 NCH
   ChunkState<NB> st;
@@ -667,13 +700,17 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
 }
 
 // One workgroup per piece, scheduled as the ragged kernel (ragged_schedule,
-// ragged_piece_of): piece i of the batch is workgroup c of unit (b, h).
-template <int NCH>
+// ragged_piece_of): piece i of the batch is workgroup c of unit (b, h).  PG:
+// the cache is paged; the workgroup first stages sequence b's page ids that
+// it uses in LDS -- the pages of its live beacon rows, then of its live raw
+// rows and of the rows that receive the chunk's tokens.
+template <int NCH, bool PG>
 __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(AttnArgs a) {
   constexpr int BN = NCH > 0 ? NCH : 4;
   constexpr int TRB = SegView<BN, true>::kRows, TRR = SegView<4, true>::kRows;
   __shared__ ChunkShared sh;
   __shared__ RaggedPick pick;
+  __shared__ int32_t ptab[PG ? kMaxPageEntries : 1];
   const int tid = threadIdx.x;
   const int Hkv = a.num_kv_heads, P = a.chunks;
   const int pi = ragged_piece_of((int)blockIdx.x, P);
@@ -683,7 +720,19 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(
   if (pi >= uni(pick.total)) return;
   const int b = uni(pick.b), kb = uni(pick.k), first = uni(pick.first);
   const int h = (pi - first) / kb, c = pi - first - h * kb;
-  chunk_unit<NCH>(a, sh, b * Hkv + h, b, h, c, kb, uni(pick.nb), uni(pick.w), first + h * kb);
+  const int nbr = uni(pick.nb), wr = uni(pick.w);
+  if constexpr (PG) {
+    // at most ceil(N_cap / rows) + ceil(W_cap / rows) <= kMaxPageEntries ids
+    const int sh_ = a.page_shift, pm = (1 << sh_) - 1;
+    const int nbp = (nbr + pm) >> sh_;
+    const int wst = a.k_new ? min(wr + a.num_tokens, a.seg[1].rows) : wr;
+    const int n = nbp + ((wst + pm) >> sh_);
+    const int32_t* bt = a.page_table[0] + (size_t)b * a.table_width[0];
+    const int32_t* rt = a.page_table[1] + (size_t)b * a.table_width[1];
+    for (int i = tid; i < n; i += kThreads) ptab[i] = i < nbp ? bt[i] : rt[i - nbp];
+    lds_barrier();
+  }
+  chunk_unit<NCH, PG>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb, ptab);
 }
 
 }  // namespace slimkv

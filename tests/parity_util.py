@@ -404,6 +404,87 @@ def run_gpu_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool
     return out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu()
 
 
+def run_gpu_chunk_paged(inp: synth.LayerInputs, ch: synth.ChunkInputs, pc: synth.PagedCache, *,
+                        append: bool = True, lengths: bool = True, num_splits: int = 0,
+                        raw_table=None, device="cuda"):
+    """slimkv_decode_attn_chunk_paged on ``pc`` (the pages of ``inp``'s
+    capacity arrays) and the chunk ``ch``; the raw pools are cloned first.
+    Returns (out [B, Q, H_q, d], lse [B, Q, H_q], K pool, V pool) on the host."""
+    wl = inp.workload
+    g = inp.to(device)
+    c = ch.to(device)
+    Q = ch.num_tokens
+    ncap, wcap = inp.num_beacons, inp.raw_window
+    # the tables stay referenced until the call: the struct keeps raw pointers
+    bt = pc.beacon_table.to(device)
+    rt = (pc.raw_table if raw_table is None else raw_table).to(device)
+    CK, CV = pc.C_K.to(device), pc.C_V.to(device)
+    K, V = pc.K_raw.to(device).clone(), pc.V_raw.to(device).clone()
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=num_splits)
+    pages = lda.make_pages(page_rows=pc.page_rows, beacon_table=bt if ncap else None,
+                           raw_table=rt if wcap else None, beacon_pages=pc.beacon_pages,
+                           raw_pages=pc.raw_pages)
+    B, Hq, d = g.q.shape
+    out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device=device)
+    lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=device)
+    ws = torch.zeros(lda.slimkv_chunk_workspace_bytes(prob, Q), dtype=torch.uint8, device=device)
+    lda.slimkv_decode_attn_chunk_paged(prob, pages, Q, c.q, g.q_pos, g.U_K, g.U_V,
+                                       CK if ncap else None, CV if ncap else None,
+                                       K if wcap else None, V if wcap else None,
+                                       c.num_beacons if lengths else None,
+                                       c.raw_len if lengths else None,
+                                       c.k_new if append else None, c.v_new if append else None,
+                                       out, lse, ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu()
+
+
+def assert_chunk_paged_writes(K_after, V_after, pc: synth.PagedCache, ch: synth.ChunkInputs, k_app,
+                              wcap: int, raw_table=None, units=None):
+    """The paged chunk call wrote exactly its tokens' rows -- raw row w_b + u
+    for every token u with w_b + u below the capacity, in the page the raw
+    table gives for that row (none if the id is out of range) -- with the
+    oracle's keys (as in assert_new_rows; k_app [B, Q, H_kv, d] or
+    {(b, h): [Q, d]}) and v_new, checked for ``units`` (default all); every
+    other element of both pools, NaN fillers included, keeps its bits.
+    k_app None: no tokens, nothing written."""
+    table = (pc.raw_table if raw_table is None else raw_table).cpu().numpy()
+    PR = pc.page_rows
+    Ka, Va = storage_to_f64(K_after), storage_to_f64(V_after)
+    vnew = storage_to_f64(ch.v_new)
+    raw_len = ch.raw_len.cpu().numpy()
+    B, Q, Hkv = vnew.shape[0], vnew.shape[1], vnew.shape[2]
+    check = set(units or [(b, h) for b in range(B) for h in range(Hkv)])
+    mask = np.zeros(K_after.shape[:3], dtype=bool)
+    off_by_ulp = compared = 0
+    for b in range(B if k_app is not None else 0):
+        w = int(np.clip(raw_len[b], 0, wcap))
+        for u in range(Q):
+            if w + u >= wcap:
+                break
+            pid = int(table[b, (w + u) // PR])
+            if not 0 <= pid < K_after.shape[0]:
+                continue
+            r = (w + u) % PR
+            mask[pid, :, r] = True
+            for h in range(Hkv):
+                if (b, h) in check:
+                    exp = k_app[(b, h)][u] if isinstance(k_app, dict) else k_app[b, u, h]
+                    off_by_ulp += _key_ulps(Ka[pid, h, r], exp, K_after.dtype, (b, h, u))
+                    compared += Ka.shape[-1]
+                    assert np.array_equal(Va[pid, h, r], vnew[b, u, h]), f"value ({b}, {h}, {u})"
+    assert off_by_ulp <= max(1, compared // 10000), f"{off_by_ulp} of {compared} key elements"
+    keep = ~mask
+    assert np.array_equal(storage_bits(K_after)[keep], storage_bits(pc.K_raw)[keep]), \
+        "K pool: other rows written"
+    assert np.array_equal(storage_bits(V_after)[keep], storage_bits(pc.V_raw)[keep]), \
+        "V pool: other rows written"
+    print(f"[parity] paged chunk rows: {int(mask.sum())} written, {off_by_ulp} key elements one "
+          f"ulp off", flush=True)
+
+
 def oracle_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool = True,
                  lengths: bool = True, units=None):
     """oracle.decode_chunk on the whole layer (or the listed units)."""

@@ -41,7 +41,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 7
+    assert lda.slimkv_abi_version() == 8
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -349,6 +349,48 @@ def test_chunk_checks(lib):
     assert _call_chunk(lib, prob, 3, ptrs=dict(lse=0x240000 - lse_bytes + 4)) == ALIAS
     # the raw window is written with new tokens
     assert _call_chunk(lib, prob, 2, ptrs=dict(k_new=0x3000000 + 64)) == ALIAS
+
+
+def _call_chunk_paged(lib, prob, pages, Q, *, ptrs=None, ws_bytes=16):
+    """slimkv_decode_attn_chunk_paged with fake device addresses (every case
+    fails validation before any HIP call)."""
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, nb=0x210000, raw=0x220000,
+             k_new=0x230000, v_new=0x240000, out=0x5000000, lse=0x6000000, ws=0x7000000)
+    p.update(ptrs or {})
+    v = {k: (None if x is None else ctypes.c_void_p(x)) for k, x in p.items()}
+    pg = ctypes.byref(pages) if pages is not None else None
+    return lib.slimkv_decode_attn_chunk_paged(ctypes.byref(prob), pg, Q, v["q"], v["q_pos"],
+                                              v["U_K"], v["U_V"], v["C_K"], v["C_V"], v["K_raw"],
+                                              v["V_raw"], v["nb"], v["raw"], v["k_new"],
+                                              v["v_new"], v["out"], v["lse"], v["ws"], ws_bytes,
+                                              None)
+
+
+def test_chunk_paged_checks(lib):
+    """The paged chunk call takes the chunk call's token rules and the paged
+    call's table rules; its workspace is the chunk call's."""
+    prob = _problem()  # G = 4: up to 4 tokens; one page of 64 rows per segment
+    ws = lib.slimkv_chunk_workspace_bytes(ctypes.byref(prob), 4)
+    assert _call_chunk_paged(lib, prob, _pages(), 4) == WS
+    assert _call_chunk_paged(lib, prob, _pages(), 4, ws_bytes=ws - 1) == WS
+    assert _call_chunk_paged(lib, prob, _pages(), 5) == UNSUP
+    assert _call_chunk_paged(lib, prob, _pages(), 0) == SHAPE
+    assert _call_chunk_paged(lib, _problem(dtype="fp32"), _pages(), 2) == UNSUP
+    assert _call_chunk_paged(lib, prob, None, 2) == NULL
+    assert _call_chunk_paged(lib, prob, _pages(page_rows=96), 2) == SHAPE
+    assert _call_chunk_paged(lib, prob, _pages(raw_table=None), 2) == NULL
+    assert _call_chunk_paged(lib, prob, _pages(raw_table_width=0), 2) == SHAPE
+    assert _call_chunk_paged(lib, prob, _pages(), 2, ptrs=dict(v_new=None)) == NULL
+    # the raw pool (4 pages x 2 heads x 64 rows x 128 x 2 B = 0x20000) is written
+    assert _call_chunk_paged(lib, prob, _pages(), 2, ptrs=dict(k_new=0x3000000 + 0x20000)) == WS
+    assert _call_chunk_paged(lib, prob, _pages(), 2,
+                             ptrs=dict(k_new=0x3000000 + 0x20000 - 16)) == ALIAS
+    # out carries the token axis (3 tokens: 3 x 2 x 8 x 128 x 4 bytes) and must not meet a table
+    out_bytes = 3 * 2 * 8 * 128 * 4
+    assert _call_chunk_paged(lib, prob, _pages(), 3, ptrs=dict(out=0x250000 - out_bytes)) == WS
+    assert _call_chunk_paged(lib, prob, _pages(), 3,
+                             ptrs=dict(out=0x250000 - out_bytes + 4)) == ALIAS
 
 
 def test_alibi_checks(lib):
