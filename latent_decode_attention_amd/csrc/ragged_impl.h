@@ -107,6 +107,24 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedPick& p
   // iterations would run under an execution mask at every step of the search.
   const int per = (B + 63) / 64;
   const int b0 = lane * per;
+  const int units = B * Hkv;
+  if (units >= P) {
+    // As many units as slots or more: whatever the lengths, every unit gets
+    // one piece (the search below would end at a share no unit exceeds), so
+    // piece pi is unit pi and only its sequence's lengths are needed.
+    if (lane == 0) {
+      const int b = min(pi / Hkv, B - 1);
+      const int nb = a.seq_beacons ? a.seq_beacons[b] : ncap;
+      const int w = a.seq_raw ? a.seq_raw[b] : wcap;
+      pick.b = b;
+      pick.first = b * Hkv;
+      pick.k = 1;
+      pick.nb = min(max(nb, 0), ncap);
+      pick.w = min(max(w, 0), wcap);
+      pick.total = units;
+    }
+    return;
+  }
   int nbv[kPer], wv[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
@@ -145,7 +163,6 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedPick& p
   // L >= T / P, as P pieces must hold T tiles; and L = T / (P - units)
   // always fits (sum of ceil(t / L) <= T / L + units), which bounds the
   // search when the slots outnumber the units
-  const int units = B * Hkv;
   int lo = max(1, (T + P - 1) / P), hi = max(lo, tmax);
   if (P > units) hi = min(hi, max(lo, (T + (P - units) - 1) / (P - units)));
   if (per == 1 && hi - lo < 64 && tmax < (1 << 23)) {
