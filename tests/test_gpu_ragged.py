@@ -73,9 +73,11 @@ def test_only_new_token(gpu_device):
     check_ragged(wl, fixed={}, append=False, what="nothing at all")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 64, 333])
+@pytest.mark.parametrize("splits", [1, 2, 7, 15, 16, 17, 64, 333])
 def test_grid_sizes(splits, gpu_device):
-    """Shares that cut units anywhere (down to one workgroup for the batch)."""
+    """Shares that cut units anywhere (down to one workgroup for the batch);
+    16 slots for the 16 units is the largest grid scheduled one piece per
+    unit without a search, 17 the smallest searched."""
     check_ragged(custom(B=8, Hkv=2, G=4, nb=600, w=200, index=102), num_splits=splits,
                  what=f"grid {splits}")
 
