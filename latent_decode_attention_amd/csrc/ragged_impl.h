@@ -23,6 +23,9 @@
 //   * Each workgroup recomputes the schedule from the lengths at its start:
 //     one wave loads them, finds the share and finds its own piece, with
 //     wave-wide sums on the VALU (no LDS tables, no shuffles through LDS).
+//     Up to 64 sequences, the lanes test up to 64 candidate shares at once;
+//     with at least as many units as slots, every unit is one piece and only
+//     the workgroup's own sequence is read (see ragged_schedule).
 //   * Pieces alternate between the CUs' first and second workgroup slots
 //     and spread over the XCDs (see ragged_piece_of).
 //   * The unit's first workgroup scores the new token and stores its row
