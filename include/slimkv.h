@@ -151,6 +151,18 @@ slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q,
  * slimkv_decode_attn_ragged -- the same attention for one serving decode
  * step over a ragged batch, with the step's new token.
  *
+ * Passages: page "Can SlimKV compress KV cache jointly across tokens and
+ * features", section "Latent-space attention removes the rebuild step" (the
+ * attention itself: raw-token keys keep rotation, beacon keys do not), and
+ * section "Speedups are real, but memory is set by the ratio" (a decode run
+ * generates tokens one at a time, so each step adds one raw-token row to the
+ * cache it attends over); section "Why feature compression stalls at key
+ * reconstruction" (the cache and its memory traffic are what limit
+ * long-context serving, where sequences of a batch hold different lengths).
+ * The pages do not spell out the cache update; the reading taken here is
+ * append-then-attend: the new token is rotated at its own position, joins
+ * the softmax as one more raw row, and is stored.
+ *
  * The cache arrays are sized to capacities: problem->num_beacons is N_cap,
  * the beacon rows each (b, kv head) holds in C_K [B, H_kv, N_cap, r_K] and
  * C_V, and problem->raw_window is W_cap, the raw rows of K_raw, V_raw
@@ -225,6 +237,10 @@ typedef struct slimkv_pages {
 /*
  * slimkv_decode_attn_paged -- slimkv_decode_attn_ragged over a paged cache.
  *
+ * Passages: as for slimkv_decode_attn_ragged.  The pages never mention
+ * paging; it is read here as a storage indirection that changes no result,
+ * so the defining computation stays the contiguous one.
+ *
  * Computes exactly what slimkv_decode_attn_ragged computes for the logical
  * arrays the pages describe (out and lse are bitwise equal to that call's
  * on the same rows): the same clamped lengths n_b <= N_cap and w_b <= W_cap
@@ -262,7 +278,19 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
 /*
  * slimkv_decode_attn_chunk -- the same attention for a chunk of Q query
  * tokens per sequence: speculative decoding checks several drafted tokens
- * in one pass, chunked prefill feeds a prompt Q tokens at a time.  Token t
+ * in one pass, chunked prefill feeds a prompt Q tokens at a time.
+ *
+ * Passages: page "Can SlimKV compress KV cache jointly across tokens and
+ * features", section "Latent-space attention removes the rebuild step" (the
+ * attention for every query: rotated, grouped, projected into the beacon
+ * latent space), and section "Speedups are real, but memory is set by the
+ * ratio" (time-to-first-token, i.e. queries that arrive several at a time,
+ * gains from skipping full-key materialisation too).  With Q queries per
+ * KV head the latent products become dense, so they run on the matrix
+ * cores.  Causality among the chunk's own tokens is the ordinary decoder
+ * reading: token t sees tokens 0 .. t.
+ *
+ * Token t
  * of sequence b sits at position q_pos[b] + t.  Each of its query heads is
  * rotated there and attends, under one softmax, over the sequence's live
  * beacon rows (latent, as in slimkv_decode_attn), its live raw rows, and the
@@ -302,6 +330,9 @@ slimkv_status slimkv_decode_attn_chunk(const slimkv_problem* problem,
  * slimkv_decode_attn_chunk_paged -- slimkv_decode_attn_chunk over a paged
  * cache (speculative decoding in a serving engine whose cache lives in
  * pages).
+ *
+ * Passages: as for slimkv_decode_attn_chunk; paging as for
+ * slimkv_decode_attn_paged (a storage indirection that changes no result).
  *
  * Computes exactly what slimkv_decode_attn_chunk computes for the logical
  * arrays the pages describe (out and lse are bitwise equal to that call's

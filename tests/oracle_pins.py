@@ -392,6 +392,23 @@ def pin_append_rounding(library):
     assert np.array_equal(k_app, bf16_round(rot)), "new key not rounded once to bf16"
 
 
+def pin_append_rounding_fp32(library):
+    """fp32 storage: the new key is the rotation rounded once to fp32 (IEEE
+    round to nearest even, as numpy's float64 -> float32 conversion does),
+    not kept in double and not rounded twice through bf16."""
+    p = ragged_problem(47, B=3, Hkv=2, G=2, d=64, ncap=5, rk=16, rv=16, wcap=4, theta=500000.0,
+                       q_pos=40000)
+    pf = dict(p)
+    for name in ("q", "U_K", "U_V", "C_K", "C_V", "K_raw", "V_raw", "k_new", "v_new"):
+        pf[name] = p[name].astype(np.float32)
+    _, _, k_app = run_ragged(pf, library)
+    rot = rope_complex(pf["k_new"].astype(np.float64), p["q_pos"][:, None], p["theta"])
+    want = rot.astype(np.float32).astype(np.float64)
+    assert np.array_equal(np.asarray(k_app, dtype=np.float64), want), \
+        "new key not rounded once to fp32"
+    assert not np.array_equal(want, rot), "fixture too coarse: rounding never changes a value"
+
+
 # ---------------------------------------------------------------------------
 # The reconstruction variant that keeps beacon-key rotation (oracle.decode
 # with beacon_pos): rebuilt beacon keys are rotated at their positions.
@@ -725,6 +742,7 @@ ALL_PINS = [
     pin_append_token,
     pin_append_self_score,
     pin_append_rounding,
+    pin_append_rounding_fp32,
     pin_beacon_rope_reference,
     pin_beacon_rope_relative,
     pin_chunk_reference,

@@ -67,6 +67,11 @@ MUTANTS = {
     "alibi_slope_of_kv_head": ("const double m_h = slope[hq];", "const double m_h = slope[h];"),
     "alibi_beacons_unbiased": ("s[j] = p->scale * acc - m_h * (qp - (double)bpos[j]);",
                                "s[j] = p->scale * acc;"),
+    "fp32_storage_not_rounded": ("if (dtype == ORACLE_F32) return (double)(float)x;",
+                                 "if (dtype == ORACLE_F32) return x;"),
+    "fp32_storage_rounded_through_bf16": (
+        "if (dtype == ORACLE_F32) return (double)(float)x;",
+        "if (dtype == ORACLE_F32) dtype = ORACLE_BF16;"),
     "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
                                "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
