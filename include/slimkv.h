@@ -148,6 +148,35 @@ slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q,
                                  void* stream);
 
 /*
+ * slimkv_decode_attn_noalloc -- slimkv_decode_attn without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * The workspace is a scratch array inside the library, one per device
+ * (16 MiB, SLIMKV_NOALLOC_SCRATCH_BYTES, held until the process ends).  A
+ * call needs 64 bytes per (b, kv head) unit plus (2 + d) * 4 bytes per query
+ * head for each workgroup sharing a unit's rows (about 1.1 MB for batch 16,
+ * 32/8 heads on a 256-CU device); a call that needs more than the scratch
+ * holds returns SLIMKV_ERR_WORKSPACE and launches nothing (that check needs
+ * the device's compute-unit count, a device query).  The call allocates and
+ * frees nothing: it launches a small kernel that clears the scratch's
+ * counters, then the attention kernel.  Every call on a device shares that
+ * device's scratch and leaves its contents behind, so calls that can overlap
+ * on one device (on different streams) race and must not be issued; calls
+ * ordered on one stream are fine.  Results equal slimkv_decode_attn's with
+ * the same problem (bitwise: same kernels, same split).  Arguments, layouts
+ * and checks as for slimkv_decode_attn.
+ */
+#define SLIMKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+slimkv_status slimkv_decode_attn_noalloc(const slimkv_problem* problem, const void* q,
+                                         const int32_t* q_pos, const void* U_K,
+                                         const void* U_V, const void* C_K,
+                                         const void* C_V, const void* K_raw,
+                                         const void* V_raw, float* out, float* lse,
+                                         void* stream);
+
+/*
  * slimkv_decode_attn_ragged -- the same attention for one serving decode
  * step over a ragged batch, with the step's new token.
  *

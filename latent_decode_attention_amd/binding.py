@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
 
-EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_ragged",
+EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_noalloc",
+           "slimkv_decode_attn_ragged",
            "slimkv_decode_attn_paged", "slimkv_chunk_workspace_bytes", "slimkv_decode_attn_chunk",
            "slimkv_decode_attn_chunk_paged", "slimkv_decode_attn_alibi",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
@@ -98,6 +99,8 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_workspace_bytes.restype = sz
     lib.slimkv_decode_attn.argtypes = [prob] + [vp] * 10 + [vp, sz, vp]
     lib.slimkv_decode_attn.restype = ctypes.c_int
+    lib.slimkv_decode_attn_noalloc.argtypes = [prob] + [vp] * 10 + [vp]
+    lib.slimkv_decode_attn_noalloc.restype = ctypes.c_int
     lib.slimkv_decode_attn_ragged.argtypes = [prob] + [vp] * 14 + [vp, sz, vp]
     lib.slimkv_decode_attn_ragged.restype = ctypes.c_int
     lib.slimkv_decode_attn_paged.argtypes = [prob, ctypes.POINTER(slimkv_pages)] + [vp] * 14 + [
@@ -179,6 +182,14 @@ def slimkv_decode_attn(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
         ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
         _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def slimkv_decode_attn_noalloc(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out, lse,
+                               stream=None) -> None:
+    lib = load_library()
+    _check(lib, lib.slimkv_decode_attn_noalloc(
+        ctypes.byref(problem), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def slimkv_decode_attn_ragged(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, num_beacons,

@@ -15,6 +15,9 @@
 #include "internal.h"
 #include "slimkv.h"
 
+static_assert(slimkv::kNoAllocScratchBytes == SLIMKV_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size");
+
 namespace slimkv {
 namespace {
 
@@ -239,11 +242,13 @@ struct Alibi {
   int32_t first = 0, stride = 0;  // beacon j at first + j * stride
 };
 
+// noalloc: the workspace is the library's device scratch (ws must be NULL;
+// slimkv_decode_attn_noalloc), laid out for the chunk count this call uses.
 slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const int32_t* q_pos,
                   const void* U_K, const void* U_V, const void* C_K, const void* C_V,
                   const void* K_raw, const void* V_raw, float* out, float* lse, void* ws,
                   size_t ws_bytes, void* stream, const int32_t* beacon_pos = nullptr,
-                  const Alibi& alibi = Alibi()) {
+                  const Alibi& alibi = Alibi(), bool noalloc = false) {
   Plan pl;
   slimkv_status st = make_plan(p, op, pl);
   if (st != SLIMKV_OK) return st;
@@ -305,15 +310,41 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     for (const Range& o : outs)
       if (overlap(o, bp)) return fail(SLIMKV_ERR_ALIAS, "%s overlaps beacon_pos", o.name);
   }
-  if (!ws) return fail(SLIMKV_ERR_NULL, "workspace is NULL");
-  if ((uintptr_t)ws % 16 != 0) return fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
-  if (ws_bytes < pl.total)
-    return fail(SLIMKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs& a = pl.attn;
+  if (!noalloc) {
+    if (!ws) return fail(SLIMKV_ERR_NULL, "workspace is NULL");
+    if ((uintptr_t)ws % 16 != 0) return fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < pl.total)
+      return fail(SLIMKV_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, pl.total);
+  } else {
+    // The scratch holds the counters and one partial slot per workgroup of
+    // this call: the chunk count is fixed here (as the launcher would pick
+    // it), which needs the device's workgroup slots -- a device query; no
+    // launch happens before every check has passed.
+    if (a.chunks <= 0) {
+      const int slots = attention_slots(a, pl.dtype);
+      if (slots <= 0) return fail(SLIMKV_ERR_HIP, "device query failed");
+      a.chunks = choose_chunks(pl.units, a.unit_bytes, slots, 64 << 10);
+    }
+    const size_t G = a.group, k = a.chunks;
+    pl.off_counters = 0;
+    size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+    pl.off_ml = off;
+    off = round_up(off + pl.units * k * G * 2 * sizeof(float), kAlign);
+    pl.off_acc = off;
+    pl.total = round_up(off + pl.units * k * G * kHeadDim * sizeof(float), kAlign);
+    if (pl.total > kNoAllocScratchBytes)
+      return fail(SLIMKV_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch (%lld units x %zu workgroups); the "
+                  "no-alloc entry point holds %zu (use slimkv_decode_attn with a workspace)",
+                  pl.total, (long long)pl.units, k, kNoAllocScratchBytes);
+    const hipError_t e = noalloc_scratch(pl.off_ml, s, &ws);
+    if (e != hipSuccess) return fail(SLIMKV_ERR_HIP, "scratch set-up failed: %s", hipGetErrorString(e));
+  }
 
   // ---- all checks passed: launch
   char* wsb = static_cast<char*>(ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  AttnArgs& a = pl.attn;
   a.q = q;
   a.q_pos = q_pos;
   a.U_K = U_K;
@@ -573,6 +604,14 @@ slimkv_status slimkv_decode_attn(const slimkv_problem* problem, const void* q, c
                                  void* workspace, size_t workspace_bytes, void* stream) {
   return slimkv::run(problem, SLIMKV_OP_LATENT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
                      lse, workspace, workspace_bytes, stream);
+}
+
+slimkv_status slimkv_decode_attn_noalloc(const slimkv_problem* problem, const void* q,
+                                         const int32_t* q_pos, const void* U_K, const void* U_V,
+                                         const void* C_K, const void* C_V, const void* K_raw,
+                                         const void* V_raw, float* out, float* lse, void* stream) {
+  return slimkv::run(problem, SLIMKV_OP_LATENT, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, out,
+                     lse, nullptr, 0, stream, nullptr, slimkv::Alibi(), true);
 }
 
 slimkv_status slimkv_reconstruct_attn(const slimkv_problem* problem, const void* q,

@@ -257,13 +257,32 @@ hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, h
   }
 }
 
-hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  int nch = 0;  // beacon rows at full width, or none
-  if (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0) {
-    nch = (a.seg[0].rk + 31) / 32;
-    const int nv = (a.seg[0].rv + 31) / 32;
-    if (nv > nch) nch = nv;
+int attention_slots_g1(int, int, bool);
+int attention_slots_g2(int, int, bool);
+int attention_slots_g3(int, int, bool);
+int attention_slots_g4(int, int, bool);
+int attention_slots_g5(int, int, bool);
+int attention_slots_g6(int, int, bool);
+int attention_slots_g7(int, int, bool);
+int attention_slots_g8(int, int, bool);
+
+int attention_slots(const AttnArgs& a, int dtype) {
+  const int nch = beacon_chunks(a);
+  const bool alibi = a.alibi_slopes != nullptr;
+  switch (a.group) {
+    case 1: return attention_slots_g1(dtype, nch, alibi);
+    case 2: return attention_slots_g2(dtype, nch, alibi);
+    case 3: return attention_slots_g3(dtype, nch, alibi);
+    case 4: return attention_slots_g4(dtype, nch, alibi);
+    case 5: return attention_slots_g5(dtype, nch, alibi);
+    case 6: return attention_slots_g6(dtype, nch, alibi);
+    case 7: return attention_slots_g7(dtype, nch, alibi);
+    default: return attention_slots_g8(dtype, nch, alibi);
   }
+}
+
+hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const int nch = beacon_chunks(a);  // 0: beacon rows at full width, or none
   switch (a.group) {
     case 1: return launch_attention_g1(a, dtype, nch, s, ev0, ev1);
     case 2: return launch_attention_g2(a, dtype, nch, s, ev0, ev1);

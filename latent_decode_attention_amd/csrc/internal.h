@@ -21,6 +21,7 @@ constexpr int kMinPageShift = 6;       // pages hold at least 64 rows: no tile s
 constexpr int kMaxPageShift = 16;
 constexpr int kChunkRows = 16;         // query rows (tokens x heads) per unit in chunk calls
 constexpr int kChunkMaxSlots = 2048;   // workgroup slots a chunk call is shaped for, at most
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // device scratch of the no-alloc entry point
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -120,5 +121,16 @@ hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s);
 
 // Tile height (rows) a segment of the given widths is swept in.
 int tile_rows(int dtype, int rk, int rv);
+
+// Workgroup slots of the attention kernel that launch_attention would run
+// for `a` (the device's CUs x resident workgroups of that kernel, at most
+// kWgPerCu per CU), or <= 0 on a HIP error.  A device query, no launch.
+int attention_slots(const AttnArgs& a, int dtype);
+
+// The no-alloc entry point's device scratch (kNoAllocScratchBytes, one copy
+// per device, kept until the process ends): its address on the current
+// device (taken once per device with hipGetSymbolAddress), after launching
+// on `s` a kernel that zeroes its first clear_bytes bytes.
+hipError_t noalloc_scratch(size_t clear_bytes, hipStream_t s, void** ptr);
 
 }  // namespace slimkv

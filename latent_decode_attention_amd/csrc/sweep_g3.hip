@@ -10,4 +10,7 @@ hipError_t launch_ragged_g3(AttnArgs a, int dtype, int nch, int64_t max_wgs, hip
                               hipEvent_t ev0, hipEvent_t ev1) {
   return launch_ragged_group<3>(a, dtype, nch, max_wgs, s, ev0, ev1);
 }
+int attention_slots_g3(int dtype, int nch, bool alibi) {
+  return attention_slots_group<3>(dtype, nch, alibi);
+}
 }  // namespace slimkv

@@ -10,4 +10,7 @@ hipError_t launch_ragged_g4(AttnArgs a, int dtype, int nch, int64_t max_wgs, hip
                               hipEvent_t ev0, hipEvent_t ev1) {
   return launch_ragged_group<4>(a, dtype, nch, max_wgs, s, ev0, ev1);
 }
+int attention_slots_g4(int dtype, int nch, bool alibi) {
+  return attention_slots_group<4>(dtype, nch, alibi);
+}
 }  // namespace slimkv

@@ -1416,6 +1416,13 @@ const void* attention_kernel_for(int dtype, int nch) {
   }
 }
 
+// Workgroup slots of the kernel launch_attention_group<G> would run.
+template <int G>
+int attention_slots_group(int dtype, int nch, bool alibi) {
+  return device_slots(alibi ? attention_kernel_for<G, true>(dtype, nch)
+                            : attention_kernel_for<G, false>(dtype, nch));
+}
+
 // Launch for group size G (nch as for attention_kernel_for).
 template <int G>
 hipError_t launch_attention_group(AttnArgs a, int dtype, int nch, hipStream_t s, hipEvent_t ev0,
