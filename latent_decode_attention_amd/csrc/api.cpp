@@ -48,7 +48,7 @@ struct Plan {
   int64_t units;
   int dtype;
   int elem;
-  size_t off_counters, off_ml, off_acc, off_kb, off_vb, total;
+  size_t off_counters, off_flags, off_ml, off_acc, off_kb, off_vb, total;
 };
 
 bool rank_ok(int r) { return r >= 16 && r <= kHeadDim && r % 16 == 0; }
@@ -152,12 +152,14 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   a.rank_v = sb.kind == kSegLatent ? p->rank_v : 0;
   a.rank_k = sb.kind == kSegLatent ? p->rank_k : 0;
 
-  // workspace layout: per-unit counters (must start zeroed), then one
-  // partial slot per workgroup for up to kMaxChunks workgroups per unit
-  // (ragged: one per piece, fewer than grid + units)
+  // workspace layout: per-unit counters and per-slot flags (must start
+  // zeroed), then one partial slot per workgroup for up to kMaxChunks
+  // workgroups per unit (ragged: one per piece, fewer than grid + units)
   const int64_t G = a.group, slots = ragged ? kMaxChunks + 1 : kMaxChunks;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+  pl.off_flags = off;
+  off = round_up(off + (size_t)(pl.units * slots) * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
   off = round_up(off + (size_t)(pl.units * slots * G * 2) * sizeof(float), kAlign);
   pl.off_acc = off;
@@ -192,6 +194,8 @@ slimkv_status make_chunk_plan(const slimkv_problem* p, int32_t num_tokens, Plan&
   pl.attn.num_tokens = num_tokens;
   pl.off_counters = 0;
   size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+  pl.off_flags = off;
+  off = round_up(off + (size_t)slots * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
   off = round_up(off + (size_t)(slots * M * 2) * sizeof(float), kAlign);
   pl.off_acc = off;
@@ -330,6 +334,8 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     const size_t G = a.group, k = a.chunks;
     pl.off_counters = 0;
     size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+    pl.off_flags = off;
+    off = round_up(off + pl.units * k * sizeof(uint32_t), kAlign);
     pl.off_ml = off;
     off = round_up(off + pl.units * k * G * 2 * sizeof(float), kAlign);
     pl.off_acc = off;
@@ -353,6 +359,7 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     a.inv_freq_pow2[k] = pow(p->rope_theta, -2.0 * (double)(1 << k) / (double)kHeadDim);
   a.score_scale = (double)p->scale * 1.4426950408889634074;  // scale * log2(e)
   a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
+  a.flags = reinterpret_cast<uint32_t*>(wsb + pl.off_flags);
   a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
   a.out = out;
@@ -375,21 +382,17 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
     rb.batch = p->batch;
     rb.num_kv_heads = p->num_kv_heads;
     rb.num_beacons = p->num_beacons;
-    rb.C = C_K;
-    rb.U = U_K;
-    rb.dst = wsb + pl.off_kb;
-    rb.rank = (int32_t)rk;
+    rb.C[0] = C_K;
+    rb.U[0] = U_K;
+    rb.dst[0] = wsb + pl.off_kb;
+    rb.rank[0] = (int32_t)rk;
+    rb.C[1] = C_V;
+    rb.U[1] = U_V;
+    rb.dst[1] = wsb + pl.off_vb;
+    rb.rank[1] = (int32_t)rv;
     rb.pos = beacon_pos;  // keys only
     for (int k = 0; k < 6; ++k) rb.inv_freq_pow2[k] = a.inv_freq_pow2[k];
     err = launch_rebuild(rb, pl.dtype, s);
-    if (err == hipSuccess) {
-      rb.C = C_V;
-      rb.U = U_V;
-      rb.dst = wsb + pl.off_vb;
-      rb.rank = (int32_t)rv;
-      rb.pos = nullptr;
-      err = launch_rebuild(rb, pl.dtype, s);
-    }
   }
   if (err == hipSuccess) {
     const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
@@ -545,6 +548,7 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
     a.inv_freq_pow2[k] = pow(p->rope_theta, -2.0 * (double)(1 << k) / (double)kHeadDim);
   a.score_scale = (double)p->scale * 1.4426950408889634074;
   a.counters = reinterpret_cast<uint32_t*>(wsb + pl.off_counters);
+  a.flags = reinterpret_cast<uint32_t*>(wsb + pl.off_flags);
   a.part_ml = reinterpret_cast<float*>(wsb + pl.off_ml);
   a.part_acc = reinterpret_cast<float*>(wsb + pl.off_acc);
   a.out = out;

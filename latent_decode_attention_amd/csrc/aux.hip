@@ -16,16 +16,25 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
-// Rebuild (reconstruction comparison paths only): dst = C U^T per unit, i.e.
-// the full-dimension beacon keys or values the latent path never forms,
-// rounded to the storage dtype.  With a.pos (the variant that keeps
-// beacon-key rotation, page "Can SlimKV compress KV cache jointly across
-// tokens and features", section "Speedups are real, but memory is set by
-// the ratio") row j is rotated at position pos[j] -- rotate-half pairs
-// (i, i + d/2), angle pos * theta^(-2i/d) formed and reduced mod 2*pi in
-// fp64, sine and cosine in fp32 -- before it is rounded.  bf16: one wave
-// per 16 rows, MFMA 16x16x32 over 8 column tiles, staged through LDS in
-// fp32 for 16-byte stores.
+// Rebuild (reconstruction comparison paths only): K_b = C_K U_K^T and
+// V_b = C_V U_V^T for every (b, kv head), i.e. the full-dimension beacon keys
+// and values the latent path never forms, rounded to the storage dtype.
+// With a.pos (the variant that keeps beacon-key rotation, page "Can SlimKV
+// compress KV cache jointly across tokens and features", section "Speedups
+// are real, but memory is set by the ratio") rebuilt key row j is rotated at
+// position pos[j] -- rotate-half pairs (i, i + d/2), angle pos * theta^(-2i/d)
+// formed and reduced mod 2*pi in fp64, sine and cosine in fp32 -- before it
+// is rounded.  One launch rebuilds both: job 0 the keys, job 1 the values.
+//
+// bf16 (MFMA 16x16x32): a workgroup takes 64 beacon rows of one KV head and
+// walks the batch, so the head's basis (staged in LDS) and the rows'
+// rotation are loaded and formed once and serve every sequence.  The basis
+// is the A operand (basis row = output column on M, rank on K) and the
+// transposed latent rows the B operand (rank on K, beacon row on N):
+// lane (n, kg) then ends with columns 16t + 4kg .. +3 of row n for each
+// 16-column tile t -- the two halves of every rotation pair in one lane,
+// and 8 contiguous output bytes per store.  The next sequence's latent rows
+// are requested before the current ones are multiplied.
 
 // Sine and cosine of pos * theta^(-2i/d) for pair i < 64 (see above).
 __device__ __forceinline__ void rebuild_sincos(const RebuildArgs& a, int pos, int i, float& s,
@@ -40,94 +49,113 @@ __device__ __forceinline__ void rebuild_sincos(const RebuildArgs& a, int pos, in
   const double r = fma(-kk, kTwoPiLo, fma(-kk, kTwoPiHi, ang));
   sincosf((float)r, &s, &c);
 }
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   uint32_t u = __float_as_uint(x);
   u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return u >> 16;
 }
 
-__global__ __launch_bounds__(kThreads) void rebuild_bf16_kernel(RebuildArgs a) {
-  constexpr int kPitch = kHeadDim + 4;  // fp32 elements per LDS row
-  __shared__ __attribute__((aligned(16))) float tile[kWaves][16][kPitch];
+constexpr int kRebuildRows = 64;  // beacon rows per workgroup (16 per wave)
+constexpr int kUPad = 8;           // staged basis rows padded by 16 bytes (LDS banks)
+
+template <int NCHK>
+__global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t ul[kHeadDim * (32 * NCHK + kUPad)];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
-  const int nblk = (a.num_beacons + 63) / 64;
-  const int unit = blockIdx.x / nblk;
-  const int rb = blockIdx.x - unit * nblk;
-  const int h = unit % a.num_kv_heads;
-  const int r = a.rank;
-  const int row0 = rb * 64 + wave * 16;
-  const uint16_t* C = static_cast<const uint16_t*>(a.C) + (size_t)unit * a.num_beacons * r;
-  const uint16_t* U = static_cast<const uint16_t*>(a.U) + (size_t)h * kHeadDim * r;
-  uint16_t* D = static_cast<uint16_t*>(a.dst) + (size_t)unit * a.num_beacons * kHeadDim;
-  const int nchk = (r + 31) / 32;
+  const int nb = a.num_beacons, hkv = a.num_kv_heads;
+  const int nblk = (nb + kRebuildRows - 1) / kRebuildRows;
+  const int per_job = hkv * nblk;
+  const int job = blockIdx.x / per_job;
+  const int rem = blockIdx.x - job * per_job;
+  const int h = rem / nblk, rb = rem - h * nblk;
+  const int r = a.rank[job];
+  const int nchk = (r + 31) / 32;  // workgroup-uniform
+  const int us = r + kUPad;        // staged row stride (elements)
+  const int row = rb * kRebuildRows + wave * 16 + n;
+  const bool row_ok = row < nb;
+  const int rowc = row_ok ? row : nb - 1;  // loads stay in bounds; the store is skipped
 
-  bf16x8_t av[4];
+  const uint16_t* C = static_cast<const uint16_t*>(a.C[job]);
+  uint16_t* D = static_cast<uint16_t*>(a.dst[job]);
+  auto load_rows = [&](int b, bf16x8_t* cb) {
+    const uint16_t* Cr = C + (((size_t)b * hkv + h) * nb + rowc) * r;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int row = row0 + n, k0 = 32 * c + 8 * kg;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (c < nchk && row < a.num_beacons && k0 < r)
-      v = *reinterpret_cast<const u32x4_t*>(C + (size_t)row * r + k0);
-    av[c] = __builtin_bit_cast(bf16x8_t, v);
-  }
-#pragma unroll
-  for (int nt = 0; nt < kHeadDim / 16; ++nt) {
-    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (c < nchk) {
-        const int col = nt * 16 + n, k0 = 32 * c + 8 * kg;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (k0 < r) v = *reinterpret_cast<const u32x4_t*>(U + (size_t)col * r + k0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[c], __builtin_bit_cast(bf16x8_t, v), d, 0, 0, 0);
-      }
+    for (int c = 0; c < NCHK; ++c) {
+      const int k0 = 32 * c + 8 * kg;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (c < nchk && k0 < r) v = *reinterpret_cast<const u32x4_t*>(Cr + k0);
+      cb[c] = __builtin_bit_cast(bf16x8_t, v);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tile[wave][4 * kg + e][nt * 16 + n] = d[e];
+  };
+  bf16x8_t cur[NCHK], nxt[NCHK];
+  load_rows(0, cur);
+  // the head's basis, staged once: row i (output column), rank k
+  {
+    const uint16_t* U = static_cast<const uint16_t*>(a.U[job]) + (size_t)h * kHeadDim * r;
+    const int words = kHeadDim * r / 8, wpr = r / 8;
+    for (int w = tid; w < words; w += kThreads) {
+      const int i = w / wpr, k8 = w - i * wpr;
+      *reinterpret_cast<u32x4_t*>(&ul[i * us + 8 * k8]) =
+          *reinterpret_cast<const u32x4_t*>(U + (size_t)w * 8);
+    }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // each lane writes 8 columns of both halves of a row, i.e. the 8 rotation
-  // pairs (i, i + d/2) of one row, whose angles it computes once
+  // rotation of this lane's pairs (16t + 4kg + e, + d/2), t < 4 (keys with pos)
+  const bool rot = job == 0 && a.pos != nullptr;
+  float cs[4][4], sn[4][4];
+  if (rot) {
+    const int p = a.pos[rowc];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int idx = lane + 64 * j;
-    const int row = idx >> 3, seg = idx & 7;
-    if (row0 + row < a.num_beacons) {
-      const float* t = &tile[wave][row][0];
-      float lo[8], hi[8];
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        lo[e] = t[seg * 8 + e];
-        hi[e] = t[seg * 8 + e + kHeadDim / 2];
-      }
-      if (a.pos) {
-        const int p = a.pos[row0 + row];
+      for (int e = 0; e < 4; ++e) rebuild_sincos(a, p, 16 * t + 4 * kg + e, sn[t][e], cs[t][e]);
+  }
+  __syncthreads();
+  for (int b = 0; b < a.batch; ++b) {
+    if (b + 1 < a.batch) load_rows(b + 1, nxt);
+    uint16_t* Dr = D + (((size_t)b * hkv + h) * nb + row) * kHeadDim + 4 * kg;
+    // column tiles t and t + 4 together: they hold the two halves of this
+    // lane's rotation pairs
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float sn, cs;
-          rebuild_sincos(a, p, seg * 8 + e, sn, cs);
-          const float x = lo[e], y = hi[e];
-          lo[e] = x * cs - y * sn;
-          hi[e] = y * cs + x * sn;
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCHK; ++c) {
+        if (c < nchk) {
+          const int k0 = 32 * c + 8 * kg;
+          u32x4_t a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+          if (k0 < r) {
+            a0 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + n) * us + k0]);
+            a1 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + 64 + n) * us + k0]);
+          }
+          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), cur[c], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), cur[c], d1, 0, 0, 0);
         }
       }
-      u32x4_t wl, wh;
+      if (rot) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wl[e] = (uint32_t)f32_to_bf16(lo[2 * e]) | ((uint32_t)f32_to_bf16(lo[2 * e + 1]) << 16);
-        wh[e] = (uint32_t)f32_to_bf16(hi[2 * e]) | ((uint32_t)f32_to_bf16(hi[2 * e + 1]) << 16);
+        for (int e = 0; e < 4; ++e) {
+          const float x = d0[e], y = d1[e];
+          d0[e] = x * cs[t][e] - y * sn[t][e];
+          d1[e] = y * cs[t][e] + x * sn[t][e];
+        }
       }
-      uint16_t* dst = D + (size_t)(row0 + row) * kHeadDim + seg * 8;
-      *reinterpret_cast<u32x4_t*>(dst) = wl;
-      *reinterpret_cast<u32x4_t*>(dst + kHeadDim / 2) = wh;
+      if (row_ok) {
+        *reinterpret_cast<uint2*>(Dr + 16 * t) =
+            make_uint2(f32_to_bf16(d0[0]) | (f32_to_bf16(d0[1]) << 16),
+                       f32_to_bf16(d0[2]) | (f32_to_bf16(d0[3]) << 16));
+        *reinterpret_cast<uint2*>(Dr + 16 * t + 64) =
+            make_uint2(f32_to_bf16(d1[0]) | (f32_to_bf16(d1[1]) << 16),
+                       f32_to_bf16(d1[2]) | (f32_to_bf16(d1[3]) << 16));
+      }
     }
+#pragma unroll
+    for (int c = 0; c < NCHK; ++c) cur[c] = nxt[c];
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rebuild_f32_kernel(RebuildArgs a) {
+// fp32: one thread per output element (the fp32 workloads are small).
+__global__ __launch_bounds__(kThreads) void rebuild_f32_kernel(RebuildArgs a, int job) {
   const size_t total = (size_t)a.batch * a.num_kv_heads * a.num_beacons * kHeadDim;
   const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= total) return;
@@ -135,22 +163,22 @@ __global__ __launch_bounds__(kThreads) void rebuild_f32_kernel(RebuildArgs a) {
   const size_t row = idx / kHeadDim;  // global beacon row
   const size_t unit = row / a.num_beacons;
   const int h = (int)(unit % a.num_kv_heads);
-  const int r = a.rank;
-  const float* C = static_cast<const float*>(a.C) + row * r;
-  const float* U = static_cast<const float*>(a.U) + ((size_t)h * kHeadDim + col) * r;
+  const int r = a.rank[job];
+  const float* C = static_cast<const float*>(a.C[job]) + row * r;
+  const float* U = static_cast<const float*>(a.U[job]) + ((size_t)h * kHeadDim + col) * r;
   float acc = 0.0f;
   for (int k = 0; k < r; ++k) acc = fmaf(C[k], U[k], acc);
-  if (a.pos) {
+  if (job == 0 && a.pos) {
     // the partner column i +- d/2 of the same row, rebuilt the same way
     const int pc = col ^ (kHeadDim / 2);
-    const float* Up = static_cast<const float*>(a.U) + ((size_t)h * kHeadDim + pc) * r;
+    const float* Up = static_cast<const float*>(a.U[job]) + ((size_t)h * kHeadDim + pc) * r;
     float pacc = 0.0f;
     for (int k = 0; k < r; ++k) pacc = fmaf(C[k], Up[k], pacc);
     float sn, cs;
     rebuild_sincos(a, a.pos[row % a.num_beacons], col & (kHeadDim / 2 - 1), sn, cs);
     acc = col < kHeadDim / 2 ? acc * cs - pacc * sn : acc * cs + pacc * sn;
   }
-  static_cast<float*>(a.dst)[idx] = acc;
+  static_cast<float*>(a.dst[job])[idx] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -167,10 +195,20 @@ hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s) {
   if (dtype == 0) {
     const size_t total = (size_t)a.batch * a.num_kv_heads * a.num_beacons * kHeadDim;
     const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(rebuild_f32_kernel, grid, block, 0, s, a);
-  } else {
-    const dim3 grid((unsigned)(a.batch * a.num_kv_heads * ((a.num_beacons + 63) / 64)));
-    hipLaunchKernelGGL(rebuild_bf16_kernel, grid, block, 0, s, a);
+    for (int job = 0; job < 2; ++job) {
+      hipLaunchKernelGGL(rebuild_f32_kernel, grid, block, 0, s, a, job);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int nchk = std::max((a.rank[0] + 31) / 32, (a.rank[1] + 31) / 32);
+  const dim3 grid((unsigned)(2 * a.num_kv_heads * ((a.num_beacons + kRebuildRows - 1) / kRebuildRows)));
+  switch (nchk) {
+    case 1: hipLaunchKernelGGL(rebuild_bf16_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(rebuild_bf16_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(rebuild_bf16_kernel<3>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(rebuild_bf16_kernel<4>, grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }

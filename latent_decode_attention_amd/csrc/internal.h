@@ -61,6 +61,8 @@ struct AttnArgs {
   int32_t rank_k;         // r_K of a latent beacon segment (0 if none)
   uint32_t* counters;     // [units][kCounterStride]: workgroups done, tiles handed out
                           // (zero between calls)
+  uint32_t* flags;        // [partial slots]: 1 while a slot holds a published partial the
+                          // unit's merge has not read (zero between calls)
   float* part_ml;         // [units, chunks, G, 2]  (max, sum of exp), log2 units
   float* part_acc;        // [units, chunks, G, d]  exp-weighted value sums
   float* out;             // [B, H_q, d]
@@ -91,12 +93,15 @@ struct AttnArgs {
   int32_t beacon_first, beacon_stride;
 };
 
+// The full-width rebuild of the reconstruction paths: job 0 the keys
+// (C_K, U_K), job 1 the values (C_V, U_V), both in one launch.
 struct RebuildArgs {
-  const void* C;  // [B, H_kv, N_b, r]
-  const void* U;  // [H_kv, d, r]
-  void* dst;      // [B, H_kv, N_b, d]
-  int32_t batch, num_kv_heads, num_beacons, rank;
-  const int32_t* pos;       // [N_b]: rotate row j at pos[j] before rounding (keys), or null
+  const void* C[2];  // [B, H_kv, N_b, r_job]
+  const void* U[2];  // [H_kv, d, r_job]
+  void* dst[2];      // [B, H_kv, N_b, d]
+  int32_t rank[2];
+  int32_t batch, num_kv_heads, num_beacons;
+  const int32_t* pos;       // [N_b]: rotate key row j at pos[j] before rounding, or null
   double inv_freq_pow2[6];  // theta^(-2 * 2^k / d), as in AttnArgs (with pos)
 };
 

@@ -188,8 +188,13 @@ struct alignas(16) AttnShared {
   float qlat[kMaxGroup][kHeadDim];
   float wml[2][kWaves][kMaxGroup][2];  // each wave's (max, sum) per head, per segment
   float sml[2][kMaxGroup][2];          // the workgroup's (max, sum) per head, per segment
+  float pml[kMaxGroup][2];             // the workgroup's partial: (max, sum) per head
   int is_last;
 };
+
+// The workgroup's partial sums, [G][d], once the sweeps' per-wave sums are
+// merged (they reuse the first wave's beacon-sum space).
+__device__ __forceinline__ float* partial_sums(AttnShared& sh) { return &sh.u.s.beacon[0][0][0]; }
 
 // Rotation angle q_pos * theta^(-2i/d) for pair i < 64: the frequency is the
 // product of the host's theta^(-2 * 2^k / d) over i's set bits (a few fp64
@@ -865,11 +870,12 @@ __device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const Se
 // its segment's max); the latent beacon sum is lifted once with U_V on the
 // matrix cores (bf16: the latent sum as hi + lo bf16 terms; fp32: exact
 // products); beacon and raw are combined by their maxima; the result --
-// (max, sum) and G x d sums per head -- is written with device-coherent
-// stores.
+// (max, sum) and G x d sums per head -- is left in LDS (sh.pml and
+// partial_sums(sh)), for the unit's merge or for publishing.
 template <int G, bool BF16, bool BLAT>
 __device__ __forceinline__ void wg_partial(const AttnArgs& a, AttnShared& sh, int h, int wave, int rvb,
-                                           const u32x4_t (&uw)[2][4], float* ml_out, float* acc_out) {
+                                           const u32x4_t (&uw)[2][4]) {
+  float* acc_out = partial_sums(sh);
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
   // (1) each segment's sums over the waves, rescaled to the segment's max
@@ -964,8 +970,10 @@ __device__ __forceinline__ void wg_partial(const AttnArgs& a, AttnShared& sh, in
       const int r0 = 16 * (wave + kWaves * t) + 4 * kg;
       const f32x4_t raw = *reinterpret_cast<const f32x4_t*>(&sh.qrot[gl][r0]);
       if (n < G) {
+        f32x4_t v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) store_coherent(&acc_out[n * kHeadDim + r0 + e], wb * d[t][e] + wr * raw[e]);
+        for (int e = 0; e < 4; ++e) v[e] = wb * d[t][e] + wr * raw[e];
+        *reinterpret_cast<f32x4_t*>(&acc_out[n * kHeadDim + r0]) = v;
       }
     }
   } else {
@@ -976,42 +984,89 @@ __device__ __forceinline__ void wg_partial(const AttnArgs& a, AttnShared& sh, in
       weights(g, wb, wr);
       const f32x4_t v = wb * *reinterpret_cast<const f32x4_t*>(&sh.qlat[g][col]) +
                         wr * *reinterpret_cast<const f32x4_t*>(&sh.qrot[g][col]);
-      const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(acc_out, G * kHeadDim * 4);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (g * kHeadDim + col) * 4, 0,
-                                             kCoherent);
+      *reinterpret_cast<f32x4_t*>(&acc_out[g * kHeadDim + col]) = v;
     }
   }
   if (tid < G) {
     float wb, wr;
     weights(tid, wb, wr);
-    const float M = fmaxf(sh.sml[0][tid][0], sh.sml[1][tid][0]);
-    store_coherent(&ml_out[2 * tid], M);
-    store_coherent(&ml_out[2 * tid + 1], wb * sh.sml[0][tid][1] + wr * sh.sml[1][tid][1]);
+    sh.pml[tid][0] = fmaxf(sh.sml[0][tid][0], sh.sml[1][tid][0]);
+    sh.pml[tid][1] = wb * sh.sml[0][tid][1] + wr * sh.sml[1][tid][1];
   }
 }
 
+// Publish the workgroup's partial (from LDS) into partial slot `slot` with
+// device-coherent stores, then -- once every store has completed -- raise
+// the slot's flag, which the unit's merging workgroup waits for.
+template <int G>
+__device__ __forceinline__ void publish_partial(const AttnArgs& a, AttnShared& sh, size_t slot) {
+  const int tid = threadIdx.x;
+  const float* acc = partial_sums(sh);
+  if (tid < G * kHeadDim / 4) {
+    const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&acc[g * kHeadDim + 4 * c4]);
+    const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(a.part_acc + slot * G * kHeadDim, G * kHeadDim * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rs, (g * kHeadDim + 4 * c4) * 4,
+                                           0, kCoherent);
+  }
+  if (tid < G) {
+    store_coherent(&a.part_ml[(slot * G + tid) * 2], sh.pml[tid][0]);
+    store_coherent(&a.part_ml[(slot * G + tid) * 2 + 1], sh.pml[tid][1]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every thread's stores have completed
+  if (tid == 0) __hip_atomic_store(&a.flags[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Run by the unit's merging workgroup: wait until the flags of the unit's
+// other n - 1 partial slots (slot0 + i, i != own) are raised, i.e. their
+// partials are complete in memory.  Their workgroups have all counted
+// themselves done before this one, so each is past its sweep and about to
+// publish; the wait ends within a few microseconds.  It is bounded anyway
+// (kSpinLimit polls): false if it ran out.  Wave 0 polls; the caller
+// synchronises the workgroup after it.  No other workgroup touches these
+// flags again in this call, so the merger lowers them right after.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ bool wait_flags(const AttnArgs& a, size_t slot0, int n, int own) {
+  const int lane = threadIdx.x & 63;
+  for (int it = 0; it < kSpinLimit; ++it) {
+    uint32_t f = 1u;
+    if (lane < n && lane != own)
+      f = __hip_atomic_load(&a.flags[slot0 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__builtin_amdgcn_ballot_w64(f == 0u) == 0) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------------------
-// Merge of the unit's k partials (run by the unit's last workgroup):
+// Merge of the unit's k partials (run by the unit's merging workgroup, after
+// wait_flags): slots slot0 .. slot0 + k - 1, its own (slot0 + own) still in
+// LDS, in slot order whichever workgroup merges:
 //   M = max_s m_s, L = sum_s 2^(m_s - M) l_s, out = sum_s 2^(m_s - M) acc_s / L,
 //   lse = ln 2 * (M + log2 L).
 // Thread (g, c4) owns 16-byte column c4 of head g and folds the partials in
-// one at a time; a batch of 8 partials' loads is in flight at once.  No LDS,
-// no barriers.
+// one at a time; a batch of 8 partials' loads is in flight at once.  The
+// other slots' flags are lowered once their partials are read.
 template <int G>
-__device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, int h) {
+__device__ __forceinline__ void merge_unit(const AttnArgs& a, const AttnShared& sh, int slot0, int k,
+                                           int own, int b, int h) {
   const int tid = threadIdx.x;
   if (tid >= G * kHeadDim / 4) return;
-  const int k = a.chunks;
   const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
   constexpr int kB = 8;
   const __amdgpu_buffer_rsrc_t rml =
-      coherent_rsrc(a.part_ml + (size_t)unit * k * G * 2, (uint32_t)(k * G * 2 * 4));
+      coherent_rsrc(a.part_ml + (size_t)slot0 * G * 2, (uint32_t)(k * G * 2 * 4));
   const __amdgpu_buffer_rsrc_t racc =
-      coherent_rsrc(a.part_acc + (size_t)unit * k * G * kHeadDim, (uint32_t)(k * G * kHeadDim * 4));
+      coherent_rsrc(a.part_acc + (size_t)slot0 * G * kHeadDim, (uint32_t)(k * G * kHeadDim * 4));
+  const f32x4_t own_acc = *reinterpret_cast<const f32x4_t*>(&const_cast<AttnShared&>(sh).u.s.beacon[0][0][0]
+                                                              + g * kHeadDim + 4 * c4);
+  const float own_m = sh.pml[g][0], own_l = sh.pml[g][1];
   float M = -INFINITY, L = 0.0f;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = 0; s0 < k; s0 += kB) {
-    // unconditional loads from clamped slots; surplus ones are not folded in
+    // unconditional loads from clamped slots; surplus ones (and the own
+    // slot's, whose values come from LDS) are not folded in
     uint32_t mlw[kB][2];
     u32x4_t v[kB];
 #pragma unroll
@@ -1025,7 +1080,10 @@ __device__ __forceinline__ void merge_unit(const AttnArgs& a, int unit, int b, i
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       if (s0 + u < k) {
-        const float m = __uint_as_float(mlw[u][0]), l = __uint_as_float(mlw[u][1]);
+        const bool mine = s0 + u == own;
+        if (mine) v[u] = __builtin_bit_cast(u32x4_t, own_acc);
+        const float m = mine ? own_m : __uint_as_float(mlw[u][0]);
+        const float l = mine ? own_l : __uint_as_float(mlw[u][1]);
         const float mn = fmaxf(M, m);
         if (mn != -INFINITY) {  // a partial with no rows (m = -inf, l = 0, sums 0) adds nothing
           const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(m - mn);
@@ -1150,11 +1208,14 @@ struct TokenPartial {
 // once); write out and lse.  Thread (g, c4) owns 16-byte column c4 of head
 // g.  With no rows at all the unit gets out 0 and lse -inf.
 template <int G, bool BF16>
-__device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, int h, int slot0,
-                                              int nslots) {
+__device__ __forceinline__ void ragged_finish(const AttnArgs& a, const AttnShared& sh, int u, int b,
+                                              int h, int slot0, int nslots, int own) {
   const int tid = threadIdx.x;
   if (tid >= G * kHeadDim / 4) return;
   const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+  const f32x4_t own_acc = *reinterpret_cast<const f32x4_t*>(&const_cast<AttnShared&>(sh).u.s.beacon[0][0][0]
+                                                              + g * kHeadDim + 4 * c4);
+  const float own_m = sh.pml[g][0], own_l = sh.pml[g][1];
   constexpr int kB = 8;
   float M = -INFINITY, L = 0.0f;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1188,7 +1249,10 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, int u, int b, i
 #pragma unroll
       for (int k = 0; k < kB; ++k) {
         if (s0 + k < nslots) {
-          const float m = __uint_as_float(mlw[k][0]), l = __uint_as_float(mlw[k][1]);
+          const bool mine = s0 + k == own;
+          if (mine) v[k] = __builtin_bit_cast(u32x4_t, own_acc);
+          const float m = mine ? own_m : __uint_as_float(mlw[k][0]);
+          const float l = mine ? own_l : __uint_as_float(mlw[k][1]);
           const float mn = fmaxf(M, m);
           if (mn != -INFINITY) {
             const float a1 = __builtin_amdgcn_exp2f(M - mn), a2 = __builtin_amdgcn_exp2f(m - mn);
@@ -1344,34 +1408,55 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   wave_reduce<G, BF16>(st, rw.lpr);
   lds_barrier();  // every wave is done with its exp-weights (which alias the raw sums)
                     // and with the query (whose space takes the merged sums)
+  // ---- Every wave of the workgroup has swept its last tile: count the
+  // workgroup done now, so that the reply comes back while the partial is
+  // formed.  The workgroup that brings the count to k merges the unit; the
+  // others publish their partials and raise their slots' flags, which the
+  // merger waits for (they counted themselves done first, so they are all
+  // past their sweeps).  The merger keeps its own partial in LDS.
+  uint32_t done = 0;
+  if (tid == 0)
+    done = __hip_atomic_fetch_add(&a.counters[(size_t)unit * kCounterStride], 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
   wave_park<G, kFullNch, BF16, PG>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
   lds_barrier();
-  const size_t slot = (size_t)slot0 + c;
-  wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw, a.part_ml + slot * G * 2,
-                            a.part_acc + slot * G * kHeadDim);
-
-  // ---- the last workgroup of the unit merges everything.  Every thread
-  // waits for its coherent partial stores to complete before the barrier;
-  // only then does thread 0 count the workgroup as done.  The workgroup that
-  // brings the count to k reads all partials with coherent loads.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // (nothing is in flight any more: costs no extra wait)
-  if (tid == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(&a.counters[(size_t)unit * kCounterStride], 1u,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh.is_last = done == (uint32_t)(k - 1);
-  }
+  wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw);
+  if (tid == 0) sh.is_last = done == (uint32_t)(k - 1);
   lds_barrier();
-  if (!sh.is_last) return;
-  // ready for the next call: every workgroup of the unit has counted itself
-  // done, after its last request to the tile counter had completed
+  if (!sh.is_last) {
+    publish_partial<G>(a, sh, (size_t)slot0 + c);
+    return;
+  }
+  bool ok = true;
+  if (wave == 0) ok = wait_flags(a, slot0, k, c);
+  if (tid == 0) sh.is_last = ok ? 1 : 2;
+  lds_barrier();
+  // ready for the next call: lower the other slots' flags; once this
+  // workgroup's own requests to the unit's counters have completed (the
+  // other workgroups' completed before they raised their flags), clear the
+  // counters
+  if (tid < k && tid != c)
+    __hip_atomic_store(&a.flags[(size_t)slot0 + tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   if (tid < 2)
     __hip_atomic_store(&a.counters[(size_t)unit * kCounterStride + tid], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  if (sh.is_last != 1) {
+    // a partial never arrived (its workgroup did not run to its end): the
+    // unit's results are undefined and are written as NaN
+    if (tid < G * kHeadDim / 4) {
+      const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
+      float* out = a.out + (((size_t)b * a.num_q_heads + (size_t)h * G + g) * kHeadDim + 4 * c4);
+      *reinterpret_cast<f32x4_t*>(out) = f32x4_t{NAN, NAN, NAN, NAN};
+      if (a.lse && c4 == 0) a.lse[(size_t)b * a.num_q_heads + (size_t)h * G + g] = NAN;
+    }
+    return;
+  }
   if constexpr (RAGGED)
-    ragged_finish<G, BF16>(a, unit, b, h, slot0, k);
+    ragged_finish<G, BF16>(a, sh, unit, b, h, slot0, k, c);
   else
-    merge_unit<G>(a, unit, b, h);
+    merge_unit<G>(a, sh, slot0, k, c, b, h);
 }
 
 // Grid: `chunks` workgroups per (b, kv head) unit, numbered chunk-major

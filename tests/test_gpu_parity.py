@@ -245,10 +245,15 @@ def test_workspace_reused_across_plans(gpu_device):
         assert_parity(out.double().cpu().numpy(), ref, "bf16", f"reuse splits={splits}",
                       lse.double().cpu().numpy(), ref_lse)
     # every unit's counter line (16 uint32 per unit: workgroups done, tiles
-    # handed out, the rest unused) is back at zero
+    # handed out, the rest unused) and every partial slot's flag (one uint32
+    # per slot, 64 slots per unit, from the next 256-byte boundary) are back
+    # at zero
     units = wl.batch * wl.num_kv_heads
     counters = ws[:COUNTER_STRIDE * 4 * units].view(torch.int32).view(units, COUNTER_STRIDE)
     assert int(counters.abs().sum()) == 0, counters[counters.abs().sum(dim=1) != 0]
+    f0 = (COUNTER_STRIDE * 4 * units + 255) // 256 * 256
+    flags = ws[f0:f0 + 64 * 4 * units].view(torch.int32)
+    assert int(flags.abs().sum()) == 0, torch.nonzero(flags)
 
 
 def test_many_chunks_repeatable(gpu_device):
