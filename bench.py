@@ -12,25 +12,45 @@ before timing and stay resident in HBM.  The step's calls are captured once
 as a HIP graph and replayed (checked bit for bit against the eager step;
 --eager launches them directly).  The timed region is bracketed by device
 synchronisation and measured with events on the stream the library
-launches on.  Prints ONE JSON line.
+launches on, one event between consecutive steps, so the line carries the
+mean over the region and the median / p10 / p90 of the single steps.
+Prints ONE JSON line.
 
 Reported beside the headline tokens/s:
-  * roofline of the sweep kernel (algorithmic cache bytes per launch over
-    its average launch time, against 8 TB/s);
-  * the comparison at 128K on one layer: latent path at 16x vs the
+  * roofline of the sweep kernel: algorithmic bytes per launch over its
+    average launch time from the events (gaps between launches included),
+    against 8 TB/s; the same figure from the committed rocprofv3
+    kernel-trace summary when it was taken on these kernel sources; and the
+    streaming-read ceiling, a plain read of the same bytes by the library's
+    own read kernel (slimkv_bench_stream_read) in the same process;
+  * the comparison at 128K on one layer: latent path at 4/8/16/32x vs the
     reconstruct-then-attend paths on the same beacons (without and with the
     rotation of rebuilt beacon keys) and vs uncompressed full-KV attention
-    over all 131072 tokens; the ragged serving step, over capacity-sized
-    arrays and over a paged cache, and with 4 query tokens per sequence;
-    the same step as an ALiBi backbone runs it; the 48-layer Qwen step;
-  * the fp64 CPU oracle timed on a bounded sample on this host's cores.
+    over all 131072 tokens; the 32K one-layer workload; the ragged serving
+    step, over capacity-sized arrays and over a paged cache, and with 4
+    query tokens per sequence; the step as an ALiBi backbone runs it; the
+    48-layer Qwen step.  One-layer calls rotate over copies of their inputs
+    that together exceed 1 GB, so no call finds its inputs in the 256 MB
+    last-level cache;
+  * the fp64 CPU oracle timed on a bounded sample on this host's cores; its
+    first layer is the step's last one, whose outputs the GPU left in
+    out/lse after the timed replays, so the same run checks what it timed
+    against the oracle (the "parity" block).
+
+    python bench.py --calibrate        plain copy / read / write kernels of
+                                       known size, for scaling PMC counters
+    python bench.py --profile-summary DIR
+                                       summarise a rocprofv3 kernel trace
+                                       (CSV in DIR) per kernel instance
 """
 
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
+import math
 import os
 import pathlib
 import sys
@@ -40,6 +60,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 1_100_000_000  # one-layer calls rotate over input copies totalling more
 
 
 def parse_args():
@@ -51,9 +72,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--eager", action="store_true",
-                    help="launch each step's calls directly instead of replaying the step as one "
-                         "captured HIP graph")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one captured HIP graph per step instead of the calls "
+                         "launched directly (both are always checked bit for bit against each "
+                         "other, and the other one is reported beside the headline)")
     ap.add_argument("--ragged", action="store_true",
                     help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
                          "of the capacities, new token stored) and print its figures as one JSON line")
@@ -67,9 +89,21 @@ def parse_args():
     ap.add_argument("--alibi", action="store_true",
                     help="only time the step as an ALiBi backbone runs it (slimkv_decode_attn_alibi) "
                          "and print its figures as one JSON line")
+    ap.add_argument("--only", default="",
+                    help="only time one comparison entry (c2, c5_4x, c5_8x, c5_16x, c5_32x, "
+                         "full_kv, read_ceiling) and print it as one JSON line")
     ap.add_argument("--calibrate", action="store_true",
-                    help="only run a plain 1 GiB device copy (torch) and a 512 MiB read-only "
-                         "reduction, for scaling hardware byte counters and as a read ceiling")
+                    help="only run plain kernels of known size (a 1 GiB copy, a 1 GiB read, a "
+                         "1 GiB write) for scaling hardware byte counters")
+    ap.add_argument("--report", nargs="+", metavar="JSON", default=None,
+                    help="print a markdown report of benchmark results: files holding one bench "
+                         "JSON line each, or a driver record with the line under 'parsed' (no GPU "
+                         "needed)")
+    ap.add_argument("--profile-summary", metavar="DIR", default="",
+                    help="summarise the rocprofv3 kernel trace (*kernel_trace.csv) under DIR and "
+                         "print it as JSON (no GPU needed): the attention kernel's last "
+                         "--steps x layers dispatches of --workload (the timed steps of a bench "
+                         "run with the same --steps), per layer and per step")
     return ap.parse_args()
 
 
@@ -88,47 +122,82 @@ def layer_call_bytes(wl, layer, elem):
     return cache, cache + bases + q + out
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 PMC summary, or None if that measurement was taken on other
-    kernel sources or another workload."""
-    rec_path = pathlib.Path(ROOT) / "profiles" / "attention_kernel_c3_traffic.json"
-    if not rec_path.exists():
-        return None
-    rec = json.loads(rec_path.read_text())
+def source_sha256():
+    """sha256 over the kernel sources (name and bytes of every file under csrc/)."""
     h = hashlib.sha256()
     for f in sorted((pathlib.Path(ROOT) / "latent_decode_attention_amd" / "csrc").iterdir()):
         h.update(f.name.encode())
         h.update(f.read_bytes())
-    if rec.get("source_sha256") != h.hexdigest() or rec.get("workload") != workload_name:
+    return h.hexdigest()
+
+
+def committed_record(name, workload_name):
+    """A committed summary under profiles/ (JSON), or None if it was taken on
+    other kernel sources or another workload."""
+    rec_path = pathlib.Path(ROOT) / "profiles" / name
+    if not rec_path.exists():
         return None
-    return rec["traffic_bytes_per_launch"]
+    rec = json.loads(rec_path.read_text())
+    if rec.get("source_sha256") != source_sha256() or rec.get("workload") != workload_name:
+        return None
+    return rec
 
 
-def attn_kernel_bytes(wl, layer, elem):
-    """Algorithmic bytes one latent call must move: the cache rows, q, U_K,
-    U_V, and the fp32 out and lse."""
-    return layer_call_bytes(wl, layer, elem)[1]
+def pct(xs):
+    """(median, p10, p90) of a list, in its units."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    p10, p50, p90 = np.percentile(a, [10, 50, 90])
+    return float(p50), float(p10), float(p90)
 
 
-def time_calls(fn, iters, warmup, torch):
+def timed_steps(torch, run, steps, warmup):
+    """Run ``run`` warmup times, then ``steps`` times back to back with an
+    event recorded before the first and after every step, all on the
+    current stream.  Returns (mean ms over the whole region, per-step ms)."""
     for _ in range(warmup):
-        fn()
+        run()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(iters):
-        fn()
-    e.record()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        run()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters  # ms
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def capture(torch, fn):
+    """Run ``fn`` once eagerly, then capture it as a HIP graph."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+def step_stats(ms, per):
+    med, p10, p90 = pct(per)
+    return {"ms_per_step": round(ms, 4), "median_ms": round(med, 4), "p10_ms": round(p10, 4),
+            "p90_ms": round(p90, 4)}
 
 
 def main():
     args = parse_args()
+    if args.report:
+        print(report(args.report), end="")
+        return
+    if args.profile_summary:
+        import synth
+        print(json.dumps(profile_summary(args.profile_summary, synth.get_workload(args.workload),
+                                         args.steps)), flush=True)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the method's "
-              "hot path runs on one GPU's share; see DESIGN.md on sharding)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs "
+              "the attention on one GPU's share only (sharding by KV head or batch needs no "
+              "exchange and is described in the design notes, not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -138,7 +207,10 @@ def main():
 
     dev = torch.device("cuda:0")
     if args.calibrate:
-        calibrate(torch, dev)
+        calibrate(lda, torch, dev)
+        return
+    if args.only:
+        print(json.dumps(compare(lda, synth, torch, dev, only=args.only)), flush=True)
         return
     wl = synth.get_workload(args.workload)
     elem = wl.elem_bytes
@@ -173,49 +245,68 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    run, launch = step, "eager launches"
-    if not args.eager:
-        # A decode step's calls have no host work between them; a serving loop
-        # replays them as one captured graph.  The replay must reproduce the
-        # eager step bit for bit (the library allocates and resets nothing
-        # outside its kernels, so the captured launches are the whole step).
-        ref_out, ref_lse = out.clone(), lse.clone()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        out.zero_()
-        lse.zero_()
-        graph.replay()
-        torch.cuda.synchronize()
-        if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
-            raise RuntimeError("graph replay differs from the eager step")
-        run, launch = graph.replay, f"one captured HIP graph per step ({wl.layers} calls)"
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        run()
-    stop.record()
+    # The step's calls have no host work between them: they are launched
+    # back to back on one stream (what a native serving loop does), or
+    # replayed as one captured graph (what a Python serving loop does to save
+    # launch overhead).  The replay must reproduce the launched step bit for
+    # bit: the library allocates and resets nothing outside its kernels, so
+    # the captured launches are the whole step.
+    ref_out, ref_lse = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    out.zero_()
+    lse.zero_()
+    graph.replay()
     torch.cuda.synchronize()
+    if not (torch.equal(out, ref_out) and torch.equal(lse, ref_lse)):
+        raise RuntimeError("graph replay differs from the launched step")
+    modes = {"launched": (step, f"{wl.layers} calls launched back to back on one stream"),
+             "graph": (graph.replay, f"one captured HIP graph per step ({wl.layers} calls)")}
+    head, other = ("graph", "launched") if args.graph else ("launched", "graph")
+    run, launch = modes[head]
+    t0 = time.perf_counter()
+    ms_step, per_step = timed_steps(torch, run, args.steps, 0)
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_other, per_other = timed_steps(torch, modes[other][0], args.steps, 2)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
-    cache_step = sum(layer_call_bytes(wl, layer, elem)[0] for layer in range(wl.layers))
     total_step = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
     step_gbps = total_step / (ms_step * 1e-3) / 1e9
-    log(f"{ms_step:.3f} ms/step, {tokens_per_s:.0f} tokens/s, {step_gbps:.0f} GB/s "
-        f"(wall {wall:.2f}s)")
+    stats = step_stats(ms_step, per_step)
+    log(f"{ms_step:.4f} ms/step (median {stats['median_ms']}, p10 {stats['p10_ms']}, p90 "
+        f"{stats['p90_ms']}), {tokens_per_s:.0f} tokens/s, {step_gbps:.0f} GB/s (wall {wall:.2f}s)")
 
     # Each latent call is one kernel launch, so the events around the timed
     # region divided by the launches give that kernel's average launch time,
     # the short gap between back-to-back launches included.
     launches = wl.layers * args.steps
     kern_us = ms_step * 1e3 / wl.layers
-    kern_bytes = sum(attn_kernel_bytes(wl, layer, elem) for layer in range(wl.layers)) / wl.layers
+    kern_bytes = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers)) / wl.layers
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
-    log(f"attention kernel: {kern_us:.1f} us average over {launches} launches, "
-        f"{achieved:.0f} GB/s")
-
+    log(f"attention kernel: {kern_us:.2f} us average over {launches} launches, "
+        f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBPS:.4f} of peak)")
+    traffic = committed_record("attention_kernel_c3_traffic.json", wl.name)
+    prof = committed_record(f"attention_kernel_{args.workload}_trace.json", wl.name)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic["traffic_bytes_per_launch"] if traffic else None,
+        "kernel": "attention_kernel (the whole latent call is this one launch)",
+        "bytes_per_launch": int(kern_bytes),
+        "launch_us": round(kern_us, 2),
+        "launch_us_from": "events over the timed region / launches (gaps included); frac uses it",
+        "launches_timed": launches,
+        "rocprof": ({"launch_us": prof["launch_us"], "frac": prof["frac"],
+                     "summary": prof["summary"], "traced_step_ms": prof.get("traced_step_ms")}
+                    if prof else None),
+    }
+    other_stats = step_stats(ms_other, per_other)
+    other_stats.update({"tokens_per_s": round(wl.batch / (ms_other * 1e-3), 1),
+                        "launch_us": round(ms_other * 1e3 / wl.layers, 2), "launch": modes[other][1]})
+    log(f"same step, {other}: {other_stats}")
     result = {
         "metric": "decode-attn tokens/s + HBM GB/s (% peak) at 128K, latent vs full-KV, 1 GPU",
         "value": round(tokens_per_s, 1),
@@ -224,6 +315,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "median_ms_per_step": stats["median_ms"],
+        "p10_ms_per_step": stats["p10_ms"],
+        "p90_ms_per_step": stats["p90_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -243,19 +337,16 @@ def main():
         },
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac_of_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl.name),
-            "kernel": "attention_kernel (the whole latent call is this one launch)",
-            "bytes_per_launch": int(kern_bytes),
-            "launch_us": round(kern_us, 2),
-            "launches_timed": launches,
-        },
+        "roofline": roofline,
+        f"step_{other}": other_stats,
     }
+    # the last layer's out / lse, as the timed replays left them (checked
+    # against the oracle in the CPU-baseline leg)
+    last_out, last_lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+    ceiling = read_ceiling(lda, torch, dev, int(kern_bytes))
+    roofline["read_ceiling"] = ceiling
+    log(f"read ceiling: {ceiling}")
 
     if not args.no_compare:
         result["comparison"] = compare(lda, synth, torch, dev)
@@ -275,93 +366,205 @@ def main():
     del ws
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s, synth)
+        base, parity = cpu_baseline(wl, layers, args.cpu_budget_s, synth, last_out, last_lse)
+        result["cpu_baseline"] = base
+        result["parity"] = parity
+    else:
+        result["parity"] = None
     print(json.dumps(result), flush=True)
 
 
-def calibrate(torch, dev):
-    """A plain copy of known size (1 GiB read + 1 GiB written per launch) to
-    scale FETCH_SIZE / WRITE_SIZE counters, and a read-only sum over 512 MiB
-    as a streaming-read reference."""
+# ---------------------------------------------------------------------------
+# Plain kernels: the streaming-read ceiling and counter calibration.
+
+def read_ceiling(lda, torch, dev, nbytes):
+    """The fastest plain streaming read of ``nbytes`` bytes in one launch of
+    the library's read kernel, over a sweep of its loads in flight per lane
+    and grid sizes.  Two buffers alternate, each larger than half the
+    last-level cache and together more than it, so no launch reads cached
+    bytes.  Per configuration: a captured graph of 8 launches, replayed 5
+    times; the per-launch time is the median replay / 8."""
+    nbytes = (max(nbytes, 16) + 15) // 16 * 16
+    bufs = [torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = None
+    sweep = []
+    for wgs in (cus, 2 * cus, 4 * cus, 8 * cus):
+        for fl in (1, 2, 4, 8, 16):
+            def fn():
+                for i in range(8):
+                    lda.slimkv_bench_stream_read(bufs[i % 2], sink, in_flight=fl, workgroups=wgs)
+            g = capture(torch, fn)
+            _, per = timed_steps(torch, g.replay, 5, 1)
+            us = pct(per)[0] * 1e3 / 8
+            sweep.append((wgs, fl, round(us, 2)))
+            if best is None or us < best[0]:
+                best = (us, wgs, fl)
+            del g
+    log("read sweep (workgroups, loads in flight per lane, us): " + str(sweep))
+    us, wgs, fl = best
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us": round(us, 2), "gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "config": f"{wgs} workgroups x 256 threads, {fl} 16-byte loads in flight per lane",
+            "kernel": "slimkv_bench_stream_read (libslimkv)"}
+
+
+def calibrate(lda, torch, dev):
+    """Plain kernels of known size, for scaling FETCH_SIZE / WRITE_SIZE: a
+    1 GiB device copy (torch), a 1 GiB read (the library's read kernel) and
+    a 1 GiB write (the library's flush kernel), three launches each."""
     n = 1 << 30
     src = torch.ones(n // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
-    t_copy = time_calls(lambda: dst.copy_(src), 10, 3, torch)
-    rd = src[: (n // 4)]
-    t_sum = time_calls(lambda: rd.sum(dtype=torch.float32), 10, 3, torch)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def t3(fn):
+        fn()
+        torch.cuda.synchronize()
+        _, per = timed_steps(torch, fn, 3, 0)
+        return pct(per)[0]
+
+    rd = src[: (n // 2 - 8)]  # the read kernel takes at most 2^31 - 16 bytes: read 1 GiB - 16
+    t_copy = t3(lambda: dst.copy_(src))
+    t_read = t3(lambda: lda.slimkv_bench_stream_read(rd, sink, in_flight=4))
+    t_write = t3(lambda: lda.slimkv_bench_flush(dst))
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n,
                       "copy_us": round(t_copy * 1e3, 1),
-                      "copy_gbps": round(2 * n / (t_copy * 1e-3) / 1e9, 1),
-                      "sum_bytes_read": n // 2, "sum_us": round(t_sum * 1e3, 1),
-                      "sum_read_gbps": round((n // 2) / (t_sum * 1e-3) / 1e9, 1)}), flush=True)
+                      "read_bytes": rd.numel() * 2, "read_us": round(t_read * 1e3, 1),
+                      "write_bytes": n, "write_us": round(t_write * 1e3, 1)}), flush=True)
 
 
-def compare(lda, synth, torch, dev):
-    """One 128K layer (B=16): latent at 16x vs reconstruct on the same beacons
-    vs full-KV over 131072 tokens, plus the latent sweep at 4x/8x/32x."""
+# ---------------------------------------------------------------------------
+# One-layer comparisons at 128K, with rotated inputs.
+
+def rotated_call_us(torch, calls, reps=10):
+    """Capture the list of calls (each over its own copy of the inputs) as
+    one graph, replay it ``reps`` times with an event between replays, and
+    return per-call (mean, median, p10, p90) in us."""
+    def fn():
+        for c in calls:
+            c()
+    g = capture(torch, fn)
+    ms, per = timed_steps(torch, g.replay, reps, 2)
+    n = len(calls)
+    med, p10, p90 = pct(per)
+    return ms * 1e3 / n, med * 1e3 / n, p10 * 1e3 / n, p90 * 1e3 / n
+
+
+def timing_entry(us_tuple, nbytes):
+    mean, med, p10, p90 = us_tuple
+    gbps = nbytes / (mean * 1e-6) / 1e9
+    return {"us": round(mean, 1), "median_us": round(med, 1), "p10_us": round(p10, 1),
+            "p90_us": round(p90, 1), "gbps": round(gbps, 1),
+            "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def layer_sets(synth, wl, dev, nbytes):
+    """Copies of one layer's inputs (distinct seeds) that together exceed
+    ROTATE_BYTES."""
+    n = max(1, math.ceil(ROTATE_BYTES / nbytes))
+    return [synth.make_layer(wl, 0, base_seed=s, device=dev) for s in range(n)]
+
+
+def latent_bytes(wl):
+    return layer_call_bytes(wl, 0, wl.elem_bytes)[1]
+
+
+def recon_bytes(wl):
+    """Reconstruct-then-attend: the latent bytes, plus the rebuilt beacon
+    keys and values written once and read back once at full width."""
+    units = wl.batch * wl.num_kv_heads
+    return latent_bytes(wl) + 2 * 2 * units * wl.num_beacons * wl.head_dim * wl.elem_bytes
+
+
+def compare(lda, synth, torch, dev, only=""):
+    """One layer at 128K (B=16): the latent path at 4/8/16/32x vs the
+    reconstruct paths on the same beacons (16x) vs full KV over 131072
+    tokens; the 32K one-layer workload; the read ceiling on full KV's bytes."""
     res = {}
-    full_wl = synth.get_workload("c5_full")
-    log("comparison: generating full-KV cache (131072 tokens)")
-    K, V = synth.make_full_kv(full_wl, 0, device=dev)
-    base = synth.make_layer(full_wl, 0, device=dev, num_beacons=0, raw_window=128)
-    pf = lda.make_problem(batch=full_wl.batch, num_q_heads=full_wl.num_q_heads,
-                          num_kv_heads=full_wl.num_kv_heads, num_beacons=0, rank_k=0, rank_v=0,
-                          raw_window=full_wl.context, scale=full_wl.scale,
-                          rope_theta=full_wl.rope_theta, dtype=full_wl.dtype)
-    out, lse = lda.alloc_outputs(pf, dev)
-    ws = lda.alloc_workspace(pf, lda.SLIMKV_OP_FULL_KV, dev)
-    t_full = time_calls(lambda: lda.full_kv_attn(pf, base.q, base.q_pos, K, V, out, lse, ws),
-                        10, 3, torch)
-    bytes_full = 2 * K.numel() * K.element_size()
-    res["full_kv"] = {"us": round(t_full * 1e3, 1), "gbps": round(bytes_full / t_full / 1e6, 1)}
-    del K, V, ws
-    torch.cuda.empty_cache()
-    for key in ("c5_4x", "c5_8x", "c5_16x", "c5_32x"):
+    keys = [only] if only else ["full_kv", "c5_4x", "c5_8x", "c5_16x", "c5_32x", "c2"]
+    t_full = None
+    if "full_kv" in keys or not only:
+        full_wl = synth.get_workload("c5_full")
+        log("comparison: generating full-KV cache (131072 tokens)")
+        K, V = synth.make_full_kv(full_wl, 0, device=dev)
+        base = synth.make_layer(full_wl, 0, device=dev, num_beacons=0, raw_window=128)
+        pf = lda.make_problem(batch=full_wl.batch, num_q_heads=full_wl.num_q_heads,
+                              num_kv_heads=full_wl.num_kv_heads, num_beacons=0, rank_k=0, rank_v=0,
+                              raw_window=full_wl.context, scale=full_wl.scale,
+                              rope_theta=full_wl.rope_theta, dtype=full_wl.dtype)
+        out, lse = lda.alloc_outputs(pf, dev)
+        ws = lda.alloc_workspace(pf, lda.SLIMKV_OP_FULL_KV, dev)
+        bytes_full = 2 * K.numel() * K.element_size()
+        us = rotated_call_us(torch, [lambda: lda.full_kv_attn(pf, base.q, base.q_pos, K, V, out,
+                                                              lse, ws)], reps=10)
+        t_full = us[0]
+        res["full_kv"] = timing_entry(us, bytes_full)
+        log(f"comparison full_kv: {res['full_kv']}")
+        del K, V, ws
+        torch.cuda.empty_cache()
+    if only == "read_ceiling":
+        return read_ceiling(lda, torch, dev, 403_310_592)
+    for key in [k for k in keys if k.startswith("c5_") or k == "c2"]:
         wl = synth.get_workload(key)
-        x = synth.make_layer(wl, 0, device=dev)
-        p = lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
+        nbytes = latent_bytes(wl)
+        sets = layer_sets(synth, wl, dev, nbytes)
+        x0 = sets[0]
+        p = lda.problem_from_tensors(x0.q, x0.U_K, x0.C_K, x0.K_raw, U_V=x0.U_V,
                                      rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
                                      scale=wl.scale)
+        out, lse = lda.alloc_outputs(p, dev)
         ws = lda.alloc_workspace(p, lda.SLIMKV_OP_LATENT, dev)
-        t = time_calls(lambda: lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K,
-                                                      x.C_V, x.K_raw, x.V_raw, out, lse, ws),
-                       20, 3, torch)
-        cache = wl.layer_bytes(0)
-        entry = {"us": round(t * 1e3, 1), "gbps": round(cache / t / 1e6, 1),
-                 "speedup_vs_full_kv": round(t_full / t, 2)}
+        calls = [lambda x=x: lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V,
+                                                    x.K_raw, x.V_raw, out, lse, ws) for x in sets]
+        entry = timing_entry(rotated_call_us(torch, calls, reps=10), nbytes)
+        entry["input_copies"] = len(sets)
+        if t_full is not None and key != "c2":
+            entry["speedup_vs_full_kv"] = round(t_full / entry["us"], 2)
+        if key == "c2":
+            entry["tokens_per_s"] = round(wl.batch / (entry["us"] * 1e-6), 1)
         if key == "c5_16x":
+            del ws
+            torch.cuda.empty_cache()
+            rb = recon_bytes(wl)
+            rsets = sets[: max(1, math.ceil(ROTATE_BYTES / rb))]
             wsr = lda.alloc_workspace(p, lda.SLIMKV_OP_RECONSTRUCT, dev)
-            tr = time_calls(lambda: lda.slimkv_reconstruct_attn(
-                p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw, out, lse, wsr),
-                10, 3, torch)
-            entry["reconstruct_us"] = round(tr * 1e3, 1)
-            entry["speedup_vs_reconstruct"] = round(tr / t, 2)
+            rcalls = [lambda x=x: lda.slimkv_reconstruct_attn(
+                p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw, out, lse, wsr)
+                for x in rsets]
+            er = timing_entry(rotated_call_us(torch, rcalls, reps=10), rb)
+            entry["reconstruct"] = er
+            entry["speedup_vs_reconstruct"] = round(er["us"] / entry["us"], 2)
             # the variant the page times: rebuilt beacon keys rotated at their
             # positions (one beacon per s tokens, at the end of its span)
             s_tok = wl.context // wl.num_beacons
             bpos = ((torch.arange(wl.num_beacons, device=dev, dtype=torch.int64) + 1) * s_tok
                     - 1).to(torch.int32)
-            trr = time_calls(lambda: lda.slimkv_reconstruct_rope_attn(
+            rrcalls = [lambda x=x: lda.slimkv_reconstruct_rope_attn(
                 p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw, bpos, out, lse,
-                wsr), 10, 3, torch)
-            entry["reconstruct_rope_us"] = round(trr * 1e3, 1)
-            entry["speedup_vs_reconstruct_rope"] = round(trr / t, 2)
+                wsr) for x in rsets]
+            err = timing_entry(rotated_call_us(torch, rrcalls, reps=10), rb)
+            entry["reconstruct_rope"] = err
+            entry["speedup_vs_reconstruct_rope"] = round(err["us"] / entry["us"], 2)
             del wsr
         res[key] = entry
-        del x, ws
+        del sets, x0, calls
         torch.cuda.empty_cache()
         log(f"comparison {key}: {entry}")
-    return res
+    return res if not only else res.get(only, res)
 
 
-def replay_ms(torch, step, steps):
-    """Capture ``step`` as one graph and time its replays (ms per step)."""
-    step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    return time_calls(graph.replay, steps, 3, torch)
+# ---------------------------------------------------------------------------
+# Whole steps of other entry points and workloads, replayed as graphs.
+
+def replay_stats(torch, step, steps):
+    """Capture ``step`` as one graph and time its replays."""
+    g = capture(torch, step)
+    return timed_steps(torch, g.replay, steps, 3)
 
 
 def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
@@ -407,24 +610,30 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
                                              pc.K_raw, pc.V_raw, st.num_beacons, st.raw_len,
                                              st.k_new, st.v_new, out, lse, ws)
     else:
+        # the call stores the new token into the raw arrays: give it copies,
+        # so the headline step's inputs (checked against the oracle at the
+        # end) stay as they were
+        raws = [(x.K_raw.clone(), x.V_raw.clone()) for x in layers]
+
         def step():
-            for p, x, st in zip(probs, layers, steps_in):
+            for p, x, st, (kr, vr) in zip(probs, layers, steps_in, raws):
                 lda.slimkv_decode_attn_ragged(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V,
-                                              x.K_raw, x.V_raw, st.num_beacons, st.raw_len,
+                                              kr, vr, st.num_beacons, st.raw_len,
                                               st.k_new, st.v_new, out, lse, ws)
 
-    ms = replay_ms(torch, step, steps)
+    ms, per = replay_stats(torch, step, steps)
     gbps = bytes_step / (ms * 1e-3) / 1e9
-    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
-           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
-           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-           "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
-                        f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + new token"}
+    res = step_stats(ms, per)
+    res.update({"us_per_layer": round(ms * 1e3 / wl.layers, 2),
+                "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
+                             f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + new token"})
     if page_rows:
         res["page_rows"] = page_rows
         del paged, tables
     log(f"{'paged' if page_rows else 'ragged'} step: {res}")
-    del ws
+    del ws, step
     torch.cuda.empty_cache()
     return res
 
@@ -474,25 +683,28 @@ def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens, page_rows=
                                                    pc.C_V, pc.K_raw, pc.V_raw, c.num_beacons,
                                                    c.raw_len, c.k_new, c.v_new, out, lse, ws)
     else:
+        raws = [(x.K_raw.clone(), x.V_raw.clone()) for x in layers]  # the call stores tokens
+
         def step():
-            for p, x, c in zip(probs, layers, chunks):
+            for p, x, c, (kr, vr) in zip(probs, layers, chunks, raws):
                 lda.slimkv_decode_attn_chunk(p, Q, c.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V,
-                                             x.K_raw, x.V_raw, c.num_beacons, c.raw_len, c.k_new,
+                                             kr, vr, c.num_beacons, c.raw_len, c.k_new,
                                              c.v_new, out, lse, ws)
 
-    ms = replay_ms(torch, step, steps)
+    ms, per = replay_stats(torch, step, steps)
     gbps = bytes_step / (ms * 1e-3) / 1e9
-    res = {"tokens_per_chunk": Q, "ms_per_step": round(ms, 4),
-           "us_per_layer": round(ms * 1e3 / wl.layers, 2),
-           "query_tokens_per_s": round(wl.batch * Q / (ms * 1e-3), 1), "gbps": round(gbps, 1),
-           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
-           "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
-                        f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + {Q} tokens"}
+    res = {"tokens_per_chunk": Q}
+    res.update(step_stats(ms, per))
+    res.update({"us_per_layer": round(ms * 1e3 / wl.layers, 2),
+                "query_tokens_per_s": round(wl.batch * Q / (ms * 1e-3), 1),
+                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                "live_rows": f"beacons {int(nb.min())}..{int(nb.max())} (mean {nb.mean():.0f}), raw "
+                             f"{int(rw.min())}..{int(rw.max())} (mean {rw.mean():.0f}) + {Q} tokens"})
     if page_rows:
         res["page_rows"] = page_rows
         del paged, tables
     log(f"{'paged ' if page_rows else ''}chunk step: {res}")
-    del ws, chunks
+    del ws, chunks, step
     torch.cuda.empty_cache()
     return res
 
@@ -517,12 +729,13 @@ def alibi_step(lda, synth, torch, dev, wl, layers, steps):
             lda.slimkv_decode_attn_alibi(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
                                          x.V_raw, slopes, first, stride, out, lse, ws)
 
-    ms = replay_ms(torch, step, steps)
+    ms, per = replay_stats(torch, step, steps)
     total = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
     gbps = total / (ms * 1e-3) / 1e9
-    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
-           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
-           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    res = step_stats(ms, per)
+    res.update({"us_per_layer": round(ms * 1e3 / wl.layers, 2),
+                "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
     log(f"alibi step: {res}")
     del ws
     torch.cuda.empty_cache()
@@ -547,24 +760,36 @@ def other_step(lda, synth, torch, dev, name, steps):
             lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw,
                                    out, lse, ws)
 
-    ms = replay_ms(torch, step, steps)
+    ms, per = replay_stats(torch, step, steps)
     total = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
     gbps = total / (ms * 1e-3) / 1e9
-    res = {"ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / wl.layers, 2),
-           "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
-           "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    res = step_stats(ms, per)
+    res.update({"us_per_layer": round(ms * 1e3 / wl.layers, 2),
+                "tokens_per_s": round(wl.batch / (ms * 1e-3), 1), "gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)})
     log(f"{name} step: {res}")
     del layers, ws
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(wl, layers, budget_s, synth):
+# ---------------------------------------------------------------------------
+# The CPU baseline (the fp64 oracle on the host's cores) and the parity of
+# the timed outputs.
+
+BF16_MAX_ABS, BF16_REL_L2, FP32_REL_L2 = 1e-2, 5e-3, 1e-5
+
+
+def cpu_baseline(wl, layers, budget_s, synth, last_out, last_lse):
     """The fp64 oracle on this host's cores over whole layers (the same
     inputs the GPU ran, copied to host memory once), in passes over the
-    step's layers until the time budget is spent; the step time is the time
-    per multiply-add times the step's multiply-add count (each layer's count
-    depends on its rank)."""
+    step's layers until the time budget is spent, starting with the last
+    layer; the step time is the time per multiply-add times the step's
+    multiply-add count (each layer's count depends on its rank).  The first
+    call's result -- the last layer -- is compared with the out and lse the
+    GPU's timed replays left behind: returns (baseline, parity)."""
+    import numpy as np
+
     import oracle
 
     threads = oracle.max_threads()
@@ -577,27 +802,233 @@ def cpu_baseline(wl, layers, budget_s, synth):
     st = synth.to_numpy_storage
     host = {}
     done, spent, calls = 0, 0.0, 0
+    parity = None
+    order = [wl.layers - 1] + list(range(wl.layers - 1))
     while spent < budget_s and calls < 64 * wl.layers:
-        layer = calls % wl.layers
+        layer = order[calls % wl.layers]
         if layer not in host:
             x = layers[layer]
             host[layer] = [st(t) for t in (x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw,
                                            x.V_raw)]
         t0 = time.perf_counter()
-        oracle.decode(*host[layer], num_kv_heads=wl.num_kv_heads, scale=wl.scale,
-                      rope_theta=wl.rope_theta, threads=threads)
+        ref, ref_lse = oracle.decode(*host[layer], num_kv_heads=wl.num_kv_heads, scale=wl.scale,
+                                     rope_theta=wl.rope_theta, threads=threads)
         spent += time.perf_counter() - t0
+        if parity is None:
+            diff = last_out - ref
+            rel = float(np.linalg.norm(diff) / np.linalg.norm(ref))
+            max_abs = float(np.abs(diff).max())
+            per_head = np.linalg.norm(diff, axis=-1) / np.linalg.norm(ref, axis=-1)
+            lse_err = float(np.abs(last_lse - ref_lse).max())
+            bf16 = wl.dtype == "bf16"
+            ok = (max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2) if bf16 else rel <= FP32_REL_L2
+            parity = {"checked": f"layer {layer} (the step's last), all {wl.batch} x "
+                                 f"{wl.num_q_heads} heads, GPU out/lse from the timed replays vs "
+                                 "the fp64 oracle",
+                      "rel_l2": float(f"{rel:.3e}"), "max_abs": float(f"{max_abs:.3e}"),
+                      "worst_head_rel_l2": float(f"{float(per_head.max()):.3e}"),
+                      "lse_max_abs": float(f"{lse_err:.3e}"),
+                      "bar": ("max-abs <= 1e-2 and rel-L2 <= 5e-3" if bf16 else "rel-L2 <= 1e-5"),
+                      "pass": bool(ok)}
+            log(f"parity of the timed outputs: {parity}")
         done += macs(layer)
         calls += 1
     log(f"cpu oracle: {calls} layer calls in {spent:.1f}s")
     total = sum(macs(layer) for layer in range(wl.layers))
     step_s = spent * total / done
     passes = f"{calls / wl.layers:.2f} passes over the {wl.layers} layers"
-    return {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": threads,
+    base = {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"{calls} layer calls ({passes}; all {wl.batch * wl.num_kv_heads} units "
                        f"each) timed in {spent:.1f}s with fp64 C+OpenMP; step time {step_s:.2f}s "
                        f"= time per multiply-add x the step's multiply-add count")}
+    return base, parity
+
+
+# ---------------------------------------------------------------------------
+# Markdown report of bench results.
+
+def _load_result(path):
+    """(bench JSON line, source note) from a file: a driver record whose
+    'parsed' holds the line (with the full line in the run's stdout), or a
+    file whose last JSON line is the bench line."""
+    text = pathlib.Path(path).read_text()
+    try:
+        rec = json.loads(text)
+    except json.JSONDecodeError:
+        rec = None
+    if isinstance(rec, dict) and "run" in rec:
+        line = None
+        for ln in reversed(rec["run"].get("stdout_tail", "").splitlines()):
+            if ln.startswith("{") and '"metric"' in ln:
+                line = json.loads(ln)
+                break
+        line = line or rec.get("parsed", {})
+        note = (f"{path}: driver run of `{rec.get('cmd', '')}` on {rec.get('where', '?')}, "
+                f"commit {str(rec.get('head', '?'))[:12]}, {rec.get('driver_run_s', '?')} s")
+        return line, note
+    if isinstance(rec, dict) and "metric" in rec:
+        return rec, str(path)
+    for ln in reversed(text.splitlines()):
+        if ln.startswith("{") and '"metric"' in ln:
+            return json.loads(ln), str(path)
+    raise SystemExit(f"{path}: no bench JSON line found")
+
+
+def report(paths):
+    out = ["# Benchmark report", "",
+           "Generated by `python bench.py --report " + " ".join(paths) + "` from the files below; "
+           "every figure is copied or derived from them. Peak HBM bandwidth of MI355X: 8 TB/s.", ""]
+    for path in paths:
+        r, note = _load_result(path)
+        rf = r.get("roofline") or {}
+        out += [f"## {r.get('config', {}).get('workload', '?').split(':')[0]}", "", f"Source: {note}", ""]
+        out += ["| measure | value |", "|---|---|"]
+        out.append(f"| decode-attention tokens/s (whole step, {r.get('config', {}).get('launch', '')}) "
+                   f"| **{r.get('value')}** |")
+        med = r.get("median_ms_per_step")
+        pc = (f" (median {med}, p10 {r.get('p10_ms_per_step')}, p90 {r.get('p90_ms_per_step')})"
+              if med is not None else "")
+        out.append(f"| ms per step, mean over {r.get('steps')} steps | {r.get('ms_per_step')}{pc} |")
+        out.append(f"| HBM GB/s over the step (algorithmic bytes) | {r.get('hbm_gbps')} "
+                   f"({100 * r.get('hbm_frac_of_peak', 0):.1f}% of peak) |")
+        if rf:
+            out.append(f"| attention kernel, per launch (events) | {rf.get('launch_us')} us, "
+                       f"{rf.get('achieved')} GB/s, **{100 * rf.get('frac', 0):.1f}% of peak** |")
+            rp = rf.get("rocprof")
+            if rp:
+                out.append(f"| same, rocprofv3 kernel trace (`profiles/{rp.get('summary')}`) | "
+                           f"{rp.get('launch_us')} us, {100 * rp.get('frac', 0):.1f}% of peak |")
+            else:
+                out.append("| same, rocprofv3 kernel trace | no committed trace for these kernel "
+                           "sources |")
+            tr = rf.get("traffic")
+            ratio = tr / rf.get("bytes_per_launch", 1) if tr else 0.0
+            out.append("| HBM traffic per launch (PMC) | " +
+                       (f"{tr / 1e6:.1f} MB ({ratio:.3f} x algorithmic) |" if tr
+                        else "not measured on these kernel sources |"))
+            ce = rf.get("read_ceiling")
+            if ce:
+                out.append(f"| streaming-read ceiling, same bytes, one launch | {ce.get('us')} us, "
+                           f"{ce.get('gbps')} GB/s ({100 * ce.get('frac_of_peak', 0):.1f}% of peak); "
+                           f"attention kernel at {100 * rf.get('achieved', 0) / ce.get('gbps', 1):.1f}% "
+                           f"of it |")
+        other = [k for k in r if k.startswith("step_")]
+        for k in other:
+            o = r[k]
+            out.append(f"| same step, {o.get('launch')} | {o.get('ms_per_step')} ms, "
+                       f"{o.get('tokens_per_s')} tokens/s |")
+        cb = r.get("cpu_baseline")
+        if cb:
+            out.append(f"| CPU oracle (fp64, {cb.get('cores')} host threads) | {cb.get('value')} "
+                       f"{cb.get('unit')}: {cb.get('sample')} |")
+        par = r.get("parity")
+        if par:
+            out.append(f"| parity of the timed outputs ({par.get('checked')}) | rel-L2 "
+                       f"{par.get('rel_l2')}, max-abs {par.get('max_abs')}, lse {par.get('lse_max_abs')}; "
+                       f"bar {par.get('bar')}: **{'pass' if par.get('pass') else 'FAIL'}** |")
+        out.append("")
+        cmp_ = r.get("comparison") or {}
+        one = {k: v for k, v in cmp_.items() if k in ("full_kv", "c2") or k.startswith("c5_")}
+        if one:
+            out += ["### One layer at 128K (B 16), inputs rotated over copies > 1 GB", "",
+                    "| path | us (median, p10-p90) | GB/s | % of peak | speedup |", "|---|---|---|---|---|"]
+            for k, v in one.items():
+                sp = []
+                if "speedup_vs_full_kv" in v:
+                    sp.append(f"{v['speedup_vs_full_kv']}x vs full KV")
+                if "speedup_vs_reconstruct" in v:
+                    sp.append(f"{v['speedup_vs_reconstruct']}x vs reconstruct")
+                if "speedup_vs_reconstruct_rope" in v:
+                    sp.append(f"{v['speedup_vs_reconstruct_rope']}x vs reconstruct with beacon RoPE")
+                out.append(f"| {k} | {v.get('us')} ({v.get('median_us')}, {v.get('p10_us')}-"
+                           f"{v.get('p90_us')}) | {v.get('gbps')} | "
+                           f"{100 * v.get('frac_of_peak', 0):.1f} | {'; '.join(sp)} |")
+                for sub in ("reconstruct", "reconstruct_rope"):
+                    if sub in v:
+                        w = v[sub]
+                        out.append(f"| {k} {sub.replace('_', ' ')} | {w.get('us')} ({w.get('median_us')}, "
+                                   f"{w.get('p10_us')}-{w.get('p90_us')}) | {w.get('gbps')} | "
+                                   f"{100 * w.get('frac_of_peak', 0):.1f} | baseline |")
+            out.append("")
+        steps = {k: v for k, v in cmp_.items() if k not in one}
+        if steps:
+            out += ["### Other whole steps (graph replay)", "",
+                    "| step | ms (median) | us per layer | rate | GB/s | % of peak |",
+                    "|---|---|---|---|---|---|"]
+            for k, v in steps.items():
+                rate = v.get("tokens_per_s") or v.get("query_tokens_per_s")
+                out.append(f"| {k} | {v.get('ms_per_step')} ({v.get('median_ms')}) | "
+                           f"{v.get('us_per_layer')} | {rate} | {v.get('gbps')} | "
+                           f"{100 * v.get('frac_of_peak', 0):.1f} |")
+            out.append("")
+    return "\n".join(out) + "\n"
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 kernel-trace summary.
+
+def profile_summary(directory, wl, steps):
+    """The attention kernel's dispatches in a rocprofv3 kernel trace (CSV):
+    the last steps x layers of them (the timed steps; within a step the
+    dispatches follow the layers in order, so dispatch i of a step is layer
+    i and its algorithmic bytes are known).  Durations are End - Start of
+    each dispatch, in us; every other kernel is listed with its totals."""
+    import csv
+
+    import numpy as np
+    files = sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {directory}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
+                             row["Kernel_Name"].split("(")[0]))
+    rows.sort()
+    att = [r for r in rows if "attention_kernel" in r[2]]
+    n = steps * wl.layers
+    if len(att) < n:
+        raise SystemExit(f"{len(att)} attention dispatches, fewer than {steps} x {wl.layers}")
+    last = att[-n:]
+    dur = np.array([(e - s) / 1e3 for s, e, _ in last]).reshape(steps, wl.layers)
+    elem = wl.elem_bytes
+    per_layer = []
+    for layer in range(wl.layers):
+        b = layer_call_bytes(wl, layer, elem)[1]
+        us = float(dur[:, layer].mean())
+        per_layer.append({"layer": layer, "rank": wl.ranks[layer], "kernel": last[layer][2],
+                          "avg_us": round(us, 2), "bytes": b,
+                          "gbps": round(b / (us * 1e-6) / 1e9, 1)})
+    step_sum = dur.sum(axis=1)
+    span = (last[-1][1] - last[0][0]) / 1e3 / steps
+    launch_us = float(dur.mean())
+    mean_bytes = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers)) / wl.layers
+    gbps = mean_bytes / (launch_us * 1e-6) / 1e9
+    by_rank = {}
+    for p in per_layer:
+        by_rank.setdefault(p["rank"], []).append(p)
+    ranks = {str(r): {"layers": len(ps), "kernel": ps[0]["kernel"],
+                      "avg_us": round(float(np.mean([p["avg_us"] for p in ps])), 2),
+                      "bytes": ps[0]["bytes"],
+                      "gbps": round(ps[0]["bytes"] / (float(np.mean([p["avg_us"] for p in ps]))
+                                                      * 1e-6) / 1e9, 1)}
+             for r, ps in sorted(by_rank.items())}
+    others = {}
+    for s, e, name in rows:
+        if "attention_kernel" not in name:
+            o = others.setdefault(name[:80], [0, 0.0])
+            o[0] += 1
+            o[1] += (e - s) / 1e3
+    return {"workload": wl.name, "steps": steps, "dispatches": n,
+            "launch_us": round(launch_us, 3), "gbps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": int(mean_bytes),
+            "kernel_sum_per_step_us": round(float(step_sum.mean()), 1),
+            "first_start_to_last_end_per_step_us": round(span, 1),
+            "per_rank": ranks, "per_layer": per_layer,
+            "other_kernels": {k: {"calls": v[0], "sum_us": round(v[1], 1)} for k, v in others.items()},
+            "files": [os.path.relpath(f, directory) for f in files]}
 
 
 if __name__ == "__main__":

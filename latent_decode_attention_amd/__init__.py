@@ -17,5 +17,6 @@ from .binding import (SLIMKV_BF16, SLIMKV_FLAG_DYNAMIC_TILES, SLIMKV_FP32,  # no
                       slimkv_pages, slimkv_problem,
                       slimkv_reconstruct_attn, slimkv_reconstruct_rope_attn,
                       slimkv_set_kernel_events, slimkv_status_string,
-                      slimkv_workspace_bytes)
+                      slimkv_workspace_bytes, slimkv_bench_stream_read,
+                      slimkv_bench_flush)
 from .helpers import alloc_outputs, alloc_workspace, problem_from_tensors  # noqa: F401

@@ -29,7 +29,8 @@ EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_n
            "slimkv_decode_attn_chunk_paged", "slimkv_decode_attn_alibi",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
-           "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version")
+           "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version",
+           "slimkv_bench_stream_read", "slimkv_bench_flush")
 
 
 class slimkv_problem(ctypes.Structure):  # noqa: N801  (C name)
@@ -130,6 +131,10 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_set_kernel_events.restype = ctypes.c_int
     lib.slimkv_abi_version.argtypes = []
     lib.slimkv_abi_version.restype = ctypes.c_int32
+    lib.slimkv_bench_stream_read.argtypes = [vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.slimkv_bench_stream_read.restype = ctypes.c_int
+    lib.slimkv_bench_flush.argtypes = [vp, sz, ctypes.c_uint32, vp]
+    lib.slimkv_bench_flush.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -322,3 +327,28 @@ def slimkv_last_error() -> str:
 
 def slimkv_abi_version() -> int:
     return int(load_library().slimkv_abi_version())
+
+
+def _check_bench(status: int, what: str) -> None:
+    if status != 0:
+        raise SlimKVError(status, what)
+
+
+def slimkv_bench_stream_read(src, sink, *, in_flight: int = 4, workgroups: int = 0,
+                             nbytes: int | None = None, stream=None) -> None:
+    """Stream ``nbytes`` (default: all) of the tensor ``src`` once through the
+    plain read kernel; its checksum goes to ``sink`` (a 1-element int32 or
+    uint32 tensor)."""
+    lib = load_library()
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check_bench(lib.slimkv_bench_stream_read(_ptr(src), n, int(in_flight), int(workgroups),
+                                              _ptr(sink), _stream(stream)),
+                 f"slimkv_bench_stream_read({n} bytes, in_flight {in_flight})")
+
+
+def slimkv_bench_flush(buf, seed: int = 0, stream=None) -> None:
+    """Overwrite the whole of ``buf`` (a contiguous device tensor)."""
+    lib = load_library()
+    n = buf.numel() * buf.element_size()
+    _check_bench(lib.slimkv_bench_flush(_ptr(buf), n, int(seed) & 0xffffffff, _stream(stream)),
+                 f"slimkv_bench_flush({n} bytes)")

@@ -10,13 +10,18 @@ import pytest
 import latent_decode_attention_amd as lda
 from latent_decode_attention_amd import binding
 
-HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "slimkv.h"
+INCLUDE = pathlib.Path(__file__).resolve().parents[1] / "include"
+HEADER = INCLUDE / "slimkv.h"
 OK, NULL, SHAPE, UNSUP, WS, ALIGN, ALIAS = 0, 1, 2, 3, 4, 5, 6
 
 
 def header_functions():
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in sorted(INCLUDE.glob("*.h")):
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -435,3 +440,21 @@ def test_reconstruct_rope_checks(lib):
     assert call(out=ctypes.c_void_p(0x210000 - 16)) == ALIAS  # out runs into beacon_pos
     assert call(bp=None, p=_problem(num_beacons=0)) == WS      # no beacons: no positions needed
 
+
+
+def test_bench_helpers_reject_bad_arguments(lib):
+    """The measurement helpers check their arguments before any HIP call."""
+    vp = ctypes.c_void_p
+    src, sink = vp(0x1000000), vp(0x100)
+    assert lib.slimkv_bench_stream_read(None, 1024, 4, 0, sink, None) == NULL
+    assert lib.slimkv_bench_stream_read(src, 1024, 4, 0, None, None) == NULL
+    assert lib.slimkv_bench_stream_read(vp(0x1000008), 1024, 4, 0, sink, None) == ALIGN
+    assert lib.slimkv_bench_stream_read(src, 1000, 4, 0, sink, None) == SHAPE
+    assert lib.slimkv_bench_stream_read(src, 0, 4, 0, sink, None) == SHAPE
+    assert lib.slimkv_bench_stream_read(src, 1 << 31, 4, 0, sink, None) == SHAPE
+    assert lib.slimkv_bench_stream_read(src, 1024, 3, 0, sink, None) == UNSUP
+    assert lib.slimkv_bench_stream_read(src, 1024, 4, -1, sink, None) == SHAPE
+    assert lib.slimkv_bench_stream_read(src, 1024, 4, 0, vp(0x1000010), None) == ALIAS
+    assert lib.slimkv_bench_flush(None, 1024, 0, None) == NULL
+    assert lib.slimkv_bench_flush(vp(0x1000004), 1024, 0, None) == ALIGN
+    assert lib.slimkv_bench_flush(src, 1000, 0, None) == SHAPE
