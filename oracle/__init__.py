@@ -7,7 +7,8 @@ never imports the library: the two share no code.
 ``decode`` runs the plain C implementation in ``slimkv_oracle.c`` (double
 precision throughout, OpenMP over (batch, kv head) units); ``decode_ragged``
 the same with per-sequence lengths and the decode step's new token;
-``decode_chunk`` a chunk of several query tokens per sequence.  Its definition
+``decode_chunk`` a chunk of several query tokens per sequence; ``decode_alibi``
+and ``decode_chunk_alibi`` the ALiBi variant (no rotation, a distance bias).  Its definition
 follows page "Can SlimKV compress KV cache jointly across tokens and
 features", section "Latent-space attention removes the rebuild step": the
 rotated query is projected into each KV head's beacon latent space, scored
@@ -90,6 +91,12 @@ def load(path=LIBRARY) -> ctypes.CDLL:
             lib.slimkv_oracle_decode_alibi.argtypes = [ctypes.POINTER(_Problem)] + [
                 ctypes.c_void_p] * 10 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_int]
+        if hasattr(lib, "slimkv_oracle_decode_chunk_alibi"):
+            lib.slimkv_oracle_decode_chunk_alibi.restype = ctypes.c_int
+            lib.slimkv_oracle_decode_chunk_alibi.argtypes = [
+                ctypes.POINTER(_Problem), ctypes.c_int] + [ctypes.c_void_p] * 14 + [
+                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int]
         lib.slimkv_oracle_max_threads.restype = ctypes.c_int
         _lib_cache[key] = lib
     return _lib_cache[key]
@@ -310,6 +317,66 @@ def decode_alibi(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, beacon_pos, slop
     if rc != 0:
         raise ValueError(f"oracle rejected the problem (code {rc})")
     return out, lse
+
+
+def decode_chunk_alibi(q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw, *, beacon_pos, slopes,
+                       num_kv_heads: int, scale: float, num_beacons=None, raw_len=None,
+                       k_new=None, v_new=None, units=None, threads: int = 0,
+                       library: pathlib.Path = LIBRARY):
+    """fp64 ALiBi attention of a serving step: ``decode_chunk``'s ragged
+    cache, new tokens and Q query tokens per sequence, scored as in
+    ``decode_alibi`` (nothing rotated; score gets -slopes[h_q] * (q_pos_t -
+    k_pos)).  Positions: query token t at q_pos[b] + t, beacon j at
+    beacon_pos[j], new token u at q_pos[b] + u, live raw row i at
+    q_pos[b] - w_b + i with new tokens and q_pos[b] - w_b + 1 + i without.
+    q [B, Q, H_q, d] (a 3-d q is one token per sequence).  Returns (out, lse,
+    k_app) shaped [B, Q, H_q, d], [B, Q, H_q], [B, Q, H_kv, d] (squeezed to
+    3-d / 2-d when q was 3-d)."""
+    q = np.ascontiguousarray(q)
+    squeeze = q.ndim == 3
+    if squeeze:
+        q = q[:, None]
+        k_new = None if k_new is None else np.ascontiguousarray(k_new)[:, None]
+        v_new = None if v_new is None else np.ascontiguousarray(v_new)[:, None]
+    dt = q.dtype
+    if dt not in _DTYPE:
+        raise TypeError(f"unsupported storage dtype {dt}")
+    B, Q, Hq, d = q.shape
+    q_pos = _arr(q_pos, np.dtype(np.int32))
+    ncap = 0 if C_K is None else int(np.shape(C_K)[2])
+    wcap = 0 if K_raw is None else int(np.shape(K_raw)[2])
+    rk = int(np.shape(U_K)[2]) if U_K is not None else 0
+    rv = int(np.shape(U_V)[2]) if U_V is not None else 0
+    U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new = (
+        _arr(x, dt) for x in (U_K, U_V, C_K, C_V, K_raw, V_raw, k_new, v_new))
+    nbl = _arr(num_beacons, np.dtype(np.int32))
+    rwl = _arr(raw_len, np.dtype(np.int32))
+    bp = _arr(beacon_pos, np.dtype(np.int32)) if ncap else None
+    sl = np.ascontiguousarray(slopes, dtype=np.float64)
+    if sl.shape != (Hq,):
+        raise ValueError("slopes must have one entry per query head")
+    prob = _Problem(B, Hq, num_kv_heads, d, ncap, rk, rv, wcap, float(scale), 10000.0, _DTYPE[dt])
+    out = np.full((B, Q, Hq, d), np.nan, dtype=np.float64)
+    lse = np.full((B, Q, Hq), np.nan, dtype=np.float64)
+    k_app = np.full((B, Q, num_kv_heads, d), np.nan, dtype=np.float64)
+    if units is None:
+        unit_arr, n_units = None, 0
+    else:
+        unit_arr = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+        n_units = unit_arr.shape[0]
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    rc = load(library).slimkv_oracle_decode_chunk_alibi(
+        ctypes.byref(prob), int(Q), ptr(q), ptr(q_pos), ptr(U_K), ptr(U_V), ptr(C_K), ptr(C_V),
+        ptr(K_raw), ptr(V_raw), ptr(nbl), ptr(rwl), ptr(k_new), ptr(v_new), ptr(bp), ptr(sl),
+        ptr(unit_arr), n_units, ptr(out), ptr(lse), ptr(k_app), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the problem (code {rc})")
+    if squeeze:
+        return out[:, 0], lse[:, 0], k_app[:, 0]
+    return out, lse, k_app
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

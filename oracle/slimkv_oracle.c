@@ -40,7 +40,9 @@
  * slimkv_oracle_decode_chunk takes a chunk of several query tokens per
  * sequence, each attending causally to the chunk's new tokens (see
  * oracle_chunk_unit).  slimkv_oracle_decode_alibi is the ALiBi variant (no
- * rotation, a linear distance bias on every score; see oracle_alibi_unit).
+ * rotation, a linear distance bias on every score; see oracle_alibi_unit),
+ * and slimkv_oracle_decode_chunk_alibi its serving form (ragged lengths, new
+ * tokens, several query tokens; see oracle_alibi_chunk_unit).
  */
 #include <math.h>
 #include <stdint.h>
@@ -743,6 +745,193 @@ int slimkv_oracle_decode_chunk(const oracle_problem* p, int num_tokens, const vo
       }
       oracle_chunk_unit(&pp, num_tokens, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
                         num_beacons_b, raw_len, k_new, v_new, out, lse, k_app, work);
+    }
+    free(work);
+  }
+  if (failed == 1) return ORACLE_NO_MEMORY;
+  if (failed == 2) return ORACLE_BAD_SHAPE;
+  return ORACLE_OK;
+}
+
+/*
+ * The ALiBi variant of a serving step: ragged lengths, optional new tokens,
+ * and Q >= 1 query tokens per sequence (Q = 1: one decode step; the
+ * uniform variant above is the case of full lengths, no new tokens and
+ * Q = 1).  As in oracle_alibi_unit nothing is rotated and every score gets
+ * -slope[hq] * (q_pos_t - k_pos) after the scaled product.  Positions, the
+ * reading of a window that ends at the newest token:
+ *   query token t        q_pos[b] + t
+ *   beacon j             bpos[j]
+ *   new token u          q_pos[b] + u
+ *   live raw row i < w   q_pos[b] - w + i with new tokens (they follow the
+ *                        raw rows), q_pos[b] - w + 1 + i without (the first
+ *                        query's own token is the last raw row)
+ * Query token t attends over the live beacon rows, the live raw rows and
+ * the new tokens 0 .. t; new keys are stored as given (no rotation), so
+ * k_app (if given) receives them widened.  Lengths are clamped as in
+ * oracle_unit.  Layouts as in oracle_chunk_unit.
+ */
+static void oracle_alibi_chunk_unit(const oracle_problem* p, int ntok, int b, int h,
+                                    const void* q, const int32_t* q_pos, const void* U_K,
+                                    const void* U_V, const void* C_K, const void* C_V,
+                                    const void* K_raw, const void* V_raw, const int32_t* nb_len,
+                                    const int32_t* raw_len, const void* k_new, const void* v_new,
+                                    const int32_t* bpos, const double* slope, double* out,
+                                    double* lse, double* k_app, double* work) {
+  const int d = p->head_dim;
+  const int H = p->num_kv_heads, Hq = p->num_q_heads, G = Hq / H;
+  const int ncap = p->num_beacons, wcap = p->raw_window;
+  const int rk = p->rank_k, rv = p->rank_v;
+  const int dt = p->dtype;
+  int nb = nb_len ? nb_len[b] : ncap, w = raw_len ? raw_len[b] : wcap;
+  nb = nb < 0 ? 0 : (nb > ncap ? ncap : nb);
+  w = w < 0 ? 0 : (w > wcap ? wcap : w);
+  const int app = k_new != NULL;
+
+  double* qv = work;                         /* [d]           the query (unrotated) */
+  double* qlat = qv + d;                     /* [rk]          latent query          */
+  double* sc = qlat + rk;                    /* [nb + w + Q]  scores, weights       */
+  double* vl = sc + (size_t)nb + w + ntok;   /* [rv]          latent value sum      */
+  double* vr = vl + rv;                      /* [d]           raw value sum         */
+
+  const size_t unit = (size_t)b * H + h;
+  const size_t ck0 = unit * (size_t)ncap * rk, cv0 = unit * (size_t)ncap * rv;
+  const size_t kr0 = unit * (size_t)wcap * d;
+  const size_t uk0 = (size_t)h * d * rk, uv0 = (size_t)h * d * rv;
+  const double qp0 = (double)q_pos[b];
+  const double raw0 = qp0 - (double)w + (app ? 0.0 : 1.0); /* position of raw row 0 */
+
+  for (int u = 0; u < ntok && app && k_app; ++u) {
+    const size_t k0 = (((size_t)b * ntok + u) * H + h) * d;
+    for (int i = 0; i < d; ++i) k_app[k0 + i] = widen(k_new, dt, k0 + i);
+  }
+
+  for (int t = 0; t < ntok; ++t) {
+    const double qpos = qp0 + (double)t;
+    const int seen = app ? t + 1 : 0;
+    const size_t n = (size_t)nb + (size_t)w + (size_t)seen;
+    for (int g = 0; g < G; ++g) {
+      const int hq = h * G + g;
+      const double m_h = slope[hq];
+      const size_t row = ((size_t)b * ntok + t) * Hq + hq;
+      const size_t q0 = row * d;
+      if (n == 0) {
+        for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;
+        if (lse) lse[row] = -INFINITY;
+        continue;
+      }
+      for (int i = 0; i < d; ++i) qv[i] = widen(q, dt, q0 + i);
+      for (int k = 0; k < rk; ++k) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qv[i] * widen(U_K, dt, uk0 + (size_t)i * rk + k);
+        qlat[k] = acc;
+      }
+      for (int j = 0; j < nb; ++j) {
+        double acc = 0.0;
+        for (int k = 0; k < rk; ++k) acc += qlat[k] * widen(C_K, dt, ck0 + (size_t)j * rk + k);
+        sc[j] = p->scale * acc - m_h * (qpos - (double)bpos[j]);
+      }
+      for (int j = 0; j < w; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qv[i] * widen(K_raw, dt, kr0 + (size_t)j * d + i);
+        sc[nb + j] = p->scale * acc - m_h * (qpos - (raw0 + (double)j));
+      }
+      for (int u = 0; u < seen; ++u) {
+        const size_t k0 = (((size_t)b * ntok + u) * H + h) * d;
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qv[i] * widen(k_new, dt, k0 + i);
+        sc[nb + w + u] = p->scale * acc - m_h * (qpos - (qp0 + (double)u));
+      }
+      double mx = -INFINITY;
+      for (size_t j = 0; j < n; ++j) mx = sc[j] > mx ? sc[j] : mx;
+      double den = 0.0;
+      for (size_t j = 0; j < n; ++j) {
+        sc[j] = exp(sc[j] - mx);
+        den += sc[j];
+      }
+      for (size_t j = 0; j < n; ++j) sc[j] /= den;
+      for (int k = 0; k < rv; ++k) vl[k] = 0.0;
+      for (int j = 0; j < nb; ++j)
+        for (int k = 0; k < rv; ++k) vl[k] += sc[j] * widen(C_V, dt, cv0 + (size_t)j * rv + k);
+      for (int i = 0; i < d; ++i) vr[i] = 0.0;
+      for (int j = 0; j < w; ++j)
+        for (int i = 0; i < d; ++i) vr[i] += sc[nb + j] * widen(V_raw, dt, kr0 + (size_t)j * d + i);
+      for (int u = 0; u < seen; ++u) {
+        const size_t v0 = (((size_t)b * ntok + u) * H + h) * d;
+        for (int i = 0; i < d; ++i) vr[i] += sc[nb + w + u] * widen(v_new, dt, v0 + i);
+      }
+      for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * vl[k];
+        out[q0 + i] = acc + vr[i];
+      }
+      if (lse) lse[row] = mx + log(den);
+    }
+  }
+}
+
+/*
+ * ALiBi counterpart of slimkv_oracle_decode_chunk (see
+ * oracle_alibi_chunk_unit): bpos [N_b] int32 beacon positions, slope [H_q]
+ * doubles; num_tokens = Q >= 1.
+ */
+int slimkv_oracle_decode_chunk_alibi(const oracle_problem* p, int num_tokens, const void* q,
+                                     const int32_t* q_pos, const void* U_K, const void* U_V,
+                                     const void* C_K, const void* C_V, const void* K_raw,
+                                     const void* V_raw, const int32_t* num_beacons_b,
+                                     const int32_t* raw_len, const void* k_new,
+                                     const void* v_new, const int32_t* bpos,
+                                     const double* slope, const int32_t* units, int64_t n_units,
+                                     double* out, double* lse, double* k_app, int threads) {
+  if (!p || !q || !q_pos || !out || !slope || num_tokens < 1) return ORACLE_BAD_SHAPE;
+  if (p->dtype != ORACLE_F64 && p->dtype != ORACLE_F32 && p->dtype != ORACLE_BF16)
+    return ORACLE_BAD_DTYPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 ||
+      p->num_q_heads % p->num_kv_heads != 0 || p->head_dim < 1 || p->num_beacons < 0 ||
+      p->raw_window < 0)
+    return ORACLE_BAD_SHAPE;
+  if (p->num_beacons > 0 &&
+      (p->rank_k < 1 || p->rank_v < 1 || !U_K || !U_V || !C_K || !C_V || !bpos))
+    return ORACLE_BAD_SHAPE;
+  if (p->raw_window > 0 && (!K_raw || !V_raw)) return ORACLE_BAD_SHAPE;
+  if ((k_new == NULL) != (v_new == NULL)) return ORACLE_BAD_SHAPE;
+
+  const int64_t all = (int64_t)p->batch * p->num_kv_heads;
+  const int64_t count = units ? n_units : all;
+  const int rk = p->num_beacons > 0 ? p->rank_k : 0;
+  const int rv = p->num_beacons > 0 ? p->rank_v : 0;
+  const size_t work_len = 2 * (size_t)p->head_dim + rk + rv + (size_t)p->num_beacons +
+                          p->raw_window + num_tokens;
+  oracle_problem pp = *p;
+  pp.rank_k = rk;
+  pp.rank_v = rv;
+
+  int failed = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#else
+  (void)threads;
+#endif
+#pragma omp parallel
+  {
+    double* work = (double*)malloc(work_len * sizeof(double));
+    if (!work) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t u = 0; u < count; ++u) {
+      if (!work) continue;
+      int b = units ? units[2 * u] : (int)(u / p->num_kv_heads);
+      int h = units ? units[2 * u + 1] : (int)(u % p->num_kv_heads);
+      if (b < 0 || b >= p->batch || h < 0 || h >= p->num_kv_heads) {
+#pragma omp atomic write
+        failed = 2;
+        continue;
+      }
+      oracle_alibi_chunk_unit(&pp, num_tokens, b, h, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                              num_beacons_b, raw_len, k_new, v_new, bpos, slope, out, lse, k_app,
+                              work);
     }
     free(work);
   }

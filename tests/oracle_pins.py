@@ -728,6 +728,179 @@ def pin_alibi_steep(library):
             _close(out[b, hq], p["V_raw"][b, 0, -1], tol=1e-12, what="steep alibi")
 
 
+
+# ---------------------------------------------------------------------------
+# The ALiBi variant of a serving step (oracle.decode_chunk_alibi): ragged
+# lengths, new tokens and several query tokens per sequence.  Positions:
+# query token t at q_pos + t, beacon j at beacon_pos[j], new token u at
+# q_pos + u, live raw row i at q_pos - w + i with new tokens (they follow the
+# raw rows) and q_pos - w + 1 + i without.
+
+
+def alibi_step_problem(seed, *, Q=1, append=True, **shape):
+    p = ragged_problem(seed, append=False, **shape)
+    nb = p["C_K"].shape[2]
+    rng = np.random.default_rng(seed + 4000)
+    B, Hkv, d = p["q"].shape[0], p["num_kv_heads"], p["q"].shape[2]
+    Hq = p["q"].shape[1]
+    p["q"] = rng.standard_normal((B, Q, Hq, d))
+    p["q_pos"] = rng.integers(50, 200, size=B).astype(np.int32)
+    p["beacon_pos"] = ((np.arange(nb) + 1) * 4 - 1).astype(np.int32)
+    p["slopes"] = rng.uniform(0.01, 0.5, size=Hq)
+    if append:
+        p["k_new"] = rng.standard_normal((B, Q, Hkv, d))
+        p["v_new"] = rng.standard_normal((B, Q, Hkv, d))
+    return p
+
+
+def run_alibi_step(p, library, **over):
+    args = dict(p)
+    args.update(over)
+    ncap = args["C_K"].shape[2]
+    wcap = args["K_raw"].shape[2]
+    return oracle.decode_chunk_alibi(
+        args["q"], args["q_pos"], args["U_K"], args["U_V"],
+        args["C_K"] if ncap else None, args["C_V"] if ncap else None,
+        args["K_raw"] if wcap else None, args["V_raw"] if wcap else None,
+        beacon_pos=args["beacon_pos"], slopes=args["slopes"], num_kv_heads=args["num_kv_heads"],
+        scale=args["scale"], num_beacons=args.get("num_beacons"), raw_len=args.get("raw_len"),
+        k_new=args.get("k_new"), v_new=args.get("v_new"), library=library)
+
+
+def alibi_step_reference(p):
+    """Each sequence and query token alone: the live beacon rows rebuilt to
+    full width, the live raw rows and the new tokens up to the query, listed
+    with their positions; plain attention with the bias."""
+    q = p["q"]
+    B, Q, Hq, d = q.shape
+    Hkv = p["num_kv_heads"]
+    G = Hq // Hkv
+    out = np.zeros((B, Q, Hq, d))
+    lse = np.zeros((B, Q, Hq))
+    app = p.get("k_new") is not None
+    for b in range(B):
+        nbc = int(np.clip(p["num_beacons"][b], 0, p["C_K"].shape[2]))
+        wc = int(np.clip(p["raw_len"][b], 0, p["K_raw"].shape[2]))
+        qp = int(p["q_pos"][b])
+        for t in range(Q):
+            for hq in range(Hq):
+                h = hq // G
+                keys = [p["C_K"][b, h, j] @ p["U_K"][h].T for j in range(nbc)]
+                vals = [p["C_V"][b, h, j] @ p["U_V"][h].T for j in range(nbc)]
+                pos = [int(p["beacon_pos"][j]) for j in range(nbc)]
+                first_raw = qp - wc if app else qp - wc + 1
+                keys += [p["K_raw"][b, h, i] for i in range(wc)]
+                vals += [p["V_raw"][b, h, i] for i in range(wc)]
+                pos += [first_raw + i for i in range(wc)]
+                if app:
+                    keys += [p["k_new"][b, u, h] for u in range(t + 1)]
+                    vals += [p["v_new"][b, u, h] for u in range(t + 1)]
+                    pos += [qp + u for u in range(t + 1)]
+                if not keys:
+                    lse[b, t, hq] = -np.inf
+                    continue
+                K, V = np.array(keys), np.array(vals)
+                sc = p["scale"] * (K @ q[b, t, hq]) - p["slopes"][hq] * (qp + t - np.array(pos, float))
+                m = sc.max()
+                e = np.exp(sc - m)
+                out[b, t, hq] = e @ V / e.sum()
+                lse[b, t, hq] = m + np.log(e.sum())
+    return out, lse
+
+
+def pin_alibi_step_reference(library):
+    """Ragged lengths (clamped), new tokens, several query tokens: each
+    sequence against plain attention over its listed rows and positions."""
+    for seed, Q, app, shape in ((80, 1, True, dict(B=4, Hkv=2, G=2, d=16, ncap=9, rk=4, rv=6, wcap=7)),
+                                (81, 3, True, dict(B=3, Hkv=1, G=4, d=32, ncap=6, rk=8, rv=4, wcap=5)),
+                                (82, 2, False, dict(B=3, Hkv=2, G=1, d=16, ncap=5, rk=4, rv=4, wcap=6)),
+                                (83, 2, True, dict(B=2, Hkv=1, G=2, d=16, ncap=0, rk=4, rv=4, wcap=4))):
+        p = alibi_step_problem(seed, Q=Q, append=app, **shape)
+        if shape["B"] > 2:
+            p["num_beacons"][1] = 0
+            p["raw_len"][1] = 0
+            p["num_beacons"][2] = shape["ncap"] + 3  # clamped
+            p["raw_len"][2] = -1
+        out, lse, k_app = run_alibi_step(p, library)
+        ref, ref_lse = alibi_step_reference(p)
+        _close(out, ref, what=f"alibi step out Q={Q} app={app}")
+        fin = np.isfinite(ref_lse)
+        assert np.array_equal(fin, np.isfinite(lse)), "alibi step: empty rows"
+        _close(lse[fin], ref_lse[fin], what=f"alibi step lse Q={Q}")
+        if app:
+            _close(k_app, p["k_new"], tol=0.0, what="alibi new keys are stored as given")
+
+
+def pin_alibi_step_is_uniform_alibi(library):
+    """Full lengths, no new tokens, one query token: exactly the uniform
+    ALiBi variant (whose raw window also ends at the query)."""
+    p = alibi_step_problem(84, Q=1, append=False, B=2, Hkv=2, G=3, d=16, ncap=7, rk=4, rv=6, wcap=5)
+    p["num_beacons"][:] = 7
+    p["raw_len"][:] = 5
+    out, lse, _ = run_alibi_step(p, library)
+    ref, ref_lse = oracle.decode_alibi(p["q"][:, 0], p["q_pos"], p["U_K"], p["U_V"], p["C_K"],
+                                       p["C_V"], p["K_raw"], p["V_raw"],
+                                       beacon_pos=p["beacon_pos"], slopes=p["slopes"],
+                                       num_kv_heads=2, scale=p["scale"], library=library)
+    _close(out[:, 0], ref, tol=1e-14, what="alibi step vs uniform alibi")
+    _close(lse[:, 0], ref_lse, tol=1e-14, what="alibi step vs uniform alibi lse")
+
+
+def pin_alibi_step_sequential(library):
+    """A chunk of Q tokens equals Q single-token steps, each appending its
+    token (raw_len + 1) at the next position (q_pos + 1): the positions of
+    the chunk's rows and tokens agree with those of the steps."""
+    Q = 3
+    p = alibi_step_problem(85, Q=Q, B=2, Hkv=1, G=2, d=16, ncap=5, rk=4, rv=4, wcap=9)
+    p["raw_len"][:] = [3, 5]
+    out, lse, _ = run_alibi_step(p, library)
+    K, V = p["K_raw"].copy(), p["V_raw"].copy()
+    for t in range(Q):
+        for b in range(2):
+            w = int(p["raw_len"][b]) + t
+            if t:
+                K[b, :, w - 1] = p["k_new"][b, t - 1]
+                V[b, :, w - 1] = p["v_new"][b, t - 1]
+        o1, l1, _ = run_alibi_step(p, library, q=p["q"][:, t:t + 1], q_pos=p["q_pos"] + t,
+                                   raw_len=p["raw_len"] + t, K_raw=K, V_raw=V,
+                                   k_new=p["k_new"][:, t:t + 1], v_new=p["v_new"][:, t:t + 1])
+        _close(out[:, t], o1[:, 0], what=f"alibi chunk token {t} vs a step")
+        _close(lse[:, t], l1[:, 0], what=f"alibi chunk token {t} vs a step lse")
+
+
+def pin_alibi_step_causal_and_translation(library):
+    """Later tokens do not reach earlier queries; moving every position
+    (queries and beacons) by one offset changes nothing."""
+    p = alibi_step_problem(86, Q=3, B=2, Hkv=2, G=2, d=16, ncap=6, rk=4, rv=4, wcap=6)
+    out, lse, _ = run_alibi_step(p, library)
+    kn = p["k_new"].copy()
+    kn[:, 2] += 5.0
+    out2, _, _ = run_alibi_step(p, library, k_new=kn)
+    assert np.array_equal(out[:, :2], out2[:, :2]), "a later token reached an earlier query"
+    assert not np.allclose(out[:, 2], out2[:, 2]), "the last token's own key is unused"
+    out3, lse3, _ = run_alibi_step(p, library, q_pos=p["q_pos"] + 1000,
+                                   beacon_pos=p["beacon_pos"] + 1000)
+    _close(out3, out, tol=1e-12, what="alibi step translation")
+    _close(lse3, lse, tol=1e-12, what="alibi step translation lse")
+
+
+def pin_alibi_step_token_only(library):
+    """A sequence holding only its new token: output its value, lse the plain
+    scaled score (zero distance to itself), at any position."""
+    for qp in (0, 99, 131071):
+        p = alibi_step_problem(87, Q=1, B=2, Hkv=2, G=2, d=16, ncap=4, rk=4, rv=4, wcap=3)
+        p["num_beacons"][:] = 0
+        p["raw_len"][:] = 0
+        p["q_pos"][:] = qp
+        out, lse, _ = run_alibi_step(p, library)
+        for b in range(2):
+            for hq in range(4):
+                h = hq // 2
+                _close(out[b, 0, hq], p["v_new"][b, 0, h], tol=1e-14, what="token-only out")
+                s = p["scale"] * float(p["q"][b, 0, hq] @ p["k_new"][b, 0, h])
+                _close(lse[b, 0, hq], s, tol=1e-12, what=f"token-only lse at {qp}")
+
+
 ALL_PINS = [
     pin_reconstruct_identity,
     pin_raw_only_rope_gqa,
@@ -756,4 +929,9 @@ ALL_PINS = [
     pin_alibi_translation,
     pin_alibi_two_rows,
     pin_alibi_steep,
+    pin_alibi_step_reference,
+    pin_alibi_step_is_uniform_alibi,
+    pin_alibi_step_sequential,
+    pin_alibi_step_causal_and_translation,
+    pin_alibi_step_token_only,
 ]

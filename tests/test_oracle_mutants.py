@@ -72,6 +72,16 @@ MUTANTS = {
     "fp32_storage_rounded_through_bf16": (
         "if (dtype == ORACLE_F32) return (double)(float)x;",
         "if (dtype == ORACLE_F32) dtype = ORACLE_BF16;"),
+    "alibi_step_raw_rows_ignore_new_tokens": ("const double raw0 = qp0 - (double)w + (app ? 0.0 : 1.0);",
+                                              "const double raw0 = qp0 - (double)w + 1.0;"),
+    "alibi_step_token_one_position_late": ("m_h * (qpos - (qp0 + (double)u))",
+                                           "m_h * (qpos - (qp0 + (double)u + 1.0))"),
+    "alibi_step_query_position_fixed": ("    const double qpos = qp0 + (double)t;\n    const int seen",
+                                        "    const double qpos = qp0;\n    const int seen"),
+    "alibi_step_beacons_unbiased": ("sc[j] = p->scale * acc - m_h * (qpos - (double)bpos[j]);",
+                                    "sc[j] = p->scale * acc;"),
+    "alibi_step_token_value_of_first": ("vr[i] += sc[nb + w + u] * widen(v_new, dt, v0 + i);\n      }\n      for (int i = 0; i < d; ++i) {\n        double acc = 0.0;\n        for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * vl[k];\n        out[q0 + i] = acc + vr[i];\n      }\n      if (lse) lse[row] = mx + log(den);\n    }\n  }\n}\n\n/*\n * ALiBi counterpart",
+                                        "vr[i] += sc[nb + w + u] * widen(v_new, dt, v0 - (size_t)u * H * d + i);\n      }\n      for (int i = 0; i < d; ++i) {\n        double acc = 0.0;\n        for (int k = 0; k < rv; ++k) acc += widen(U_V, dt, uv0 + (size_t)i * rv + k) * vl[k];\n        out[q0 + i] = acc + vr[i];\n      }\n      if (lse) lse[row] = mx + log(den);\n    }\n  }\n}\n\n/*\n * ALiBi counterpart"),
     "empty_sequence_uniform": ("for (int i = 0; i < d; ++i) out[q0 + i] = 0.0;",
                                "for (int i = 0; i < d; ++i) out[q0 + i] = 1.0 / d;"),
 }
