@@ -2,15 +2,16 @@
 """Decode-attention benchmark for libslimkv on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
-                    [--no-cpu-baseline] [--no-compare] [--eager]
+                    [--no-cpu-baseline] [--no-compare] [--graph]
 
 A step is one decode token's attention over every layer of the workload:
 for the default workload (Llama-3.1-8B shape, 128K context, 16x token
 compression, batch 16) that is 32 calls of slimkv_decode_attn, one per
 layer, each with its own latent rank.  All inputs are generated on the GPU
-before timing and stay resident in HBM.  The step's calls are captured once
-as a HIP graph and replayed (checked bit for bit against the eager step;
---eager launches them directly).  The timed region is bracketed by device
+before timing and stay resident in HBM.  The step's calls are launched back
+to back on one stream (checked bit for bit against the same calls captured
+once as a HIP graph and replayed; --graph times the replays instead, and
+the other form is reported beside the headline).  The timed region is bracketed by device
 synchronisation and measured with events on the stream the library
 launches on, one event between consecutive steps, so the line carries the
 mean over the region and the median / p10 / p90 of the single steps.

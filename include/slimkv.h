@@ -44,8 +44,10 @@
  *     then describes the failed check (per calling thread).
  *   - The workspace is scratch of slimkv_workspace_bytes() bytes.  It must
  *     be zero-filled once before its first use; each completed call leaves
- *     it fit for the next (one workspace per stream: two calls that share a
- *     workspace must be ordered on one stream).
+ *     it fit for the next.  Calls that share a workspace must be ordered on
+ *     one stream: calls running at the same time on different streams must
+ *     not share one (their counters would mix).  SLIMKV_FLAG_CHECK_WORKSPACE
+ *     checks the counters before a call.
  *   - bf16 means the upper 16 bits of an IEEE-754 binary32 (round to
  *     nearest even is the caller's business).
  */
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SLIMKV_ABI_VERSION 8
+#define SLIMKV_ABI_VERSION 9
 
 typedef enum slimkv_status {
   SLIMKV_OK = 0,
@@ -100,7 +102,7 @@ typedef struct slimkv_problem {
   double rope_theta;    /* rotary base, finite and > 1                       */
   int32_t num_splits;   /* 0: library picks; > 0: workgroups that share each
                            (b, kv head)'s rows (at most 64)                 */
-  int32_t flags;        /* 0 or SLIMKV_FLAG_DYNAMIC_TILES; other bits 0      */
+  int32_t flags;        /* SLIMKV_FLAG_* bits below; other bits 0            */
 } slimkv_problem;
 
 /*
@@ -114,6 +116,20 @@ typedef struct slimkv_problem {
  * tolerances).
  */
 #define SLIMKV_FLAG_DYNAMIC_TILES 1
+
+/*
+ * Workspace check (debugging).  With SLIMKV_FLAG_CHECK_WORKSPACE a call
+ * first runs a small kernel that checks that the workspace's counters and
+ * flags are zero, as the contract requires (a workspace that was never
+ * zero-filled, one left by a call that did not run to its end, or one used
+ * by calls on two streams at once breaks it).  Nonzero words are cleared,
+ * so the call's results are still right, and bit 0 of the workspace's
+ * status word is set; slimkv_workspace_status reads it.  The check costs
+ * one extra launch per call.  Accepted by every entry point (ragged, paged
+ * and chunk calls take no other flag); the no-alloc entry point clears its
+ * scratch on every call, so there the flag has nothing to check.
+ */
+#define SLIMKV_FLAG_CHECK_WORKSPACE 2
 
 /*
  * Workspace bytes the given op needs for this problem, or 0 if the problem
@@ -424,6 +440,71 @@ slimkv_status slimkv_decode_attn_alibi(const slimkv_problem* problem,
                                        void* stream);
 
 /*
+ * ALiBi forms of the serving calls.  The same steps as
+ * slimkv_decode_attn_ragged, _paged, _chunk and _chunk_paged, for an ALiBi
+ * backbone (page "Can SlimKV compress KV cache jointly across tokens and
+ * features", section "Latent-space attention removes the rebuild step":
+ * ALiBi adds its positional bias after the query-key product, so it
+ * composes with the latent beacon scores).  As in slimkv_decode_attn_alibi
+ * nothing is rotated -- not the queries, not the raw keys, not the new
+ * tokens, which are scored and stored as given -- and every score gets
+ *   -slopes[h_q] * (q_pos_t - k_pos)
+ * after the scaled product.  Positions, for sequence b with w_b live raw
+ * rows (the reading of a window that ends at the newest token):
+ *   query token t       q_pos[b] + t
+ *   beacon j            beacon_first + j * beacon_stride
+ *   new token u         q_pos[b] + u
+ *   live raw row i      q_pos[b] - w_b + i when the call brings new tokens
+ *                       (they follow the raw rows); q_pos[b] - w_b + 1 + i
+ *                       without (the first query's own token is the last
+ *                       raw row, as in slimkv_decode_attn_alibi)
+ * Distances are formed in int32 and converted to fp32 (exact below 2^24).
+ * Every other argument, limit and rule (lengths, clamping, the stores of
+ * new tokens, pages, workspace) is that of the rotary call of the same name
+ * without _alibi; problem->rope_theta is unused but still checked.
+ */
+typedef struct slimkv_alibi {
+  const float* slopes;    /* [H_q] fp32 (device), e.g. the ALiBi paper's slopes */
+  int32_t beacon_first;   /* position of beacon 0, >= 0                        */
+  int32_t beacon_stride;  /* positions between consecutive beacons, >= 0;
+                             the last beacon's position must fit in int32      */
+} slimkv_alibi;
+
+slimkv_status slimkv_decode_attn_ragged_alibi(const slimkv_problem* problem,
+                                              const slimkv_alibi* alibi, const void* q,
+                                              const int32_t* q_pos, const void* U_K,
+                                              const void* U_V, const void* C_K, const void* C_V,
+                                              void* K_raw, void* V_raw,
+                                              const int32_t* num_beacons_b, const int32_t* raw_len,
+                                              const void* k_new, const void* v_new, float* out,
+                                              float* lse, void* workspace, size_t workspace_bytes,
+                                              void* stream);
+slimkv_status slimkv_decode_attn_paged_alibi(const slimkv_problem* problem,
+                                             const slimkv_pages* pages, const slimkv_alibi* alibi,
+                                             const void* q, const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K, const void* C_V,
+                                             void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b, const int32_t* raw_len,
+                                             const void* k_new, const void* v_new, float* out,
+                                             float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+slimkv_status slimkv_decode_attn_chunk_alibi(const slimkv_problem* problem,
+                                             const slimkv_alibi* alibi, int32_t num_tokens,
+                                             const void* q, const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K, const void* C_V,
+                                             void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b, const int32_t* raw_len,
+                                             const void* k_new, const void* v_new, float* out,
+                                             float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream);
+slimkv_status slimkv_decode_attn_chunk_paged_alibi(
+    const slimkv_problem* problem, const slimkv_pages* pages, const slimkv_alibi* alibi,
+    int32_t num_tokens, const void* q, const int32_t* q_pos, const void* U_K, const void* U_V,
+    const void* C_K, const void* C_V, void* K_raw, void* V_raw, const int32_t* num_beacons_b,
+    const int32_t* raw_len, const void* k_new, const void* v_new, float* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * slimkv_reconstruct_attn -- comparison path: the decode step of the
  * reconstruction-based variant timed against SlimKV on the same page
  * (section "Speedups are real, but memory is set by the ratio"): beacon keys
@@ -498,6 +579,15 @@ const char* slimkv_status_string(slimkv_status status);
 
 /* Detail of the last failed call on this thread ("" if none). */
 const char* slimkv_last_error(void);
+
+/*
+ * The status word of a workspace (4 bytes at its start): 0 while every call
+ * made with SLIMKV_FLAG_CHECK_WORKSPACE found the counters and flags at
+ * zero; bit 0 set once one did not.  Zero-filling the workspace clears it.
+ * Debugging aid: copies the word to the host with a synchronous hipMemcpy,
+ * so it waits for the device.
+ */
+slimkv_status slimkv_workspace_status(const void* workspace, uint32_t* status);
 
 /* SLIMKV_ABI_VERSION of the loaded library. */
 int32_t slimkv_abi_version(void);

@@ -19,6 +19,7 @@ LIBRARY = pathlib.Path(__file__).resolve().parent / "libslimkv.so"
 SLIMKV_FP32, SLIMKV_BF16 = 0, 1
 SLIMKV_OP_LATENT, SLIMKV_OP_RECONSTRUCT, SLIMKV_OP_FULL_KV, SLIMKV_OP_LATENT_RAGGED = 0, 1, 2, 3
 SLIMKV_FLAG_DYNAMIC_TILES = 1
+SLIMKV_FLAG_CHECK_WORKSPACE = 2
 STATUS_NAMES = {0: "SLIMKV_OK", 1: "SLIMKV_ERR_NULL", 2: "SLIMKV_ERR_SHAPE",
                 3: "SLIMKV_ERR_UNSUPPORTED", 4: "SLIMKV_ERR_WORKSPACE", 5: "SLIMKV_ERR_ALIGN",
                 6: "SLIMKV_ERR_ALIAS", 7: "SLIMKV_ERR_HIP"}
@@ -27,9 +28,12 @@ EXPORTS = ("slimkv_workspace_bytes", "slimkv_decode_attn", "slimkv_decode_attn_n
            "slimkv_decode_attn_ragged",
            "slimkv_decode_attn_paged", "slimkv_chunk_workspace_bytes", "slimkv_decode_attn_chunk",
            "slimkv_decode_attn_chunk_paged", "slimkv_decode_attn_alibi",
+           "slimkv_decode_attn_ragged_alibi", "slimkv_decode_attn_paged_alibi",
+           "slimkv_decode_attn_chunk_alibi", "slimkv_decode_attn_chunk_paged_alibi",
            "slimkv_reconstruct_attn", "slimkv_reconstruct_rope_attn", "full_kv_attn",
            "slimkv_set_kernel_events",
-           "slimkv_status_string", "slimkv_last_error", "slimkv_abi_version",
+           "slimkv_workspace_status", "slimkv_status_string", "slimkv_last_error",
+           "slimkv_abi_version",
            "slimkv_bench_stream_read", "slimkv_bench_flush")
 
 
@@ -75,6 +79,20 @@ class slimkv_pages(ctypes.Structure):  # noqa: N801  (C name)
 assert ctypes.sizeof(slimkv_pages) == 40
 
 
+class slimkv_alibi(ctypes.Structure):  # noqa: N801  (C name)
+    """Mirror of ``slimkv_alibi`` in include/slimkv.h (16 bytes); slopes is a
+    device pointer."""
+
+    _fields_ = [
+        ("slopes", ctypes.c_void_p),
+        ("beacon_first", ctypes.c_int32),
+        ("beacon_stride", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(slimkv_alibi) == 16
+
+
 class SlimKVError(RuntimeError):
     def __init__(self, status: int, detail: str):
         self.status = status
@@ -110,6 +128,17 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_decode_attn_alibi.argtypes = [prob] + [vp] * 9 + [ctypes.c_int32, ctypes.c_int32] + [
         vp, vp, vp, sz, vp]
     lib.slimkv_decode_attn_alibi.restype = ctypes.c_int
+    al = ctypes.POINTER(slimkv_alibi)
+    pgs = ctypes.POINTER(slimkv_pages)
+    lib.slimkv_decode_attn_ragged_alibi.argtypes = [prob, al] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_ragged_alibi.restype = ctypes.c_int
+    lib.slimkv_decode_attn_paged_alibi.argtypes = [prob, pgs, al] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_paged_alibi.restype = ctypes.c_int
+    lib.slimkv_decode_attn_chunk_alibi.argtypes = [prob, al, ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
+    lib.slimkv_decode_attn_chunk_alibi.restype = ctypes.c_int
+    lib.slimkv_decode_attn_chunk_paged_alibi.argtypes = [prob, pgs, al, ctypes.c_int32] + [vp] * 14 + [
+        vp, sz, vp]
+    lib.slimkv_decode_attn_chunk_paged_alibi.restype = ctypes.c_int
     lib.slimkv_chunk_workspace_bytes.argtypes = [prob, ctypes.c_int32]
     lib.slimkv_chunk_workspace_bytes.restype = sz
     lib.slimkv_decode_attn_chunk.argtypes = [prob, ctypes.c_int32] + [vp] * 14 + [vp, sz, vp]
@@ -129,6 +158,8 @@ def load_library(path: pathlib.Path | None = None) -> ctypes.CDLL:
     lib.slimkv_last_error.restype = ctypes.c_char_p
     lib.slimkv_set_kernel_events.argtypes = [vp, vp]
     lib.slimkv_set_kernel_events.restype = ctypes.c_int
+    lib.slimkv_workspace_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+    lib.slimkv_workspace_status.restype = ctypes.c_int
     lib.slimkv_abi_version.argtypes = []
     lib.slimkv_abi_version.restype = ctypes.c_int32
     lib.slimkv_bench_stream_read.argtypes = [vp, sz, ctypes.c_int32, ctypes.c_int32, vp, vp]
@@ -242,6 +273,63 @@ def slimkv_decode_attn_alibi(problem, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw
         _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def make_alibi(slopes, beacon_first: int, beacon_stride: int) -> slimkv_alibi:
+    """slimkv_alibi from a float32 [H_q] device tensor of slopes."""
+    if slopes.dtype != torch.float32:
+        raise TypeError("slopes must be float32")
+    return slimkv_alibi(_ptr(slopes), int(beacon_first), int(beacon_stride))
+
+
+def slimkv_decode_attn_ragged_alibi(problem, alibi, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                                    num_beacons, raw_len, k_new, v_new, out, lse, workspace,
+                                    stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_ragged_alibi(
+        ctypes.byref(problem), ctypes.byref(alibi) if alibi is not None else None, _ptr(q),
+        _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw),
+        _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_decode_attn_paged_alibi(problem, pages, alibi, q, q_pos, U_K, U_V, C_K, C_V, K_raw,
+                                   V_raw, num_beacons, raw_len, k_new, v_new, out, lse, workspace,
+                                   stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_paged_alibi(
+        ctypes.byref(problem), ctypes.byref(pages) if pages is not None else None,
+        ctypes.byref(alibi) if alibi is not None else None, _ptr(q), _ptr(q_pos), _ptr(U_K),
+        _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons),
+        _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def slimkv_decode_attn_chunk_alibi(problem, alibi, num_tokens, q, q_pos, U_K, U_V, C_K, C_V,
+                                   K_raw, V_raw, num_beacons, raw_len, k_new, v_new, out, lse,
+                                   workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_chunk_alibi(
+        ctypes.byref(problem), ctypes.byref(alibi) if alibi is not None else None,
+        int(num_tokens), _ptr(q), _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V),
+        _ptr(K_raw), _ptr(V_raw), _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new),
+        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def slimkv_decode_attn_chunk_paged_alibi(problem, pages, alibi, num_tokens, q, q_pos, U_K, U_V,
+                                         C_K, C_V, K_raw, V_raw, num_beacons, raw_len, k_new,
+                                         v_new, out, lse, workspace, stream=None) -> None:
+    lib = load_library()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib, lib.slimkv_decode_attn_chunk_paged_alibi(
+        ctypes.byref(problem), ctypes.byref(pages) if pages is not None else None,
+        ctypes.byref(alibi) if alibi is not None else None, int(num_tokens), _ptr(q),
+        _ptr(q_pos), _ptr(U_K), _ptr(U_V), _ptr(C_K), _ptr(C_V), _ptr(K_raw), _ptr(V_raw),
+        _ptr(num_beacons), _ptr(raw_len), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def slimkv_chunk_workspace_bytes(problem: slimkv_problem, num_tokens: int) -> int:
     lib = load_library()
     n = lib.slimkv_chunk_workspace_bytes(ctypes.byref(problem), int(num_tokens))
@@ -323,6 +411,16 @@ def slimkv_status_string(status: int) -> str:
 
 def slimkv_last_error() -> str:
     return load_library().slimkv_last_error().decode()
+
+
+def slimkv_workspace_status(workspace) -> int:
+    """The workspace's status word (bit 0: a call made with
+    SLIMKV_FLAG_CHECK_WORKSPACE found its counters or flags not at zero).
+    Synchronous: waits for the device."""
+    lib = load_library()
+    word = ctypes.c_uint32(0)
+    _check(lib, lib.slimkv_workspace_status(_ptr(workspace), ctypes.byref(word)))
+    return int(word.value)
 
 
 def slimkv_abi_version() -> int:

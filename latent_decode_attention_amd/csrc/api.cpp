@@ -60,10 +60,10 @@ slimkv_status check_problem(const slimkv_problem* p, slimkv_op op) {
       op != SLIMKV_OP_LATENT_RAGGED)
     return fail(SLIMKV_ERR_UNSUPPORTED, "unknown op %d", (int)op);
   const bool ragged = op == SLIMKV_OP_LATENT_RAGGED;
-  if ((p->flags & ~SLIMKV_FLAG_DYNAMIC_TILES) != 0)
+  if ((p->flags & ~(SLIMKV_FLAG_DYNAMIC_TILES | SLIMKV_FLAG_CHECK_WORKSPACE)) != 0)
     return fail(SLIMKV_ERR_SHAPE, "unknown flag bits 0x%x", (unsigned)p->flags);
-  if (ragged && p->flags != 0)
-    return fail(SLIMKV_ERR_UNSUPPORTED, "ragged calls take no flags (fixed schedule only)");
+  if (ragged && (p->flags & SLIMKV_FLAG_DYNAMIC_TILES) != 0)
+    return fail(SLIMKV_ERR_UNSUPPORTED, "ragged calls deal their tiles in a fixed order only");
   if (ragged && p->batch > kMaxRaggedBatch)
     return fail(SLIMKV_ERR_UNSUPPORTED, "ragged batch %d exceeds %d", p->batch, kMaxRaggedBatch);
   if (p->dtype != SLIMKV_FP32 && p->dtype != SLIMKV_BF16)
@@ -156,8 +156,8 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
   // zeroed), then one partial slot per workgroup for up to kMaxChunks
   // workgroups per unit (ragged: one per piece, fewer than grid + units)
   const int64_t G = a.group, slots = ragged ? kMaxChunks + 1 : kMaxChunks;
-  pl.off_counters = 0;
-  size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+  pl.off_counters = kWsHeader;
+  size_t off = round_up(kWsHeader + pl.units * kCounterStride * sizeof(uint32_t), kAlign);
   pl.off_flags = off;
   off = round_up(off + (size_t)(pl.units * slots) * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
@@ -192,8 +192,8 @@ slimkv_status make_chunk_plan(const slimkv_problem* p, int32_t num_tokens, Plan&
   // each unit's tokens
   const int64_t M = (int64_t)G * num_tokens, slots = 2 * pl.units + kChunkMaxSlots;
   pl.attn.num_tokens = num_tokens;
-  pl.off_counters = 0;
-  size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+  pl.off_counters = kWsHeader;
+  size_t off = round_up(kWsHeader + pl.units * kCounterStride * sizeof(uint32_t), kAlign);
   pl.off_flags = off;
   off = round_up(off + (size_t)slots * sizeof(uint32_t), kAlign);
   pl.off_ml = off;
@@ -246,6 +246,18 @@ struct Alibi {
   int32_t first = 0, stride = 0;  // beacon j at first + j * stride
 };
 
+// Checks of an ALiBi call's parameters (slopes set): positions of the
+// beacons fit in int32, the slopes are 4-byte aligned.
+slimkv_status check_alibi(const slimkv_problem* p, const Alibi& alibi) {
+  if (!alibi.slopes) return SLIMKV_OK;
+  const int64_t last = (int64_t)alibi.first + (int64_t)std::max(p->num_beacons - 1, 0) * alibi.stride;
+  if (alibi.stride < 0 || alibi.first < 0 || last > INT32_MAX)
+    return fail(SLIMKV_ERR_SHAPE, "beacon positions first %d + j * stride %d must be >= 0 and "
+                "fit in int32", alibi.first, alibi.stride);
+  if ((uintptr_t)alibi.slopes % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "slopes is not 4-byte aligned");
+  return SLIMKV_OK;
+}
+
 // noalloc: the workspace is the library's device scratch (ws must be NULL;
 // slimkv_decode_attn_noalloc), laid out for the chunk count this call uses.
 slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const int32_t* q_pos,
@@ -256,13 +268,8 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   Plan pl;
   slimkv_status st = make_plan(p, op, pl);
   if (st != SLIMKV_OK) return st;
-  if (alibi.slopes) {
-    const int64_t last = (int64_t)alibi.first + (int64_t)std::max(p->num_beacons - 1, 0) * alibi.stride;
-    if (alibi.stride < 0 || alibi.first < 0 || last > INT32_MAX)
-      return fail(SLIMKV_ERR_SHAPE, "beacon positions first %d + j * stride %d must be >= 0 and "
-                  "fit in int32", alibi.first, alibi.stride);
-    if ((uintptr_t)alibi.slopes % 4 != 0) return fail(SLIMKV_ERR_ALIGN, "slopes is not 4-byte aligned");
-  }
+  st = check_alibi(p, alibi);
+  if (st != SLIMKV_OK) return st;
   const size_t e = (size_t)pl.elem;
   const size_t B = p->batch, Hq = p->num_q_heads, Hkv = p->num_kv_heads, d = kHeadDim;
   const size_t nb = p->num_beacons, w = p->raw_window;
@@ -332,8 +339,8 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
       a.chunks = choose_chunks(pl.units, a.unit_bytes, slots, 64 << 10);
     }
     const size_t G = a.group, k = a.chunks;
-    pl.off_counters = 0;
-    size_t off = round_up(pl.units * kCounterStride * sizeof(uint32_t), kAlign);
+    pl.off_counters = kWsHeader;
+    size_t off = round_up(kWsHeader + pl.units * kCounterStride * sizeof(uint32_t), kAlign);
     pl.off_flags = off;
     off = round_up(off + pl.units * k * sizeof(uint32_t), kAlign);
     pl.off_ml = off;
@@ -377,7 +384,9 @@ slimkv_status run(const slimkv_problem* p, slimkv_op op, const void* q, const in
   }
 
   hipError_t err = hipSuccess;
-  if (op == SLIMKV_OP_RECONSTRUCT && beacons) {
+  if ((p->flags & SLIMKV_FLAG_CHECK_WORKSPACE) && !noalloc)
+    err = launch_workspace_check(reinterpret_cast<uint32_t*>(wsb), pl.off_counters, pl.off_ml, s);
+  if (err == hipSuccess && op == SLIMKV_OP_RECONSTRUCT && beacons) {
     RebuildArgs rb{};
     rb.batch = p->batch;
     rb.num_kv_heads = p->num_kv_heads;
@@ -458,10 +467,12 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
                          const void* C_V, void* K_raw, void* V_raw, const int32_t* seq_beacons,
                          const int32_t* seq_raw, const void* k_new, const void* v_new, float* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream, bool paged,
-                         int32_t chunk = 0) {
+                         int32_t chunk = 0, const Alibi& alibi = Alibi()) {
   Plan pl;
   slimkv_status st = chunk > 0 ? make_chunk_plan(p, chunk, pl)
                                : make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
+  if (st != SLIMKV_OK) return st;
+  st = check_alibi(p, alibi);
   if (st != SLIMKV_OK) return st;
   const size_t e = (size_t)pl.elem;
   const size_t T = chunk > 0 ? (size_t)chunk : 1;  // query tokens per sequence
@@ -529,6 +540,11 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   for (const Range* x : {&kr, &vr})
     if (x->p && (uintptr_t)x->p % 16 != 0)
       return fail(SLIMKV_ERR_ALIGN, "%s is not 16-byte aligned", x->name);
+  if (alibi.slopes) {
+    const Range sl{alibi.slopes, Hq * sizeof(float), "slopes"};
+    for (const Range& o : outs)
+      if (overlap(o, sl)) return fail(SLIMKV_ERR_ALIAS, "%s overlaps slopes", o.name);
+  }
   st = check_pointers(in, 7, req, n_req, outs, 0, 16);  // presence and 16-byte alignment
   if (st != SLIMKV_OK) return st;
   st = check_pointers(all_in, n_in, req, 0, outs, 5, 1);  // overlaps
@@ -563,6 +579,9 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   }
   a.seq_beacons = seq_beacons;
   a.seq_raw = seq_raw;
+  a.alibi_slopes = alibi.slopes;
+  a.beacon_first = alibi.first;
+  a.beacon_stride = alibi.stride;
   a.k_new = append ? k_new : nullptr;
   a.v_new = append ? v_new : nullptr;
   a.k_store = K_raw;
@@ -581,6 +600,11 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
     a.page_shift = shift;
   }
   a.deterministic = 1;
+  if (p->flags & SLIMKV_FLAG_CHECK_WORKSPACE) {
+    const hipError_t e = launch_workspace_check(reinterpret_cast<uint32_t*>(wsb), pl.off_counters,
+                                                pl.off_ml, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  }
   const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
   const hipError_t err = chunk > 0
@@ -685,6 +709,73 @@ slimkv_status slimkv_decode_attn_alibi(const slimkv_problem* problem, const void
                      lse, workspace, workspace_bytes, stream, nullptr, al);
 }
 
+static slimkv::Alibi alibi_of(const slimkv_alibi* al) {
+  slimkv::Alibi r;
+  r.slopes = al->slopes;
+  r.first = al->beacon_first;
+  r.stride = al->beacon_stride;
+  return r;
+}
+
+slimkv_status slimkv_decode_attn_ragged_alibi(const slimkv_problem* problem,
+                                              const slimkv_alibi* alibi, const void* q,
+                                              const int32_t* q_pos, const void* U_K,
+                                              const void* U_V, const void* C_K, const void* C_V,
+                                              void* K_raw, void* V_raw,
+                                              const int32_t* num_beacons_b, const int32_t* raw_len,
+                                              const void* k_new, const void* v_new, float* out,
+                                              float* lse, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  if (!alibi || !alibi->slopes) return slimkv::fail(SLIMKV_ERR_NULL, "alibi or its slopes is NULL");
+  return slimkv::run_ragged(problem, nullptr, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, false, 0, alibi_of(alibi));
+}
+
+slimkv_status slimkv_decode_attn_paged_alibi(const slimkv_problem* problem,
+                                             const slimkv_pages* pages, const slimkv_alibi* alibi,
+                                             const void* q, const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K, const void* C_V,
+                                             void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b, const int32_t* raw_len,
+                                             const void* k_new, const void* v_new, float* out,
+                                             float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (!alibi || !alibi->slopes) return slimkv::fail(SLIMKV_ERR_NULL, "alibi or its slopes is NULL");
+  return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, true, 0, alibi_of(alibi));
+}
+
+slimkv_status slimkv_decode_attn_chunk_alibi(const slimkv_problem* problem,
+                                             const slimkv_alibi* alibi, int32_t num_tokens,
+                                             const void* q, const int32_t* q_pos, const void* U_K,
+                                             const void* U_V, const void* C_K, const void* C_V,
+                                             void* K_raw, void* V_raw,
+                                             const int32_t* num_beacons_b, const int32_t* raw_len,
+                                             const void* k_new, const void* v_new, float* out,
+                                             float* lse, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (!alibi || !alibi->slopes) return slimkv::fail(SLIMKV_ERR_NULL, "alibi or its slopes is NULL");
+  if (num_tokens < 1) return slimkv::fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
+  return slimkv::run_ragged(problem, nullptr, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, false, num_tokens, alibi_of(alibi));
+}
+
+slimkv_status slimkv_decode_attn_chunk_paged_alibi(
+    const slimkv_problem* problem, const slimkv_pages* pages, const slimkv_alibi* alibi,
+    int32_t num_tokens, const void* q, const int32_t* q_pos, const void* U_K, const void* U_V,
+    const void* C_K, const void* C_V, void* K_raw, void* V_raw, const int32_t* num_beacons_b,
+    const int32_t* raw_len, const void* k_new, const void* v_new, float* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!alibi || !alibi->slopes) return slimkv::fail(SLIMKV_ERR_NULL, "alibi or its slopes is NULL");
+  if (num_tokens < 1) return slimkv::fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
+  return slimkv::run_ragged(problem, pages, q, q_pos, U_K, U_V, C_K, C_V, K_raw, V_raw,
+                            num_beacons_b, raw_len, k_new, v_new, out, lse, workspace,
+                            workspace_bytes, stream, true, num_tokens, alibi_of(alibi));
+}
+
 size_t slimkv_chunk_workspace_bytes(const slimkv_problem* problem, int32_t num_tokens) {
   slimkv::Plan pl;
   if (slimkv::make_chunk_plan(problem, num_tokens, pl) != SLIMKV_OK) return 0;
@@ -744,5 +835,15 @@ slimkv_status slimkv_set_kernel_events(void* start, void* stop) {
 }
 
 int32_t slimkv_abi_version(void) { return SLIMKV_ABI_VERSION; }
+
+slimkv_status slimkv_workspace_status(const void* workspace, uint32_t* status) {
+  if (!workspace || !status) return slimkv::fail(SLIMKV_ERR_NULL, "workspace or status is NULL");
+  if ((uintptr_t)workspace % 16 != 0)
+    return slimkv::fail(SLIMKV_ERR_ALIGN, "workspace is not 16-byte aligned");
+  const hipError_t e = hipMemcpy(status, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess)
+    return slimkv::fail(SLIMKV_ERR_HIP, "reading the status word failed: %s", hipGetErrorString(e));
+  return SLIMKV_OK;
+}
 
 }  // extern "C"

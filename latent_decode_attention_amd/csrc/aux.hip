@@ -33,8 +33,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // transposed latent rows the B operand (rank on K, beacon row on N):
 // lane (n, kg) then ends with columns 16t + 4kg .. +3 of row n for each
 // 16-column tile t -- the two halves of every rotation pair in one lane,
-// and 8 contiguous output bytes per store.  The next sequence's latent rows
-// are requested before the current ones are multiplied.
+// and 8 contiguous output bytes per store.  The latent rows of the next
+// four sequences are in flight while one is multiplied.
 
 // Sine and cosine of pos * theta^(-2i/d) for pair i < 64 (see above).
 __device__ __forceinline__ void rebuild_sincos(const RebuildArgs& a, int pos, int i, float& s,
@@ -57,6 +57,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 
 constexpr int kRebuildRows = 64;  // beacon rows per workgroup (16 per wave)
 constexpr int kUPad = 8;           // staged basis rows padded by 16 bytes (LDS banks)
+constexpr int kRebuildAhead = 4;   // sequences whose latent rows are in flight per wave
 
 template <int NCHK>
 __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a) {
@@ -88,8 +89,11 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
       cb[c] = __builtin_bit_cast(bf16x8_t, v);
     }
   };
-  bf16x8_t cur[NCHK], nxt[NCHK];
-  load_rows(0, cur);
+  // the latent rows of the next kRebuildAhead sequences are in flight while
+  // one is multiplied: a ring of buffers, indexed at compile time
+  bf16x8_t ring[kRebuildAhead][NCHK];
+#pragma unroll
+  for (int i = 0; i < kRebuildAhead; ++i) load_rows(min(i, a.batch - 1), ring[i]);
   // the head's basis, staged once: row i (output column), rank k
   {
     const uint16_t* U = static_cast<const uint16_t*>(a.U[job]) + (size_t)h * kHeadDim * r;
@@ -111,46 +115,55 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
       for (int e = 0; e < 4; ++e) rebuild_sincos(a, p, 16 * t + 4 * kg + e, sn[t][e], cs[t][e]);
   }
   __syncthreads();
-  for (int b = 0; b < a.batch; ++b) {
-    if (b + 1 < a.batch) load_rows(b + 1, nxt);
-    uint16_t* Dr = D + (((size_t)b * hkv + h) * nb + row) * kHeadDim + 4 * kg;
-    // column tiles t and t + 4 together: they hold the two halves of this
-    // lane's rotation pairs
+  for (int b0 = 0; b0 < a.batch; b0 += kRebuildAhead) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < kRebuildAhead; ++i) {
+      const int b = b0 + i;
+      if (b < a.batch) {  // workgroup-uniform
+        bf16x8_t cur[NCHK];
 #pragma unroll
-      for (int c = 0; c < NCHK; ++c) {
-        if (c < nchk) {
-          const int k0 = 32 * c + 8 * kg;
-          u32x4_t a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-          if (k0 < r) {
-            a0 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + n) * us + k0]);
-            a1 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + 64 + n) * us + k0]);
+        for (int c = 0; c < NCHK; ++c) cur[c] = ring[i][c];
+        if (b + kRebuildAhead < a.batch) load_rows(b + kRebuildAhead, ring[i]);
+        uint16_t* Dr = D + (((size_t)b * hkv + h) * nb + row) * kHeadDim + 4 * kg;
+        // column tiles t and t + 4 together: they hold the two halves of this
+        // lane's rotation pairs
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f}, d1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int c = 0; c < NCHK; ++c) {
+            if (c < nchk) {
+              const int k0 = 32 * c + 8 * kg;
+              u32x4_t a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+              if (k0 < r) {
+                a0 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + n) * us + k0]);
+                a1 = *reinterpret_cast<const u32x4_t*>(&ul[(16 * t + 64 + n) * us + k0]);
+              }
+              d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), cur[c], d0, 0,
+                                                           0, 0);
+              d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), cur[c], d1, 0,
+                                                           0, 0);
+            }
           }
-          d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), cur[c], d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), cur[c], d1, 0, 0, 0);
-        }
-      }
-      if (rot) {
+          if (rot) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = d0[e], y = d1[e];
-          d0[e] = x * cs[t][e] - y * sn[t][e];
-          d1[e] = y * cs[t][e] + x * sn[t][e];
+            for (int e = 0; e < 4; ++e) {
+              const float x = d0[e], y = d1[e];
+              d0[e] = x * cs[t][e] - y * sn[t][e];
+              d1[e] = y * cs[t][e] + x * sn[t][e];
+            }
+          }
+          if (row_ok) {
+            *reinterpret_cast<uint2*>(Dr + 16 * t) =
+                make_uint2(f32_to_bf16(d0[0]) | (f32_to_bf16(d0[1]) << 16),
+                           f32_to_bf16(d0[2]) | (f32_to_bf16(d0[3]) << 16));
+            *reinterpret_cast<uint2*>(Dr + 16 * t + 64) =
+                make_uint2(f32_to_bf16(d1[0]) | (f32_to_bf16(d1[1]) << 16),
+                           f32_to_bf16(d1[2]) | (f32_to_bf16(d1[3]) << 16));
+          }
         }
-      }
-      if (row_ok) {
-        *reinterpret_cast<uint2*>(Dr + 16 * t) =
-            make_uint2(f32_to_bf16(d0[0]) | (f32_to_bf16(d0[1]) << 16),
-                       f32_to_bf16(d0[2]) | (f32_to_bf16(d0[3]) << 16));
-        *reinterpret_cast<uint2*>(Dr + 16 * t + 64) =
-            make_uint2(f32_to_bf16(d1[0]) | (f32_to_bf16(d1[1]) << 16),
-                       f32_to_bf16(d1[2]) | (f32_to_bf16(d1[3]) << 16));
       }
     }
-#pragma unroll
-    for (int c = 0; c < NCHK; ++c) cur[c] = nxt[c];
   }
 }
 
@@ -179,6 +192,28 @@ __global__ __launch_bounds__(kThreads) void rebuild_f32_kernel(RebuildArgs a, in
     acc = col < kHeadDim / 2 ? acc * cs - pacc * sn : acc * cs + pacc * sn;
   }
   static_cast<float*>(a.dst[job])[idx] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// The workspace check (SLIMKV_FLAG_CHECK_WORKSPACE).
+__global__ __launch_bounds__(256) void workspace_check_kernel(uint32_t* ws, uint32_t begin,
+                                                              uint32_t end) {
+  bool found = false;
+  for (uint32_t i = begin + blockIdx.x * 256u + threadIdx.x; i < end; i += gridDim.x * 256u) {
+    if (ws[i] != 0u) {
+      found = true;
+      ws[i] = 0u;
+    }
+  }
+  if (__builtin_amdgcn_ballot_w64(found) != 0 && (threadIdx.x & 63) == 0)
+    __hip_atomic_fetch_or(&ws[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_workspace_check(uint32_t* ws, size_t begin, size_t end, hipStream_t s) {
+  const uint32_t b = (uint32_t)(begin / 4), e = (uint32_t)(end / 4);
+  const unsigned blocks = std::max(1u, std::min((e - b + 255u) / 256u, 256u));
+  hipLaunchKernelGGL(workspace_check_kernel, dim3(blocks), dim3(256), 0, s, ws, b, e);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

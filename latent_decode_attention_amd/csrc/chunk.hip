@@ -5,14 +5,14 @@
 
 namespace slimkv {
 
-template <bool PG>
+template <bool PG, bool AL>
 static const void* chunk_kernel_for(int nch) {
   switch (nch) {
-    case 0: return reinterpret_cast<const void*>(&chunk_kernel<0, PG>);
-    case 1: return reinterpret_cast<const void*>(&chunk_kernel<1, PG>);
-    case 2: return reinterpret_cast<const void*>(&chunk_kernel<2, PG>);
-    case 3: return reinterpret_cast<const void*>(&chunk_kernel<3, PG>);
-    default: return reinterpret_cast<const void*>(&chunk_kernel<4, PG>);
+    case 0: return reinterpret_cast<const void*>(&chunk_kernel<0, PG, AL>);
+    case 1: return reinterpret_cast<const void*>(&chunk_kernel<1, PG, AL>);
+    case 2: return reinterpret_cast<const void*>(&chunk_kernel<2, PG, AL>);
+    case 3: return reinterpret_cast<const void*>(&chunk_kernel<3, PG, AL>);
+    default: return reinterpret_cast<const void*>(&chunk_kernel<4, PG, AL>);
   }
 }
 
@@ -25,7 +25,9 @@ hipError_t launch_chunk(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev
                       ? std::max((a.seg[0].rk + 31) / 32, (a.seg[0].rv + 31) / 32)
                       : 0;
   const bool paged = a.page_table[0] != nullptr || a.page_table[1] != nullptr;
-  const void* kfn = paged ? chunk_kernel_for<true>(nch) : chunk_kernel_for<false>(nch);
+  const bool alibi = a.alibi_slopes != nullptr;
+  const void* kfn = paged ? (alibi ? chunk_kernel_for<true, true>(nch) : chunk_kernel_for<true, false>(nch))
+                          : (alibi ? chunk_kernel_for<false, true>(nch) : chunk_kernel_for<false, false>(nch));
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   int64_t P = a.chunks;
   if (P <= 0) {

@@ -91,7 +91,7 @@ __device__ __forceinline__ void split_bf16x4(const f32x4_t& x, s16x4_t& hi, s16x
 // issue() requests the query and (latent beacons) both halves of U_K;
 // finish() rotates the rows into sh.qrot (rows past M zero) and projects
 // them, sh.qlat = qrot U_K, staging U_K in LDS half by half.
-template <int NCH>
+template <int NCH, bool ROTATE = true>
 struct ChunkPrologue {
   static constexpr bool kLat = NCH > 0;
   static constexpr int kHalf = kHeadDim / 2;
@@ -136,11 +136,16 @@ struct ChunkPrologue {
       const int m = p / kHalf, i = p % kHalf;
       float r1 = 0.0f, r2 = 0.0f;
       if (m < M) {
-        float sn, cs;
-        rope_sincos(a, pos0 + m / G, i, sn, cs);
         const float v1 = bits_to_float<true>(x1[j]), v2 = bits_to_float<true>(x2[j]);
-        r1 = (v1 * cs - v2 * sn) * sc;
-        r2 = (v2 * cs + v1 * sn) * sc;
+        if constexpr (ROTATE) {
+          float sn, cs;
+          rope_sincos(a, pos0 + m / G, i, sn, cs);
+          r1 = (v1 * cs - v2 * sn) * sc;
+          r2 = (v2 * cs + v1 * sn) * sc;
+        } else {  // an ALiBi backbone rotates nothing
+          r1 = v1 * sc;
+          r2 = v2 * sc;
+        }
       }
       sh.u.s.qrot[m][i] = r1;
       sh.u.s.qrot[m][i + kHalf] = r2;
@@ -241,14 +246,17 @@ struct ChunkState {
 // key features; width: value columns.  RAW: a raw tile, summed into accr
 // (a rescale then applies to accb too); else a beacon tile, summed into
 // accb (accr is not started: a wave's beacon tiles come first).
-template <int S, bool RAW, int NB, int SA, int SB, bool PG>
+// ALIBI: score (row, query row m) gets s2 * (row * step - ofs), with s2 the
+// query head's slope in log2 units and row * step - ofs = k_pos - (q_pos +
+// t_m) for this lane's query row m (zero s2 on padding rows).
+template <int S, bool RAW, int NB, int SA, int SB, bool PG, bool ALIBI = false>
 __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t0, int nchk, int width,
                                            const bf16x8_t (&qh)[S], const bf16x8_t (&ql)[S],
                                            ChunkState<NB>& st, uint16_t* vt,
                                            const SegView<SA, true, PG>& bv,
                                            const SegView<SB, true, PG>& rw, int jn, int nbt,
                                            int total, const TailRows& tail, u32x4_t* kbuf,
-                                           u32x4_t* vbuf) {
+                                           u32x4_t* vbuf, float s2 = 0.0f, int ofs = 0, int step = 0) {
   constexpr int SUB = SegView<S, true, PG>::kSub;
   constexpr int TR = SegView<S, true, PG>::kRows;
   constexpr int TRA = SegView<SA, true, PG>::kRows, TRB = SegView<SB, true, PG>::kRows;
@@ -268,6 +276,10 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[c], d, 0, 0, 0);
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[c], d, 0, 0, 0);
       }
+    }
+    if constexpr (ALIBI) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d[e] = fmaf(s2, (float)((t0 + 16 * s + 4 * kg + e) * step - ofs), d[e]);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -358,8 +370,10 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
 // capacity: no workgroup reads those rows in this call); PG: in the page
 // the raw table gives for the row (ptab from rtab0; none if that id is out
 // of range).  Thread (m, c8) owns 8 columns of row m (16 threads, one DPP
-// row, per query row).
-template <bool PG>
+// row, per query row).  ALIBI: nothing is rotated (the keys are scored and
+// stored as given) and query row m (token t) scoring token tk adds its
+// head's slope times the distance tk - t (in log2 units).
+template <bool PG, bool ALIBI = false>
 __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShared& sh, int u, int b,
                                                     int h, int wlive, int M, int G,
                                                     const int32_t* ptab, int rtab0) {
@@ -377,10 +391,16 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
     const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
     const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
     const uint16_t v1 = vs[i], v2 = vs[i + kHalf];
-    double s64, c64;
-    sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
-    const uint32_t b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
-    const uint32_t b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
+    uint32_t b1, b2;
+    if constexpr (ALIBI) {
+      b1 = static_cast<const uint16_t*>(a.k_new)[kb + i];
+      b2 = static_cast<const uint16_t*>(a.k_new)[kb + i + kHalf];
+    } else {
+      double s64, c64;
+      sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
+      b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
+      b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
+    }
     kn[t][i] = bits_to_float<true>(b1);
     kn[t][i + kHalf] = bits_to_float<true>(b2);
     vn[t][i] = bits_to_float<true>(v1);
@@ -408,6 +428,7 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
   lds_barrier();
   const int mm = tid / 16, c8 = tid & 15;
   const int m = min(mm, M - 1), t = m / G;
+  const float s2 = ALIBI ? a.alibi_slopes[h * G + m % G] * 1.4426950408889634f : 0.0f;
   float Mx = -INFINITY, L = 0.0f;
   f32x4_t acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
   for (int tk = 0; tk <= t; ++tk) {  // the 16 threads of a row share t
@@ -415,6 +436,7 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
 #pragma unroll
     for (int e = 0; e < 8; ++e) dot += sh.u.s.qrot[m][8 * c8 + e] * kn[tk][8 * c8 + e];
     dot = row16_sum(dot);
+    if constexpr (ALIBI) dot = fmaf(s2, (float)(tk - t), dot);
     const float mn = fmaxf(Mx, dot);
     const float a1 = __builtin_amdgcn_exp2f(Mx - mn), a2 = __builtin_amdgcn_exp2f(dot - mn);
     L = L * a1 + a2;
@@ -516,7 +538,7 @@ __device__ __forceinline__ void chunk_finish(const AttnArgs& a, int u, int b, in
 // unit (b, h), as attend_unit, with the unit's live rows nbr, wr.  PG: the
 // rows are paged; ptab (LDS) holds the unit's beacon page ids, then its raw
 // page ids (those of its live rows and of the rows its tokens are stored in).
-template <int NCH, bool PG>
+template <int NCH, bool PG, bool ALIBI = false>
 __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, int unit, int b, int h,
                                            int c, int k, int nbr, int wr, int slot0,
                                            const int32_t* ptab) {
@@ -563,7 +585,7 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
     tail.klane = tail.vlane = 64;
   }
 
-  ChunkPrologue<NCH> pro;
+  ChunkPrologue<NCH, !ALIBI> pro;
   pro.issue(a, b, h, M, G);
   u32x4_t kbuf[Traits<true>::kMaxLoads], vbuf[Traits<true>::kMaxLoads];
   int j = wu;
@@ -575,7 +597,19 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   }
   pro.finish(a, sh, wave, M, G);
   if (c == 0 && a.k_new)  // workgroup-uniform
-    chunk_token_partial<PG>(a, sh, unit, b, h, wr, M, G, ptab, nbp);
+    chunk_token_partial<PG, ALIBI>(a, sh, unit, b, h, wr, M, G, ptab, nbp);
+  // ALiBi: this lane's query row m = n (token n / G, head n % G): its slope
+  // in log2 units (zero on padding rows) and each segment's offset, so that
+  // row * step - ofs = k_pos - q_pos - t (beacon j at first + j stride; raw
+  // row i at q_pos - wr + i with new tokens, q_pos - wr + 1 + i without)
+  float s2 = 0.0f;
+  int bofs = 0, rofs = 0;
+  if constexpr (ALIBI) {
+    const int tm = n / G;
+    s2 = n < M ? a.alibi_slopes[h * G + n % G] * 1.4426950408889634f : 0.0f;
+    bofs = a.q_pos[b] - a.beacon_first + tm;
+    rofs = (a.k_new ? wr : wr - 1) + tm;
+  }
 
   constexpr int NB = BLAT ? 2 * BN : 1;  // latent sum blocks: r_V <= 32 NCH
   ChunkState<NB> st;
@@ -591,8 +625,9 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
     chunk_query<BN>(sh.u.s.qlat, rk, qlh, qll);
     const int nchk = (rk + 31) / 32;
     for (; j < nbt; j += nwaves)
-      chunk_tile<BN, false>(bv, j * TRB, nchk, rv, qlh, qll, st, vt, bv, rw, j + nwaves, nbt, total,
-                            tail, kbuf, vbuf);
+      chunk_tile<BN, false, NB, BN, 4, PG, ALIBI>(bv, j * TRB, nchk, rv, qlh, qll, st, vt, bv, rw,
+                                                  j + nwaves, nbt, total, tail, kbuf, vbuf, s2,
+                                                  bofs, a.beacon_stride);
   }
 #pragma unroll
   for (int cb = 0; cb < kHeadDim / 16; ++cb) st.accr[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -600,8 +635,9 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
     bf16x8_t qrh[4], qrl[4];
     chunk_query<4>(sh.u.s.qrot, kHeadDim, qrh, qrl);
     for (; j < total; j += nwaves)
-      chunk_tile<4, true>(rw, (j - nbt) * TRR, 4, kHeadDim, qrh, qrl, st, vt, bv, rw, j + nwaves, nbt,
-                          total, tail, kbuf, vbuf);
+      chunk_tile<4, true, NB, BN, 4, PG, ALIBI>(rw, (j - nbt) * TRR, 4, kHeadDim, qrh, qrl, st, vt,
+                                                bv, rw, j + nwaves, nbt, total, tail, kbuf, vbuf,
+                                                s2, rofs, 1);
   }
   st.l = xor32_sum(xor16_sum(st.l));
   __builtin_amdgcn_s_setprio(2);  // from here on only the unit's finish: ahead of streaming waves
@@ -704,7 +740,7 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
 // the cache is paged; the workgroup first stages sequence b's page ids that
 // it uses in LDS -- the pages of its live beacon rows, then of its live raw
 // rows and of the rows that receive the chunk's tokens.
-template <int NCH, bool PG>
+template <int NCH, bool PG, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(AttnArgs a) {
   constexpr int BN = NCH > 0 ? NCH : 4;
   constexpr int TRB = SegView<BN, true>::kRows, TRR = SegView<4, true>::kRows;
@@ -732,7 +768,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(
     for (int i = tid; i < n; i += kThreads) ptab[i] = i < nbp ? bt[i] : rt[i - nbp];
     lds_barrier();
   }
-  chunk_unit<NCH, PG>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb, ptab);
+  chunk_unit<NCH, PG, ALIBI>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb, ptab);
 }
 
 }  // namespace slimkv

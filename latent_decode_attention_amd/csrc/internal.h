@@ -15,6 +15,10 @@ constexpr int kMaxGroup = 8;           // query heads per KV head (G)
 constexpr int kMaxChunks = 64;         // workgroups per unit (each writes one partial slot)
 constexpr int kCounterStride = 16;     // uint32 per unit's counters: one 64-byte line each
 constexpr int kWgPerCu = 2;            // resident attention workgroups per CU the grid targets
+#ifndef SLIMKV_ATTN_DEPTH
+#define SLIMKV_ATTN_DEPTH 1
+#endif
+constexpr int kAttnDepth = SLIMKV_ATTN_DEPTH;  // tile depth of the uniform bf16 attention kernel
 constexpr int kMaxRaggedBatch = 1024;  // sequences per ragged call (their lengths sit in LDS)
 constexpr int kMaxPageEntries = 4096;  // page-table entries of one sequence (staged in LDS)
 constexpr int kMinPageShift = 6;       // pages hold at least 64 rows: no tile spans two pages
@@ -22,6 +26,8 @@ constexpr int kMaxPageShift = 16;
 constexpr int kChunkRows = 16;         // query rows (tokens x heads) per unit in chunk calls
 constexpr int kChunkMaxSlots = 2048;   // workgroup slots a chunk call is shaped for, at most
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;  // device scratch of the no-alloc entry point
+constexpr size_t kWsHeader = 256;      // workspace bytes before the counters: word 0 is the
+                                       // status SLIMKV_FLAG_CHECK_WORKSPACE reports in
 
 enum SegKind : int32_t {
   kSegLatent = 0,  // beacon rows: keys of width r_K scored with the latent
@@ -126,6 +132,12 @@ hipError_t launch_rebuild(const RebuildArgs& a, int dtype, hipStream_t s);
 
 // Tile height (rows) a segment of the given widths is swept in.
 int tile_rows(int dtype, int rk, int rv);
+
+// SLIMKV_FLAG_CHECK_WORKSPACE: one small kernel, launched on `s` before a
+// call's kernels, that finds every nonzero 32-bit word of ws[begin, end)
+// (the counters and flags, which must start at zero), clears it, and sets
+// bit 0 of ws word 0 when it found one.
+hipError_t launch_workspace_check(uint32_t* ws, size_t begin, size_t end, hipStream_t s);
 
 // Workgroup slots of the attention kernel that launch_attention would run
 // for `a` (the device's CUs x resident workgroups of that kernel, at most

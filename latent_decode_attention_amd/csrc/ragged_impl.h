@@ -250,7 +250,7 @@ __device__ __forceinline__ int ragged_piece_of(int blk, int P) {
 // workgroup first stages sequence b's page ids that it uses -- the pages
 // of its live beacon rows, then of its live raw rows and of the row that
 // receives the new token -- in LDS.
-template <int G, int NCH, bool BF16, bool PG>
+template <int G, int NCH, bool BF16, bool PG, bool ALIBI = false>
 __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel(AttnArgs a) {
   constexpr bool BLAT = NCH > 0;
   constexpr int kFullNch = BF16 ? 4 : 8;
@@ -282,21 +282,22 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel
     for (int i = tid; i < n; i += kThreads) ptab[i] = i < nbp ? bt[i] : rt[i - nbp];
     lds_barrier();
   }
-  attend_unit<G, NCH, BF16, true, PG>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb, ptab);
+  attend_unit<G, NCH, BF16, true, PG, ALIBI>(a, sh, b * Hkv + h, b, h, c, kb, nbr, wr, first + h * kb,
+                                             ptab);
 }
 
 // Launch for group size G; nch as for launch_attention_group.
-template <int G, bool PG>
+template <int G, bool PG, bool AL>
 const void* ragged_kernel_for(int dtype, int nch) {
   if (dtype == 0)
-    return nch == 0 ? reinterpret_cast<const void*>(&ragged_kernel<G, 0, false, PG>)
-                    : reinterpret_cast<const void*>(&ragged_kernel<G, 8, false, PG>);
+    return nch == 0 ? reinterpret_cast<const void*>(&ragged_kernel<G, 0, false, PG, AL>)
+                    : reinterpret_cast<const void*>(&ragged_kernel<G, 8, false, PG, AL>);
   switch (nch) {
-    case 0: return reinterpret_cast<const void*>(&ragged_kernel<G, 0, true, PG>);
-    case 1: return reinterpret_cast<const void*>(&ragged_kernel<G, 1, true, PG>);
-    case 2: return reinterpret_cast<const void*>(&ragged_kernel<G, 2, true, PG>);
-    case 3: return reinterpret_cast<const void*>(&ragged_kernel<G, 3, true, PG>);
-    default: return reinterpret_cast<const void*>(&ragged_kernel<G, 4, true, PG>);
+    case 0: return reinterpret_cast<const void*>(&ragged_kernel<G, 0, true, PG, AL>);
+    case 1: return reinterpret_cast<const void*>(&ragged_kernel<G, 1, true, PG, AL>);
+    case 2: return reinterpret_cast<const void*>(&ragged_kernel<G, 2, true, PG, AL>);
+    case 3: return reinterpret_cast<const void*>(&ragged_kernel<G, 3, true, PG, AL>);
+    default: return reinterpret_cast<const void*>(&ragged_kernel<G, 4, true, PG, AL>);
   }
 }
 
@@ -306,7 +307,11 @@ template <int G>
 hipError_t launch_ragged_group(AttnArgs a, int dtype, int nch, int64_t max_wgs, hipStream_t s,
                                hipEvent_t ev0, hipEvent_t ev1) {
   const bool paged = a.page_table[0] != nullptr || a.page_table[1] != nullptr;
-  const void* kfn = paged ? ragged_kernel_for<G, true>(dtype, nch) : ragged_kernel_for<G, false>(dtype, nch);
+  const bool alibi = a.alibi_slopes != nullptr;
+  const void* kfn = paged ? (alibi ? ragged_kernel_for<G, true, true>(dtype, nch)
+                                   : ragged_kernel_for<G, true, false>(dtype, nch))
+                          : (alibi ? ragged_kernel_for<G, false, true>(dtype, nch)
+                                   : ragged_kernel_for<G, false, false>(dtype, nch));
   int64_t P = a.chunks;
   if (P <= 0) {
     P = device_slots(kfn);

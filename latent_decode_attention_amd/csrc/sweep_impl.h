@@ -160,10 +160,11 @@ struct Traits<false> {
   static constexpr int kMaxLoads = 8;
 };
 
-// 16-row subtiles per tile for a given chunk count (of K or V, the larger).
-template <bool BF16, int NCH>
+// 16-row subtiles per tile for a given chunk count (of K or V, the larger):
+// about 8 KB of keys and values per tile, times D (the tile depth).
+template <bool BF16, int NCH, int D = 1>
 struct TileShape {
-  static constexpr int kSub = BF16 ? (NCH == 1 ? 4 : (NCH == 2 ? 2 : 1)) : 1;
+  static constexpr int kSub = (BF16 ? (NCH == 1 ? 4 : (NCH == 2 ? 2 : 1)) : 1) * D;
   static constexpr int kRows = 16 * kSub;
 };
 
@@ -176,7 +177,7 @@ struct alignas(16) AttnShared {
     } pro;
     struct {
       union {
-        float p[kWaves][64 * 8];                 // exp-weights of the current tile, per wave
+        float p[kWaves][128 * 8];                // exp-weights of the current tile, per wave
         float raw[kWaves][kMaxGroup][kHeadDim];  // each wave's raw-row sums (after the sweeps)
       } t;
       float beacon[kWaves][kMaxGroup][kHeadDim];  // each wave's beacon-row sums
@@ -415,13 +416,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // unit's page ids sit in LDS (tab, from index tab0).  Each tile then gets
 // its own descriptors, over the live rows of its page only; a page id
 // outside [0, npages) gets empty descriptors, so its rows read as zeros.
-template <int NCH, bool BF16, bool PAGED = false>
+template <int NCH, bool BF16, bool PAGED = false, int D = 1>
 struct SegView {
   using Tr = Traits<BF16>;
-  static constexpr int kSub = TileShape<BF16, NCH>::kSub;
-  static constexpr int kRows = TileShape<BF16, NCH>::kRows;
+  static constexpr int kSub = TileShape<BF16, NCH, D>::kSub;
+  static constexpr int kRows = TileShape<BF16, NCH, D>::kRows;
   static constexpr int kKeySlots = kSub * NCH;
-  static_assert(kRows <= (1 << kMinPageShift), "a tile must fit in a page");
+  static constexpr int kLoads = Tr::kMaxLoads * D;  // 16-byte loads per lane per tile (keys or values)
+  static_assert(!PAGED || kRows <= (1 << kMinPageShift), "a tile must fit in a page");
   __amdgpu_buffer_rsrc_t kr, vr;  // this unit's key and value rows (contiguous)
   int rows, rk, rv, ntiles;
   int kstride, vstride;  // bytes per key / value row
@@ -530,9 +532,9 @@ struct TailRows {
 // Page id of the tile a wave requests next (row ta of `a` if use_a, else
 // row tb of `b` if use_b), one LDS read; 0 for contiguous views and for the
 // tail.
-template <int NA, int NB, bool BF16, bool PG>
-__device__ __forceinline__ int tile_page(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
-                                         const SegView<NB, BF16, PG>& b, int tb, bool use_b) {
+template <int NA, int NB, bool BF16, bool PG, int D>
+__device__ __forceinline__ int tile_page(const SegView<NA, BF16, PG, D>& a, int ta, bool use_a,
+                                         const SegView<NB, BF16, PG, D>& b, int tb, bool use_b) {
   if constexpr (!PG) {
     return 0;
   } else {
@@ -548,12 +550,12 @@ __device__ __forceinline__ int tile_page(const SegView<NA, BF16, PG>& a, int ta,
 // registers need no copies afterwards (separate loads per source under a
 // branch would be merged by copies that wait for the loads).  pid: the
 // chosen tile's page id (see tile_page) when the views are paged.
-template <bool CROSS, int NA, int NB, bool BF16, bool PG>
-__device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
-                                               const SegView<NB, BF16, PG>& b, int tb, bool use_b,
+template <bool CROSS, int NA, int NB, bool BF16, bool PG, int D>
+__device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16, PG, D>& a, int ta, bool use_a,
+                                               const SegView<NB, BF16, PG, D>& b, int tb, bool use_b,
                                                const TailRows& tail, int pid, u32x4_t* kbuf) {
-  constexpr int KA = SegView<NA, BF16, PG>::kKeySlots, KB = SegView<NB, BF16, PG>::kKeySlots;
-  constexpr int K = Traits<BF16>::kMaxLoads;
+  constexpr int KA = SegView<NA, BF16, PG, D>::kKeySlots, KB = SegView<NB, BF16, PG, D>::kKeySlots;
+  constexpr int K = SegView<NA, BF16, PG, D>::kLoads;
   static_assert(KA <= K && KB <= K, "tile too large");
   const bool ub = CROSS && use_b;
   const __amdgpu_buffer_rsrc_t r = use_a ? a.key_rsrc(ta, pid) : (ub ? b.key_rsrc(tb, pid) : tail.r);
@@ -565,15 +567,15 @@ __device__ __forceinline__ void load_tile_keys(const SegView<NA, BF16, PG>& a, i
     kbuf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + off, 0, kStream);
   }
 }
-template <bool CROSS, int NA, int NB, bool BF16, bool PG>
-__device__ __forceinline__ void load_tile_values(const SegView<NA, BF16, PG>& a, int ta, bool use_a,
-                                                 const SegView<NB, BF16, PG>& b, int tb, bool use_b,
+template <bool CROSS, int NA, int NB, bool BF16, bool PG, int D>
+__device__ __forceinline__ void load_tile_values(const SegView<NA, BF16, PG, D>& a, int ta, bool use_a,
+                                                 const SegView<NB, BF16, PG, D>& b, int tb, bool use_b,
                                                  const TailRows& tail, int pid, u32x4_t* vbuf) {
   const bool ub = CROSS && use_b;
   const __amdgpu_buffer_rsrc_t r = use_a ? a.val_rsrc(ta, pid) : (ub ? b.val_rsrc(tb, pid) : tail.r);
   const int base = use_a ? a.val_base(ta) : (ub ? b.val_base(tb) : tail.vlane);
 #pragma unroll
-  for (int i = 0; i < Traits<BF16>::kMaxLoads; ++i) {
+  for (int i = 0; i < SegView<NA, BF16, PG, D>::kLoads; ++i) {
     const int off = use_a ? a.val_off(i) : (ub ? b.val_off(i) : tail.val_off(i));
     vbuf[i] = __builtin_amdgcn_raw_buffer_load_b128(r, base + off, 0, kStream);
   }
@@ -649,9 +651,9 @@ struct TileFeed {
 // its nearest tiles first, and its running max stops growing after its
 // first tile of the segment instead of growing (and rescaling every sum)
 // on every tile.
-template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG, bool ALIBI = false>
-__device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbase,
-                                      const SegView<NCH2, BF16, PG>& nx, int nxbase, int pend, int& j,
+template <int G, int NCH, bool BF16, bool CROSS, int NCH2, bool PG, bool ALIBI = false, int D = 1>
+__device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG, D>& sv, int pbase,
+                                      const SegView<NCH2, BF16, PG, D>& nx, int nxbase, int pend, int& j,
                                       TileFeed& feed, const TailRows& tail, const float* qsrc, int rq,
                                       u32x4_t* kbuf, u32x4_t* vbuf, float* pw,
                                       WaveState<G, BF16>& st, const float* slope2 = nullptr,
@@ -659,13 +661,14 @@ __device__ __forceinline__ void sweep(const SegView<NCH, BF16, PG>& sv, int pbas
   using Tr = Traits<BF16>;
   constexpr int EPL = Tr::kEpl;
   constexpr int KCH = Tr::kChunkK;
-  constexpr int SUB = SegView<NCH, BF16, PG>::kSub;
-  constexpr int TR = SegView<NCH, BF16, PG>::kRows;
-  constexpr int VMAX = Tr::kMaxLoads;
+  constexpr int SUB = SegView<NCH, BF16, PG, D>::kSub;
+  constexpr int TR = SegView<NCH, BF16, PG, D>::kRows;
+  constexpr int VMAX = SegView<NCH, BF16, PG, D>::kLoads;
   constexpr int GP = G <= 4 ? 4 : 8;  // padded heads per LDS row
   constexpr int NGRP = (G + 3) / 4;   // 16-lane groups holding real heads
-  static_assert(SUB * NCH <= Tr::kMaxLoads, "tile too large");
-  constexpr int TR2 = SegView<NCH2, BF16, PG>::kRows;
+  static_assert(SUB * NCH <= VMAX, "tile too large");
+  static_assert(TR * GP <= 128 * 8, "exp-weights of a tile exceed their LDS space");
+  constexpr int TR2 = SegView<NCH2, BF16, PG, D>::kRows;
   const int pstop = min(pbase + sv.ntiles, pend);
   if (j >= pstop) return;  // wave-uniform
 
@@ -841,8 +844,8 @@ __device__ __forceinline__ void wave_reduce(WaveState<G, BF16>& st, int lpr) {
 }
 
 // Park a reduced wave state in LDS: (max, sum) per head and the G x rv sums.
-template <int G, int NCH, bool BF16, bool PG>
-__device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const SegView<NCH, BF16, PG>& sv,
+template <int G, int NCH, bool BF16, bool PG, int D>
+__device__ __forceinline__ void wave_park(const WaveState<G, BF16>& st, const SegView<NCH, BF16, PG, D>& sv,
                                           float (*wacc)[kHeadDim], float (*wml)[2]) {
   const int lane = threadIdx.x & 63, n = lane & 15, kg = lane >> 4;
   if (n == 0) {
@@ -1127,7 +1130,9 @@ __device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
 // merge.  The token's row is stored when the raw window has room (wlive <
 // its capacity): no workgroup reads that row in this call.  PG: through the
 // raw pages' ids at ptab[rtab0 ..] (no store if the id is out of range).
-template <int G, bool BF16>
+// ALIBI: an ALiBi backbone rotates nothing, so the key is scored and stored
+// as given; it sits at the query's own position, so its bias is zero.
+template <int G, bool BF16, bool ALIBI = false>
 struct TokenPartial {
   uint32_t k1[4], k2[4], v[4];  // storage bits: key elements i and their rotation partners, values
   __device__ __forceinline__ void issue(const AttnArgs& a, int u) {
@@ -1153,10 +1158,14 @@ struct TokenPartial {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * c4 + e, pi = i & (kHeadDim / 2 - 1);
-      double s64, c64;
-      sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
-      const double ki = (double)bits_to_float<BF16>(k1[e]), kp = (double)bits_to_float<BF16>(k2[e]);
-      kbits[e] = storage_bits_from_f64<BF16>(i < kHeadDim / 2 ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
+      if constexpr (ALIBI) {
+        kbits[e] = k1[e];
+      } else {
+        double s64, c64;
+        sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
+        const double ki = (double)bits_to_float<BF16>(k1[e]), kp = (double)bits_to_float<BF16>(k2[e]);
+        kbits[e] = storage_bits_from_f64<BF16>(i < kHeadDim / 2 ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
+      }
       dot += sh.qrot[g][i] * bits_to_float<BF16>(kbits[e]);
     }
     dot = xor16_sum(row16_sum(dot));  // the 32 threads of head g; log2 units (pre-scaled query)
@@ -1298,7 +1307,7 @@ __device__ __forceinline__ void ragged_finish(const AttnArgs& a, const AttnShare
 // page ids, then its raw page ids.
 // NCH > 0: latent beacons swept in NCH MFMA chunks; NCH == 0: beacon rows
 // are full width (rebuilt beacons) or absent.
-template <int G, int NCH, bool BF16, bool RAGGED, bool PG = false, bool ALIBI = false>
+template <int G, int NCH, bool BF16, bool RAGGED, bool PG = false, bool ALIBI = false, int D = 1>
 __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, int unit, int b, int h,
                                             int c, int k, int nbr, int wr, int slot0,
                                             const int32_t* ptab = nullptr) {
@@ -1311,8 +1320,8 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   const int nwaves = kWaves * k;
   const int wu = kWaves * c + wave;  // this wave's number within the unit
 
-  SegView<BN, BF16, PG> bv;        // beacon rows
-  SegView<kFullNch, BF16, PG> rw;  // raw rows
+  SegView<BN, BF16, PG, D> bv;        // beacon rows
+  SegView<kFullNch, BF16, PG, D> rw;  // raw rows
   const int brk = BLAT ? a.seg[0].rk : kHeadDim, brv = BLAT ? a.seg[0].rv : kHeadDim;
   int nbp = 0;  // the unit's beacon pages (paged)
   if constexpr (PG) {
@@ -1353,15 +1362,15 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   QueryPrologue<G, BF16, NCH, !ALIBI> pro;
   pro.issue(a, b, h, wave);
   // ragged calls: the unit's first workgroup makes the new token's partial
-  TokenPartial<G, BF16> tokp;
+  TokenPartial<G, BF16, ALIBI> tokp;
   const bool tok = RAGGED && c == 0 && a.k_new != nullptr && tid < G * kHeadDim / 4;
   if (tok) tokp.issue(a, unit);
-  u32x4_t kbuf[Traits<BF16>::kMaxLoads], vbuf[Traits<BF16>::kMaxLoads];
+  u32x4_t kbuf[Traits<BF16>::kMaxLoads * D], vbuf[Traits<BF16>::kMaxLoads * D];
   int j = wu;
   {
     // (ALiBi: each segment's tiles in reverse, as in sweep)
-    const int tb = (ALIBI ? nbt - 1 - j : j) * SegView<BN, BF16, PG>::kRows;
-    const int tr = (ALIBI ? rw.ntiles - 1 - (j - nbt) : j - nbt) * SegView<kFullNch, BF16, PG>::kRows;
+    const int tb = (ALIBI ? nbt - 1 - j : j) * SegView<BN, BF16, PG, D>::kRows;
+    const int tr = (ALIBI ? rw.ntiles - 1 - (j - nbt) : j - nbt) * SegView<kFullNch, BF16, PG, D>::kRows;
     const bool ub = j < nbt, ur = j >= nbt && j < total;
     const int pid = tile_page(bv, tb, ub, rw, tr, ur);
     load_tile_keys<true>(bv, tb, ub, rw, tr, ur, tail, pid, kbuf);
@@ -1381,17 +1390,20 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
     for (int i = 0; i < 4; ++i)
       slope2[i] = a.alibi_slopes[h * G + min(4 * kg + i, G - 1)] * 1.4426950408889634f;
     bdist0 = a.q_pos[b] - a.beacon_first;
-    rdist0 = wr - 1;
+    // raw row t sits at q_pos - wr + t when the call brings the decode
+    // step's new token (which follows the raw rows, at q_pos), at
+    // q_pos - wr + 1 + t when the query's own token is the last raw row
+    rdist0 = (RAGGED && a.k_new) ? wr : wr - 1;
   }
   WaveState<G, BF16> st;
   st.reset();
-  sweep<G, BN, BF16, true, kFullNch, PG, ALIBI>(bv, 0, rw, nbt, total, j, feed, tail,
+  sweep<G, BN, BF16, true, kFullNch, PG, ALIBI, D>(bv, 0, rw, nbt, total, j, feed, tail,
                                           BLAT ? &sh.qlat[0][0] : &sh.qrot[0][0], bv.rk, kbuf, vbuf,
                                           pw, st, slope2, bdist0, a.beacon_stride);
   wave_reduce<G, BF16>(st, bv.lpr);
-  wave_park<G, BN, BF16, PG>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
+  wave_park<G, BN, BF16, PG, D>(st, bv, sh.u.s.beacon[wave], sh.wml[0][wave]);
   st.reset();
-  sweep<G, kFullNch, BF16, false, kFullNch, PG, ALIBI>(rw, nbt, rw, total, total, j, feed, tail,
+  sweep<G, kFullNch, BF16, false, kFullNch, PG, ALIBI, D>(rw, nbt, rw, total, total, j, feed, tail,
                                                        &sh.qrot[0][0], kHeadDim, kbuf, vbuf, pw, st,
                                                        slope2, rdist0, 1);
   // From here on the wave only finishes the unit: raise its issue priority
@@ -1399,6 +1411,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   // (on the critical path of the whole call) is not starved by them.
   __builtin_amdgcn_s_setprio(2);
   // bf16 latent beacons: the tile registers now hold the lift's U_V rows
+  // 16 wave + n (t = 0) and 64 + 16 wave + n (t = 1), features 32c + 8kg ..
+  // +7 (past r_V they read on into the next row, or zeros past the end, and
+  // meet zero latent entries)
   u32x4_t uw[2][4];
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) {
@@ -1418,7 +1433,7 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   if (tid == 0)
     done = __hip_atomic_fetch_add(&a.counters[(size_t)unit * kCounterStride], 1u, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
-  wave_park<G, kFullNch, BF16, PG>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
+  wave_park<G, kFullNch, BF16, PG, D>(st, rw, sh.u.s.t.raw[wave], sh.wml[1][wave]);
   lds_barrier();
   wg_partial<G, BF16, BLAT>(a, sh, h, wave, bv.rv, uw);
   if (tid == 0) sh.is_last = done == (uint32_t)(k - 1);
@@ -1467,7 +1482,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
 // speed of its slot or its XCD.  This numbering gives every unit workgroups
 // of every age on different XCDs, so the units finish together.
 template <int G, int NCH, bool BF16, bool ALIBI = false>
-__global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, (BF16 && G <= 4 && kAttnDepth == 1) ? 3 : 2) void attention_kernel(
+    AttnArgs a) {
+  constexpr int D = BF16 ? kAttnDepth : 1;
   __shared__ AttnShared sh;
   const int k = a.chunks;
   const int units = a.batch * a.num_kv_heads;
@@ -1476,8 +1493,8 @@ __global__ __launch_bounds__(kThreads, (BF16 && G <= 4) ? 3 : 2) void attention_
   const int unit = (int)(((int64_t)blockIdx.x - (int64_t)c * units + c) % units);
   const int b = unit / a.num_kv_heads;
   const int h = unit - b * a.num_kv_heads;
-  attend_unit<G, NCH, BF16, false, false, ALIBI>(a, sh, unit, b, h, c, k, a.seg[0].rows,
-                                                 a.seg[1].rows, unit * k);
+  attend_unit<G, NCH, BF16, false, false, ALIBI, D>(a, sh, unit, b, h, c, k, a.seg[0].rows,
+                                                    a.seg[1].rows, unit * k);
 }
 
 // Workgroup slots the grid fills on the current device: CUs x resident

@@ -46,7 +46,7 @@ def test_problem_struct_layout():
 
 
 def test_version_and_status_strings(lib):
-    assert lda.slimkv_abi_version() == 8
+    assert lda.slimkv_abi_version() == 9
     for code in range(8):
         assert lda.slimkv_status_string(code)
     assert lda.slimkv_status_string(99) == "unknown status"
@@ -103,12 +103,24 @@ def test_shape_errors(lib, over, status):
 
 def test_unknown_flag_bits_rejected(lib):
     prob = _problem()
-    prob.flags = 2
+    prob.flags = 4
     assert _call(lib, prob) == SHAPE
     assert "flag" in lda.slimkv_last_error()
     assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) == 0
-    prob.flags = lda.SLIMKV_FLAG_DYNAMIC_TILES
-    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) > 0
+    for f in (lda.SLIMKV_FLAG_DYNAMIC_TILES, lda.SLIMKV_FLAG_CHECK_WORKSPACE,
+              lda.SLIMKV_FLAG_DYNAMIC_TILES | lda.SLIMKV_FLAG_CHECK_WORKSPACE):
+        prob.flags = f
+        assert lib.slimkv_workspace_bytes(ctypes.byref(prob), 0) > 0
+
+
+def test_workspace_status_checks(lib):
+    """slimkv_workspace_status rejects NULL and misaligned workspaces
+    before it touches the device."""
+    word = ctypes.c_uint32(7)
+    assert lib.slimkv_workspace_status(None, ctypes.byref(word)) == NULL
+    assert lib.slimkv_workspace_status(ctypes.c_void_p(0x100000), None) == NULL
+    assert lib.slimkv_workspace_status(ctypes.c_void_p(0x100004), ctypes.byref(word)) == ALIGN
+    assert word.value == 7
 
 
 def test_null_problem(lib):
@@ -212,6 +224,9 @@ def test_ragged_checks(lib):
     # the schedule is fixed; the lengths live in LDS
     prob.flags = lda.SLIMKV_FLAG_DYNAMIC_TILES
     assert _call_ragged(lib, prob) == UNSUP
+    prob.flags = lda.SLIMKV_FLAG_CHECK_WORKSPACE
+    assert lib.slimkv_workspace_bytes(ctypes.byref(prob), ragged) > 0
+    prob.flags = 0
     assert _call_ragged(lib, _problem(batch=1025)) == UNSUP
     assert _call_ragged(lib, _problem(batch=1024), ws_bytes=16) == WS
     # the new token's key and value come together
@@ -458,3 +473,53 @@ def test_bench_helpers_reject_bad_arguments(lib):
     assert lib.slimkv_bench_flush(None, 1024, 0, None) == NULL
     assert lib.slimkv_bench_flush(vp(0x1000004), 1024, 0, None) == ALIGN
     assert lib.slimkv_bench_flush(src, 1000, 0, None) == SHAPE
+
+
+def test_alibi_struct_layout():
+    text = HEADER.read_text()
+    body = re.search(r"typedef struct slimkv_alibi \{(.*?)\} slimkv_alibi;", text, re.S).group(1)
+    names = re.findall(r"^\s*(?:const float\*|int32_t)\s+(\w+);", body, re.M)
+    assert names == [f for f, _ in binding.slimkv_alibi._fields_]
+    assert ctypes.sizeof(binding.slimkv_alibi) == 16
+
+
+def test_alibi_serving_checks(lib):
+    """The ALiBi forms of the serving calls: the rotary call's checks, plus a
+    NULL alibi or slopes, beacon positions that leave int32, and misaligned
+    slopes -- all before any HIP call."""
+    vp = ctypes.c_void_p
+    p = dict(q=0x100000, q_pos=0x200000, U_K=0x300000, U_V=0x400000, C_K=0x1000000,
+             C_V=0x2000000, K_raw=0x3000000, V_raw=0x4000000, nb=0x210000, raw=0x220000,
+             k_new=0x230000, v_new=0x240000, out=0x5000000, lse=0x6000000, ws=0x7000000)
+    v = {k: vp(x) for k, x in p.items()}
+    tail = (v["q"], v["q_pos"], v["U_K"], v["U_V"], v["C_K"], v["C_V"], v["K_raw"], v["V_raw"],
+            v["nb"], v["raw"], v["k_new"], v["v_new"], v["out"], v["lse"], v["ws"], 1 << 30, None)
+    prob = _problem()
+    pages = lda.make_pages(page_rows=64)
+    pages.beacon_table_width = 1
+    pages.raw_table_width = 1
+    pages.beacon_pages = pages.raw_pages = 4
+    pages.beacon_table = 0x250000
+    pages.raw_table = 0x260000
+
+    def calls(al):
+        a = ctypes.byref(al) if al is not None else None
+        pp = ctypes.byref(prob)
+        return [lib.slimkv_decode_attn_ragged_alibi(pp, a, *tail),
+                lib.slimkv_decode_attn_paged_alibi(pp, ctypes.byref(pages), a, *tail),
+                lib.slimkv_decode_attn_chunk_alibi(pp, a, 2, *tail),
+                lib.slimkv_decode_attn_chunk_paged_alibi(pp, ctypes.byref(pages), a, 2, *tail)]
+
+    good = binding.slimkv_alibi(0x280000, 15, 16)
+    # with good parameters every call gets as far as the (too small) workspace
+    ws_small = tail[:-2] + (16, None)
+    pp = ctypes.byref(prob)
+    assert lib.slimkv_decode_attn_ragged_alibi(pp, ctypes.byref(good), *ws_small) == WS
+    assert lib.slimkv_decode_attn_chunk_alibi(pp, ctypes.byref(good), 2, *ws_small) == WS
+    assert calls(None) == [NULL] * 4
+    assert calls(binding.slimkv_alibi(None, 15, 16)) == [NULL] * 4
+    assert calls(binding.slimkv_alibi(0x280000, -1, 16)) == [SHAPE] * 4
+    assert calls(binding.slimkv_alibi(0x280000, 0, -16)) == [SHAPE] * 4
+    assert calls(binding.slimkv_alibi(0x280000, 0, 1 << 30)) == [SHAPE] * 4  # 63 beacons past int32
+    assert calls(binding.slimkv_alibi(0x280002, 15, 16)) == [ALIGN] * 4
+    assert calls(binding.slimkv_alibi(0x5000000, 15, 16)) == [ALIAS] * 4  # slopes inside out

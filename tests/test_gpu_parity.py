@@ -19,8 +19,10 @@ from parity_util import (RECON_LSE_TOL, assert_parity, beacon_positions, gather_
 pytestmark = pytest.mark.gpu
 
 LAT, REC, FULL = lda.SLIMKV_OP_LATENT, lda.SLIMKV_OP_RECONSTRUCT, lda.SLIMKV_OP_FULL_KV
-# The workspace opens with one 64-byte line of counters per (b, kv head)
-# unit: 16 uint32, of which the first two are used.
+# The workspace opens with a 256-byte header (word 0: the status word of
+# SLIMKV_FLAG_CHECK_WORKSPACE), then one 64-byte line of counters per
+# (b, kv head) unit: 16 uint32, of which the first two are used.
+WS_HEADER = 256
 COUNTER_STRIDE = 16
 
 
@@ -249,11 +251,53 @@ def test_workspace_reused_across_plans(gpu_device):
     # per slot, 64 slots per unit, from the next 256-byte boundary) are back
     # at zero
     units = wl.batch * wl.num_kv_heads
-    counters = ws[:COUNTER_STRIDE * 4 * units].view(torch.int32).view(units, COUNTER_STRIDE)
+    c0 = WS_HEADER
+    counters = ws[c0:c0 + COUNTER_STRIDE * 4 * units].view(torch.int32).view(units, COUNTER_STRIDE)
     assert int(counters.abs().sum()) == 0, counters[counters.abs().sum(dim=1) != 0]
-    f0 = (COUNTER_STRIDE * 4 * units + 255) // 256 * 256
+    f0 = (c0 + COUNTER_STRIDE * 4 * units + 255) // 256 * 256
     flags = ws[f0:f0 + 64 * 4 * units].view(torch.int32)
     assert int(flags.abs().sum()) == 0, torch.nonzero(flags)
+    assert lda.slimkv_workspace_status(ws) == 0
+
+
+def test_workspace_check_flag(gpu_device):
+    """SLIMKV_FLAG_CHECK_WORKSPACE: a workspace whose counters and flags
+    hold garbage (as one left by an interrupted call would) still gives the
+    right result, and the status word reports it; a clean workspace keeps
+    the status at zero."""
+    wl = custom(B=2, Hkv=2, G=4, nb=700, w=90, r=64, index=97)
+    inp = synth.make_layer(wl)
+    g = inp.to("cuda")
+    ref, ref_lse = oracle_layer(inp)
+    prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
+                                    rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
+                                    scale=wl.scale, num_splits=5,
+                                    flags=lda.SLIMKV_FLAG_CHECK_WORKSPACE)
+    ws = lda.alloc_workspace(prob, LAT, "cuda")
+    units = wl.batch * wl.num_kv_heads
+    out, lse = lda.alloc_outputs(prob, "cuda")
+    note("workspace check: clean workspace")
+    lda.slimkv_decode_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw, g.V_raw,
+                           out, lse, ws)
+    torch.cuda.synchronize()
+    assert lda.slimkv_workspace_status(ws) == 0
+    assert_parity(out.double().cpu().numpy(), ref, "bf16", "check flag clean",
+                  lse.double().cpu().numpy(), ref_lse)
+    # plant garbage in every unit's done counter and in one partial flag
+    c0 = WS_HEADER
+    ws[c0:c0 + COUNTER_STRIDE * 4 * units].view(torch.int32).view(units, COUNTER_STRIDE)[:, 0] = 3
+    f0 = (c0 + COUNTER_STRIDE * 4 * units + 255) // 256 * 256
+    ws[f0:f0 + 4].view(torch.int32)[0] = 1
+    out.fill_(float("nan"))
+    note("workspace check: planted counters")
+    lda.slimkv_decode_attn(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, g.K_raw, g.V_raw,
+                           out, lse, ws)
+    torch.cuda.synchronize()
+    assert lda.slimkv_workspace_status(ws) == 1
+    assert_parity(out.double().cpu().numpy(), ref, "bf16", "check flag planted",
+                  lse.double().cpu().numpy(), ref_lse)
+    counters = ws[c0:c0 + COUNTER_STRIDE * 4 * units].view(torch.int32)
+    assert int(counters.abs().sum()) == 0
 
 
 def test_many_chunks_repeatable(gpu_device):
