@@ -32,9 +32,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // is the A operand (basis row = output column on M, rank on K) and the
 // transposed latent rows the B operand (rank on K, beacon row on N):
 // lane (n, kg) then ends with columns 16t + 4kg .. +3 of row n for each
-// 16-column tile t -- the two halves of every rotation pair in one lane,
-// and 8 contiguous output bytes per store.  The latent rows of the next
-// four sequences are in flight while one is multiplied.
+// 16-column tile t -- the two halves of every rotation pair in one lane.
+// Each wave turns its 16 finished rows around in LDS, so that its stores
+// write whole rows, 16 bytes per lane (four rows per store).  The latent
+// rows of the next four sequences are in flight while one is multiplied.
 
 // Sine and cosine of pos * theta^(-2i/d) for pair i < 64 (see above).
 __device__ __forceinline__ void rebuild_sincos(const RebuildArgs& a, int pos, int i, float& s,
@@ -58,10 +59,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 constexpr int kRebuildRows = 64;  // beacon rows per workgroup (16 per wave)
 constexpr int kUPad = 8;           // staged basis rows padded by 16 bytes (LDS banks)
 constexpr int kRebuildAhead = 4;   // sequences whose latent rows are in flight per wave
+constexpr int kOPitch = kHeadDim + 8;  // a wave's staged output rows (elements; padded)
 
 template <int NCHK>
 __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ul[kHeadDim * (32 * NCHK + kUPad)];
+  __shared__ __attribute__((aligned(16))) uint16_t ot[kWaves][16 * kOPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, kg = lane >> 4;
   const int nb = a.num_beacons, hkv = a.num_kv_heads;
@@ -74,8 +77,8 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
   const int nchk = (r + 31) / 32;  // workgroup-uniform
   const int us = r + kUPad;        // staged row stride (elements)
   const int row = rb * kRebuildRows + wave * 16 + n;
-  const bool row_ok = row < nb;
-  const int rowc = row_ok ? row : nb - 1;  // loads stay in bounds; the store is skipped
+  const int rowc = row < nb ? row : nb - 1;  // loads stay in bounds; the store is skipped
+  uint16_t* ow = ot[wave];
 
   const uint16_t* C = static_cast<const uint16_t*>(a.C[job]);
   uint16_t* D = static_cast<uint16_t*>(a.dst[job]);
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
 #pragma unroll
         for (int c = 0; c < NCHK; ++c) cur[c] = ring[i][c];
         if (b + kRebuildAhead < a.batch) load_rows(b + kRebuildAhead, ring[i]);
-        uint16_t* Dr = D + (((size_t)b * hkv + h) * nb + row) * kHeadDim + 4 * kg;
+        uint16_t* orow = ow + n * kOPitch + 4 * kg;
         // column tiles t and t + 4 together: they hold the two halves of this
         // lane's rotation pairs
 #pragma unroll
@@ -153,14 +156,31 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
               d1[e] = y * cs[t][e] + x * sn[t][e];
             }
           }
-          if (row_ok) {
-            *reinterpret_cast<uint2*>(Dr + 16 * t) =
-                make_uint2(f32_to_bf16(d0[0]) | (f32_to_bf16(d0[1]) << 16),
-                           f32_to_bf16(d0[2]) | (f32_to_bf16(d0[3]) << 16));
-            *reinterpret_cast<uint2*>(Dr + 16 * t + 64) =
-                make_uint2(f32_to_bf16(d1[0]) | (f32_to_bf16(d1[1]) << 16),
-                           f32_to_bf16(d1[2]) | (f32_to_bf16(d1[3]) << 16));
-          }
+          *reinterpret_cast<uint2*>(orow + 16 * t) =
+              make_uint2(f32_to_bf16(d0[0]) | (f32_to_bf16(d0[1]) << 16),
+                         f32_to_bf16(d0[2]) | (f32_to_bf16(d0[3]) << 16));
+          *reinterpret_cast<uint2*>(orow + 16 * t + 64) =
+              make_uint2(f32_to_bf16(d1[0]) | (f32_to_bf16(d1[1]) << 16),
+                         f32_to_bf16(d1[2]) | (f32_to_bf16(d1[3]) << 16));
+        }
+        // the wave's 16 rows, read back row by row: store i writes rows
+        // 4i .. 4i + 3, lane (row 4i + lane / 16) taking 8 columns
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        u32x4_t ov[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ov[i] = *reinterpret_cast<const u32x4_t*>(ow + (4 * i + (lane >> 4)) * kOPitch + 8 * (lane & 15));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row0 = rb * kRebuildRows + wave * 16;
+        uint16_t* Dw = D + (((size_t)b * hkv + h) * nb + row0) * kHeadDim + 8 * (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 4 * i + (lane >> 4);
+          if (row0 + rr < nb) *reinterpret_cast<u32x4_t*>(Dw + (size_t)rr * kHeadDim) = ov[i];
         }
       }
     }
