@@ -340,7 +340,7 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
  * rotated there and attends, under one softmax, over the sequence's live
  * beacon rows (latent, as in slimkv_decode_attn), its live raw rows, and the
  * chunk's new tokens 0 .. t -- token u's key rotated at q_pos[b] + u in
- * double precision and rounded once to bf16 -- but not over the chunk's
+ * double precision and rounded once to the cache dtype -- but not over the chunk's
  * later tokens.  The tokens u with w_b + u < W_cap are then stored as raw
  * rows w_b + u of K_raw and V_raw (rotated key, value); the others are
  * attended but not stored.  Without k_new and v_new every query of the
@@ -354,7 +354,8 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
  *                                  both or neither
  *   out           [B, Q, H_q, d] fp32;  lse [B, Q, H_q] fp32 or NULL
  * Capacity-sized caches, lengths, clamping, limits (batch <= 1024, flags 0)
- * and num_splits as for slimkv_decode_attn_ragged.  bf16 only.  Workspace:
+ * and num_splits as for slimkv_decode_attn_ragged.  bf16 or fp32 caches
+ * (fp32: the products on the fp32 matrix instructions).  Workspace:
  * slimkv_chunk_workspace_bytes(problem, num_tokens) bytes, zero-filled
  * before first use.
  */

@@ -176,13 +176,12 @@ slimkv_status make_plan(const slimkv_problem* p, slimkv_op op, Plan& pl) {
 }
 
 // Plan of a chunk call: the ragged call's segments and schedule limits,
-// bf16 only, G * Q <= kChunkRows query rows per unit; partial slots for
+// G * Q <= kChunkRows query rows per unit; partial slots for
 // every piece the launcher can make (at most units + kChunkMaxSlots), each
 // holding G * Q rows.
 slimkv_status make_chunk_plan(const slimkv_problem* p, int32_t num_tokens, Plan& pl) {
   slimkv_status st = make_plan(p, SLIMKV_OP_LATENT_RAGGED, pl);
   if (st != SLIMKV_OK) return st;
-  if (p->dtype != SLIMKV_BF16) return fail(SLIMKV_ERR_UNSUPPORTED, "chunk calls take bf16 caches");
   const int G = p->num_q_heads / p->num_kv_heads;
   if (num_tokens < 1) return fail(SLIMKV_ERR_SHAPE, "num_tokens must be >= 1");
   if ((int64_t)G * num_tokens > kChunkRows)
@@ -608,7 +607,7 @@ slimkv_status run_ragged(const slimkv_problem* p, const slimkv_pages* pg, const 
   const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
   g_ev_start = g_ev_stop = nullptr;
   const hipError_t err = chunk > 0
-                            ? launch_chunk(a, static_cast<hipStream_t>(stream), ev0, ev1)
+                            ? launch_chunk(a, pl.dtype, static_cast<hipStream_t>(stream), ev0, ev1)
                             : launch_ragged(a, pl.dtype, static_cast<hipStream_t>(stream), ev0, ev1);
   if (err != hipSuccess) return fail(SLIMKV_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
   g_last_error.clear();

@@ -1,7 +1,8 @@
-// chunk.hip -- the chunk kernel (several query tokens per sequence, bf16;
-// capacity-sized or paged caches) and its launcher.
+// chunk.hip -- the chunk kernels (several query tokens per sequence, bf16
+// or fp32; capacity-sized or paged caches) and their launcher.
 #include "sweep_impl.h"
 #include "chunk_impl.h"
+#include "chunk_f32_impl.h"
 
 namespace slimkv {
 
@@ -16,18 +17,28 @@ static const void* chunk_kernel_for(int nch) {
   }
 }
 
+template <bool PG, bool AL>
+static const void* chunk_f32_kernel_for(bool lat) {
+  return lat ? reinterpret_cast<const void*>(&chunk_f32_kernel<true, PG, AL>)
+             : reinterpret_cast<const void*>(&chunk_f32_kernel<false, PG, AL>);
+}
+
 // P = a.chunks (> 0: as given; <= 0: the device's workgroup slots), at most
 // kChunkMaxSlots and 64 per unit; the grid adds one block per unit, so the
 // pieces (at most max(P, units)) fit the workspace's units + kChunkMaxSlots
 // partial slots.
-hipError_t launch_chunk(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  const int nch = (a.seg[0].kind == kSegLatent && a.seg[0].rows > 0)
-                      ? std::max((a.seg[0].rk + 31) / 32, (a.seg[0].rv + 31) / 32)
-                      : 0;
+hipError_t launch_chunk(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  const bool lat = a.seg[0].kind == kSegLatent && a.seg[0].rows > 0;
+  const int nch = lat ? std::max((a.seg[0].rk + 31) / 32, (a.seg[0].rv + 31) / 32) : 0;
   const bool paged = a.page_table[0] != nullptr || a.page_table[1] != nullptr;
   const bool alibi = a.alibi_slopes != nullptr;
-  const void* kfn = paged ? (alibi ? chunk_kernel_for<true, true>(nch) : chunk_kernel_for<true, false>(nch))
-                          : (alibi ? chunk_kernel_for<false, true>(nch) : chunk_kernel_for<false, false>(nch));
+  const void* kfn;
+  if (dtype == 0)
+    kfn = paged ? (alibi ? chunk_f32_kernel_for<true, true>(lat) : chunk_f32_kernel_for<true, false>(lat))
+                : (alibi ? chunk_f32_kernel_for<false, true>(lat) : chunk_f32_kernel_for<false, false>(lat));
+  else
+    kfn = paged ? (alibi ? chunk_kernel_for<true, true>(nch) : chunk_kernel_for<true, false>(nch))
+                : (alibi ? chunk_kernel_for<false, true>(nch) : chunk_kernel_for<false, false>(nch));
   const int64_t units = (int64_t)a.batch * a.num_kv_heads;
   int64_t P = a.chunks;
   if (P <= 0) {

@@ -372,9 +372,10 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
 // of range).  Thread (m, c8) owns 8 columns of row m (16 threads, one DPP
 // row, per query row).  ALIBI: nothing is rotated (the keys are scored and
 // stored as given) and query row m (token t) scoring token tk adds its
-// head's slope times the distance tk - t (in log2 units).
-template <bool PG, bool ALIBI = false>
-__device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShared& sh, int u, int b,
+// head's slope times the distance tk - t (in log2 units).  BF16 / SH: the
+// storage dtype and the kernel's LDS layout (fp32 caches have their own).
+template <bool PG, bool ALIBI = false, bool BF16 = true, typename SH = ChunkShared>
+__device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, SH& sh, int u, int b,
                                                     int h, int wlive, int M, int G,
                                                     const int32_t* ptab, int rtab0) {
   const int tid = threadIdx.x;
@@ -387,24 +388,23 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
   for (int p = tid; p < Q * kHalf; p += kThreads) {
     const int t = p / kHalf, i = p % kHalf;
     const size_t kb = (((size_t)b * Q + t) * Hkv + h) * kHeadDim;
-    const double k1 = (double)ld_elem<true>(a.k_new, kb + i);
-    const double k2 = (double)ld_elem<true>(a.k_new, kb + i + kHalf);
-    const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + kb;
-    const uint16_t v1 = vs[i], v2 = vs[i + kHalf];
+    const uint32_t v1 = ld_bits<BF16>(a.v_new, kb + i), v2 = ld_bits<BF16>(a.v_new, kb + i + kHalf);
     uint32_t b1, b2;
     if constexpr (ALIBI) {
-      b1 = static_cast<const uint16_t*>(a.k_new)[kb + i];
-      b2 = static_cast<const uint16_t*>(a.k_new)[kb + i + kHalf];
+      b1 = ld_bits<BF16>(a.k_new, kb + i);
+      b2 = ld_bits<BF16>(a.k_new, kb + i + kHalf);
     } else {
+      const double k1 = (double)ld_elem<BF16>(a.k_new, kb + i);
+      const double k2 = (double)ld_elem<BF16>(a.k_new, kb + i + kHalf);
       double s64, c64;
       sincos(rope_angle(a, pos0 + t, i), &s64, &c64);  // the reduced angle
-      b1 = storage_bits_from_f64<true>(k1 * c64 - k2 * s64);
-      b2 = storage_bits_from_f64<true>(k2 * c64 + k1 * s64);
+      b1 = storage_bits_from_f64<BF16>(k1 * c64 - k2 * s64);
+      b2 = storage_bits_from_f64<BF16>(k2 * c64 + k1 * s64);
     }
-    kn[t][i] = bits_to_float<true>(b1);
-    kn[t][i + kHalf] = bits_to_float<true>(b2);
-    vn[t][i] = bits_to_float<true>(v1);
-    vn[t][i + kHalf] = bits_to_float<true>(v2);
+    kn[t][i] = bits_to_float<BF16>(b1);
+    kn[t][i + kHalf] = bits_to_float<BF16>(b2);
+    vn[t][i] = bits_to_float<BF16>(v1);
+    vn[t][i + kHalf] = bits_to_float<BF16>(v2);
     if (wlive + t < wcap) {
       const int r = wlive + t;
       size_t row = ((size_t)u * wcap + r) * kHeadDim;
@@ -416,12 +416,21 @@ __device__ __forceinline__ void chunk_token_partial(const AttnArgs& a, ChunkShar
         row = ((((size_t)pid * a.num_kv_heads + h) << sh_) + (r & ((1 << sh_) - 1))) * kHeadDim;
       }
       if (store) {
-        uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
-        uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
-        kd[i] = (uint16_t)b1;
-        kd[i + kHalf] = (uint16_t)b2;
-        vd[i] = v1;
-        vd[i + kHalf] = v2;
+        if constexpr (BF16) {
+          uint16_t* kd = static_cast<uint16_t*>(a.k_store) + row;
+          uint16_t* vd = static_cast<uint16_t*>(a.v_store) + row;
+          kd[i] = (uint16_t)b1;
+          kd[i + kHalf] = (uint16_t)b2;
+          vd[i] = (uint16_t)v1;
+          vd[i + kHalf] = (uint16_t)v2;
+        } else {
+          uint32_t* kd = static_cast<uint32_t*>(a.k_store) + row;
+          uint32_t* vd = static_cast<uint32_t*>(a.v_store) + row;
+          kd[i] = b1;
+          kd[i + kHalf] = b2;
+          vd[i] = v1;
+          vd[i + kHalf] = v2;
+        }
       }
     }
   }

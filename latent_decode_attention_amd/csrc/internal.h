@@ -121,9 +121,9 @@ hipError_t launch_attention(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0
 // capacity-sized arrays or, with page tables in `a`, over page pools.
 hipError_t launch_ragged(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
-// A chunk of query tokens per sequence over a ragged cache (bf16; one
-// launch; see chunk_impl.h).
-hipError_t launch_chunk(AttnArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// A chunk of query tokens per sequence over a ragged cache (one launch;
+// bf16: chunk_impl.h, fp32 (dtype 0): chunk_f32_impl.h).
+hipError_t launch_chunk(AttnArgs a, int dtype, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 // Chunks per unit: the count in [1, kMaxChunks] whose workgroups fill the
 // device's slots best (no chunk under min_chunk_bytes).

@@ -189,6 +189,12 @@ def test_chunk(G, Q, r, rv, gpu_device):
           what=f"chunk G{G} Q{Q}")
 
 
+@pytest.mark.parametrize("page_rows", [0, 64])
+def test_chunk_fp32(page_rows, gpu_device):
+    check(small(dtype="fp32", B=4, G=4, nb=300, w=90, r=32, index=230 + page_rows), Q=3,
+          page_rows=page_rows, what=f"chunk fp32 pages {page_rows}")
+
+
 def test_chunk_without_new_tokens(gpu_device):
     check(small(B=4, nb=500, w=150, index=220), Q=4, append=False, what="chunk no tokens")
 

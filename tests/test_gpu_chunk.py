@@ -122,6 +122,28 @@ def test_single_token_matches_ragged_call(gpu_device):
     assert torch.equal(K_c, K_r) and torch.equal(V_c, V_r)
 
 
+# fp32 caches (the fp32 matrix-instruction kernel): the fp32 bar
+@pytest.mark.parametrize("G,Q,r,rv", [(4, 4, 64, None), (1, 16, 32, None), (8, 2, 128, None),
+                                      (5, 3, 48, 96)])
+def test_fp32(G, Q, r, rv, gpu_device):
+    wl = custom(dtype="fp32", B=5, Hkv=2, G=G, nb=300, w=70, r=r, index=160 + G * Q)
+    check_chunk(wl, Q, rank_v=rv, what=f"fp32 G{G} Q{Q} r{r}")
+
+
+def test_fp32_edges(gpu_device):
+    """fp32: raw rows only, beacons only, windows with room for part of the
+    chunk, a grid of one workgroup, no new tokens."""
+    wl = custom(dtype="fp32", B=6, Hkv=2, G=4, nb=0, w=100, index=166)
+    check_chunk(wl, 4, fixed={0: (0, 0), 1: (0, 100), 2: (0, 98)}, what="fp32 raw only")
+    wl = custom(dtype="fp32", B=4, Hkv=2, G=2, nb=300, w=0, r=96, index=167)
+    check_chunk(wl, 8, fixed={0: (0, 0), 1: (300, 0)}, what="fp32 beacons only")
+    wl = custom(dtype="fp32", B=5, Hkv=2, G=4, nb=200, w=60, index=168)
+    check_chunk(wl, 4, fixed={0: (200, 60), 1: (200, 58), 2: (0, 59), 3: (0, 0)}, num_splits=1,
+                what="fp32 full windows, one workgroup")
+    check_chunk(custom(dtype="fp32", B=4, Hkv=2, G=4, nb=250, w=50, index=169), 3, append=False,
+                what="fp32 no new tokens")
+
+
 @pytest.mark.parametrize("layer", [0, 6])  # ranks 48, 128
 def test_c3_chunk_sampled(layer, gpu_device):
     """The 128K Llama step's shapes with 4 drafted tokens per sequence (16

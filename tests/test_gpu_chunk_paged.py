@@ -116,6 +116,12 @@ def test_bitwise_equal_to_contiguous(gpu_device):
             assert torch.equal(V_p[pid, :, r], V_c[b, :, w + u])
 
 
+@pytest.mark.parametrize("page_rows", [64, 256])
+def test_fp32(page_rows, gpu_device):
+    wl = custom(dtype="fp32", B=5, Hkv=2, G=4, nb=400, w=150, r=48, index=250 + page_rows)
+    check(wl, 3, page_rows=page_rows, what=f"fp32 pages {page_rows}")
+
+
 def test_out_of_range_page_ids(gpu_device):
     """A table entry outside [0, pages) reads as a page of zeros and is never
     written: sequence 4's second beacon page is -1, and sequence 6's tokens'
