@@ -34,7 +34,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // lane (n, kg) then ends with columns 16t + 4kg .. +3 of row n for each
 // 16-column tile t -- the two halves of every rotation pair in one lane.
 // Each wave turns its 16 finished rows around in LDS, so that its stores
-// write whole rows, 16 bytes per lane (four rows per store).  The latent
+// write whole rows, 16 bytes per lane (four rows per store), with the
+// non-temporal policy.  The latent
 // rows of the next four sequences are in flight while one is multiplied.
 
 // Sine and cosine of pos * theta^(-2i/d) for pair i < 64 (see above).
@@ -180,7 +181,8 @@ __global__ __launch_bounds__(kThreads, 2) void rebuild_bf16_kernel(RebuildArgs a
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * i + (lane >> 4);
-          if (row0 + rr < nb) *reinterpret_cast<u32x4_t*>(Dw + (size_t)rr * kHeadDim) = ov[i];
+          if (row0 + rr < nb)  // streamed out (non-temporal): read once, by the next kernel
+            __builtin_nontemporal_store(ov[i], reinterpret_cast<u32x4_t*>(Dw + (size_t)rr * kHeadDim));
         }
       }
     }
