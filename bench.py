@@ -2,16 +2,18 @@
 """Decode-attention benchmark for libslimkv on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
-                    [--no-cpu-baseline] [--no-compare] [--graph]
+                    [--no-cpu-baseline] [--no-compare] [--launched]
 
 A step is one decode token's attention over every layer of the workload:
 for the default workload (Llama-3.1-8B shape, 128K context, 16x token
 compression, batch 16) that is 32 calls of slimkv_decode_attn, one per
 layer, each with its own latent rank.  All inputs are generated on the GPU
-before timing and stay resident in HBM.  The step's calls are launched back
-to back on one stream (checked bit for bit against the same calls captured
-once as a HIP graph and replayed; --graph times the replays instead, and
-the other form is reported beside the headline).  The timed region is bracketed by device
+before timing and stay resident in HBM.  The step's calls are captured once
+as a HIP graph and replayed, as a serving loop does to keep host overhead
+off the GPU's timeline (checked bit for bit against the same calls launched
+directly; --launched times those instead, and the other form is reported
+beside the headline).  Launched from Python, the calls are within 1-2% of
+the replays on a quiet host and up to 4% slower on a busy one.  The timed region is bracketed by device
 synchronisation and measured with events on the stream the library
 launches on, one event between consecutive steps, so the line carries the
 mean over the region and the median / p10 / p90 of the single steps.
@@ -73,10 +75,10 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--graph", action="store_true",
-                    help="time the step as one captured HIP graph per step instead of the calls "
-                         "launched directly (both are always checked bit for bit against each "
-                         "other, and the other one is reported beside the headline)")
+    ap.add_argument("--launched", action="store_true",
+                    help="time the step's calls launched directly instead of one captured HIP "
+                         "graph per step (both are always checked bit for bit against each other, "
+                         "and the other one is reported beside the headline)")
     ap.add_argument("--ragged", action="store_true",
                     help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
                          "of the capacities, new token stored) and print its figures as one JSON line")
@@ -102,9 +104,34 @@ def parse_args():
                          "needed)")
     ap.add_argument("--profile-summary", metavar="DIR", default="",
                     help="summarise the rocprofv3 kernel trace (*kernel_trace.csv) under DIR and "
-                         "print it as JSON (no GPU needed): the attention kernel's last "
-                         "--steps x layers dispatches of --workload (the timed steps of a bench "
-                         "run with the same --steps), per layer and per step")
+                         "print it as JSON (no GPU needed): the attention kernel's dispatches "
+                         "in the headline's timed steps of a bench run of --workload with the "
+                         "same --steps, per layer and per step")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    default=None,
+                    help="summarise rocprofv3 --pmc runs (*counter_collection.csv under each "
+                         "directory): FETCH_SIZE and WRITE_SIZE of a bench run of --workload "
+                         "with the same --steps, and of 'bench.py --calibrate', which gives the "
+                         "scale from counter units to bytes (no GPU needed)")
+    ap.add_argument("--kernel", default="attention_kernel",
+                    help="with --profile-summary or --traffic-summary: the kernel to summarise; "
+                         "other than attention_kernel, every dispatch of it, per instance")
+    ap.add_argument("--record", metavar="NAME", default="",
+                    help="with --profile-summary or --traffic-summary: also write "
+                         "profiles/NAME.json (read by the bench for the same kernel sources) "
+                         "and profiles/NAME.md")
+    ap.add_argument("--run-json", nargs="+", metavar="JSON", default=[],
+                    help="with --profile-summary (one file) or --traffic-summary (two: the FETCH "
+                         "and the WRITE run): the JSON line each profiled bench run printed, for "
+                         "its warm-up step counts")
+    ap.add_argument("--label", default="",
+                    help="with --record and --kernel other than attention_kernel: the run's "
+                         "workload, in words")
+    ap.add_argument("--untraced", metavar="JSON", default="",
+                    help="with --record: the bench JSON line of the same command run without "
+                         "the profiler on the same box, quoted beside the trace")
+    ap.add_argument("--command", metavar="TEXT", nargs="+", default=None,
+                    help="with --record: the commands that made the profile, for the summary")
     return ap.parse_args()
 
 
@@ -152,13 +179,33 @@ def pct(xs):
     return float(p50), float(p10), float(p90)
 
 
-def timed_steps(torch, run, steps, warmup):
-    """Run ``run`` warmup times, then ``steps`` times back to back with an
-    event recorded before the first and after every step, all on the
-    current stream.  Returns (mean ms over the whole region, per-step ms)."""
+WARM_MIN_S = 0.1  # untimed warm-up before every timed region lasts at least this long
+
+
+def timed_steps(torch, run, steps, warmup, info=None):
+    """Run ``run`` warmup times -- and on, in groups of 4, until the warm-up
+    has lasted WARM_MIN_S of wall time -- then ``steps`` times back to back
+    with an event recorded before the first and after every step, all on the
+    current stream.  Returns (mean ms over the whole region, per-step ms).
+
+    The floor on the warm-up's length: after the GPU has been idle (input
+    generation, graph capture, host work between measurements) its first
+    ~15 ms of streaming run up to 15% slower (kernel traces of the c3 step
+    show ~6 slow steps after an idle gap, whichever launch form), so a
+    fixed count of short warm-up steps would leave part of that ramp inside
+    the timed region.  info (a dict): receives the warm-up steps run."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    n = warmup
+    while time.perf_counter() - t0 < WARM_MIN_S:
+        for _ in range(4):
+            run()
+        n += 4
+        torch.cuda.synchronize()
+    if info is not None:
+        info["warmup_steps"] = n
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
@@ -190,10 +237,20 @@ def main():
     if args.report:
         print(report(args.report), end="")
         return
-    if args.profile_summary:
+    if args.profile_summary or args.traffic_summary:
         import synth
-        print(json.dumps(profile_summary(args.profile_summary, synth.get_workload(args.workload),
-                                         args.steps)), flush=True)
+        wl = synth.get_workload(args.workload)
+        if args.kernel != "attention_kernel":
+            summ = (instance_trace_summary(args.profile_summary, args.kernel) if args.profile_summary
+                    else instance_traffic_summary(*args.traffic_summary, args.kernel))
+        elif args.profile_summary:
+            summ = profile_summary(args.profile_summary, wl, args.steps, other_warm(args.run_json, 0))
+        else:
+            summ = traffic_summary(*args.traffic_summary, wl, args.steps,
+                                   (other_warm(args.run_json, 0), other_warm(args.run_json, 1)))
+        if args.record:
+            write_record(args.record, summ, args)
+        print(json.dumps(summ), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build runs "
@@ -242,9 +299,8 @@ def main():
             lda.slimkv_decode_attn(p, x.q, x.q_pos, x.U_K, x.U_V, x.C_K, x.C_V, x.K_raw, x.V_raw,
                                    out, lse, ws)
 
-    log(f"warmup {args.warmup} steps, timing {args.steps}")
-    for _ in range(args.warmup):
-        step()
+    log(f"warmup {args.warmup} steps (and at least {WARM_MIN_S * 1e3:.0f} ms), timing {args.steps}")
+    step()
     torch.cuda.synchronize()
     # The step's calls have no host work between them: they are launched
     # back to back on one stream (what a native serving loop does), or
@@ -264,12 +320,13 @@ def main():
         raise RuntimeError("graph replay differs from the launched step")
     modes = {"launched": (step, f"{wl.layers} calls launched back to back on one stream"),
              "graph": (graph.replay, f"one captured HIP graph per step ({wl.layers} calls)")}
-    head, other = ("graph", "launched") if args.graph else ("launched", "graph")
+    head, other = ("launched", "graph") if args.launched else ("graph", "launched")
     run, launch = modes[head]
     t0 = time.perf_counter()
-    ms_step, per_step = timed_steps(torch, run, args.steps, 0)
+    warm_head, warm_other = {}, {}
+    ms_step, per_step = timed_steps(torch, run, args.steps, args.warmup, warm_head)
     wall = time.perf_counter() - t0
-    ms_other, per_other = timed_steps(torch, modes[other][0], args.steps, 2)
+    ms_other, per_other = timed_steps(torch, modes[other][0], args.steps, 2, warm_other)
     tokens_per_s = wl.batch / (ms_step * 1e-3)
     total_step = sum(layer_call_bytes(wl, layer, elem)[1] for layer in range(wl.layers))
     step_gbps = total_step / (ms_step * 1e-3) / 1e9
@@ -286,7 +343,7 @@ def main():
     achieved = kern_bytes / (kern_us * 1e-6) / 1e9
     log(f"attention kernel: {kern_us:.2f} us average over {launches} launches, "
         f"{achieved:.0f} GB/s ({achieved / HBM_PEAK_GBPS:.4f} of peak)")
-    traffic = committed_record("attention_kernel_c3_traffic.json", wl.name)
+    traffic = committed_record(f"attention_kernel_{args.workload}_traffic.json", wl.name)
     prof = committed_record(f"attention_kernel_{args.workload}_trace.json", wl.name)
     roofline = {
         "bound": "hbm",
@@ -315,6 +372,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": {"headline": warm_head["warmup_steps"], "other": warm_other["warmup_steps"],
+                             "floor_ms": WARM_MIN_S * 1e3},
         "ms_per_step": round(ms_step, 4),
         "median_ms_per_step": stats["median_ms"],
         "p10_ms_per_step": stats["p10_ms"],
@@ -969,12 +1028,32 @@ def report(paths):
 # ---------------------------------------------------------------------------
 # rocprofv3 kernel-trace summary.
 
-def profile_summary(directory, wl, steps):
-    """The attention kernel's dispatches in a rocprofv3 kernel trace (CSV):
-    the last steps x layers of them (the timed steps; within a step the
-    dispatches follow the layers in order, so dispatch i of a step is layer
-    i and its algorithmic bytes are known).  Durations are End - Start of
-    each dispatch, in us; every other kernel is listed with its totals."""
+def kernel_name(full):
+    """A trace's kernel name without its parameter list and return type."""
+    anon = "(anonymous namespace)"
+    name = full.replace(anon, "\x00").split("(")[0].replace("\x00", anon)
+    return name[5:] if name.startswith("void ") else name
+
+
+def headline_dispatches(items, wl, steps, other_warm=2):
+    """The attention dispatches of the headline's timed steps in a bench run
+    with --no-compare --no-cpu-baseline (in launch order): after them the
+    bench times the other launch form, ``other_warm`` warm-up steps (its
+    JSON line's warmup_steps_run.other) and ``steps`` steps, which are
+    skipped.  Within a step the dispatches follow the layers in order, so
+    dispatch i of a step is layer i and its bytes are known."""
+    n, other = steps * wl.layers, (steps + other_warm) * wl.layers
+    if len(items) < n + other:
+        raise SystemExit(f"{len(items)} attention dispatches, fewer than the {n} timed and "
+                         f"{other} after them that a bench run with --steps {steps} makes")
+    return items[len(items) - other - n:len(items) - other]
+
+
+def profile_summary(directory, wl, steps, other_warm=2):
+    """The attention kernel's dispatches in a rocprofv3 kernel trace (CSV)
+    of the headline's timed steps (headline_dispatches).  Durations are End -
+    Start of each dispatch, in us; every other kernel is listed with its
+    totals."""
     import csv
 
     import numpy as np
@@ -986,13 +1065,11 @@ def profile_summary(directory, wl, steps):
         with open(f, newline="") as fh:
             for row in csv.DictReader(fh):
                 rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
-                             row["Kernel_Name"].split("(")[0]))
+                             kernel_name(row["Kernel_Name"])))
     rows.sort()
     att = [r for r in rows if "attention_kernel" in r[2]]
-    n = steps * wl.layers
-    if len(att) < n:
-        raise SystemExit(f"{len(att)} attention dispatches, fewer than {steps} x {wl.layers}")
-    last = att[-n:]
+    last = headline_dispatches(att, wl, steps, other_warm)
+    n = len(last)
     dur = np.array([(e - s) / 1e3 for s, e, _ in last]).reshape(steps, wl.layers)
     elem = wl.elem_bytes
     per_layer = []
@@ -1022,14 +1099,266 @@ def profile_summary(directory, wl, steps):
             o = others.setdefault(name[:80], [0, 0.0])
             o[0] += 1
             o[1] += (e - s) / 1e3
-    return {"workload": wl.name, "steps": steps, "dispatches": n,
+    return {"kind": "kernel_trace", "kernel": "attention_kernel", "workload": wl.name,
+            "steps": steps, "dispatches": n,
             "launch_us": round(launch_us, 3), "gbps": round(gbps, 1),
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": int(mean_bytes),
             "kernel_sum_per_step_us": round(float(step_sum.mean()), 1),
+            "traced_step_ms": round(span / 1e3, 4),
             "first_start_to_last_end_per_step_us": round(span, 1),
             "per_rank": ranks, "per_layer": per_layer,
             "other_kernels": {k: {"calls": v[0], "sum_us": round(v[1], 1)} for k, v in others.items()},
             "files": [os.path.relpath(f, directory) for f in files]}
+
+
+def read_counters(directory):
+    """Per dispatch of a rocprofv3 --pmc run (*counter_collection.csv under
+    directory): (dispatch id, kernel name, {counter: value}), in dispatch
+    order."""
+    import csv
+    files = sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                             recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {directory}")
+    by = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                d = by.setdefault(int(row["Dispatch_Id"]), [kernel_name(row["Kernel_Name"]), {}])
+                d[1][row["Counter_Name"]] = d[1].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return [(k, v[0], v[1]) for k, v in sorted(by.items())]
+
+
+def calibration_scales(cal_fetch_dir, cal_write_dir):
+    """Bytes per counter KiB: FETCH_SIZE of the library's plain read kernel
+    over 1 GiB - 16 bytes and WRITE_SIZE of its write kernel over 1 GiB
+    (bench.py --calibrate), medians over their dispatches; and the FETCH_SIZE
+    of the torch copy of 1 GiB (a cross-check)."""
+    import numpy as np
+    cal_f = [(n, c["FETCH_SIZE"]) for _, n, c in read_counters(cal_fetch_dir) if "FETCH_SIZE" in c]
+    cal_w = [(n, c["WRITE_SIZE"]) for _, n, c in read_counters(cal_write_dir) if "WRITE_SIZE" in c]
+
+    def median_of(rows, key):
+        vals = [v for name, v in rows if key in name]
+        if not vals:
+            raise SystemExit(f"no calibration dispatch named *{key}*")
+        return float(np.median(vals))
+    gib = 1 << 30
+    copy_f = [v for name, v in cal_f if "stream_read" not in name and "flush" not in name]
+    return ((gib - 16) / (median_of(cal_f, "stream_read_kernel") * 1024),
+            gib / (median_of(cal_w, "flush_kernel") * 1024),
+            float(np.median(copy_f)) if copy_f else None)
+
+
+def instance_trace_summary(directory, kernel):
+    """Every dispatch of ``kernel`` in a rocprofv3 kernel trace, per
+    instance: calls, mean / min / max duration in us."""
+    import csv
+
+    import numpy as np
+    files = sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {directory}")
+    by = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                name = kernel_name(row["Kernel_Name"])
+                if kernel in name:
+                    by.setdefault(name, []).append(
+                        (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    if not by:
+        raise SystemExit(f"no dispatch of {kernel} under {directory}")
+    inst = {k: {"calls": len(v), "avg_us": round(float(np.mean(v)), 2),
+                "min_us": round(float(np.min(v)), 2), "max_us": round(float(np.max(v)), 2)}
+            for k, v in sorted(by.items())}
+    allv = [x for v in by.values() for x in v]
+    return {"kind": "instance_trace", "kernel": kernel, "workload": "",
+            "dispatches": len(allv), "launch_us": round(float(np.mean(allv)), 2), "instances": inst,
+            "files": [os.path.relpath(f, directory) for f in files]}
+
+
+def instance_traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel):
+    """FETCH_SIZE and WRITE_SIZE of every dispatch of ``kernel``, per
+    instance, scaled to bytes by calibration_scales."""
+    import numpy as np
+    rs, ws_, copy_kib = calibration_scales(cal_fetch_dir, cal_write_dir)
+    by = {}
+    for counter, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for _, name, c in read_counters(directory):
+            if kernel in name and counter in c:
+                by.setdefault(name, {}).setdefault(counter, []).append(c[counter])
+    if not by:
+        raise SystemExit(f"no counters for {kernel}")
+    inst = {}
+    rd_all, wr_all = [], []
+    for name, c in sorted(by.items()):
+        f, w = c.get("FETCH_SIZE", [0.0]), c.get("WRITE_SIZE", [0.0])
+        rd_all += [x * 1024 * rs for x in f]
+        wr_all += [x * 1024 * ws_ for x in w]
+        inst[name] = {"dispatches": len(f), "fetch_kib": round(float(np.mean(f)), 1),
+                      "write_kib": round(float(np.mean(w)), 1),
+                      "read_mb": round(float(np.mean(f)) * 1024 * rs / 1e6, 2),
+                      "write_mb": round(float(np.mean(w)) * 1024 * ws_ / 1e6, 2)}
+    return {"kind": "instance_traffic", "kernel": kernel, "workload": "", "fetch_scale": round(rs, 4),
+            "write_scale": round(ws_, 4),
+            "copy_fetch_kib_per_gib": round(copy_kib, 1) if copy_kib else None,
+            "read_bytes_per_launch": int(np.mean(rd_all)), "write_bytes_per_launch": int(np.mean(wr_all)),
+            "traffic_bytes_per_launch": int(np.mean(rd_all) + np.mean(wr_all)), "instances": inst}
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, wl, steps, other_warm=(2, 2)):
+    """HBM bytes of the attention kernel from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, one counter per run), each scaled by what the same
+    counter reads for the calibration kernels of known size (bench.py
+    --calibrate: the library's plain read kernel for reads, its flush kernel
+    for writes; the torch copy is a cross-check).  The dispatches are the
+    headline's timed steps (headline_dispatches), so each one's layer and
+    algorithmic bytes are known."""
+    import numpy as np
+
+    def one(directory, counter):
+        return [(name, c[counter]) for _, name, c in read_counters(directory) if counter in c]
+
+    read_scale, write_scale, copy_kib = calibration_scales(cal_fetch_dir, cal_write_dir)
+    fetch = headline_dispatches([r for r in one(fetch_dir, "FETCH_SIZE") if "attention_kernel" in r[0]],
+                                wl, steps, other_warm[0])
+    write = headline_dispatches([r for r in one(write_dir, "WRITE_SIZE") if "attention_kernel" in r[0]],
+                                wl, steps, other_warm[1])
+    elem = wl.elem_bytes
+    per_rank = {}
+    rd_all, wr_all, alg_all = [], [], []
+    for i, ((name, f), (_, w)) in enumerate(zip(fetch, write)):
+        layer = i % wl.layers
+        alg = layer_call_bytes(wl, layer, elem)[1]
+        rd, wr = f * 1024 * read_scale, w * 1024 * write_scale
+        rd_all.append(rd)
+        wr_all.append(wr)
+        alg_all.append(alg)
+        e = per_rank.setdefault(str(wl.ranks[layer]), {"kernel": name, "dispatches": 0, "fetch_kib": [],
+                                                        "write_kib": [], "alg": alg})
+        e["dispatches"] += 1
+        e["fetch_kib"].append(f)
+        e["write_kib"].append(w)
+    ranks = {}
+    for r, e in sorted(per_rank.items(), key=lambda x: int(x[0])):
+        fk, wk = float(np.mean(e["fetch_kib"])), float(np.mean(e["write_kib"]))
+        ranks[r] = {"kernel": e["kernel"], "dispatches": e["dispatches"], "fetch_kib": round(fk, 1),
+                    "write_kib": round(wk, 1), "read_mb": round(fk * 1024 * read_scale / 1e6, 2),
+                    "write_mb": round(wk * 1024 * write_scale / 1e6, 2),
+                    "algorithmic_mb": round(e["alg"] / 1e6, 2),
+                    "read_over_algorithmic": round(fk * 1024 * read_scale / e["alg"], 4)}
+    traffic = float(np.mean(rd_all) + np.mean(wr_all))
+    alg = float(np.mean(alg_all))
+    return {"kind": "pmc_traffic", "kernel": "attention_kernel", "workload": wl.name, "steps": steps,
+            "dispatches": len(fetch), "fetch_scale": round(read_scale, 4),
+            "write_scale": round(write_scale, 4),
+            "copy_fetch_kib_per_gib": round(copy_kib, 1) if copy_kib else None,
+            "traffic_bytes_per_launch": int(traffic), "read_bytes_per_launch": int(np.mean(rd_all)),
+            "write_bytes_per_launch": int(np.mean(wr_all)), "algorithmic_bytes_per_launch": int(alg),
+            "traffic_over_algorithmic": round(traffic / alg, 4), "per_rank": ranks}
+
+
+def other_warm(files, i):
+    """Warm-up steps of the other launch form in the profiled run whose
+    JSON line is files[i] (2, the count before the warm-up had a time floor,
+    if not given)."""
+    if i >= len(files):
+        return 2
+    with open(files[i]) as fh:
+        line = json.loads(fh.read().strip().splitlines()[-1])
+    return int(line.get("warmup_steps_run", {}).get("other", 2))
+
+
+def write_record(name, summ, args):
+    """profiles/NAME.json (the summary, stamped with the kernel sources'
+    sha256) and profiles/NAME.md (the same as a table, with the commands)."""
+    rec = dict(summ)
+    rec["source_sha256"] = source_sha256()
+    rec["commands"] = args.command or []
+    untraced = None
+    if args.untraced:
+        with open(args.untraced) as fh:
+            untraced = json.loads(fh.read().strip().splitlines()[-1])
+        rec["untraced"] = {k: untraced.get(k) for k in ("ms_per_step", "median_ms_per_step",
+                                                         "value", "unit")}
+        rec["untraced"]["launch_us"] = untraced.get("roofline", {}).get("launch_us")
+    rec["summary"] = f"profiles/{name}.md"
+    if not rec["workload"]:
+        rec["workload"] = args.label or args.record
+    out = pathlib.Path(ROOT) / "profiles"
+    (out / f"{name}.json").write_text(json.dumps(rec, indent=1) + "\n")
+    kind = rec["kind"]
+    lines = [f"# {rec['kernel']} on {rec['workload']}: "
+             + ("kernel trace" if kind.endswith("trace") else "HBM traffic (PMC)"), ""]
+    lines += ["Commands (repository root, MI355X):", ""]
+    lines += [f"    {c}" for c in rec["commands"]] + [""]
+    lines += [f"Kernel source sha256 (latent_decode_attention_amd/csrc): `{rec['source_sha256']}`", ""]
+    if kind == "instance_trace":
+        lines += [f"Every dispatch of {rec['kernel']} in the run ({rec['dispatches']}), per instance.",
+                  "", "| kernel instance | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for k, e in rec["instances"].items():
+            lines.append(f"| {k} | {e['calls']} | {e['avg_us']} | {e['min_us']} | {e['max_us']} |")
+        lines += ["", f"Average over all dispatches: **{rec['launch_us']} us**."]
+        if untraced:
+            lines += ["", "The same command without the profiler on the same box: "
+                      + json.dumps({k: v for k, v in untraced.items()
+                                    if k in ("ms_per_step", "median_ms", "us_per_layer", "gbps",
+                                             "frac_of_peak", "live_rows", "tokens_per_chunk")})]
+    elif kind == "instance_traffic":
+        lines += [f"Scale from counter units to bytes: reads x{rec['fetch_scale']}, writes "
+                  f"x{rec['write_scale']} (bench.py --calibrate).", "",
+                  "| kernel instance | dispatches | FETCH KiB | WRITE KiB | read MB | write MB |",
+                  "|---|---|---|---|---|---|"]
+        for k, e in rec["instances"].items():
+            lines.append(f"| {k} | {e['dispatches']} | {e['fetch_kib']} | {e['write_kib']} | "
+                         f"{e['read_mb']} | {e['write_mb']} |")
+        lines += ["", f"Per dispatch over the run: read {rec['read_bytes_per_launch'] / 1e6:.1f} MB + "
+                  f"write {rec['write_bytes_per_launch'] / 1e6:.2f} MB."]
+        if untraced and untraced.get("gbps") and untraced.get("us_per_layer"):
+            live = untraced["gbps"] * untraced["us_per_layer"] * 1e3
+            lines += [f"The step's algorithmic (live) bytes per layer, from the untraced run: "
+                      f"{live / 1e6:.1f} MB; measured / algorithmic = "
+                      f"{rec['traffic_bytes_per_launch'] / live:.3f}."]
+            rec["algorithmic_bytes_per_launch"] = int(live)
+            (out / f"{name}.json").write_text(json.dumps(rec, indent=1) + "\n")
+    elif kind == "kernel_trace":
+        lines += [f"{rec['dispatches']} dispatches: the headline's {rec['steps']} timed steps x "
+                  f"{rec['dispatches'] // rec['steps']} layers.", "",
+                  "| ranks | kernel instance | layers | avg us | algorithmic MB/launch | GB/s |",
+                  "|---|---|---|---|---|---|"]
+        for r, e in rec["per_rank"].items():
+            lines.append(f"| {r} | {e['kernel']} | {e['layers']} | {e['avg_us']} | "
+                         f"{e['bytes'] / 1e6:.1f} | {e['gbps']} |")
+        lines += ["", f"Average over the step's layers: **{rec['launch_us']} us per launch**, "
+                  f"{rec['bytes_per_launch'] / 1e6:.1f} MB algorithmic -> {rec['gbps']} GB/s = "
+                  f"**{100 * rec['frac']:.2f}% of 8 TB/s**.",
+                  f"Per step: kernel durations sum to {rec['kernel_sum_per_step_us']} us; first "
+                  f"start to last end {rec['first_start_to_last_end_per_step_us']} us."]
+        if untraced:
+            lines += ["", f"The same command without the profiler on the same box: "
+                      f"{untraced.get('ms_per_step')} ms per step (events over the timed region, "
+                      f"gaps between launches included), {rec['untraced']['launch_us']} us per "
+                      f"launch. The traced kernel sum per step is "
+                      f"{rec['kernel_sum_per_step_us'] / 1e3 / untraced.get('ms_per_step'):.3f} "
+                      f"of that step."]
+    else:
+        lines += [f"Scale from counter units to bytes: reads x{rec['fetch_scale']} (the library's "
+                  f"plain read kernel over 1 GiB), writes x{rec['write_scale']} (its write kernel over "
+                  f"1 GiB); a torch copy of 1 GiB reads {rec['copy_fetch_kib_per_gib']} KiB of "
+                  f"FETCH_SIZE.", "",
+                  "| ranks | kernel instance | dispatches | FETCH KiB | WRITE KiB | read MB | write MB | "
+                  "algorithmic MB | read / algorithmic |", "|---|---|---|---|---|---|---|---|---|"]
+        for r, e in rec["per_rank"].items():
+            lines.append(f"| {r} | {e['kernel']} | {e['dispatches']} | {e['fetch_kib']} | "
+                         f"{e['write_kib']} | {e['read_mb']} | {e['write_mb']} | "
+                         f"{e['algorithmic_mb']} | {e['read_over_algorithmic']} |")
+        lines += ["", f"Per launch over the step's layers: read {rec['read_bytes_per_launch'] / 1e6:.1f} "
+                  f"MB + write {rec['write_bytes_per_launch'] / 1e6:.2f} MB = "
+                  f"**{rec['traffic_bytes_per_launch'] / 1e6:.1f} MB**, against "
+                  f"{rec['algorithmic_bytes_per_launch'] / 1e6:.1f} MB algorithmic "
+                  f"({rec['traffic_over_algorithmic']}x)."]
+    (out / f"{name}.md").write_text("\n".join(lines) + "\n")
 
 
 if __name__ == "__main__":

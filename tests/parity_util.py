@@ -183,26 +183,40 @@ def ragged_edge_cases(nb, w):
     return {0: (0, 0), 1: (nb, w), 2: (nb + 7, -5), 3: (1, 1)}
 
 
+def plant_counters(ws, units, value=3):
+    """Write ``value`` into every unit's counters (they follow the
+    workspace's 256-byte header, 16 uint32 per unit), as a call that did not
+    run to its end could leave them."""
+    ws[256:256 + 64 * units].view(torch.int32).view(units, 16)[:, :2] = value
+
+
 def run_gpu_ragged(inp: synth.LayerInputs, step: synth.StepInputs, *, append: bool = True,
-                   lengths: bool = True, num_splits: int = 0, device="cuda"):
+                   lengths: bool = True, num_splits: int = 0, device="cuda", flags: int = 0,
+                   plant=None, status=None):
     """slimkv_decode_attn_ragged on ``inp`` (capacity-sized arrays) and
     ``step``.  The raw cache is cloned first (the call writes the new rows);
-    returns (out, lse, K_raw, V_raw) on the host."""
+    returns (out, lse, K_raw, V_raw) on the host.  plant(ws): applied to the
+    zero-filled workspace before the call; status (a list): receives the
+    workspace's status word after it."""
     wl = inp.workload
     g = inp.to(device)
     st = step.to(device)
     K, V = g.K_raw.clone(), g.V_raw.clone()
     prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
                                     rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
-                                    scale=wl.scale, num_splits=num_splits)
+                                    scale=wl.scale, num_splits=num_splits, flags=flags)
     out, lse = lda.alloc_outputs(prob, device)
     ws = lda.alloc_workspace(prob, lda.SLIMKV_OP_LATENT_RAGGED, device)
+    if plant is not None:
+        plant(ws)
     lda.slimkv_decode_attn_ragged(prob, g.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, K, V,
                                   st.num_beacons if lengths else None,
                                   st.raw_len if lengths else None,
                                   st.k_new if append else None, st.v_new if append else None,
                                   out, lse, ws)
     torch.cuda.synchronize()
+    if status is not None:
+        status.append(lda.slimkv_workspace_status(ws))
     return (out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu())
 
 
@@ -379,10 +393,12 @@ def assert_paged_writes(K_after, V_after, pc: synth.PagedCache, step, k_app, wca
 
 
 def run_gpu_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool = True,
-                  lengths: bool = True, num_splits: int = 0, device="cuda"):
+                  lengths: bool = True, num_splits: int = 0, device="cuda", flags: int = 0,
+                  plant=None, status=None):
     """slimkv_decode_attn_chunk on ``inp`` (capacity-sized arrays) and the
     chunk ``ch``; the raw cache is cloned first.  Returns (out [B, Q, H_q, d],
-    lse [B, Q, H_q], K_raw, V_raw) on the host."""
+    lse [B, Q, H_q], K_raw, V_raw) on the host.  plant, status: as for
+    run_gpu_ragged."""
     wl = inp.workload
     g = inp.to(device)
     c = ch.to(device)
@@ -390,17 +406,21 @@ def run_gpu_chunk(inp: synth.LayerInputs, ch: synth.ChunkInputs, *, append: bool
     K, V = g.K_raw.clone(), g.V_raw.clone()
     prob = lda.problem_from_tensors(g.q, g.U_K, g.C_K, g.K_raw, U_V=g.U_V,
                                     rope_theta=wl.rope_theta, num_kv_heads=wl.num_kv_heads,
-                                    scale=wl.scale, num_splits=num_splits)
+                                    scale=wl.scale, num_splits=num_splits, flags=flags)
     B, Hq, d = g.q.shape
     out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device=device)
     lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=device)
     ws = torch.zeros(lda.slimkv_chunk_workspace_bytes(prob, Q), dtype=torch.uint8, device=device)
+    if plant is not None:
+        plant(ws)
     lda.slimkv_decode_attn_chunk(prob, Q, c.q, g.q_pos, g.U_K, g.U_V, g.C_K, g.C_V, K, V,
                                  c.num_beacons if lengths else None,
                                  c.raw_len if lengths else None,
                                  c.k_new if append else None, c.v_new if append else None,
                                  out, lse, ws)
     torch.cuda.synchronize()
+    if status is not None:
+        status.append(lda.slimkv_workspace_status(ws))
     return out.double().cpu().numpy(), lse.double().cpu().numpy(), K.cpu(), V.cpu()
 
 

@@ -165,3 +165,23 @@ def test_c3_chunk_sampled(layer, gpu_device):
     assert_chunk_rows(K, V, inp.K_raw, inp.V_raw, ch, {u: ref[u][2] for u in units}, units=units)
     del inp, K, V
     torch.cuda.empty_cache()
+
+
+def test_workspace_check_flag(gpu_device):
+    """SLIMKV_FLAG_CHECK_WORKSPACE on a chunk call: counters left nonzero are
+    found, cleared and reported; the result is still right."""
+    import latent_decode_attention_amd as lda
+    from parity_util import plant_counters
+    wl = custom(B=5, Hkv=2, G=4, nb=400, w=100, index=170)
+    inp = synth.make_layer(wl)
+    ch = synth.make_chunk(wl, inp, 3, fixed=edge_cases(inp.num_beacons, inp.raw_window))
+    note("chunk workspace check, planted counters")
+    status = []
+    out, lse, _, _ = run_gpu_chunk(inp, ch, num_splits=9, flags=lda.SLIMKV_FLAG_CHECK_WORKSPACE,
+                                   plant=lambda ws: plant_counters(ws, wl.batch * wl.num_kv_heads),
+                                   status=status)
+    ref, ref_lse, _ = oracle_chunk(inp, ch)
+    empty = np.isneginf(ref_lse)
+    assert_parity(out, ref, wl.dtype, "chunk workspace check",
+                  np.where(empty, 0.0, lse), np.where(empty, 0.0, ref_lse))
+    assert status == [1]

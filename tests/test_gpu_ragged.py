@@ -129,3 +129,25 @@ def test_large_batches(B, splits, gpu_device):
     wl = custom(B=B, Hkv=1, G=4, nb=64, w=40, r=32, index=105 + B % 7)
     fixed = {0: (0, 0), 1: (64, 40), B - 1: (70, -3), B // 2: (1, 0)}
     check_ragged(wl, num_splits=splits, fixed=fixed, what=f"B={B} splits={splits}")
+
+
+@pytest.mark.parametrize("planted", [False, True])
+def test_workspace_check_flag(planted, gpu_device):
+    """SLIMKV_FLAG_CHECK_WORKSPACE on a ragged call: counters left nonzero (as
+    by an interrupted call) are found, cleared and reported, and the result
+    is still right; a clean workspace reports nothing."""
+    import latent_decode_attention_amd as lda
+    from parity_util import plant_counters
+    wl = custom(B=6, Hkv=2, G=4, nb=500, w=120, index=180 + planted)
+    inp = synth.make_layer(wl)
+    step = synth.make_step(wl, inp, fixed=edge_cases(inp.num_beacons, inp.raw_window))
+    note(f"ragged workspace check, planted={planted}")
+    status = []
+    out, lse, _, _ = run_gpu_ragged(inp, step, num_splits=7, flags=lda.SLIMKV_FLAG_CHECK_WORKSPACE,
+                                    plant=(lambda ws: plant_counters(ws, wl.batch * wl.num_kv_heads))
+                                    if planted else None, status=status)
+    ref, ref_lse, _ = oracle_ragged(inp, step)
+    empty = np.isneginf(ref_lse)
+    assert_parity(out, ref, wl.dtype, f"workspace check planted={planted}",
+                  np.where(empty, 0.0, lse), np.where(empty, 0.0, ref_lse))
+    assert status == [1 if planted else 0]
