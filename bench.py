@@ -957,7 +957,7 @@ def report(paths):
                        f"{rf.get('achieved')} GB/s, **{100 * rf.get('frac', 0):.1f}% of peak** |")
             rp = rf.get("rocprof")
             if rp:
-                out.append(f"| same, rocprofv3 kernel trace (`profiles/{rp.get('summary')}`) | "
+                out.append(f"| same, rocprofv3 kernel trace (`{rp.get('summary')}`) | "
                            f"{rp.get('launch_us')} us, {100 * rp.get('frac', 0):.1f}% of peak |")
             else:
                 out.append("| same, rocprofv3 kernel trace | no committed trace for these kernel "
@@ -1022,6 +1022,12 @@ def report(paths):
                            f"{v.get('us_per_layer')} | {rate} | {v.get('gbps')} | "
                            f"{100 * v.get('frac_of_peak', 0):.1f} |")
             out.append("")
+    # the lines themselves, so that the report can be checked (and remade
+    # with --report from a file holding one of them)
+    out += ["## Source lines", ""]
+    for path in paths:
+        r, note = _load_result(path)
+        out += [f"{note}:", "", "```json", json.dumps(r), "```", ""]
     return "\n".join(out) + "\n"
 
 
