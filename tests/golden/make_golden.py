@@ -46,6 +46,12 @@ CASES = {
                           dict(tokens=2, fixed={0: (5, 3), 1: (1, 6)})),
     "decode_alibi_bf16": ("decode_alibi", dict(dtype="bf16", B=2, Hkv=1, G=2, nb=6, w=4, r=16,
                                                context=200, index=403), dict(ratio=16)),
+    "decode_chunk_fp32": ("decode_chunk", dict(dtype="fp32", B=2, Hkv=1, G=2, nb=4, w=5, r=16,
+                                               context=4096, index=404),
+                          dict(tokens=3, fixed={0: (4, 2), 1: (0, 5)})),
+    "decode_chunk_alibi_bf16": ("decode_chunk_alibi", dict(dtype="bf16", B=2, Hkv=1, G=2, nb=6,
+                                                           w=5, r=16, context=300, index=405),
+                                dict(tokens=2, ratio=16, fixed={0: (6, 3), 1: (2, 5)})),
 }
 
 
@@ -74,6 +80,16 @@ def run_case(name):
         ch = synth.make_chunk(wl, inp, extra["tokens"], fixed=extra["fixed"])
         out, lse, k_app = oracle.decode_chunk(
             st(ch.q), st(inp.q_pos), *common, rope_theta=wl.rope_theta,
+            num_beacons=st(ch.num_beacons), raw_len=st(ch.raw_len), k_new=st(ch.k_new),
+            v_new=st(ch.v_new), **kw)
+        res = dict(out=out, lse=lse, k_app=k_app)
+    elif entry == "decode_chunk_alibi":
+        ch = synth.make_chunk(wl, inp, extra["tokens"], fixed=extra["fixed"])
+        first, stride = synth.beacon_grid(extra["ratio"])
+        slopes = synth.alibi_slopes(wl.num_q_heads).astype(np.float32).astype(np.float64)
+        out, lse, k_app = oracle.decode_chunk_alibi(
+            st(ch.q), st(inp.q_pos), *common,
+            beacon_pos=(first + stride * np.arange(nb)).astype(np.int32), slopes=slopes,
             num_beacons=st(ch.num_beacons), raw_len=st(ch.raw_len), k_new=st(ch.k_new),
             v_new=st(ch.v_new), **kw)
         res = dict(out=out, lse=lse, k_app=k_app)
