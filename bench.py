@@ -124,6 +124,9 @@ def parse_args():
                     help="with --profile-summary (one file) or --traffic-summary (two: the FETCH "
                          "and the WRITE run): the JSON line each profiled bench run printed, for "
                          "its warm-up step counts")
+    ap.add_argument("--algorithmic-bytes", type=float, default=0.0,
+                    help="with --traffic-summary --kernel K --record: the bytes one dispatch of K "
+                         "must move, for the measured / algorithmic ratio")
     ap.add_argument("--label", default="",
                     help="with --record and --kernel other than attention_kernel: the run's "
                          "workload, in words")
@@ -1306,11 +1309,20 @@ def write_record(name, summ, args):
         for k, e in rec["instances"].items():
             lines.append(f"| {k} | {e['calls']} | {e['avg_us']} | {e['min_us']} | {e['max_us']} |")
         lines += ["", f"Average over all dispatches: **{rec['launch_us']} us**."]
+        if args.algorithmic_bytes:
+            gbps = args.algorithmic_bytes / (rec["launch_us"] * 1e-6) / 1e9
+            rec["algorithmic_bytes_per_launch"] = int(args.algorithmic_bytes)
+            rec["gbps"] = round(gbps, 1)
+            rec["frac"] = round(gbps / HBM_PEAK_GBPS, 4)
+            (out / f"{name}.json").write_text(json.dumps(rec, indent=1) + "\n")
+            lines += [f"Algorithmic bytes per dispatch (given): {args.algorithmic_bytes / 1e6:.1f} MB -> "
+                      f"{gbps:.1f} GB/s = **{100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s**."]
         if untraced:
             lines += ["", "The same command without the profiler on the same box: "
                       + json.dumps({k: v for k, v in untraced.items()
-                                    if k in ("ms_per_step", "median_ms", "us_per_layer", "gbps",
-                                             "frac_of_peak", "live_rows", "tokens_per_chunk")})]
+                                    if k in ("ms_per_step", "median_ms", "us_per_layer", "us", "gbps",
+                                             "frac_of_peak", "live_rows", "tokens_per_chunk",
+                                             "reconstruct", "reconstruct_rope")})]
     elif kind == "instance_traffic":
         lines += [f"Scale from counter units to bytes: reads x{rec['fetch_scale']}, writes "
                   f"x{rec['write_scale']} (bench.py --calibrate).", "",
@@ -1321,9 +1333,12 @@ def write_record(name, summ, args):
                          f"{e['read_mb']} | {e['write_mb']} |")
         lines += ["", f"Per dispatch over the run: read {rec['read_bytes_per_launch'] / 1e6:.1f} MB + "
                   f"write {rec['write_bytes_per_launch'] / 1e6:.2f} MB."]
-        if untraced and untraced.get("gbps") and untraced.get("us_per_layer"):
-            live = untraced["gbps"] * untraced["us_per_layer"] * 1e3
-            lines += [f"The step's algorithmic (live) bytes per layer, from the untraced run: "
+        live = args.algorithmic_bytes or (untraced["gbps"] * untraced["us_per_layer"] * 1e3
+                                          if untraced and untraced.get("gbps")
+                                          and untraced.get("us_per_layer") else 0.0)
+        if live:
+            lines += [f"Algorithmic bytes per dispatch ("
+                      f"{'given' if args.algorithmic_bytes else 'the live bytes per layer of the untraced run'}): "
                       f"{live / 1e6:.1f} MB; measured / algorithmic = "
                       f"{rec['traffic_bytes_per_launch'] / live:.3f}."]
             rec["algorithmic_bytes_per_launch"] = int(live)
