@@ -233,8 +233,9 @@ slimkv_status slimkv_decode_attn_noalloc(const slimkv_problem* problem, const vo
  *   K_raw, V_raw  written at the rows above when k_new is given
  * Other arguments as for slimkv_decode_attn.  N_cap + W_cap may be 0 (then
  * only the new token is attended).  The batch is at most 1024 sequences and
- * flags must be 0 (the tiles of the whole batch are shared out over the
- * grid in a fixed order, so repeated calls are bitwise equal).  Work is
+ * the only flag accepted is SLIMKV_FLAG_CHECK_WORKSPACE (the tiles of the
+ * whole batch are shared out over the grid in a fixed order, so repeated
+ * calls are bitwise equal).  Work is
  * shared out by tiles: each (b, kv head) gets workgroups in proportion to
  * its live rows, shaped for P workgroup slots -- the device's (num_splits
  * = 0) or num_splits -- with at most 64 per (b, kv head).  Workspace:
@@ -353,7 +354,8 @@ slimkv_status slimkv_decode_attn_paged(const slimkv_problem* problem,
  *   k_new, v_new  [B, Q, H_kv, d]  the chunk's tokens (key before rotation),
  *                                  both or neither
  *   out           [B, Q, H_q, d] fp32;  lse [B, Q, H_q] fp32 or NULL
- * Capacity-sized caches, lengths, clamping, limits (batch <= 1024, flags 0)
+ * Capacity-sized caches, lengths, clamping, limits (batch <= 1024, flags as
+ * for the ragged call)
  * and num_splits as for slimkv_decode_attn_ragged.  bf16 or fp32 caches
  * (fp32: the products on the fp32 matrix instructions).  Workspace:
  * slimkv_chunk_workspace_bytes(problem, num_tokens) bytes, zero-filled
