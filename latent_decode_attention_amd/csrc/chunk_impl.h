@@ -248,8 +248,10 @@ struct ChunkState {
 // accb (accr is not started: a wave's beacon tiles come first).
 // ALIBI: score (row, query row m) gets s2 * (row * step - ofs), with s2 the
 // query head's slope in log2 units and row * step - ofs = k_pos - (q_pos +
-// t_m) for this lane's query row m (zero s2 on padding rows).
-template <int S, bool RAW, int NB, int SA, int SB, bool PG, bool ALIBI = false>
+// t_m) for this lane's query row m (zero s2 on padding rows).  FETCH =
+// false: the tile after this one is already in flight in other registers,
+// so nothing is requested (jn, bv, rw, tail are unused).
+template <int S, bool RAW, int NB, int SA, int SB, bool PG, bool ALIBI = false, bool FETCH = true>
 __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t0, int nchk, int width,
                                            const bf16x8_t (&qh)[S], const bf16x8_t (&ql)[S],
                                            ChunkState<NB>& st, uint16_t* vt,
@@ -264,19 +266,28 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, kg = lane >> 4;
 
-  // scores S^T: lane (n = query row, kg) gets cache rows 16s + 4kg + e
+  // scores S^T: lane (n = query row, kg) gets cache rows 16s + 4kg + e;
+  // each subtile takes chunk c's hi then lo term, c ascending, with the
+  // subtiles interleaved so that consecutive products are independent
   f32x4_t sc[SUB];
 #pragma unroll
-  for (int s = 0; s < SUB; ++s) {
-    f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < SUB; ++s) sc[s] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < S; ++c) {
-      if (c < nchk) {
-        const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, kbuf[s * S + c]);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh[c], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql[c], d, 0, 0, 0);
-      }
+  for (int c = 0; c < S; ++c) {
+    if (c < nchk) {
+#pragma unroll
+      for (int s = 0; s < SUB; ++s)
+        sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[s * S + c]),
+                                                        qh[c], sc[s], 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < SUB; ++s)
+        sc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kbuf[s * S + c]),
+                                                        ql[c], sc[s], 0, 0, 0);
     }
+  }
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+    f32x4_t d = sc[s];
     if constexpr (ALIBI) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[e] = fmaf(s2, (float)((t0 + 16 * s + 4 * kg + e) * step - ofs), d[e]);
@@ -287,8 +298,8 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
     sc[s] = d;
   }
   const bool ua = jn < nbt, ub = jn >= nbt && jn < total;
-  const int pid = tile_page(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub);
-  load_tile_keys<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, kbuf);
+  const int pid = FETCH ? tile_page(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub) : 0;
+  if constexpr (FETCH) load_tile_keys<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, kbuf);
 
   // this tile's values into the wave's LDS tile, row-major with padded rows
   const int pitch = width + kVPad;
@@ -304,7 +315,7 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  load_tile_values<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, vbuf);
+  if constexpr (FETCH) load_tile_values<true>(bv, jn * TRA, ua, rw, (jn - nbt) * TRB, ub, tail, pid, vbuf);
 
   // online softmax per query row (max over the row's 4 k-group lanes)
   float mx = sc[0][0];
@@ -338,20 +349,24 @@ __device__ __forceinline__ void chunk_tile(const SegView<S, true, PG>& sv, int t
 
   // O^T[col][m] += sum over rows V[row][col] P[m][row]: A operand lane
   // (n = column within the block, kg) holds rows 16s + 4kg .. +3
+  // (each block takes subtile s's hi then lo term, s ascending; the blocks
+  // are interleaved so that consecutive products are independent)
   constexpr int NA = RAW ? kHeadDim / 16 : NB;
   f32x4_t* acc = RAW ? st.accr : st.accb;
 #pragma unroll
-  for (int cb = 0; cb < NA; ++cb) {
-    if (16 * cb < width) {
+  for (int s = 0; s < SUB; ++s) {
+    s16x4_t va[NA];
 #pragma unroll
-      for (int s = 0; s < SUB; ++s) {
-        s16x4_t va;
+    for (int cb = 0; cb < NA; ++cb)
+      if (16 * cb < width)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) va[e] = (short)vt[(16 * s + 4 * kg + e) * pitch + 16 * cb + n];
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph[s], acc[cb], 0, 0, 0);
-        acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl[s], acc[cb], 0, 0, 0);
-      }
-    }
+        for (int e = 0; e < 4; ++e) va[cb][e] = (short)vt[(16 * s + 4 * kg + e) * pitch + 16 * cb + n];
+#pragma unroll
+    for (int cb = 0; cb < NA; ++cb)
+      if (16 * cb < width) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[cb], ph[s], acc[cb], 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < NA; ++cb)
+      if (16 * cb < width) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[cb], pl[s], acc[cb], 0, 0, 0);
   }
   // the next tile overwrites the LDS tile: every lane has read it by now
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -596,13 +611,24 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
 
   ChunkPrologue<NCH, !ALIBI> pro;
   pro.issue(a, b, h, M, G);
+  // The wave's first tile, and -- when its first two tiles are both beacon
+  // tiles -- its second, so that two tiles are in flight while the long
+  // prologue runs (else the second set of slots reads the tail rows, and
+  // goes unused).  The loads are issued on every path, so that the
+  // prologue's waits do not depend on the branch.
   u32x4_t kbuf[Traits<true>::kMaxLoads], vbuf[Traits<true>::kMaxLoads];
+  u32x4_t kbuf2[Traits<true>::kMaxLoads], vbuf2[Traits<true>::kMaxLoads];
   int j = wu;
+  const bool two = BLAT && wu + nwaves < nbt;  // wave-uniform
   {
     const bool ub = j < nbt, ur = j >= nbt && j < total;
     const int pid = tile_page(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur);
     load_tile_keys<true>(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur, tail, pid, kbuf);
     load_tile_values<true>(bv, j * TRB, ub, rw, (j - nbt) * TRR, ur, tail, pid, vbuf);
+    const int j2 = j + nwaves;
+    const int pid2 = tile_page(bv, j2 * TRB, two, rw, 0, false);
+    load_tile_keys<true>(bv, j2 * TRB, two, rw, 0, false, tail, pid2, kbuf2);
+    load_tile_values<true>(bv, j2 * TRB, two, rw, 0, false, tail, pid2, vbuf2);
   }
   pro.finish(a, sh, wave, M, G);
   if (c == 0 && a.k_new)  // workgroup-uniform
@@ -633,6 +659,16 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
     bf16x8_t qlh[BN], qll[BN];
     chunk_query<BN>(sh.u.s.qlat, rk, qlh, qll);
     const int nchk = (rk + 31) / 32;
+    if (two) {
+      // the first tile requests the third; the second is already here
+      chunk_tile<BN, false, NB, BN, 4, PG, ALIBI>(bv, j * TRB, nchk, rv, qlh, qll, st, vt, bv, rw,
+                                                  j + 2 * nwaves, nbt, total, tail, kbuf, vbuf, s2,
+                                                  bofs, a.beacon_stride);
+      chunk_tile<BN, false, NB, BN, 4, PG, ALIBI, false>(bv, (j + nwaves) * TRB, nchk, rv, qlh, qll,
+                                                         st, vt, bv, rw, 0, nbt, total, tail, kbuf2,
+                                                         vbuf2, s2, bofs, a.beacon_stride);
+      j += 2 * nwaves;
+    }
     for (; j < nbt; j += nwaves)
       chunk_tile<BN, false, NB, BN, 4, PG, ALIBI>(bv, j * TRB, nchk, rv, qlh, qll, st, vt, bv, rw,
                                                   j + nwaves, nbt, total, tail, kbuf, vbuf, s2,
@@ -673,16 +709,21 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
     s16x4_t bh[NB], bl[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) split_bf16x4(st.accb[cb], bh[cb], bl[cb]);
+    // each accumulator takes block cb's hi then lo term, cb ascending; the
+    // d blocks are interleaved so that consecutive products are independent
 #pragma unroll
-    for (int db = 0; db < kHeadDim / 16; ++db) {
+    for (int cb = 0; cb < NB; ++cb) {
+      if (cb < ncb) {
+        s16x4_t ua[kHeadDim / 16];
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        if (cb < ncb) {
-          const s16x4_t ua =
-              *reinterpret_cast<const s16x4_t*>(sh.u.uv + (16 * db + n) * upitch + 16 * cb + 4 * kg);
-          st.accr[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua, bh[cb], st.accr[db], 0, 0, 0);
-          st.accr[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua, bl[cb], st.accr[db], 0, 0, 0);
-        }
+        for (int db = 0; db < kHeadDim / 16; ++db)
+          ua[db] = *reinterpret_cast<const s16x4_t*>(sh.u.uv + (16 * db + n) * upitch + 16 * cb + 4 * kg);
+#pragma unroll
+        for (int db = 0; db < kHeadDim / 16; ++db)
+          st.accr[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua[db], bh[cb], st.accr[db], 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < kHeadDim / 16; ++db)
+          st.accr[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ua[db], bl[cb], st.accr[db], 0, 0, 0);
       }
     }
     lds_barrier();  // every wave is done with U_V (the park aliases it)
