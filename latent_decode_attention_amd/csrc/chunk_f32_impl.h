@@ -224,7 +224,7 @@ __device__ __forceinline__ void chunk_unit_f32(const AttnArgs& a, ChunkSharedF32
   const int n = lane & 15, kg = lane >> 4;
   const int G = a.group, M = G * a.num_tokens;
   const int nwaves = kWaves * k;
-  const int wu = kWaves * c + wave;
+  const int wu = kWaves * ((c + k - 1) % k) + wave;  // the token workgroup dealt last
   const int rk = BLAT ? a.seg[0].rk : 0, rv = BLAT ? a.seg[0].rv : 0;
 
   SegView<8, false, PG> bv, rw;

@@ -574,7 +574,10 @@ __device__ __forceinline__ void chunk_unit(const AttnArgs& a, ChunkShared& sh, i
   const int n = lane & 15, kg = lane >> 4;
   const int G = a.group, M = G * a.num_tokens;
   const int nwaves = kWaves * k;
-  const int wu = kWaves * c + wave;
+  // the order in which tiles are dealt: the unit's first workgroup, which
+  // also makes the chunk tokens' partial, comes last, so that it is the
+  // one that gets a tile fewer when the unit's tiles do not divide evenly
+  const int wu = kWaves * ((c + k - 1) % k) + wave;
   const int rk = BLAT ? a.seg[0].rk : 0, rv = BLAT ? a.seg[0].rv : 0;
 
   SegView<BN, true, PG> bv;

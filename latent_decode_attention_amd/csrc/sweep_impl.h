@@ -1318,7 +1318,11 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int n = lane & 15, kg = lane >> 4;
   const int nwaves = kWaves * k;
-  const int wu = kWaves * c + wave;  // this wave's number within the unit
+  // this wave's number within the unit (the order in which tiles are
+  // dealt); a ragged unit's first workgroup, which also makes the new
+  // token's partial, is dealt last, so that it is the one that gets a tile
+  // fewer when the unit's tiles do not divide evenly
+  const int wu = kWaves * (RAGGED ? (c + k - 1) % k : c) + wave;
 
   SegView<BN, BF16, PG, D> bv;        // beacon rows
   SegView<kFullNch, BF16, PG, D> rw;  // raw rows
