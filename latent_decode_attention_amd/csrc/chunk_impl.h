@@ -40,6 +40,7 @@
 namespace slimkv {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kVPad = 4;  // value-tile row padding (elements)
 // The largest padded value tile: 64 rows of r_V <= 32 (larger ranks have
@@ -96,22 +97,19 @@ struct ChunkPrologue {
   static constexpr bool kLat = NCH > 0;
   static constexpr int kHalf = kHeadDim / 2;
   static constexpr int kPairs = kChunkRows * kHalf / kThreads;             // 4
-  static constexpr int kWords = kLat ? 64 * kHeadDim / 8 / kThreads : 1;   // per half, r_K <= 128
-  uint32_t x1[kPairs], x2[kPairs];
+  static constexpr int kWords = kLat ? 64 * 32 * NCH / 8 / kThreads : 1;  // per half, r_K <= 32 NCH
+  u32x4_t qraw;  // query row tid / 16 (clamped to M - 1), columns 8 (tid % 16) .. +7
   int pos0;
   u32x4_t uk[2][kWords];
 
   __device__ __forceinline__ void issue(const AttnArgs& a, int b, int h, int M, int G) {
     const int tid = threadIdx.x;
     const int Q = a.num_tokens;
-#pragma unroll
-    for (int j = 0; j < kPairs; ++j) {
-      const int p = min(tid + kThreads * j, M * kHalf - 1);
-      const int m = p / kHalf, i = p % kHalf;
+    {
+      const int m = min(tid / 16, M - 1), c8 = tid & 15;
       const int t = m / G, g = m - t * G;
-      const size_t base = (((size_t)b * Q + t) * a.num_q_heads + (size_t)h * G + g) * kHeadDim;
-      x1[j] = ld_bits<true>(a.q, base + i);
-      x2[j] = ld_bits<true>(a.q, base + i + kHalf);
+      const size_t base = (((size_t)b * Q + t) * a.num_q_heads + (size_t)h * G + g) * kHeadDim + 8 * c8;
+      qraw = load16(static_cast<const uint16_t*>(a.q) + base);
     }
     pos0 = a.q_pos[b];
     if constexpr (kLat) {
@@ -130,16 +128,42 @@ struct ChunkPrologue {
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = lane & 15, kg = lane >> 4;
     const float sc = (float)a.score_scale;
+    // the query rows into sh.qrot as they are (rotated in place below)
+    {
+      float* dst = &sh.u.s.qrot[tid / 16][8 * (tid & 15)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = __uint_as_float(qraw[e] << 16);
+        dst[2 * e + 1] = __uint_as_float(qraw[e] & 0xffff0000u);
+      }
+    }
+    // the rotation depends on the token, not the head: each (token, pair)
+    // angle is taken once, into a table in the space qlat takes later
+    f32x2_t(*tab)[kHalf] = reinterpret_cast<f32x2_t(*)[kHalf]>(&sh.u.s.qlat[0][0]);
+    if constexpr (ROTATE) {
+      const int Q = a.num_tokens;
+#pragma unroll
+      for (int j = 0; j < kPairs; ++j) {
+        const int t = wave + kWaves * j;  // token, pair `lane`
+        if (t < Q) {
+          float sn, cs;
+          rope_sincos(a, pos0 + t, lane, sn, cs);
+          tab[t][lane] = f32x2_t{sn, cs};
+        }
+      }
+    }
+    lds_barrier();
+    // each (row, pair) is read and rewritten by one thread only
 #pragma unroll
     for (int j = 0; j < kPairs; ++j) {
       const int p = tid + kThreads * j;  // < 16 * 64
       const int m = p / kHalf, i = p % kHalf;
       float r1 = 0.0f, r2 = 0.0f;
       if (m < M) {
-        const float v1 = bits_to_float<true>(x1[j]), v2 = bits_to_float<true>(x2[j]);
+        const float v1 = sh.u.s.qrot[m][i], v2 = sh.u.s.qrot[m][i + kHalf];
         if constexpr (ROTATE) {
-          float sn, cs;
-          rope_sincos(a, pos0 + m / G, i, sn, cs);
+          const f32x2_t t2 = tab[m / G][i];
+          const float sn = t2[0], cs = t2[1];
           r1 = (v1 * cs - v2 * sn) * sc;
           r2 = (v2 * cs + v1 * sn) * sc;
         } else {  // an ALiBi backbone rotates nothing
