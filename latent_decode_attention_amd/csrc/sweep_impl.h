@@ -235,6 +235,7 @@ struct QueryPrologue {
   static constexpr bool kStage = BF16 && kLat;    // U_K staged through LDS
   static constexpr int kHalf = kHeadDim / 2;
   static constexpr int kPairs = (G * kHalf + kThreads - 1) / kThreads;  // rotation pairs per thread
+  static_assert(kThreads % kHalf == 0, "a thread's pairs share one index");
   static constexpr int kTiles = kLat ? kHeadDim / 16 / kWaves : 0;       // latent column tiles per wave
   // 16-byte words of U_K per thread when staged: r_K <= 32 * NCH
   static constexpr int kWords = kStage ? kHeadDim * 32 * NCH / 8 / kThreads : 1;
@@ -300,6 +301,11 @@ struct QueryPrologue {
         }
       }
     }
+    // a thread's pairs all have index i = lane (kThreads is a multiple of
+    // kHalf), and the heads share the position: with more than one pair per
+    // thread (G > 4) one angle, taken first, serves them all
+    float sn1 = 0.0f, cs1 = 1.0f;
+    if constexpr (ROTATE && kPairs > 1) rope_sincos(a, pos, lane, sn1, cs1);
 #pragma unroll
     for (int j = 0; j < kPairs; ++j) {
       const int p = tid + kThreads * j;
@@ -308,8 +314,8 @@ struct QueryPrologue {
         const float v1 = bits_to_float<BF16>(x1[j]), v2 = bits_to_float<BF16>(x2[j]);
         const float sc = (float)a.score_scale;
         if constexpr (ROTATE) {
-          float sn, cs;
-          rope_sincos(a, pos, i, sn, cs);
+          float sn = sn1, cs = cs1;
+          if constexpr (kPairs == 1) rope_sincos(a, pos, i, sn, cs);
           sh.qrot[g][i] = (v1 * cs - v2 * sn) * sc;
           sh.qrot[g][i + kHalf] = (v2 * cs + v1 * sn) * sc;
         } else {  // an ALiBi backbone rotates nothing
