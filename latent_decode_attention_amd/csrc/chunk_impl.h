@@ -827,7 +827,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void chunk_kernel(
   const int tid = threadIdx.x;
   const int Hkv = a.num_kv_heads, P = a.chunks;
   const int pi = ragged_piece_of((int)blockIdx.x, P);
-  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, pick, tid & 63, P, pi);
+  ragged_schedule_wg<TRB, TRR>(a, pick, tid, P, pi);
   lds_barrier();
   const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
   if (pi >= uni(pick.total)) return;

@@ -49,6 +49,7 @@ namespace slimkv {
 // nothing to do).
 struct RaggedPick {
   int32_t b, first, k, nb, w, total;
+  int32_t cnt[kWaves][64];  // the waves' partial piece counts per candidate share
 };
 
 // Wave-wide sums and maxima of integers on the VALU (DPP rotations within
@@ -228,6 +229,78 @@ __device__ __forceinline__ void ragged_schedule(const AttnArgs& a, RaggedPick& p
   if (lane == 63) pick.total = incl;
 }
 
+// ragged_schedule run by the whole workgroup (tid = threadIdx.x): up to 64
+// sequences with fewer than 64 candidate shares, the four waves count the
+// pieces at every candidate over a quarter of the sequences each (wave w
+// takes sequences w, w + 4, ...) and add their counts through LDS, so the
+// search takes a quarter of the steps; wave 0 then numbers the pieces.
+// Every other case is ragged_schedule on wave 0.  The share found, and so
+// the pick, is the same.  The caller's LDS barrier follows.
+template <int TRB, int TRR>
+__device__ __forceinline__ void ragged_schedule_wg(const AttnArgs& a, RaggedPick& pick, int tid, int P,
+                                                   int pi) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int B = a.batch, ncap = a.seg[0].rows, wcap = a.seg[1].rows, Hkv = a.num_kv_heads;
+  const int units = B * Hkv;
+  // workgroup-uniform throughout: every wave sees the same lengths
+  bool fast = units < P && B <= 64;
+  int nb = 0, w = 0, tiles = -1, lo = 1, hi = 1;
+  const bool mine = lane < B;
+  if (fast) {
+    // lane b holds sequence b (every wave loads the lengths)
+    const int bl = min(lane, B - 1);
+    nb = a.seq_beacons ? a.seq_beacons[bl] : ncap;
+    w = a.seq_raw ? a.seq_raw[bl] : wcap;
+    nb = min(max(nb, 0), ncap);
+    w = min(max(w, 0), wcap);
+    tiles = mine ? (nb + TRB - 1) / TRB + (w + TRR - 1) / TRR : -1;
+    const int T = wave_sum_i(mine ? tiles : 0) * Hkv;
+    const int tmax = wave_max_i(mine ? tiles : 0);
+    lo = max(1, (T + P - 1) / P);
+    hi = max(lo, tmax);
+    if (P > units) hi = min(hi, max(lo, (T + (P - units) - 1) / (P - units)));
+    fast = hi - lo < 64 && tmax < (1 << 23);
+  }
+  if (!fast) {
+    if (wave == 0) ragged_schedule<TRB, TRR>(a, pick, lane, P, pi);
+    return;
+  }
+  // ceil(t / L) for t, L below 2^23, from the reciprocal, clamped to 65 and
+  // corrected by one either way (as in ragged_schedule), then clamped to
+  // [1, kMaxChunks]
+  const auto pieces_at = [](int t, int L, float rc) {
+    int q = min((int)__builtin_ceilf((float)t * rc), kMaxChunks + 1);
+    if (__mul24(q - 1, L) >= t) --q;
+    if (__mul24(q, L) < t) ++q;
+    return min(max(q, 1), kMaxChunks);
+  };
+  // lane j: pieces at share lo + j over this wave's sequences
+  const int Lc = lo + lane;
+  const float rc = __builtin_amdgcn_rcpf((float)Lc);
+  int c = 0;
+  for (int s = wave; s < B; s += kWaves) c += pieces_at(__builtin_amdgcn_readlane(tiles, s), Lc, rc);
+  pick.cnt[wave][lane] = c;
+  lds_barrier();
+  if (wave != 0) return;
+  c = pick.cnt[0][lane];
+#pragma unroll
+  for (int v = 1; v < kWaves; ++v) c += pick.cnt[v][lane];
+  const uint64_t fits = __builtin_amdgcn_ballot_w64(c * Hkv <= P && Lc <= hi);
+  const int L = fits ? lo + __builtin_ctzll(fits) : hi;
+  const int pk = mine ? pieces_at(tiles, L, __builtin_amdgcn_rcpf((float)L)) : 0;
+  const int psum = pk * Hkv;
+  const int incl = wave_scan_i(psum, lane);
+  const int run = incl - psum;
+  if (pk > 0 && pi >= run && pi < run + psum) {
+    pick.b = lane;
+    pick.first = run;
+    pick.k = pk;
+    pick.nb = nb;
+    pick.w = w;
+  }
+  if (lane == 63) pick.total = incl;
+}
+
 // Piece (workgroup slot) of block blk among the first P blocks, which take
 // a CU's first and second workgroup slots in turn: the first half of them
 // the even pieces, the second half the odd ones shifted by four blocks, so
@@ -262,7 +335,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu * kWaves / 4) void ragged_kernel
   const int tid = threadIdx.x;
   const int Hkv = a.num_kv_heads, P = a.chunks;
   const int pi = ragged_piece_of((int)blockIdx.x, P);
-  if ((tid >> 6) == 0) ragged_schedule<TRB, TRR>(a, pick, tid & 63, P, pi);
+  ragged_schedule_wg<TRB, TRR>(a, pick, tid, P, pi);
   lds_barrier();
   // values read back from LDS are the same in every lane: readfirstlane
   // keeps what derives from them (addresses, descriptors) in scalar registers
