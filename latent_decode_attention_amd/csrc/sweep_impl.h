@@ -190,6 +190,7 @@ struct alignas(16) AttnShared {
   float wml[2][kWaves][kMaxGroup][2];  // each wave's (max, sum) per head, per segment
   float sml[2][kMaxGroup][2];          // the workgroup's (max, sum) per head, per segment
   float pml[kMaxGroup][2];             // the workgroup's partial: (max, sum) per head
+  uint32_t tokk[kHeadDim];             // the new token's key, rotated and rounded (storage bits)
   int is_last;
 };
 
@@ -1130,8 +1131,10 @@ __device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
 // workgroup in its prologue, while its first tile is in flight: thread
 // (g, c4) owns 16-byte column c4 of head g.  The token's key is rotated at
 // q_pos in fp64 and rounded once to the storage dtype -- the row the cache
-// keeps -- and scored against the rotated, pre-scaled query in LDS (summed
-// over the head's 32 threads); the partial (score, 1, value) goes to the
+// keeps: rotate() has thread p < 64 turn pair (p, p + 64), one angle each,
+// into sh.tokk, which every head then reads -- and scored against the
+// rotated, pre-scaled query in LDS (summed over the head's 32 threads);
+// the partial (score, 1, value) goes to the
 // unit's token slot (a.tok_slot0 + u) with device-coherent stores, for the
 // merge.  The token's row is stored when the raw window has room (wlive <
 // its capacity): no workgroup reads that row in this call.  PG: through the
@@ -1140,17 +1143,34 @@ __device__ __forceinline__ uint32_t storage_bits_from_f64(double x) {
 // as given; it sits at the query's own position, so its bias is zero.
 template <int G, bool BF16, bool ALIBI = false>
 struct TokenPartial {
-  uint32_t k1[4], k2[4], v[4];  // storage bits: key elements i and their rotation partners, values
+  static constexpr int kHalf = kHeadDim / 2;
+  static constexpr int kThreadsUsed = G * kHeadDim / 4 > kHalf ? G * kHeadDim / 4 : kHalf;
+  uint32_t kp1, kp2, v[4];  // storage bits: key pair (p, p + 64) with p = tid % 64; values
+  // Run by threads tid < kThreadsUsed of the unit's first workgroup.
   __device__ __forceinline__ void issue(const AttnArgs& a, int u) {
     const int tid = threadIdx.x;
-    const int c4 = tid % (kHeadDim / 4);
+    const int c4 = tid % (kHeadDim / 4), p = tid % kHalf;
     const size_t kb = (size_t)u * kHeadDim;
+    kp1 = ld_bits<BF16>(a.k_new, kb + p);
+    kp2 = ld_bits<BF16>(a.k_new, kb + p + kHalf);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * c4 + e;
-      k1[e] = ld_bits<BF16>(a.k_new, kb + i);
-      k2[e] = ld_bits<BF16>(a.k_new, kb + (i ^ (kHeadDim / 2)));
-      v[e] = ld_bits<BF16>(a.v_new, kb + i);
+    for (int e = 0; e < 4; ++e) v[e] = ld_bits<BF16>(a.v_new, kb + 4 * c4 + e);
+  }
+  // Run by every thread of the unit's first workgroup; the caller's LDS
+  // barrier follows before finish().
+  __device__ __forceinline__ void rotate(const AttnArgs& a, AttnShared& sh, int pos) const {
+    const int tid = threadIdx.x;
+    if (tid < kHalf) {
+      uint32_t b1 = kp1, b2 = kp2;
+      if constexpr (!ALIBI) {
+        double s64, c64;
+        sincos(rope_angle(a, pos, tid), &s64, &c64);  // the reduced angle: no large-argument path
+        const double k1 = (double)bits_to_float<BF16>(kp1), k2 = (double)bits_to_float<BF16>(kp2);
+        b1 = storage_bits_from_f64<BF16>(k1 * c64 - k2 * s64);
+        b2 = storage_bits_from_f64<BF16>(k2 * c64 + k1 * s64);
+      }
+      sh.tokk[tid] = b1;
+      sh.tokk[tid + kHalf] = b2;
     }
   }
   template <bool PG>
@@ -1158,20 +1178,12 @@ struct TokenPartial {
                                          int wlive, const int32_t* ptab, int rtab0) const {
     const int tid = threadIdx.x;
     const int g = tid / (kHeadDim / 4), c4 = tid % (kHeadDim / 4);
-    const int pos = a.q_pos[b];
     uint32_t kbits[4];
     float dot = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 4 * c4 + e, pi = i & (kHeadDim / 2 - 1);
-      if constexpr (ALIBI) {
-        kbits[e] = k1[e];
-      } else {
-        double s64, c64;
-        sincos(rope_angle(a, pos, pi), &s64, &c64);  // the reduced angle: no large-argument path
-        const double ki = (double)bits_to_float<BF16>(k1[e]), kp = (double)bits_to_float<BF16>(k2[e]);
-        kbits[e] = storage_bits_from_f64<BF16>(i < kHeadDim / 2 ? ki * c64 - kp * s64 : ki * c64 + kp * s64);
-      }
+      const int i = 4 * c4 + e;
+      kbits[e] = sh.tokk[i];
       dot += sh.qrot[g][i] * bits_to_float<BF16>(kbits[e]);
     }
     dot = xor16_sum(row16_sum(dot));  // the 32 threads of head g; log2 units (pre-scaled query)
@@ -1373,8 +1385,9 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
   pro.issue(a, b, h, wave);
   // ragged calls: the unit's first workgroup makes the new token's partial
   TokenPartial<G, BF16, ALIBI> tokp;
-  const bool tok = RAGGED && c == 0 && a.k_new != nullptr && tid < G * kHeadDim / 4;
-  if (tok) tokp.issue(a, unit);
+  const bool tokwg = RAGGED && c == 0 && a.k_new != nullptr;  // workgroup-uniform
+  const bool tok = tokwg && tid < G * kHeadDim / 4;
+  if (tokwg && tid < TokenPartial<G, BF16, ALIBI>::kThreadsUsed) tokp.issue(a, unit);
   u32x4_t kbuf[Traits<BF16>::kMaxLoads * D], vbuf[Traits<BF16>::kMaxLoads * D];
   int j = wu;
   {
@@ -1387,8 +1400,13 @@ __device__ __forceinline__ void attend_unit(const AttnArgs& a, AttnShared& sh, i
     load_tile_values<true>(bv, tb, ub, rw, tr, ur, tail, pid, vbuf);
   }
   pro.finish(a, sh, wave);
-  if constexpr (RAGGED)
-    if (tok) tokp.template finish<PG>(a, sh, unit, b, h, wr, ptab, nbp);
+  if constexpr (RAGGED) {
+    if (tokwg) {
+      tokp.rotate(a, sh, pro.pos);  // the query's position
+      lds_barrier();
+      if (tok) tokp.template finish<PG>(a, sh, unit, b, h, wr, ptab, nbp);
+    }
+  }
 
   float* pw = sh.u.s.t.p[wave];
   // ALiBi: this lane's heads' slopes in log2 units, and each segment's
