@@ -131,6 +131,26 @@ def test_large_batches(B, splits, gpu_device):
     check_ragged(wl, num_splits=splits, fixed=fixed, what=f"B={B} splits={splits}")
 
 
+@pytest.mark.parametrize("B", [64, 65])
+def test_schedule_batch_boundary(B, gpu_device):
+    """64 sequences: the largest batch whose share search runs on all four
+    waves of a workgroup (one sequence per lane); 65: the single-wave
+    schedule with several sequences per lane."""
+    wl = custom(B=B, Hkv=2, G=4, nb=96, w=40, r=32, index=107 + B % 5)
+    fixed = {0: (0, 0), 1: (96, 40), B - 1: (50, 3), B // 2: (1, 0)}
+    check_ragged(wl, fixed=fixed, what=f"B={B}")
+
+
+def test_schedule_wide_share_range(gpu_device):
+    """One sequence of 129 tiles (8192 beacons in 64-row tiles, and a raw
+    tile) among fifteen of two, in 17 workgroup slots for 16 units: the
+    candidate shares run from 10 to 129, more than the 64 a wave tests at
+    once, so the schedule takes the single-wave bisection."""
+    wl = custom(B=16, Hkv=1, G=4, nb=8192, w=16, r=32, index=110)
+    fixed = {i: ((8192, 4) if i == 0 else (8, 4)) for i in range(16)}
+    check_ragged(wl, fixed=fixed, num_splits=17, what="wide share range")
+
+
 @pytest.mark.parametrize("planted", [False, True])
 def test_workspace_check_flag(planted, gpu_device):
     """SLIMKV_FLAG_CHECK_WORKSPACE on a ragged call: counters left nonzero (as
