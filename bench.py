@@ -82,6 +82,9 @@ def parse_args():
     ap.add_argument("--ragged", action="store_true",
                     help="only time the ragged serving step of the c3 workload (live lengths 50-100%% "
                          "of the capacities, new token stored) and print its figures as one JSON line")
+    ap.add_argument("--even-lengths", action="store_true",
+                    help="with --ragged or --chunk: every sequence at the drawn lengths' means (the "
+                         "same live bytes, split evenly over the units)")
     ap.add_argument("--paged", type=int, default=0, metavar="ROWS",
                     help="with --ragged or --chunk: the cache in pages of ROWS rows (a power "
                          "of two >= 64) at shuffled page ids, through slimkv_decode_attn_paged "
@@ -295,14 +298,14 @@ def main():
     layers = [synth.make_layer(wl, layer, device=dev) for layer in range(wl.layers)]
     if args.ragged:
         print(json.dumps(ragged_step(lda, synth, torch, dev, wl, layers, args.steps,
-                                     page_rows=args.paged)), flush=True)
+                                     page_rows=args.paged, even=args.even_lengths)), flush=True)
         return
     if args.alibi:
         print(json.dumps(alibi_step(lda, synth, torch, dev, wl, layers, args.steps)), flush=True)
         return
     if args.chunk:
         print(json.dumps(chunk_step(lda, synth, torch, dev, wl, layers, args.steps, args.chunk,
-                                    page_rows=args.paged)),
+                                    page_rows=args.paged, even=args.even_lengths)),
               flush=True)
         return
     probs = [lda.problem_from_tensors(x.q, x.U_K, x.C_K, x.K_raw, U_V=x.U_V,
@@ -434,10 +437,16 @@ def main():
                                                                  args.steps)
             result["comparison"]["c3_paged_step"] = ragged_step(lda, synth, torch, dev, wl, layers,
                                                                 args.steps, page_rows=64)
+            # the same live bytes with every sequence at the mean lengths: what
+            # an even split of the work over the workgroups gives
+            result["comparison"]["c3_ragged_step_even_lengths"] = ragged_step(
+                lda, synth, torch, dev, wl, layers, args.steps, even=True)
             result["comparison"]["c3_chunk4_step"] = chunk_step(lda, synth, torch, dev, wl, layers,
                                                                  args.steps, 4)
             result["comparison"]["c3_chunk4_paged_step"] = chunk_step(
                 lda, synth, torch, dev, wl, layers, args.steps, 4, page_rows=64)
+            result["comparison"]["c3_chunk4_step_even_lengths"] = chunk_step(
+                lda, synth, torch, dev, wl, layers, args.steps, 4, even=True)
             result["comparison"]["c3_alibi_step"] = alibi_step(lda, synth, torch, dev, wl, layers,
                                                                args.steps)
             result["comparison"]["c4_step"] = other_step(lda, synth, torch, dev, "c4", args.steps)
@@ -646,7 +655,16 @@ def replay_stats(torch, step, steps):
     return timed_steps(torch, g.replay, steps, 3)
 
 
-def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
+def even_lengths(synth, wl, layer, dev, first):
+    """The step's lengths with every sequence at the drawn lengths' (rounded)
+    means: about the same live bytes, split evenly over the units, so that
+    the schedule's pieces all carry the same tiles."""
+    m = (int(round(float(first.num_beacons.float().mean()))),
+         int(round(float(first.raw_len.float().mean()))))
+    return synth.make_step(wl, layer, device=dev, fixed={b: m for b in range(wl.batch)})
+
+
+def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0, even=False):
     """The same 32-layer step as a serving step over a ragged batch: each
     sequence keeps a seeded number of live beacons (4096..8192) and raw rows
     (1024..2047) in the arrays, and every layer attends and stores the step's
@@ -654,9 +672,12 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
     pages of that many rows at seeded, shuffled page ids, and the step runs
     slimkv_decode_attn_paged on them.  Bytes: the live rows, the new token's
     key and value read and written, q, the bases, out and lse (the page
-    tables add 4 bytes per page, left out)."""
+    tables add 4 bytes per page, left out).  even: every sequence at the
+    drawn lengths' means instead (even_lengths)."""
     elem = wl.elem_bytes
     first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
+    if even:
+        first = even_lengths(synth, wl, layers[0], dev, first)
     steps_in, probs, bytes_step = [], [], 0
     nb = first.num_beacons.cpu().numpy().clip(0, wl.num_beacons)
     rw = first.raw_len.cpu().numpy().clip(0, wl.raw_window)
@@ -717,17 +738,20 @@ def ragged_step(lda, synth, torch, dev, wl, layers, steps, page_rows=0):
     return res
 
 
-def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens, page_rows=0):
+def chunk_step(lda, synth, torch, dev, wl, layers, steps, num_tokens, page_rows=0, even=False):
     """The ragged serving step of ragged_step with a chunk of num_tokens
     query tokens per sequence (e.g. drafted tokens checked in one pass):
     every layer attends each token over the live rows and the chunk's tokens
     up to it, and stores the tokens (slimkv_decode_attn_chunk).  page_rows >
     0: the cache lies in pages of that many rows at seeded, shuffled page
     ids (slimkv_decode_attn_chunk_paged).  Bytes: the live rows, the tokens'
-    keys and values read and written, the queries, the bases, out and lse."""
+    keys and values read and written, the queries, the bases, out and lse.
+    even: every sequence at the drawn lengths' means instead (even_lengths)."""
     elem = wl.elem_bytes
     Q = num_tokens
     first = synth.make_step(wl, layers[0], device=dev, beacons=(0.5, 1.0), raw=(0.5, 1.0))
+    if even:
+        first = even_lengths(synth, wl, layers[0], dev, first)
     nb = first.num_beacons.cpu().numpy().clip(0, wl.num_beacons)
     rw = first.raw_len.cpu().numpy().clip(0, wl.raw_window - Q)
     raw_len = torch.from_numpy(rw.astype("int32")).to(dev)

@@ -183,3 +183,20 @@ def test_committed_profiles_match_the_kernel_sources():
         assert rec["source_sha256"] == sha, f"{p.name} was taken on other kernel sources"
         md = p.with_suffix(".md")
         assert md.exists() and sha in md.read_text()
+
+
+def test_even_lengths_keep_the_drawn_means():
+    """The even-lengths serving line: every sequence gets the drawn lengths'
+    rounded means, so the live rows (and bytes) match the drawn step's to
+    within rounding and the pieces of the schedule all carry the same tiles."""
+    import synth
+
+    wl = synth.get_workload("c3")
+    stand_in = types.SimpleNamespace(num_beacons=wl.num_beacons, raw_window=wl.raw_window, layer=0)
+    first = synth.make_step(wl, stand_in, beacons=(0.5, 1.0), raw=(0.5, 1.0))
+    even = bench.even_lengths(synth, wl, stand_in, "cpu", first)
+    nb, rw = first.num_beacons.numpy(), first.raw_len.numpy()
+    assert len(set(even.num_beacons.tolist())) == 1 and len(set(even.raw_len.tolist())) == 1
+    assert abs(int(even.num_beacons.sum()) - int(nb.sum())) <= wl.batch // 2
+    assert abs(int(even.raw_len.sum()) - int(rw.sum())) <= wl.batch // 2
+    assert nb.min() < nb.max()  # the drawn lengths are ragged
